@@ -1,0 +1,232 @@
+"""fp64 CPU oracle for the TTT-layer forward pass.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path imports this module: only
+tests/, __graft_entry__.smoke() and the cpu_baseline leg of bench.py may use it.
+It shares no code with the HIP library (test_sequence_layers_amd/csrc) and does
+not import the package; the two meet only through the seeded input generator.
+
+What it computes, per (batch, head) pair -- every head is an independent inner
+model (Vision-TTT summary on gist.science, "Methodologie" item 3: the hidden
+state is split over several heads):
+
+* Tokens are rows. The inner linear model predicts k.W with W of shape [D, D];
+  the inner MLP predicts GELU(k.W1).W2.
+* The self-supervised loss of one token is l(W; k, v) = 1/2 ||f_W(k) - v||^2
+  (reconstruction loss: Vision-TTT summary, "Methodologie" item 1; ViT^3
+  review on techloop.online, design-space study: an MSE-type loss). A step over
+  a batch of n tokens averages the per-token gradients, so the step is
+  W <- W - (eta/n) * sum_j grad l_j(W) (the gradient-descent rule in
+  "Methodologie" item 1 of the Vision-TTT summary, with mini-batches of
+  "Methodologie" item 3).
+* Gradients are hand-derived closed forms, not autograd (ViT^3 review, section
+  on the official code: the authors write the inner gradient by hand).
+
+Everything is evaluated in the PRIMAL form: the weights each output is read with
+are materialised explicitly. The GPU path uses different algebra (dual forms,
+affine segment maps), so the two share neither code nor association order.
+
+Inputs are [B, N, H, D] arrays (already rounded to the I/O dtype; they are
+widened to float64 here); inner states are [H, ...] (shared over the batch) or
+[B, H, ...] (one per batch element).
+
+Parity status: every function here is pinned by tests/test_oracle_pins.py
+(closed forms, special cases, finite differences, autograd, exact rational
+arithmetic). None is "parity unpinned".
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+from scipy.special import erf
+
+_SQRT2 = math.sqrt(2.0)
+_INV_SQRT_2PI = 1.0 / math.sqrt(2.0 * math.pi)
+
+
+def _bhnd(x) -> np.ndarray:
+    """[B, N, H, D] -> float64 [B, H, N, D]."""
+    return np.ascontiguousarray(np.transpose(np.asarray(x, dtype=np.float64), (0, 2, 1, 3)))
+
+
+def _bnhd(x) -> np.ndarray:
+    """float64 [B, H, N, D] -> [B, N, H, D]."""
+    return np.ascontiguousarray(np.transpose(x, (0, 2, 1, 3)))
+
+
+def _state(w, B: int, H: int) -> np.ndarray:
+    """[H, r, c] or [B, H, r, c] -> float64 [B, H, r, c] (a private copy)."""
+    w = np.asarray(w, dtype=np.float64)
+    if w.ndim == 3:
+        w = np.broadcast_to(w, (B,) + w.shape)
+    if w.shape[:2] != (B, H):
+        raise ValueError(f"state shape {w.shape} does not match B={B}, H={H}")
+    return np.array(w)
+
+
+def _t(x: np.ndarray) -> np.ndarray:
+    """Transpose of the last two axes."""
+    return np.swapaxes(x, -1, -2)
+
+
+def _check_chunk(N: int, chunk: int) -> None:
+    if chunk <= 0 or N % chunk != 0:
+        raise ValueError(f"sequence length {N} is not a multiple of the mini-batch size {chunk}")
+
+
+# --------------------------------------------------------------------------------------------
+# Variant (a): single-epoch full-batch update (ViT^3)
+# --------------------------------------------------------------------------------------------
+def fullbatch(q, k, v, w0, eta: float):
+    """One full-batch gradient step on all N (k, v) pairs, then read out Q.
+
+    ViT^3 review (techloop.online), "core idea" section: train the inner model on
+    (K, V), get W*, output F_{W*}(Q); design-space study: one epoch, full batch,
+    inner learning rate 1.0. With l_j = 1/2 ||k_j W - v_j||^2 averaged over N:
+        W* = W0 - (eta/N) K^T (K W0 - V),   O = Q W*.
+    Returns (O [B,N,H,D], W* [B,H,D,D]).
+    """
+    Q, K, V = _bhnd(q), _bhnd(k), _bhnd(v)
+    B, H, N, _ = Q.shape
+    W0 = _state(w0, B, H)
+    E = K @ W0 - V                       # residuals f_W0(k_j) - v_j, one row per token
+    G = _t(K) @ E                        # sum_j of per-token gradients k_j^T e_j
+    W = W0 - (eta / N) * G
+    return _bnhd(Q @ W), W
+
+
+# --------------------------------------------------------------------------------------------
+# Variant (b): bidirectional chunked scan (Vision-TTT)
+# --------------------------------------------------------------------------------------------
+def _scan_noncausal(Q, K, V, W0, eta: float, b: int):
+    """Mini-batch GD over consecutive chunks of b tokens; each chunk is read out
+    with the state *after* its own update (non-causal inside the chunk)."""
+    N = Q.shape[2]
+    W = W0.copy()
+    O = np.empty_like(Q)
+    for c0 in range(0, N, b):
+        Kc, Vc = K[:, :, c0:c0 + b], V[:, :, c0:c0 + b]
+        W = W - (eta / b) * (_t(Kc) @ (Kc @ W - Vc))
+        O[:, :, c0:c0 + b] = Q[:, :, c0:c0 + b] @ W
+    return O, W
+
+
+def chunked_bidir(q, k, v, w0, eta: float, chunk: int):
+    """Forward scan plus a scan of the token-reversed sequence, both from W0, summed.
+
+    Vision-TTT summary (gist.science), "Methodologie" item 2: tokens are scanned
+    both forwards and backwards; item 3: mini-batch gradient steps of b tokens.
+    The reversed run's outputs are flipped back to token order before the sum.
+    Returns (O, W_fwd_end, W_rev_end).
+    """
+    Q, K, V = _bhnd(q), _bhnd(k), _bhnd(v)
+    B, H, N, _ = Q.shape
+    _check_chunk(N, chunk)
+    W0 = _state(w0, B, H)
+    Of, Wf = _scan_noncausal(Q, K, V, W0, eta, chunk)
+    rev = slice(None, None, -1)
+    Or, Wr = _scan_noncausal(Q[:, :, rev], K[:, :, rev], V[:, :, rev], W0, eta, chunk)
+    return _bnhd(Of + Or[:, :, rev]), Wf, Wr
+
+
+# --------------------------------------------------------------------------------------------
+# Variant (c): causal mini-batch TTT-Linear and TTT-MLP
+# --------------------------------------------------------------------------------------------
+def chunked_causal(q, k, v, w0, eta: float, chunk: int):
+    """TTT-Linear (TTT-Linear/TTT-MLP abstract: the hidden state is a linear model
+    updated by a self-supervised step) with causal mini-batches of b tokens.
+
+    Inside a chunk every gradient is taken at the chunk's start state W_s; token i
+    is read out with W_s - (eta/b) * sum_{j <= i} grad l_j(W_s) (its own gradient
+    included), and the chunk hands W_s - (eta/b) * sum_{all j} grad l_j(W_s) on.
+    Returns (O, W_end).
+    """
+    Q, K, V = _bhnd(q), _bhnd(k), _bhnd(v)
+    B, H, N, D = Q.shape
+    _check_chunk(N, chunk)
+    a = eta / chunk
+    W = _state(w0, B, H)
+    O = np.empty_like(Q)
+    for c0 in range(0, N, chunk):
+        Ws = W
+        S = np.zeros_like(Ws)
+        for i in range(c0, c0 + chunk):
+            ki, vi, qi = K[:, :, i:i + 1], V[:, :, i:i + 1], Q[:, :, i:i + 1]
+            S = S + _t(ki) @ (ki @ Ws - vi)          # grad of 1/2||k_i W - v_i||^2 at W_s
+            O[:, :, i:i + 1] = qi @ (Ws - a * S)     # token i's own weights
+        W = Ws - a * S
+    return _bnhd(O), W
+
+
+def gelu(x):
+    """Exact GELU, x * Phi(x)."""
+    return 0.5 * x * (1.0 + erf(x / _SQRT2))
+
+
+def gelu_prime(x):
+    """d/dx [x Phi(x)] = Phi(x) + x phi(x)."""
+    return 0.5 * (1.0 + erf(x / _SQRT2)) + x * np.exp(-0.5 * x * x) * _INV_SQRT_2PI
+
+
+def mlp_token_grad(k, v, W1, W2):
+    """Hand-derived gradient of l = 1/2 ||GELU(k W1) W2 - v||^2 for one token per (b, h).
+
+    k, v: [..., 1, D]; W1: [..., D, Dh]; W2: [..., Dh, D]. Returns (dl/dW1, dl/dW2).
+    """
+    z = k @ W1
+    x = gelu(z)
+    e = x @ W2 - v
+    g2 = _t(x) @ e
+    dz = (e @ _t(W2)) * gelu_prime(z)
+    g1 = _t(k) @ dz
+    return g1, g2
+
+
+def mlp_causal(q, k, v, w1, w2, eta: float, chunk: int):
+    """TTT-MLP (TTT-Linear/TTT-MLP abstract: the hidden state is a two-layer MLP)
+    with causal mini-batches of b tokens; f(x) = GELU(x W1) W2, no bias.
+
+    Token i is read out with (W1_s - (eta/b) A1_i, W2_s - (eta/b) A2_i), where
+    A*_i sums the per-token gradients of tokens j <= i in the chunk, each taken at
+    the chunk's start state (W1_s, W2_s). Returns (O, W1_end, W2_end).
+    """
+    Q, K, V = _bhnd(q), _bhnd(k), _bhnd(v)
+    B, H, N, D = Q.shape
+    _check_chunk(N, chunk)
+    a = eta / chunk
+    W1 = _state(w1, B, H)
+    W2 = _state(w2, B, H)
+    O = np.empty_like(Q)
+    for c0 in range(0, N, chunk):
+        W1s, W2s = W1, W2
+        A1 = np.zeros_like(W1s)
+        A2 = np.zeros_like(W2s)
+        for i in range(c0, c0 + chunk):
+            ki, vi, qi = K[:, :, i:i + 1], V[:, :, i:i + 1], Q[:, :, i:i + 1]
+            g1, g2 = mlp_token_grad(ki, vi, W1s, W2s)
+            A1 = A1 + g1
+            A2 = A2 + g2
+            O[:, :, i:i + 1] = gelu(qi @ (W1s - a * A1)) @ (W2s - a * A2)
+        W1 = W1s - a * A1
+        W2 = W2s - a * A2
+    return _bnhd(O), W1, W2
+
+
+def run(inputs, w_override=None):
+    """Run the oracle on a synth.Inputs object; returns the output [B,N,H,D] float64.
+
+    w_override replaces the initial state(s): a [B,H,..] array for TTT-Linear or
+    a (W1, W2) pair for TTT-MLP.
+    """
+    wl = inputs.wl
+    q, k, v = inputs.q64, inputs.k64, inputs.v64
+    if wl.op == "fullbatch":
+        return fullbatch(q, k, v, inputs.w0 if w_override is None else w_override, wl.eta)[0]
+    if wl.op == "bidir":
+        return chunked_bidir(q, k, v, inputs.w0 if w_override is None else w_override, wl.eta, wl.chunk)[0]
+    if wl.op == "causal":
+        return chunked_causal(q, k, v, inputs.w0 if w_override is None else w_override, wl.eta, wl.chunk)[0]
+    if wl.op == "mlp":
+        w1, w2 = (inputs.w1, inputs.w2) if w_override is None else w_override
+        return mlp_causal(q, k, v, w1, w2, wl.eta, wl.chunk)[0]
+    raise ValueError(wl.op)
