@@ -1,0 +1,288 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle, element by element.
+
+Metric (per (batch, head) slice): max |gpu - oracle| / max |oracle|, worst slice reported.
+Bars: 1e-2 for bf16 I/O with fp32 accumulation, 1e-4 for fp32 I/O.
+Full-size workloads are compared in full where the oracle is fast (full-batch, bidirectional,
+causal TTT-Linear), and on sampled (batch, head) slices for TTT-MLP (heads are independent, so
+a slice of the inputs gives exactly that slice of the outputs).
+"""
+import numpy as np
+import pytest
+
+from oracle import ttt_oracle as O
+from test_sequence_layers_amd import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+BF16_TOL = 1e-2
+F32_TOL = 1e-4
+
+
+def T():
+    import test_sequence_layers_amd as lib
+
+    return lib
+
+
+def dev(a, dtype):
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def slice_err(got, ref):
+    """Worst per-(b, h) normalised max error; inputs [B, N, H, D]."""
+    num = np.abs(got - ref).max(axis=(1, 3))
+    den = np.abs(ref).max(axis=(1, 3))
+    return float((num / np.maximum(den, 1e-30)).max())
+
+
+def run_gpu(x, w0=None, w1=None, w2=None, want_state=False, q_is_k=False):
+    """Run the workload of synth.Inputs x on the GPU; returns (out, states...)."""
+    lib = T()
+    wl = x.wl
+    q, k, v = dev(x.q, wl.dtype), dev(x.k, wl.dtype), dev(x.v, wl.dtype)
+    if q_is_k:
+        q = k
+    B, H, D = wl.B, wl.H, wl.D
+    if wl.op == "mlp":
+        W1 = torch.from_numpy(np.ascontiguousarray(x.w1 if w1 is None else w1)).cuda()
+        W2 = torch.from_numpy(np.ascontiguousarray(x.w2 if w2 is None else w2)).cuda()
+        s1 = torch.full((B, H, D, wl.Dh), float("nan"), device="cuda") if want_state else None
+        s2 = torch.full((B, H, wl.Dh, D), float("nan"), device="cuda") if want_state else None
+        out = lib.ttt_mlp_forward(q, k, v, W1, W2, wl.chunk, wl.eta, w1_out=s1, w2_out=s2)
+        torch.cuda.synchronize()
+        return (host(out), s1.cpu().numpy() if want_state else None, s2.cpu().numpy() if want_state else None)
+    W0 = torch.from_numpy(np.ascontiguousarray(x.w0 if w0 is None else w0)).cuda()
+    nst = 2 if wl.op == "bidir" else 1
+    so = torch.full((nst, B, H, D, D), float("nan"), device="cuda") if want_state else None
+    so_arg = so if (so is None or nst == 2) else so[0]
+    if wl.op == "fullbatch":
+        out = lib.ttt_forward_fullbatch(q, k, v, W0, wl.eta, w_out=so_arg)
+    elif wl.op == "causal":
+        out = lib.ttt_forward_chunked_causal(q, k, v, W0, wl.chunk, wl.eta, w_out=so_arg)
+    else:
+        out = lib.ttt_forward_chunked_bidir(q, k, v, W0, wl.chunk, wl.eta, w_out=so_arg)
+    torch.cuda.synchronize()
+    return host(out), (so.cpu().numpy() if want_state else None)
+
+
+def oracle_full(x, w0=None, q_is_k=False):
+    wl = x.wl
+    q = x.k64 if q_is_k else x.q64
+    w0 = x.w0 if w0 is None else w0
+    if wl.op == "fullbatch":
+        return O.fullbatch(q, x.k64, x.v64, w0, wl.eta)
+    if wl.op == "causal":
+        return O.chunked_causal(q, x.k64, x.v64, w0, wl.eta, wl.chunk)
+    if wl.op == "bidir":
+        return O.chunked_bidir(q, x.k64, x.v64, w0, wl.eta, wl.chunk)
+    return O.mlp_causal(q, x.k64, x.v64, x.w1, x.w2, wl.eta, wl.chunk)
+
+
+def tol(wl):
+    return F32_TOL if wl.dtype == "fp32" else BF16_TOL
+
+
+W = synth.WORKLOADS
+
+# Small cases: several tiles, ragged tails (full-batch), every supported D / chunk.
+SMALL = [
+    W["fullbatch_tiny_fp32"],
+    W["fullbatch_tiny_fp32"].with_(B=2, N=100, H=3, D=64, seed=21),
+    W["fullbatch_tiny_fp32"].with_(B=1, N=333, H=2, D=32, seed=22),
+    W["hvit3t_stage1_fullbatch"].with_(B=2, N=200, seed=23),
+    W["hvit3t_stage1_fullbatch"].with_(B=3, N=1000, H=2, D=16, seed=24),
+    W["vit3s_fullbatch"].with_(B=2, N=197, seed=25),
+    W["vit3s_fullbatch"].with_(B=1, N=1, seed=26),
+    W["vittt_bidir_1280"].with_(B=2, N=512, seed=31),
+    W["vittt_bidir_1280"].with_(B=1, N=256, H=2, D=32, chunk=16, seed=32),
+    W["vittt_bidir_1280"].with_(B=1, N=192, H=2, D=16, chunk=32, seed=33),
+    W["vittt_bidir_1280"].with_(B=1, N=64, H=1, seed=34),
+    W["vittt_bidir_1280"].with_(B=1, N=128, H=2, D=64, chunk=16, dtype="fp32", seed=35),
+    W["ttt_linear_causal_16k"].with_(B=1, N=256, H=2, seed=41),
+    W["ttt_linear_causal_16k"].with_(B=2, N=192, H=1, chunk=64, seed=42),
+    W["ttt_linear_causal_16k"].with_(B=1, N=128, H=3, D=32, chunk=32, seed=43),
+    W["ttt_linear_causal_16k"].with_(B=1, N=64, H=2, D=16, chunk=16, seed=44),
+    W["ttt_linear_causal_16k"].with_(B=1, N=128, H=2, D=32, chunk=16, dtype="fp32", seed=45),
+    W["ttt_mlp_causal_8k"].with_(B=1, N=128, H=2, seed=51),
+    W["ttt_mlp_causal_8k"].with_(B=2, N=16, H=1, seed=52),
+]
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=lambda w: f"{w.op}-{w.dtype}-B{w.B}N{w.N}H{w.H}D{w.D}c{w.chunk}")
+def test_small_parity(wl):
+    x = synth.make_inputs(wl)
+    got = run_gpu(x)[0]
+    ref = oracle_full(x)[0]
+    err = slice_err(got, ref)
+    print(f"{wl.name} {wl.op} err={err:.3e}")
+    assert err <= tol(wl)
+
+
+@pytest.mark.parametrize("name", ["vit3s_fullbatch", "hvit3t_stage1_fullbatch", "fullbatch_16k",
+                                  "vittt_bidir_1280", "ttt_linear_causal_16k"])
+def test_full_size_parity(name):
+    wl = W[name]
+    x = synth.make_inputs(wl)
+    got = run_gpu(x)[0]
+    ref = oracle_full(x)[0]
+    err = slice_err(got, ref)
+    print(f"{name} err={err:.3e}")
+    assert err <= BF16_TOL
+
+
+@pytest.mark.parametrize("name,heads", [("ttt_mlp_causal_8k", [(0, 0), (3, 11)]),
+                                        ("ttt_mlp_causal_16k", [(1, 5)])])
+def test_full_size_mlp_sampled_heads(name, heads):
+    wl = W[name]
+    x = synth.make_inputs(wl)
+    got = run_gpu(x)[0]
+    for b, h in heads:
+        ref = O.mlp_causal(x.q64[b:b + 1, :, h:h + 1], x.k64[b:b + 1, :, h:h + 1], x.v64[b:b + 1, :, h:h + 1],
+                           x.w1[h:h + 1], x.w2[h:h + 1], wl.eta, wl.chunk)[0]
+        err = slice_err(got[b:b + 1, :, h:h + 1], ref)
+        print(f"{name} (b={b}, h={h}) err={err:.3e}")
+        assert err <= BF16_TOL
+
+
+# ------------------------------------------------------------------ states, edge cases, invariants
+@pytest.mark.parametrize("wl", [W["hvit3t_stage1_fullbatch"].with_(B=2, N=300, seed=61),
+                                W["vittt_bidir_1280"].with_(B=2, N=256, seed=62),
+                                W["ttt_linear_causal_16k"].with_(B=2, N=128, H=2, seed=63)],
+                         ids=lambda w: w.op)
+def test_end_states(wl):
+    x = synth.make_inputs(wl)
+    out, st = run_gpu(x, want_state=True)
+    ref = oracle_full(x)
+    if wl.op == "bidir":
+        for i, wref in enumerate(ref[1:]):
+            assert np.abs(st[i] - wref).max() / np.abs(wref).max() <= BF16_TOL
+    else:
+        assert np.abs(st[0] - ref[1]).max() / np.abs(ref[1]).max() <= BF16_TOL
+
+
+def test_mlp_end_states():
+    wl = W["ttt_mlp_causal_8k"].with_(B=1, N=64, H=2, seed=64)
+    x = synth.make_inputs(wl)
+    _, s1, s2 = run_gpu(x, want_state=True)
+    _, r1, r2 = oracle_full(x)
+    assert np.abs(s1 - r1).max() / np.abs(r1).max() <= BF16_TOL
+    assert np.abs(s2 - r2).max() / np.abs(r2).max() <= BF16_TOL
+
+
+@pytest.mark.parametrize("wl", [W["hvit3t_stage1_fullbatch"].with_(B=2, N=300, seed=71),
+                                W["vittt_bidir_1280"].with_(B=1, N=256, seed=72),
+                                W["ttt_linear_causal_16k"].with_(B=1, N=128, H=2, seed=73)],
+                         ids=lambda w: w.op)
+def test_w0_zero_isolates_update(wl):
+    """W0 = 0: the output is all update path (for full-batch, linear attention)."""
+    x = synth.make_inputs(wl, zero_w=True)
+    got = run_gpu(x)[0]
+    ref = oracle_full(x)[0]
+    assert slice_err(got, ref) <= BF16_TOL
+
+
+@pytest.mark.parametrize("op", ["fullbatch", "bidir", "causal", "mlp"])
+def test_eta_zero_reads_initial_state(op):
+    base = {"fullbatch": W["hvit3t_stage1_fullbatch"].with_(B=1, N=128), "bidir": W["vittt_bidir_1280"].with_(B=1, N=128),
+            "causal": W["ttt_linear_causal_16k"].with_(B=1, N=64, H=2), "mlp": W["ttt_mlp_causal_8k"].with_(B=1, N=32, H=2)}[op]
+    wl = base.with_(eta=0.0, seed=80)
+    x = synth.make_inputs(wl)
+    got = run_gpu(x)[0]
+    ref = oracle_full(x)[0]
+    assert slice_err(got, ref) <= BF16_TOL
+
+
+@pytest.mark.parametrize("wl", [W["hvit3t_stage1_fullbatch"].with_(B=3, N=130, seed=81),
+                                W["vittt_bidir_1280"].with_(B=2, N=128, seed=82),
+                                W["ttt_linear_causal_16k"].with_(B=3, N=64, H=2, seed=83)],
+                         ids=lambda w: w.op)
+def test_per_batch_initial_state(wl):
+    x = synth.make_inputs(wl)
+    rs = np.random.default_rng(5)
+    w0b = (rs.standard_normal((wl.B, wl.H, wl.D, wl.D)) * 0.05).astype(np.float32)
+    got = run_gpu(x, w0=w0b)[0]
+    ref = oracle_full(x, w0=w0b)[0]
+    assert slice_err(got, ref) <= BF16_TOL
+
+
+@pytest.mark.parametrize("wl", [W["hvit3t_stage1_fullbatch"].with_(B=1, N=256, seed=84),
+                                W["vittt_bidir_1280"].with_(B=1, N=128, seed=85),
+                                W["ttt_linear_causal_16k"].with_(B=1, N=64, H=2, seed=86)],
+                         ids=lambda w: w.op)
+def test_shared_qk_projection(wl):
+    """q and k may be the same buffer (Vision-TTT shares its Q/K projection)."""
+    x = synth.make_inputs(wl)
+    got = run_gpu(x, q_is_k=True)[0]
+    ref = oracle_full(x, q_is_k=True)[0]
+    assert slice_err(got, ref) <= BF16_TOL
+
+
+def test_causal_resume_from_state_equals_one_call():
+    wl = W["ttt_linear_causal_16k"].with_(B=2, N=256, H=2, seed=87)
+    x = synth.make_inputs(wl)
+    full, st = run_gpu(x, want_state=True)
+    h = wl.N // 2
+    xa = synth.Inputs(wl.with_(N=h), x.q[:, :h], x.k[:, :h], x.v[:, :h], w0=x.w0)
+    xb = synth.Inputs(wl.with_(N=h), x.q[:, h:], x.k[:, h:], x.v[:, h:], w0=x.w0)
+    oa, sa = run_gpu(xa, want_state=True)
+    ob, sb = run_gpu(xb, w0=sa[0], want_state=True)
+    both = np.concatenate([oa, ob], axis=1)
+    assert slice_err(both, full) <= 1e-3
+    assert np.abs(sb[0] - st[0]).max() / np.abs(st[0]).max() <= 1e-3
+
+
+@pytest.mark.parametrize("wl", [W["hvit3t_stage1_fullbatch"].with_(B=4, N=1000, seed=91),
+                                W["vittt_bidir_1280"].with_(B=2, N=512, seed=92),
+                                W["ttt_linear_causal_16k"].with_(B=1, N=512, H=4, seed=93),
+                                W["ttt_mlp_causal_8k"].with_(B=1, N=64, H=2, seed=94)],
+                         ids=lambda w: w.op)
+def test_deterministic(wl):
+    """Fixed-order reductions only (no float atomics): two runs are bit-identical."""
+    x = synth.make_inputs(wl)
+    a = run_gpu(x)[0]
+    b = run_gpu(x)[0]
+    assert np.array_equal(a, b)
+
+
+def test_invalid_arguments_leave_output_untouched():
+    lib = T()
+    q = torch.randn(1, 64, 1, 48, device="cuda").to(torch.bfloat16)
+    w0 = torch.zeros(1, 48, 48, device="cuda")
+    o = torch.full_like(q, 7.0)
+    with pytest.raises(lib.TTTError) as e:
+        lib.ttt_forward_fullbatch(q, q, q, w0, 1.0, o=o)
+    assert e.value.status == 2
+    assert bool((o.float() == 7.0).all())
+    q = torch.randn(1, 100, 1, 64, device="cuda").to(torch.bfloat16)
+    w0 = torch.zeros(1, 64, 64, device="cuda")
+    o = torch.full_like(q, 7.0)
+    with pytest.raises(lib.TTTError) as e:
+        lib.ttt_forward_chunked_causal(q, q, q, w0, 16, 1.0, o=o)
+    assert e.value.status == 1
+    assert bool((o.float() == 7.0).all())
+    ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(lib.TTTError) as e:
+        lib.ttt_forward_fullbatch(q, q, q, w0, 1.0, o=o, workspace=ws)
+    assert e.value.status == 3
+    assert bool((o.float() == 7.0).all())
+
+
+def test_runs_on_a_side_stream():
+    wl = W["ttt_linear_causal_16k"].with_(B=1, N=128, H=2, seed=95)
+    x = synth.make_inputs(wl)
+    lib = T()
+    s = torch.cuda.Stream()
+    q, k, v = dev(x.q, "bf16"), dev(x.k, "bf16"), dev(x.v, "bf16")
+    w0 = torch.from_numpy(x.w0).cuda()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        out = lib.ttt_forward_chunked_causal(q, k, v, w0, wl.chunk, wl.eta)
+    s.synchronize()
+    assert slice_err(host(out), oracle_full(x)[0]) <= BF16_TOL
