@@ -1,0 +1,253 @@
+#!/usr/bin/env python3
+"""Benchmark of the TTT-layer forward on one MI355X; prints ONE JSON line.
+
+One step = one forward of every layer variant of the library, each at its reference shape:
+  * full-batch TTT-Linear, H-ViT^3-T stage 1: B=64, N=3136 (56x56), 2 heads x 32, bf16
+  * bidirectional chunked scan, Vision-TTT at 1280x1280 / 16-px patches: B=8, N=6400, 3 x 64, b=64
+  * causal TTT-Linear language layer: B=2, N=16384, 12 x 64, b=16
+  * causal TTT-MLP language layer: B=4, N=8192, 12 x 64, hidden 256, b=16
+Inputs are synthetic (seeded i.i.d. Gaussians of those shapes) and resident in HBM before the
+timed region. The four layers' inputs (584 MB) exceed the 256 MB Infinity Cache, so every layer
+starts with its inputs evicted by the other three.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+SUITE = ["hvit3t_stage1_fullbatch", "vittt_bidir_1280", "ttt_linear_causal_16k", "ttt_mlp_causal_8k"]
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, TFLOP/s
+KERNEL_SOURCES = {              # kernel source of each layer (for the traffic-counter freshness check)
+    "fullbatch": "test_sequence_layers_amd/csrc/fullbatch.hip",
+    "bidir": "test_sequence_layers_amd/csrc/chunked.hip",
+    "causal": "test_sequence_layers_amd/csrc/chunked.hip",
+    "mlp": "test_sequence_layers_amd/csrc/mlp.hip",
+}
+
+
+def alg_flops(wl) -> float:
+    """Algorithmic flops of one layer forward (per token and head: full-batch 6d^2, bidirectional
+    12d^2, causal TTT-Linear 6d^2 + 4bd, TTT-MLP 14 d Dh + 4b(d + Dh))."""
+    d, b = wl.D, wl.chunk
+    per = {"fullbatch": 6 * d * d, "bidir": 12 * d * d, "causal": 6 * d * d + 4 * b * d,
+           "mlp": 14 * d * wl.Dh + 4 * b * (d + wl.Dh)}[wl.op]
+    return float(per) * wl.tokens * wl.H
+
+
+def source_hash(op: str) -> str:
+    with open(os.path.join(ROOT, KERNEL_SOURCES[op]), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def load_traffic(op: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it is still current."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{op}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256") != source_hash(op):
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def to_device(x, torch):
+    import numpy as np
+
+    def cv(a):
+        if x.wl.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    d = {"q": cv(x.q), "k": cv(x.k), "v": cv(x.v)}
+    if x.wl.op == "mlp":
+        d["w1"] = torch.from_numpy(x.w1).cuda()
+        d["w2"] = torch.from_numpy(x.w2).cuda()
+    else:
+        d["w0"] = torch.from_numpy(x.w0).cuda()
+    d["o"] = torch.empty_like(d["q"])
+    return d
+
+
+def make_call(T, wl, d, torch):
+    op = {"fullbatch": T.TTT_OP_FULLBATCH, "causal": T.TTT_OP_CAUSAL, "bidir": T.TTT_OP_BIDIR,
+          "mlp": T.TTT_OP_MLP}[wl.op]
+    need = T.ttt_workspace_size(op, T.TTT_BF16, wl.B, wl.H, wl.N, wl.D, wl.Dh, wl.chunk)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    if wl.op == "fullbatch":
+        return lambda: T.ttt_forward_fullbatch(d["q"], d["k"], d["v"], d["w0"], wl.eta, o=d["o"], workspace=ws)
+    if wl.op == "causal":
+        return lambda: T.ttt_forward_chunked_causal(d["q"], d["k"], d["v"], d["w0"], wl.chunk, wl.eta, o=d["o"],
+                                                    workspace=ws)
+    if wl.op == "bidir":
+        return lambda: T.ttt_forward_chunked_bidir(d["q"], d["k"], d["v"], d["w0"], wl.chunk, wl.eta, o=d["o"],
+                                                   workspace=ws)
+    return lambda: T.ttt_mlp_forward(d["q"], d["k"], d["v"], d["w1"], d["w2"], wl.chunk, wl.eta, o=d["o"],
+                                     workspace=ws)
+
+
+def cpu_baseline(inputs) -> dict:
+    """The fp64 oracle, single-threaded, on a bounded sample of every layer (a subset of the
+    independent (batch, head) pairs), scaled to the whole suite step."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import ttt_oracle as O
+
+    samples = {"hvit3t_stage1_fullbatch": (64, 2), "vittt_bidir_1280": (8, 3), "ttt_linear_causal_16k": (1, 12),
+               "ttt_mlp_causal_8k": (1, 4)}  # (batches, heads) of each layer that the oracle runs
+    total_s = 0.0
+    desc = []
+    with threadpool_limits(limits=1):
+        for name in SUITE:
+            x = inputs[name]
+            wl = x.wl
+            nb, nh = samples[name]
+            sl = (slice(0, nb), slice(None), slice(0, nh))
+            q, k, v = x.q64[sl], x.k64[sl], x.v64[sl]
+            t0 = time.perf_counter()
+            if wl.op == "fullbatch":
+                O.fullbatch(q, k, v, x.w0[:nh], wl.eta)
+            elif wl.op == "bidir":
+                O.chunked_bidir(q, k, v, x.w0[:nh], wl.eta, wl.chunk)
+            elif wl.op == "causal":
+                O.chunked_causal(q, k, v, x.w0[:nh], wl.eta, wl.chunk)
+            else:
+                O.mlp_causal(q, k, v, x.w1[:nh], x.w2[:nh], wl.eta, wl.chunk)
+            dt = time.perf_counter() - t0
+            scale = (wl.B * wl.H) / (nb * nh)
+            total_s += dt * scale
+            desc.append(f"{name}: {nb}x{nh} of {wl.B}x{wl.H} (batch x head) pairs in {dt:.2f} s")
+    tokens = sum(inputs[n].wl.tokens for n in SUITE)
+    return {"value": tokens / total_s, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": "fp64 numpy oracle, one thread; " + "; ".join(desc) +
+                      "; each layer's time scaled by its (batch, head) count"}
+
+
+def copy_calibration(torch, reps: int = 5) -> None:
+    """A plain copy of known size, for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings."""
+    n = 1 << 28  # 256 Mi floats = 1 GiB each way
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "reps": reps}))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layers", default=",".join(SUITE), help="comma-separated subset of the suite (profiling)")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); every (batch, head) "
+              "pair is independent, so N GPUs would each run this step on their own shard.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import test_sequence_layers_amd as T
+    from test_sequence_layers_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    T.load_library()  # fails loudly when the HIP library is missing
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return 0
+
+    layers = [n for n in args.layers.split(",") if n]
+    inputs = {n: synth.make_inputs(synth.WORKLOADS[n]) for n in layers}
+    dev = {n: to_device(inputs[n], torch) for n in layers}
+    calls = {n: make_call(T, inputs[n].wl, dev[n], torch) for n in layers}
+    stream = torch.cuda.current_stream()
+
+    def step(events=None):
+        for n in layers:
+            if events is not None:
+                events[n][0].record(stream)
+            calls[n]()
+            if events is not None:
+                events[n][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in layers}
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    layer_ms = {n: sum(e[n][0].elapsed_time(e[n][1]) for e in evs) / args.steps for n in layers}
+    ms_per_step = elapsed * 1000.0 / args.steps
+    tokens = sum(inputs[n].wl.tokens for n in layers)
+    per_layer = {}
+    for n in layers:
+        wl = inputs[n].wl
+        s = layer_ms[n] / 1000.0
+        per_layer[n] = {
+            "op": wl.op, "B": wl.B, "N": wl.N, "H": wl.H, "D": wl.D, "chunk": wl.chunk, "Dh": wl.Dh,
+            "ms": round(layer_ms[n], 5), "tokens_per_s": wl.tokens / s,
+            "alg_GBs": wl.io_bytes / s / 1e9, "hbm_frac": wl.io_bytes / s / 1e9 / PEAK_HBM_GBS,
+            "alg_TFLOPs": alg_flops(wl) / s / 1e12, "mfma_frac": alg_flops(wl) / s / 1e12 / PEAK_BF16_TFLOPS,
+        }
+    dom = max(layers, key=lambda n: layer_ms[n])
+    wl = inputs[dom].wl
+    s = layer_ms[dom] / 1000.0
+    if wl.op == "mlp":
+        ach = alg_flops(wl) / s / 1e12
+        roof = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": ach / PEAK_BF16_TFLOPS}
+    else:
+        ach = wl.io_bytes / s / 1e9
+        roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS}
+    roof["traffic"] = load_traffic(wl.op)
+    roof["kernel_layer"] = dom
+
+    out = {
+        "metric": "TTT-layer fwd tokens/sec at N=3136/6400/16384; % of HBM-BW roofline",
+        "value": tokens / (ms_per_step / 1000.0),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "ttt_layer_suite", "layers": layers, "tokens_per_step": tokens,
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "per_layer": per_layer,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inputs)
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
