@@ -10,29 +10,60 @@
 // update by a forward scan and by a scan of the reversed sequence from the same W0; the two are
 // summed: O_c = Q_c (W^f_c + W^r_c), where W^r_c is the reverse scan's state after chunk c.
 //
-// The d output columns of W are independent regressions (column j of the update only involves
-// column j of W and V), so wave w of a workgroup owns columns [16w, 16w + 16) of the state and
-// keeps them in MFMA accumulator layout for the whole scan; no state ever leaves registers
-// between chunks. K, V, Q of one chunk are staged through LDS.
+// Parallel structure. The chunk step is affine in the state: W -> A_c W + B_c with
+// A_c = I - a K_c^T K_c and B_c = a K_c^T V_c (a = eta/b). A run of chunks (a "segment") therefore
+// composes to one affine map, and the sequence is processed in three launches:
+//   1. chunk_compose: one workgroup per (segment, b, h) composes its segment's map by scanning
+//      the 2D-column state [P | R] from [I | 0] (columns are independent regressions). It stores
+//      Dev = I - P (the small deviation, which keeps bf16 operands accurate) and R. Every A_c is
+//      symmetric, so the reverse scan's composite of the segment is Dev^T; its offset
+//      R_rev = a sum_c (K_c P_{c-1})^T V_c is accumulated alongside.
+//   2. chunk_prefix: one workgroup per (b, h, direction) folds the segment maps in order from W0
+//      and stores every segment's entry state (W <- W - Dev W + R per segment).
+//   3. chunk_scan: one workgroup per (segment, b, h) rescans its segment from its true entry
+//      state and writes the outputs. For the bidirectional scan it first runs the reverse scan
+//      over its chunks, keeping each W^r_c (bf16) in LDS, then the forward scan with the read-out.
+// A single segment (short sequences) skips launches 1 and 2.
+//
+// Inside every kernel, wave w owns columns [16w, 16w + 16) of its state (the columns of W are
+// independent regressions), held in MFMA accumulator layout; the chunk's K, V, Q are staged
+// through LDS with the next chunk prefetched into registers.
 #include "device.hpp"
 #include "internal.hpp"
 
 namespace ttt {
 namespace {
 
-enum ScanMode { kCausal = 0, kReverseStore = 1, kForwardBoth = 2 };
+enum ScanMode { kCausal = 0, kBidir = 1 };
 
-// Stage a [CH x D] bf16 tile (token stride ts) into LDS with row pitch P.
-template <int D, int CH, int P, int NTH>
-__device__ __forceinline__ void stage_chunk(bf16* dst, const bf16* src, long long ts) {
-  constexpr int CPR = D / 8;
-  for (int c = threadIdx.x; c < CH * CPR; c += NTH) {
-    const int row = c / CPR, col = (c % CPR) * 8;
-    st16(dst + row * P + col, ld16(src + row * ts + col));
+// LDS bytes available for the reverse states of one bidirectional scan segment.
+constexpr int kRevLdsBytes = 96 * 1024;
+template <int D>
+constexpr int max_seg_len() { return kRevLdsBytes / (D * D * 2); }
+
+// ---------------------------------------------------------------- staging with prefetch
+// A [CH x D] bf16 tile (token stride ts) moves HBM -> registers (prefetch) -> LDS (row pitch P).
+template <int D, int CH, int NTH>
+struct TileRegs {
+  static constexpr int CPR = D / 8;                    // 16-byte pieces per row
+  static constexpr int PIECES = CH * CPR;
+  static constexpr int PER = (PIECES + NTH - 1) / NTH;  // pieces per thread
+  uint4 v[PER];
+  __device__ __forceinline__ void load(const bf16* src, long long ts) {
+    for (int i = 0; i < PER; ++i) {
+      const int c = threadIdx.x + i * NTH;
+      if (PIECES % NTH == 0 || c < PIECES) v[i] = ld16(src + (c / CPR) * ts + (c % CPR) * 8);
+    }
   }
-}
+  template <int P>
+  __device__ __forceinline__ void store(bf16* dst) const {
+    for (int i = 0; i < PER; ++i) {
+      const int c = threadIdx.x + i * NTH;
+      if (PIECES % NTH == 0 || c < PIECES) st16(dst + (c / CPR) * P + (c % CPR) * 8, v[i]);
+    }
+  }
+};
 
-// Write a [CH x D] bf16 tile from LDS to global memory.
 template <int D, int CH, int P, int NTH>
 __device__ __forceinline__ void store_chunk(bf16* dst, const bf16* src, long long ts) {
   constexpr int CPR = D / 8;
@@ -42,75 +73,254 @@ __device__ __forceinline__ void store_chunk(bf16* dst, const bf16* src, long lon
   }
 }
 
-// A operand: 16 rows of a row-major LDS tile (pitch P) starting at `row0`, features
-// [32ks, 32ks + 32) in the c-layout k map (matching a state held in C layout).
-template <int P>
-__device__ __forceinline__ bf16x8 a_rows_clayout(const bf16* t, int row0, int ks, int r, int g) {
-  const bf16* p = t + (row0 + r) * P + 32 * ks + 4 * g;
-  return cat8(ld4(p), ld4(p + 16));
-}
-
+// ---------------------------------------------------------------- MFMA building blocks
 // B operand from a state held in C layout (tiles m = 2ks, 2ks + 1 cover features 32ks..32ks+31).
 __device__ __forceinline__ bf16x8 b_state(const f32x4* W, int ks) {
   return cat8(to_bf16x4(W[2 * ks]), to_bf16x4(W[2 * ks + 1]));
 }
 
-// Y[16 tokens x 16 cols] = X_rows(row0..row0+15) . W[:, cols] + init, contraction over D.
+// Y[16 rows x 16 cols] = X_rows(row0..row0+15) . W[:, cols] + init, contraction over D; the A
+// operand reads X rows from LDS in the c-layout k map that matches W's accumulator layout.
 template <int D, int P>
 __device__ __forceinline__ f32x4 rows_times_state(const bf16* X, int row0, const f32x4* W,
                                                   f32x4 init, int r, int g) {
   if constexpr (D >= 32) {
-    for (int ks = 0; ks < D / 32; ++ks) init = mma32(a_rows_clayout<P>(X, row0, ks, r, g), b_state(W, ks), init);
+    for (int ks = 0; ks < D / 32; ++ks) {
+      const bf16* p = X + (row0 + r) * P + 32 * ks + 4 * g;
+      init = mma32(cat8(ld4(p), ld4(p + 16)), b_state(W, ks), init);
+    }
   } else {
     init = mma16(ld4(X + (row0 + r) * P + 4 * g), to_bf16x4(W[0]), init);
   }
   return init;
 }
 
+// W[:, cols] += K^T (-a E): A = K^T (row = feature 16m + r, k = token 16p + 4g + j), B = -a E_p.
+template <int D, int NP, int P>
+__device__ __forceinline__ void update_state(f32x4* W, const f32x4* E, const bf16* sK, float a,
+                                             int r, int g) {
+  for (int p = 0; p < NP; ++p) {
+    const bf16x4 eb = to_bf16x4_scaled(E[p], -a);
+    for (int m = 0; m < D / 16; ++m)
+      W[m] = mma16(ld4_col(&sK[(16 * p + 4 * g) * P + 16 * m + r], P), eb, W[m]);
+  }
+}
+
+// E_p = K_p W - V_p[:, 16*vcol ..] for every 16-token tile p (V skipped when vcol < 0).
+template <int D, int NP, int P>
+__device__ __forceinline__ void residuals(f32x4* E, const f32x4* W, const bf16* sK,
+                                          const bf16* sV, int vcol, int r, int g) {
+  for (int p = 0; p < NP; ++p) {
+    f32x4 init = zero4();
+    if (vcol >= 0)
+      for (int j = 0; j < 4; ++j) init[j] = -(float)sV[(16 * p + 4 * g + j) * P + 16 * vcol + r];
+    E[p] = rows_times_state<D, P>(sK, 16 * p, W, init, r, g);
+  }
+}
+
+// ---------------------------------------------------------------- 1. compose
+template <int D, int CH, bool BIDIR>
+__global__ __launch_bounds__(D / 8 * 64) void chunk_compose_bf16(
+    const bf16* __restrict__ k, const bf16* __restrict__ v, int H, int N, float a, int S, int L,
+    float* __restrict__ comp) {
+  constexpr int P = D + 8, NT = D / 16, NP = CH / 16, NTH = 2 * NT * 64;
+  constexpr long long DD = (long long)D * D;
+  __shared__ __align__(16) bf16 sK[CH * P];
+  __shared__ __align__(16) bf16 sV[CH * P];
+
+  const int s = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H;
+  const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
+  const bool pwave = w < NT;        // P columns (init I, no V); else R columns (init 0, V)
+  const int col = pwave ? w : w - NT;
+  const int C = N / CH;
+  const int lo = s * L, hi = min(C, lo + L);
+  const long long ts = (long long)H * D;
+  const long long head0 = (long long)b * N * ts + (long long)h * D;
+
+  f32x4 X[NT], RR[NT];
+  for (int m = 0; m < NT; ++m)
+    for (int j = 0; j < 4; ++j) {
+      X[m][j] = (pwave && 16 * m + 4 * g + j == 16 * col + r) ? 1.f : 0.f;
+      RR[m][j] = 0.f;
+    }
+
+  TileRegs<D, CH, NTH> pk, pv;
+  pk.load(k + head0 + (long long)lo * CH * ts, ts);
+  pv.load(v + head0 + (long long)lo * CH * ts, ts);
+  for (int c = lo; c < hi; ++c) {
+    __syncthreads();
+    pk.template store<P>(sK);
+    pv.template store<P>(sV);
+    if (c + 1 < hi) {
+      pk.load(k + head0 + (long long)(c + 1) * CH * ts, ts);
+      pv.load(v + head0 + (long long)(c + 1) * CH * ts, ts);
+    }
+    __syncthreads();
+    f32x4 Y[NP];
+    residuals<D, NP, P>(Y, X, sK, sV, pwave ? -1 : col, r, g);
+    if constexpr (BIDIR) {
+      if (pwave) {  // R_rev[16col + i][16n + .] += a (K_c P_{c-1})^T V_c
+        for (int p = 0; p < NP; ++p) {
+          const bf16x4 ya = to_bf16x4_scaled(Y[p], a);
+          for (int n = 0; n < NT; ++n)
+            RR[n] = mma16(ya, ld4_col(&sV[(16 * p + 4 * g) * P + 16 * n + r], P), RR[n]);
+        }
+      }
+    }
+    update_state<D, NP, P>(X, Y, sK, a, r, g);
+  }
+
+  // comp[(bh * S + s)] holds Dev_f, R_f, [Dev_r, R_r], each D x D row-major.
+  float* out = comp + ((long long)bh * S + s) * (BIDIR ? 4 : 2) * DD;
+  for (int m = 0; m < NT; ++m)
+    for (int j = 0; j < 4; ++j) {
+      const int row = 16 * m + 4 * g + j, cc = 16 * col + r;
+      if (pwave) {
+        const float dev = (row == cc ? 1.f : 0.f) - X[m][j];
+        out[row * D + cc] = dev;
+        if constexpr (BIDIR) out[2 * DD + cc * D + row] = dev;  // Dev_r = Dev_f^T
+      } else {
+        out[DD + row * D + cc] = X[m][j];
+      }
+    }
+  if constexpr (BIDIR) {
+    if (pwave)
+      for (int n = 0; n < NT; ++n)
+        for (int j = 0; j < 4; ++j) out[3 * DD + (16 * col + 4 * g + j) * D + 16 * n + r] = RR[n][j];
+  }
+}
+
+// ---------------------------------------------------------------- 2. prefix over segments
+template <int D, bool BIDIR>
+__global__ __launch_bounds__(D / 16 * 64) void chunk_prefix(const float* __restrict__ w0,
+                                                            long long w0_bstride, int H, int S,
+                                                            const float* __restrict__ comp,
+                                                            float* __restrict__ win) {
+  constexpr int NT = D / 16;
+  constexpr long long DD = (long long)D * D;
+  const int bh = blockIdx.x, dir = blockIdx.y, b = bh / H, h = bh % H;
+  const int BH = gridDim.x;
+  const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
+  const float* W0 = w0 + b * w0_bstride + h * DD;
+  f32x4 W[NT];
+  for (int m = 0; m < NT; ++m)
+    for (int j = 0; j < 4; ++j) W[m][j] = W0[(16 * m + 4 * g + j) * D + 16 * w + r];
+  const int nc = BIDIR ? 4 : 2;
+  float* dst_base = win + ((long long)dir * BH + bh) * S * DD;
+  for (int i = 0; i < S; ++i) {
+    const int s = dir == 0 ? i : S - 1 - i;
+    float* dst = dst_base + s * DD;
+    for (int m = 0; m < NT; ++m)
+      for (int j = 0; j < 4; ++j) dst[(16 * m + 4 * g + j) * D + 16 * w + r] = W[m][j];
+    if (i == S - 1) break;
+    const float* cp = comp + ((long long)bh * S + s) * nc * DD + (dir == 0 ? 0 : 2 * DD);
+    const float* Dev = cp;
+    const float* R = cp + DD;
+    f32x4 acc[NT];
+    for (int m = 0; m < NT; ++m)
+      for (int j = 0; j < 4; ++j) acc[m][j] = W[m][j] + R[(16 * m + 4 * g + j) * D + 16 * w + r];
+    for (int m = 0; m < NT; ++m) {
+      if constexpr (D >= 32) {
+        for (int ks = 0; ks < D / 32; ++ks) {
+          const float* dp = Dev + (16 * m + r) * D + 32 * ks + 4 * g;
+          const float4 lo4 = *reinterpret_cast<const float4*>(dp);
+          const float4 hi4 = *reinterpret_cast<const float4*>(dp + 16);
+          const bf16x8 av = cat8(to_bf16x4(f32x4{-lo4.x, -lo4.y, -lo4.z, -lo4.w}),
+                                 to_bf16x4(f32x4{-hi4.x, -hi4.y, -hi4.z, -hi4.w}));
+          acc[m] = mma32(av, b_state(W, ks), acc[m]);
+        }
+      } else {
+        const float4 d4 = *reinterpret_cast<const float4*>(Dev + (16 * m + r) * D + 4 * g);
+        acc[m] = mma16(to_bf16x4(f32x4{-d4.x, -d4.y, -d4.z, -d4.w}), to_bf16x4(W[0]), acc[m]);
+      }
+    }
+    for (int m = 0; m < NT; ++m) W[m] = acc[m];
+  }
+}
+
+// ---------------------------------------------------------------- 3. segment scan
 template <int D, int CH, int MODE>
 __global__ __launch_bounds__(D / 16 * 64) void chunk_scan_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const float* __restrict__ w0, long long w0_bstride, int H, int N, float a,
-    float* __restrict__ states, bf16* __restrict__ o, float* __restrict__ w_out) {
+    const float* __restrict__ w0, long long w0_bstride, int H, int N, float a, int S, int L,
+    const float* __restrict__ win, bf16* __restrict__ o, float* __restrict__ w_out) {
   constexpr int P = D + 8;
   constexpr int NT = D / 16;   // waves = column tiles = row tiles
   constexpr int NP = CH / 16;  // 16-token tiles per chunk
   constexpr int NTH = NT * 64;
+  constexpr long long DD = (long long)D * D;
+  constexpr int LMAX = MODE == kBidir ? max_seg_len<D>() : 1;
   __shared__ __align__(16) bf16 sK[CH * P];
   __shared__ __align__(16) bf16 sV[CH * P];
   __shared__ __align__(16) bf16 sQ[CH * P];
   __shared__ __align__(16) bf16 sO[CH * P];
+  __shared__ __align__(16) bf16x4 sWr[MODE == kBidir ? LMAX * NT * NT * 64 : 1];
 
-  const int bh = blockIdx.x, b = bh / H, h = bh % H;
+  const int s = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H;
+  const int BH = gridDim.y;
   const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
   const int C = N / CH;
+  const int lo = s * L, hi = min(C, lo + L);
   const long long ts = (long long)H * D;
-  const long long dd = (long long)D * D;
-  const float* W0 = w0 + b * w0_bstride + h * dd;
-
-  f32x4 W[NT];  // W[16m + 4g + j][16w + r]
-  for (int m = 0; m < NT; ++m)
-    for (int j = 0; j < 4; ++j) W[m][j] = W0[(16 * m + 4 * g + j) * D + 16 * w + r];
-
   const long long head0 = (long long)b * N * ts + (long long)h * D;
-  float* st_bh = states ? states + bh * (long long)C * dd : nullptr;
 
-  for (int it = 0; it < C; ++it) {
-    const int c = (MODE == kReverseStore) ? C - 1 - it : it;
+  // Entry state of this segment (C layout): W0 for a single segment, else from the prefix pass.
+  auto entry = [&](int dir, f32x4* W) {
+    const float* src = S == 1 ? w0 + b * w0_bstride + h * DD
+                              : win + (((long long)dir * BH + bh) * S + s) * DD;
+    for (int m = 0; m < NT; ++m)
+      for (int j = 0; j < 4; ++j) W[m][j] = src[(16 * m + 4 * g + j) * D + 16 * w + r];
+  };
+  auto save = [&](float* dst, const f32x4* W) {
+    for (int m = 0; m < NT; ++m)
+      for (int j = 0; j < 4; ++j) dst[(16 * m + 4 * g + j) * D + 16 * w + r] = W[m][j];
+  };
+
+  f32x4 W[NT];
+  TileRegs<D, CH, NTH> pk, pv, pq;
+
+  if constexpr (MODE == kBidir) {
+    // Reverse scan over the segment's chunks (last to first), keeping each W^r_c in LDS.
+    entry(1, W);
+    pk.load(k + head0 + (long long)(hi - 1) * CH * ts, ts);
+    pv.load(v + head0 + (long long)(hi - 1) * CH * ts, ts);
+    for (int c = hi - 1; c >= lo; --c) {
+      __syncthreads();
+      pk.template store<P>(sK);
+      pv.template store<P>(sV);
+      if (c - 1 >= lo) {
+        pk.load(k + head0 + (long long)(c - 1) * CH * ts, ts);
+        pv.load(v + head0 + (long long)(c - 1) * CH * ts, ts);
+      }
+      __syncthreads();
+      f32x4 E[NP];
+      residuals<D, NP, P>(E, W, sK, sV, w, r, g);
+      update_state<D, NP, P>(W, E, sK, a, r, g);
+      for (int m = 0; m < NT; ++m) sWr[(((c - lo) * NT + w) * NT + m) * 64 + l] = to_bf16x4(W[m]);
+    }
+    if (s == 0 && w_out) save(w_out + (long long)BH * DD + bh * DD, W);
+  }
+
+  // Forward scan over the segment with the read-out.
+  entry(0, W);
+  pk.load(k + head0 + (long long)lo * CH * ts, ts);
+  pv.load(v + head0 + (long long)lo * CH * ts, ts);
+  pq.load(q + head0 + (long long)lo * CH * ts, ts);
+  for (int c = lo; c < hi; ++c) {
     const long long tok0 = head0 + (long long)c * CH * ts;
     __syncthreads();
-    stage_chunk<D, CH, P, NTH>(sK, k + tok0, ts);
-    stage_chunk<D, CH, P, NTH>(sV, v + tok0, ts);
-    if (MODE != kReverseStore) stage_chunk<D, CH, P, NTH>(sQ, q + tok0, ts);
+    pk.template store<P>(sK);
+    pv.template store<P>(sV);
+    pq.template store<P>(sQ);
+    if (c + 1 < hi) {
+      pk.load(k + tok0 + CH * ts, ts);
+      pv.load(v + tok0 + CH * ts, ts);
+      pq.load(q + tok0 + CH * ts, ts);
+    }
     __syncthreads();
 
-    // E_p = K_p W_s - V_p for the wave's 16 columns (C layout: row = token 16p + 4g + j).
     f32x4 E[NP];
-    for (int p = 0; p < NP; ++p) {
-      f32x4 init;
-      for (int j = 0; j < 4; ++j) init[j] = -(float)sV[(16 * p + 4 * g + j) * P + 16 * w + r];
-      E[p] = rows_times_state<D, P>(sK, 16 * p, W, init, r, g);
-    }
+    residuals<D, NP, P>(E, W, sK, sV, w, r, g);
 
     if constexpr (MODE == kCausal) {
       // O_p = Q_p W_s - a * sum_{p' <= p} tril(P_{p p'}) E_{p'},  P = Q K^T.
@@ -134,44 +344,31 @@ __global__ __launch_bounds__(D / 16 * 64) void chunk_scan_bf16(
         }
         for (int j = 0; j < 4; ++j) sO[(16 * p + 4 * g + j) * P + 16 * w + r] = (bf16)acc[j];
       }
-    }
-
-    // W += (-a K^T) E: A = K^T (row = feature 16m + r, k = token 16p + 4g + j), B = -a E_p.
-    for (int p = 0; p < NP; ++p) {
-      const bf16x4 eb = to_bf16x4_scaled(E[p], -a);
-      for (int m = 0; m < NT; ++m)
-        W[m] = mma16(ld4_col(&sK[(16 * p + 4 * g) * P + 16 * m + r], P), eb, W[m]);
-    }
-
-    if constexpr (MODE == kReverseStore) {
-      f32x4* dst = reinterpret_cast<f32x4*>(st_bh + c * dd);
-      for (int m = 0; m < NT; ++m) dst[(w * NT + m) * 64 + l] = W[m];
-    }
-    if constexpr (MODE == kForwardBoth) {
-      const f32x4* src = reinterpret_cast<const f32x4*>(st_bh + c * dd);
+      update_state<D, NP, P>(W, E, sK, a, r, g);
+    } else {
+      update_state<D, NP, P>(W, E, sK, a, r, g);
       f32x4 Ws[NT];
-      for (int m = 0; m < NT; ++m) Ws[m] = W[m] + src[(w * NT + m) * 64 + l];
+      for (int m = 0; m < NT; ++m) {
+        const bf16x4 wr = sWr[(((c - lo) * NT + w) * NT + m) * 64 + l];
+        for (int j = 0; j < 4; ++j) Ws[m][j] = W[m][j] + (float)wr[j];
+      }
       for (int p = 0; p < NP; ++p) {
         const f32x4 acc = rows_times_state<D, P>(sQ, 16 * p, Ws, zero4(), r, g);
         for (int j = 0; j < 4; ++j) sO[(16 * p + 4 * g + j) * P + 16 * w + r] = (bf16)acc[j];
       }
     }
-    if constexpr (MODE != kReverseStore) {
-      __syncthreads();
-      store_chunk<D, CH, P, NTH>(o + tok0, sO, ts);
-    }
+    __syncthreads();
+    store_chunk<D, CH, P, NTH>(o + tok0, sO, ts);
   }
-
-  if (w_out) {
-    float* dst = w_out + (MODE == kReverseStore ? (long long)gridDim.x * dd : 0) + bh * dd;
-    for (int m = 0; m < NT; ++m)
-      for (int j = 0; j < 4; ++j) dst[(16 * m + 4 * g + j) * D + 16 * w + r] = W[m][j];
-  }
+  if (s == S - 1 && w_out) save(w_out + bh * DD, W);
 }
 
 // ---------------------------------------------------------------- fp32 I/O, plain FMA
 // One workgroup per (b, h); the state lives in LDS and tokens are processed one by one in the
-// primal form (weights of each token materialised), in true fp32.
+// primal form (weights of each token materialised), in true fp32. The reverse scan of the
+// bidirectional variant stores its per-chunk states in the workspace.
+enum F32Mode { kF32Causal = 0, kF32ReverseStore = 1, kF32ForwardBoth = 2 };
+
 template <int D, int MODE>
 __global__ __launch_bounds__(256) void chunk_scan_f32(const float* __restrict__ q,
                                                       const float* __restrict__ k,
@@ -192,14 +389,14 @@ __global__ __launch_bounds__(256) void chunk_scan_f32(const float* __restrict__ 
   const long long head0 = (long long)b * N * ts + (long long)h * D;
   float* st_bh = states ? states + bh * (long long)C * dd : nullptr;
   for (int it = 0; it < C; ++it) {
-    const int c = (MODE == kReverseStore) ? C - 1 - it : it;
+    const int c = (MODE == kF32ReverseStore) ? C - 1 - it : it;
     for (int e = tid; e < D * D; e += 256) sS[e / D][e % D] = 0.f;
     __syncthreads();
     for (int i = 0; i < CH; ++i) {
       const long long off = head0 + ((long long)c * CH + i) * ts;
       if (tid < D) {
         sk[tid] = k[off + tid];
-        sq[tid] = (MODE == kReverseStore) ? 0.f : q[off + tid];
+        sq[tid] = (MODE == kF32ReverseStore) ? 0.f : q[off + tid];
       }
       __syncthreads();
       if (tid < D) {  // e = k W_s - v
@@ -213,7 +410,7 @@ __global__ __launch_bounds__(256) void chunk_scan_f32(const float* __restrict__ 
         if (e < D * D) sS[e / D][e % D] = fmaf(sk[e / D], se[e % D], sS[e / D][e % D]);
       }
       __syncthreads();
-      if (MODE == kCausal && tid < D) {  // o_i = q_i (W_s - a S_i)
+      if (MODE == kF32Causal && tid < D) {  // o_i = q_i (W_s - a S_i)
         float acc = 0.f;
         for (int j = 0; j < D; ++j) acc = fmaf(sq[j], fmaf(-a, sS[j][tid], sW[j][tid]), acc);
         o[off + tid] = acc;
@@ -222,9 +419,9 @@ __global__ __launch_bounds__(256) void chunk_scan_f32(const float* __restrict__ 
     }
     for (int e = tid; e < D * D; e += 256) sW[e / D][e % D] = fmaf(-a, sS[e / D][e % D], sW[e / D][e % D]);
     __syncthreads();
-    if (MODE == kReverseStore)
+    if (MODE == kF32ReverseStore)
       for (int e = tid; e < D * D; e += 256) st_bh[c * dd + e] = sW[e / D][e % D];
-    if (MODE == kForwardBoth) {
+    if (MODE == kF32ForwardBoth) {
       for (int e = tid; e < D * D; e += 256) sS[e / D][e % D] = sW[e / D][e % D] + st_bh[c * dd + e];
       __syncthreads();
       for (int e = tid; e < CH * D; e += 256) {
@@ -238,8 +435,34 @@ __global__ __launch_bounds__(256) void chunk_scan_f32(const float* __restrict__ 
     __syncthreads();
   }
   if (w_out) {
-    float* dst = w_out + (MODE == kReverseStore ? (long long)gridDim.x * dd : 0) + bh * dd;
+    float* dst = w_out + (MODE == kF32ReverseStore ? (long long)gridDim.x * dd : 0) + bh * dd;
     for (int e = tid; e < D * D; e += 256) dst[e] = sW[e / D][e % D];
+  }
+}
+
+// ---------------------------------------------------------------- planning and launch
+struct ChunkPlan {
+  int S, L;  // segments per (b, h) and chunks per segment
+};
+
+template <int D>
+ChunkPlan chunk_plan_d(bool bidir, int B, int H, int N, int CH) {
+  const int C = N / CH;
+  const int BH = B * H;
+  int S = (1024 + BH - 1) / BH;  // about 1024 workgroups for the scan
+  if (S > C / 8) S = C / 8;       // keep at least 8 chunks per segment
+  if (S < 1) S = 1;
+  int L = (C + S - 1) / S;
+  if (bidir && L > max_seg_len<D>()) L = max_seg_len<D>();
+  S = (C + L - 1) / L;
+  return ChunkPlan{S, L};
+}
+
+ChunkPlan chunk_plan(bool bidir, int B, int H, int N, int D, int CH) {
+  switch (D) {
+    case 16: return chunk_plan_d<16>(bidir, B, H, N, CH);
+    case 32: return chunk_plan_d<32>(bidir, B, H, N, CH);
+    default: return chunk_plan_d<64>(bidir, B, H, N, CH);
   }
 }
 
@@ -248,18 +471,31 @@ hipError_t launch_bf16(bool bidir, int B, int H, int N, float a, const void* q, 
                        const void* v, const float* w0, long long w0s, void* o, float* w_out,
                        void* ws, hipStream_t st) {
   const int BH = B * H;
-  const dim3 grid(BH), block(D / 16 * 64);
-  if (!bidir) {
-    hipLaunchKernelGGL((chunk_scan_bf16<D, CH, kCausal>), grid, block, 0, st, (const bf16*)q,
-                       (const bf16*)k, (const bf16*)v, w0, w0s, H, N, a, nullptr, (bf16*)o, w_out);
+  const ChunkPlan pl = chunk_plan(bidir, B, H, N, D, CH);
+  const long long DD = (long long)D * D;
+  float* comp = static_cast<float*>(ws);
+  float* win = comp + (long long)BH * pl.S * (bidir ? 4 : 2) * DD;
+  if (pl.S > 1) {
+    if (bidir) {
+      hipLaunchKernelGGL((chunk_compose_bf16<D, CH, true>), dim3(pl.S, BH), dim3(D / 8 * 64), 0, st,
+                         (const bf16*)k, (const bf16*)v, H, N, a, pl.S, pl.L, comp);
+      hipLaunchKernelGGL((chunk_prefix<D, true>), dim3(BH, 2), dim3(D / 16 * 64), 0, st, w0, w0s, H,
+                         pl.S, comp, win);
+    } else {
+      hipLaunchKernelGGL((chunk_compose_bf16<D, CH, false>), dim3(pl.S, BH), dim3(D / 8 * 64), 0,
+                         st, (const bf16*)k, (const bf16*)v, H, N, a, pl.S, pl.L, comp);
+      hipLaunchKernelGGL((chunk_prefix<D, false>), dim3(BH, 1), dim3(D / 16 * 64), 0, st, w0, w0s,
+                         H, pl.S, comp, win);
+    }
+  }
+  if (bidir) {
+    hipLaunchKernelGGL((chunk_scan_bf16<D, CH, kBidir>), dim3(pl.S, BH), dim3(D / 16 * 64), 0, st,
+                       (const bf16*)q, (const bf16*)k, (const bf16*)v, w0, w0s, H, N, a, pl.S,
+                       pl.L, win, (bf16*)o, w_out);
   } else {
-    float* states = static_cast<float*>(ws);
-    hipLaunchKernelGGL((chunk_scan_bf16<D, CH, kReverseStore>), grid, block, 0, st,
-                       (const bf16*)q, (const bf16*)k, (const bf16*)v, w0, w0s, H, N, a, states,
-                       (bf16*)o, w_out);
-    hipLaunchKernelGGL((chunk_scan_bf16<D, CH, kForwardBoth>), grid, block, 0, st,
-                       (const bf16*)q, (const bf16*)k, (const bf16*)v, w0, w0s, H, N, a, states,
-                       (bf16*)o, w_out);
+    hipLaunchKernelGGL((chunk_scan_bf16<D, CH, kCausal>), dim3(pl.S, BH), dim3(D / 16 * 64), 0,
+                       st, (const bf16*)q, (const bf16*)k, (const bf16*)v, w0, w0s, H, N, a, pl.S,
+                       pl.L, win, (bf16*)o, w_out);
   }
   return hipGetLastError();
 }
@@ -270,15 +506,15 @@ hipError_t launch_f32(bool bidir, int B, int H, int N, int CH, float a, const vo
                       float* w_out, void* ws, hipStream_t st) {
   const int BH = B * H;
   if (!bidir) {
-    hipLaunchKernelGGL((chunk_scan_f32<D, kCausal>), dim3(BH), dim3(256), 0, st, (const float*)q,
-                       (const float*)k, (const float*)v, w0, w0s, H, N, CH, a, nullptr,
-                       (float*)o, w_out);
+    hipLaunchKernelGGL((chunk_scan_f32<D, kF32Causal>), dim3(BH), dim3(256), 0, st,
+                       (const float*)q, (const float*)k, (const float*)v, w0, w0s, H, N, CH, a,
+                       nullptr, (float*)o, w_out);
   } else {
     float* states = static_cast<float*>(ws);
-    hipLaunchKernelGGL((chunk_scan_f32<D, kReverseStore>), dim3(BH), dim3(256), 0, st,
+    hipLaunchKernelGGL((chunk_scan_f32<D, kF32ReverseStore>), dim3(BH), dim3(256), 0, st,
                        (const float*)q, (const float*)k, (const float*)v, w0, w0s, H, N, CH, a,
                        states, (float*)o, w_out);
-    hipLaunchKernelGGL((chunk_scan_f32<D, kForwardBoth>), dim3(BH), dim3(256), 0, st,
+    hipLaunchKernelGGL((chunk_scan_f32<D, kF32ForwardBoth>), dim3(BH), dim3(256), 0, st,
                        (const float*)q, (const float*)k, (const float*)v, w0, w0s, H, N, CH, a,
                        states, (float*)o, w_out);
   }
@@ -300,11 +536,16 @@ hipError_t launch_bf16_d(bool bidir, int B, int H, int N, int CH, float a, const
 }  // namespace
 
 size_t chunked_workspace_bytes(bool bidir, bool bf16_io, int B, int H, int N, int D, int chunk) {
-  (void)bf16_io;
-  (void)chunk;
-  if (!bidir) return 0;
-  // reverse-scan state after every chunk: C * D * D fp32 per (b, h)
-  return (size_t)B * H * (size_t)N / (size_t)chunk * D * D * sizeof(float);
+  const size_t BH = (size_t)B * H, DD = (size_t)D * D;
+  if (!bf16_io) {
+    if (!bidir) return 0;
+    // fp32 path: reverse-scan state after every chunk, C * D * D fp32 per (b, h)
+    return BH * ((size_t)N / (size_t)chunk) * DD * sizeof(float);
+  }
+  const ChunkPlan pl = chunk_plan(bidir, B, H, N, D, chunk);
+  if (pl.S == 1) return 0;
+  // segment maps (Dev, R [, Dev_rev, R_rev]) + entry states per direction
+  return BH * pl.S * DD * sizeof(float) * ((bidir ? 4 : 2) + (bidir ? 2 : 1));
 }
 
 hipError_t chunked_launch(bool bidir, bool bf16_io, int B, int H, int N, int D, int chunk,

@@ -16,7 +16,8 @@
 // transposed (hidden x token) so each product's accumulator tile feeds the next product's B
 // operand directly; only the small per-chunk activations (X2, D1, E: tokens x features, bf16) go
 // through LDS for transposes. Cross-wave sums over the hidden dimension (Z2 and the read-out)
-// use LDS in a fixed wave order, so results are deterministic.
+// use LDS in a fixed wave order, so results are deterministic. K, V, Q of a chunk are staged
+// through double-buffered LDS; the next chunk's loads are issued before the current chunk's work.
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -35,12 +36,6 @@ constexpr int kPt = 24;            // pitch of [row][token] tiles (16 tokens + p
 __device__ __forceinline__ float gelu_f(float x) {
   return 0.5f * x * (1.f + erff(x * 0.70710678118654752440f));
 }
-// d/dx x Phi(x) = Phi(x) + x phi(x)
-__device__ __forceinline__ float gelu_d(float x) {
-  return 0.5f * (1.f + erff(x * 0.70710678118654752440f)) +
-         x * expf(-0.5f * x * x) * 0.39894228040143267794f;
-}
-
 __device__ __forceinline__ bf16x8 cat_tiles(f32x4 lo, f32x4 hi) {
   return cat8(to_bf16x4(lo), to_bf16x4(hi));
 }
@@ -49,13 +44,12 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ w1, const float* __restrict__ w2, long long wbs, int H, int N,
     float a, bf16* __restrict__ o, float* __restrict__ w1_out, float* __restrict__ w2_out) {
-  __shared__ __align__(16) bf16 sK[kCh * kP];
-  __shared__ __align__(16) bf16 sV[kCh * kP];
-  __shared__ __align__(16) bf16 sQ[kCh * kP];
+  __shared__ __align__(16) bf16 sKVQ[2][3][kCh * kP];
   __shared__ __align__(16) bf16 sX2[kWaves * kHw * kPt];  // -a X2^T per wave, [hidden][token]
   __shared__ __align__(16) bf16 sD1[kWaves * kHw * kPt];  // -a D1^T per wave, [hidden][token]
   __shared__ __align__(16) bf16 sE[kD * kPt];             // E^T, [feature][token]
   __shared__ __align__(16) f32x4 sRed[kWaves * 5 * 64];   // per-wave partial tiles, lane-private
+  __shared__ __align__(16) bf16x4 sEt[4 * 64];            // E^T tiles, lane-private accumulator layout
 
   const int bh = blockIdx.x, b = bh / H, h = bh % H;
   const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
@@ -81,47 +75,43 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
   const int C = N / kCh;
   const long long head0 = (long long)b * N * ts + (long long)h * kD;
 
+  // Staging: threads 0..383 each move one 16-byte piece of K, V or Q (16 rows x 8 pieces each).
+  // Chunk c is read from LDS buffer c & 1; chunk c + 1 is loaded into registers at the start of
+  // iteration c and written to the other buffer at its end.
+  const int t = threadIdx.x;
+  const int prow = (t & 127) >> 3, pcol = (t & 7) * 8, which = t >> 7;
+  const bf16* psrc = t < 128 ? k : (t < 256 ? v : q);
+  if (t < 384) st16(&sKVQ[0][which][prow * kP + pcol], ld16(psrc + head0 + prow * ts + pcol));
+
   for (int c = 0; c < C; ++c) {
     const long long tok0 = head0 + (long long)c * kCh * ts;
-    __syncthreads();
-    {  // stage K, V, Q: 16 rows x 8 chunks of 16 B each
-      const int t = threadIdx.x;
-      const int row = (t & 127) >> 3, col = (t & 7) * 8;
-      const bf16* src = t < 128 ? k : (t < 256 ? v : q);
-      bf16* dst = t < 128 ? sK : (t < 256 ? sV : sQ);
-      if (t < 384) st16(&dst[row * kP + col], ld16(src + tok0 + row * ts + col));
-    }
+    const bf16* sK = sKVQ[c & 1][0];
+    const bf16* sV = sKVQ[c & 1][1];
+    const bf16* sQ = sKVQ[c & 1][2];
+    uint4 pf = make_uint4(0u, 0u, 0u, 0u);
+    const bool pre = t < 384 && c + 1 < C;
+    if (pre) pf = ld16(psrc + tok0 + kCh * ts + prow * ts + pcol);
     __syncthreads();
 
-    // Z1^T, Z1q^T (hidden x token): A = W1^T from W1t, B = K^T / Q^T rows (c-layout k map).
-    f32x4 Z1[kNh], Z1q[kNh];
-    bf16x8 kb[2], qb[2];
-    for (int ks = 0; ks < 2; ++ks) {
-      const bf16* pk = &sK[r * kP + 32 * ks + 4 * g];
-      const bf16* pq = &sQ[r * kP + 32 * ks + 4 * g];
-      kb[ks] = cat8(ld4(pk), ld4(pk + 16));
-      qb[ks] = cat8(ld4(pq), ld4(pq + 16));
-    }
-    for (int n = 0; n < kNh; ++n) {
-      Z1[n] = zero4();
-      Z1q[n] = zero4();
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 aw = cat_tiles(W1t[2 * ks][n], W1t[2 * ks + 1][n]);
-        Z1[n] = mma32(aw, kb[ks], Z1[n]);
-        Z1q[n] = mma32(aw, qb[ks], Z1q[n]);
-      }
-    }
-    // Mt[t' = 4g + j][t = r] = k_t' . q_t
-    f32x4 Mt = zero4();
-    for (int ks = 0; ks < 2; ++ks)
-      Mt = mma32(ld8(&sK[r * kP + 32 * ks + 8 * g]), ld8(&sQ[r * kP + 32 * ks + 8 * g]), Mt);
-
+    // Z1^T (hidden x token): A = W1^T from W1t, B = K^T rows (c-layout k map).
     f32x4 X2[kNh], Gp[kNh];
-    for (int n = 0; n < kNh; ++n)
-      for (int j = 0; j < 4; ++j) {
-        X2[n][j] = gelu_f(Z1[n][j]);
-        Gp[n][j] = gelu_d(Z1[n][j]);
+    {
+      bf16x8 kb[2];
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16* pk = &sK[r * kP + 32 * ks + 4 * g];
+        kb[ks] = cat8(ld4(pk), ld4(pk + 16));
       }
+      for (int n = 0; n < kNh; ++n) {
+        f32x4 z = zero4();
+        for (int ks = 0; ks < 2; ++ks) z = mma32(cat_tiles(W1t[2 * ks][n], W1t[2 * ks + 1][n]), kb[ks], z);
+        for (int j = 0; j < 4; ++j) {
+          const float x = z[j];
+          const float cdf = 0.5f * (1.f + erff(x * 0.70710678118654752440f));
+          X2[n][j] = x * cdf;                                                       // GELU
+          Gp[n][j] = cdf + x * expf(-0.5f * x * x) * 0.39894228040143267794f;      // GELU'
+        }
+      }
+    }
 
     // Z2^T partial (output x token) over this wave's hidden slice: A = W2^T (from W2t), B = X2^T.
     for (int o2 = 0; o2 < 4; ++o2) {
@@ -131,40 +121,59 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
                     cat_tiles(X2[2 * kh], X2[2 * kh + 1]), acc);
       sRed[(w * 5 + o2) * 64 + l] = acc;
     }
-    __syncthreads();
-
-    // E^T = sum over waves (fixed order) of Z2^T - V^T, all four output tiles.
-    f32x4 Et[4];
-    for (int o2 = 0; o2 < 4; ++o2) {
-      f32x4 s = sRed[o2 * 64 + l];
-      for (int ww = 1; ww < kWaves; ++ww) s = s + sRed[(ww * 5 + o2) * 64 + l];
-      const bf16x4 vv = ld4(&sV[r * kP + 16 * o2 + 4 * g]);
-      for (int j = 0; j < 4; ++j) Et[o2][j] = s[j] - (float)vv[j];
-      if (o2 == w)
-        for (int j = 0; j < 4; ++j) sE[(16 * o2 + 4 * g + j) * kPt + r] = (bf16)Et[o2][j];
-    }
     for (int n = 0; n < kNh; ++n)
       for (int j = 0; j < 4; ++j) myX2[(16 * n + 4 * g + j) * kPt + r] = (bf16)(-a * X2[n][j]);
+    __syncthreads();
 
-    // dX2^T = W2 E^T (hidden x token): A = W2 rows (from W2x), B = E^T. D1^T = dX2^T * GELU'(Z1^T).
-    for (int n = 0; n < kNh; ++n) {
-      f32x4 acc = zero4();
-      for (int ko = 0; ko < 2; ++ko)
-        acc = mma32(cat_tiles(W2x[2 * ko][n], W2x[2 * ko + 1][n]),
-                    cat_tiles(Et[2 * ko], Et[2 * ko + 1]), acc);
-      for (int j = 0; j < 4; ++j) myD1[(16 * n + 4 * g + j) * kPt + r] = (bf16)(-a * acc[j] * Gp[n][j]);
+    // Waves 0..3: E^T tile w = sum over waves (fixed order) of Z2^T - V^T; shared as bf16 twice:
+    // [feature][token] rows (sE) and the lane-private accumulator layout (sEt).
+    if (w < 4) {
+      f32x4 s = sRed[w * 64 + l];
+      for (int ww = 1; ww < kWaves; ++ww) s = s + sRed[(ww * 5 + w) * 64 + l];
+      const bf16x4 vv = ld4(&sV[r * kP + 16 * w + 4 * g]);
+      bf16x4 eb;
+      for (int j = 0; j < 4; ++j) {
+        eb[j] = (bf16)(s[j] - (float)vv[j]);
+        sE[(16 * w + 4 * g + j) * kPt + r] = eb[j];
+      }
+      sEt[w * 64 + l] = eb;
     }
     __syncthreads();
 
-    // Z1q^T += (-a D1^T) tril(Q K^T)^T: A = D1^T rows (LDS), B = Mt with t' <= t kept.
-    f32x4 Mm = Mt;
+    // dX2^T = W2 E^T (hidden x token): A = W2 rows (from W2x), B = E^T. D1^T = dX2^T * GELU'(Z1^T).
+    {
+      bf16x8 eb[2];
+      for (int ko = 0; ko < 2; ++ko) eb[ko] = cat8(sEt[(2 * ko) * 64 + l], sEt[(2 * ko + 1) * 64 + l]);
+      for (int n = 0; n < kNh; ++n) {
+        f32x4 acc = zero4();
+        for (int ko = 0; ko < 2; ++ko) acc = mma32(cat_tiles(W2x[2 * ko][n], W2x[2 * ko + 1][n]), eb[ko], acc);
+        for (int j = 0; j < 4; ++j) myD1[(16 * n + 4 * g + j) * kPt + r] = (bf16)(-a * acc[j] * Gp[n][j]);
+      }
+    }
+    // The wave reads its D1 rows back across lanes below. A wave-local LDS wait was measured to be
+    // insufficient here (nondeterministic results), so this is a full workgroup barrier.
+    __syncthreads();
+    // Read-out. Mt[t' = 4g + j][t = r] = k_t' . q_t, kept for t' <= t.
+    f32x4 Mt = zero4();
+    for (int ks = 0; ks < 2; ++ks)
+      Mt = mma32(ld8(&sK[r * kP + 32 * ks + 8 * g]), ld8(&sQ[r * kP + 32 * ks + 8 * g]), Mt);
     for (int j = 0; j < 4; ++j)
-      if (4 * g + j > r) Mm[j] = 0.f;
-    const bf16x4 Mb = to_bf16x4(Mm);
+      if (4 * g + j > r) Mt[j] = 0.f;
+    const bf16x4 Mb = to_bf16x4(Mt);
+    // Z1q^T = W1^T Q^T + (-a D1^T) tril(Q K^T)^T (the wave's own D1 rows, written above).
     f32x4 X2q[kNh];
-    for (int n = 0; n < kNh; ++n) {
-      Z1q[n] = mma16(ld4(&myD1[(16 * n + r) * kPt + 4 * g]), Mb, Z1q[n]);
-      for (int j = 0; j < 4; ++j) X2q[n][j] = gelu_f(Z1q[n][j]);
+    {
+      bf16x8 qb[2];
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16* pq = &sQ[r * kP + 32 * ks + 4 * g];
+        qb[ks] = cat8(ld4(pq), ld4(pq + 16));
+      }
+      for (int n = 0; n < kNh; ++n) {
+        f32x4 z = zero4();
+        for (int ks = 0; ks < 2; ++ks) z = mma32(cat_tiles(W1t[2 * ks][n], W1t[2 * ks + 1][n]), qb[ks], z);
+        z = mma16(ld4(&myD1[(16 * n + r) * kPt + 4 * g]), Mb, z);
+        for (int j = 0; j < 4; ++j) X2q[n][j] = gelu_f(z[j]);
+      }
     }
 
     // O^T partial = W2^T X2q^T, and N2^T partial = X2 X2q^T (token x token), this wave's hidden slice.
@@ -183,19 +192,18 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
     }
     __syncthreads();
 
-    // Wave w finishes output tile w: O^T = sum of partials - a E^T tril(X2q X2^T)^T; store.
-    for (int o2 = 0; o2 < 4; ++o2) {
-      if (o2 != w) continue;
-      f32x4 s = sRed[o2 * 64 + l];
+    // Waves 0..3 finish output tile w: O^T = sum of partials - a E^T tril(X2q X2^T)^T; store.
+    if (w < 4) {
+      f32x4 s = sRed[w * 64 + l];
       f32x4 n2 = sRed[4 * 64 + l];
       for (int ww = 1; ww < kWaves; ++ww) {
-        s = s + sRed[(ww * 5 + o2) * 64 + l];
+        s = s + sRed[(ww * 5 + w) * 64 + l];
         n2 = n2 + sRed[(ww * 5 + 4) * 64 + l];
       }
       for (int j = 0; j < 4; ++j)
         if (4 * g + j > r) n2[j] = 0.f;
-      s = mma16(ld4(&sE[(16 * o2 + r) * kPt + 4 * g]), to_bf16x4_scaled(n2, -a), s);
-      *reinterpret_cast<bf16x4*>(o + tok0 + r * ts + 16 * o2 + 4 * g) = to_bf16x4(s);
+      s = mma16(ld4(&sE[(16 * w + r) * kPt + 4 * g]), to_bf16x4_scaled(n2, -a), s);
+      *reinterpret_cast<bf16x4*>(o + tok0 + r * ts + 16 * w + 4 * g) = to_bf16x4(s);
     }
 
     // State updates at the end of the chunk (the read-out above used the start state).
@@ -210,6 +218,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
         W2x[o2][n] = mma16(e, x2, W2x[o2][n]);   // W2^T += E^T (-a X2)
       }
     }
+    if (pre) st16(&sKVQ[(c + 1) & 1][which][prow * kP + pcol], pf);
   }
 
   const long long bhl = bh;

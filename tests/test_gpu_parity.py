@@ -114,6 +114,34 @@ SMALL = [
     W["ttt_mlp_causal_8k"].with_(B=2, N=16, H=1, seed=52),
 ]
 
+# Chunked cases long enough to be split into several segments (compose + prefix + rescan),
+# including a ragged last segment, for every head dim and chunk size.
+SEGMENTED = [
+    W["ttt_linear_causal_16k"].with_(B=1, N=2048, H=2, seed=101),
+    W["ttt_linear_causal_16k"].with_(B=1, N=1600, H=2, seed=102),           # 100 chunks, ragged last segment
+    W["ttt_linear_causal_16k"].with_(B=1, N=1024, H=3, D=32, chunk=32, seed=103),
+    W["ttt_linear_causal_16k"].with_(B=2, N=1024, H=1, D=16, chunk=16, seed=104),
+    W["ttt_linear_causal_16k"].with_(B=1, N=4096, H=1, chunk=64, seed=105),
+    W["vittt_bidir_1280"].with_(B=1, N=4096, H=2, seed=111),
+    W["vittt_bidir_1280"].with_(B=1, N=3200, H=1, seed=112),                # 50 chunks, ragged last segment
+    W["vittt_bidir_1280"].with_(B=1, N=2048, H=2, D=32, chunk=16, seed=113),
+    W["vittt_bidir_1280"].with_(B=1, N=2048, H=2, D=16, chunk=32, seed=114),
+    W["vittt_bidir_1280"].with_(B=2, N=2048, H=1, D=64, chunk=16, seed=115),
+]
+
+
+@pytest.mark.parametrize("wl", SEGMENTED, ids=lambda w: f"{w.op}-B{w.B}N{w.N}H{w.H}D{w.D}c{w.chunk}")
+def test_segmented_parity(wl):
+    x = synth.make_inputs(wl)
+    out, st = run_gpu(x, want_state=True)
+    ref = oracle_full(x)
+    err = slice_err(out, ref[0])
+    print(f"{wl.op} N={wl.N} err={err:.3e}")
+    assert err <= BF16_TOL
+    refs = ref[1:] if wl.op == "bidir" else ref[1:2]
+    for i, wref in enumerate(refs):
+        assert np.abs(st[i] - wref).max() / np.abs(wref).max() <= BF16_TOL
+
 
 @pytest.mark.parametrize("wl", SMALL, ids=lambda w: f"{w.op}-{w.dtype}-B{w.B}N{w.N}H{w.H}D{w.D}c{w.chunk}")
 def test_small_parity(wl):
@@ -234,8 +262,13 @@ def test_causal_resume_from_state_equals_one_call():
     oa, sa = run_gpu(xa, want_state=True)
     ob, sb = run_gpu(xb, w0=sa[0], want_state=True)
     both = np.concatenate([oa, ob], axis=1)
-    assert slice_err(both, full) <= 1e-3
-    assert np.abs(sb[0] - st[0]).max() / np.abs(st[0]).max() <= 1e-3
+    # Each run takes its own bf16 rounding path (one call may split the sequence into segments,
+    # the halves may not), so both are held to the oracle at the parity bar; the invariant itself
+    # is pinned exactly on the fp64 oracle.
+    ref_o, ref_w = oracle_full(x)
+    assert slice_err(both, ref_o) <= BF16_TOL
+    assert slice_err(full, ref_o) <= BF16_TOL
+    assert np.abs(sb[0] - ref_w).max() / np.abs(ref_w).max() <= BF16_TOL
 
 
 @pytest.mark.parametrize("wl", [W["hvit3t_stage1_fullbatch"].with_(B=4, N=1000, seed=91),
