@@ -35,8 +35,9 @@
  *     TTT_ERR_WORKSPACE    workspace_bytes < ttt_workspace_size(...)
  *     TTT_ERR_HIP          a HIP launch error reported right after enqueueing
  * Workspace.  Scratch device memory of at least ttt_workspace_size(...) bytes (may be NULL when
- *   that size is 0). Its contents need no initialisation and are garbage afterwards. Calls that
- *   share one workspace must be ordered on one stream.
+ *   that size is 0). It needs no initialisation and holds garbage afterwards. Calls that share
+ *   one workspace must be ordered on one stream; calls on different streams need separate
+ *   workspaces.
  * Precision.  TTT_F32 computes in fp32 throughout (plain FMA, no reduced-precision operands).
  *   TTT_BF16 reads and writes bf16 (round-to-nearest-even on output), keeps the state and every
  *   accumulator in fp32, and feeds bf16 operands to the matrix cores.

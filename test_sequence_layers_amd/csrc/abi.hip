@@ -94,7 +94,7 @@ size_t ttt_workspace_size(ttt_op op, ttt_dtype dt, int B, int H, int N, int D, i
   const bool bf = dt == TTT_BF16;
   switch (op) {
     case TTT_OP_FULLBATCH:
-      return round_up(ttt::fb_workspace_bytes(B, H, N, D), 256);
+      return round_up(ttt::fb_workspace_bytes(bf, B, H, N, D), 256);
     case TTT_OP_CAUSAL:
     case TTT_OP_BIDIR:
       if (!supported_chunk(chunk) || N % chunk != 0) return 0;

@@ -2,13 +2,18 @@
 // single epoch, full batch, inner learning rate 1.0; "core idea": train on (K, V), read out Q):
 //   W* = W0 - (eta/N) K^T (K W0 - V),  O = Q W*   for every (batch, head).
 //
-// Three launches on the caller's stream:
-//   1. fb_partial: grid (splits, B*H). Each workgroup streams a token range of one (b, h) through
-//      LDS and accumulates the partial gradient G_s = K_s^T (K_s W0 - V_s) with MFMA.
-//   2. fb_reduce:  grid (B*H). Sums the split partials in a fixed order (deterministic) and forms W*.
-//   3. fb_readout: grid (splits, B*H). Streams Q and writes O = Q W*.
+// bf16 I/O: three launches. Heads whose D-vectors are adjacent in a token row are grouped up to
+// 128 bytes per row (2 heads of 32, 4 of 16, 1 of 64), so every staged row is a full, contiguous
+// cache line. Work items are (group, token split), one per workgroup.
+//   fb_partial_bf16: stream K, V tiles (double-buffered LDS, next tile prefetched into
+//                    registers) and accumulate the split's partial gradient
+//                    G_s = K_s^T (K_s W0 - V_s) with MFMA;
+//   fb_reduce_bf16:  W* = W0 - (eta/N) sum_s G_s, summed in a fixed split order (deterministic);
+//   fb_readout_bf16: stream Q and write O = Q W*.
 // HBM traffic is the algorithmic Q, K, V read plus the O write; the partials are d x d fp32 per
 // split and stay in L2 / Infinity Cache.
+//
+// fp32 I/O: three plain-FMA launches (partial gradients, fixed-order reduction, read-out).
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -19,127 +24,210 @@ constexpr int kTile = 64;      // tokens per staged tile (bf16 path)
 constexpr int kThreads = 256;  // 4 waves per workgroup
 constexpr int kTileF = 32;     // tokens per staged tile (fp32 path)
 
-// Stage a [64 x D] bf16 tile into LDS (row pitch P); rows >= valid become zeros, which adds
-// nothing to K^T (K W0 - V).
-template <int D, int P>
-__device__ __forceinline__ void stage_bf16(bf16* dst, const bf16* src, long long ts, int valid) {
-  constexpr int CPR = D / 8;
-  for (int c = threadIdx.x; c < kTile * CPR; c += kThreads) {
-    const int row = c / CPR, col = (c % CPR) * 8;
-    uint4 val = make_uint4(0u, 0u, 0u, 0u);
-    if (row < valid) val = ld16(src + row * ts + col);
-    st16(dst + row * P + col, val);
-  }
-}
-
 // ---------------------------------------------------------------- bf16 I/O, MFMA
-template <int D>
+// Shared geometry of the bf16 kernels: a head group of HG heads of D features (COLS <= 64
+// channels, one 128-byte row per token), (head, 16-column) pairs spread over the 4 waves.
+template <int D, int HG>
+struct Geo {
+  static constexpr int NT = D / 16;
+  static constexpr int COLS = HG * D;
+  static constexpr int PAIRS = COLS / 16;
+  static constexpr int WPP = 4 / PAIRS;  // waves per pair; they split the 16-token sub-tiles
+  static constexpr int P = COLS + 8;     // LDS row pitch (elements)
+  static constexpr int CPR = COLS / 8;   // 16-byte pieces per row
+  static constexpr int PIECES = kTile * CPR;
+  static constexpr int PER = (PIECES + kThreads - 1) / kThreads;
+  static constexpr int KS = D >= 32 ? D / 32 : 1;
+};
+
+// Register <-> LDS staging of one 64-token tile of a head group (rows past n1 read as zeros).
+template <class G>
+struct Stager {
+  const bf16* src;
+  long long base, ts;
+  int n1;
+  __device__ __forceinline__ void load(uint4* regs, int t0) const {
+    for (int i = 0; i < G::PER; ++i) {
+      const int c = threadIdx.x + i * kThreads;
+      uint4 val = make_uint4(0u, 0u, 0u, 0u);
+      if (G::PIECES % kThreads == 0 || c < G::PIECES) {
+        const int row = c / G::CPR, col = (c % G::CPR) * 8;
+        if (t0 + row < n1) val = ld16(src + base + (long long)(t0 + row) * ts + col);
+      }
+      regs[i] = val;
+    }
+  }
+  __device__ __forceinline__ static void store(bf16* dst, const uint4* regs) {
+    for (int i = 0; i < G::PER; ++i) {
+      const int c = threadIdx.x + i * kThreads;
+      if (G::PIECES % kThreads == 0 || c < G::PIECES) st16(dst + (c / G::CPR) * G::P + (c % G::CPR) * 8, regs[i]);
+    }
+  }
+};
+
+// 1. Partial gradient of one token split of one head group: G_s = K_s^T (K_s W0 - V_s).
+template <int D, int HG>
 __global__ __launch_bounds__(kThreads) void fb_partial_bf16(
     const bf16* __restrict__ k, const bf16* __restrict__ v, const float* __restrict__ w0,
-    long long w0_bstride, int H, int N, int tps, int S, float* __restrict__ partial) {
-  constexpr int P = D + 8;     // LDS row pitch (elements); +16 B keeps row reads conflict-free
-  constexpr int NT = D / 16;   // 16-column tiles of W / G
-  constexpr int WPT = 4 / NT;  // waves sharing one column tile; they split the 16-token sub-tiles
-  __shared__ __align__(16) bf16 sK[kTile * P];
-  __shared__ __align__(16) bf16 sV[kTile * P];
-  __shared__ float sG[4 * D * 16];
+    long long w0_bstride, int H, int N, int S, int tps, float* __restrict__ partial) {
+  using G = Geo<D, HG>;
+  constexpr long long DD = (long long)D * D;
+  __shared__ __align__(16) bf16 sK[2][kTile * G::P];
+  __shared__ __align__(16) bf16 sV[2][kTile * G::P];
+  static_assert(sizeof(float) * 4 * D * 16 <= sizeof(bf16) * 2 * kTile * G::P, "partials fit in sK");
+  float* sG = reinterpret_cast<float*>(&sK[0][0]);
 
-  const int s = blockIdx.x, bh = blockIdx.y;
-  const int b = bh / H, h = bh % H;
+  const int grp = blockIdx.x / S, s = blockIdx.x % S;
+  const int b = grp / (H / HG), h0 = (grp % (H / HG)) * HG;
   const int n0 = s * tps, n1 = min(N, n0 + tps);
+  const int ntiles = (n1 - n0 + kTile - 1) / kTile;
   const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
-  const int n = w % NT, tw = w / NT;
+  const int pair = w % G::PAIRS, tw = w / G::PAIRS;
+  const int hl = pair / G::NT, n = pair % G::NT;  // head within the group, column tile
   const long long ts = (long long)H * D;
-  const float* W0 = w0 + b * w0_bstride + (long long)h * D * D;
+  const long long base = (long long)b * N * ts + (long long)h0 * D;
+  const Stager<G> stk{k, base, ts, n1}, stv{v, base, ts, n1};
 
-  // B operand fragments of W0[:, 16n .. 16n+16), contiguous k map.
-  constexpr int KS = D >= 32 ? D / 32 : 1;
-  bf16x8 wb[KS];
+  bf16x8 wb[G::KS];  // B operand: W0[:, 16n .. 16n + 16), contiguous k map
   bf16x4 wb4;
-  if constexpr (D >= 32) {
-    for (int ks = 0; ks < KS; ++ks)
-      for (int i = 0; i < 8; ++i) wb[ks][i] = (bf16)W0[(32 * ks + 8 * g + i) * D + 16 * n + r];
-  } else {
-    for (int i = 0; i < 4; ++i) wb4[i] = (bf16)W0[(4 * g + i) * D + 16 * n + r];
-  }
-
-  f32x4 G[NT];
-  for (int m = 0; m < NT; ++m) G[m] = zero4();
-
-  const long long base = ((long long)b * N + n0) * ts + (long long)h * D;
-  for (int t0 = n0; t0 < n1; t0 += kTile) {
-    __syncthreads();
-    stage_bf16<D, P>(sK, k + base + (long long)(t0 - n0) * ts, ts, n1 - t0);
-    stage_bf16<D, P>(sV, v + base + (long long)(t0 - n0) * ts, ts, n1 - t0);
-    __syncthreads();
-    for (int p = tw; p < 4; p += WPT) {
-      // E = K W0 - V on 16 tokens x 16 columns (C layout: row = token 16p + 4g + j).
-      f32x4 e;
-      for (int j = 0; j < 4; ++j) e[j] = -(float)sV[(16 * p + 4 * g + j) * P + 16 * n + r];
-      if constexpr (D >= 32) {
-        for (int ks = 0; ks < KS; ++ks) e = mma32(ld8(&sK[(16 * p + r) * P + 32 * ks + 8 * g]), wb[ks], e);
-      } else {
-        e = mma16(ld4(&sK[(16 * p + r) * P + 4 * g]), wb4, e);
-      }
-      // G[:, n] += K^T E: E's C layout is already the B operand (k = token 4g + j).
-      const bf16x4 eb = to_bf16x4(e);
-      for (int m = 0; m < NT; ++m)
-        G[m] = mma16(ld4_col(&sK[(16 * p + 4 * g) * P + 16 * m + r], P), eb, G[m]);
+  {
+    const float* W0 = w0 + b * w0_bstride + (long long)(h0 + hl) * DD;
+    if constexpr (D >= 32) {
+      for (int ks = 0; ks < G::KS; ++ks)
+        for (int i = 0; i < 8; ++i) wb[ks][i] = (bf16)W0[(32 * ks + 8 * g + i) * D + 16 * n + r];
+    } else {
+      for (int i = 0; i < 4; ++i) wb4[i] = (bf16)W0[(4 * g + i) * D + 16 * n + r];
     }
   }
-  // Sum the waves that share a column tile, in a fixed order.
-  for (int m = 0; m < NT; ++m)
-    for (int j = 0; j < 4; ++j) sG[(w * D + 16 * m + 4 * g + j) * 16 + r] = G[m][j];
+  f32x4 acc[G::NT];
+  for (int m = 0; m < G::NT; ++m) acc[m] = zero4();
+  uint4 rk[G::PER], rv[G::PER];
+  stk.load(rk, n0);
+  stv.load(rv, n0);
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it & 1;
+    Stager<G>::store(sK[buf], rk);
+    Stager<G>::store(sV[buf], rv);
+    if (it + 1 < ntiles) {  // the next tile loads while this one is processed
+      stk.load(rk, n0 + (it + 1) * kTile);
+      stv.load(rv, n0 + (it + 1) * kTile);
+    }
+    __syncthreads();
+    const bf16* tK = sK[buf] + hl * D;
+    const bf16* tV = sV[buf] + hl * D;
+    for (int p = tw; p < 4; p += G::WPP) {
+      f32x4 e;  // E = K W0 - V, 16 tokens x 16 columns (C layout: row = token 16p + 4g + j)
+      for (int j = 0; j < 4; ++j) e[j] = -(float)tV[(16 * p + 4 * g + j) * G::P + 16 * n + r];
+      if constexpr (D >= 32) {
+        for (int ks = 0; ks < G::KS; ++ks) e = mma32(ld8(&tK[(16 * p + r) * G::P + 32 * ks + 8 * g]), wb[ks], e);
+      } else {
+        e = mma16(ld4(&tK[(16 * p + r) * G::P + 4 * g]), wb4, e);
+      }
+      const bf16x4 eb = to_bf16x4(e);  // acc[:, n] += K^T E (E's C layout is the B operand)
+      for (int m = 0; m < G::NT; ++m)
+        acc[m] = mma16(ld4_col(&tK[(16 * p + 4 * g) * G::P + 16 * m + r], G::P), eb, acc[m]);
+    }
+  }
+  __syncthreads();  // tile buffers free: sum the waves sharing a pair through sK, in a fixed order
+  for (int m = 0; m < G::NT; ++m)
+    for (int j = 0; j < 4; ++j) sG[(w * D + 16 * m + 4 * g + j) * 16 + r] = acc[m][j];
   __syncthreads();
-  float* out = partial + ((long long)bh * S + s) * D * D;
-  for (int e = threadIdx.x; e < D * D; e += kThreads) {
-    const int i = e / D, c = e % D, nn = c / 16, rr = c % 16;
-    float acc = 0.f;
-    for (int t = 0; t < WPT; ++t) acc += sG[((t * NT + nn) * D + i) * 16 + rr];
-    out[e] = acc;
+  float* part = partial + ((long long)grp * S + s) * HG * DD;
+  for (int e = threadIdx.x; e < HG * D * D; e += kThreads) {
+    const int hh = e / (D * D), rem = e % (D * D), i = rem / D, c = rem % D;
+    const int pr = hh * G::NT + c / 16;
+    float sum = 0.f;
+    for (int t = 0; t < G::WPP; ++t) sum += sG[((t * G::PAIRS + pr) * D + i) * 16 + (c % 16)];
+    part[e] = sum;
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads) void fb_readout_bf16(const bf16* __restrict__ q,
-                                                            const float* __restrict__ wstar, int H,
-                                                            int N, int tps, bf16* __restrict__ o) {
-  constexpr int NT = D / 16;
-  constexpr int KS = D >= 32 ? D / 32 : 1;
-  const int s = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H;
-  const int n0 = s * tps, n1 = min(N, n0 + tps);
-  const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
-  const float* W = wstar + (long long)bh * D * D;
-  const long long ts = (long long)H * D;
+// 2. W* = W0 - (eta/N) sum_s G_s, summed over the splits in a fixed order (deterministic). One
+// thread per element; 16 of its split partials are in flight at a time.
+template <int D, int HG>
+__global__ __launch_bounds__(kThreads) void fb_reduce_bf16(const float* __restrict__ partial,
+                                                           int S, const float* __restrict__ w0,
+                                                           long long w0_bstride, int H,
+                                                           float scale, float* __restrict__ wstar,
+                                                           float* __restrict__ w_out) {
+  constexpr int E = HG * D * D;               // elements of one group's matrices
+  constexpr int WG_PER_GROUP = E / kThreads;  // workgroups per group, one element per thread
+  constexpr long long DD = (long long)D * D;
+  const int grp = blockIdx.x / WG_PER_GROUP;
+  const int e = (blockIdx.x % WG_PER_GROUP) * kThreads + threadIdx.x;
+  const int b = grp / (H / HG), hh = e / (D * D), rem = e % (D * D);
+  const float* pg = partial + (long long)grp * S * E + e;
+  float sum = 0.f;
+  for (int s0 = 0; s0 < S; s0 += 16) {
+    float val[16];
+    for (int u = 0; u < 16; ++u) val[u] = s0 + u < S ? pg[(long long)(s0 + u) * E] : 0.f;
+    for (int u = 0; u < 16; ++u) sum += val[u];
+  }
+  const int h = (grp % (H / HG)) * HG + hh;
+  const float wv = w0[b * w0_bstride + (long long)h * DD + rem] - scale * sum;
+  wstar[(long long)grp * E + e] = wv;
+  if (w_out) w_out[((long long)b * H + h) * DD + rem] = wv;
+}
 
-  // O^T = W*^T Q^T: A = W*^T (lane: row c = 16n + r, k = feature), B = Q^T (lane: token column).
-  bf16x8 wa[NT][KS];
-  bf16x4 wa4[NT];
-  for (int n = 0; n < NT; ++n) {
+// 3. O = Q W*, computed as O^T = W*^T Q^T (lane (r, g) gets 4 adjacent outputs of a token); the
+// O tile is assembled in LDS and written as full 128-byte rows.
+template <int D, int HG>
+__global__ __launch_bounds__(kThreads) void fb_readout_bf16(const bf16* __restrict__ q,
+                                                            const float* __restrict__ wstar,
+                                                            int H, int N, int S, int tps,
+                                                            bf16* __restrict__ o) {
+  using G = Geo<D, HG>;
+  constexpr long long DD = (long long)D * D;
+  __shared__ __align__(16) bf16 sQ[2][kTile * G::P];
+  __shared__ __align__(16) bf16 sO[2][kTile * G::P];
+  const int grp = blockIdx.x / S, s = blockIdx.x % S;
+  const int b = grp / (H / HG), h0 = (grp % (H / HG)) * HG;
+  const int n0 = s * tps, n1 = min(N, n0 + tps);
+  const int ntiles = (n1 - n0 + kTile - 1) / kTile;
+  const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
+  const int pair = w % G::PAIRS, tw = w / G::PAIRS;
+  const int hl = pair / G::NT, n = pair % G::NT;
+  const long long ts = (long long)H * D;
+  const long long base = (long long)b * N * ts + (long long)h0 * D;
+  const Stager<G> stq{q, base, ts, n1};
+
+  uint4 rq[G::PER];
+  stq.load(rq, n0);
+  bf16x8 wa[G::KS];  // A = W*^T: lane holds W*[k][16n + r], contiguous k map
+  bf16x4 wa4;
+  {
+    const float* Ws = wstar + (long long)grp * HG * DD + hl * DD;
     if constexpr (D >= 32) {
-      for (int ks = 0; ks < KS; ++ks)
-        for (int i = 0; i < 8; ++i) wa[n][ks][i] = (bf16)W[(32 * ks + 8 * g + i) * D + 16 * n + r];
+      for (int ks = 0; ks < G::KS; ++ks)
+        for (int i = 0; i < 8; ++i) wa[ks][i] = (bf16)Ws[(32 * ks + 8 * g + i) * D + 16 * n + r];
     } else {
-      for (int i = 0; i < 4; ++i) wa4[n][i] = (bf16)W[(4 * g + i) * D + 16 * n + r];
+      for (int i = 0; i < 4; ++i) wa4[i] = (bf16)Ws[(4 * g + i) * D + 16 * n + r];
     }
   }
-  for (int t0 = n0 + 16 * w; t0 < n1; t0 += 64) {
-    const int t = t0 + r;
-    const bool ok = t < n1;
-    const bf16* qrow = q + ((long long)b * N + (ok ? t : t0)) * ts + (long long)h * D;
-    bf16* orow = o + ((long long)b * N + (ok ? t : t0)) * ts + (long long)h * D;
-    if constexpr (D >= 32) {
-      bf16x8 qb[KS];
-      for (int ks = 0; ks < KS; ++ks) qb[ks] = ld8(qrow + 32 * ks + 8 * g);
-      for (int n = 0; n < NT; ++n) {
-        f32x4 acc = zero4();
-        for (int ks = 0; ks < KS; ++ks) acc = mma32(wa[n][ks], qb[ks], acc);
-        if (ok) *reinterpret_cast<bf16x4*>(orow + 16 * n + 4 * g) = to_bf16x4(acc);
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it & 1;
+    const int t0 = n0 + it * kTile;
+    Stager<G>::store(sQ[buf], rq);
+    if (it + 1 < ntiles) stq.load(rq, t0 + kTile);
+    __syncthreads();
+    const bf16* tQ = sQ[buf] + hl * D;
+    bf16* tO = sO[buf] + hl * D;
+    for (int p = tw; p < 4; p += G::WPP) {
+      f32x4 acc = zero4();
+      if constexpr (D >= 32) {
+        for (int ks = 0; ks < G::KS; ++ks) acc = mma32(wa[ks], ld8(&tQ[(16 * p + r) * G::P + 32 * ks + 8 * g]), acc);
+      } else {
+        acc = mma16(wa4, ld4(&tQ[(16 * p + r) * G::P + 4 * g]), acc);
       }
-    } else {
-      const bf16x4 qb = ld4(qrow + 4 * g);
-      f32x4 acc = mma16(wa4[0], qb, zero4());
-      if (ok) *reinterpret_cast<bf16x4*>(orow + 4 * g) = to_bf16x4(acc);
+      *reinterpret_cast<bf16x4*>(&tO[(16 * p + r) * G::P + 16 * n + 4 * g]) = to_bf16x4(acc);
+    }
+    __syncthreads();
+    for (int i = 0; i < G::PER; ++i) {
+      const int c = threadIdx.x + i * kThreads;
+      if (G::PIECES % kThreads == 0 || c < G::PIECES) {
+        const int row = c / G::CPR, col = (c % G::CPR) * 8;
+        if (t0 + row < n1) st16(o + base + (long long)(t0 + row) * ts + col, ld16(&sO[buf][row * G::P + col]));
+      }
     }
   }
 }
@@ -242,42 +330,18 @@ __global__ __launch_bounds__(kThreads) void fb_reduce(const float* __restrict__ 
   }
 }
 
-template <int D>
-hipError_t fb_launch_d(bool bf16_io, int B, int H, int N, float eta, const void* q, const void* k,
-                       const void* v, const float* w0, long long w0s, void* o, float* w_out,
-                       void* ws, hipStream_t st) {
-  const FbPlan pl = fb_plan(B, H, N, D);
-  const int BH = B * H;
-  float* partial = static_cast<float*>(ws);
-  float* wstar = partial + (size_t)BH * pl.splits * D * D;
-  const dim3 grid(pl.splits, BH);
-  if (bf16_io) {
-    hipLaunchKernelGGL(fb_partial_bf16<D>, grid, dim3(kThreads), 0, st, (const bf16*)k,
-                       (const bf16*)v, w0, w0s, H, N, pl.tokens_per_split, pl.splits, partial);
-  } else {
-    hipLaunchKernelGGL(fb_partial_f32<D>, grid, dim3(kThreads), 0, st, (const float*)k,
-                       (const float*)v, w0, w0s, H, N, pl.tokens_per_split, pl.splits, partial);
-  }
-  hipLaunchKernelGGL(fb_reduce, dim3(BH), dim3(kThreads), 0, st, partial, pl.splits, w0, w0s, H,
-                     D, eta / (float)N, wstar, w_out);
-  if (bf16_io) {
-    hipLaunchKernelGGL(fb_readout_bf16<D>, grid, dim3(kThreads), 0, st, (const bf16*)q, wstar, H,
-                       N, pl.tokens_per_split, (bf16*)o);
-  } else {
-    hipLaunchKernelGGL(fb_readout_f32<D>, grid, dim3(kThreads), 0, st, (const float*)q, wstar, H,
-                       N, pl.tokens_per_split, (float*)o);
-  }
-  return hipGetLastError();
+// Heads per group: the largest power of two dividing H whose D-vectors fit in one 128-byte row
+// (1, 2 or 4: the group's (head, 16-column) pairs must divide the 4 waves).
+int head_group(int H, int D) {
+  int hg = 64 / D;
+  while (hg > 1 && H % hg != 0) hg /= 2;
+  return hg;
 }
 
-}  // namespace
-
-FbPlan fb_plan(int B, int H, int N, int D) {
-  (void)D;
-  const int BH = B * H;
+FbPlan plan_splits(int groups, int N) {
   const int tiles = (N + kTile - 1) / kTile;
   // Aim for about 1024 workgroups (4 per CU on 256 CUs), never below one 64-token tile each.
-  int splits = (1024 + BH - 1) / BH;
+  int splits = (1024 + groups - 1) / groups;
   if (splits > tiles) splits = tiles;
   if (splits < 1) splits = 1;
   const int tiles_per = (tiles + splits - 1) / splits;
@@ -287,19 +351,78 @@ FbPlan fb_plan(int B, int H, int N, int D) {
   return p;
 }
 
-size_t fb_workspace_bytes(int B, int H, int N, int D) {
-  const FbPlan p = fb_plan(B, H, N, D);
+template <int D, int HG>
+hipError_t launch_bf16(int B, int H, int N, float eta, const void* q, const void* k, const void* v,
+                       const float* w0, long long w0s, void* o, float* w_out, void* ws,
+                       hipStream_t st) {
+  const int groups = B * (H / HG);
+  const FbPlan pl = plan_splits(groups, N);
+  float* partial = static_cast<float*>(ws);
+  float* wstar = partial + (size_t)groups * pl.splits * HG * D * D;
+  const int items = groups * pl.splits;
+  hipLaunchKernelGGL((fb_partial_bf16<D, HG>), dim3(items), dim3(kThreads), 0, st, (const bf16*)k,
+                     (const bf16*)v, w0, w0s, H, N, pl.splits, pl.tokens_per_split, partial);
+  hipLaunchKernelGGL((fb_reduce_bf16<D, HG>), dim3(groups * (HG * D * D / kThreads)),
+                     dim3(kThreads), 0, st, partial, pl.splits, w0, w0s, H, eta / (float)N, wstar,
+                     w_out);
+  hipLaunchKernelGGL((fb_readout_bf16<D, HG>), dim3(items), dim3(kThreads), 0, st, (const bf16*)q,
+                     wstar, H, N, pl.splits, pl.tokens_per_split, (bf16*)o);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_f32(int B, int H, int N, float eta, const void* q, const void* k, const void* v,
+                      const float* w0, long long w0s, void* o, float* w_out, void* ws,
+                      hipStream_t st) {
+  const int BH = B * H;
+  const FbPlan pl = plan_splits(BH, N);
+  float* partial = static_cast<float*>(ws);
+  float* wstar = partial + (size_t)BH * pl.splits * D * D;
+  const dim3 grid(pl.splits, BH);
+  hipLaunchKernelGGL(fb_partial_f32<D>, grid, dim3(kThreads), 0, st, (const float*)k,
+                     (const float*)v, w0, w0s, H, N, pl.tokens_per_split, pl.splits, partial);
+  hipLaunchKernelGGL(fb_reduce, dim3(BH), dim3(kThreads), 0, st, partial, pl.splits, w0, w0s, H,
+                     D, eta / (float)N, wstar, w_out);
+  hipLaunchKernelGGL(fb_readout_f32<D>, grid, dim3(kThreads), 0, st, (const float*)q, wstar, H,
+                     N, pl.tokens_per_split, (float*)o);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+FbPlan fb_plan(int B, int H, int N, int D) { return plan_splits(B * (H / head_group(H, D)), N); }
+
+size_t fb_workspace_bytes(bool bf16_io, int B, int H, int N, int D) {
   const size_t dd = (size_t)D * D * sizeof(float);
-  return (size_t)B * H * p.splits * dd + (size_t)B * H * dd;
+  if (!bf16_io) {
+    const FbPlan p = plan_splits(B * H, N);
+    return (size_t)B * H * p.splits * dd + (size_t)B * H * dd;
+  }
+  const int hg = head_group(H, D);
+  const int groups = B * (H / hg);
+  const FbPlan p = plan_splits(groups, N);
+  return (size_t)groups * p.splits * hg * dd + (size_t)groups * hg * dd;
 }
 
 hipError_t fb_launch(bool bf16_io, int B, int H, int N, int D, float eta, const void* q,
                      const void* k, const void* v, const float* w0, long long w0s, void* o,
                      float* w_out, void* ws, hipStream_t st) {
-  switch (D) {
-    case 16: return fb_launch_d<16>(bf16_io, B, H, N, eta, q, k, v, w0, w0s, o, w_out, ws, st);
-    case 32: return fb_launch_d<32>(bf16_io, B, H, N, eta, q, k, v, w0, w0s, o, w_out, ws, st);
-    case 64: return fb_launch_d<64>(bf16_io, B, H, N, eta, q, k, v, w0, w0s, o, w_out, ws, st);
+  if (!bf16_io) {
+    switch (D) {
+      case 16: return launch_f32<16>(B, H, N, eta, q, k, v, w0, w0s, o, w_out, ws, st);
+      case 32: return launch_f32<32>(B, H, N, eta, q, k, v, w0, w0s, o, w_out, ws, st);
+      case 64: return launch_f32<64>(B, H, N, eta, q, k, v, w0, w0s, o, w_out, ws, st);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  const int hg = head_group(H, D);
+  switch (D * 8 + hg) {
+    case 64 * 8 + 1: return launch_bf16<64, 1>(B, H, N, eta, q, k, v, w0, w0s, o, w_out, ws, st);
+    case 32 * 8 + 2: return launch_bf16<32, 2>(B, H, N, eta, q, k, v, w0, w0s, o, w_out, ws, st);
+    case 32 * 8 + 1: return launch_bf16<32, 1>(B, H, N, eta, q, k, v, w0, w0s, o, w_out, ws, st);
+    case 16 * 8 + 4: return launch_bf16<16, 4>(B, H, N, eta, q, k, v, w0, w0s, o, w_out, ws, st);
+    case 16 * 8 + 2: return launch_bf16<16, 2>(B, H, N, eta, q, k, v, w0, w0s, o, w_out, ws, st);
+    case 16 * 8 + 1: return launch_bf16<16, 1>(B, H, N, eta, q, k, v, w0, w0s, o, w_out, ws, st);
     default: return hipErrorInvalidValue;
   }
 }

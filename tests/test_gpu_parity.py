@@ -319,3 +319,40 @@ def test_runs_on_a_side_stream():
         out = lib.ttt_forward_chunked_causal(q, k, v, w0, wl.chunk, wl.eta)
     s.synchronize()
     assert slice_err(host(out), oracle_full(x)[0]) <= BF16_TOL
+
+
+@pytest.mark.parametrize("wl", [W["hvit3t_stage1_fullbatch"].with_(B=4, N=3136, seed=121),
+                                W["vit3s_fullbatch"].with_(B=3, N=196, H=6, seed=122),
+                                W["hvit3t_stage1_fullbatch"].with_(B=2, N=700, H=3, D=16, seed=123)],
+                         ids=lambda w: f"B{w.B}N{w.N}H{w.H}D{w.D}")
+def test_fullbatch_repeated_calls_identical(wl):
+    """Repeated calls on one workspace give bit-identical results (fixed-order split reduction) at
+    the bf16 bar, for head groups of 1, 2 and 4 heads and a ragged token split."""
+    lib = T()
+    x = synth.make_inputs(wl)
+    q, k, v = dev(x.q, "bf16"), dev(x.k, "bf16"), dev(x.v, "bf16")
+    w0 = torch.from_numpy(x.w0).cuda()
+    need = lib.ttt_workspace_size(lib.TTT_OP_FULLBATCH, lib.TTT_BF16, wl.B, wl.H, wl.N, wl.D)
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda")  # garbage, not zeros
+    outs = []
+    for _ in range(3):
+        outs.append(host(lib.ttt_forward_fullbatch(q, k, v, w0, wl.eta, workspace=ws)))
+        torch.cuda.synchronize()
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[1], outs[2])
+    assert slice_err(outs[0], oracle_full(x)[0]) <= BF16_TOL
+
+
+def test_fullbatch_workspace_reuse_with_new_inputs():
+    """A workspace reused by a second call with different inputs gives that call's result (no value
+    from the first call's partial gradients or W* leaks into the second)."""
+    lib = T()
+    wa = W["hvit3t_stage1_fullbatch"].with_(B=8, N=3136, seed=131)
+    wb = wa.with_(seed=132)
+    need = lib.ttt_workspace_size(lib.TTT_OP_FULLBATCH, lib.TTT_BF16, wa.B, wa.H, wa.N, wa.D)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    for wl in (wa, wb, wa):
+        x = synth.make_inputs(wl)
+        q, k, v = dev(x.q, "bf16"), dev(x.k, "bf16"), dev(x.v, "bf16")
+        out = host(lib.ttt_forward_fullbatch(q, k, v, torch.from_numpy(x.w0).cuda(), wl.eta, workspace=ws))
+        torch.cuda.synchronize()
+        assert slice_err(out, oracle_full(x)[0]) <= BF16_TOL
