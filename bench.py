@@ -28,11 +28,11 @@ if ROOT not in sys.path:
 SUITE = ["hvit3t_stage1_fullbatch", "vittt_bidir_1280", "ttt_linear_causal_16k", "ttt_mlp_causal_8k"]
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, TFLOP/s
-KERNEL_SOURCES = {              # kernel source of each layer (for the traffic-counter freshness check)
-    "fullbatch": "test_sequence_layers_amd/csrc/fullbatch.hip",
-    "bidir": "test_sequence_layers_amd/csrc/chunked.hip",
-    "causal": "test_sequence_layers_amd/csrc/chunked.hip",
-    "mlp": "test_sequence_layers_amd/csrc/mlp.hip",
+KERNEL_SOURCES = {              # kernel sources of each layer (for the traffic-counter freshness check)
+    "fullbatch": ["test_sequence_layers_amd/csrc/fullbatch.hip", "test_sequence_layers_amd/csrc/device.hpp"],
+    "bidir": ["test_sequence_layers_amd/csrc/chunked.hip", "test_sequence_layers_amd/csrc/device.hpp"],
+    "causal": ["test_sequence_layers_amd/csrc/chunked.hip", "test_sequence_layers_amd/csrc/device.hpp"],
+    "mlp": ["test_sequence_layers_amd/csrc/mlp.hip", "test_sequence_layers_amd/csrc/device.hpp"],
 }
 
 
@@ -46,8 +46,11 @@ def alg_flops(wl) -> float:
 
 
 def source_hash(op: str) -> str:
-    with open(os.path.join(ROOT, KERNEL_SOURCES[op]), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[op]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def load_traffic(op: str):
@@ -145,6 +148,48 @@ def copy_calibration(torch, reps: int = 5) -> None:
     print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "reps": reps}))
 
 
+def counter_means(path: str) -> dict:
+    """Mean Counter_Value (KiB) per kernel name of a rocprofv3 --pmc counter_collection.csv."""
+    import csv
+
+    acc = {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            acc.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def write_traffic(pmc_dir: str) -> int:
+    """Turn rocprofv3 FETCH_SIZE / WRITE_SIZE runs into profiles/traffic_<op>.json (HBM bytes per
+    layer launch). Expects <pmc_dir>/pmc_<layer>_<COUNTER>/run_counter_collection.csv for every
+    suite layer and pmc_copy_<COUNTER> from `--copy-calibration`; each counter is scaled by
+    (bytes the 1 GiB copy moved) / (what the counter read for that copy)."""
+    from test_sequence_layers_amd import synth
+
+    def csv_path(tag, counter):
+        return os.path.join(pmc_dir, f"pmc_{tag}_{counter}", "run_counter_collection.csv")
+
+    scale = {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        copy = [v for k, v in counter_means(csv_path("copy", counter)).items() if "copyBuffer" in k]
+        scale[counter] = (1 << 30) / (copy[0] * 1024.0)
+    for name in SUITE:
+        wl = synth.WORKLOADS[name]
+        kernels = {}
+        for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+            for k, kib in counter_means(csv_path(name, counter)).items():
+                if "ttt::" in k or "_ZN3ttt" in k:
+                    kernels.setdefault(k, {})[counter] = kib * 1024.0 * scale[counter]
+        total = sum(v.get("FETCH_SIZE", 0.0) + v.get("WRITE_SIZE", 0.0) for v in kernels.values())
+        rec = {"layer": name, "op": wl.op, "traffic_bytes_per_launch": total,
+               "algorithmic_bytes_per_launch": wl.io_bytes, "counter_scale": scale,
+               "per_kernel_bytes": kernels, "source_sha256": source_hash(wl.op)}
+        with open(os.path.join(ROOT, "profiles", f"traffic_{wl.op}.json"), "w") as f:
+            json.dump(rec, f, indent=1)
+        print(f"{name}: {total / 1e6:.2f} MB per launch (algorithmic {wl.io_bytes / 1e6:.2f} MB)")
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -153,7 +198,10 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--layers", default=",".join(SUITE), help="comma-separated subset of the suite (profiling)")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--write-traffic", metavar="PMC_DIR", help="write profiles/traffic_<op>.json from counter runs")
     args = ap.parse_args()
+    if args.write_traffic:
+        return write_traffic(args.write_traffic)
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); every (batch, head) "
               "pair is independent, so N GPUs would each run this step on their own shard.", file=sys.stderr)
