@@ -325,7 +325,10 @@ __global__ __launch_bounds__(D / 16 * 64) void chunk_scan_bf16(
     if constexpr (MODE == kCausal) {
       // O_p = Q_p W_s - a * sum_{p' <= p} tril(P_{p p'}) E_{p'},  P = Q K^T.
       for (int p = 0; p < NP; ++p) {
-        f32x4 acc = rows_times_state<D, P>(sQ, 16 * p, W, zero4(), r, g);
+        // Q_p W_s and the masked term get separate accumulators: a 16x16x16 product must not
+        // accumulate onto a 16x16x32 product's result (on gfx950 that chain read a stale value).
+        const f32x4 qw = rows_times_state<D, P>(sQ, 16 * p, W, zero4(), r, g);
+        f32x4 acc = zero4();
         for (int pp = 0; pp <= p; ++pp) {
           // Pt[t' = 16pp + 4g + j][t = 16p + r] = k_t' . q_t
           f32x4 pt = zero4();
@@ -342,7 +345,7 @@ __global__ __launch_bounds__(D / 16 * 64) void chunk_scan_bf16(
           // A = -a P (row t = lane r, k = t' = 4g + j), B = E_{p'} (k = t', column = lane r).
           acc = mma16(to_bf16x4_scaled(pt, -a), to_bf16x4(E[pp]), acc);
         }
-        for (int j = 0; j < 4; ++j) sO[(16 * p + 4 * g + j) * P + 16 * w + r] = (bf16)acc[j];
+        for (int j = 0; j < 4; ++j) sO[(16 * p + 4 * g + j) * P + 16 * w + r] = (bf16)(qw[j] + acc[j]);
       }
       update_state<D, NP, P>(W, E, sK, a, r, g);
     } else {

@@ -3,21 +3,30 @@
 // gist.science, "Methodologie" item 3).
 //
 // Inner model f(x) = GELU(x W1) W2, W1 [D, Dh], W2 [Dh, D], loss 1/2 ||f(k) - v||^2 per token.
-// Per chunk of b tokens with start state (W1, W2), all gradients taken at the start state
-// (dual form of the primal per-token definition):
+// Per chunk of b tokens with start state (W1, W2), all gradients taken at the start state:
 //   Z1 = K W1, X2 = GELU(Z1), E = X2 W2 - V, D1 = (E W2^T) * GELU'(Z1)
-//   Z1q = Q W1 - a tril(Q K^T) D1,  X2q = GELU(Z1q),  O = X2q W2 - a tril(X2q X2^T) E
-//   W1 <- W1 - a K^T D1,  W2 <- W2 - a X2^T E,   a = eta / b, tril keeps the diagonal.
+//   W1' = W1 - a K^T D1,  W2' = W2 - a X2^T E,   a = eta / b
+// and token t is read out with the start state minus a times the gradients of tokens t' <= t.
+// Written with the END state of the chunk (W1', W2') this read-out is
+//   Z1q = Q W1' + a striu(Q K^T) D1,  X2q = GELU(Z1q),  O = X2q W2' + a striu(X2q X2^T) E
+// (striu keeps t' > t), which is the same quantity: Q W1 - a tril(Q K^T) D1 = Q W1' + a (Q K^T -
+// tril(Q K^T)) D1. The end state of chunk c is the start state of chunk c + 1, so the read-out of
+// chunk c is computed in the same pass as chunk c + 1's forward, sharing its weight operands.
 //
 // One workgroup per (batch, head), 8 waves; wave w owns hidden units [32w, 32w + 32): its slice
 // of W1 (columns), of W2 (rows) and a second copy of its W2 slice in transposed accumulator
-// layout (needed as the operand of E W2^T). All three stay in MFMA accumulator registers for the
-// whole sequence and are updated in place by MFMA. The per-chunk products are computed
-// transposed (hidden x token) so each product's accumulator tile feeds the next product's B
-// operand directly; only the small per-chunk activations (X2, D1, E: tokens x features, bf16) go
-// through LDS for transposes. Cross-wave sums over the hidden dimension (Z2 and the read-out)
-// use LDS in a fixed wave order, so results are deterministic. K, V, Q of a chunk are staged
-// through double-buffered LDS; the next chunk's loads are issued before the current chunk's work.
+// layout (the operand of E W2^T). All three stay in MFMA accumulator registers for the whole
+// sequence and are updated in place by MFMA. Z1, X2 and D1 are produced as [token][hidden]
+// accumulator tiles, which are directly the operands of the weight updates; the one transpose
+// needed (X2^T, for the contraction over hidden units) is a product with an identity tile. The
+// cross-wave sums over hidden units (Z2 and the read-out) go through LDS in a fixed wave order,
+// so results are deterministic. Two workgroup barriers per chunk; K, V, Q are staged through a
+// three-deep LDS ring, each chunk's loads issued two chunks ahead.
+//
+// No 16x16x16 product accumulates onto the result of a 16x16x32 product: on gfx950 such a
+// mixed-shape accumulator chain was measured to read a stale accumulator (wrong results that
+// depended on the instruction schedule), so terms of different shapes get separate accumulators
+// and are added in registers.
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -30,11 +39,21 @@ constexpr int kCh = 16;       // tokens per chunk
 constexpr int kWaves = 8;
 constexpr int kHw = kDh / kWaves;  // hidden units per wave
 constexpr int kNh = kHw / 16;      // 16-unit hidden tiles per wave
-constexpr int kP = kD + 8;         // pitch of the K/V/Q tiles (elements)
-constexpr int kPt = 24;            // pitch of [row][token] tiles (16 tokens + pad)
+constexpr int kP = kD + 8;         // pitch of [token][feature] tiles (elements)
+constexpr int kPt = kCh + 8;       // pitch of [feature][token] tiles
+constexpr int kRing = 3;           // K/V/Q staging depth
+constexpr int kSlots = 9;          // partial tiles per wave: Z2^T x4, O^T x4, N2^T
 
-__device__ __forceinline__ float gelu_f(float x) {
-  return 0.5f * x * (1.f + erff(x * 0.70710678118654752440f));
+constexpr float kInvSqrt2 = 0.70710678118654752440f;
+constexpr float kInvSqrt2Pi = 0.39894228040143267794f;
+constexpr float kNegHalfLog2e = -0.72134752044448170368f;  // -log2(e) / 2
+
+// GELU(x) = x Phi(x) (exact erf form) and GELU'(x) = Phi(x) + x phi(x).
+__device__ __forceinline__ float gelu_f(float x) { return 0.5f * x * (1.f + erff(x * kInvSqrt2)); }
+__device__ __forceinline__ void gelu_and_slope(float x, float& y, float& dy) {
+  const float cdf = 0.5f * (1.f + erff(x * kInvSqrt2));
+  y = x * cdf;
+  dy = cdf + x * kInvSqrt2Pi * __builtin_amdgcn_exp2f(x * x * kNegHalfLog2e);
 }
 __device__ __forceinline__ bf16x8 cat_tiles(f32x4 lo, f32x4 hi) {
   return cat8(to_bf16x4(lo), to_bf16x4(hi));
@@ -44,12 +63,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ w1, const float* __restrict__ w2, long long wbs, int H, int N,
     float a, bf16* __restrict__ o, float* __restrict__ w1_out, float* __restrict__ w2_out) {
-  __shared__ __align__(16) bf16 sKVQ[2][3][kCh * kP];
-  __shared__ __align__(16) bf16 sX2[kWaves * kHw * kPt];  // -a X2^T per wave, [hidden][token]
-  __shared__ __align__(16) bf16 sD1[kWaves * kHw * kPt];  // -a D1^T per wave, [hidden][token]
-  __shared__ __align__(16) bf16 sE[kD * kPt];             // E^T, [feature][token]
-  __shared__ __align__(16) f32x4 sRed[kWaves * 5 * 64];   // per-wave partial tiles, lane-private
-  __shared__ __align__(16) bf16x4 sEt[4 * 64];            // E^T tiles, lane-private accumulator layout
+  __shared__ __align__(16) bf16 sKVQ[kRing][3][kCh * kP];
+  __shared__ __align__(16) bf16 sE[2][kCh * kP];           // E [token][out]
+  __shared__ __align__(16) bf16 sEt[2][kD * kPt];          // E^T [out][token]
+  __shared__ __align__(16) f32x4 sRed[kWaves * kSlots * 64];  // lane-private partial tiles
 
   const int bh = blockIdx.x, b = bh / H, h = bh % H;
   const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
@@ -69,156 +86,154 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
         W2t[n][m][j] = W2g[(hid0 + 16 * n + 4 * g + j) * kD + 16 * m + r];
         W2x[m][n][j] = W2g[(hid0 + 16 * n + r) * kD + 16 * m + 4 * g + j];
       }
+  bf16x4 ident;  // identity tile as the B operand: lane holds I[4g + i][r]
+  for (int i = 0; i < 4; ++i) ident[i] = (bf16)(4 * g + i == r ? 1.f : 0.f);
 
-  bf16* myX2 = sX2 + w * kHw * kPt;
-  bf16* myD1 = sD1 + w * kHw * kPt;
   const int C = N / kCh;
   const long long head0 = (long long)b * N * ts + (long long)h * kD;
-
   // Staging: threads 0..383 each move one 16-byte piece of K, V or Q (16 rows x 8 pieces each).
-  // Chunk c is read from LDS buffer c & 1; chunk c + 1 is loaded into registers at the start of
-  // iteration c and written to the other buffer at its end.
   const int t = threadIdx.x;
   const int prow = (t & 127) >> 3, pcol = (t & 7) * 8, which = t >> 7;
-  const bf16* psrc = t < 128 ? k : (t < 256 ? v : q);
-  if (t < 384) st16(&sKVQ[0][which][prow * kP + pcol], ld16(psrc + head0 + prow * ts + pcol));
+  const bf16* psrc = (t < 128 ? k : (t < 256 ? v : q)) + head0 + prow * ts + pcol;
+  if (t < 384) {
+    st16(&sKVQ[0][which][prow * kP + pcol], ld16(psrc));
+    if (C > 1) st16(&sKVQ[1][which][prow * kP + pcol], ld16(psrc + kCh * ts));
+  }
+  __syncthreads();
 
-  for (int c = 0; c < C; ++c) {
-    const long long tok0 = head0 + (long long)c * kCh * ts;
-    const bf16* sK = sKVQ[c & 1][0];
-    const bf16* sV = sKVQ[c & 1][1];
-    const bf16* sQ = sKVQ[c & 1][2];
+  bf16x4 d1p[kNh];  // a * D1 of the previous chunk, [token][hidden] tiles
+  bf16x8 x2tp;      // X2^T of the previous chunk, [hidden][token] tiles (both, c-layout k map)
+  for (int n = 0; n < kNh; ++n) d1p[n] = bf16x4{};
+  x2tp = bf16x8{};
+
+  for (int c = 0; c <= C; ++c) {
+    const bool fwd = c < C, rd = c > 0;  // forward of chunk c, read-out of chunk c - 1
+    const bool pre = t < 384 && c + 2 < C;
     uint4 pf = make_uint4(0u, 0u, 0u, 0u);
-    const bool pre = t < 384 && c + 1 < C;
-    if (pre) pf = ld16(psrc + tok0 + kCh * ts + prow * ts + pcol);
-    __syncthreads();
+    if (pre) pf = ld16(psrc + (long long)(c + 2) * kCh * ts);
+    const bf16* sK = sKVQ[c % kRing][0];
+    const bf16* sV = sKVQ[c % kRing][1];
+    const bf16* sKp = sKVQ[(c + 2) % kRing][0];  // chunk c - 1
+    const bf16* sQp = sKVQ[(c + 2) % kRing][2];
+    bf16* sEc = sE[c & 1];
+    bf16* sEtc = sEt[c & 1];
+    const bf16* sEtp = sEt[(c + 1) & 1];
 
-    // Z1^T (hidden x token): A = W1^T from W1t, B = K^T rows (c-layout k map).
-    f32x4 X2[kNh], Gp[kNh];
-    {
-      bf16x8 kb[2];
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16* pk = &sK[r * kP + 32 * ks + 4 * g];
-        kb[ks] = cat8(ld4(pk), ld4(pk + 16));
-      }
+    // ---------------- phase 1: products with the current weights
+    bf16x8 w1b[2][kNh];  // W1 tiles (k = features, c-layout k map)
+    for (int ks = 0; ks < 2; ++ks)
+      for (int n = 0; n < kNh; ++n) w1b[ks][n] = cat_tiles(W1t[2 * ks][n], W1t[2 * ks + 1][n]);
+    if (rd) {
+      // M[t'][t] = k_t' . q_t of chunk c - 1, kept for t' > t.
+      f32x4 mt = zero4();
+      for (int ks = 0; ks < 2; ++ks)
+        mt = mma32(ld8(&sKp[r * kP + 32 * ks + 8 * g]), ld8(&sQp[r * kP + 32 * ks + 8 * g]), mt);
+      for (int j = 0; j < 4; ++j)
+        if (4 * g + j <= r) mt[j] = 0.f;
+      const bf16x4 mb = to_bf16x4(mt);
+      // Z1q^T [hidden][token] = W1^T Q^T + a D1^T M.
+      f32x4 X2q[kNh];
       for (int n = 0; n < kNh; ++n) {
         f32x4 z = zero4();
-        for (int ks = 0; ks < 2; ++ks) z = mma32(cat_tiles(W1t[2 * ks][n], W1t[2 * ks + 1][n]), kb[ks], z);
+        for (int ks = 0; ks < 2; ++ks) {
+          const bf16* pq = &sQp[r * kP + 32 * ks + 4 * g];
+          z = mma32(w1b[ks][n], cat8(ld4(pq), ld4(pq + 16)), z);
+        }
+        const f32x4 zd = mma16(d1p[n], mb, zero4());  // own accumulator (no mixed-shape chain)
+        for (int j = 0; j < 4; ++j) X2q[n][j] = gelu_f(z[j] + zd[j]);
+      }
+      const bf16x8 x2q = cat_tiles(X2q[0], X2q[1]);
+      // O^T partial [out][token] = W2^T X2q^T; N2^T partial [t'][t] = X2 X2q^T.
+      for (int o2 = 0; o2 < 4; ++o2)
+        sRed[(w * kSlots + 4 + o2) * 64 + l] = mma32(cat_tiles(W2t[0][o2], W2t[1][o2]), x2q, zero4());
+      sRed[(w * kSlots + 8) * 64 + l] = mma32(x2tp, x2q, zero4());
+    }
+    f32x4 Gp[kNh];
+    bf16x4 x2n[kNh];  // -a X2, [token][hidden] tiles
+    if (fwd) {
+      // Z1 [token][hidden] = K W1: A = K rows (c-layout k map), B = W1 tiles.
+      f32x4 xt[kNh];
+      for (int n = 0; n < kNh; ++n) {
+        f32x4 z = zero4();
+        for (int ks = 0; ks < 2; ++ks) {
+          const bf16* pk = &sK[r * kP + 32 * ks + 4 * g];
+          z = mma32(cat8(ld4(pk), ld4(pk + 16)), w1b[ks][n], z);
+        }
+        f32x4 x2;
         for (int j = 0; j < 4; ++j) {
-          const float x = z[j];
-          const float cdf = 0.5f * (1.f + erff(x * 0.70710678118654752440f));
-          X2[n][j] = x * cdf;                                                       // GELU
-          Gp[n][j] = cdf + x * expf(-0.5f * x * x) * 0.39894228040143267794f;      // GELU'
+          float y, dy;
+          gelu_and_slope(z[j], y, dy);
+          x2[j] = y;
+          Gp[n][j] = dy;
+        }
+        xt[n] = mma16(to_bf16x4(x2), ident, zero4());  // X2^T [hidden][token]
+        x2n[n] = to_bf16x4_scaled(x2, -a);
+      }
+      x2tp = cat_tiles(xt[0], xt[1]);
+      // Z2^T partial [out][token] over this wave's hidden units.
+      for (int o2 = 0; o2 < 4; ++o2)
+        sRed[(w * kSlots + o2) * 64 + l] = mma32(cat_tiles(W2t[0][o2], W2t[1][o2]), x2tp, zero4());
+    }
+    __syncthreads();
+
+    // ---------------- phase 2: cross-wave sums (fixed wave order)
+    if (fwd && w < 4) {  // E^T tile w = Z2^T - V^T, stored as E [token][out] and E^T [out][token]
+      f32x4 s = sRed[w * 64 + l];
+      for (int ww = 1; ww < kWaves; ++ww) s = s + sRed[(ww * kSlots + w) * 64 + l];
+      const bf16x4 vv = ld4(&sV[r * kP + 16 * w + 4 * g]);
+      bf16x4 eb;
+      for (int j = 0; j < 4; ++j) eb[j] = (bf16)(s[j] - (float)vv[j]);
+      *reinterpret_cast<bf16x4*>(&sEc[r * kP + 16 * w + 4 * g]) = eb;
+      for (int j = 0; j < 4; ++j) sEtc[(16 * w + 4 * g + j) * kPt + r] = eb[j];
+    }
+    if (rd && w >= 4) {  // O^T tile of chunk c - 1 = sum of partials + a E^T striu(X2q X2^T)^T
+      const int o4 = w - 4;
+      f32x4 s = sRed[(4 + o4) * 64 + l];
+      f32x4 n2 = sRed[8 * 64 + l];
+      for (int ww = 1; ww < kWaves; ++ww) {
+        s = s + sRed[(ww * kSlots + 4 + o4) * 64 + l];
+        n2 = n2 + sRed[(ww * kSlots + 8) * 64 + l];
+      }
+      for (int j = 0; j < 4; ++j)
+        if (4 * g + j <= r) n2[j] = 0.f;
+      s = mma16(ld4(&sEtp[(16 * o4 + r) * kPt + 4 * g]), to_bf16x4_scaled(n2, a), s);
+      const long long tokp = head0 + (long long)(c - 1) * kCh * ts;
+      *reinterpret_cast<bf16x4*>(o + tokp + r * ts + 16 * o4 + 4 * g) = to_bf16x4(s);
+    }
+    __syncthreads();
+
+    // ---------------- phase 3: backward and state update of chunk c
+    if (fwd) {
+      // dX2 [token][hidden] = E W2^T: A = E rows (c-layout k map), B = W2x tiles.
+      bf16x8 ea[2];
+      for (int ko = 0; ko < 2; ++ko) {
+        const bf16* pe = &sEc[r * kP + 32 * ko + 4 * g];
+        ea[ko] = cat8(ld4(pe), ld4(pe + 16));
+      }
+      bf16x4 d1n[kNh];  // -a D1 ([token][hidden] tiles)
+      for (int n = 0; n < kNh; ++n) {
+        f32x4 acc = zero4();
+        for (int ko = 0; ko < 2; ++ko) acc = mma32(ea[ko], cat_tiles(W2x[2 * ko][n], W2x[2 * ko + 1][n]), acc);
+        f32x4 d1;
+        for (int j = 0; j < 4; ++j) d1[j] = acc[j] * Gp[n][j];
+        d1n[n] = to_bf16x4_scaled(d1, -a);
+        d1p[n] = to_bf16x4_scaled(d1, a);
+      }
+      // W1 += K^T (-a D1): A = K^T (row feature, k token), B = -a D1.
+      for (int m = 0; m < 4; ++m) {
+        const bf16x4 kt = ld4_col(&sK[(4 * g) * kP + 16 * m + r], kP);
+        for (int n = 0; n < kNh; ++n) W1t[m][n] = mma16(kt, d1n[n], W1t[m][n]);
+      }
+      // W2 += X2^T (-a E) and W2^T += E^T (-a X2): E^T rows give both operands.
+      for (int o2 = 0; o2 < 4; ++o2) {
+        const bf16x4 e = ld4(&sEtc[(16 * o2 + r) * kPt + 4 * g]);
+        for (int n = 0; n < kNh; ++n) {
+          W2t[n][o2] = mma16(x2n[n], e, W2t[n][o2]);
+          W2x[o2][n] = mma16(e, x2n[n], W2x[o2][n]);
         }
       }
     }
-
-    // Z2^T partial (output x token) over this wave's hidden slice: A = W2^T (from W2t), B = X2^T.
-    for (int o2 = 0; o2 < 4; ++o2) {
-      f32x4 acc = zero4();
-      for (int kh = 0; kh < kNh / 2; ++kh)
-        acc = mma32(cat_tiles(W2t[2 * kh][o2], W2t[2 * kh + 1][o2]),
-                    cat_tiles(X2[2 * kh], X2[2 * kh + 1]), acc);
-      sRed[(w * 5 + o2) * 64 + l] = acc;
-    }
-    for (int n = 0; n < kNh; ++n)
-      for (int j = 0; j < 4; ++j) myX2[(16 * n + 4 * g + j) * kPt + r] = (bf16)(-a * X2[n][j]);
-    __syncthreads();
-
-    // Waves 0..3: E^T tile w = sum over waves (fixed order) of Z2^T - V^T; shared as bf16 twice:
-    // [feature][token] rows (sE) and the lane-private accumulator layout (sEt).
-    if (w < 4) {
-      f32x4 s = sRed[w * 64 + l];
-      for (int ww = 1; ww < kWaves; ++ww) s = s + sRed[(ww * 5 + w) * 64 + l];
-      const bf16x4 vv = ld4(&sV[r * kP + 16 * w + 4 * g]);
-      bf16x4 eb;
-      for (int j = 0; j < 4; ++j) {
-        eb[j] = (bf16)(s[j] - (float)vv[j]);
-        sE[(16 * w + 4 * g + j) * kPt + r] = eb[j];
-      }
-      sEt[w * 64 + l] = eb;
-    }
-    __syncthreads();
-
-    // dX2^T = W2 E^T (hidden x token): A = W2 rows (from W2x), B = E^T. D1^T = dX2^T * GELU'(Z1^T).
-    {
-      bf16x8 eb[2];
-      for (int ko = 0; ko < 2; ++ko) eb[ko] = cat8(sEt[(2 * ko) * 64 + l], sEt[(2 * ko + 1) * 64 + l]);
-      for (int n = 0; n < kNh; ++n) {
-        f32x4 acc = zero4();
-        for (int ko = 0; ko < 2; ++ko) acc = mma32(cat_tiles(W2x[2 * ko][n], W2x[2 * ko + 1][n]), eb[ko], acc);
-        for (int j = 0; j < 4; ++j) myD1[(16 * n + 4 * g + j) * kPt + r] = (bf16)(-a * acc[j] * Gp[n][j]);
-      }
-    }
-    // The wave reads its D1 rows back across lanes below. A wave-local LDS wait was measured to be
-    // insufficient here (nondeterministic results), so this is a full workgroup barrier.
-    __syncthreads();
-    // Read-out. Mt[t' = 4g + j][t = r] = k_t' . q_t, kept for t' <= t.
-    f32x4 Mt = zero4();
-    for (int ks = 0; ks < 2; ++ks)
-      Mt = mma32(ld8(&sK[r * kP + 32 * ks + 8 * g]), ld8(&sQ[r * kP + 32 * ks + 8 * g]), Mt);
-    for (int j = 0; j < 4; ++j)
-      if (4 * g + j > r) Mt[j] = 0.f;
-    const bf16x4 Mb = to_bf16x4(Mt);
-    // Z1q^T = W1^T Q^T + (-a D1^T) tril(Q K^T)^T (the wave's own D1 rows, written above).
-    f32x4 X2q[kNh];
-    {
-      bf16x8 qb[2];
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16* pq = &sQ[r * kP + 32 * ks + 4 * g];
-        qb[ks] = cat8(ld4(pq), ld4(pq + 16));
-      }
-      for (int n = 0; n < kNh; ++n) {
-        f32x4 z = zero4();
-        for (int ks = 0; ks < 2; ++ks) z = mma32(cat_tiles(W1t[2 * ks][n], W1t[2 * ks + 1][n]), qb[ks], z);
-        z = mma16(ld4(&myD1[(16 * n + r) * kPt + 4 * g]), Mb, z);
-        for (int j = 0; j < 4; ++j) X2q[n][j] = gelu_f(z[j]);
-      }
-    }
-
-    // O^T partial = W2^T X2q^T, and N2^T partial = X2 X2q^T (token x token), this wave's hidden slice.
-    for (int o2 = 0; o2 < 4; ++o2) {
-      f32x4 acc = zero4();
-      for (int kh = 0; kh < kNh / 2; ++kh)
-        acc = mma32(cat_tiles(W2t[2 * kh][o2], W2t[2 * kh + 1][o2]),
-                    cat_tiles(X2q[2 * kh], X2q[2 * kh + 1]), acc);
-      sRed[(w * 5 + o2) * 64 + l] = acc;
-    }
-    {
-      f32x4 acc = zero4();
-      for (int kh = 0; kh < kNh / 2; ++kh)
-        acc = mma32(cat_tiles(X2[2 * kh], X2[2 * kh + 1]), cat_tiles(X2q[2 * kh], X2q[2 * kh + 1]), acc);
-      sRed[(w * 5 + 4) * 64 + l] = acc;
-    }
-    __syncthreads();
-
-    // Waves 0..3 finish output tile w: O^T = sum of partials - a E^T tril(X2q X2^T)^T; store.
-    if (w < 4) {
-      f32x4 s = sRed[w * 64 + l];
-      f32x4 n2 = sRed[4 * 64 + l];
-      for (int ww = 1; ww < kWaves; ++ww) {
-        s = s + sRed[(ww * 5 + w) * 64 + l];
-        n2 = n2 + sRed[(ww * 5 + 4) * 64 + l];
-      }
-      for (int j = 0; j < 4; ++j)
-        if (4 * g + j > r) n2[j] = 0.f;
-      s = mma16(ld4(&sE[(16 * w + r) * kPt + 4 * g]), to_bf16x4_scaled(n2, -a), s);
-      *reinterpret_cast<bf16x4*>(o + tok0 + r * ts + 16 * w + 4 * g) = to_bf16x4(s);
-    }
-
-    // State updates at the end of the chunk (the read-out above used the start state).
-    for (int n = 0; n < kNh; ++n) {
-      const bf16x4 d1 = ld4(&myD1[(16 * n + r) * kPt + 4 * g]);   // (-a D1)[t][hidden]
-      const bf16x4 x2 = ld4(&myX2[(16 * n + r) * kPt + 4 * g]);   // (-a X2)[t][hidden]
-      for (int m = 0; m < 4; ++m)  // W1 += K^T (-a D1)
-        W1t[m][n] = mma16(ld4_col(&sK[(4 * g) * kP + 16 * m + r], kP), d1, W1t[m][n]);
-      for (int o2 = 0; o2 < 4; ++o2) {
-        const bf16x4 e = ld4(&sE[(16 * o2 + r) * kPt + 4 * g]);  // E[t][out]
-        W2t[n][o2] = mma16(x2, e, W2t[n][o2]);   // W2   += (-a X2)^T E
-        W2x[o2][n] = mma16(e, x2, W2x[o2][n]);   // W2^T += E^T (-a X2)
-      }
-    }
-    if (pre) st16(&sKVQ[(c + 1) & 1][which][prow * kP + pcol], pf);
+    if (pre) st16(&sKVQ[(c + 2) % kRing][which][prow * kP + pcol], pf);
   }
 
   const long long bhl = bh;

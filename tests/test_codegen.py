@@ -1,0 +1,85 @@
+"""Checks on the gfx950 machine code of the HIP kernels (CPU only: hipcc cross-compiles).
+
+On gfx950, a 16x16x16 MFMA that takes as its accumulator input the result of a 16x16x32 MFMA
+(a "mixed-shape accumulator chain") was measured to read a stale accumulator: results were wrong
+in a way that depended on the instruction schedule. The kernels therefore keep terms of different
+MFMA shapes in separate accumulators. This test compiles every kernel source to gfx950 assembly
+with the library's own flags and fails if any such chain appears in the generated code.
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from test_sequence_layers_amd import build as B
+
+HIPCC = B.HIPCC if os.path.exists(B.HIPCC) else shutil.which("hipcc")
+KERNEL_SOURCES = [s for s in B.SOURCES if s != "abi.hip"]
+
+
+def _regs(tok):
+    tok = tok.strip()
+    m = re.match(r"([va])\[(\d+):(\d+)\]$", tok)
+    if m:
+        return {(m.group(1), r) for r in range(int(m.group(2)), int(m.group(3)) + 1)}
+    m = re.match(r"([va])(\d+)$", tok)
+    return {(m.group(1), int(m.group(2)))} if m else set()
+
+
+def mixed_shape_chains(asm_lines):
+    """(distance, producer, consumer) for every MFMA whose accumulator input (SrcC) was last
+    written by an MFMA of a different opcode within the same basic block."""
+    ins = [ln.strip() for ln in asm_lines]
+    ins = [ln for ln in ins if ln and not ln.startswith((";", "."))]
+    hits = []
+    for i, line in enumerate(ins):
+        if not line.startswith("v_mfma"):
+            continue
+        op, rest = line.split(None, 1)
+        ops = [t.strip() for t in rest.split(",")]
+        if len(ops) < 4:
+            continue
+        src_c = _regs(ops[3])
+        if not src_c:
+            continue
+        for j in range(i - 1, -1, -1):
+            prev = ins[j]
+            if prev.endswith(":") or prev.startswith(("s_cbranch", "s_branch", "s_barrier", "s_setpc")):
+                break
+            if " " not in prev:
+                continue
+            pop, prest = prev.split(None, 1)
+            if pop.startswith(("ds_write", "global_store", "buffer_store", "scratch_store", "s_")):
+                continue
+            if _regs(prest.split(",")[0]) & src_c:
+                if pop.startswith("v_mfma") and pop != op:
+                    hits.append((i - j, pop, op))
+                break
+    return hits
+
+
+def test_scanner_finds_a_planted_chain():
+    planted = [
+        "v_mfma_f32_16x16x32_bf16 v[10:13], v[0:3], v[4:7], 0",
+        "v_cvt_pk_bf16_f32 v20, v21, v22",
+        "v_mfma_f32_16x16x16_bf16 v[10:13], v[14:15], v[16:17], v[10:13]",
+        "v_mov_b32_e32 v30, 0",
+        "v_mfma_f32_16x16x32_bf16 v[40:43], v[0:3], v[4:7], 0",
+        "v_mov_b32_e32 v40, 0",  # an intervening write breaks the dependency
+        "v_mfma_f32_16x16x16_bf16 v[40:43], v[14:15], v[16:17], v[40:43]",
+    ]
+    assert mixed_shape_chains(planted) == [(2, "v_mfma_f32_16x16x32_bf16", "v_mfma_f32_16x16x16_bf16")]
+
+
+@pytest.mark.skipif(HIPCC is None, reason="hipcc not available")
+@pytest.mark.parametrize("src", KERNEL_SOURCES)
+def test_no_mixed_shape_mfma_accumulator_chains(src, tmp_path):
+    out = tmp_path / (src + ".s")
+    cmd = [HIPCC, *[f for f in B.FLAGS if f != "-fPIC"], "--cuda-device-only", "-S",
+           os.path.join(B.CSRC, src), "-o", str(out)]
+    p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    assert p.returncode == 0, p.stdout[-2000:]
+    hits = mixed_shape_chains(out.read_text().splitlines())
+    assert not hits, f"{src}: mixed-shape MFMA accumulator chains {hits[:5]}"
