@@ -21,7 +21,8 @@
 // needed (X2^T, for the contraction over hidden units) is a product with an identity tile. The
 // cross-wave sums over hidden units (Z2 and the read-out) go through LDS in a fixed wave order,
 // so results are deterministic. Two workgroup barriers per chunk; K, V, Q are staged through a
-// three-deep LDS ring, each chunk's loads issued two chunks ahead.
+// four-deep LDS ring: each chunk's global loads are issued three chunks ahead into one of two
+// alternating register sets and stored to LDS two chunks ahead.
 //
 // No 16x16x16 product accumulates onto the result of a 16x16x32 product: on gfx950 such a
 // mixed-shape accumulator chain was measured to read a stale accumulator (wrong results that
@@ -41,19 +42,68 @@ constexpr int kHw = kDh / kWaves;  // hidden units per wave
 constexpr int kNh = kHw / 16;      // 16-unit hidden tiles per wave
 constexpr int kP = kD + 8;         // pitch of [token][feature] tiles (elements)
 constexpr int kPt = kCh + 8;       // pitch of [feature][token] tiles
-constexpr int kRing = 3;           // K/V/Q staging depth
-constexpr int kSlots = 9;          // partial tiles per wave: Z2^T x4, O^T x4, N2^T
+constexpr int kRing = 4;           // K/V/Q staging depth
+constexpr int kSlots = 8;          // partial tiles per wave: Z2^T x4, O^T x4
 
 constexpr float kInvSqrt2 = 0.70710678118654752440f;
 constexpr float kInvSqrt2Pi = 0.39894228040143267794f;
 constexpr float kNegHalfLog2e = -0.72134752044448170368f;  // -log2(e) / 2
 
-// GELU(x) = x Phi(x) (exact erf form) and GELU'(x) = Phi(x) + x phi(x).
-__device__ __forceinline__ float gelu_f(float x) { return 0.5f * x * (1.f + erff(x * kInvSqrt2)); }
-__device__ __forceinline__ void gelu_and_slope(float x, float& y, float& dy) {
-  const float cdf = 0.5f * (1.f + erff(x * kInvSqrt2));
-  y = x * cdf;
-  dy = cdf + x * kInvSqrt2Pi * __builtin_amdgcn_exp2f(x * x * kNegHalfLog2e);
+// GELU(x) = x Phi(x) with Phi(x) = (1 + erf(x / sqrt 2)) / 2 (exact erf form) and
+// GELU'(x) = Phi(x) + x phi(x), phi the standard normal density.
+// Fast path, used when every lane's argument has x^2 <= 2 (|x / sqrt 2| <= 1): erf(u) = u P(u^2)
+// with P the degree-5 least-squares polynomial for erf(u)/u on u^2 in [0, 1] (fitted on Chebyshev
+// nodes; max abs error of erf 1.1e-7 in fp32 Horner form), so Phi(x) = 1/2 + x R(x^2) with
+// R(t) = P(t / 2) / (2 sqrt 2). Otherwise the library erf is used.
+constexpr float kErfP[6] = {1.1283791065216064f, -0.37612348794937134f, 0.11280364543199539f,
+                            -0.026716385036706924f, 0.004923277534544468f, -0.0005654105916619301f};
+constexpr float kInvTwoSqrt2 = 0.35355339059327376220f;
+constexpr float kR0 = kErfP[0] * kInvTwoSqrt2, kR1 = kErfP[1] * kInvTwoSqrt2 / 2.f,
+                kR2 = kErfP[2] * kInvTwoSqrt2 / 4.f, kR3 = kErfP[3] * kInvTwoSqrt2 / 8.f,
+                kR4 = kErfP[4] * kInvTwoSqrt2 / 16.f, kR5 = kErfP[5] * kInvTwoSqrt2 / 32.f;
+
+__device__ __forceinline__ float cdf_fast(float x, float t) {  // t = x * x <= 2
+  float r = fmaf(kR5, t, kR4);
+  r = fmaf(r, t, kR3);
+  r = fmaf(r, t, kR2);
+  r = fmaf(r, t, kR1);
+  r = fmaf(r, t, kR0);
+  return fmaf(x, r, 0.5f);
+}
+__device__ __forceinline__ float cdf_lib(float x) { return 0.5f * (1.f + erff(x * kInvSqrt2)); }
+
+// X = GELU(Z) for two [4]-element tiles per lane.
+__device__ __forceinline__ void gelu_tiles(const f32x4* z, f32x4* y) {
+  float tmax = 0.f;
+  for (int n = 0; n < kNh; ++n)
+    for (int j = 0; j < 4; ++j) tmax = fmaxf(tmax, z[n][j] * z[n][j]);
+  if (!__any(tmax > 2.f)) {
+    for (int n = 0; n < kNh; ++n)
+      for (int j = 0; j < 4; ++j) y[n][j] = z[n][j] * cdf_fast(z[n][j], z[n][j] * z[n][j]);
+  } else {
+    for (int n = 0; n < kNh; ++n)
+      for (int j = 0; j < 4; ++j) y[n][j] = z[n][j] * cdf_lib(z[n][j]);
+  }
+}
+// X = GELU(Z) and S = GELU'(Z) for two tiles per lane.
+__device__ __forceinline__ void gelu_slope_tiles(const f32x4* z, f32x4* y, f32x4* dy) {
+  float tmax = 0.f;
+  for (int n = 0; n < kNh; ++n)
+    for (int j = 0; j < 4; ++j) tmax = fmaxf(tmax, z[n][j] * z[n][j]);
+  f32x4 cdf[kNh];
+  if (!__any(tmax > 2.f)) {
+    for (int n = 0; n < kNh; ++n)
+      for (int j = 0; j < 4; ++j) cdf[n][j] = cdf_fast(z[n][j], z[n][j] * z[n][j]);
+  } else {
+    for (int n = 0; n < kNh; ++n)
+      for (int j = 0; j < 4; ++j) cdf[n][j] = cdf_lib(z[n][j]);
+  }
+  for (int n = 0; n < kNh; ++n)
+    for (int j = 0; j < 4; ++j) {
+      const float x = z[n][j];
+      y[n][j] = x * cdf[n][j];
+      dy[n][j] = fmaf(x * kInvSqrt2Pi, __builtin_amdgcn_exp2f(x * x * kNegHalfLog2e), cdf[n][j]);
+    }
 }
 __device__ __forceinline__ bf16x8 cat_tiles(f32x4 lo, f32x4 hi) {
   return cat8(to_bf16x4(lo), to_bf16x4(hi));
@@ -95,9 +145,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
   const int t = threadIdx.x;
   const int prow = (t & 127) >> 3, pcol = (t & 7) * 8, which = t >> 7;
   const bf16* psrc = (t < 128 ? k : (t < 256 ? v : q)) + head0 + prow * ts + pcol;
+  uint4 pfA = make_uint4(0u, 0u, 0u, 0u), pfB = make_uint4(0u, 0u, 0u, 0u);
   if (t < 384) {
     st16(&sKVQ[0][which][prow * kP + pcol], ld16(psrc));
     if (C > 1) st16(&sKVQ[1][which][prow * kP + pcol], ld16(psrc + kCh * ts));
+    if (C > 2) pfB = ld16(psrc + 2 * kCh * ts);
   }
   __syncthreads();
 
@@ -106,18 +158,18 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
   for (int n = 0; n < kNh; ++n) d1p[n] = bf16x4{};
   x2tp = bf16x8{};
 
-  for (int c = 0; c <= C; ++c) {
+  // One chunk step: forward of chunk c, read-out of chunk c - 1. pf_cur holds chunk c + 2 (loaded
+  // one step earlier); chunk c + 3 is loaded into pf_next.
+  auto step = [&](const int c, uint4& pf_next, const uint4& pf_cur) {
     const bool fwd = c < C, rd = c > 0;  // forward of chunk c, read-out of chunk c - 1
-    const bool pre = t < 384 && c + 2 < C;
-    uint4 pf = make_uint4(0u, 0u, 0u, 0u);
-    if (pre) pf = ld16(psrc + (long long)(c + 2) * kCh * ts);
+    if (t < 384 && c + 3 < C) pf_next = ld16(psrc + (long long)(c + 3) * kCh * ts);
     const bf16* sK = sKVQ[c % kRing][0];
     const bf16* sV = sKVQ[c % kRing][1];
-    const bf16* sKp = sKVQ[(c + 2) % kRing][0];  // chunk c - 1
-    const bf16* sQp = sKVQ[(c + 2) % kRing][2];
+    const bf16* sKp = sKVQ[(c + kRing - 1) % kRing][0];  // chunk c - 1
+    const bf16* sQp = sKVQ[(c + kRing - 1) % kRing][2];
     bf16* sEc = sE[c & 1];
     bf16* sEtc = sEt[c & 1];
-    const bf16* sEtp = sEt[(c + 1) & 1];
+    const bf16* sEtp = sEt[(c + 1) & 1];  // E^T of chunk c - 1
 
     // ---------------- phase 1: products with the current weights
     bf16x8 w1b[2][kNh];  // W1 tiles (k = features, c-layout k map)
@@ -132,7 +184,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
         if (4 * g + j <= r) mt[j] = 0.f;
       const bf16x4 mb = to_bf16x4(mt);
       // Z1q^T [hidden][token] = W1^T Q^T + a D1^T M.
-      f32x4 X2q[kNh];
+      f32x4 Z1q[kNh], X2q[kNh];
       for (int n = 0; n < kNh; ++n) {
         f32x4 z = zero4();
         for (int ks = 0; ks < 2; ++ks) {
@@ -140,34 +192,39 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
           z = mma32(w1b[ks][n], cat8(ld4(pq), ld4(pq + 16)), z);
         }
         const f32x4 zd = mma16(d1p[n], mb, zero4());  // own accumulator (no mixed-shape chain)
-        for (int j = 0; j < 4; ++j) X2q[n][j] = gelu_f(z[j] + zd[j]);
+        Z1q[n] = z + zd;
       }
+      gelu_tiles(Z1q, X2q);
       const bf16x8 x2q = cat_tiles(X2q[0], X2q[1]);
-      // O^T partial [out][token] = W2^T X2q^T; N2^T partial [t'][t] = X2 X2q^T.
-      for (int o2 = 0; o2 < 4; ++o2)
-        sRed[(w * kSlots + 4 + o2) * 64 + l] = mma32(cat_tiles(W2t[0][o2], W2t[1][o2]), x2q, zero4());
-      sRed[(w * kSlots + 8) * 64 + l] = mma32(x2tp, x2q, zero4());
+      // This wave's share of O^T [out][token]: W2^T X2q^T over its hidden units, plus
+      // a E^T striu(X2q X2^T)^T with X2q X2^T summed over the same units (t' > t kept).
+      f32x4 n2 = mma32(x2tp, x2q, zero4());  // [t'][t] = sum_h X2[t'][h] X2q[t][h]
+      for (int j = 0; j < 4; ++j)
+        if (4 * g + j <= r) n2[j] = 0.f;
+      const bf16x4 n2b = to_bf16x4_scaled(n2, a);
+      for (int o2 = 0; o2 < 4; ++o2) {
+        const f32x4 ow = mma32(cat_tiles(W2t[0][o2], W2t[1][o2]), x2q, zero4());
+        const f32x4 oe = mma16(ld4(&sEtp[(16 * o2 + r) * kPt + 4 * g]), n2b, zero4());
+        sRed[(w * kSlots + 4 + o2) * 64 + l] = ow + oe;
+      }
     }
     f32x4 Gp[kNh];
     bf16x4 x2n[kNh];  // -a X2, [token][hidden] tiles
     if (fwd) {
       // Z1 [token][hidden] = K W1: A = K rows (c-layout k map), B = W1 tiles.
-      f32x4 xt[kNh];
+      f32x4 Z1[kNh], X2[kNh], xt[kNh];
       for (int n = 0; n < kNh; ++n) {
         f32x4 z = zero4();
         for (int ks = 0; ks < 2; ++ks) {
           const bf16* pk = &sK[r * kP + 32 * ks + 4 * g];
           z = mma32(cat8(ld4(pk), ld4(pk + 16)), w1b[ks][n], z);
         }
-        f32x4 x2;
-        for (int j = 0; j < 4; ++j) {
-          float y, dy;
-          gelu_and_slope(z[j], y, dy);
-          x2[j] = y;
-          Gp[n][j] = dy;
-        }
-        xt[n] = mma16(to_bf16x4(x2), ident, zero4());  // X2^T [hidden][token]
-        x2n[n] = to_bf16x4_scaled(x2, -a);
+        Z1[n] = z;
+      }
+      gelu_slope_tiles(Z1, X2, Gp);
+      for (int n = 0; n < kNh; ++n) {
+        xt[n] = mma16(to_bf16x4(X2[n]), ident, zero4());  // X2^T [hidden][token]
+        x2n[n] = to_bf16x4_scaled(X2[n], -a);
       }
       x2tp = cat_tiles(xt[0], xt[1]);
       // Z2^T partial [out][token] over this wave's hidden units.
@@ -186,17 +243,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
       *reinterpret_cast<bf16x4*>(&sEc[r * kP + 16 * w + 4 * g]) = eb;
       for (int j = 0; j < 4; ++j) sEtc[(16 * w + 4 * g + j) * kPt + r] = eb[j];
     }
-    if (rd && w >= 4) {  // O^T tile of chunk c - 1 = sum of partials + a E^T striu(X2q X2^T)^T
+    if (rd && w >= 4) {  // O^T tile of chunk c - 1 = sum of the waves' shares
       const int o4 = w - 4;
       f32x4 s = sRed[(4 + o4) * 64 + l];
-      f32x4 n2 = sRed[8 * 64 + l];
-      for (int ww = 1; ww < kWaves; ++ww) {
-        s = s + sRed[(ww * kSlots + 4 + o4) * 64 + l];
-        n2 = n2 + sRed[(ww * kSlots + 8) * 64 + l];
-      }
-      for (int j = 0; j < 4; ++j)
-        if (4 * g + j <= r) n2[j] = 0.f;
-      s = mma16(ld4(&sEtp[(16 * o4 + r) * kPt + 4 * g]), to_bf16x4_scaled(n2, a), s);
+      for (int ww = 1; ww < kWaves; ++ww) s = s + sRed[(ww * kSlots + 4 + o4) * 64 + l];
       const long long tokp = head0 + (long long)(c - 1) * kCh * ts;
       *reinterpret_cast<bf16x4*>(o + tokp + r * ts + 16 * o4 + 4 * g) = to_bf16x4(s);
     }
@@ -233,7 +283,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
         }
       }
     }
-    if (pre) st16(&sKVQ[(c + 2) % kRing][which][prow * kP + pcol], pf);
+    if (t < 384 && c + 2 < C) st16(&sKVQ[(c + 2) % kRing][which][prow * kP + pcol], pf_cur);
+  };
+  for (int c = 0; c <= C; c += 2) {  // two steps per trip: the register sets swap roles
+    step(c, pfA, pfB);
+    if (c + 1 <= C) step(c + 1, pfB, pfA);
   }
 
   const long long bhl = bh;

@@ -204,6 +204,25 @@ def test_mlp_end_states():
     assert np.abs(s2 - r2).max() / np.abs(r2).max() <= BF16_TOL
 
 
+@pytest.mark.parametrize("scale", [25.0, 40.0])
+def test_mlp_large_first_layer_weights(scale):
+    """W1 far above the N(0, 0.02^2) init, so the hidden pre-activations reach |x| > sqrt 2 in many
+    waves: the GELU takes its library-erf path there and its polynomial path elsewhere. eta = 0.1
+    keeps the inner training stable at these weights (at eta = 1 the exact dynamics overflow)."""
+    wl = W["ttt_mlp_causal_8k"].with_(B=1, N=256, H=2, seed=65, eta=0.1)
+    x = synth.make_inputs(wl)
+    w1 = (x.w1 * scale).astype(np.float32)
+    z1 = np.einsum("bnhd,hde->bnhe", x.k64, w1.astype(np.float64))
+    assert np.mean(np.abs(z1) > np.sqrt(2.0)) > 0.005  # the library path is exercised
+    out, s1, s2 = run_gpu(x, w1=w1, want_state=True)
+    ref, r1, r2 = O.mlp_causal(x.q64, x.k64, x.v64, w1, x.w2, wl.eta, wl.chunk)
+    err = slice_err(out, ref)
+    print(f"scale {scale}: err={err:.3e}")
+    assert err <= BF16_TOL
+    assert np.abs(s1 - r1).max() / np.abs(r1).max() <= BF16_TOL
+    assert np.abs(s2 - r2).max() / np.abs(r2).max() <= BF16_TOL
+
+
 @pytest.mark.parametrize("wl", [W["hvit3t_stage1_fullbatch"].with_(B=2, N=300, seed=71),
                                 W["vittt_bidir_1280"].with_(B=1, N=256, seed=72),
                                 W["ttt_linear_causal_16k"].with_(B=1, N=128, H=2, seed=73)],
