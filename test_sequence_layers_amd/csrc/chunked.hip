@@ -36,6 +36,11 @@ namespace {
 
 enum ScanMode { kCausal = 0, kBidir = 1 };
 
+// Segment map record of one (b, h, segment, direction): -Dev as bf16 [D][D] (the MFMA operand of
+// the prefix fold, already negated) followed by R as fp32 [D][D]; kMapFloats<D> floats in all.
+template <int D>
+constexpr int kMapFloats = D * D / 2 + D * D;
+
 // LDS bytes available for the reverse states of one bidirectional scan segment.
 constexpr int kRevLdsBytes = 96 * 1024;
 template <int D>
@@ -170,71 +175,122 @@ __global__ __launch_bounds__(D / 8 * 64) void chunk_compose_bf16(
     update_state<D, NP, P>(X, Y, sK, a, r, g);
   }
 
-  // comp[(bh * S + s)] holds Dev_f, R_f, [Dev_r, R_r], each D x D row-major.
-  float* out = comp + ((long long)bh * S + s) * (BIDIR ? 4 : 2) * DD;
+  // comp[(bh * S + s)] holds the forward map record and, for the bidirectional scan, the
+  // reverse one: -Dev (bf16) then R (fp32), each D x D row-major.
+  float* rec = comp + ((long long)bh * S + s) * (BIDIR ? 2 : 1) * kMapFloats<D>;
+  bf16* ndev_f = reinterpret_cast<bf16*>(rec);
+  float* r_f = rec + DD / 2;
+  bf16* ndev_r = reinterpret_cast<bf16*>(rec + kMapFloats<D>);
+  float* r_r = rec + kMapFloats<D> + DD / 2;
   for (int m = 0; m < NT; ++m)
     for (int j = 0; j < 4; ++j) {
       const int row = 16 * m + 4 * g + j, cc = 16 * col + r;
       if (pwave) {
-        const float dev = (row == cc ? 1.f : 0.f) - X[m][j];
-        out[row * D + cc] = dev;
-        if constexpr (BIDIR) out[2 * DD + cc * D + row] = dev;  // Dev_r = Dev_f^T
+        const bf16 nd = (bf16)(X[m][j] - (row == cc ? 1.f : 0.f));  // -Dev = P - I
+        ndev_f[row * D + cc] = nd;
+        if constexpr (BIDIR) ndev_r[cc * D + row] = nd;  // Dev_r = Dev_f^T
       } else {
-        out[DD + row * D + cc] = X[m][j];
+        r_f[row * D + cc] = X[m][j];
       }
     }
   if constexpr (BIDIR) {
     if (pwave)
       for (int n = 0; n < NT; ++n)
-        for (int j = 0; j < 4; ++j) out[3 * DD + (16 * col + 4 * g + j) * D + 16 * n + r] = RR[n][j];
+        for (int j = 0; j < 4; ++j) r_r[(16 * col + 4 * g + j) * D + 16 * n + r] = RR[n][j];
   }
 }
 
 // ---------------------------------------------------------------- 2. prefix over segments
+// One workgroup per (b, h, direction) folds the segment maps in order, W <- W + (-Dev) W + R,
+// storing each segment's entry state. The fold is a chain of small products, so its speed is the
+// latency of one step: the map records stream through a kPrefixDepth-deep LDS ring, each loaded
+// kPrefixDepth - 1 steps ahead (HBM -> registers -> LDS), one barrier per step.
+constexpr int kPrefixDepth = 4;
+
 template <int D, bool BIDIR>
 __global__ __launch_bounds__(D / 16 * 64) void chunk_prefix(const float* __restrict__ w0,
                                                             long long w0_bstride, int H, int S,
                                                             const float* __restrict__ comp,
                                                             float* __restrict__ win) {
-  constexpr int NT = D / 16;
+  constexpr int NT = D / 16, NTH = NT * 64;
   constexpr long long DD = (long long)D * D;
+  constexpr int PD = D + 8;                   // -Dev row pitch (bf16 elements)
+  constexpr int PR = D + 4;                   // R row pitch (floats)
+  constexpr int DEV_PIECES = D * D / 8;       // 16-byte pieces of -Dev
+  constexpr int R_PIECES = D * D / 4;         // 16-byte pieces of R
+  constexpr int PIECES = DEV_PIECES + R_PIECES;
+  constexpr int PER = (PIECES + NTH - 1) / NTH;
+  __shared__ __align__(16) bf16 sDev[kPrefixDepth][D * PD];
+  __shared__ __align__(16) float sR[kPrefixDepth][D * PR];
+
   const int bh = blockIdx.x, dir = blockIdx.y, b = bh / H, h = bh % H;
   const int BH = gridDim.x;
   const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
+  const int nrec = BIDIR ? 2 : 1;
+  auto record = [&](int i) {  // map record of the i-th fold step
+    const int s = dir == 0 ? i : S - 1 - i;
+    return comp + (((long long)bh * S + s) * nrec + dir) * kMapFloats<D>;
+  };
+  auto load = [&](int i, uint4* regs) {
+    const uint4* src = reinterpret_cast<const uint4*>(record(i));
+    for (int u = 0; u < PER; ++u) {
+      const int c = threadIdx.x + u * NTH;
+      if (PIECES % NTH == 0 || c < PIECES) regs[u] = src[c];
+    }
+  };
+  auto store = [&](int slot, const uint4* regs) {
+    for (int u = 0; u < PER; ++u) {
+      const int c = threadIdx.x + u * NTH;
+      if (c < DEV_PIECES) {
+        const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+        st16(&sDev[slot][row * PD + col], regs[u]);
+      } else if (PIECES % NTH == 0 || c < PIECES) {
+        const int e = (c - DEV_PIECES) * 4, row = e / D, col = e % D;
+        *reinterpret_cast<uint4*>(&sR[slot][row * PR + col]) = regs[u];
+      }
+    }
+  };
+
   const float* W0 = w0 + b * w0_bstride + h * DD;
   f32x4 W[NT];
   for (int m = 0; m < NT; ++m)
     for (int j = 0; j < 4; ++j) W[m][j] = W0[(16 * m + 4 * g + j) * D + 16 * w + r];
-  const int nc = BIDIR ? 4 : 2;
   float* dst_base = win + ((long long)dir * BH + bh) * S * DD;
+  const int steps = S - 1;  // maps applied: segments 0 .. S-2 in fold order
+  {
+    uint4 regs[PER];
+    for (int i = 0; i < kPrefixDepth - 1 && i < steps; ++i) {
+      load(i, regs);
+      store(i, regs);
+    }
+  }
   for (int i = 0; i < S; ++i) {
     const int s = dir == 0 ? i : S - 1 - i;
     float* dst = dst_base + s * DD;
     for (int m = 0; m < NT; ++m)
       for (int j = 0; j < 4; ++j) dst[(16 * m + 4 * g + j) * D + 16 * w + r] = W[m][j];
-    if (i == S - 1) break;
-    const float* cp = comp + ((long long)bh * S + s) * nc * DD + (dir == 0 ? 0 : 2 * DD);
-    const float* Dev = cp;
-    const float* R = cp + DD;
+    if (i == steps) break;
+    uint4 regs[PER];
+    const bool pre = i + kPrefixDepth - 1 < steps;
+    if (pre) load(i + kPrefixDepth - 1, regs);
+    __syncthreads();  // step i's record is in LDS
+    const int slot = i % kPrefixDepth;
     f32x4 acc[NT];
     for (int m = 0; m < NT; ++m)
-      for (int j = 0; j < 4; ++j) acc[m][j] = W[m][j] + R[(16 * m + 4 * g + j) * D + 16 * w + r];
+      for (int j = 0; j < 4; ++j) acc[m][j] = W[m][j] + sR[slot][(16 * m + 4 * g + j) * PR + 16 * w + r];
     for (int m = 0; m < NT; ++m) {
       if constexpr (D >= 32) {
         for (int ks = 0; ks < D / 32; ++ks) {
-          const float* dp = Dev + (16 * m + r) * D + 32 * ks + 4 * g;
-          const float4 lo4 = *reinterpret_cast<const float4*>(dp);
-          const float4 hi4 = *reinterpret_cast<const float4*>(dp + 16);
-          const bf16x8 av = cat8(to_bf16x4(f32x4{-lo4.x, -lo4.y, -lo4.z, -lo4.w}),
-                                 to_bf16x4(f32x4{-hi4.x, -hi4.y, -hi4.z, -hi4.w}));
-          acc[m] = mma32(av, b_state(W, ks), acc[m]);
+          const bf16* dp = &sDev[slot][(16 * m + r) * PD + 32 * ks + 4 * g];
+          acc[m] = mma32(cat8(ld4(dp), ld4(dp + 16)), b_state(W, ks), acc[m]);
         }
       } else {
-        const float4 d4 = *reinterpret_cast<const float4*>(Dev + (16 * m + r) * D + 4 * g);
-        acc[m] = mma16(to_bf16x4(f32x4{-d4.x, -d4.y, -d4.z, -d4.w}), to_bf16x4(W[0]), acc[m]);
+        acc[m] = mma16(ld4(&sDev[slot][(16 * m + r) * PD + 4 * g]), to_bf16x4(W[0]), acc[m]);
       }
     }
     for (int m = 0; m < NT; ++m) W[m] = acc[m];
+    // The slot of step i + depth - 1 held step i - 1's record, read before this step's barrier.
+    if (pre) store((i + kPrefixDepth - 1) % kPrefixDepth, regs);
   }
 }
 
@@ -477,7 +533,7 @@ hipError_t launch_bf16(bool bidir, int B, int H, int N, float a, const void* q, 
   const ChunkPlan pl = chunk_plan(bidir, B, H, N, D, CH);
   const long long DD = (long long)D * D;
   float* comp = static_cast<float*>(ws);
-  float* win = comp + (long long)BH * pl.S * (bidir ? 4 : 2) * DD;
+  float* win = comp + (long long)BH * pl.S * (bidir ? 2 : 1) * kMapFloats<D>;
   if (pl.S > 1) {
     if (bidir) {
       hipLaunchKernelGGL((chunk_compose_bf16<D, CH, true>), dim3(pl.S, BH), dim3(D / 8 * 64), 0, st,
@@ -547,8 +603,9 @@ size_t chunked_workspace_bytes(bool bidir, bool bf16_io, int B, int H, int N, in
   }
   const ChunkPlan pl = chunk_plan(bidir, B, H, N, D, chunk);
   if (pl.S == 1) return 0;
-  // segment maps (Dev, R [, Dev_rev, R_rev]) + entry states per direction
-  return BH * pl.S * DD * sizeof(float) * ((bidir ? 4 : 2) + (bidir ? 2 : 1));
+  // segment map records (-Dev bf16 + R fp32, per direction) + entry states per direction
+  const size_t ndir = bidir ? 2 : 1;
+  return BH * pl.S * ndir * (DD / 2 + DD) * sizeof(float) + BH * pl.S * ndir * DD * sizeof(float);
 }
 
 hipError_t chunked_launch(bool bidir, bool bf16_io, int B, int H, int N, int D, int chunk,
