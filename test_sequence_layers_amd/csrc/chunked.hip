@@ -28,6 +28,8 @@
 // Inside every kernel, wave w owns columns [16w, 16w + 16) of its state (the columns of W are
 // independent regressions), held in MFMA accumulator layout; the chunk's K, V, Q are staged
 // through LDS with the next chunk prefetched into registers.
+#include <atomic>
+
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -504,17 +506,79 @@ struct ChunkPlan {
   int S, L;  // segments per (b, h) and chunks per segment
 };
 
-template <int D>
-ChunkPlan chunk_plan_d(bool bidir, int B, int H, int N, int CH) {
+// Resident workgroups of the segment kernels, for the current device. The compose and scan
+// kernels walk their segment's chunks one after another (latency-bound), so the plan sizes the
+// grid to be resident in one round: a partial second round would double their time. Queried once
+// per (kernel, device) and cached; without a usable device the defaults of MI355X apply
+// (256 CUs, 2 workgroups per CU).
+struct Residency {
+  int cus, per_cu;
+};
+constexpr int kMaxDevices = 64;
+
+template <class Kernel>
+int cached_per_cu(Kernel kernel, int threads, int dev, std::atomic<int>* cache) {
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n < 1) {
+    (void)hipGetLastError();
+    n = 2;
+  }
+  cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+int device_cus(int dev) {
+  static std::atomic<int> cache[kMaxDevices];
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) {
+    (void)hipGetLastError();
+    n = 256;
+  }
+  cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+template <int D, int CH>
+Residency residency(bool bidir) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return Residency{256, 2};
+  }
+  static std::atomic<int> c_comp[2][kMaxDevices], c_scan[2][kMaxDevices];
+  const int comp = bidir ? cached_per_cu(chunk_compose_bf16<D, CH, true>, D / 8 * 64, dev, c_comp[1])
+                         : cached_per_cu(chunk_compose_bf16<D, CH, false>, D / 8 * 64, dev, c_comp[0]);
+  const int scan = bidir ? cached_per_cu(chunk_scan_bf16<D, CH, kBidir>, D / 16 * 64, dev, c_scan[1])
+                         : cached_per_cu(chunk_scan_bf16<D, CH, kCausal>, D / 16 * 64, dev, c_scan[0]);
+  return Residency{device_cus(dev), comp < scan ? comp : scan};
+}
+
+template <int D, int CH>
+ChunkPlan chunk_plan_dc(bool bidir, int B, int H, int N) {
   const int C = N / CH;
   const int BH = B * H;
-  int S = (1024 + BH - 1) / BH;  // about 1024 workgroups for the scan
-  if (S > C / 8) S = C / 8;       // keep at least 8 chunks per segment
+  const Residency res = residency<D, CH>(bidir);
+  const int slots = res.cus * res.per_cu;  // workgroups resident at once
+  int S = slots / BH;                       // segments per (b, h): one resident round
+  if (S > C / 4) S = C / 4;                 // keep at least 4 chunks per segment
   if (S < 1) S = 1;
   int L = (C + S - 1) / S;
   if (bidir && L > max_seg_len<D>()) L = max_seg_len<D>();
   S = (C + L - 1) / L;
   return ChunkPlan{S, L};
+}
+
+template <int D>
+ChunkPlan chunk_plan_d(bool bidir, int B, int H, int N, int CH) {
+  switch (CH) {
+    case 16: return chunk_plan_dc<D, 16>(bidir, B, H, N);
+    case 32: return chunk_plan_dc<D, 32>(bidir, B, H, N);
+    default: return chunk_plan_dc<D, 64>(bidir, B, H, N);
+  }
 }
 
 ChunkPlan chunk_plan(bool bidir, int B, int H, int N, int D, int CH) {
