@@ -107,8 +107,8 @@ def cpu_baseline(inputs) -> dict:
 
     from oracle import ttt_oracle as O
 
-    samples = {"hvit3t_stage1_fullbatch": (64, 2), "vittt_bidir_1280": (8, 3), "ttt_linear_causal_16k": (1, 12),
-               "ttt_mlp_causal_8k": (1, 4)}  # (batches, heads) of each layer that the oracle runs
+    samples = {"hvit3t_stage1_fullbatch": (64, 2), "vittt_bidir_1280": (8, 3), "ttt_linear_causal_16k": (2, 12),
+               "ttt_mlp_causal_8k": (1, 12)}  # (batches, heads) of each layer that the oracle runs (about 10 s)
     total_s = 0.0
     desc = []
     with threadpool_limits(limits=1):
