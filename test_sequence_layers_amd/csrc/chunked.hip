@@ -49,27 +49,50 @@ template <int D>
 constexpr int max_seg_len() { return kRevLdsBytes / (D * D * 2); }
 
 // ---------------------------------------------------------------- staging with prefetch
-// A [CH x D] bf16 tile (token stride ts) moves HBM -> registers (prefetch) -> LDS (row pitch P).
-template <int D, int CH, int NTH>
-struct TileRegs {
-  static constexpr int CPR = D / 8;                    // 16-byte pieces per row
-  static constexpr int PIECES = CH * CPR;
-  static constexpr int PER = (PIECES + NTH - 1) / NTH;  // pieces per thread
+// The [CH x D] bf16 tiles of NTS tensors of one chunk (token stride ts) move HBM -> registers ->
+// LDS (row pitch P). The workgroup's threads form G groups; group j holds the chunks whose step
+// index is j mod G: it loads a chunk G steps before the step that uses it and stores it to LDS at
+// the start of that step, so each load has G steps to arrive with one register set per thread.
+template <int D, int CH, int NTH, int NTS, int G>
+struct ChunkStager {
+  static_assert(NTH % G == 0 && NTS >= 1 && NTS <= 3, "staging geometry");
+  static constexpr int CPR = D / 8;  // 16-byte pieces per row
+  static constexpr int TILE = CH * CPR;
+  static constexpr int PIECES = NTS * TILE;
+  static constexpr int GT = NTH / G;  // threads per group
+  static constexpr int PER = (PIECES + GT - 1) / GT;
   uint4 v[PER];
-  __device__ __forceinline__ void load(const bf16* src, long long ts) {
+  int group, idx;
+  __device__ __forceinline__ ChunkStager() : group(threadIdx.x / GT), idx(threadIdx.x % GT) {}
+  __device__ __forceinline__ bool mine(int step) const { return step % G == group; }
+  __device__ __forceinline__ void load(const bf16* t0, const bf16* t1, const bf16* t2,
+                                       long long ts) {
     for (int i = 0; i < PER; ++i) {
-      const int c = threadIdx.x + i * NTH;
-      if (PIECES % NTH == 0 || c < PIECES) v[i] = ld16(src + (c / CPR) * ts + (c % CPR) * 8);
+      const int p = idx + i * GT;
+      if (PIECES % GT == 0 || p < PIECES) {
+        const int sel = p / TILE, rem = p % TILE;
+        const bf16* src = sel == 0 ? t0 : (sel == 1 ? t1 : t2);
+        v[i] = ld16(src + (rem / CPR) * ts + (rem % CPR) * 8);
+      }
     }
   }
   template <int P>
-  __device__ __forceinline__ void store(bf16* dst) const {
+  __device__ __forceinline__ void store(bf16* d0, bf16* d1, bf16* d2) const {
     for (int i = 0; i < PER; ++i) {
-      const int c = threadIdx.x + i * NTH;
-      if (PIECES % NTH == 0 || c < PIECES) st16(dst + (c / CPR) * P + (c % CPR) * 8, v[i]);
+      const int p = idx + i * GT;
+      if (PIECES % GT == 0 || p < PIECES) {
+        const int sel = p / TILE, rem = p % TILE;
+        bf16* dst = sel == 0 ? d0 : (sel == 1 ? d1 : d2);
+        st16(dst + (rem / CPR) * P + (rem % CPR) * 8, v[i]);
+      }
     }
   }
 };
+
+// Prefetch groups: 16-token chunks leave half of the threads idle for one chunk's tiles, so two
+// groups stage alternate chunks two steps ahead at no register cost.
+template <int CH>
+constexpr int stage_groups() { return CH == 16 ? 2 : 1; }
 
 template <int D, int CH, int P, int NTH>
 __device__ __forceinline__ void store_chunk(bf16* dst, const bf16* src, long long ts) {
@@ -151,16 +174,18 @@ __global__ __launch_bounds__(D / 8 * 64) void chunk_compose_bf16(
       RR[m][j] = 0.f;
     }
 
-  TileRegs<D, CH, NTH> pk, pv;
-  pk.load(k + head0 + (long long)lo * CH * ts, ts);
-  pv.load(v + head0 + (long long)lo * CH * ts, ts);
+  constexpr int G = stage_groups<CH>();
+  ChunkStager<D, CH, NTH, 2, G> st;
+  const bf16* kb = k + head0;
+  const bf16* vb = v + head0;
+  const long long cs = (long long)CH * ts;  // elements between consecutive chunks
+  for (int j = 0; j < G && lo + j < hi; ++j)
+    if (st.mine(j)) st.load(kb + (lo + j) * cs, vb + (lo + j) * cs, nullptr, ts);
   for (int c = lo; c < hi; ++c) {
     __syncthreads();
-    pk.template store<P>(sK);
-    pv.template store<P>(sV);
-    if (c + 1 < hi) {
-      pk.load(k + head0 + (long long)(c + 1) * CH * ts, ts);
-      pv.load(v + head0 + (long long)(c + 1) * CH * ts, ts);
+    if (st.mine(c - lo)) {
+      st.template store<P>(sK, sV, nullptr);
+      if (c + G < hi) st.load(kb + (c + G) * cs, vb + (c + G) * cs, nullptr, ts);
     }
     __syncthreads();
     f32x4 Y[NP];
@@ -335,20 +360,23 @@ __global__ __launch_bounds__(D / 16 * 64) void chunk_scan_bf16(
   };
 
   f32x4 W[NT];
-  TileRegs<D, CH, NTH> pk, pv, pq;
+  constexpr int G = stage_groups<CH>();
+  const bf16* qb = q + head0;
+  const bf16* kb = k + head0;
+  const bf16* vb = v + head0;
+  const long long cs = (long long)CH * ts;  // elements between consecutive chunks
 
   if constexpr (MODE == kBidir) {
     // Reverse scan over the segment's chunks (last to first), keeping each W^r_c in LDS.
     entry(1, W);
-    pk.load(k + head0 + (long long)(hi - 1) * CH * ts, ts);
-    pv.load(v + head0 + (long long)(hi - 1) * CH * ts, ts);
+    ChunkStager<D, CH, NTH, 2, G> sr;
+    for (int j = 0; j < G && hi - 1 - j >= lo; ++j)
+      if (sr.mine(j)) sr.load(kb + (hi - 1 - j) * cs, vb + (hi - 1 - j) * cs, nullptr, ts);
     for (int c = hi - 1; c >= lo; --c) {
       __syncthreads();
-      pk.template store<P>(sK);
-      pv.template store<P>(sV);
-      if (c - 1 >= lo) {
-        pk.load(k + head0 + (long long)(c - 1) * CH * ts, ts);
-        pv.load(v + head0 + (long long)(c - 1) * CH * ts, ts);
+      if (sr.mine(hi - 1 - c)) {
+        sr.template store<P>(sK, sV, nullptr);
+        if (c - G >= lo) sr.load(kb + (c - G) * cs, vb + (c - G) * cs, nullptr, ts);
       }
       __syncthreads();
       f32x4 E[NP];
@@ -361,19 +389,15 @@ __global__ __launch_bounds__(D / 16 * 64) void chunk_scan_bf16(
 
   // Forward scan over the segment with the read-out.
   entry(0, W);
-  pk.load(k + head0 + (long long)lo * CH * ts, ts);
-  pv.load(v + head0 + (long long)lo * CH * ts, ts);
-  pq.load(q + head0 + (long long)lo * CH * ts, ts);
+  ChunkStager<D, CH, NTH, 3, G> sf;
+  for (int j = 0; j < G && lo + j < hi; ++j)
+    if (sf.mine(j)) sf.load(kb + (lo + j) * cs, vb + (lo + j) * cs, qb + (lo + j) * cs, ts);
   for (int c = lo; c < hi; ++c) {
     const long long tok0 = head0 + (long long)c * CH * ts;
     __syncthreads();
-    pk.template store<P>(sK);
-    pv.template store<P>(sV);
-    pq.template store<P>(sQ);
-    if (c + 1 < hi) {
-      pk.load(k + tok0 + CH * ts, ts);
-      pv.load(v + tok0 + CH * ts, ts);
-      pq.load(q + tok0 + CH * ts, ts);
+    if (sf.mine(c - lo)) {
+      sf.template store<P>(sK, sV, sQ);
+      if (c + G < hi) sf.load(kb + (c + G) * cs, vb + (c + G) * cs, qb + (c + G) * cs, ts);
     }
     __syncthreads();
 
