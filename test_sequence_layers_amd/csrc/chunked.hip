@@ -128,11 +128,16 @@ __device__ __forceinline__ f32x4 rows_times_state(const bf16* X, int row0, const
 // W[:, cols] += K^T (-a E): A = K^T (row = feature 16m + r, k = token 16p + 4g + j), B = -a E_p.
 template <int D, int NP, int P>
 __device__ __forceinline__ void update_state(f32x4* W, const f32x4* E, const bf16* sK, float a,
-                                             int r, int g) {
+                                             bf16x4 ident, int r, int g) {
   for (int p = 0; p < NP; ++p) {
     const bf16x4 eb = to_bf16x4_scaled(E[p], -a);
-    for (int m = 0; m < D / 16; ++m)
-      W[m] = mma16(ld4_col(&sK[(16 * p + 4 * g) * P + 16 * m + r], P), eb, W[m]);
+    for (int m = 0; m < D / 16; ++m) {
+      // 16-token chunks: K^T tiles via the matrix cores (fewer LDS instructions); longer chunks:
+      // 2-byte column reads (the extra products cost more there).
+      const bf16x4 kt = NP == 1 ? tile_columns(&sK[16 * p * P + 16 * m], P, ident, r, g)
+                                : ld4_col(&sK[(16 * p + 4 * g) * P + 16 * m + r], P);
+      W[m] = mma16(kt, eb, W[m]);
+    }
   }
 }
 
@@ -155,11 +160,14 @@ __global__ __launch_bounds__(D / 8 * 64) void chunk_compose_bf16(
     float* __restrict__ comp) {
   constexpr int P = D + 8, NT = D / 16, NP = CH / 16, NTH = 2 * NT * 64;
   constexpr long long DD = (long long)D * D;
-  __shared__ __align__(16) bf16 sK[CH * P];
-  __shared__ __align__(16) bf16 sV[CH * P];
+  // Double-buffered chunk tiles: chunk c is staged while other waves may still read chunk c - 1,
+  // so one barrier per chunk suffices.
+  __shared__ __align__(16) bf16 sKb[2][CH * P];
+  __shared__ __align__(16) bf16 sVb[2][CH * P];
 
   const int s = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H;
   const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
+  const bf16x4 ident = identity_b(r, g);
   const bool pwave = w < NT;        // P columns (init I, no V); else R columns (init 0, V)
   const int col = pwave ? w : w - NT;
   const int C = N / CH;
@@ -182,7 +190,8 @@ __global__ __launch_bounds__(D / 8 * 64) void chunk_compose_bf16(
   for (int j = 0; j < G && lo + j < hi; ++j)
     if (st.mine(j)) st.load(kb + (lo + j) * cs, vb + (lo + j) * cs, nullptr, ts);
   for (int c = lo; c < hi; ++c) {
-    __syncthreads();
+    bf16* sK = sKb[(c - lo) & 1];
+    bf16* sV = sVb[(c - lo) & 1];
     if (st.mine(c - lo)) {
       st.template store<P>(sK, sV, nullptr);
       if (c + G < hi) st.load(kb + (c + G) * cs, vb + (c + G) * cs, nullptr, ts);
@@ -195,11 +204,13 @@ __global__ __launch_bounds__(D / 8 * 64) void chunk_compose_bf16(
         for (int p = 0; p < NP; ++p) {
           const bf16x4 ya = to_bf16x4_scaled(Y[p], a);
           for (int n = 0; n < NT; ++n)
-            RR[n] = mma16(ya, ld4_col(&sV[(16 * p + 4 * g) * P + 16 * n + r], P), RR[n]);
+            RR[n] = mma16(ya, NP == 1 ? tile_columns(&sV[16 * p * P + 16 * n], P, ident, r, g)
+                                      : ld4_col(&sV[(16 * p + 4 * g) * P + 16 * n + r], P),
+                          RR[n]);
         }
       }
     }
-    update_state<D, NP, P>(X, Y, sK, a, r, g);
+    update_state<D, NP, P>(X, Y, sK, a, ident, r, g);
   }
 
   // comp[(bh * S + s)] holds the forward map record and, for the bidirectional scan, the
@@ -333,15 +344,21 @@ __global__ __launch_bounds__(D / 16 * 64) void chunk_scan_bf16(
   constexpr int NTH = NT * 64;
   constexpr long long DD = (long long)D * D;
   constexpr int LMAX = MODE == kBidir ? max_seg_len<D>() : 1;
-  __shared__ __align__(16) bf16 sK[CH * P];
-  __shared__ __align__(16) bf16 sV[CH * P];
-  __shared__ __align__(16) bf16 sQ[CH * P];
-  __shared__ __align__(16) bf16 sO[CH * P];
-  __shared__ __align__(16) bf16x4 sWr[MODE == kBidir ? LMAX * NT * NT * 64 : 1];
+  constexpr int WR_BYTES = MODE == kBidir ? LMAX * NT * NT * 64 * 8 : 8;
+  // Chunk tiles (K, V, Q, O) are double-buffered when LDS allows (one barrier per chunk: chunk c
+  // is staged while other waves may still read chunk c - 1, and chunk c - 1's O tile is written
+  // out after chunk c's barrier); otherwise single buffers with three barriers per chunk.
+  constexpr int NBUF = WR_BYTES + 2 * 4 * CH * P * 2 <= 160 * 1024 ? 2 : 1;
+  __shared__ __align__(16) bf16 sKb[NBUF][CH * P];
+  __shared__ __align__(16) bf16 sVb[NBUF][CH * P];
+  __shared__ __align__(16) bf16 sQb[NBUF][CH * P];
+  __shared__ __align__(16) bf16 sOb[NBUF][CH * P];
+  __shared__ __align__(16) bf16x4 sWr[WR_BYTES / 8];
 
   const int s = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H;
   const int BH = gridDim.y;
   const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
+  const bf16x4 ident = identity_b(r, g);
   const int C = N / CH;
   const int lo = s * L, hi = min(C, lo + L);
   const long long ts = (long long)H * D;
@@ -373,7 +390,10 @@ __global__ __launch_bounds__(D / 16 * 64) void chunk_scan_bf16(
     for (int j = 0; j < G && hi - 1 - j >= lo; ++j)
       if (sr.mine(j)) sr.load(kb + (hi - 1 - j) * cs, vb + (hi - 1 - j) * cs, nullptr, ts);
     for (int c = hi - 1; c >= lo; --c) {
-      __syncthreads();
+      const int buf = NBUF == 2 ? (hi - 1 - c) & 1 : 0;
+      bf16* sK = sKb[buf];
+      bf16* sV = sVb[buf];
+      if (NBUF == 1) __syncthreads();
       if (sr.mine(hi - 1 - c)) {
         sr.template store<P>(sK, sV, nullptr);
         if (c - G >= lo) sr.load(kb + (c - G) * cs, vb + (c - G) * cs, nullptr, ts);
@@ -381,25 +401,33 @@ __global__ __launch_bounds__(D / 16 * 64) void chunk_scan_bf16(
       __syncthreads();
       f32x4 E[NP];
       residuals<D, NP, P>(E, W, sK, sV, w, r, g);
-      update_state<D, NP, P>(W, E, sK, a, r, g);
+      update_state<D, NP, P>(W, E, sK, a, ident, r, g);
       for (int m = 0; m < NT; ++m) sWr[(((c - lo) * NT + w) * NT + m) * 64 + l] = to_bf16x4(W[m]);
     }
     if (s == 0 && w_out) save(w_out + (long long)BH * DD + bh * DD, W);
   }
 
-  // Forward scan over the segment with the read-out.
+  // Forward scan over the segment with the read-out. (For the bidirectional scan, the barrier
+  // below orders the reverse pass's last tile reads before the first forward store.)
+  if (MODE == kBidir) __syncthreads();
   entry(0, W);
   ChunkStager<D, CH, NTH, 3, G> sf;
   for (int j = 0; j < G && lo + j < hi; ++j)
     if (sf.mine(j)) sf.load(kb + (lo + j) * cs, vb + (lo + j) * cs, qb + (lo + j) * cs, ts);
   for (int c = lo; c < hi; ++c) {
     const long long tok0 = head0 + (long long)c * CH * ts;
-    __syncthreads();
+    const int buf = NBUF == 2 ? (c - lo) & 1 : 0;
+    bf16* sK = sKb[buf];
+    bf16* sV = sVb[buf];
+    bf16* sQ = sQb[buf];
+    bf16* sO = sOb[buf];
+    if (NBUF == 1) __syncthreads();
     if (sf.mine(c - lo)) {
       sf.template store<P>(sK, sV, sQ);
       if (c + G < hi) sf.load(kb + (c + G) * cs, vb + (c + G) * cs, qb + (c + G) * cs, ts);
     }
     __syncthreads();
+    if (NBUF == 2 && c > lo) store_chunk<D, CH, P, NTH>(o + tok0 - CH * ts, sOb[buf ^ 1], ts);
 
     f32x4 E[NP];
     residuals<D, NP, P>(E, W, sK, sV, w, r, g);
@@ -429,9 +457,9 @@ __global__ __launch_bounds__(D / 16 * 64) void chunk_scan_bf16(
         }
         for (int j = 0; j < 4; ++j) sO[(16 * p + 4 * g + j) * P + 16 * w + r] = (bf16)(qw[j] + acc[j]);
       }
-      update_state<D, NP, P>(W, E, sK, a, r, g);
+      update_state<D, NP, P>(W, E, sK, a, ident, r, g);
     } else {
-      update_state<D, NP, P>(W, E, sK, a, r, g);
+      update_state<D, NP, P>(W, E, sK, a, ident, r, g);
       f32x4 Ws[NT];
       for (int m = 0; m < NT; ++m) {
         const bf16x4 wr = sWr[(((c - lo) * NT + w) * NT + m) * 64 + l];
@@ -442,8 +470,14 @@ __global__ __launch_bounds__(D / 16 * 64) void chunk_scan_bf16(
         for (int j = 0; j < 4; ++j) sO[(16 * p + 4 * g + j) * P + 16 * w + r] = (bf16)acc[j];
       }
     }
+    if (NBUF == 1) {
+      __syncthreads();
+      store_chunk<D, CH, P, NTH>(o + tok0, sO, ts);
+    }
+  }
+  if (NBUF == 2) {  // the last chunk's O tile
     __syncthreads();
-    store_chunk<D, CH, P, NTH>(o + tok0, sO, ts);
+    store_chunk<D, CH, P, NTH>(o + head0 + (long long)(hi - 1) * CH * ts, sOb[(hi - 1 - lo) & 1], ts);
   }
   if (s == S - 1 && w_out) save(w_out + bh * DD, W);
 }

@@ -70,6 +70,21 @@ __device__ __forceinline__ bf16x8 ld8(const bf16* p) { return *reinterpret_cast<
 __device__ __forceinline__ bf16x4 ld4(const bf16* p) { return *reinterpret_cast<const bf16x4*>(p); }
 
 // Four bf16 read down a column (stride in elements), e.g. a transposed operand from a row-major tile.
+// Identity tile as an MFMA B operand: lane (r, g) holds I[4g + i][r].
+__device__ __forceinline__ bf16x4 identity_b(int r, int g) {
+  bf16x4 x;
+  for (int i = 0; i < 4; ++i) x[i] = (bf16)(4 * g + i == r ? 1.f : 0.f);
+  return x;
+}
+
+// A 16 x 16 bf16 tile T (T[t][c] = base[t * pitch + c]) in accumulator layout: lane (r, g) holds
+// T[4g + i][r], i.e. the A operand of T^T and the B operand of T. It is formed on the matrix cores
+// as T * I from row-contiguous LDS reads (exact), instead of four 2-byte column reads.
+__device__ __forceinline__ bf16x4 tile_columns(const bf16* base, int pitch, bf16x4 ident, int r,
+                                               int g) {
+  return to_bf16x4(mma16(ld4(base + r * pitch + 4 * g), ident, zero4()));
+}
+
 __device__ __forceinline__ bf16x4 ld4_col(const bf16* p, int stride) {
   bf16x4 r;
   r[0] = p[0];

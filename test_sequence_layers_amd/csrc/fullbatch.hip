@@ -82,6 +82,7 @@ __global__ __launch_bounds__(kThreads) void fb_partial_bf16(
   const int n0 = s * tps, n1 = min(N, n0 + tps);
   const int ntiles = (n1 - n0 + kTile - 1) / kTile;
   const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
+  const bf16x4 ident = identity_b(r, g);
   const int pair = w % G::PAIRS, tw = w / G::PAIRS;
   const int hl = pair / G::NT, n = pair % G::NT;  // head within the group, column tile
   const long long ts = (long long)H * D;
@@ -125,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void fb_partial_bf16(
       }
       const bf16x4 eb = to_bf16x4(e);  // acc[:, n] += K^T E (E's C layout is the B operand)
       for (int m = 0; m < G::NT; ++m)
-        acc[m] = mma16(ld4_col(&tK[(16 * p + 4 * g) * G::P + 16 * m + r], G::P), eb, acc[m]);
+        acc[m] = mma16(tile_columns(&tK[16 * p * G::P + 16 * m], G::P, ident, r, g), eb, acc[m]);
     }
   }
   __syncthreads();  // tile buffers free: sum the waves sharing a pair through sK, in a fixed order
