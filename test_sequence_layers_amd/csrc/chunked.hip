@@ -18,8 +18,9 @@
 //      Dev = I - P (the small deviation, which keeps bf16 operands accurate) and R. Every A_c is
 //      symmetric, so the reverse scan's composite of the segment is Dev^T; its offset
 //      R_rev = a sum_c (K_c P_{c-1})^T V_c is accumulated alongside.
-//   2. chunk_prefix: one workgroup per (b, h, direction) folds the segment maps in order from W0
-//      and stores every segment's entry state (W <- W - Dev W + R per segment).
+//   2. chunk_prefix: one single-wave workgroup per (b, h, direction, 16-column tile) folds the
+//      segment maps in order from W0 and stores every segment's entry state
+//      (W <- W - Dev W + R per segment).
 //   3. chunk_scan: one workgroup per (segment, b, h) rescans its segment from its true entry
 //      state and writes the outputs. For the bidirectional scan it first runs the reverse scan
 //      over its chunks, keeping each W^r_c (bf16) in LDS, then the forward scan with the read-out.
@@ -38,10 +39,32 @@ namespace {
 
 enum ScanMode { kCausal = 0, kBidir = 1 };
 
-// Segment map record of one (b, h, segment, direction): -Dev as bf16 [D][D] (the MFMA operand of
-// the prefix fold, already negated) followed by R as fp32 [D][D]; kMapFloats<D> floats in all.
+// Segment map record of one (b, h, segment, direction): -Dev as bf16 (the MFMA operand of the
+// prefix fold, already negated) followed by R as fp32; kMapFloats<D> floats in all. Records and
+// segment entry states are stored as MFMA register tiles, so that each lane moves its operands
+// with 16-byte accesses:
+//  - state tiles (R and the entry states, fp32): tile (column tile n, row tile m) holds, for lane
+//    l = r + 16g, rows 16m + 4g + j (j < 4) of column 16n + r, contiguous (the accumulator layout);
+//  - -Dev tiles (bf16): the A operand of the fold's product. Tile (row tile m, k slot ks) holds,
+//    for lane l = r + 16g, row 16m + r at k = 32ks + 4g + i and 32ks + 16 + 4g + i (i < 4); for
+//    D = 16 only k = 4g + i.
 template <int D>
 constexpr int kMapFloats = D * D / 2 + D * D;
+template <int D>
+constexpr int kDevElems = D >= 32 ? 8 : 4;
+
+template <int D>
+__device__ __forceinline__ long long state_tile(int n, int m, int l) {  // float offset
+  return ((long long)(n * (D / 16) + m) * 64 + l) * 4;
+}
+
+template <int D>
+__device__ __forceinline__ int dev_offset(int row, int kcol) {  // bf16 offset of -Dev[row][kcol]
+  constexpr int KS = D >= 32 ? D / 32 : 1;
+  const int kk = kcol & 31, half = kk >> 4, gg = (kk & 15) >> 2;
+  return (((row >> 4) * KS + (kcol >> 5)) * 64 + (row & 15) + 16 * gg) * kDevElems<D> + (kk & 3) +
+         4 * half;
+}
 
 // LDS bytes available for the reverse states of one bidirectional scan segment.
 constexpr int kRevLdsBytes = 96 * 1024;
@@ -214,7 +237,7 @@ __global__ __launch_bounds__(D / 8 * 64) void chunk_compose_bf16(
   }
 
   // comp[(bh * S + s)] holds the forward map record and, for the bidirectional scan, the
-  // reverse one: -Dev (bf16) then R (fp32), each D x D row-major.
+  // reverse one (-Dev_r = -Dev_f^T, R_rev).
   float* rec = comp + ((long long)bh * S + s) * (BIDIR ? 2 : 1) * kMapFloats<D>;
   bf16* ndev_f = reinterpret_cast<bf16*>(rec);
   float* r_f = rec + DD / 2;
@@ -225,111 +248,105 @@ __global__ __launch_bounds__(D / 8 * 64) void chunk_compose_bf16(
       const int row = 16 * m + 4 * g + j, cc = 16 * col + r;
       if (pwave) {
         const bf16 nd = (bf16)(X[m][j] - (row == cc ? 1.f : 0.f));  // -Dev = P - I
-        ndev_f[row * D + cc] = nd;
-        if constexpr (BIDIR) ndev_r[cc * D + row] = nd;  // Dev_r = Dev_f^T
-      } else {
-        r_f[row * D + cc] = X[m][j];
+        ndev_f[dev_offset<D>(row, cc)] = nd;
+        if constexpr (BIDIR) ndev_r[dev_offset<D>(cc, row)] = nd;  // Dev_r = Dev_f^T
       }
     }
+  if (!pwave)
+    for (int m = 0; m < NT; ++m) *reinterpret_cast<f32x4*>(r_f + state_tile<D>(col, m, l)) = X[m];
   if constexpr (BIDIR) {
-    if (pwave)
-      for (int n = 0; n < NT; ++n)
-        for (int j = 0; j < 4; ++j) r_r[(16 * col + 4 * g + j) * D + 16 * n + r] = RR[n][j];
+    if (pwave)  // RR[n] is R_rev's tile (column tile n, row tile col)
+      for (int n = 0; n < NT; ++n) *reinterpret_cast<f32x4*>(r_r + state_tile<D>(n, col, l)) = RR[n];
   }
 }
 
 // ---------------------------------------------------------------- 2. prefix over segments
-// One workgroup per (b, h, direction) folds the segment maps in order, W <- W + (-Dev) W + R,
-// storing each segment's entry state. The fold is a chain of small products, so its speed is the
-// latency of one step: the map records stream through a kPrefixDepth-deep LDS ring, each loaded
-// kPrefixDepth - 1 steps ahead (HBM -> registers -> LDS), one barrier per step.
-constexpr int kPrefixDepth = 4;
+// The columns of W are independent regressions, so the fold over the segment maps,
+// W[:, cols] <- W[:, cols] + (-Dev) W[:, cols] + R[:, cols], runs as one single-wave workgroup
+// per (b, h, direction, 16-column tile), storing each segment's entry state. Its speed is the
+// latency of one step (a few dependent products), so there is no LDS and no barrier: each lane
+// loads its own operands of a map record (rows of -Dev, its R entries) straight into registers,
+// kPrefixSets steps ahead, rotating through kPrefixSets register sets.
+constexpr int kPrefixSets = 4;
+
+template <int D>
+struct PrefixOperands {
+  static constexpr int NT = D / 16, KS = D >= 32 ? D / 32 : 1;
+  bf16x8 dev[NT][KS];  // -Dev tiles (D >= 32)
+  bf16x4 dev16;        // -Dev tile for D = 16
+  f32x4 rr[NT];        // R tiles (column tile col, row tile m)
+  __device__ __forceinline__ void load(const float* rec, int col, int l) {
+    const bf16* nd = reinterpret_cast<const bf16*>(rec);
+    const float* R = rec + D * D / 2;
+    if constexpr (D >= 32) {
+      for (int m = 0; m < NT; ++m)
+        for (int ks = 0; ks < KS; ++ks)
+          dev[m][ks] = *reinterpret_cast<const bf16x8*>(nd + ((m * KS + ks) * 64 + l) * 8);
+    } else {
+      dev16 = *reinterpret_cast<const bf16x4*>(nd + l * 4);
+    }
+    for (int m = 0; m < NT; ++m) rr[m] = *reinterpret_cast<const f32x4*>(R + state_tile<D>(col, m, l));
+  }
+};
 
 template <int D, bool BIDIR>
-__global__ __launch_bounds__(D / 16 * 64) void chunk_prefix(const float* __restrict__ w0,
-                                                            long long w0_bstride, int H, int S,
-                                                            const float* __restrict__ comp,
-                                                            float* __restrict__ win) {
-  constexpr int NT = D / 16, NTH = NT * 64;
+__global__ __launch_bounds__(64) void chunk_prefix(const float* __restrict__ w0,
+                                                   long long w0_bstride, int H, int S,
+                                                   const float* __restrict__ comp,
+                                                   float* __restrict__ win) {
+  constexpr int NT = D / 16;
   constexpr long long DD = (long long)D * D;
-  constexpr int PD = D + 8;                   // -Dev row pitch (bf16 elements)
-  constexpr int PR = D + 4;                   // R row pitch (floats)
-  constexpr int DEV_PIECES = D * D / 8;       // 16-byte pieces of -Dev
-  constexpr int R_PIECES = D * D / 4;         // 16-byte pieces of R
-  constexpr int PIECES = DEV_PIECES + R_PIECES;
-  constexpr int PER = (PIECES + NTH - 1) / NTH;
-  __shared__ __align__(16) bf16 sDev[kPrefixDepth][D * PD];
-  __shared__ __align__(16) float sR[kPrefixDepth][D * PR];
-
-  const int bh = blockIdx.x, dir = blockIdx.y, b = bh / H, h = bh % H;
+  const int bh = blockIdx.x, dir = blockIdx.y, col = blockIdx.z, b = bh / H, h = bh % H;
   const int BH = gridDim.x;
-  const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
+  const int l = threadIdx.x, r = l & 15, g = l >> 4;
   const int nrec = BIDIR ? 2 : 1;
   auto record = [&](int i) {  // map record of the i-th fold step
     const int s = dir == 0 ? i : S - 1 - i;
     return comp + (((long long)bh * S + s) * nrec + dir) * kMapFloats<D>;
   };
-  auto load = [&](int i, uint4* regs) {
-    const uint4* src = reinterpret_cast<const uint4*>(record(i));
-    for (int u = 0; u < PER; ++u) {
-      const int c = threadIdx.x + u * NTH;
-      if (PIECES % NTH == 0 || c < PIECES) regs[u] = src[c];
-    }
-  };
-  auto store = [&](int slot, const uint4* regs) {
-    for (int u = 0; u < PER; ++u) {
-      const int c = threadIdx.x + u * NTH;
-      if (c < DEV_PIECES) {
-        const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-        st16(&sDev[slot][row * PD + col], regs[u]);
-      } else if (PIECES % NTH == 0 || c < PIECES) {
-        const int e = (c - DEV_PIECES) * 4, row = e / D, col = e % D;
-        *reinterpret_cast<uint4*>(&sR[slot][row * PR + col]) = regs[u];
-      }
-    }
-  };
 
   const float* W0 = w0 + b * w0_bstride + h * DD;
-  f32x4 W[NT];
+  f32x4 W[NT];  // W[16m + 4g + j][16 col + r]
   for (int m = 0; m < NT; ++m)
-    for (int j = 0; j < 4; ++j) W[m][j] = W0[(16 * m + 4 * g + j) * D + 16 * w + r];
+    for (int j = 0; j < 4; ++j) W[m][j] = W0[(16 * m + 4 * g + j) * D + 16 * col + r];
   float* dst_base = win + ((long long)dir * BH + bh) * S * DD;
   const int steps = S - 1;  // maps applied: segments 0 .. S-2 in fold order
-  {
-    uint4 regs[PER];
-    for (int i = 0; i < kPrefixDepth - 1 && i < steps; ++i) {
-      load(i, regs);
-      store(i, regs);
-    }
-  }
-  for (int i = 0; i < S; ++i) {
-    const int s = dir == 0 ? i : S - 1 - i;
-    float* dst = dst_base + s * DD;
-    for (int m = 0; m < NT; ++m)
-      for (int j = 0; j < 4; ++j) dst[(16 * m + 4 * g + j) * D + 16 * w + r] = W[m][j];
-    if (i == steps) break;
-    uint4 regs[PER];
-    const bool pre = i + kPrefixDepth - 1 < steps;
-    if (pre) load(i + kPrefixDepth - 1, regs);
-    __syncthreads();  // step i's record is in LDS
-    const int slot = i % kPrefixDepth;
+  PrefixOperands<D> set0, set1, set2, set3;
+  set0.load(record(0), col, l);
+  set1.load(record(min(1, S - 1)), col, l);
+  set2.load(record(min(2, S - 1)), col, l);
+  set3.load(record(min(3, S - 1)), col, l);
+  auto store = [&](int i) {  // entry state of the i-th segment in fold order
+    float* dst = dst_base + (dir == 0 ? i : S - 1 - i) * DD;
+    for (int m = 0; m < NT; ++m) *reinterpret_cast<f32x4*>(dst + state_tile<D>(col, m, l)) = W[m];
+  };
+  auto step = [&](int i, PrefixOperands<D>& op) {  // applies map i, stores entry state i + 1
     f32x4 acc[NT];
-    for (int m = 0; m < NT; ++m)
-      for (int j = 0; j < 4; ++j) acc[m][j] = W[m][j] + sR[slot][(16 * m + 4 * g + j) * PR + 16 * w + r];
+    for (int m = 0; m < NT; ++m) acc[m] = W[m] + op.rr[m];
     for (int m = 0; m < NT; ++m) {
       if constexpr (D >= 32) {
-        for (int ks = 0; ks < D / 32; ++ks) {
-          const bf16* dp = &sDev[slot][(16 * m + r) * PD + 32 * ks + 4 * g];
-          acc[m] = mma32(cat8(ld4(dp), ld4(dp + 16)), b_state(W, ks), acc[m]);
-        }
+        for (int ks = 0; ks < D / 32; ++ks) acc[m] = mma32(op.dev[m][ks], b_state(W, ks), acc[m]);
       } else {
-        acc[m] = mma16(ld4(&sDev[slot][(16 * m + r) * PD + 4 * g]), to_bf16x4(W[0]), acc[m]);
+        acc[m] = mma16(op.dev16, to_bf16x4(W[0]), acc[m]);
       }
     }
     for (int m = 0; m < NT; ++m) W[m] = acc[m];
-    // The slot of step i + depth - 1 held step i - 1's record, read before this step's barrier.
-    if (pre) store((i + kPrefixDepth - 1) % kPrefixDepth, regs);
+    store(i + 1);
+    // Unconditional (clamped to the last record, which exists) so that every step issues the
+    // same memory operations and the compiler's waits stay kPrefixSets steps behind the loads.
+    op.load(record(min(i + kPrefixSets, S - 1)), col, l);
+  };
+  store(0);
+  int i = 0;
+  for (; i + kPrefixSets <= steps; i += kPrefixSets) {
+    step(i, set0);
+    step(i + 1, set1);
+    step(i + 2, set2);
+    step(i + 3, set3);
   }
+  if (i < steps) step(i, set0);
+  if (i + 1 < steps) step(i + 1, set1);
+  if (i + 2 < steps) step(i + 2, set2);
 }
 
 // ---------------------------------------------------------------- 3. segment scan
@@ -364,12 +381,17 @@ __global__ __launch_bounds__(D / 16 * 64) void chunk_scan_bf16(
   const long long ts = (long long)H * D;
   const long long head0 = (long long)b * N * ts + (long long)h * D;
 
-  // Entry state of this segment (C layout): W0 for a single segment, else from the prefix pass.
+  // Entry state of this segment (C layout): W0 for a single segment, else the prefix pass's
+  // state tiles.
   auto entry = [&](int dir, f32x4* W) {
-    const float* src = S == 1 ? w0 + b * w0_bstride + h * DD
-                              : win + (((long long)dir * BH + bh) * S + s) * DD;
-    for (int m = 0; m < NT; ++m)
-      for (int j = 0; j < 4; ++j) W[m][j] = src[(16 * m + 4 * g + j) * D + 16 * w + r];
+    if (S == 1) {
+      const float* src = w0 + b * w0_bstride + h * DD;
+      for (int m = 0; m < NT; ++m)
+        for (int j = 0; j < 4; ++j) W[m][j] = src[(16 * m + 4 * g + j) * D + 16 * w + r];
+    } else {
+      const float* src = win + (((long long)dir * BH + bh) * S + s) * DD;
+      for (int m = 0; m < NT; ++m) W[m] = *reinterpret_cast<const f32x4*>(src + state_tile<D>(w, m, l));
+    }
   };
   auto save = [&](float* dst, const f32x4* W) {
     for (int m = 0; m < NT; ++m)
@@ -660,12 +682,12 @@ hipError_t launch_bf16(bool bidir, int B, int H, int N, float a, const void* q, 
     if (bidir) {
       hipLaunchKernelGGL((chunk_compose_bf16<D, CH, true>), dim3(pl.S, BH), dim3(D / 8 * 64), 0, st,
                          (const bf16*)k, (const bf16*)v, H, N, a, pl.S, pl.L, comp);
-      hipLaunchKernelGGL((chunk_prefix<D, true>), dim3(BH, 2), dim3(D / 16 * 64), 0, st, w0, w0s, H,
+      hipLaunchKernelGGL((chunk_prefix<D, true>), dim3(BH, 2, D / 16), dim3(64), 0, st, w0, w0s, H,
                          pl.S, comp, win);
     } else {
       hipLaunchKernelGGL((chunk_compose_bf16<D, CH, false>), dim3(pl.S, BH), dim3(D / 8 * 64), 0,
                          st, (const bf16*)k, (const bf16*)v, H, N, a, pl.S, pl.L, comp);
-      hipLaunchKernelGGL((chunk_prefix<D, false>), dim3(BH, 1), dim3(D / 16 * 64), 0, st, w0, w0s,
+      hipLaunchKernelGGL((chunk_prefix<D, false>), dim3(BH, 1, D / 16), dim3(64), 0, st, w0, w0s,
                          H, pl.S, comp, win);
     }
   }
