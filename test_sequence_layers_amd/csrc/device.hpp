@@ -69,7 +69,6 @@ __device__ __forceinline__ f32x4 add4(f32x4 a, f32x4 b) { return a + b; }
 __device__ __forceinline__ bf16x8 ld8(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 __device__ __forceinline__ bf16x4 ld4(const bf16* p) { return *reinterpret_cast<const bf16x4*>(p); }
 
-// Four bf16 read down a column (stride in elements), e.g. a transposed operand from a row-major tile.
 // Identity tile as an MFMA B operand: lane (r, g) holds I[4g + i][r].
 __device__ __forceinline__ bf16x4 identity_b(int r, int g) {
   bf16x4 x;
@@ -85,6 +84,19 @@ __device__ __forceinline__ bf16x4 tile_columns(const bf16* base, int pitch, bf16
   return to_bf16x4(mma16(ld4(base + r * pitch + 4 * g), ident, zero4()));
 }
 
+// A 16 x 16 bf16 tile T (T[t][c] = base[t * pitch + c], base in LDS) in accumulator layout, by
+// gfx950's LDS transpose read (ds_read_b64_tr_b16): lane (r, g) gets T[4g + j][r]. Within each
+// 16-lane group that instruction gives lane t, as its element j, element t & 3 of the 8 bytes
+// addressed by lane 4j + (t >> 2); so lane 4j + q of group g addresses T[4g + j][4q .. 4q + 3].
+// base and pitch must keep those 8-byte reads aligned.
+__device__ __forceinline__ bf16x4 tile_tr(const bf16* base, int pitch, int l) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const int u = l & 15;
+  const bf16* p = base + (4 * (l >> 4) + (u >> 2)) * pitch + 4 * (u & 3);
+  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p));
+}
+
+// Four bf16 read down a column (stride in elements), e.g. a transposed operand from a row-major tile.
 __device__ __forceinline__ bf16x4 ld4_col(const bf16* p, int stride) {
   bf16x4 r;
   r[0] = p[0];

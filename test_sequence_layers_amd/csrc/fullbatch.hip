@@ -5,9 +5,10 @@
 // bf16 I/O: three launches. Heads whose D-vectors are adjacent in a token row are grouped up to
 // 128 bytes per row (2 heads of 32, 4 of 16, 1 of 64), so every staged row is a full, contiguous
 // cache line. Work items are (group, token split), one per workgroup.
-//   fb_partial_bf16: stream K, V tiles (double-buffered LDS, next tile prefetched into
-//                    registers) and accumulate the split's partial gradient
-//                    G_s = K_s^T (K_s W0 - V_s) with MFMA;
+//   fb_partial_bf16: stream K, V tiles (double-buffered LDS, up to four tiles in flight in
+//                    registers) and accumulate K_s^T K_s and K_s^T V_s with MFMA (operands by LDS
+//                    transpose reads), then the split's partial gradient
+//                    G_s = K_s^T (K_s W0 - V_s) = (K_s^T K_s) W0 - K_s^T V_s;
 //   fb_reduce_bf16:  W* = W0 - (eta/N) sum_s G_s, summed in a fixed split order (deterministic);
 //   fb_readout_bf16: stream Q and write O = Q W*.
 // HBM traffic is the algorithmic Q, K, V read plus the O write; the partials are d x d fp32 per
@@ -22,6 +23,11 @@ namespace {
 
 constexpr int kTile = 64;      // tokens per staged tile (bf16 path)
 constexpr int kThreads = 256;  // 4 waves per workgroup
+// Register sets per thread for staged tiles (bf16 path): a split's first tile_sets(D) tiles are
+// all in flight from the start, and tile it + tile_sets(D) loads as soon as tile it has moved to
+// LDS. The plan keeps splits within that many tiles where the workgroup count allows, so that a
+// workgroup waits for HBM about once. (Two for D = 64, whose MFMA operands need the registers.)
+constexpr int tile_sets(int D) { return D >= 64 ? 2 : 4; }
 constexpr int kTileF = 32;     // tokens per staged tile (fp32 path)
 
 // ---------------------------------------------------------------- bf16 I/O, MFMA
@@ -65,16 +71,25 @@ struct Stager {
   }
 };
 
-// 1. Partial gradient of one token split of one head group: G_s = K_s^T (K_s W0 - V_s).
+// 1. Partial gradient of one token split of one head group: G_s = K_s^T (K_s W0 - V_s), formed as
+// (K_s^T K_s) W0 - K_s^T V_s. The two D x D products accumulate over the split's tokens with every
+// MFMA operand read from LDS by transpose reads (contraction over tokens); W0 is applied once at
+// the end. Wave w owns task (head, 16-row block m); waves sharing a task split the 32-token steps.
+// K^T K is symmetric, so the wave accumulates its column block m, tiles (c, m) in accumulator
+// layout, which are the A operands of its row block m, k block c, for the product with W0.
 template <int D, int HG>
-__global__ __launch_bounds__(kThreads) void fb_partial_bf16(
+__global__ __launch_bounds__(kThreads, 4) void fb_partial_bf16(
     const bf16* __restrict__ k, const bf16* __restrict__ v, const float* __restrict__ w0,
     long long w0_bstride, int H, int N, int S, int tps, float* __restrict__ partial) {
   using G = Geo<D, HG>;
+  constexpr int NT = G::NT;
   constexpr long long DD = (long long)D * D;
+  constexpr int TASKS = HG * NT;  // (head, 16-row block) of G_s
+  constexpr int WPT = 4 / TASKS;  // waves per task
   __shared__ __align__(16) bf16 sK[2][kTile * G::P];
   __shared__ __align__(16) bf16 sV[2][kTile * G::P];
-  static_assert(sizeof(float) * 4 * D * 16 <= sizeof(bf16) * 2 * kTile * G::P, "partials fit in sK");
+  static_assert(TASKS * WPT == 4, "tasks divide the waves");
+  static_assert(sizeof(float) * 4 * 16 * D <= sizeof(bf16) * 2 * kTile * G::P, "partials fit in sK");
   float* sG = reinterpret_cast<float*>(&sK[0][0]);
 
   const int grp = blockIdx.x / S, s = blockIdx.x % S;
@@ -82,63 +97,81 @@ __global__ __launch_bounds__(kThreads) void fb_partial_bf16(
   const int n0 = s * tps, n1 = min(N, n0 + tps);
   const int ntiles = (n1 - n0 + kTile - 1) / kTile;
   const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
-  const bf16x4 ident = identity_b(r, g);
-  const int pair = w % G::PAIRS, tw = w / G::PAIRS;
-  const int hl = pair / G::NT, n = pair % G::NT;  // head within the group, column tile
+  const int task = w % TASKS, tw = w / TASKS;
+  const int hl = task / NT, m = task % NT;  // head within the group, row block
   const long long ts = (long long)H * D;
   const long long base = (long long)b * N * ts + (long long)h0 * D;
   const Stager<G> stk{k, base, ts, n1}, stv{v, base, ts, n1};
 
-  bf16x8 wb[G::KS];  // B operand: W0[:, 16n .. 16n + 16), contiguous k map
-  bf16x4 wb4;
-  {
-    const float* W0 = w0 + b * w0_bstride + (long long)(h0 + hl) * DD;
-    if constexpr (D >= 32) {
-      for (int ks = 0; ks < G::KS; ++ks)
-        for (int i = 0; i < 8; ++i) wb[ks][i] = (bf16)W0[(32 * ks + 8 * g + i) * D + 16 * n + r];
-    } else {
-      for (int i = 0; i < 4; ++i) wb4[i] = (bf16)W0[(4 * g + i) * D + 16 * n + r];
-    }
-  }
-  f32x4 acc[G::NT];
-  for (int m = 0; m < G::NT; ++m) acc[m] = zero4();
-  uint4 rk[G::PER], rv[G::PER];
-  stk.load(rk, n0);
-  stv.load(rv, n0);
-  for (int it = 0; it < ntiles; ++it) {
+  f32x4 kk[NT], kv[NT];  // tiles (c, m) of K^T K and (m, n) of K^T V
+  for (int c = 0; c < NT; ++c) kk[c] = kv[c] = zero4();
+  constexpr int SETS = tile_sets(D);
+  struct Regs {
+    uint4 k[G::PER], v[G::PER];
+  } sets[SETS];
+  auto load = [&](Regs& R, int it) {
+    stk.load(R.k, n0 + it * kTile);
+    stv.load(R.v, n0 + it * kTile);
+  };
+#pragma unroll
+  for (int u = 0; u < SETS; ++u)
+    if (u < ntiles) load(sets[u], u);
+  auto step = [&](int it, Regs& R) {
     const int buf = it & 1;
-    Stager<G>::store(sK[buf], rk);
-    Stager<G>::store(sV[buf], rv);
-    if (it + 1 < ntiles) {  // the next tile loads while this one is processed
-      stk.load(rk, n0 + (it + 1) * kTile);
-      stv.load(rv, n0 + (it + 1) * kTile);
-    }
+    Stager<G>::store(sK[buf], R.k);
+    Stager<G>::store(sV[buf], R.v);
+    if (it + SETS < ntiles) load(R, it + SETS);
     __syncthreads();
     const bf16* tK = sK[buf] + hl * D;
     const bf16* tV = sV[buf] + hl * D;
-    for (int p = tw; p < 4; p += G::WPP) {
-      f32x4 e;  // E = K W0 - V, 16 tokens x 16 columns (C layout: row = token 16p + 4g + j)
-      for (int j = 0; j < 4; ++j) e[j] = -(float)tV[(16 * p + 4 * g + j) * G::P + 16 * n + r];
-      if constexpr (D >= 32) {
-        for (int ks = 0; ks < G::KS; ++ks) e = mma32(ld8(&tK[(16 * p + r) * G::P + 32 * ks + 8 * g]), wb[ks], e);
-      } else {
-        e = mma16(ld4(&tK[(16 * p + r) * G::P + 4 * g]), wb4, e);
+    for (int ks = tw; ks < kTile / 32; ks += WPT) {
+      // Operands over 32 tokens, k map {4g + j} u {16 + 4g + j}: lane (r, g) holds column r.
+      const bf16* k0 = tK + 32 * ks * G::P;
+      const bf16* v0 = tV + 32 * ks * G::P;
+      // (Block m is read on its own: m varies by wave, and indexing registers with it would
+      // become select chains.)
+      const bf16x8 km = cat8(tile_tr(k0 + 16 * m, G::P, l), tile_tr(k0 + 16 * G::P + 16 * m, G::P, l));
+      bf16x8 tk[NT], tv[NT];
+      for (int c = 0; c < NT; ++c) {
+        tk[c] = cat8(tile_tr(k0 + 16 * c, G::P, l), tile_tr(k0 + 16 * G::P + 16 * c, G::P, l));
+        tv[c] = cat8(tile_tr(v0 + 16 * c, G::P, l), tile_tr(v0 + 16 * G::P + 16 * c, G::P, l));
       }
-      const bf16x4 eb = to_bf16x4(e);  // acc[:, n] += K^T E (E's C layout is the B operand)
-      for (int m = 0; m < G::NT; ++m)
-        acc[m] = mma16(tile_columns(&tK[16 * p * G::P + 16 * m], G::P, ident, r, g), eb, acc[m]);
+      for (int c = 0; c < NT; ++c) kk[c] = mma32(tk[c], km, kk[c]);
+      for (int n = 0; n < NT; ++n) kv[n] = mma32(km, tv[n], kv[n]);
+    }
+  };
+  for (int it = 0; it < ntiles; it += SETS) {
+#pragma unroll
+    for (int u = 0; u < SETS; ++u)
+      if (it + u < ntiles) step(it + u, sets[u]);
+  }
+  // Row block m of (K^T K) W0 - K^T V. Tile (c, m) of K^T K in accumulator layout is, by
+  // symmetry, the A operand of rows 16m.. and k block c. Kept in its own accumulators (the
+  // 16x16x16 products must not take a 16x16x32 result as their accumulator input).
+  // W0 (shared by every split of the head, so an L2 read) is loaded only here, to keep the
+  // registers of the tile loop free.
+  const float* W0 = w0 + b * w0_bstride + (long long)(h0 + hl) * DD;
+  bf16x4 ka[NT];
+  for (int c = 0; c < NT; ++c) ka[c] = to_bf16x4(kk[c]);
+  f32x4 gw[NT];
+  for (int n = 0; n < NT; ++n) {
+    gw[n] = zero4();
+    for (int c = 0; c < NT; ++c) {
+      bf16x4 wb;  // B operand: W0[16c + 4g + i][16n + r]
+      for (int i = 0; i < 4; ++i) wb[i] = (bf16)W0[(16 * c + 4 * g + i) * D + 16 * n + r];
+      gw[n] = mma16(ka[c], wb, gw[n]);
     }
   }
-  __syncthreads();  // tile buffers free: sum the waves sharing a pair through sK, in a fixed order
-  for (int m = 0; m < G::NT; ++m)
-    for (int j = 0; j < 4; ++j) sG[(w * D + 16 * m + 4 * g + j) * 16 + r] = acc[m][j];
+  __syncthreads();  // tile buffers free: sum the waves sharing a task through sK, in a fixed order
+  for (int n = 0; n < NT; ++n)
+    for (int j = 0; j < 4; ++j) sG[(w * 16 + 4 * g + j) * D + 16 * n + r] = gw[n][j] - kv[n][j];
   __syncthreads();
   float* part = partial + ((long long)grp * S + s) * HG * DD;
   for (int e = threadIdx.x; e < HG * D * D; e += kThreads) {
     const int hh = e / (D * D), rem = e % (D * D), i = rem / D, c = rem % D;
-    const int pr = hh * G::NT + c / 16;
+    const int tk = hh * NT + i / 16;
     float sum = 0.f;
-    for (int t = 0; t < G::WPP; ++t) sum += sG[((t * G::PAIRS + pr) * D + i) * 16 + (c % 16)];
+    for (int t = 0; t < WPT; ++t) sum += sG[((t * TASKS + tk) * 16 + i % 16) * D + c];
     part[e] = sum;
   }
 }
@@ -192,8 +225,11 @@ __global__ __launch_bounds__(kThreads) void fb_readout_bf16(const bf16* __restri
   const long long base = (long long)b * N * ts + (long long)h0 * D;
   const Stager<G> stq{q, base, ts, n1};
 
-  uint4 rq[G::PER];
-  stq.load(rq, n0);
+  constexpr int SETS = tile_sets(D);
+  uint4 sets[SETS][G::PER];
+#pragma unroll
+  for (int u = 0; u < SETS; ++u)
+    if (u < ntiles) stq.load(sets[u], n0 + u * kTile);
   bf16x8 wa[G::KS];  // A = W*^T: lane holds W*[k][16n + r], contiguous k map
   bf16x4 wa4;
   {
@@ -205,11 +241,11 @@ __global__ __launch_bounds__(kThreads) void fb_readout_bf16(const bf16* __restri
       for (int i = 0; i < 4; ++i) wa4[i] = (bf16)Ws[(4 * g + i) * D + 16 * n + r];
     }
   }
-  for (int it = 0; it < ntiles; ++it) {
+  auto step = [&](int it, uint4* rq) {
     const int buf = it & 1;
     const int t0 = n0 + it * kTile;
     Stager<G>::store(sQ[buf], rq);
-    if (it + 1 < ntiles) stq.load(rq, t0 + kTile);
+    if (it + SETS < ntiles) stq.load(rq, t0 + SETS * kTile);
     __syncthreads();
     const bf16* tQ = sQ[buf] + hl * D;
     bf16* tO = sO[buf] + hl * D;
@@ -230,6 +266,11 @@ __global__ __launch_bounds__(kThreads) void fb_readout_bf16(const bf16* __restri
         if (t0 + row < n1) st16(o + base + (long long)(t0 + row) * ts + col, ld16(&sO[buf][row * G::P + col]));
       }
     }
+  };
+  for (int it = 0; it < ntiles; it += SETS) {
+#pragma unroll
+    for (int u = 0; u < SETS; ++u)
+      if (it + u < ntiles) step(it + u, sets[u]);
   }
 }
 
@@ -339,10 +380,13 @@ int head_group(int H, int D) {
   return hg;
 }
 
-FbPlan plan_splits(int groups, int N) {
+FbPlan plan_splits(int groups, int N, int sets) {
   const int tiles = (N + kTile - 1) / kTile;
-  // Aim for about 1024 workgroups (4 per CU on 256 CUs), never below one 64-token tile each.
+  // Aim for about 1024 workgroups (4 per CU on 256 CUs), never below one 64-token tile each;
+  // more splits (up to 4096 workgroups) where that keeps every split within `sets` tiles.
   int splits = (1024 + groups - 1) / groups;
+  const int need = (tiles + sets - 1) / sets;
+  if (splits < need && (long long)groups * need <= 4096) splits = need;
   if (splits > tiles) splits = tiles;
   if (splits < 1) splits = 1;
   const int tiles_per = (tiles + splits - 1) / splits;
@@ -357,7 +401,7 @@ hipError_t launch_bf16(int B, int H, int N, float eta, const void* q, const void
                        const float* w0, long long w0s, void* o, float* w_out, void* ws,
                        hipStream_t st) {
   const int groups = B * (H / HG);
-  const FbPlan pl = plan_splits(groups, N);
+  const FbPlan pl = plan_splits(groups, N, tile_sets(D));
   float* partial = static_cast<float*>(ws);
   float* wstar = partial + (size_t)groups * pl.splits * HG * D * D;
   const int items = groups * pl.splits;
@@ -376,7 +420,7 @@ hipError_t launch_f32(int B, int H, int N, float eta, const void* q, const void*
                       const float* w0, long long w0s, void* o, float* w_out, void* ws,
                       hipStream_t st) {
   const int BH = B * H;
-  const FbPlan pl = plan_splits(BH, N);
+  const FbPlan pl = plan_splits(BH, N, 1);
   float* partial = static_cast<float*>(ws);
   float* wstar = partial + (size_t)BH * pl.splits * D * D;
   const dim3 grid(pl.splits, BH);
@@ -391,17 +435,19 @@ hipError_t launch_f32(int B, int H, int N, float eta, const void* q, const void*
 
 }  // namespace
 
-FbPlan fb_plan(int B, int H, int N, int D) { return plan_splits(B * (H / head_group(H, D)), N); }
+FbPlan fb_plan(int B, int H, int N, int D) {
+  return plan_splits(B * (H / head_group(H, D)), N, tile_sets(D));
+}
 
 size_t fb_workspace_bytes(bool bf16_io, int B, int H, int N, int D) {
   const size_t dd = (size_t)D * D * sizeof(float);
   if (!bf16_io) {
-    const FbPlan p = plan_splits(B * H, N);
+    const FbPlan p = plan_splits(B * H, N, 1);
     return (size_t)B * H * p.splits * dd + (size_t)B * H * dd;
   }
   const int hg = head_group(H, D);
   const int groups = B * (H / hg);
-  const FbPlan p = plan_splits(groups, N);
+  const FbPlan p = plan_splits(groups, N, tile_sets(D));
   return (size_t)groups * p.splits * hg * dd + (size_t)groups * hg * dd;
 }
 
