@@ -9,12 +9,16 @@
 //                    registers) and accumulate K_s^T K_s and K_s^T V_s with MFMA (operands by LDS
 //                    transpose reads), then the split's partial gradient
 //                    G_s = K_s^T (K_s W0 - V_s) = (K_s^T K_s) W0 - K_s^T V_s;
-//   fb_reduce_bf16:  W* = W0 - (eta/N) sum_s G_s, summed in a fixed split order (deterministic);
-//   fb_readout_bf16: stream Q and write O = Q W*.
+//   fb_reduce_bf16:  W* = W0 - (eta/N) sum_s G_s, summed in a fixed split order (deterministic),
+//                    stored in bf16 as the read-out's MFMA operands;
+//   fb_readout_bf16: stream Q straight into MFMA operands, one wave per 16-token block, and
+//                    write O = Q W*.
 // HBM traffic is the algorithmic Q, K, V read plus the O write; the partials are d x d fp32 per
 // split and stay in L2 / Infinity Cache.
 //
 // fp32 I/O: three plain-FMA launches (partial gradients, fixed-order reduction, read-out).
+#include <type_traits>
+
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -176,13 +180,27 @@ __global__ __launch_bounds__(kThreads, 4) void fb_partial_bf16(
   }
 }
 
+// W* for the read-out is stored in bf16 as the read-out's MFMA A operands (W*^T tiles), so that
+// a lane loads each operand with one access. Operand (head hl, column tile n, k step ks), lane
+// l = r + 16g, element i holds W*[kb * ks + e * g + i][16n + r] with e = 8 (D >= 32, k steps of
+// 32) or e = 4 (D = 16, one k step of 16), kb = 4e.
+template <int D>
+constexpr int kOpElems = D >= 32 ? 8 : 4;
+
+template <int D>
+__device__ __forceinline__ int wstar_operand_offset(int hl, int row, int col) {
+  constexpr int NT = D / 16, E = kOpElems<D>, KS = D / (4 * E);
+  return (((hl * NT + col / 16) * KS + row / (4 * E)) * 64 + col % 16 + 16 * ((row % (4 * E)) / E)) * E +
+         row % E;
+}
+
 // 2. W* = W0 - (eta/N) sum_s G_s, summed over the splits in a fixed order (deterministic). One
 // thread per element; 16 of its split partials are in flight at a time.
 template <int D, int HG>
 __global__ __launch_bounds__(kThreads) void fb_reduce_bf16(const float* __restrict__ partial,
                                                            int S, const float* __restrict__ w0,
                                                            long long w0_bstride, int H,
-                                                           float scale, float* __restrict__ wstar,
+                                                           float scale, bf16* __restrict__ wop,
                                                            float* __restrict__ w_out) {
   constexpr int E = HG * D * D;               // elements of one group's matrices
   constexpr int WG_PER_GROUP = E / kThreads;  // workgroups per group, one element per thread
@@ -199,78 +217,95 @@ __global__ __launch_bounds__(kThreads) void fb_reduce_bf16(const float* __restri
   }
   const int h = (grp % (H / HG)) * HG + hh;
   const float wv = w0[b * w0_bstride + (long long)h * DD + rem] - scale * sum;
-  wstar[(long long)grp * E + e] = wv;
+  wop[(long long)grp * E + wstar_operand_offset<D>(hh, rem / D, rem % D)] = (bf16)wv;
   if (w_out) w_out[((long long)b * H + h) * DD + rem] = wv;
 }
 
-// 3. O = Q W*, computed as O^T = W*^T Q^T (lane (r, g) gets 4 adjacent outputs of a token); the
-// O tile is assembled in LDS and written as full 128-byte rows.
+// 3. O = Q W*, computed as O^T = W*^T Q^T (lane (r, g) gets 4 adjacent outputs of token r). Each
+// wave streams its own 16-token blocks of the split (blocks w, w + 4, ...), kReadSets of them in
+// flight from the start, and moves them through a wave-private LDS tile: full-row 16-byte pieces
+// to and from HBM, operand-shaped pieces to and from the matrix cores. No workgroup barriers:
+// a wave's LDS operations execute in order, and a wavefront-scope fence keeps the compiler from
+// reordering them.
+constexpr int kReadSets = 4;
+
 template <int D, int HG>
 __global__ __launch_bounds__(kThreads) void fb_readout_bf16(const bf16* __restrict__ q,
-                                                            const float* __restrict__ wstar,
+                                                            const bf16* __restrict__ wop,
                                                             int H, int N, int S, int tps,
                                                             bf16* __restrict__ o) {
   using G = Geo<D, HG>;
-  constexpr long long DD = (long long)D * D;
-  __shared__ __align__(16) bf16 sQ[2][kTile * G::P];
-  __shared__ __align__(16) bf16 sO[2][kTile * G::P];
+  constexpr int NT = D / 16, E = kOpElems<D>, KS = D / (4 * E);
+  constexpr int BP = 16 * G::CPR;       // 16-byte pieces of a 16-token block
+  constexpr int PPL = (BP + 63) / 64;   // pieces per lane
+  __shared__ __align__(16) bf16 sQ[4][16 * G::P];
+  __shared__ __align__(16) bf16 sO[4][16 * G::P];
   const int grp = blockIdx.x / S, s = blockIdx.x % S;
   const int b = grp / (H / HG), h0 = (grp % (H / HG)) * HG;
   const int n0 = s * tps, n1 = min(N, n0 + tps);
-  const int ntiles = (n1 - n0 + kTile - 1) / kTile;
   const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
-  const int pair = w % G::PAIRS, tw = w / G::PAIRS;
-  const int hl = pair / G::NT, n = pair % G::NT;
+  const int blocks = (n1 - n0 + 15) / 16;
+  const int mine = blocks > w ? (blocks - w + 3) / 4 : 0;
   const long long ts = (long long)H * D;
   const long long base = (long long)b * N * ts + (long long)h0 * D;
-  const Stager<G> stq{q, base, ts, n1};
+  bf16* myQ = sQ[w];
+  bf16* myO = sO[w];
 
-  constexpr int SETS = tile_sets(D);
-  uint4 sets[SETS][G::PER];
-#pragma unroll
-  for (int u = 0; u < SETS; ++u)
-    if (u < ntiles) stq.load(sets[u], n0 + u * kTile);
-  bf16x8 wa[G::KS];  // A = W*^T: lane holds W*[k][16n + r], contiguous k map
-  bf16x4 wa4;
+  using Op = typename std::conditional<(D >= 32), bf16x8, bf16x4>::type;
+  Op wa[HG][NT][KS];  // A operands W*^T
   {
-    const float* Ws = wstar + (long long)grp * HG * DD + hl * DD;
-    if constexpr (D >= 32) {
-      for (int ks = 0; ks < G::KS; ++ks)
-        for (int i = 0; i < 8; ++i) wa[ks][i] = (bf16)Ws[(32 * ks + 8 * g + i) * D + 16 * n + r];
-    } else {
-      for (int i = 0; i < 4; ++i) wa4[i] = (bf16)Ws[(4 * g + i) * D + 16 * n + r];
-    }
+    const bf16* src = wop + (long long)grp * HG * D * D;
+    for (int hl = 0; hl < HG; ++hl)
+      for (int n = 0; n < NT; ++n)
+        for (int ks = 0; ks < KS; ++ks)
+          wa[hl][n][ks] = *reinterpret_cast<const Op*>(src + (((hl * NT + n) * KS + ks) * 64 + l) * E);
   }
-  auto step = [&](int it, uint4* rq) {
-    const int buf = it & 1;
-    const int t0 = n0 + it * kTile;
-    Stager<G>::store(sQ[buf], rq);
-    if (it + SETS < ntiles) stq.load(rq, t0 + SETS * kTile);
-    __syncthreads();
-    const bf16* tQ = sQ[buf] + hl * D;
-    bf16* tO = sO[buf] + hl * D;
-    for (int p = tw; p < 4; p += G::WPP) {
-      f32x4 acc = zero4();
-      if constexpr (D >= 32) {
-        for (int ks = 0; ks < G::KS; ++ks) acc = mma32(wa[ks], ld8(&tQ[(16 * p + r) * G::P + 32 * ks + 8 * g]), acc);
-      } else {
-        acc = mma16(wa4, ld4(&tQ[(16 * p + r) * G::P + 4 * g]), acc);
-      }
-      *reinterpret_cast<bf16x4*>(&tO[(16 * p + r) * G::P + 16 * n + 4 * g]) = to_bf16x4(acc);
-    }
-    __syncthreads();
-    for (int i = 0; i < G::PER; ++i) {
-      const int c = threadIdx.x + i * kThreads;
-      if (G::PIECES % kThreads == 0 || c < G::PIECES) {
-        const int row = c / G::CPR, col = (c % G::CPR) * 8;
-        if (t0 + row < n1) st16(o + base + (long long)(t0 + row) * ts + col, ld16(&sO[buf][row * G::P + col]));
-      }
+  struct Regs {
+    uint4 x[PPL];
+  } sets[kReadSets];
+  auto valid = [&](int c) { return BP % 64 == 0 || c < BP; };
+  auto load = [&](Regs& R, int i) {
+    const int t0 = n0 + 16 * (w + 4 * i);
+    for (int u = 0; u < PPL; ++u) {
+      const int c = l + 64 * u, row = c / G::CPR;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (valid(c) && t0 + row < n1) v = ld16(q + base + (t0 + row) * ts + (c % G::CPR) * 8);
+      R.x[u] = v;
     }
   };
-  for (int it = 0; it < ntiles; it += SETS) {
 #pragma unroll
-    for (int u = 0; u < SETS; ++u)
-      if (it + u < ntiles) step(it + u, sets[u]);
+  for (int u = 0; u < kReadSets; ++u)
+    if (u < mine) load(sets[u], u);
+  auto step = [&](int i, Regs& R) {
+    const int t0 = n0 + 16 * (w + 4 * i);
+    for (int u = 0; u < PPL; ++u) {
+      const int c = l + 64 * u;
+      if (valid(c)) st16(myQ + (c / G::CPR) * G::P + (c % G::CPR) * 8, R.x[u]);
+    }
+    if (i + kReadSets < mine) load(R, i + kReadSets);
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    for (int hl = 0; hl < HG; ++hl)
+      for (int n = 0; n < NT; ++n) {
+        f32x4 acc = zero4();
+        for (int ks = 0; ks < KS; ++ks) {
+          const Op qb = *reinterpret_cast<const Op*>(myQ + r * G::P + hl * D + 4 * E * ks + E * g);
+          if constexpr (D >= 32) acc = mma32(wa[hl][n][ks], qb, acc);
+          else acc = mma16(wa[hl][n][ks], qb, acc);
+        }
+        *reinterpret_cast<bf16x4*>(myO + r * G::P + hl * D + 16 * n + 4 * g) = to_bf16x4(acc);
+      }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    for (int u = 0; u < PPL; ++u) {
+      const int c = l + 64 * u, row = c / G::CPR;
+      if (valid(c) && t0 + row < n1)
+        st16(o + base + (t0 + row) * ts + (c % G::CPR) * 8, ld16(myO + row * G::P + (c % G::CPR) * 8));
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  };
+  for (int i = 0; i < mine; i += kReadSets) {
+#pragma unroll
+    for (int u = 0; u < kReadSets; ++u)
+      if (i + u < mine) step(i + u, sets[u]);
   }
 }
 
@@ -403,15 +438,15 @@ hipError_t launch_bf16(int B, int H, int N, float eta, const void* q, const void
   const int groups = B * (H / HG);
   const FbPlan pl = plan_splits(groups, N, tile_sets(D));
   float* partial = static_cast<float*>(ws);
-  float* wstar = partial + (size_t)groups * pl.splits * HG * D * D;
+  bf16* wop = reinterpret_cast<bf16*>(partial + (size_t)groups * pl.splits * HG * D * D);
   const int items = groups * pl.splits;
   hipLaunchKernelGGL((fb_partial_bf16<D, HG>), dim3(items), dim3(kThreads), 0, st, (const bf16*)k,
                      (const bf16*)v, w0, w0s, H, N, pl.splits, pl.tokens_per_split, partial);
   hipLaunchKernelGGL((fb_reduce_bf16<D, HG>), dim3(groups * (HG * D * D / kThreads)),
-                     dim3(kThreads), 0, st, partial, pl.splits, w0, w0s, H, eta / (float)N, wstar,
+                     dim3(kThreads), 0, st, partial, pl.splits, w0, w0s, H, eta / (float)N, wop,
                      w_out);
   hipLaunchKernelGGL((fb_readout_bf16<D, HG>), dim3(items), dim3(kThreads), 0, st, (const bf16*)q,
-                     wstar, H, N, pl.splits, pl.tokens_per_split, (bf16*)o);
+                     wop, H, N, pl.splits, pl.tokens_per_split, (bf16*)o);
   return hipGetLastError();
 }
 
