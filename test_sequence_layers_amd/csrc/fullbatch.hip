@@ -6,15 +6,15 @@
 // 128 bytes per row (2 heads of 32, 4 of 16, 1 of 64), so every staged row is a full, contiguous
 // cache line. Work items are (group, token split), one per workgroup.
 //   fb_partial_bf16: stream K, V tiles (double-buffered LDS, up to four tiles in flight in
-//                    registers) and accumulate K_s^T K_s and K_s^T V_s with MFMA (operands by LDS
-//                    transpose reads), then the split's partial gradient
-//                    G_s = K_s^T (K_s W0 - V_s) = (K_s^T K_s) W0 - K_s^T V_s;
-//   fb_reduce_bf16:  W* = W0 - (eta/N) sum_s G_s, summed in a fixed split order (deterministic),
-//                    stored in bf16 as the read-out's MFMA operands;
+//                    registers) and accumulate the split's K_s^T K_s and K_s^T V_s with MFMA
+//                    (operands by LDS transpose reads); since K^T (K W0 - V) = (K^T K) W0 - K^T V,
+//                    these two sums carry the gradient;
+//   fb_reduce_bf16:  W* = W0 - (eta/N) (sum_s K_s^T K_s W0 - sum_s K_s^T V_s), summed in a fixed
+//                    split order (deterministic), stored in bf16 as the read-out's MFMA operands;
 //   fb_readout_bf16: stream Q straight into MFMA operands, one wave per 16-token block, and
 //                    write O = Q W*.
-// HBM traffic is the algorithmic Q, K, V read plus the O write; the partials are d x d fp32 per
-// split and stay in L2 / Infinity Cache.
+// HBM traffic is the algorithmic Q, K, V read plus the O write; the partials are two d x d fp32
+// matrices per split and stay in L2 / Infinity Cache.
 //
 // fp32 I/O: three plain-FMA launches (partial gradients, fixed-order reduction, read-out).
 #include <type_traits>
@@ -75,12 +75,54 @@ struct Stager {
   }
 };
 
-// 1. Partial gradient of one token split of one head group: G_s = K_s^T (K_s W0 - V_s), formed as
-// (K_s^T K_s) W0 - K_s^T V_s. The two D x D products accumulate over the split's tokens with every
-// MFMA operand read from LDS by transpose reads (contraction over tokens); W0 is applied once at
-// the end. Wave w owns task (head, 16-row block m); waves sharing a task split the 32-token steps.
-// K^T K is symmetric, so the wave accumulates its column block m, tiles (c, m) in accumulator
-// layout, which are the A operands of its row block m, k block c, for the product with W0.
+// W* for the read-out is stored in bf16 as the read-out's MFMA A operands (W*^T tiles), so that
+// a lane loads each operand with one access. Operand (head hl, column tile n, k step ks), lane
+// l = r + 16g, element i holds W*[kb * ks + e * g + i][16n + r] with e = 8 (D >= 32, k steps of
+// 32) or e = 4 (D = 16, one k step of 16), kb = 4e.
+template <int D>
+constexpr int kOpElems = D >= 32 ? 8 : 4;
+
+template <int D>
+__device__ __forceinline__ int wstar_operand_offset(int hl, int row, int col) {
+  constexpr int NT = D / 16, E = kOpElems<D>, KS = D / (4 * E);
+  return (((hl * NT + col / 16) * KS + row / (4 * E)) * 64 + col % 16 + 16 * ((row % (4 * E)) / E)) * E +
+         row % E;
+}
+
+// Row block m of W* = W0 - scale ((K^T K) W0 - K^T V) for head hl of a group, from the summed
+// accumulator tiles acc[0 .. NT) = (c, m) of K^T K and acc[NT .. 2NT) = (m, n) of K^T V. By
+// symmetry, tile (c, m) of K^T K in accumulator layout is the A operand of rows 16m.. and k block
+// c. (The 16x16x16 products keep their own accumulators: they must not take a 16x16x32 result as
+// their accumulator input.) Writes the read-out operands and, if w_out is set, W* in fp32.
+template <int D>
+__device__ __forceinline__ void wstar_rows(const f32x4* acc, int hl, int m, const float* W0,
+                                           float scale, bf16* wop_grp, float* w_out, int r, int g) {
+  constexpr int NT = D / 16;
+  bf16x4 ka[NT];
+  for (int c = 0; c < NT; ++c) ka[c] = to_bf16x4(acc[c]);
+  for (int n = 0; n < NT; ++n) {
+    f32x4 gw = zero4();
+    for (int c = 0; c < NT; ++c) {
+      bf16x4 wb;  // B operand: W0[16c + 4g + i][16n + r]
+      for (int i = 0; i < 4; ++i) wb[i] = (bf16)W0[(16 * c + 4 * g + i) * D + 16 * n + r];
+      gw = mma16(ka[c], wb, gw);
+    }
+    for (int j = 0; j < 4; ++j) {  // W*[16m + 4g + j][16n + r]
+      const int row = 16 * m + 4 * g + j, col = 16 * n + r;
+      const float wv = W0[row * D + col] - scale * (gw[j] - acc[NT + n][j]);
+      wop_grp[wstar_operand_offset<D>(hl, row, col)] = (bf16)wv;
+      if (w_out) w_out[row * D + col] = wv;
+    }
+  }
+}
+
+// 1. Gradient sums of one token split of one head group: the split's gradient at W0 is
+// K_s^T (K_s W0 - V_s) = (K_s^T K_s) W0 - K_s^T V_s, so the kernel accumulates K_s^T K_s and
+// K_s^T V_s over the split's tokens, every MFMA operand read from LDS by transpose reads
+// (contraction over tokens); W0 is applied once per group by the reduction. Wave w owns task
+// (head, 16-row block m); waves sharing a task split the 32-token steps. K^T K is symmetric, so
+// the wave accumulates its column block m, tiles (c, m) in accumulator layout, which are the A
+// operands of row block m, k block c, in the product with W0.
 template <int D, int HG>
 __global__ __launch_bounds__(kThreads, 4) void fb_partial_bf16(
     const bf16* __restrict__ k, const bf16* __restrict__ v, const float* __restrict__ w0,
@@ -93,7 +135,8 @@ __global__ __launch_bounds__(kThreads, 4) void fb_partial_bf16(
   __shared__ __align__(16) bf16 sK[2][kTile * G::P];
   __shared__ __align__(16) bf16 sV[2][kTile * G::P];
   static_assert(TASKS * WPT == 4, "tasks divide the waves");
-  static_assert(sizeof(float) * 4 * 16 * D <= sizeof(bf16) * 2 * kTile * G::P, "partials fit in sK");
+  static_assert(sizeof(float) * (4 - TASKS) * 2 * NT * 256 <= sizeof(bf16) * 2 * kTile * G::P,
+                "sums of the waves sharing a task fit in sK");
   float* sG = reinterpret_cast<float*>(&sK[0][0]);
 
   const int grp = blockIdx.x / S, s = blockIdx.x % S;
@@ -149,76 +192,86 @@ __global__ __launch_bounds__(kThreads, 4) void fb_partial_bf16(
     for (int u = 0; u < SETS; ++u)
       if (it + u < ntiles) step(it + u, sets[u]);
   }
-  // Row block m of (K^T K) W0 - K^T V. Tile (c, m) of K^T K in accumulator layout is, by
-  // symmetry, the A operand of rows 16m.. and k block c. Kept in its own accumulators (the
-  // 16x16x16 products must not take a 16x16x32 result as their accumulator input).
-  // W0 (shared by every split of the head, so an L2 read) is loaded only here, to keep the
-  // registers of the tile loop free.
-  const float* W0 = w0 + b * w0_bstride + (long long)(h0 + hl) * DD;
-  bf16x4 ka[NT];
-  for (int c = 0; c < NT; ++c) ka[c] = to_bf16x4(kk[c]);
-  f32x4 gw[NT];
-  for (int n = 0; n < NT; ++n) {
-    gw[n] = zero4();
+  // The split's partial record holds, per task (head, row block m), the accumulator tiles
+  // (c, m) of K^T K then (m, n) of K^T V, lane by lane (16 bytes a lane, coalesced). Waves
+  // sharing a task add theirs first through sK, in a fixed order.
+  float* part = partial + ((long long)grp * S + s) * (2 * HG * D * D) + (long long)task * (2 * NT * 256);
+  if constexpr (WPT > 1) {
+    __syncthreads();  // tile buffers free
+    if (tw > 0)
+      for (int c = 0; c < NT; ++c) {
+        *reinterpret_cast<f32x4*>(sG + (((w - TASKS) * 2 * NT + c) * 64 + l) * 4) = kk[c];
+        *reinterpret_cast<f32x4*>(sG + (((w - TASKS) * 2 * NT + NT + c) * 64 + l) * 4) = kv[c];
+      }
+    __syncthreads();
+    if (tw == 0)
+      for (int t = 1; t < WPT; ++t) {
+        const int wt = (t - 1) * TASKS + task;
+        for (int c = 0; c < NT; ++c) {
+          kk[c] += *reinterpret_cast<const f32x4*>(sG + ((wt * 2 * NT + c) * 64 + l) * 4);
+          kv[c] += *reinterpret_cast<const f32x4*>(sG + ((wt * 2 * NT + NT + c) * 64 + l) * 4);
+        }
+      }
+  }
+  if (tw == 0)
     for (int c = 0; c < NT; ++c) {
-      bf16x4 wb;  // B operand: W0[16c + 4g + i][16n + r]
-      for (int i = 0; i < 4; ++i) wb[i] = (bf16)W0[(16 * c + 4 * g + i) * D + 16 * n + r];
-      gw[n] = mma16(ka[c], wb, gw[n]);
+      *reinterpret_cast<f32x4*>(part + (c * 64 + l) * 4) = kk[c];
+      *reinterpret_cast<f32x4*>(part + ((NT + c) * 64 + l) * 4) = kv[c];
     }
-  }
-  __syncthreads();  // tile buffers free: sum the waves sharing a task through sK, in a fixed order
-  for (int n = 0; n < NT; ++n)
-    for (int j = 0; j < 4; ++j) sG[(w * 16 + 4 * g + j) * D + 16 * n + r] = gw[n][j] - kv[n][j];
-  __syncthreads();
-  float* part = partial + ((long long)grp * S + s) * HG * DD;
-  for (int e = threadIdx.x; e < HG * D * D; e += kThreads) {
-    const int hh = e / (D * D), rem = e % (D * D), i = rem / D, c = rem % D;
-    const int tk = hh * NT + i / 16;
-    float sum = 0.f;
-    for (int t = 0; t < WPT; ++t) sum += sG[((t * TASKS + tk) * 16 + i % 16) * D + c];
-    part[e] = sum;
-  }
 }
 
-// W* for the read-out is stored in bf16 as the read-out's MFMA A operands (W*^T tiles), so that
-// a lane loads each operand with one access. Operand (head hl, column tile n, k step ks), lane
-// l = r + 16g, element i holds W*[kb * ks + e * g + i][16n + r] with e = 8 (D >= 32, k steps of
-// 32) or e = 4 (D = 16, one k step of 16), kb = 4e.
-template <int D>
-constexpr int kOpElems = D >= 32 ? 8 : 4;
-
-template <int D>
-__device__ __forceinline__ int wstar_operand_offset(int hl, int row, int col) {
-  constexpr int NT = D / 16, E = kOpElems<D>, KS = D / (4 * E);
-  return (((hl * NT + col / 16) * KS + row / (4 * E)) * 64 + col % 16 + 16 * ((row % (4 * E)) / E)) * E +
-         row % E;
-}
-
-// 2. W* = W0 - (eta/N) sum_s G_s, summed over the splits in a fixed order (deterministic). One
-// thread per element; 16 of its split partials are in flight at a time.
+// 2. W* = W0 - (eta/N) ((sum_s K_s^T K_s) W0 - sum_s K_s^T V_s), a launch of its own (summing
+// the records inside the first launch, by its last split per group, needs device-coherent
+// accesses across XCDs and measured slower). One workgroup per (group, task): wave t sums the
+// task's accumulator tiles of splits t, t + 4, ... (loads of several splits in flight), the four
+// sums are added in a fixed order (deterministic), and wave 0 forms the task's rows of W*.
 template <int D, int HG>
 __global__ __launch_bounds__(kThreads) void fb_reduce_bf16(const float* __restrict__ partial,
                                                            int S, const float* __restrict__ w0,
                                                            long long w0_bstride, int H,
                                                            float scale, bf16* __restrict__ wop,
                                                            float* __restrict__ w_out) {
-  constexpr int E = HG * D * D;               // elements of one group's matrices
-  constexpr int WG_PER_GROUP = E / kThreads;  // workgroups per group, one element per thread
+  constexpr int NT = D / 16, TASKS = HG * NT, T2 = 2 * NT;
   constexpr long long DD = (long long)D * D;
-  const int grp = blockIdx.x / WG_PER_GROUP;
-  const int e = (blockIdx.x % WG_PER_GROUP) * kThreads + threadIdx.x;
-  const int b = grp / (H / HG), hh = e / (D * D), rem = e % (D * D);
-  const float* pg = partial + (long long)grp * S * E + e;
-  float sum = 0.f;
-  for (int s0 = 0; s0 < S; s0 += 16) {
-    float val[16];
-    for (int u = 0; u < 16; ++u) val[u] = s0 + u < S ? pg[(long long)(s0 + u) * E] : 0.f;
-    for (int u = 0; u < 16; ++u) sum += val[u];
+  constexpr int WPER = (D * D + kThreads - 1) / kThreads;
+  __shared__ f32x4 sSum[3][T2][64];
+  __shared__ float sW0[D * D];
+  const int grp = blockIdx.x / TASKS, task = blockIdx.x % TASKS;
+  const int hl = task / NT, m = task % NT;
+  const int b = grp / (H / HG), h = (grp % (H / HG)) * HG + hl;
+  const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
+  const float* W0 = w0 + b * w0_bstride + (long long)h * DD;
+  float w0v[WPER];  // W0, loaded with the records and staged in LDS for wave 0
+  for (int i = 0; i < WPER; ++i) {
+    const int e = threadIdx.x + i * kThreads;
+    w0v[i] = (D * D) % kThreads == 0 || e < D * D ? W0[e] : 0.f;
   }
-  const int h = (grp % (H / HG)) * HG + hh;
-  const float wv = w0[b * w0_bstride + (long long)h * DD + rem] - scale * sum;
-  wop[(long long)grp * E + wstar_operand_offset<D>(hh, rem / D, rem % D)] = (bf16)wv;
-  if (w_out) w_out[((long long)b * H + h) * DD + rem] = wv;
+  const float* pg = partial + (long long)grp * S * (2 * HG * DD) + (long long)task * (T2 * 256) + l * 4;
+  f32x4 acc[T2];  // tiles (c, m) of K^T K, then (m, n) of K^T V
+  for (int t = 0; t < T2; ++t) acc[t] = zero4();
+  constexpr int UB = T2 >= 8 ? 2 : 4;  // splits in flight (16 tiles of loads)
+  for (int s0 = w; s0 < S; s0 += 4 * UB) {
+    f32x4 x[UB][T2];
+    for (int u = 0; u < UB; ++u) {
+      const int sp = s0 + 4 * u;
+      for (int t = 0; t < T2; ++t)
+        x[u][t] = sp < S ? *reinterpret_cast<const f32x4*>(pg + (long long)sp * (2 * HG * DD) + t * 256) : zero4();
+    }
+    for (int u = 0; u < UB; ++u)
+      for (int t = 0; t < T2; ++t) acc[t] += x[u][t];
+  }
+  for (int i = 0; i < WPER; ++i) {
+    const int e = threadIdx.x + i * kThreads;
+    if ((D * D) % kThreads == 0 || e < D * D) sW0[e] = w0v[i];
+  }
+  if (w > 0)
+    for (int t = 0; t < T2; ++t) sSum[w - 1][t][l] = acc[t];
+  __syncthreads();
+  if (w != 0) return;
+  for (int u = 0; u < 3; ++u)
+    for (int t = 0; t < T2; ++t) acc[t] += sSum[u][t][l];
+  wstar_rows<D>(acc, hl, m, sW0, scale,
+                wop + (long long)grp * HG * DD, w_out ? w_out + ((long long)b * H + h) * DD : nullptr, r, g);
 }
 
 // 3. O = Q W*, computed as O^T = W*^T Q^T (lane (r, g) gets 4 adjacent outputs of token r). Each
@@ -417,11 +470,13 @@ int head_group(int H, int D) {
 
 FbPlan plan_splits(int groups, int N, int sets) {
   const int tiles = (N + kTile - 1) / kTile;
-  // Aim for about 1024 workgroups (4 per CU on 256 CUs), never below one 64-token tile each;
-  // more splits (up to 4096 workgroups) where that keeps every split within `sets` tiles.
-  int splits = (1024 + groups - 1) / groups;
-  const int need = (tiles + sets - 1) / sets;
+  // Aim for about 512 workgroups (two per CU: the streaming rate of 256 CUs), never below one
+  // 64-token tile each; more splits (up to 4096 workgroups) where that keeps every split within
+  // 2 * sets tiles (the in-flight register sets, refilled once); at most 256 per group.
+  int splits = (512 + groups - 1) / groups;
+  const int need = (tiles + 2 * sets - 1) / (2 * sets);
   if (splits < need && (long long)groups * need <= 4096) splits = need;
+  if (splits > 256) splits = 256;
   if (splits > tiles) splits = tiles;
   if (splits < 1) splits = 1;
   const int tiles_per = (tiles + splits - 1) / splits;
@@ -438,13 +493,14 @@ hipError_t launch_bf16(int B, int H, int N, float eta, const void* q, const void
   const int groups = B * (H / HG);
   const FbPlan pl = plan_splits(groups, N, tile_sets(D));
   float* partial = static_cast<float*>(ws);
-  bf16* wop = reinterpret_cast<bf16*>(partial + (size_t)groups * pl.splits * HG * D * D);
+  float* wop_f = partial + (size_t)groups * pl.splits * 2 * HG * D * D;
+  bf16* wop = reinterpret_cast<bf16*>(wop_f);
   const int items = groups * pl.splits;
+  const float scale = eta / (float)N;
   hipLaunchKernelGGL((fb_partial_bf16<D, HG>), dim3(items), dim3(kThreads), 0, st, (const bf16*)k,
                      (const bf16*)v, w0, w0s, H, N, pl.splits, pl.tokens_per_split, partial);
-  hipLaunchKernelGGL((fb_reduce_bf16<D, HG>), dim3(groups * (HG * D * D / kThreads)),
-                     dim3(kThreads), 0, st, partial, pl.splits, w0, w0s, H, eta / (float)N, wop,
-                     w_out);
+  hipLaunchKernelGGL((fb_reduce_bf16<D, HG>), dim3(groups * HG * (D / 16)), dim3(kThreads), 0, st,
+                     partial, pl.splits, w0, w0s, H, scale, wop, w_out);
   hipLaunchKernelGGL((fb_readout_bf16<D, HG>), dim3(items), dim3(kThreads), 0, st, (const bf16*)q,
                      wop, H, N, pl.splits, pl.tokens_per_split, (bf16*)o);
   return hipGetLastError();
@@ -483,7 +539,7 @@ size_t fb_workspace_bytes(bool bf16_io, int B, int H, int N, int D) {
   const int hg = head_group(H, D);
   const int groups = B * (H / hg);
   const FbPlan p = plan_splits(groups, N, tile_sets(D));
-  return (size_t)groups * p.splits * hg * dd + (size_t)groups * hg * dd;
+  return (size_t)groups * p.splits * 2 * hg * dd + (size_t)groups * hg * dd;
 }
 
 hipError_t fb_launch(bool bf16_io, int B, int H, int N, int D, float eta, const void* q,

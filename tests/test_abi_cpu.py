@@ -46,12 +46,12 @@ def test_status_strings():
 
 def test_workspace_sizes():
     ws = T.ttt_workspace_size
-    # full-batch: split partials + W*, both d x d fp32 per (b, h)
+    # full-batch: split partials (K^T K and K^T V, d x d fp32 each per (b, h)) + W*
     assert ws(T.TTT_OP_FULLBATCH, T.TTT_BF16, 1, 2, 64, 16) > 0
     assert ws(T.TTT_OP_FULLBATCH, T.TTT_BF16, 64, 2, 3136, 32) % 256 == 0
     # the split count is capped, so the workspace stays bounded as N grows (linear in B*H only)
     # (2 heads of 32 share a 128-byte row: 4 groups, at most ~4096 splits in total)
-    bound = (4096 + 2 * 4) * 2 * 32 * 32 * 4 + 4 * 2 * 32 * 32 * 4 + 4096
+    bound = (4096 + 2 * 4) * 2 * 2 * 32 * 32 * 4 + 4 * 2 * 32 * 32 * 4 + 4096
     for n in (100000, 200000, 4000000):
         assert 0 < ws(T.TTT_OP_FULLBATCH, T.TTT_BF16, 4, 2, n, 32) <= bound
     # unsupported sizes report 0

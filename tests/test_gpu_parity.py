@@ -195,6 +195,27 @@ def test_end_states(wl):
         assert np.abs(st[0] - ref[1]).max() / np.abs(ref[1]).max() <= BF16_TOL
 
 
+# Full-batch split plans: one group with many splits, waves sharing a (head, row block) task when
+# a group has fewer than four, splits longer than the register sets (which refill them).
+FB_PLANS = [
+    W["hvit3t_stage1_fullbatch"].with_(B=1, N=2597, seed=71),           # one group, 41 splits
+    W["vit3s_fullbatch"].with_(B=1, N=5000, H=1, seed=72),              # D = 64, 79 splits
+    W["hvit3t_stage1_fullbatch"].with_(B=2, N=700, H=3, seed=73),       # one head per group: 2 waves per task
+    W["hvit3t_stage1_fullbatch"].with_(B=1, N=900, H=1, D=16, seed=74), # one 16-wide head: 4 waves per task
+    W["hvit3t_stage1_fullbatch"].with_(B=2, N=300, H=4, D=16, seed=75), # four heads per 128-byte row
+    W["vit3s_fullbatch"].with_(B=100, N=600, seed=76),                  # D = 64 splits of 4 tiles, 2 sets
+]
+
+
+@pytest.mark.parametrize("wl", FB_PLANS, ids=lambda w: f"B{w.B}N{w.N}H{w.H}D{w.D}")
+def test_fullbatch_split_plans(wl):
+    x = synth.make_inputs(wl)
+    out, st = run_gpu(x, want_state=True)
+    ref_o, ref_w = oracle_full(x)
+    assert slice_err(out, ref_o) <= BF16_TOL
+    assert np.abs(st[0] - ref_w).max() / np.abs(ref_w).max() <= BF16_TOL
+
+
 def test_mlp_end_states():
     wl = W["ttt_mlp_causal_8k"].with_(B=1, N=64, H=2, seed=64)
     x = synth.make_inputs(wl)
