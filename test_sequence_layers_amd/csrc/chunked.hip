@@ -148,18 +148,22 @@ __device__ __forceinline__ f32x4 rows_times_state(const bf16* X, int row0, const
   return init;
 }
 
-// W[:, cols] += K^T (-a E): A = K^T (row = feature 16m + r, k = token 16p + 4g + j), B = -a E_p.
+// W[:, cols] += K^T (-a E): A = K^T (row = feature 16m + r, k = token 16p + 4g + j, by LDS
+// transpose reads), B = -a E_p (accumulator layout). Chunks of 32 tokens or more contract 32 tokens
+// per product (k map {4g + j} u {16 + 4g + j} on both operands).
 template <int D, int NP, int P>
 __device__ __forceinline__ void update_state(f32x4* W, const f32x4* E, const bf16* sK, float a,
-                                             bf16x4 ident, int r, int g) {
-  for (int p = 0; p < NP; ++p) {
-    const bf16x4 eb = to_bf16x4_scaled(E[p], -a);
-    for (int m = 0; m < D / 16; ++m) {
-      // 16-token chunks: K^T tiles via the matrix cores (fewer LDS instructions); longer chunks:
-      // 2-byte column reads (the extra products cost more there).
-      const bf16x4 kt = NP == 1 ? tile_columns(&sK[16 * p * P + 16 * m], P, ident, r, g)
-                                : ld4_col(&sK[(16 * p + 4 * g) * P + 16 * m + r], P);
-      W[m] = mma16(kt, eb, W[m]);
+                                             int l) {
+  if constexpr (NP == 1) {
+    const bf16x4 eb = to_bf16x4_scaled(E[0], -a);
+    for (int m = 0; m < D / 16; ++m) W[m] = mma16(tile_tr(&sK[16 * m], P, l), eb, W[m]);
+  } else {
+    for (int p = 0; p < NP; p += 2) {
+      const bf16x8 eb = cat8(to_bf16x4_scaled(E[p], -a), to_bf16x4_scaled(E[p + 1], -a));
+      for (int m = 0; m < D / 16; ++m) {
+        const bf16x8 kt = cat8(tile_tr(&sK[16 * p * P + 16 * m], P, l), tile_tr(&sK[16 * (p + 1) * P + 16 * m], P, l));
+        W[m] = mma32(kt, eb, W[m]);
+      }
     }
   }
 }
@@ -167,11 +171,13 @@ __device__ __forceinline__ void update_state(f32x4* W, const f32x4* E, const bf1
 // E_p = K_p W - V_p[:, 16*vcol ..] for every 16-token tile p (V skipped when vcol < 0).
 template <int D, int NP, int P>
 __device__ __forceinline__ void residuals(f32x4* E, const f32x4* W, const bf16* sK,
-                                          const bf16* sV, int vcol, int r, int g) {
+                                          const bf16* sV, int vcol, int r, int g, int l) {
   for (int p = 0; p < NP; ++p) {
     f32x4 init = zero4();
-    if (vcol >= 0)
-      for (int j = 0; j < 4; ++j) init[j] = -(float)sV[(16 * p + 4 * g + j) * P + 16 * vcol + r];
+    if (vcol >= 0) {  // -V tile in accumulator layout, by an LDS transpose read
+      const bf16x4 vt = tile_tr(&sV[16 * p * P + 16 * vcol], P, l);
+      for (int j = 0; j < 4; ++j) init[j] = -(float)vt[j];
+    }
     E[p] = rows_times_state<D, P>(sK, 16 * p, W, init, r, g);
   }
 }
@@ -190,7 +196,6 @@ __global__ __launch_bounds__(D / 8 * 64) void chunk_compose_bf16(
 
   const int s = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H;
   const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
-  const bf16x4 ident = identity_b(r, g);
   const bool pwave = w < NT;        // P columns (init I, no V); else R columns (init 0, V)
   const int col = pwave ? w : w - NT;
   const int C = N / CH;
@@ -221,19 +226,23 @@ __global__ __launch_bounds__(D / 8 * 64) void chunk_compose_bf16(
     }
     __syncthreads();
     f32x4 Y[NP];
-    residuals<D, NP, P>(Y, X, sK, sV, pwave ? -1 : col, r, g);
+    residuals<D, NP, P>(Y, X, sK, sV, pwave ? -1 : col, r, g, l);
     if constexpr (BIDIR) {
       if (pwave) {  // R_rev[16col + i][16n + .] += a (K_c P_{c-1})^T V_c
-        for (int p = 0; p < NP; ++p) {
-          const bf16x4 ya = to_bf16x4_scaled(Y[p], a);
-          for (int n = 0; n < NT; ++n)
-            RR[n] = mma16(ya, NP == 1 ? tile_columns(&sV[16 * p * P + 16 * n], P, ident, r, g)
-                                      : ld4_col(&sV[(16 * p + 4 * g) * P + 16 * n + r], P),
-                          RR[n]);
+        if constexpr (NP == 1) {
+          const bf16x4 ya = to_bf16x4_scaled(Y[0], a);
+          for (int n = 0; n < NT; ++n) RR[n] = mma16(ya, tile_tr(&sV[16 * n], P, l), RR[n]);
+        } else {  // 32 tokens per product, k map {4g + j} u {16 + 4g + j}
+          for (int p = 0; p < NP; p += 2) {
+            const bf16x8 ya = cat8(to_bf16x4_scaled(Y[p], a), to_bf16x4_scaled(Y[p + 1], a));
+            for (int n = 0; n < NT; ++n)
+              RR[n] = mma32(ya, cat8(tile_tr(&sV[16 * p * P + 16 * n], P, l),
+                                     tile_tr(&sV[16 * (p + 1) * P + 16 * n], P, l)), RR[n]);
+          }
         }
       }
     }
-    update_state<D, NP, P>(X, Y, sK, a, ident, r, g);
+    update_state<D, NP, P>(X, Y, sK, a, l);
   }
 
   // comp[(bh * S + s)] holds the forward map record and, for the bidirectional scan, the
@@ -375,7 +384,6 @@ __global__ __launch_bounds__(D / 16 * 64) void chunk_scan_bf16(
   const int s = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H;
   const int BH = gridDim.y;
   const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
-  const bf16x4 ident = identity_b(r, g);
   const int C = N / CH;
   const int lo = s * L, hi = min(C, lo + L);
   const long long ts = (long long)H * D;
@@ -422,8 +430,8 @@ __global__ __launch_bounds__(D / 16 * 64) void chunk_scan_bf16(
       }
       __syncthreads();
       f32x4 E[NP];
-      residuals<D, NP, P>(E, W, sK, sV, w, r, g);
-      update_state<D, NP, P>(W, E, sK, a, ident, r, g);
+      residuals<D, NP, P>(E, W, sK, sV, w, r, g, l);
+      update_state<D, NP, P>(W, E, sK, a, l);
       for (int m = 0; m < NT; ++m) sWr[(((c - lo) * NT + w) * NT + m) * 64 + l] = to_bf16x4(W[m]);
     }
     if (s == 0 && w_out) save(w_out + (long long)BH * DD + bh * DD, W);
@@ -452,7 +460,7 @@ __global__ __launch_bounds__(D / 16 * 64) void chunk_scan_bf16(
     if (NBUF == 2 && c > lo) store_chunk<D, CH, P, NTH>(o + tok0 - CH * ts, sOb[buf ^ 1], ts);
 
     f32x4 E[NP];
-    residuals<D, NP, P>(E, W, sK, sV, w, r, g);
+    residuals<D, NP, P>(E, W, sK, sV, w, r, g, l);
 
     if constexpr (MODE == kCausal) {
       // O_p = Q_p W_s - a * sum_{p' <= p} tril(P_{p p'}) E_{p'},  P = Q K^T.
@@ -479,9 +487,9 @@ __global__ __launch_bounds__(D / 16 * 64) void chunk_scan_bf16(
         }
         for (int j = 0; j < 4; ++j) sO[(16 * p + 4 * g + j) * P + 16 * w + r] = (bf16)(qw[j] + acc[j]);
       }
-      update_state<D, NP, P>(W, E, sK, a, ident, r, g);
+      update_state<D, NP, P>(W, E, sK, a, l);
     } else {
-      update_state<D, NP, P>(W, E, sK, a, ident, r, g);
+      update_state<D, NP, P>(W, E, sK, a, l);
       f32x4 Ws[NT];
       for (int m = 0; m < NT; ++m) {
         const bf16x4 wr = sWr[(((c - lo) * NT + w) * NT + m) * 64 + l];
