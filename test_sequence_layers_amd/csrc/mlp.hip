@@ -17,8 +17,9 @@
 // of W1 (columns), of W2 (rows) and a second copy of its W2 slice in transposed accumulator
 // layout (the operand of E W2^T). All three stay in MFMA accumulator registers for the whole
 // sequence and are updated in place by MFMA. Z1, X2 and D1 are produced as [token][hidden]
-// accumulator tiles, which are directly the operands of the weight updates; the one transpose
-// needed (X2^T, for the contraction over hidden units) is a product with an identity tile. The
+// accumulator tiles, which are directly the operands of the weight updates; the transposed
+// operands of K and E (contractions over tokens) come from LDS by gfx950 transpose reads, and
+// X2^T (for the contraction over hidden units) is a product with an identity tile. The
 // cross-wave sums over hidden units (Z2 and the read-out) go through LDS in a fixed wave order,
 // so results are deterministic. Two workgroup barriers per chunk; K, V, Q are staged through a
 // four-deep LDS ring: each chunk's global loads are issued three chunks ahead into one of two
@@ -41,7 +42,6 @@ constexpr int kWaves = 8;
 constexpr int kHw = kDh / kWaves;  // hidden units per wave
 constexpr int kNh = kHw / 16;      // 16-unit hidden tiles per wave
 constexpr int kP = kD + 8;         // pitch of [token][feature] tiles (elements)
-constexpr int kPt = kCh + 8;       // pitch of [feature][token] tiles
 constexpr int kRing = 4;           // K/V/Q staging depth
 constexpr int kSlots = 8;          // partial tiles per wave: Z2^T x4, O^T x4
 
@@ -115,7 +115,6 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
     float a, bf16* __restrict__ o, float* __restrict__ w1_out, float* __restrict__ w2_out) {
   __shared__ __align__(16) bf16 sKVQ[kRing][3][kCh * kP];
   __shared__ __align__(16) bf16 sE[2][kCh * kP];           // E [token][out]
-  __shared__ __align__(16) bf16 sEt[2][kD * kPt];          // E^T [out][token]
   __shared__ __align__(16) f32x4 sRed[kWaves * kSlots * 64];  // lane-private partial tiles
 
   const int bh = blockIdx.x, b = bh / H, h = bh % H;
@@ -168,8 +167,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
     const bf16* sKp = sKVQ[(c + kRing - 1) % kRing][0];  // chunk c - 1
     const bf16* sQp = sKVQ[(c + kRing - 1) % kRing][2];
     bf16* sEc = sE[c & 1];
-    bf16* sEtc = sEt[c & 1];
-    const bf16* sEtp = sEt[(c + 1) & 1];  // E^T of chunk c - 1
+    const bf16* sEp = sE[(c + 1) & 1];  // E of chunk c - 1
 
     // ---------------- phase 1: products with the current weights
     bf16x8 w1b[2][kNh];  // W1 tiles (k = features, c-layout k map)
@@ -204,7 +202,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
       const bf16x4 n2b = to_bf16x4_scaled(n2, a);
       for (int o2 = 0; o2 < 4; ++o2) {
         const f32x4 ow = mma32(cat_tiles(W2t[0][o2], W2t[1][o2]), x2q, zero4());
-        const f32x4 oe = mma16(ld4(&sEtp[(16 * o2 + r) * kPt + 4 * g]), n2b, zero4());
+        const f32x4 oe = mma16(tile_tr(&sEp[16 * o2], kP, l), n2b, zero4());  // A = E^T
         sRed[(w * kSlots + 4 + o2) * 64 + l] = ow + oe;
       }
     }
@@ -234,14 +232,13 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
     __syncthreads();
 
     // ---------------- phase 2: cross-wave sums (fixed wave order)
-    if (fwd && w < 4) {  // E^T tile w = Z2^T - V^T, stored as E [token][out] and E^T [out][token]
+    if (fwd && w < 4) {  // E^T tile w = Z2^T - V^T, stored as E [token][out]
       f32x4 s = sRed[w * 64 + l];
       for (int ww = 1; ww < kWaves; ++ww) s = s + sRed[(ww * kSlots + w) * 64 + l];
       const bf16x4 vv = ld4(&sV[r * kP + 16 * w + 4 * g]);
       bf16x4 eb;
       for (int j = 0; j < 4; ++j) eb[j] = (bf16)(s[j] - (float)vv[j]);
       *reinterpret_cast<bf16x4*>(&sEc[r * kP + 16 * w + 4 * g]) = eb;
-      for (int j = 0; j < 4; ++j) sEtc[(16 * w + 4 * g + j) * kPt + r] = eb[j];
     }
     if (rd && w >= 4) {  // O^T tile of chunk c - 1 = sum of the waves' shares
       const int o4 = w - 4;
@@ -269,14 +266,14 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
         d1n[n] = to_bf16x4_scaled(d1, -a);
         d1p[n] = to_bf16x4_scaled(d1, a);
       }
-      // W1 += K^T (-a D1): A = K^T (row feature, k token), B = -a D1.
+      // W1 += K^T (-a D1): A = K^T (row feature, k token; LDS transpose read), B = -a D1.
       for (int m = 0; m < 4; ++m) {
-        const bf16x4 kt = ld4_col(&sK[(4 * g) * kP + 16 * m + r], kP);
+        const bf16x4 kt = tile_tr(&sK[16 * m], kP, l);
         for (int n = 0; n < kNh; ++n) W1t[m][n] = mma16(kt, d1n[n], W1t[m][n]);
       }
-      // W2 += X2^T (-a E) and W2^T += E^T (-a X2): E^T rows give both operands.
+      // W2 += X2^T (-a E) and W2^T += E^T (-a X2): E's transposed tiles give both operands.
       for (int o2 = 0; o2 < 4; ++o2) {
-        const bf16x4 e = ld4(&sEtc[(16 * o2 + r) * kPt + 4 * g]);
+        const bf16x4 e = tile_tr(&sEc[16 * o2], kP, l);
         for (int n = 0; n < kNh; ++n) {
           W2t[n][o2] = mma16(x2n[n], e, W2t[n][o2]);
           W2x[o2][n] = mma16(e, x2n[n], W2x[o2][n]);
