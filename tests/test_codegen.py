@@ -77,7 +77,7 @@ def test_scanner_finds_a_planted_chain():
 @pytest.mark.parametrize("src", KERNEL_SOURCES)
 def test_no_mixed_shape_mfma_accumulator_chains(src, tmp_path):
     out = tmp_path / (src + ".s")
-    cmd = [HIPCC, *[f for f in B.FLAGS if f != "-fPIC"], "--cuda-device-only", "-S",
+    cmd = [HIPCC, *[f for f in B.flags_for(src) if f != "-fPIC"], "--cuda-device-only", "-S",
            os.path.join(B.CSRC, src), "-o", str(out)]
     p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     assert p.returncode == 0, p.stdout[-2000:]
