@@ -52,20 +52,17 @@ constexpr float kNegHalfLog2e = -0.72134752044448170368f;  // -log2(e) / 2
 // GELU(x) = x Phi(x) with Phi(x) = (1 + erf(x / sqrt 2)) / 2 (exact erf form) and
 // GELU'(x) = Phi(x) + x phi(x), phi the standard normal density.
 // Fast path, used when every lane's argument has x^2 <= 2 (|x / sqrt 2| <= 1): erf(u) = u P(u^2)
-// with P the degree-5 least-squares polynomial for erf(u)/u on u^2 in [0, 1] (fitted on Chebyshev
-// nodes; max abs error of erf 1.1e-7 in fp32 Horner form), so Phi(x) = 1/2 + x R(x^2) with
+// with P the degree-3 least-squares polynomial for erf(u)/u on u^2 in [0, 1] (fitted on Chebyshev
+// nodes; max abs error of erf 2.7e-5 in fp32 Horner form, two orders below the bf16 rounding of
+// the products that consume GELU's output), so Phi(x) = 1/2 + x R(x^2) with
 // R(t) = P(t / 2) / (2 sqrt 2). Otherwise the library erf is used.
-constexpr float kErfP[6] = {1.1283791065216064f, -0.37612348794937134f, 0.11280364543199539f,
-                            -0.026716385036706924f, 0.004923277534544468f, -0.0005654105916619301f};
+constexpr float kErfP[4] = {1.128350616f, -0.3751908541f, 0.1079747304f, -0.0184600465f};
 constexpr float kInvTwoSqrt2 = 0.35355339059327376220f;
 constexpr float kR0 = kErfP[0] * kInvTwoSqrt2, kR1 = kErfP[1] * kInvTwoSqrt2 / 2.f,
-                kR2 = kErfP[2] * kInvTwoSqrt2 / 4.f, kR3 = kErfP[3] * kInvTwoSqrt2 / 8.f,
-                kR4 = kErfP[4] * kInvTwoSqrt2 / 16.f, kR5 = kErfP[5] * kInvTwoSqrt2 / 32.f;
+                kR2 = kErfP[2] * kInvTwoSqrt2 / 4.f, kR3 = kErfP[3] * kInvTwoSqrt2 / 8.f;
 
 __device__ __forceinline__ float cdf_fast(float x, float t) {  // t = x * x <= 2
-  float r = fmaf(kR5, t, kR4);
-  r = fmaf(r, t, kR3);
-  r = fmaf(r, t, kR2);
+  float r = fmaf(kR3, t, kR2);
   r = fmaf(r, t, kR1);
   r = fmaf(r, t, kR0);
   return fmaf(x, r, 0.5f);
@@ -107,6 +104,9 @@ __device__ __forceinline__ void gelu_slope_tiles(const f32x4* z, f32x4* y, f32x4
 }
 __device__ __forceinline__ bf16x8 cat_tiles(f32x4 lo, f32x4 hi) {
   return cat8(to_bf16x4(lo), to_bf16x4(hi));
+}
+__device__ __forceinline__ bf16x4 neg_bf16x4(bf16x4 x) {  // exact: flips the sign bits
+  return __builtin_bit_cast(bf16x4, __builtin_bit_cast(uint2, x) ^ make_uint2(0x80008000u, 0x80008000u));
 }
 
 __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
@@ -167,7 +167,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
     const bf16* sKp = sKVQ[(c + kRing - 1) % kRing][0];  // chunk c - 1
     const bf16* sQp = sKVQ[(c + kRing - 1) % kRing][2];
     bf16* sEc = sE[c & 1];
-    const bf16* sEp = sE[(c + 1) & 1];  // E of chunk c - 1
+    const bf16* sEp = sE[(c + 1) & 1];  // a E of chunk c - 1
 
     // ---------------- phase 1: products with the current weights
     bf16x8 w1b[2][kNh];  // W1 tiles (k = features, c-layout k map)
@@ -199,15 +199,15 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
       f32x4 n2 = mma32(x2tp, x2q, zero4());  // [t'][t] = sum_h X2[t'][h] X2q[t][h]
       for (int j = 0; j < 4; ++j)
         if (4 * g + j <= r) n2[j] = 0.f;
-      const bf16x4 n2b = to_bf16x4_scaled(n2, a);
+      const bf16x4 n2b = to_bf16x4(n2);  // (a is in the stored E)
       for (int o2 = 0; o2 < 4; ++o2) {
         const f32x4 ow = mma32(cat_tiles(W2t[0][o2], W2t[1][o2]), x2q, zero4());
-        const f32x4 oe = mma16(tile_tr(&sEp[16 * o2], kP, l), n2b, zero4());  // A = E^T
+        const f32x4 oe = mma16(tile_tr(&sEp[16 * o2], kP, l), n2b, zero4());  // A = (a E)^T
         sRed[(w * kSlots + 4 + o2) * 64 + l] = ow + oe;
       }
     }
     f32x4 Gp[kNh];
-    bf16x4 x2n[kNh];  // -a X2, [token][hidden] tiles
+    bf16x4 x2n[kNh];  // -X2, [token][hidden] tiles
     if (fwd) {
       // Z1 [token][hidden] = K W1: A = K rows (c-layout k map), B = W1 tiles.
       f32x4 Z1[kNh], X2[kNh], xt[kNh];
@@ -221,8 +221,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
       }
       gelu_slope_tiles(Z1, X2, Gp);
       for (int n = 0; n < kNh; ++n) {
-        xt[n] = mma16(to_bf16x4(X2[n]), ident, zero4());  // X2^T [hidden][token]
-        x2n[n] = to_bf16x4_scaled(X2[n], -a);
+        const bf16x4 x2b = to_bf16x4(X2[n]);
+        xt[n] = mma16(x2b, ident, zero4());  // X2^T [hidden][token]
+        x2n[n] = neg_bf16x4(x2b);
       }
       x2tp = cat_tiles(xt[0], xt[1]);
       // Z2^T partial [out][token] over this wave's hidden units.
@@ -232,12 +233,12 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
     __syncthreads();
 
     // ---------------- phase 2: cross-wave sums (fixed wave order)
-    if (fwd && w < 4) {  // E^T tile w = Z2^T - V^T, stored as E [token][out]
+    if (fwd && w < 4) {  // E^T tile w = Z2^T - V^T, stored as a E [token][out]
       f32x4 s = sRed[w * 64 + l];
       for (int ww = 1; ww < kWaves; ++ww) s = s + sRed[(ww * kSlots + w) * 64 + l];
       const bf16x4 vv = ld4(&sV[r * kP + 16 * w + 4 * g]);
       bf16x4 eb;
-      for (int j = 0; j < 4; ++j) eb[j] = (bf16)(s[j] - (float)vv[j]);
+      for (int j = 0; j < 4; ++j) eb[j] = (bf16)(a * (s[j] - (float)vv[j]));
       *reinterpret_cast<bf16x4*>(&sEc[r * kP + 16 * w + 4 * g]) = eb;
     }
     if (rd && w >= 4) {  // O^T tile of chunk c - 1 = sum of the waves' shares
@@ -251,7 +252,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
 
     // ---------------- phase 3: backward and state update of chunk c
     if (fwd) {
-      // dX2 [token][hidden] = E W2^T: A = E rows (c-layout k map), B = W2x tiles.
+      // a dX2 [token][hidden] = (a E) W2^T: A = a E rows (c-layout k map), B = W2x tiles.
       bf16x8 ea[2];
       for (int ko = 0; ko < 2; ++ko) {
         const bf16* pe = &sEc[r * kP + 32 * ko + 4 * g];
@@ -261,17 +262,17 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
       for (int n = 0; n < kNh; ++n) {
         f32x4 acc = zero4();
         for (int ko = 0; ko < 2; ++ko) acc = mma32(ea[ko], cat_tiles(W2x[2 * ko][n], W2x[2 * ko + 1][n]), acc);
-        f32x4 d1;
+        f32x4 d1;  // a D1
         for (int j = 0; j < 4; ++j) d1[j] = acc[j] * Gp[n][j];
-        d1n[n] = to_bf16x4_scaled(d1, -a);
-        d1p[n] = to_bf16x4_scaled(d1, a);
+        d1p[n] = to_bf16x4(d1);
+        d1n[n] = neg_bf16x4(d1p[n]);
       }
       // W1 += K^T (-a D1): A = K^T (row feature, k token; LDS transpose read), B = -a D1.
       for (int m = 0; m < 4; ++m) {
         const bf16x4 kt = tile_tr(&sK[16 * m], kP, l);
         for (int n = 0; n < kNh; ++n) W1t[m][n] = mma16(kt, d1n[n], W1t[m][n]);
       }
-      // W2 += X2^T (-a E) and W2^T += E^T (-a X2): E's transposed tiles give both operands.
+      // W2 += (-X2)^T (a E) and W2^T += (a E)^T (-X2): a E's transposed tiles give both operands.
       for (int o2 = 0; o2 < 4; ++o2) {
         const bf16x4 e = tile_tr(&sEc[16 * o2], kP, l);
         for (int n = 0; n < kNh; ++n) {

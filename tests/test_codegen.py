@@ -87,31 +87,34 @@ def test_no_mixed_shape_mfma_accumulator_chains(src, tmp_path):
 
 def _mlp_erf_coefficients():
     src = open(os.path.join(B.CSRC, "mlp.hip")).read()
-    m = re.search(r"kErfP\[6\]\s*=\s*\{([^}]*)\}", src)
+    m = re.search(r"kErfP\[(\d+)\]\s*=\s*\{([^}]*)\}", src)
     assert m, "kErfP not found in mlp.hip"
-    return [float(x.strip().rstrip("f")) for x in m.group(1).split(",")]
+    coef = [float(x.strip().rstrip("f")) for x in m.group(2).split(",")]
+    assert len(coef) == int(m.group(1))
+    return coef
 
 
 def test_mlp_fast_gelu_polynomial_matches_erf():
     """The TTT-MLP kernel's fast GELU path evaluates erf(u) = u P(u^2) for |u| <= 1 and
-    Phi(x) = 1/2 + x R(x^2) for x^2 <= 2. Evaluated here in fp32 Horner form with the kernel's
-    own coefficients, both stay within 2e-7 of scipy's erf / normal CDF."""
+    Phi(x) = 1/2 + x R(x^2) for x^2 <= 2, R(t) = P(t / 2) / (2 sqrt 2). Evaluated here in fp32
+    Horner form with the kernel's own coefficients, both stay within 3e-5 of scipy's erf / normal
+    CDF (the products that consume GELU's output round their operands to bf16, 3.9e-3)."""
     import numpy as np
     from scipy.special import erf, ndtr
 
     p = [np.float32(c) for c in _mlp_erf_coefficients()]
     u = np.linspace(-1.0, 1.0, 400001).astype(np.float32)
     s = u * u
-    acc = p[5]
-    for c in p[4::-1]:
+    acc = p[-1]
+    for c in p[-2::-1]:
         acc = acc * s + c
-    assert np.abs((u * acc).astype(np.float64) - erf(u.astype(np.float64))).max() < 2e-7
+    assert np.abs((u * acc).astype(np.float64) - erf(u.astype(np.float64))).max() < 3e-5
     k = np.float32(0.35355339059327376220)
-    r = [np.float32(p[i] * k / np.float32(2 ** i)) for i in range(6)]
+    r = [np.float32(p[i] * k / np.float32(2 ** i)) for i in range(len(p))]
     x = np.linspace(-np.sqrt(2.0), np.sqrt(2.0), 400001).astype(np.float32)
     t = x * x
-    acc = r[5]
-    for c in r[4::-1]:
+    acc = r[-1]
+    for c in r[-2::-1]:
         acc = acc * t + c
     cdf = x * acc + np.float32(0.5)
-    assert np.abs(cdf.astype(np.float64) - ndtr(x.astype(np.float64))).max() < 2e-7
+    assert np.abs(cdf.astype(np.float64) - ndtr(x.astype(np.float64))).max() < 3e-5
