@@ -2,19 +2,20 @@
 // single epoch, full batch, inner learning rate 1.0; "core idea": train on (K, V), read out Q):
 //   W* = W0 - (eta/N) K^T (K W0 - V),  O = Q W*   for every (batch, head).
 //
-// bf16 I/O: three launches. Heads whose D-vectors are adjacent in a token row are grouped up to
+// bf16 I/O: two launches. Heads whose D-vectors are adjacent in a token row are grouped up to
 // 128 bytes per row (2 heads of 32, 4 of 16, 1 of 64), so every staged row is a full, contiguous
-// cache line. Work items are (group, token split), one per workgroup.
+// cache line. Work items are (group, token split), one per workgroup; a group's items share an
+// XCD.
 //   fb_partial_bf16: stream K, V tiles (double-buffered LDS, up to four tiles in flight in
 //                    registers) and accumulate the split's K_s^T K_s and K_s^T V_s with MFMA
 //                    (operands by LDS transpose reads); since K^T (K W0 - V) = (K^T K) W0 - K^T V,
 //                    these two sums carry the gradient;
-//   fb_reduce_bf16:  W* = W0 - (eta/N) (sum_s K_s^T K_s W0 - sum_s K_s^T V_s), summed in a fixed
-//                    split order (deterministic), stored in bf16 as the read-out's MFMA operands;
-//   fb_readout_bf16: stream Q straight into MFMA operands, one wave per 16-token block, and
-//                    write O = Q W*.
-// HBM traffic is the algorithmic Q, K, V read plus the O write; the partials are two d x d fp32
-// matrices per split and stay in L2 / Infinity Cache.
+//   fb_readout_bf16: form W* = W0 - (eta/N) (sum_s K_s^T K_s W0 - sum_s K_s^T V_s) from the
+//                    group's split records (fixed order: deterministic) into LDS, then stream Q
+//                    through wave-private LDS tiles, one wave per 16-token block, and write
+//                    O = Q W*.
+// HBM traffic is the algorithmic Q, K, V read plus the O write; the split records are two d x d
+// fp32 matrices per split and stay in L2 / Infinity Cache.
 //
 // fp32 I/O: three plain-FMA launches (partial gradients, fixed-order reduction, read-out).
 #include <type_traits>
@@ -116,6 +117,14 @@ __device__ __forceinline__ void wstar_rows(const f32x4* acc, int hl, int m, cons
   }
 }
 
+// Blocks of one launch go to the 8 XCDs in turn (block i to XCD i mod 8); the work items of a
+// group are given to blocks of one XCD, so that its L2 serves the group's split records to all
+// of them.
+__device__ __forceinline__ int xcd_item(int i, int items) {
+  const int q = items / 8, rem = items % 8, x = i % 8;
+  return x * q + min(x, rem) + i / 8;
+}
+
 // 1. Gradient sums of one token split of one head group: the split's gradient at W0 is
 // K_s^T (K_s W0 - V_s) = (K_s^T K_s) W0 - K_s^T V_s, so the kernel accumulates K_s^T K_s and
 // K_s^T V_s over the split's tokens, every MFMA operand read from LDS by transpose reads
@@ -139,7 +148,8 @@ __global__ __launch_bounds__(kThreads, 4) void fb_partial_bf16(
                 "sums of the waves sharing a task fit in sK");
   float* sG = reinterpret_cast<float*>(&sK[0][0]);
 
-  const int grp = blockIdx.x / S, s = blockIdx.x % S;
+  const int item = xcd_item(blockIdx.x, gridDim.x);
+  const int grp = item / S, s = item % S;
   const int b = grp / (H / HG), h0 = (grp % (H / HG)) * HG;
   const int n0 = s * tps, n1 = min(N, n0 + tps);
   const int ntiles = (n1 - n0 + kTile - 1) / kTile;
@@ -220,83 +230,42 @@ __global__ __launch_bounds__(kThreads, 4) void fb_partial_bf16(
     }
 }
 
-// 2. W* = W0 - (eta/N) ((sum_s K_s^T K_s) W0 - sum_s K_s^T V_s), a launch of its own (summing
-// the records inside the first launch, by its last split per group, needs device-coherent
-// accesses across XCDs and measured slower). One workgroup per (group, task): wave t sums the
-// task's accumulator tiles of splits t, t + 4, ... (loads of several splits in flight), the four
-// sums are added in a fixed order (deterministic), and wave 0 forms the task's rows of W*.
-template <int D, int HG>
-__global__ __launch_bounds__(kThreads) void fb_reduce_bf16(const float* __restrict__ partial,
-                                                           int S, const float* __restrict__ w0,
-                                                           long long w0_bstride, int H,
-                                                           float scale, bf16* __restrict__ wop,
-                                                           float* __restrict__ w_out) {
-  constexpr int NT = D / 16, TASKS = HG * NT, T2 = 2 * NT;
-  constexpr long long DD = (long long)D * D;
-  constexpr int WPER = (D * D + kThreads - 1) / kThreads;
-  __shared__ f32x4 sSum[3][T2][64];
-  __shared__ float sW0[D * D];
-  const int grp = blockIdx.x / TASKS, task = blockIdx.x % TASKS;
-  const int hl = task / NT, m = task % NT;
-  const int b = grp / (H / HG), h = (grp % (H / HG)) * HG + hl;
-  const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
-  const float* W0 = w0 + b * w0_bstride + (long long)h * DD;
-  float w0v[WPER];  // W0, loaded with the records and staged in LDS for wave 0
-  for (int i = 0; i < WPER; ++i) {
-    const int e = threadIdx.x + i * kThreads;
-    w0v[i] = (D * D) % kThreads == 0 || e < D * D ? W0[e] : 0.f;
-  }
-  const float* pg = partial + (long long)grp * S * (2 * HG * DD) + (long long)task * (T2 * 256) + l * 4;
-  f32x4 acc[T2];  // tiles (c, m) of K^T K, then (m, n) of K^T V
-  for (int t = 0; t < T2; ++t) acc[t] = zero4();
-  constexpr int UB = T2 >= 8 ? 2 : 4;  // splits in flight (16 tiles of loads)
-  for (int s0 = w; s0 < S; s0 += 4 * UB) {
-    f32x4 x[UB][T2];
-    for (int u = 0; u < UB; ++u) {
-      const int sp = s0 + 4 * u;
-      for (int t = 0; t < T2; ++t)
-        x[u][t] = sp < S ? *reinterpret_cast<const f32x4*>(pg + (long long)sp * (2 * HG * DD) + t * 256) : zero4();
-    }
-    for (int u = 0; u < UB; ++u)
-      for (int t = 0; t < T2; ++t) acc[t] += x[u][t];
-  }
-  for (int i = 0; i < WPER; ++i) {
-    const int e = threadIdx.x + i * kThreads;
-    if ((D * D) % kThreads == 0 || e < D * D) sW0[e] = w0v[i];
-  }
-  if (w > 0)
-    for (int t = 0; t < T2; ++t) sSum[w - 1][t][l] = acc[t];
-  __syncthreads();
-  if (w != 0) return;
-  for (int u = 0; u < 3; ++u)
-    for (int t = 0; t < T2; ++t) acc[t] += sSum[u][t][l];
-  wstar_rows<D>(acc, hl, m, sW0, scale,
-                wop + (long long)grp * HG * DD, w_out ? w_out + ((long long)b * H + h) * DD : nullptr, r, g);
-}
-
-// 3. O = Q W*, computed as O^T = W*^T Q^T (lane (r, g) gets 4 adjacent outputs of token r). Each
-// wave streams its own 16-token blocks of the split (blocks w, w + 4, ...), kReadSets of them in
-// flight from the start, and moves them through a wave-private LDS tile: full-row 16-byte pieces
-// to and from HBM, operand-shaped pieces to and from the matrix cores. No workgroup barriers:
-// a wave's LDS operations execute in order, and a wavefront-scope fence keeps the compiler from
-// reordering them.
+// 2. O = Q W*, computed as O^T = W*^T Q^T (lane (r, g) gets 4 adjacent outputs of token r).
+// Each workgroup first forms its group's W* = W0 - (eta/N) ((sum_s K_s^T K_s) W0 - sum_s K_s^T V_s)
+// from the split records (wave (task, tw) sums the task's tiles of splits tw, tw + WPT, ...; the
+// waves of a task add theirs in a fixed order, so every workgroup of a group gets the same W*),
+// with its first Q blocks already in flight; the work items of a group share an XCD (xcd_item).
+// W* goes to LDS as the read-out's MFMA operands (wstar_rows).
+// Then each wave streams its own 16-token blocks of the split (blocks w, w + 4, ...), kReadSets
+// of them in flight, through a wave-private LDS tile: full-row 16-byte pieces to and from HBM,
+// operand-shaped pieces to and from the matrix cores. No workgroup barriers in that loop: a wave's
+// LDS operations execute in order, and a wavefront-scope fence keeps the compiler from reordering
+// them.
 constexpr int kReadSets = 4;
 
 template <int D, int HG>
-__global__ __launch_bounds__(kThreads) void fb_readout_bf16(const bf16* __restrict__ q,
-                                                            const bf16* __restrict__ wop,
-                                                            int H, int N, int S, int tps,
-                                                            bf16* __restrict__ o) {
+__global__ __launch_bounds__(kThreads) void fb_readout_bf16(
+    const bf16* __restrict__ q, const float* __restrict__ partial, const float* __restrict__ w0,
+    long long w0_bstride, int H, int N, int S, int tps, float scale, bf16* __restrict__ o,
+    float* __restrict__ w_out) {
   using G = Geo<D, HG>;
   constexpr int NT = D / 16, E = kOpElems<D>, KS = D / (4 * E);
+  constexpr long long DD = (long long)D * D;
+  constexpr int TASKS = HG * NT, WPT = 4 / TASKS, T2 = 2 * NT;
   constexpr int BP = 16 * G::CPR;       // 16-byte pieces of a 16-token block
   constexpr int PPL = (BP + 63) / 64;   // pieces per lane
+  constexpr int WPER = (HG * D * D + kThreads - 1) / kThreads;
   __shared__ __align__(16) bf16 sQ[4][16 * G::P];
   __shared__ __align__(16) bf16 sO[4][16 * G::P];
-  const int grp = blockIdx.x / S, s = blockIdx.x % S;
+  __shared__ __align__(16) float sW0[HG * D * D];
+  __shared__ __align__(16) bf16 sWop[HG * D * D];
+  __shared__ f32x4 sSum[(4 - TASKS) > 0 ? (4 - TASKS) : 1][T2][64];
+  const int item = xcd_item(blockIdx.x, gridDim.x);
+  const int grp = item / S, s = item % S;
   const int b = grp / (H / HG), h0 = (grp % (H / HG)) * HG;
   const int n0 = s * tps, n1 = min(N, n0 + tps);
   const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
+  const int task = w % TASKS, tw = w / TASKS, hl = task / NT, m = task % NT;
   const int blocks = (n1 - n0 + 15) / 16;
   const int mine = blocks > w ? (blocks - w + 3) / 4 : 0;
   const long long ts = (long long)H * D;
@@ -304,15 +273,6 @@ __global__ __launch_bounds__(kThreads) void fb_readout_bf16(const bf16* __restri
   bf16* myQ = sQ[w];
   bf16* myO = sO[w];
 
-  using Op = typename std::conditional<(D >= 32), bf16x8, bf16x4>::type;
-  Op wa[HG][NT][KS];  // A operands W*^T
-  {
-    const bf16* src = wop + (long long)grp * HG * D * D;
-    for (int hl = 0; hl < HG; ++hl)
-      for (int n = 0; n < NT; ++n)
-        for (int ks = 0; ks < KS; ++ks)
-          wa[hl][n][ks] = *reinterpret_cast<const Op*>(src + (((hl * NT + n) * KS + ks) * 64 + l) * E);
-  }
   struct Regs {
     uint4 x[PPL];
   } sets[kReadSets];
@@ -329,6 +289,54 @@ __global__ __launch_bounds__(kThreads) void fb_readout_bf16(const bf16* __restri
 #pragma unroll
   for (int u = 0; u < kReadSets; ++u)
     if (u < mine) load(sets[u], u);
+
+  // W* of the group, while those loads are in flight.
+  {
+    const float* W0g = w0 + b * w0_bstride + (long long)h0 * DD;  // the group's heads, contiguous
+    float w0v[WPER];
+    for (int i = 0; i < WPER; ++i) {
+      const int e = threadIdx.x + i * kThreads;
+      w0v[i] = (HG * D * D) % kThreads == 0 || e < HG * D * D ? W0g[e] : 0.f;
+    }
+    const float* pt = partial + (long long)grp * S * (2 * HG * DD) + (long long)task * (T2 * 256) + l * 4;
+    f32x4 acc[T2];
+    for (int t = 0; t < T2; ++t) acc[t] = zero4();
+    constexpr int UB = T2 >= 8 ? 2 : 4;  // splits in flight (16 tiles of loads)
+    for (int s0 = tw; s0 < S; s0 += UB * WPT) {
+      f32x4 x[UB][T2];
+      for (int u = 0; u < UB; ++u) {
+        const int sp = s0 + u * WPT;
+        for (int t = 0; t < T2; ++t)
+          x[u][t] = sp < S ? *reinterpret_cast<const f32x4*>(pt + (long long)sp * (2 * HG * DD) + t * 256) : zero4();
+      }
+      for (int u = 0; u < UB; ++u)
+        for (int t = 0; t < T2; ++t) acc[t] += x[u][t];
+    }
+    for (int i = 0; i < WPER; ++i) {
+      const int e = threadIdx.x + i * kThreads;
+      if ((HG * D * D) % kThreads == 0 || e < HG * D * D) sW0[e] = w0v[i];
+    }
+    if constexpr (WPT > 1) {
+      if (tw > 0)
+        for (int t = 0; t < T2; ++t) sSum[w - TASKS][t][l] = acc[t];
+    }
+    __syncthreads();
+    if (tw == 0) {
+      if constexpr (WPT > 1)
+        for (int u = 1; u < WPT; ++u)
+          for (int t = 0; t < T2; ++t) acc[t] += sSum[(u - 1) * TASKS + task][t][l];
+      wstar_rows<D>(acc, hl, m, sW0 + hl * DD, scale, sWop,
+                    (w_out && s == 0) ? w_out + ((long long)b * H + h0 + hl) * DD : nullptr, r, g);
+    }
+    __syncthreads();
+  }
+  using Op = typename std::conditional<(D >= 32), bf16x8, bf16x4>::type;
+  Op wa[HG][NT][KS];  // A operands W*^T
+  for (int hl2 = 0; hl2 < HG; ++hl2)
+    for (int n = 0; n < NT; ++n)
+      for (int ks = 0; ks < KS; ++ks)
+        wa[hl2][n][ks] = *reinterpret_cast<const Op*>(sWop + (((hl2 * NT + n) * KS + ks) * 64 + l) * E);
+
   auto step = [&](int i, Regs& R) {
     const int t0 = n0 + 16 * (w + 4 * i);
     for (int u = 0; u < PPL; ++u) {
@@ -493,16 +501,12 @@ hipError_t launch_bf16(int B, int H, int N, float eta, const void* q, const void
   const int groups = B * (H / HG);
   const FbPlan pl = plan_splits(groups, N, tile_sets(D));
   float* partial = static_cast<float*>(ws);
-  float* wop_f = partial + (size_t)groups * pl.splits * 2 * HG * D * D;
-  bf16* wop = reinterpret_cast<bf16*>(wop_f);
   const int items = groups * pl.splits;
   const float scale = eta / (float)N;
   hipLaunchKernelGGL((fb_partial_bf16<D, HG>), dim3(items), dim3(kThreads), 0, st, (const bf16*)k,
                      (const bf16*)v, w0, w0s, H, N, pl.splits, pl.tokens_per_split, partial);
-  hipLaunchKernelGGL((fb_reduce_bf16<D, HG>), dim3(groups * HG * (D / 16)), dim3(kThreads), 0, st,
-                     partial, pl.splits, w0, w0s, H, scale, wop, w_out);
   hipLaunchKernelGGL((fb_readout_bf16<D, HG>), dim3(items), dim3(kThreads), 0, st, (const bf16*)q,
-                     wop, H, N, pl.splits, pl.tokens_per_split, (bf16*)o);
+                     partial, w0, w0s, H, N, pl.splits, pl.tokens_per_split, scale, (bf16*)o, w_out);
   return hipGetLastError();
 }
 
@@ -539,7 +543,7 @@ size_t fb_workspace_bytes(bool bf16_io, int B, int H, int N, int D) {
   const int hg = head_group(H, D);
   const int groups = B * (H / hg);
   const FbPlan p = plan_splits(groups, N, tile_sets(D));
-  return (size_t)groups * p.splits * 2 * hg * dd + (size_t)groups * hg * dd;
+  return (size_t)groups * p.splits * 2 * hg * dd;
 }
 
 hipError_t fb_launch(bool bf16_io, int B, int H, int N, int D, float eta, const void* q,
