@@ -21,7 +21,9 @@
 // operands of K and E (contractions over tokens) come from LDS by gfx950 transpose reads, and
 // X2^T (for the contraction over hidden units) is a product with an identity tile. The
 // cross-wave sums over hidden units (Z2 and the read-out) go through LDS in a fixed wave order,
-// so results are deterministic. Two workgroup barriers per chunk; K, V, Q are staged through a
+// so results are deterministic. The steps between the first and the last have both a read-out
+// and a forward, known at compile time, so that their products and GELUs share basic blocks and
+// interleave. Two workgroup barriers per chunk; K, V, Q are staged through a
 // four-deep LDS ring: each chunk's global loads are issued three chunks ahead into one of two
 // alternating register sets and stored to LDS two chunks ahead.
 //
@@ -29,6 +31,8 @@
 // mixed-shape accumulator chain was measured to read a stale accumulator (wrong results that
 // depended on the instruction schedule), so terms of different shapes get separate accumulators
 // and are added in registers.
+#include <type_traits>
+
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -51,7 +55,8 @@ constexpr float kNegHalfLog2e = -0.72134752044448170368f;  // -log2(e) / 2
 
 // GELU(x) = x Phi(x) with Phi(x) = (1 + erf(x / sqrt 2)) / 2 (exact erf form) and
 // GELU'(x) = Phi(x) + x phi(x), phi the standard normal density.
-// Fast path, used when every lane's argument has x^2 <= 2 (|x / sqrt 2| <= 1): erf(u) = u P(u^2)
+// Fast path, used when every argument of the wave's GELUs in a chunk step has x^2 <= 2
+// (|x / sqrt 2| <= 1): erf(u) = u P(u^2)
 // with P the degree-3 least-squares polynomial for erf(u)/u on u^2 in [0, 1] (fitted on Chebyshev
 // nodes; max abs error of erf 2.7e-5 in fp32 Horner form, two orders below the bf16 rounding of
 // the products that consume GELU's output), so Phi(x) = 1/2 + x R(x^2) with
@@ -69,39 +74,6 @@ __device__ __forceinline__ float cdf_fast(float x, float t) {  // t = x * x <= 2
 }
 __device__ __forceinline__ float cdf_lib(float x) { return 0.5f * (1.f + erff(x * kInvSqrt2)); }
 
-// X = GELU(Z) for two [4]-element tiles per lane.
-__device__ __forceinline__ void gelu_tiles(const f32x4* z, f32x4* y) {
-  float tmax = 0.f;
-  for (int n = 0; n < kNh; ++n)
-    for (int j = 0; j < 4; ++j) tmax = fmaxf(tmax, z[n][j] * z[n][j]);
-  if (!__any(tmax > 2.f)) {
-    for (int n = 0; n < kNh; ++n)
-      for (int j = 0; j < 4; ++j) y[n][j] = z[n][j] * cdf_fast(z[n][j], z[n][j] * z[n][j]);
-  } else {
-    for (int n = 0; n < kNh; ++n)
-      for (int j = 0; j < 4; ++j) y[n][j] = z[n][j] * cdf_lib(z[n][j]);
-  }
-}
-// X = GELU(Z) and S = GELU'(Z) for two tiles per lane.
-__device__ __forceinline__ void gelu_slope_tiles(const f32x4* z, f32x4* y, f32x4* dy) {
-  float tmax = 0.f;
-  for (int n = 0; n < kNh; ++n)
-    for (int j = 0; j < 4; ++j) tmax = fmaxf(tmax, z[n][j] * z[n][j]);
-  f32x4 cdf[kNh];
-  if (!__any(tmax > 2.f)) {
-    for (int n = 0; n < kNh; ++n)
-      for (int j = 0; j < 4; ++j) cdf[n][j] = cdf_fast(z[n][j], z[n][j] * z[n][j]);
-  } else {
-    for (int n = 0; n < kNh; ++n)
-      for (int j = 0; j < 4; ++j) cdf[n][j] = cdf_lib(z[n][j]);
-  }
-  for (int n = 0; n < kNh; ++n)
-    for (int j = 0; j < 4; ++j) {
-      const float x = z[n][j];
-      y[n][j] = x * cdf[n][j];
-      dy[n][j] = fmaf(x * kInvSqrt2Pi, __builtin_amdgcn_exp2f(x * x * kNegHalfLog2e), cdf[n][j]);
-    }
-}
 __device__ __forceinline__ bf16x8 cat_tiles(f32x4 lo, f32x4 hi) {
   return cat8(to_bf16x4(lo), to_bf16x4(hi));
 }
@@ -159,8 +131,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
 
   // One chunk step: forward of chunk c, read-out of chunk c - 1. pf_cur holds chunk c + 2 (loaded
   // one step earlier); chunk c + 3 is loaded into pf_next.
-  auto step = [&](const int c, uint4& pf_next, const uint4& pf_cur) {
-    const bool fwd = c < C, rd = c > 0;  // forward of chunk c, read-out of chunk c - 1
+  auto step = [&](const int c, uint4& pf_next, const uint4& pf_cur, auto rd_tag, auto fwd_tag) {
+    constexpr bool rd = decltype(rd_tag)::value;    // read-out of chunk c - 1
+    constexpr bool fwd = decltype(fwd_tag)::value;  // forward of chunk c
     if (t < 384 && c + 3 < C) pf_next = ld16(psrc + (long long)(c + 3) * kCh * ts);
     const bf16* sK = sKVQ[c % kRing][0];
     const bf16* sV = sKVQ[c % kRing][1];
@@ -169,11 +142,16 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
     bf16* sEc = sE[c & 1];
     const bf16* sEp = sE[(c + 1) & 1];  // a E of chunk c - 1
 
-    // ---------------- phase 1: products with the current weights
+    // ---------------- phase 1: products with the current weights. The read-out of chunk c - 1
+    // and the forward of chunk c are independent; their products, GELUs and remaining products
+    // are grouped so that one basic block holds both chains.
     bf16x8 w1b[2][kNh];  // W1 tiles (k = features, c-layout k map)
     for (int ks = 0; ks < 2; ++ks)
       for (int n = 0; n < kNh; ++n) w1b[ks][n] = cat_tiles(W1t[2 * ks][n], W1t[2 * ks + 1][n]);
-    if (rd) {
+    f32x4 Z1q[kNh], X2q[kNh];  // read-out: Z1q^T [hidden][token]
+    f32x4 Z1[kNh], X2[kNh];    // forward: Z1 [token][hidden]
+    f32x4 Gp[kNh];
+    if constexpr (rd) {
       // M[t'][t] = k_t' . q_t of chunk c - 1, kept for t' > t.
       f32x4 mt = zero4();
       for (int ks = 0; ks < 2; ++ks)
@@ -181,8 +159,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
       for (int j = 0; j < 4; ++j)
         if (4 * g + j <= r) mt[j] = 0.f;
       const bf16x4 mb = to_bf16x4(mt);
-      // Z1q^T [hidden][token] = W1^T Q^T + a D1^T M.
-      f32x4 Z1q[kNh], X2q[kNh];
+      // Z1q^T = W1^T Q^T + a D1^T M.
       for (int n = 0; n < kNh; ++n) {
         f32x4 z = zero4();
         for (int ks = 0; ks < 2; ++ks) {
@@ -192,25 +169,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
         const f32x4 zd = mma16(d1p[n], mb, zero4());  // own accumulator (no mixed-shape chain)
         Z1q[n] = z + zd;
       }
-      gelu_tiles(Z1q, X2q);
-      const bf16x8 x2q = cat_tiles(X2q[0], X2q[1]);
-      // This wave's share of O^T [out][token]: W2^T X2q^T over its hidden units, plus
-      // a E^T striu(X2q X2^T)^T with X2q X2^T summed over the same units (t' > t kept).
-      f32x4 n2 = mma32(x2tp, x2q, zero4());  // [t'][t] = sum_h X2[t'][h] X2q[t][h]
-      for (int j = 0; j < 4; ++j)
-        if (4 * g + j <= r) n2[j] = 0.f;
-      const bf16x4 n2b = to_bf16x4(n2);  // (a is in the stored E)
-      for (int o2 = 0; o2 < 4; ++o2) {
-        const f32x4 ow = mma32(cat_tiles(W2t[0][o2], W2t[1][o2]), x2q, zero4());
-        const f32x4 oe = mma16(tile_tr(&sEp[16 * o2], kP, l), n2b, zero4());  // A = (a E)^T
-        sRed[(w * kSlots + 4 + o2) * 64 + l] = ow + oe;
-      }
     }
-    f32x4 Gp[kNh];
-    bf16x4 x2n[kNh];  // -X2, [token][hidden] tiles
-    if (fwd) {
-      // Z1 [token][hidden] = K W1: A = K rows (c-layout k map), B = W1 tiles.
-      f32x4 Z1[kNh], X2[kNh], xt[kNh];
+    if constexpr (fwd) {
+      // Z1 = K W1: A = K rows (c-layout k map), B = W1 tiles.
       for (int n = 0; n < kNh; ++n) {
         f32x4 z = zero4();
         for (int ks = 0; ks < 2; ++ks) {
@@ -219,13 +180,62 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
         }
         Z1[n] = z;
       }
-      gelu_slope_tiles(Z1, X2, Gp);
+    }
+    {  // GELU of both chains, one fast-path decision for the wave
+      float tmax = 0.f;
+      for (int n = 0; n < kNh; ++n)
+        for (int j = 0; j < 4; ++j) {
+          if constexpr (rd) tmax = fmaxf(tmax, Z1q[n][j] * Z1q[n][j]);
+          if constexpr (fwd) tmax = fmaxf(tmax, Z1[n][j] * Z1[n][j]);
+        }
+      auto slope = [&](float x, float cdf, int n, int j) {
+        X2[n][j] = x * cdf;
+        Gp[n][j] = fmaf(x * kInvSqrt2Pi, __builtin_amdgcn_exp2f(x * x * kNegHalfLog2e), cdf);
+      };
+      if (!__any(tmax > 2.f)) {
+        for (int n = 0; n < kNh; ++n)
+          for (int j = 0; j < 4; ++j) {
+            if constexpr (rd) X2q[n][j] = Z1q[n][j] * cdf_fast(Z1q[n][j], Z1q[n][j] * Z1q[n][j]);
+            if constexpr (fwd) slope(Z1[n][j], cdf_fast(Z1[n][j], Z1[n][j] * Z1[n][j]), n, j);
+          }
+      } else {
+        for (int n = 0; n < kNh; ++n)
+          for (int j = 0; j < 4; ++j) {
+            if constexpr (rd) X2q[n][j] = Z1q[n][j] * cdf_lib(Z1q[n][j]);
+            if constexpr (fwd) slope(Z1[n][j], cdf_lib(Z1[n][j]), n, j);
+          }
+      }
+    }
+    bf16x8 x2q;
+    bf16x4 n2b;
+    if constexpr (rd) {
+      x2q = cat_tiles(X2q[0], X2q[1]);
+      // (with the previous chunk's X2^T, before the forward below replaces it)
+      f32x4 n2 = mma32(x2tp, x2q, zero4());  // [t'][t] = sum_h X2[t'][h] X2q[t][h]
+      for (int j = 0; j < 4; ++j)
+        if (4 * g + j <= r) n2[j] = 0.f;
+      n2b = to_bf16x4(n2);  // (a is in the stored E)
+    }
+    bf16x4 x2n[kNh];  // -X2, [token][hidden] tiles
+    if constexpr (fwd) {
+      f32x4 xt[kNh];
       for (int n = 0; n < kNh; ++n) {
         const bf16x4 x2b = to_bf16x4(X2[n]);
         xt[n] = mma16(x2b, ident, zero4());  // X2^T [hidden][token]
         x2n[n] = neg_bf16x4(x2b);
       }
       x2tp = cat_tiles(xt[0], xt[1]);
+    }
+    if constexpr (rd) {
+      // This wave's share of O^T [out][token]: W2^T X2q^T over its hidden units, plus
+      // (a E)^T striu(X2q X2^T)^T with X2q X2^T summed over the same units (t' > t kept).
+      for (int o2 = 0; o2 < 4; ++o2) {
+        const f32x4 ow = mma32(cat_tiles(W2t[0][o2], W2t[1][o2]), x2q, zero4());
+        const f32x4 oe = mma16(tile_tr(&sEp[16 * o2], kP, l), n2b, zero4());  // A = (a E)^T
+        sRed[(w * kSlots + 4 + o2) * 64 + l] = ow + oe;
+      }
+    }
+    if constexpr (fwd) {
       // Z2^T partial [out][token] over this wave's hidden units.
       for (int o2 = 0; o2 < 4; ++o2)
         sRed[(w * kSlots + o2) * 64 + l] = mma32(cat_tiles(W2t[0][o2], W2t[1][o2]), x2tp, zero4());
@@ -283,9 +293,21 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
     }
     if (t < 384 && c + 2 < C) st16(&sKVQ[(c + 2) % kRing][which][prow * kP + pcol], pf_cur);
   };
-  for (int c = 0; c <= C; c += 2) {  // two steps per trip: the register sets swap roles
-    step(c, pfA, pfB);
-    if (c + 1 <= C) step(c + 1, pfB, pfA);
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  // Step 0 has no read-out, step C no forward; the steps between have both (two per trip: the
+  // register sets swap roles).
+  if (C > 0) step(0, pfA, pfB, F_{}, T_{});
+  int c = 1;
+  for (; c + 1 < C; c += 2) {
+    step(c, pfB, pfA, T_{}, T_{});
+    step(c + 1, pfA, pfB, T_{}, T_{});
+  }
+  if (c < C) {
+    step(c, pfB, pfA, T_{}, T_{});
+    step(c + 1, pfA, pfB, T_{}, F_{});
+  } else {
+    step(c, pfB, pfA, T_{}, F_{});
   }
 
   const long long bhl = bh;
