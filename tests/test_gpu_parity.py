@@ -204,6 +204,8 @@ FB_PLANS = [
     W["hvit3t_stage1_fullbatch"].with_(B=1, N=900, H=1, D=16, seed=74), # one 16-wide head: 4 waves per task
     W["hvit3t_stage1_fullbatch"].with_(B=2, N=300, H=4, D=16, seed=75), # four heads per 128-byte row
     W["vit3s_fullbatch"].with_(B=100, N=600, seed=76),                  # D = 64 splits of 4 tiles, 2 sets
+    W["hvit3t_stage1_fullbatch"].with_(B=1, N=262144, seed=77),         # split cap (256): 16 tiles a split
+    W["vit3s_fullbatch"].with_(B=1, N=100000, H=1, seed=78),            # D = 64 at the split cap
 ]
 
 
