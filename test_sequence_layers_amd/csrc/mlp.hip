@@ -166,8 +166,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
           const bf16* pq = &sQp[r * kP + 32 * ks + 4 * g];
           z = mma32(w1b[ks][n], cat8(ld4(pq), ld4(pq + 16)), z);
         }
-        const f32x4 zd = mma16(d1p[n], mb, zero4());  // own accumulator (no mixed-shape chain)
-        Z1q[n] = z + zd;
+        // a D1^T M as a 16x16x32 product with the upper k half zero in both operands, so that
+        // it chains onto the same-shape accumulator (a 16x16x16 product must not).
+        Z1q[n] = mma32(cat8(d1p[n], bf16x4{}), cat8(mb, bf16x4{}), z);
       }
     }
     if constexpr (fwd) {
@@ -226,19 +227,21 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
       }
       x2tp = cat_tiles(xt[0], xt[1]);
     }
+    bf16x8 w2a[4];  // W2^T tiles (k = this wave's hidden units), for both products below
+    for (int o2 = 0; o2 < 4; ++o2) w2a[o2] = cat_tiles(W2t[0][o2], W2t[1][o2]);
     if constexpr (rd) {
       // This wave's share of O^T [out][token]: W2^T X2q^T over its hidden units, plus
-      // (a E)^T striu(X2q X2^T)^T with X2q X2^T summed over the same units (t' > t kept).
+      // (a E)^T striu(X2q X2^T)^T with X2q X2^T summed over the same units (t' > t kept), the
+      // latter as a 16x16x32 product with a zero upper k half (same-shape chain).
       for (int o2 = 0; o2 < 4; ++o2) {
-        const f32x4 ow = mma32(cat_tiles(W2t[0][o2], W2t[1][o2]), x2q, zero4());
-        const f32x4 oe = mma16(tile_tr(&sEp[16 * o2], kP, l), n2b, zero4());  // A = (a E)^T
-        sRed[(w * kSlots + 4 + o2) * 64 + l] = ow + oe;
+        const f32x4 ow = mma32(w2a[o2], x2q, zero4());
+        sRed[(w * kSlots + 4 + o2) * 64 + l] =
+            mma32(cat8(tile_tr(&sEp[16 * o2], kP, l), bf16x4{}), cat8(n2b, bf16x4{}), ow);  // A = (a E)^T
       }
     }
     if constexpr (fwd) {
       // Z2^T partial [out][token] over this wave's hidden units.
-      for (int o2 = 0; o2 < 4; ++o2)
-        sRed[(w * kSlots + o2) * 64 + l] = mma32(cat_tiles(W2t[0][o2], W2t[1][o2]), x2tp, zero4());
+      for (int o2 = 0; o2 < 4; ++o2) sRed[(w * kSlots + o2) * 64 + l] = mma32(w2a[o2], x2tp, zero4());
     }
     __syncthreads();
 
