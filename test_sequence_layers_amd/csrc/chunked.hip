@@ -148,6 +148,24 @@ __device__ __forceinline__ f32x4 rows_times_state(const bf16* X, int row0, const
   return init;
 }
 
+// The transpose of the above without init: Y^T[16 cols x 16 rows] = W[:, cols]^T X_rows^T. The
+// state tiles in accumulator layout are the A operand of W^T; lane (r, g) gets the 4 adjacent
+// columns 4g.. of row row0 + r (one 8-byte store).
+template <int D, int P>
+__device__ __forceinline__ f32x4 state_times_rows(const bf16* X, int row0, const f32x4* W, int r,
+                                                  int g) {
+  f32x4 acc = zero4();
+  if constexpr (D >= 32) {
+    for (int ks = 0; ks < D / 32; ++ks) {
+      const bf16* p = X + (row0 + r) * P + 32 * ks + 4 * g;
+      acc = mma32(b_state(W, ks), cat8(ld4(p), ld4(p + 16)), acc);
+    }
+  } else {
+    acc = mma16(to_bf16x4(W[0]), ld4(X + (row0 + r) * P + 4 * g), acc);
+  }
+  return acc;
+}
+
 // W[:, cols] += K^T (-a E): A = K^T (row = feature 16m + r, k = token 16p + 4g + j, by LDS
 // transpose reads), B = -a E_p (accumulator layout). Chunks of 32 tokens or more contract 32 tokens
 // per product (k map {4g + j} u {16 + 4g + j} on both operands).
@@ -463,11 +481,12 @@ __global__ __launch_bounds__(D / 16 * 64) void chunk_scan_bf16(
     residuals<D, NP, P>(E, W, sK, sV, w, r, g, l);
 
     if constexpr (MODE == kCausal) {
-      // O_p = Q_p W_s - a * sum_{p' <= p} tril(P_{p p'}) E_{p'},  P = Q K^T.
+      // O_p = Q_p W_s - a * sum_{p' <= p} tril(P_{p p'}) E_{p'},  P = Q K^T, computed transposed
+      // (lane (r, g) gets columns 16w + 4g.. of token 16p + r: one 8-byte store).
       for (int p = 0; p < NP; ++p) {
-        // Q_p W_s and the masked term get separate accumulators: a 16x16x16 product must not
+        // W_s^T Q_p^T and the masked term get separate accumulators: a 16x16x16 product must not
         // accumulate onto a 16x16x32 product's result (on gfx950 that chain read a stale value).
-        const f32x4 qw = rows_times_state<D, P>(sQ, 16 * p, W, zero4(), r, g);
+        const f32x4 qw = state_times_rows<D, P>(sQ, 16 * p, W, r, g);
         f32x4 acc = zero4();
         for (int pp = 0; pp <= p; ++pp) {
           // Pt[t' = 16pp + 4g + j][t = 16p + r] = k_t' . q_t
@@ -482,10 +501,10 @@ __global__ __launch_bounds__(D / 16 * 64) void chunk_scan_bf16(
           if (pp == p)
             for (int j = 0; j < 4; ++j)
               if (4 * g + j > r) pt[j] = 0.f;
-          // A = -a P (row t = lane r, k = t' = 4g + j), B = E_{p'} (k = t', column = lane r).
-          acc = mma16(to_bf16x4_scaled(pt, -a), to_bf16x4(E[pp]), acc);
+          // A = E_{p'}^T (row = column 16w + r, k = t' = 4g + j), B = -a P^T (k = t', n = t = r).
+          acc = mma16(to_bf16x4(E[pp]), to_bf16x4_scaled(pt, -a), acc);
         }
-        for (int j = 0; j < 4; ++j) sO[(16 * p + 4 * g + j) * P + 16 * w + r] = (bf16)(qw[j] + acc[j]);
+        *reinterpret_cast<bf16x4*>(&sO[(16 * p + r) * P + 16 * w + 4 * g]) = to_bf16x4(qw + acc);
       }
       update_state<D, NP, P>(W, E, sK, a, l);
     } else {
@@ -495,10 +514,9 @@ __global__ __launch_bounds__(D / 16 * 64) void chunk_scan_bf16(
         const bf16x4 wr = sWr[(((c - lo) * NT + w) * NT + m) * 64 + l];
         for (int j = 0; j < 4; ++j) Ws[m][j] = W[m][j] + (float)wr[j];
       }
-      for (int p = 0; p < NP; ++p) {
-        const f32x4 acc = rows_times_state<D, P>(sQ, 16 * p, Ws, zero4(), r, g);
-        for (int j = 0; j < 4; ++j) sO[(16 * p + 4 * g + j) * P + 16 * w + r] = (bf16)acc[j];
-      }
+      for (int p = 0; p < NP; ++p)  // transposed: columns 16w + 4g.. of token 16p + r
+        *reinterpret_cast<bf16x4*>(&sO[(16 * p + r) * P + 16 * w + 4 * g]) =
+            to_bf16x4(state_times_rows<D, P>(sQ, 16 * p, Ws, r, g));
     }
     if (NBUF == 1) {
       __syncthreads();
