@@ -40,24 +40,19 @@ __device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
                                                    __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
 }
 
-// Round-to-nearest-even fp32 -> bf16 (gfx950 converts in hardware).
+// Round-to-nearest-even fp32 -> bf16 (gfx950 converts in hardware, two values per instruction).
+// Each half is converted as a 2-vector and the halves are joined as 32-bit words: converted
+// element by element into a 4-vector, a fragment that ends up as a 16x16x16 MFMA operand (a
+// 16-bit integer vector) was compiled as four single conversions and two byte permutes.
 __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) {
-  bf16x4 r;
-  r[0] = (bf16)x[0];
-  r[1] = (bf16)x[1];
-  r[2] = (bf16)x[2];
-  r[3] = (bf16)x[3];
-  return r;
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 lo = __builtin_convertvector(f32x2{x[0], x[1]}, bf16x2);
+  const bf16x2 hi = __builtin_convertvector(f32x2{x[2], x[3]}, bf16x2);
+  return __builtin_bit_cast(bf16x4, make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)));
 }
 
-__device__ __forceinline__ bf16x4 to_bf16x4_scaled(f32x4 x, float s) {
-  bf16x4 r;
-  r[0] = (bf16)(x[0] * s);
-  r[1] = (bf16)(x[1] * s);
-  r[2] = (bf16)(x[2] * s);
-  r[3] = (bf16)(x[3] * s);
-  return r;
-}
+__device__ __forceinline__ bf16x4 to_bf16x4_scaled(f32x4 x, float s) { return to_bf16x4(x * s); }
 
 __device__ __forceinline__ bf16x8 cat8(bf16x4 lo, bf16x4 hi) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);

@@ -23,9 +23,10 @@
 // cross-wave sums over hidden units (Z2 and the read-out) go through LDS in a fixed wave order,
 // so results are deterministic. The steps between the first and the last have both a read-out
 // and a forward, known at compile time, so that their products and GELUs share basic blocks and
-// interleave. Two workgroup barriers per chunk; K, V, Q are staged through a
-// four-deep LDS ring: each chunk's global loads are issued three chunks ahead into one of two
-// alternating register sets and stored to LDS two chunks ahead.
+// interleave. E is kept as -a E (a = eta / b), so that -a D1 and the weight updates' operands come
+// out of the products with the right sign (no separate negations). Two workgroup barriers per
+// chunk; K, V, Q are staged through a four-deep LDS ring: each chunk's global loads are issued
+// three chunks ahead into one of two alternating register sets and stored to LDS two chunks ahead.
 //
 // No 16x16x16 product accumulates onto the result of a 16x16x32 product: on gfx950 such a
 // mixed-shape accumulator chain was measured to read a stale accumulator (wrong results that
@@ -50,8 +51,8 @@ constexpr int kRing = 4;           // K/V/Q staging depth
 constexpr int kSlots = 8;          // partial tiles per wave: Z2^T x4, O^T x4
 
 constexpr float kInvSqrt2 = 0.70710678118654752440f;
-constexpr float kInvSqrt2Pi = 0.39894228040143267794f;
 constexpr float kNegHalfLog2e = -0.72134752044448170368f;  // -log2(e) / 2
+constexpr float kLog2InvSqrt2Pi = -1.32574806473615935f;   // log2(1 / sqrt(2 pi))
 
 // GELU(x) = x Phi(x) with Phi(x) = (1 + erf(x / sqrt 2)) / 2 (exact erf form) and
 // GELU'(x) = Phi(x) + x phi(x), phi the standard normal density.
@@ -76,9 +77,6 @@ __device__ __forceinline__ float cdf_lib(float x) { return 0.5f * (1.f + erff(x 
 
 __device__ __forceinline__ bf16x8 cat_tiles(f32x4 lo, f32x4 hi) {
   return cat8(to_bf16x4(lo), to_bf16x4(hi));
-}
-__device__ __forceinline__ bf16x4 neg_bf16x4(bf16x4 x) {  // exact: flips the sign bits
-  return __builtin_bit_cast(bf16x4, __builtin_bit_cast(uint2, x) ^ make_uint2(0x80008000u, 0x80008000u));
 }
 
 __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
@@ -124,7 +122,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
   }
   __syncthreads();
 
-  bf16x4 d1p[kNh];  // a * D1 of the previous chunk, [token][hidden] tiles
+  bf16x4 d1p[kNh];  // -a D1 of the previous chunk, [token][hidden] tiles
   bf16x8 x2tp;      // X2^T of the previous chunk, [hidden][token] tiles (both, c-layout k map)
   for (int n = 0; n < kNh; ++n) d1p[n] = bf16x4{};
   x2tp = bf16x8{};
@@ -140,7 +138,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
     const bf16* sKp = sKVQ[(c + kRing - 1) % kRing][0];  // chunk c - 1
     const bf16* sQp = sKVQ[(c + kRing - 1) % kRing][2];
     bf16* sEc = sE[c & 1];
-    const bf16* sEp = sE[(c + 1) & 1];  // a E of chunk c - 1
+    const bf16* sEp = sE[(c + 1) & 1];  // -a E of chunk c - 1
 
     // ---------------- phase 1: products with the current weights. The read-out of chunk c - 1
     // and the forward of chunk c are independent; their products, GELUs and remaining products
@@ -156,17 +154,16 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
       f32x4 mt = zero4();
       for (int ks = 0; ks < 2; ++ks)
         mt = mma32(ld8(&sKp[r * kP + 32 * ks + 8 * g]), ld8(&sQp[r * kP + 32 * ks + 8 * g]), mt);
-      for (int j = 0; j < 4; ++j)
-        if (4 * g + j <= r) mt[j] = 0.f;
-      const bf16x4 mb = to_bf16x4(mt);
-      // Z1q^T = W1^T Q^T + a D1^T M.
+      for (int j = 0; j < 4; ++j) mt[j] = 4 * g + j <= r ? 0.f : -mt[j];
+      const bf16x4 mb = to_bf16x4(mt);  // -M, t' > t kept (the carried D1 is -a D1)
+      // Z1q^T = W1^T Q^T + a D1^T M = W1^T Q^T + (-a D1)^T (-M).
       for (int n = 0; n < kNh; ++n) {
         f32x4 z = zero4();
         for (int ks = 0; ks < 2; ++ks) {
           const bf16* pq = &sQp[r * kP + 32 * ks + 4 * g];
           z = mma32(w1b[ks][n], cat8(ld4(pq), ld4(pq + 16)), z);
         }
-        // a D1^T M as a 16x16x32 product with the upper k half zero in both operands, so that
+        // (-a D1)^T (-M) as a 16x16x32 product with the upper k half zero in both operands, so that
         // it chains onto the same-shape accumulator (a 16x16x16 product must not).
         Z1q[n] = mma32(cat8(d1p[n], bf16x4{}), cat8(mb, bf16x4{}), z);
       }
@@ -191,7 +188,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
         }
       auto slope = [&](float x, float cdf, int n, int j) {
         X2[n][j] = x * cdf;
-        Gp[n][j] = fmaf(x * kInvSqrt2Pi, __builtin_amdgcn_exp2f(x * x * kNegHalfLog2e), cdf);
+        Gp[n][j] = fmaf(x, __builtin_amdgcn_exp2f(fmaf(x * x, kNegHalfLog2e, kLog2InvSqrt2Pi)), cdf);
       };
       if (!__any(tmax > 2.f)) {
         for (int n = 0; n < kNh; ++n)
@@ -213,17 +210,15 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
       x2q = cat_tiles(X2q[0], X2q[1]);
       // (with the previous chunk's X2^T, before the forward below replaces it)
       f32x4 n2 = mma32(x2tp, x2q, zero4());  // [t'][t] = sum_h X2[t'][h] X2q[t][h]
-      for (int j = 0; j < 4; ++j)
-        if (4 * g + j <= r) n2[j] = 0.f;
-      n2b = to_bf16x4(n2);  // (a is in the stored E)
+      for (int j = 0; j < 4; ++j) n2[j] = 4 * g + j <= r ? 0.f : -n2[j];
+      n2b = to_bf16x4(n2);  // (-a is in the stored E)
     }
-    bf16x4 x2n[kNh];  // -X2, [token][hidden] tiles
+    bf16x4 x2b[kNh];  // X2, [token][hidden] tiles
     if constexpr (fwd) {
       f32x4 xt[kNh];
       for (int n = 0; n < kNh; ++n) {
-        const bf16x4 x2b = to_bf16x4(X2[n]);
-        xt[n] = mma16(x2b, ident, zero4());  // X2^T [hidden][token]
-        x2n[n] = neg_bf16x4(x2b);
+        x2b[n] = to_bf16x4(X2[n]);
+        xt[n] = mma16(x2b[n], ident, zero4());  // X2^T [hidden][token]
       }
       x2tp = cat_tiles(xt[0], xt[1]);
     }
@@ -231,12 +226,13 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
     for (int o2 = 0; o2 < 4; ++o2) w2a[o2] = cat_tiles(W2t[0][o2], W2t[1][o2]);
     if constexpr (rd) {
       // This wave's share of O^T [out][token]: W2^T X2q^T over its hidden units, plus
-      // (a E)^T striu(X2q X2^T)^T with X2q X2^T summed over the same units (t' > t kept), the
-      // latter as a 16x16x32 product with a zero upper k half (same-shape chain).
+      // (a E)^T striu(X2q X2^T)^T = (-a E)^T (-striu(X2q X2^T))^T with X2q X2^T summed over the
+      // same units (t' > t kept), the latter as a 16x16x32 product with a zero upper k half
+      // (same-shape chain).
       for (int o2 = 0; o2 < 4; ++o2) {
         const f32x4 ow = mma32(w2a[o2], x2q, zero4());
         sRed[(w * kSlots + 4 + o2) * 64 + l] =
-            mma32(cat8(tile_tr(&sEp[16 * o2], kP, l), bf16x4{}), cat8(n2b, bf16x4{}), ow);  // A = (a E)^T
+            mma32(cat8(tile_tr(&sEp[16 * o2], kP, l), bf16x4{}), cat8(n2b, bf16x4{}), ow);  // A = (-a E)^T
       }
     }
     if constexpr (fwd) {
@@ -246,12 +242,12 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
     __syncthreads();
 
     // ---------------- phase 2: cross-wave sums (fixed wave order)
-    if (fwd && w < 4) {  // E^T tile w = Z2^T - V^T, stored as a E [token][out]
+    if (fwd && w < 4) {  // E^T tile w = Z2^T - V^T, stored as -a E [token][out]
       f32x4 s = sRed[w * 64 + l];
       for (int ww = 1; ww < kWaves; ++ww) s = s + sRed[(ww * kSlots + w) * 64 + l];
       const bf16x4 vv = ld4(&sV[r * kP + 16 * w + 4 * g]);
       bf16x4 eb;
-      for (int j = 0; j < 4; ++j) eb[j] = (bf16)(a * (s[j] - (float)vv[j]));
+      for (int j = 0; j < 4; ++j) eb[j] = (bf16)(a * ((float)vv[j] - s[j]));
       *reinterpret_cast<bf16x4*>(&sEc[r * kP + 16 * w + 4 * g]) = eb;
     }
     if (rd && w >= 4) {  // O^T tile of chunk c - 1 = sum of the waves' shares
@@ -265,32 +261,30 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
 
     // ---------------- phase 3: backward and state update of chunk c
     if (fwd) {
-      // a dX2 [token][hidden] = (a E) W2^T: A = a E rows (c-layout k map), B = W2x tiles.
+      // -a dX2 [token][hidden] = (-a E) W2^T: A = -a E rows (c-layout k map), B = W2x tiles.
       bf16x8 ea[2];
       for (int ko = 0; ko < 2; ++ko) {
         const bf16* pe = &sEc[r * kP + 32 * ko + 4 * g];
         ea[ko] = cat8(ld4(pe), ld4(pe + 16));
       }
-      bf16x4 d1n[kNh];  // -a D1 ([token][hidden] tiles)
       for (int n = 0; n < kNh; ++n) {
         f32x4 acc = zero4();
         for (int ko = 0; ko < 2; ++ko) acc = mma32(ea[ko], cat_tiles(W2x[2 * ko][n], W2x[2 * ko + 1][n]), acc);
-        f32x4 d1;  // a D1
+        f32x4 d1;  // -a D1
         for (int j = 0; j < 4; ++j) d1[j] = acc[j] * Gp[n][j];
         d1p[n] = to_bf16x4(d1);
-        d1n[n] = neg_bf16x4(d1p[n]);
       }
       // W1 += K^T (-a D1): A = K^T (row feature, k token; LDS transpose read), B = -a D1.
       for (int m = 0; m < 4; ++m) {
         const bf16x4 kt = tile_tr(&sK[16 * m], kP, l);
-        for (int n = 0; n < kNh; ++n) W1t[m][n] = mma16(kt, d1n[n], W1t[m][n]);
+        for (int n = 0; n < kNh; ++n) W1t[m][n] = mma16(kt, d1p[n], W1t[m][n]);
       }
-      // W2 += (-X2)^T (a E) and W2^T += (a E)^T (-X2): a E's transposed tiles give both operands.
+      // W2 += X2^T (-a E) and W2^T += (-a E)^T X2: -a E's transposed tiles give both operands.
       for (int o2 = 0; o2 < 4; ++o2) {
         const bf16x4 e = tile_tr(&sEc[16 * o2], kP, l);
         for (int n = 0; n < kNh; ++n) {
-          W2t[n][o2] = mma16(x2n[n], e, W2t[n][o2]);
-          W2x[o2][n] = mma16(e, x2n[n], W2x[o2][n]);
+          W2t[n][o2] = mma16(x2b[n], e, W2t[n][o2]);
+          W2x[o2][n] = mma16(e, x2b[n], W2x[o2][n]);
         }
       }
     }
