@@ -72,11 +72,13 @@ template <int D>
 constexpr int max_seg_len() { return kRevLdsBytes / (D * D * 2); }
 
 // ---------------------------------------------------------------- staging with prefetch
-// The [CH x D] bf16 tiles of NTS tensors of one chunk (token stride ts) move HBM -> registers ->
-// LDS (row pitch P). The workgroup's threads form G groups; group j holds the chunks whose step
-// index is j mod G: it loads a chunk G steps before the step that uses it and stores it to LDS at
-// the start of that step, so each load has G steps to arrive with one register set per thread.
-template <int D, int CH, int NTH, int NTS, int G>
+// The [CH x D] bf16 tiles of NTS tensors of one chunk move HBM -> registers -> LDS (row pitch P).
+// The workgroup's threads form G groups; group j holds the chunks whose step index is j mod G: it
+// loads a chunk G steps before the step that uses it and stores it to LDS at the start of that
+// step, so each load has G steps to arrive with one register set per thread. A thread's 16-byte
+// pieces sit at fixed offsets within a chunk tile, computed once; when a tile spans whole waves,
+// the tensor of a piece is the same across the wave, and choosing its base pointer is scalar work.
+template <int D, int CH, int NTH, int NTS, int G, int P>
 struct ChunkStager {
   static_assert(NTH % G == 0 && NTS >= 1 && NTS <= 3, "staging geometry");
   static constexpr int CPR = D / 8;  // 16-byte pieces per row
@@ -84,31 +86,37 @@ struct ChunkStager {
   static constexpr int PIECES = NTS * TILE;
   static constexpr int GT = NTH / G;  // threads per group
   static constexpr int PER = (PIECES + GT - 1) / GT;
+  static constexpr bool kUniform = TILE % 64 == 0 && GT % 64 == 0;
   uint4 v[PER];
-  int group, idx;
-  __device__ __forceinline__ ChunkStager() : group(threadIdx.x / GT), idx(threadIdx.x % GT) {}
-  __device__ __forceinline__ bool mine(int step) const { return step % G == group; }
-  __device__ __forceinline__ void load(const bf16* t0, const bf16* t1, const bf16* t2,
-                                       long long ts) {
+  int group;
+  int sel[PER], goff[PER], loff[PER];
+  __device__ __forceinline__ explicit ChunkStager(long long ts) : group(threadIdx.x / GT) {
+    const int idx = threadIdx.x % GT;
     for (int i = 0; i < PER; ++i) {
-      const int p = idx + i * GT;
-      if (PIECES % GT == 0 || p < PIECES) {
-        const int sel = p / TILE, rem = p % TILE;
-        const bf16* src = sel == 0 ? t0 : (sel == 1 ? t1 : t2);
-        v[i] = ld16(src + (rem / CPR) * ts + (rem % CPR) * 8);
-      }
+      const int p = idx + i * GT, rem = p % TILE;
+      sel[i] = kUniform ? __builtin_amdgcn_readfirstlane(p / TILE) : p / TILE;
+      goff[i] = (int)((rem / CPR) * ts) + (rem % CPR) * 8;
+      loff[i] = (rem / CPR) * P + (rem % CPR) * 8;
     }
   }
-  template <int P>
-  __device__ __forceinline__ void store(bf16* d0, bf16* d1, bf16* d2) const {
-    for (int i = 0; i < PER; ++i) {
-      const int p = idx + i * GT;
-      if (PIECES % GT == 0 || p < PIECES) {
-        const int sel = p / TILE, rem = p % TILE;
-        bf16* dst = sel == 0 ? d0 : (sel == 1 ? d1 : d2);
-        st16(dst + (rem / CPR) * P + (rem % CPR) * 8, v[i]);
+  __device__ __forceinline__ bool mine(int step) const { return step % G == group; }
+  __device__ __forceinline__ bool valid(int i) const {
+    return PIECES % GT == 0 || (int)(threadIdx.x % GT) + i * GT < PIECES;
+  }
+  // t0, t1, t2: the chunk's first row in each tensor.
+  __device__ __forceinline__ void load(const bf16* t0, const bf16* t1, const bf16* t2) {
+    for (int i = 0; i < PER; ++i)
+      if (valid(i)) {
+        const bf16* src = sel[i] == 0 ? t0 : (sel[i] == 1 ? t1 : t2);
+        v[i] = ld16(src + goff[i]);
       }
-    }
+  }
+  __device__ __forceinline__ void store(bf16* d0, bf16* d1, bf16* d2) const {
+    for (int i = 0; i < PER; ++i)
+      if (valid(i)) {
+        bf16* dst = sel[i] == 0 ? d0 : (sel[i] == 1 ? d1 : d2);
+        st16(dst + loff[i], v[i]);
+      }
   }
 };
 
@@ -229,18 +237,18 @@ __global__ __launch_bounds__(D / 8 * 64) void chunk_compose_bf16(
     }
 
   constexpr int G = stage_groups<CH>();
-  ChunkStager<D, CH, NTH, 2, G> st;
-  const bf16* kb = k + head0;
-  const bf16* vb = v + head0;
+  ChunkStager<D, CH, NTH, 2, G, P> st(ts);
   const long long cs = (long long)CH * ts;  // elements between consecutive chunks
-  for (int j = 0; j < G && lo + j < hi; ++j)
-    if (st.mine(j)) st.load(kb + (lo + j) * cs, vb + (lo + j) * cs, nullptr, ts);
-  for (int c = lo; c < hi; ++c) {
+  const bf16* kn = k + head0 + lo * cs;     // chunk lo + j (j < G), then chunk c + G
+  const bf16* vn = v + head0 + lo * cs;
+  for (int j = 0; j < G; ++j, kn += cs, vn += cs)
+    if (lo + j < hi && st.mine(j)) st.load(kn, vn, nullptr);
+  for (int c = lo; c < hi; ++c, kn += cs, vn += cs) {
     bf16* sK = sKb[(c - lo) & 1];
     bf16* sV = sVb[(c - lo) & 1];
     if (st.mine(c - lo)) {
-      st.template store<P>(sK, sV, nullptr);
-      if (c + G < hi) st.load(kb + (c + G) * cs, vb + (c + G) * cs, nullptr, ts);
+      st.store(sK, sV, nullptr);
+      if (c + G < hi) st.load(kn, vn, nullptr);
     }
     __syncthreads();
     f32x4 Y[NP];
@@ -434,17 +442,19 @@ __global__ __launch_bounds__(D / 16 * 64) void chunk_scan_bf16(
   if constexpr (MODE == kBidir) {
     // Reverse scan over the segment's chunks (last to first), keeping each W^r_c in LDS.
     entry(1, W);
-    ChunkStager<D, CH, NTH, 2, G> sr;
-    for (int j = 0; j < G && hi - 1 - j >= lo; ++j)
-      if (sr.mine(j)) sr.load(kb + (hi - 1 - j) * cs, vb + (hi - 1 - j) * cs, nullptr, ts);
-    for (int c = hi - 1; c >= lo; --c) {
+    ChunkStager<D, CH, NTH, 2, G, P> sr(ts);
+    const bf16* kn = kb + (hi - 1) * cs;  // chunk hi - 1 - j (j < G), then chunk c - G
+    const bf16* vn = vb + (hi - 1) * cs;
+    for (int j = 0; j < G; ++j, kn -= cs, vn -= cs)
+      if (hi - 1 - j >= lo && sr.mine(j)) sr.load(kn, vn, nullptr);
+    for (int c = hi - 1; c >= lo; --c, kn -= cs, vn -= cs) {
       const int buf = NBUF == 2 ? (hi - 1 - c) & 1 : 0;
       bf16* sK = sKb[buf];
       bf16* sV = sVb[buf];
       if (NBUF == 1) __syncthreads();
       if (sr.mine(hi - 1 - c)) {
-        sr.template store<P>(sK, sV, nullptr);
-        if (c - G >= lo) sr.load(kb + (c - G) * cs, vb + (c - G) * cs, nullptr, ts);
+        sr.store(sK, sV, nullptr);
+        if (c - G >= lo) sr.load(kn, vn, nullptr);
       }
       __syncthreads();
       f32x4 E[NP];
@@ -459,10 +469,13 @@ __global__ __launch_bounds__(D / 16 * 64) void chunk_scan_bf16(
   // below orders the reverse pass's last tile reads before the first forward store.)
   if (MODE == kBidir) __syncthreads();
   entry(0, W);
-  ChunkStager<D, CH, NTH, 3, G> sf;
-  for (int j = 0; j < G && lo + j < hi; ++j)
-    if (sf.mine(j)) sf.load(kb + (lo + j) * cs, vb + (lo + j) * cs, qb + (lo + j) * cs, ts);
-  for (int c = lo; c < hi; ++c) {
+  ChunkStager<D, CH, NTH, 3, G, P> sf(ts);
+  const bf16* kn = kb + lo * cs;  // chunk lo + j (j < G), then chunk c + G
+  const bf16* vn = vb + lo * cs;
+  const bf16* qn = qb + lo * cs;
+  for (int j = 0; j < G; ++j, kn += cs, vn += cs, qn += cs)
+    if (lo + j < hi && sf.mine(j)) sf.load(kn, vn, qn);
+  for (int c = lo; c < hi; ++c, kn += cs, vn += cs, qn += cs) {
     const long long tok0 = head0 + (long long)c * CH * ts;
     const int buf = NBUF == 2 ? (c - lo) & 1 : 0;
     bf16* sK = sKb[buf];
@@ -471,8 +484,8 @@ __global__ __launch_bounds__(D / 16 * 64) void chunk_scan_bf16(
     bf16* sO = sOb[buf];
     if (NBUF == 1) __syncthreads();
     if (sf.mine(c - lo)) {
-      sf.template store<P>(sK, sV, sQ);
-      if (c + G < hi) sf.load(kb + (c + G) * cs, vb + (c + G) * cs, qb + (c + G) * cs, ts);
+      sf.store(sK, sV, sQ);
+      if (c + G < hi) sf.load(kn, vn, qn);
     }
     __syncthreads();
     if (NBUF == 2 && c > lo) store_chunk<D, CH, P, NTH>(o + tok0 - CH * ts, sOb[buf ^ 1], ts);
