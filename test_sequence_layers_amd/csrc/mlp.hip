@@ -24,7 +24,9 @@
 // so results are deterministic. The steps between the first and the last have both a read-out
 // and a forward, known at compile time, so that their products and GELUs share basic blocks and
 // interleave. E is kept as -a E (a = eta / b), so that -a D1 and the weight updates' operands come
-// out of the products with the right sign (no separate negations). Two workgroup barriers per
+// out of the products with the right sign (no separate negations). Operand precision: the
+// products on the W1 side (inputs K, Q and D1) take bf16 operands, those on the W2 side (X2, W2,
+// E, X2 X2^T) fp16 ones, which the packed fp16 GELU path produces directly; all accumulate in fp32. Two workgroup barriers per
 // chunk; K, V, Q are staged through a four-deep LDS ring: each chunk's global loads are issued
 // three chunks ahead into one of two alternating register sets and stored to LDS two chunks ahead.
 //
@@ -59,9 +61,10 @@ constexpr float kLog2InvSqrt2Pi = -1.32574806473615935f;   // log2(1 / sqrt(2 pi
 // Fast path, used when every argument of the wave's GELUs in a chunk step has x^2 <= 2
 // (|x / sqrt 2| <= 1): erf(u) = u P(u^2)
 // with P the degree-3 least-squares polynomial for erf(u)/u on u^2 in [0, 1] (fitted on Chebyshev
-// nodes; max abs error of erf 2.7e-5 in fp32 Horner form, two orders below the bf16 rounding of
-// the products that consume GELU's output), so Phi(x) = 1/2 + x R(x^2) with
-// R(t) = P(t / 2) / (2 sqrt 2). Otherwise the library erf is used.
+// nodes; max abs error of erf 2.7e-5 in fp32 Horner form), so Phi(x) = 1/2 + x R(x^2) with
+// R(t) = P(t / 2) / (2 sqrt 2). It runs in packed fp16 (below); its GELU and GELU' stay within
+// 1.1e-3 of the exact values, about the rounding of a bf16 operand. Otherwise fp32 with the
+// library erf and exp2.
 constexpr float kErfP[4] = {1.128350616f, -0.3751908541f, 0.1079747304f, -0.0184600465f};
 constexpr float kInvTwoSqrt2 = 0.35355339059327376220f;
 constexpr float kR0 = kErfP[0] * kInvTwoSqrt2, kR1 = kErfP[1] * kInvTwoSqrt2 / 2.f,
@@ -79,12 +82,63 @@ __device__ __forceinline__ bf16x8 cat_tiles(f32x4 lo, f32x4 hi) {
   return cat8(to_bf16x4(lo), to_bf16x4(hi));
 }
 
+// fp16 operands for the products on the W2 side (X2, W2, E and the X2 X2^T terms): three more
+// mantissa bits than bf16, and the packed fp16 arithmetic of the fast GELU path yields them
+// directly (no conversions). Their range (|x| < 65504) is far above these activations.
+typedef _Float16 f16;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x4 mmah32(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mmah16(f16x4 a, f16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f16x4 to_f16x4(f32x4 x) {  // round to nearest even, two per instruction
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f16x2 lo = __builtin_convertvector(f32x2{x[0], x[1]}, f16x2);
+  const f16x2 hi = __builtin_convertvector(f32x2{x[2], x[3]}, f16x2);
+  return __builtin_bit_cast(f16x4, make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)));
+}
+__device__ __forceinline__ f16x8 cat8h(f16x4 lo, f16x4 hi) {
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ f16x8 cat_tiles_h(f32x4 lo, f32x4 hi) { return cat8h(to_f16x4(lo), to_f16x4(hi)); }
+__device__ __forceinline__ f16x4 ld4h(const f16* p) { return *reinterpret_cast<const f16x4*>(p); }
+__device__ __forceinline__ f16x4 tile_tr_h(const f16* base, int pitch, int l) {  // as tile_tr
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const int u = l & 15;
+  const f16* p = base + (4 * (l >> 4) + (u >> 2)) * pitch + 4 * (u & 3);
+  return __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p));
+}
+
+// Fast GELU path in packed fp16 (|x| <= sqrt 2): Phi(x) = 1/2 + x R(t) as above, and
+// GELU'(x) = 1/2 + x S(t), t = x^2, with S the degree-3 least-squares polynomial for
+// (Phi(x) - 1/2) / x + phi(x) on t in [0, 2] (Chebyshev nodes; max abs error of GELU' 1.2e-4).
+constexpr float kS0 = 0.7977905544868868f, kS1 = -0.26441428752463436f, kS2 = 0.0557860757632853f,
+                kS3 = -0.0059361438042217956f;
+__device__ __forceinline__ f16x4 splat(float v) { return (f16x4)(f16)v; }
+__device__ __forceinline__ f16x4 fmah(f16x4 a, f16x4 b, f16x4 c) { return __builtin_elementwise_fma(a, b, c); }
+__device__ __forceinline__ f16x4 cdf_fast_h(f16x4 x, f16x4 t) {
+  f16x4 r = fmah(splat(kR3), t, splat(kR2));
+  r = fmah(r, t, splat(kR1));
+  r = fmah(r, t, splat(kR0));
+  return fmah(x, r, splat(0.5f));
+}
+__device__ __forceinline__ f16x4 slope_fast_h(f16x4 x, f16x4 t) {
+  f16x4 r = fmah(splat(kS3), t, splat(kS2));
+  r = fmah(r, t, splat(kS1));
+  r = fmah(r, t, splat(kS0));
+  return fmah(x, r, splat(0.5f));
+}
+
 __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ w1, const float* __restrict__ w2, long long wbs, int H, int N,
     float a, bf16* __restrict__ o, float* __restrict__ w1_out, float* __restrict__ w2_out) {
   __shared__ __align__(16) bf16 sKVQ[kRing][3][kCh * kP];
-  __shared__ __align__(16) bf16 sE[2][kCh * kP];           // E [token][out]
+  __shared__ __align__(16) f16 sE[2][kCh * kP];            // -a E [token][out] (fp16)
   __shared__ __align__(16) f32x4 sRed[kWaves * kSlots * 64];  // lane-private partial tiles
 
   const int bh = blockIdx.x, b = bh / H, h = bh % H;
@@ -105,8 +159,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
         W2t[n][m][j] = W2g[(hid0 + 16 * n + 4 * g + j) * kD + 16 * m + r];
         W2x[m][n][j] = W2g[(hid0 + 16 * n + r) * kD + 16 * m + 4 * g + j];
       }
-  bf16x4 ident;  // identity tile as the B operand: lane holds I[4g + i][r]
-  for (int i = 0; i < 4; ++i) ident[i] = (bf16)(4 * g + i == r ? 1.f : 0.f);
+  f16x4 ident;  // identity tile as the B operand: lane holds I[4g + i][r]
+  for (int i = 0; i < 4; ++i) ident[i] = (f16)(4 * g + i == r ? 1.f : 0.f);
 
   const int C = N / kCh;
   const long long head0 = (long long)b * N * ts + (long long)h * kD;
@@ -123,9 +177,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
   __syncthreads();
 
   bf16x4 d1p[kNh];  // -a D1 of the previous chunk, [token][hidden] tiles
-  bf16x8 x2tp;      // X2^T of the previous chunk, [hidden][token] tiles (both, c-layout k map)
+  f16x8 x2tp;       // X2^T of the previous chunk, [hidden][token] tiles (both, c-layout k map)
   for (int n = 0; n < kNh; ++n) d1p[n] = bf16x4{};
-  x2tp = bf16x8{};
+  x2tp = f16x8{};
 
   // One chunk step: forward of chunk c, read-out of chunk c - 1. pf_cur holds chunk c + 2 (loaded
   // one step earlier); chunk c + 3 is loaded into pf_next.
@@ -137,8 +191,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
     const bf16* sV = sKVQ[c % kRing][1];
     const bf16* sKp = sKVQ[(c + kRing - 1) % kRing][0];  // chunk c - 1
     const bf16* sQp = sKVQ[(c + kRing - 1) % kRing][2];
-    bf16* sEc = sE[c & 1];
-    const bf16* sEp = sE[(c + 1) & 1];  // -a E of chunk c - 1
+    f16* sEc = sE[c & 1];
+    const f16* sEp = sE[(c + 1) & 1];  // -a E of chunk c - 1
 
     // ---------------- phase 1: products with the current weights. The read-out of chunk c - 1
     // and the forward of chunk c are independent; their products, GELUs and remaining products
@@ -146,9 +200,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
     bf16x8 w1b[2][kNh];  // W1 tiles (k = features, c-layout k map)
     for (int ks = 0; ks < 2; ++ks)
       for (int n = 0; n < kNh; ++n) w1b[ks][n] = cat_tiles(W1t[2 * ks][n], W1t[2 * ks + 1][n]);
-    f32x4 Z1q[kNh], X2q[kNh];  // read-out: Z1q^T [hidden][token]
-    f32x4 Z1[kNh], X2[kNh];    // forward: Z1 [token][hidden]
-    f32x4 Gp[kNh];
+    f32x4 Z1q[kNh];  // read-out: Z1q^T [hidden][token]
+    f32x4 Z1[kNh];   // forward: Z1 [token][hidden]
+    f16x4 x2qh[kNh], x2b[kNh], gph[kNh];  // GELU(Z1q), GELU(Z1), GELU'(Z1) as fp16 tiles
     if constexpr (rd) {
       // M[t'][t] = k_t' . q_t of chunk c - 1, kept for t' > t.
       f32x4 mt = zero4();
@@ -180,64 +234,78 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
       }
     }
     {  // GELU of both chains, one fast-path decision for the wave
-      float tmax = 0.f;
-      for (int n = 0; n < kNh; ++n)
-        for (int j = 0; j < 4; ++j) {
-          if constexpr (rd) tmax = fmaxf(tmax, Z1q[n][j] * Z1q[n][j]);
-          if constexpr (fwd) tmax = fmaxf(tmax, Z1[n][j] * Z1[n][j]);
+      f16x4 zq[kNh], zf[kNh], tq[kNh], tf[kNh];
+      f16x4 tm = splat(0.f);
+      for (int n = 0; n < kNh; ++n) {
+        if constexpr (rd) {
+          zq[n] = to_f16x4(Z1q[n]);
+          tq[n] = zq[n] * zq[n];
+          tm = __builtin_elementwise_max(tm, tq[n]);
         }
-      auto slope = [&](float x, float cdf, int n, int j) {
-        X2[n][j] = x * cdf;
-        Gp[n][j] = fmaf(x, __builtin_amdgcn_exp2f(fmaf(x * x, kNegHalfLog2e, kLog2InvSqrt2Pi)), cdf);
-      };
-      if (!__any(tmax > 2.f)) {
-        for (int n = 0; n < kNh; ++n)
-          for (int j = 0; j < 4; ++j) {
-            if constexpr (rd) X2q[n][j] = Z1q[n][j] * cdf_fast(Z1q[n][j], Z1q[n][j] * Z1q[n][j]);
-            if constexpr (fwd) slope(Z1[n][j], cdf_fast(Z1[n][j], Z1[n][j] * Z1[n][j]), n, j);
+        if constexpr (fwd) {
+          zf[n] = to_f16x4(Z1[n]);
+          tf[n] = zf[n] * zf[n];
+          tm = __builtin_elementwise_max(tm, tf[n]);
+        }
+      }
+      const float tmax = fmaxf(fmaxf((float)tm[0], (float)tm[1]), fmaxf((float)tm[2], (float)tm[3]));
+      if (!__any(!(tmax <= 2.f))) {
+        for (int n = 0; n < kNh; ++n) {
+          if constexpr (rd) x2qh[n] = zq[n] * cdf_fast_h(zq[n], tq[n]);
+          if constexpr (fwd) {
+            x2b[n] = zf[n] * cdf_fast_h(zf[n], tf[n]);
+            gph[n] = slope_fast_h(zf[n], tf[n]);
           }
-      } else {
-        for (int n = 0; n < kNh; ++n)
+        }
+      } else {  // fp32 with the library erf
+        for (int n = 0; n < kNh; ++n) {
+          f32x4 xq, xf, gp;
           for (int j = 0; j < 4; ++j) {
-            if constexpr (rd) X2q[n][j] = Z1q[n][j] * cdf_lib(Z1q[n][j]);
-            if constexpr (fwd) slope(Z1[n][j], cdf_lib(Z1[n][j]), n, j);
+            if constexpr (rd) xq[j] = Z1q[n][j] * cdf_lib(Z1q[n][j]);
+            if constexpr (fwd) {
+              const float x = Z1[n][j], cdf = cdf_lib(x);
+              xf[j] = x * cdf;
+              gp[j] = fmaf(x, __builtin_amdgcn_exp2f(fmaf(x * x, kNegHalfLog2e, kLog2InvSqrt2Pi)), cdf);
+            }
           }
+          if constexpr (rd) x2qh[n] = to_f16x4(xq);
+          if constexpr (fwd) {
+            x2b[n] = to_f16x4(xf);
+            gph[n] = to_f16x4(gp);
+          }
+        }
       }
     }
-    bf16x8 x2q;
-    bf16x4 n2b;
+    f16x8 x2q;
+    f16x4 n2b;
     if constexpr (rd) {
-      x2q = cat_tiles(X2q[0], X2q[1]);
+      x2q = cat8h(x2qh[0], x2qh[1]);
       // (with the previous chunk's X2^T, before the forward below replaces it)
-      f32x4 n2 = mma32(x2tp, x2q, zero4());  // [t'][t] = sum_h X2[t'][h] X2q[t][h]
+      f32x4 n2 = mmah32(x2tp, x2q, zero4());  // [t'][t] = sum_h X2[t'][h] X2q[t][h]
       for (int j = 0; j < 4; ++j) n2[j] = 4 * g + j <= r ? 0.f : -n2[j];
-      n2b = to_bf16x4(n2);  // (-a is in the stored E)
+      n2b = to_f16x4(n2);  // (-a is in the stored E)
     }
-    bf16x4 x2b[kNh];  // X2, [token][hidden] tiles
     if constexpr (fwd) {
       f32x4 xt[kNh];
-      for (int n = 0; n < kNh; ++n) {
-        x2b[n] = to_bf16x4(X2[n]);
-        xt[n] = mma16(x2b[n], ident, zero4());  // X2^T [hidden][token]
-      }
-      x2tp = cat_tiles(xt[0], xt[1]);
+      for (int n = 0; n < kNh; ++n) xt[n] = mmah16(x2b[n], ident, zero4());  // X2^T [hidden][token]
+      x2tp = cat_tiles_h(xt[0], xt[1]);
     }
-    bf16x8 w2a[4];  // W2^T tiles (k = this wave's hidden units), for both products below
-    for (int o2 = 0; o2 < 4; ++o2) w2a[o2] = cat_tiles(W2t[0][o2], W2t[1][o2]);
+    f16x8 w2a[4];  // W2^T tiles (k = this wave's hidden units), for both products below
+    for (int o2 = 0; o2 < 4; ++o2) w2a[o2] = cat_tiles_h(W2t[0][o2], W2t[1][o2]);
     if constexpr (rd) {
       // This wave's share of O^T [out][token]: W2^T X2q^T over its hidden units, plus
       // (a E)^T striu(X2q X2^T)^T = (-a E)^T (-striu(X2q X2^T))^T with X2q X2^T summed over the
       // same units (t' > t kept), the latter as a 16x16x32 product with a zero upper k half
       // (same-shape chain).
       for (int o2 = 0; o2 < 4; ++o2) {
-        const f32x4 ow = mma32(w2a[o2], x2q, zero4());
+        const f32x4 ow = mmah32(w2a[o2], x2q, zero4());
         sRed[(w * kSlots + 4 + o2) * 64 + l] =
-            mma32(cat8(tile_tr(&sEp[16 * o2], kP, l), bf16x4{}), cat8(n2b, bf16x4{}), ow);  // A = (-a E)^T
+            mmah32(cat8h(tile_tr_h(&sEp[16 * o2], kP, l), f16x4{}), cat8h(n2b, f16x4{}), ow);  // A = (-a E)^T
       }
     }
     if constexpr (fwd) {
       // Z2^T partial [out][token] over this wave's hidden units.
-      for (int o2 = 0; o2 < 4; ++o2) sRed[(w * kSlots + o2) * 64 + l] = mma32(w2a[o2], x2tp, zero4());
+      for (int o2 = 0; o2 < 4; ++o2) sRed[(w * kSlots + o2) * 64 + l] = mmah32(w2a[o2], x2tp, zero4());
     }
     __syncthreads();
 
@@ -246,9 +314,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
       f32x4 s = sRed[w * 64 + l];
       for (int ww = 1; ww < kWaves; ++ww) s = s + sRed[(ww * kSlots + w) * 64 + l];
       const bf16x4 vv = ld4(&sV[r * kP + 16 * w + 4 * g]);
-      bf16x4 eb;
-      for (int j = 0; j < 4; ++j) eb[j] = (bf16)(a * ((float)vv[j] - s[j]));
-      *reinterpret_cast<bf16x4*>(&sEc[r * kP + 16 * w + 4 * g]) = eb;
+      f32x4 e;
+      for (int j = 0; j < 4; ++j) e[j] = a * ((float)vv[j] - s[j]);
+      *reinterpret_cast<f16x4*>(&sEc[r * kP + 16 * w + 4 * g]) = to_f16x4(e);
     }
     if (rd && w >= 4) {  // O^T tile of chunk c - 1 = sum of the waves' shares
       const int o4 = w - 4;
@@ -262,16 +330,16 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
     // ---------------- phase 3: backward and state update of chunk c
     if (fwd) {
       // -a dX2 [token][hidden] = (-a E) W2^T: A = -a E rows (c-layout k map), B = W2x tiles.
-      bf16x8 ea[2];
+      f16x8 ea[2];
       for (int ko = 0; ko < 2; ++ko) {
-        const bf16* pe = &sEc[r * kP + 32 * ko + 4 * g];
-        ea[ko] = cat8(ld4(pe), ld4(pe + 16));
+        const f16* pe = &sEc[r * kP + 32 * ko + 4 * g];
+        ea[ko] = cat8h(ld4h(pe), ld4h(pe + 16));
       }
       for (int n = 0; n < kNh; ++n) {
         f32x4 acc = zero4();
-        for (int ko = 0; ko < 2; ++ko) acc = mma32(ea[ko], cat_tiles(W2x[2 * ko][n], W2x[2 * ko + 1][n]), acc);
+        for (int ko = 0; ko < 2; ++ko) acc = mmah32(ea[ko], cat_tiles_h(W2x[2 * ko][n], W2x[2 * ko + 1][n]), acc);
         f32x4 d1;  // -a D1
-        for (int j = 0; j < 4; ++j) d1[j] = acc[j] * Gp[n][j];
+        for (int j = 0; j < 4; ++j) d1[j] = acc[j] * (float)gph[n][j];
         d1p[n] = to_bf16x4(d1);
       }
       // W1 += K^T (-a D1): A = K^T (row feature, k token; LDS transpose read), B = -a D1.
@@ -281,10 +349,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
       }
       // W2 += X2^T (-a E) and W2^T += (-a E)^T X2: -a E's transposed tiles give both operands.
       for (int o2 = 0; o2 < 4; ++o2) {
-        const bf16x4 e = tile_tr(&sEc[16 * o2], kP, l);
+        const f16x4 e = tile_tr_h(&sEc[16 * o2], kP, l);
         for (int n = 0; n < kNh; ++n) {
-          W2t[n][o2] = mma16(x2b[n], e, W2t[n][o2]);
-          W2x[o2][n] = mma16(e, x2b[n], W2x[o2][n]);
+          W2t[n][o2] = mmah16(x2b[n], e, W2t[n][o2]);
+          W2x[o2][n] = mmah16(e, x2b[n], W2x[o2][n]);
         }
       }
     }

@@ -118,3 +118,43 @@ def test_mlp_fast_gelu_polynomial_matches_erf():
         acc = acc * t + c
     cdf = x * acc + np.float32(0.5)
     assert np.abs(cdf.astype(np.float64) - ndtr(x.astype(np.float64))).max() < 3e-5
+
+
+def _mlp_slope_coefficients():
+    src = open(os.path.join(B.CSRC, "mlp.hip")).read()
+    coef = {int(m.group(1)): float(m.group(2)) for m in re.finditer(r"kS(\d)\s*=\s*([-+0-9.eE]+)f", src)}
+    assert sorted(coef) == [0, 1, 2, 3], "kS0..kS3 not found in mlp.hip"
+    return [coef[i] for i in range(4)]
+
+
+def test_mlp_fast_gelu_in_fp16():
+    """The fast path runs in packed fp16: Phi(x) = 1/2 + x R(t), GELU(x) = x Phi(x) and
+    GELU'(x) = 1/2 + x S(t), t = x^2 <= 2, Horner form, every operation rounded to fp16 (numpy
+    rounds the product and the sum of each step separately, one rounding more than the hardware's
+    fused multiply-add). GELU and GELU' stay within 1.5e-3 of the exact values over |x| <= sqrt 2,
+    about the rounding of a bf16 operand of that size."""
+    import numpy as np
+    from scipy.special import ndtr
+
+    h = np.float16
+    k = 0.35355339059327376220
+    r = [np.float32(c * k / 2 ** i) for i, c in enumerate(_mlp_erf_coefficients())]
+    s = _mlp_slope_coefficients()
+    x = np.linspace(-np.sqrt(2.0), np.sqrt(2.0), 400001).astype(h)
+    t = (x * x).astype(h)
+
+    def horner(cs):
+        acc = h(cs[-1])
+        for c in cs[-2::-1]:
+            acc = (acc * t).astype(h)
+            acc = (acc + h(c)).astype(h)
+        return acc
+
+    cdf = ((x * horner(r)).astype(h) + h(0.5)).astype(h)
+    gelu = (x * cdf).astype(h).astype(np.float64)
+    slope = ((x * horner(s)).astype(h) + h(0.5)).astype(h).astype(np.float64)
+    xd = x.astype(np.float64)
+    phi = np.exp(-xd * xd / 2) / np.sqrt(2 * np.pi)
+    assert np.abs(gelu - xd * ndtr(xd)).max() < 1.5e-3
+    assert np.abs(slope - (ndtr(xd) + xd * phi)).max() < 1.5e-3
+
