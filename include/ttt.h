@@ -40,7 +40,9 @@
  *   workspaces.
  * Precision.  TTT_F32 computes in fp32 throughout (plain FMA, no reduced-precision operands).
  *   TTT_BF16 reads and writes bf16 (round-to-nearest-even on output), keeps the state and every
- *   accumulator in fp32, and feeds bf16 operands to the matrix cores.
+ *   accumulator in fp32, and feeds 16-bit operands to the matrix cores: bf16, except in
+ *   ttt_mlp_forward's products on the W2 side (hidden activations, W2, residuals), which take
+ *   fp16 operands (more mantissa bits; those values stay far inside fp16's range).
  * Threads.  Entry points are reentrant and keep no global state.
  */
 #ifndef TTT_H_
