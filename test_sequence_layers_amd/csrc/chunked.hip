@@ -66,6 +66,22 @@ __device__ __forceinline__ int dev_offset(int row, int kcol) {  // bf16 offset o
          4 * half;
 }
 
+// Row pitch (elements) of the [token][feature] LDS tiles. For d = 64 it is 76 (152 bytes = 38 banks of 4 bytes): the
+// two 8-byte reads 32 bytes apart that form a c-layout operand, the row reads and the transpose reads then hit
+// distinct banks (a 144-byte pitch makes the paired reads of rows r and r + 2 collide). Rows are then only 8-byte
+// aligned, so tiles move through LDS in 8-byte pieces.
+template <int D>
+constexpr int lds_pitch() { return D == 64 ? 76 : D + 8; }
+// 16 bytes between registers and an LDS row that may be only 8-byte aligned.
+__device__ __forceinline__ void st16_lds8(bf16* p, uint4 v) {
+  reinterpret_cast<uint2*>(p)[0] = make_uint2(v.x, v.y);
+  reinterpret_cast<uint2*>(p)[1] = make_uint2(v.z, v.w);
+}
+__device__ __forceinline__ uint4 ld16_lds8(const bf16* p) {
+  const uint2 a = reinterpret_cast<const uint2*>(p)[0], b = reinterpret_cast<const uint2*>(p)[1];
+  return make_uint4(a.x, a.y, b.x, b.y);
+}
+
 // LDS bytes available for the reverse states of one bidirectional scan segment.
 constexpr int kRevLdsBytes = 96 * 1024;
 template <int D>
@@ -115,7 +131,7 @@ struct ChunkStager {
     for (int i = 0; i < PER; ++i)
       if (valid(i)) {
         bf16* dst = sel[i] == 0 ? d0 : (sel[i] == 1 ? d1 : d2);
-        st16(dst + loff[i], v[i]);
+        st16_lds8(dst + loff[i], v[i]);
       }
   }
 };
@@ -130,7 +146,7 @@ __device__ __forceinline__ void store_chunk(bf16* dst, const bf16* src, long lon
   constexpr int CPR = D / 8;
   for (int c = threadIdx.x; c < CH * CPR; c += NTH) {
     const int row = c / CPR, col = (c % CPR) * 8;
-    st16(dst + row * ts + col, ld16(src + row * P + col));
+    st16(dst + row * ts + col, ld16_lds8(src + row * P + col));
   }
 }
 
@@ -213,7 +229,7 @@ template <int D, int CH, bool BIDIR>
 __global__ __launch_bounds__(D / 8 * 64) void chunk_compose_bf16(
     const bf16* __restrict__ k, const bf16* __restrict__ v, int H, int N, float a, int S, int L,
     float* __restrict__ comp) {
-  constexpr int P = D + 8, NT = D / 16, NP = CH / 16, NTH = 2 * NT * 64;
+  constexpr int P = lds_pitch<D>(), NT = D / 16, NP = CH / 16, NTH = 2 * NT * 64;
   constexpr long long DD = (long long)D * D;
   // Double-buffered chunk tiles: chunk c is staged while other waves may still read chunk c - 1,
   // so one barrier per chunk suffices.
@@ -390,7 +406,7 @@ __global__ __launch_bounds__(D / 16 * 64) void chunk_scan_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ w0, long long w0_bstride, int H, int N, float a, int S, int L,
     const float* __restrict__ win, bf16* __restrict__ o, float* __restrict__ w_out) {
-  constexpr int P = D + 8;
+  constexpr int P = lds_pitch<D>();
   constexpr int NT = D / 16;   // waves = column tiles = row tiles
   constexpr int NP = CH / 16;  // 16-token tiles per chunk
   constexpr int NTH = NT * 64;
@@ -506,8 +522,8 @@ __global__ __launch_bounds__(D / 16 * 64) void chunk_scan_bf16(
           f32x4 pt = zero4();
           if constexpr (D >= 32) {
             for (int ks = 0; ks < D / 32; ++ks)
-              pt = mma32(ld8(&sK[(16 * pp + r) * P + 32 * ks + 8 * g]),
-                         ld8(&sQ[(16 * p + r) * P + 32 * ks + 8 * g]), pt);
+              pt = mma32(cat8(ld4(&sK[(16 * pp + r) * P + 32 * ks + 4 * g]), ld4(&sK[(16 * pp + r) * P + 32 * ks + 16 + 4 * g])),
+                         cat8(ld4(&sQ[(16 * p + r) * P + 32 * ks + 4 * g]), ld4(&sQ[(16 * p + r) * P + 32 * ks + 16 + 4 * g])), pt);
           } else {
             pt = mma16(ld4(&sK[(16 * pp + r) * P + 4 * g]), ld4(&sQ[(16 * p + r) * P + 4 * g]), pt);
           }
