@@ -48,7 +48,10 @@ constexpr int kCh = 16;       // tokens per chunk
 constexpr int kWaves = 8;
 constexpr int kHw = kDh / kWaves;  // hidden units per wave
 constexpr int kNh = kHw / 16;      // 16-unit hidden tiles per wave
-constexpr int kP = kD + 8;         // pitch of [token][feature] tiles (elements)
+// Pitch of [token][feature] tiles (elements): 152 bytes = 38 banks, so the paired 8-byte operand
+// reads (32 bytes apart), the row reads and the transpose reads hit distinct banks. Rows are only
+// 8-byte aligned: staging stores go in 8-byte pieces.
+constexpr int kP = kD + 12;
 constexpr int kRing = 4;           // K/V/Q staging depth
 constexpr int kSlots = 8;          // partial tiles per wave: Z2^T x4, O^T x4
 
@@ -133,6 +136,11 @@ __device__ __forceinline__ f16x4 slope_fast_h(f16x4 x, f16x4 t) {
   return fmah(x, r, splat(0.5f));
 }
 
+__device__ __forceinline__ void st16_lds8(bf16* p, uint4 v) {
+  reinterpret_cast<uint2*>(p)[0] = make_uint2(v.x, v.y);
+  reinterpret_cast<uint2*>(p)[1] = make_uint2(v.z, v.w);
+}
+
 __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ w1, const float* __restrict__ w2, long long wbs, int H, int N,
@@ -170,8 +178,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
   const bf16* psrc = (t < 128 ? k : (t < 256 ? v : q)) + head0 + prow * ts + pcol;
   uint4 pfA = make_uint4(0u, 0u, 0u, 0u), pfB = make_uint4(0u, 0u, 0u, 0u);
   if (t < 384) {
-    st16(&sKVQ[0][which][prow * kP + pcol], ld16(psrc));
-    if (C > 1) st16(&sKVQ[1][which][prow * kP + pcol], ld16(psrc + kCh * ts));
+    st16_lds8(&sKVQ[0][which][prow * kP + pcol], ld16(psrc));
+    if (C > 1) st16_lds8(&sKVQ[1][which][prow * kP + pcol], ld16(psrc + kCh * ts));
     if (C > 2) pfB = ld16(psrc + 2 * kCh * ts);
   }
   __syncthreads();
@@ -207,7 +215,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
       // M[t'][t] = k_t' . q_t of chunk c - 1, kept for t' > t.
       f32x4 mt = zero4();
       for (int ks = 0; ks < 2; ++ks)
-        mt = mma32(ld8(&sKp[r * kP + 32 * ks + 8 * g]), ld8(&sQp[r * kP + 32 * ks + 8 * g]), mt);
+        mt = mma32(cat8(ld4(&sKp[r * kP + 32 * ks + 4 * g]), ld4(&sKp[r * kP + 32 * ks + 16 + 4 * g])),
+                   cat8(ld4(&sQp[r * kP + 32 * ks + 4 * g]), ld4(&sQp[r * kP + 32 * ks + 16 + 4 * g])), mt);
       for (int j = 0; j < 4; ++j) mt[j] = 4 * g + j <= r ? 0.f : -mt[j];
       const bf16x4 mb = to_bf16x4(mt);  // -M, t' > t kept (the carried D1 is -a D1)
       // Z1q^T = W1^T Q^T + a D1^T M = W1^T Q^T + (-a D1)^T (-M).
@@ -356,7 +365,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
         }
       }
     }
-    if (t < 384 && c + 2 < C) st16(&sKVQ[(c + 2) % kRing][which][prow * kP + pcol], pf_cur);
+    if (t < 384 && c + 2 < C) st16_lds8(&sKVQ[(c + 2) % kRing][which][prow * kP + pcol], pf_cur);
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
