@@ -82,8 +82,9 @@ __device__ __forceinline__ uint4 ld16_lds8(const bf16* p) {
   return make_uint4(a.x, a.y, b.x, b.y);
 }
 
-// LDS bytes available for the reverse states of one bidirectional scan segment.
-constexpr int kRevLdsBytes = 96 * 1024;
+// LDS bytes available for the reverse states of one bidirectional scan segment: 80 KB holds 10
+// states of d = 64 and leaves room for double-buffered 64-token tiles (one barrier per chunk).
+constexpr int kRevLdsBytes = 80 * 1024;
 template <int D>
 constexpr int max_seg_len() { return kRevLdsBytes / (D * D * 2); }
 
