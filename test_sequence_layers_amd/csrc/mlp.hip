@@ -320,17 +320,25 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
 
     // ---------------- phase 2: cross-wave sums (fixed wave order)
     if (fwd && w < 4) {  // E^T tile w = Z2^T - V^T, stored as -a E [token][out]
-      f32x4 s = sRed[w * 64 + l];
-      for (int ww = 1; ww < kWaves; ++ww) s = s + sRed[(ww * kSlots + w) * 64 + l];
+      // All nine LDS reads are issued before the adds (the compiler otherwise keeps only two or
+      // three of them in flight, and this phase is their latency).
+      f32x4 pt[kWaves];
+      for (int ww = 0; ww < kWaves; ++ww) pt[ww] = sRed[(ww * kSlots + w) * 64 + l];
       const bf16x4 vv = ld4(&sV[r * kP + 16 * w + 4 * g]);
+      __builtin_amdgcn_sched_group_barrier(0x100, 9, 0);
+      f32x4 s = pt[0];
+      for (int ww = 1; ww < kWaves; ++ww) s = s + pt[ww];
       f32x4 e;
       for (int j = 0; j < 4; ++j) e[j] = a * ((float)vv[j] - s[j]);
       *reinterpret_cast<f16x4*>(&sEc[r * kP + 16 * w + 4 * g]) = to_f16x4(e);
     }
     if (rd && w >= 4) {  // O^T tile of chunk c - 1 = sum of the waves' shares
       const int o4 = w - 4;
-      f32x4 s = sRed[(4 + o4) * 64 + l];
-      for (int ww = 1; ww < kWaves; ++ww) s = s + sRed[(ww * kSlots + 4 + o4) * 64 + l];
+      f32x4 pt[kWaves];
+      for (int ww = 0; ww < kWaves; ++ww) pt[ww] = sRed[(ww * kSlots + 4 + o4) * 64 + l];
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+      f32x4 s = pt[0];
+      for (int ww = 1; ww < kWaves; ++ww) s = s + pt[ww];
       const long long tokp = head0 + (long long)(c - 1) * kCh * ts;
       *reinterpret_cast<bf16x4*>(o + tokp + r * ts + 16 * o4 + 4 * g) = to_bf16x4(s);
     }
