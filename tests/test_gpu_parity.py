@@ -127,6 +127,9 @@ SEGMENTED = [
     W["vittt_bidir_1280"].with_(B=1, N=2048, H=2, D=32, chunk=16, seed=113),
     W["vittt_bidir_1280"].with_(B=1, N=2048, H=2, D=16, chunk=32, seed=114),
     W["vittt_bidir_1280"].with_(B=2, N=2048, H=1, D=64, chunk=16, seed=115),
+    # segments capped by the LDS budget for the reverse states (10 chunks), more segments than
+    # resident workgroups
+    W["vittt_bidir_1280"].with_(B=4, N=16384, H=3, seed=116),
 ]
 
 
