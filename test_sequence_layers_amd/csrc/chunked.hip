@@ -444,6 +444,11 @@ __global__ __launch_bounds__(D / 16 * 64) void chunk_scan_bf16(
       for (int m = 0; m < NT; ++m) W[m] = *reinterpret_cast<const f32x4*>(src + state_tile<D>(w, m, l));
     }
   };
+  // The entry state comes from global memory. Waiting for those loads here, once, keeps the
+  // compiler's wait tracking from treating the state registers as possibly still in flight inside
+  // the chunk loop, where it would otherwise wait for every outstanding load (the chunk prefetch
+  // included) before each use of the state.
+  auto entry_done = [] { __builtin_amdgcn_s_waitcnt(0); };
   auto save = [&](float* dst, const f32x4* W) {
     for (int m = 0; m < NT; ++m)
       for (int j = 0; j < 4; ++j) dst[(16 * m + 4 * g + j) * D + 16 * w + r] = W[m][j];
@@ -459,6 +464,7 @@ __global__ __launch_bounds__(D / 16 * 64) void chunk_scan_bf16(
   if constexpr (MODE == kBidir) {
     // Reverse scan over the segment's chunks (last to first), keeping each W^r_c in LDS.
     entry(1, W);
+    entry_done();
     ChunkStager<D, CH, NTH, 2, G, P> sr(ts);
     const bf16* kn = kb + (hi - 1) * cs;  // chunk hi - 1 - j (j < G), then chunk c - G
     const bf16* vn = vb + (hi - 1) * cs;
@@ -486,6 +492,7 @@ __global__ __launch_bounds__(D / 16 * 64) void chunk_scan_bf16(
   // below orders the reverse pass's last tile reads before the first forward store.)
   if (MODE == kBidir) __syncthreads();
   entry(0, W);
+  entry_done();
   ChunkStager<D, CH, NTH, 3, G, P> sf(ts);
   const bf16* kn = kb + lo * cs;  // chunk lo + j (j < G), then chunk c + G
   const bf16* vn = vb + lo * cs;
