@@ -8,9 +8,11 @@ One step = one forward of every layer variant of the library, each at its refere
   * causal TTT-MLP language layer: B=4, N=8192, 12 x 64, hidden 256, b=16
 Inputs are synthetic (seeded i.i.d. Gaussians of those shapes) and resident in HBM before the
 timed region. The four layers' inputs (584 MB) exceed the 256 MB Infinity Cache, so every layer
-starts with its inputs evicted by the other three.
+starts with its inputs evicted by the other three. Within a step the TTT-MLP layer, whose 48
+sequential chains occupy 48 CUs, runs on a second stream beside the other three layers (--serial:
+all four one after another on one stream).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--serial]
 """
 from __future__ import annotations
 
@@ -196,6 +198,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--serial", action="store_true", help="run the layers of a step one after another on one stream")
     ap.add_argument("--layers", default=",".join(SUITE), help="comma-separated subset of the suite (profiling)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--write-traffic", metavar="PMC_DIR", help="write profiles/traffic_<op>.json from counter runs")
@@ -225,14 +228,30 @@ def main() -> int:
     dev = {n: to_device(inputs[n], torch) for n in layers}
     calls = {n: make_call(T, inputs[n].wl, dev[n], torch) for n in layers}
     stream = torch.cuda.current_stream()
+    # The TTT-MLP layer is one workgroup per (batch, head) chain: 48 chains hold 48 of the 256 CUs for
+    # its whole run and leave the rest idle. The layers share no data, so a step runs the MLP on a
+    # second stream (default priority) beside the other layers. Steps never overlap: each stream's
+    # work of a step starts only after the other stream has finished its work of the previous step.
+    side = torch.cuda.Stream() if "ttt_mlp_causal_8k" in layers and len(layers) > 1 and not args.serial else None
+    layer_stream = {n: (side if side is not None and n == "ttt_mlp_causal_8k" else stream) for n in layers}
+    order = sorted(layers, key=lambda n: layer_stream[n] is stream)  # the side-stream launch first
+    main_done, side_done = torch.cuda.Event(), torch.cuda.Event()
 
     def step(marks=None, layer=None):
-        for n in layers:
-            if marks is not None and n == layer:
-                marks[0].record(stream)
-            calls[n]()
-            if marks is not None and n == layer:
-                marks[1].record(stream)
+        if side is not None:
+            stream.wait_event(side_done)  # both as last recorded: the previous step's work on each stream
+            side.wait_event(main_done)
+        for n in order:
+            st = layer_stream[n]
+            with torch.cuda.stream(st):
+                if marks is not None and n == layer:
+                    marks[0].record(st)
+                calls[n]()
+                if marks is not None and n == layer:
+                    marks[1].record(st)
+        if side is not None:
+            side_done.record(side)
+            main_done.record(stream)
 
     for _ in range(args.warmup):
         step()
@@ -306,7 +325,8 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "ttt_layer_suite", "layers": layers, "tokens_per_step": tokens,
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU",
+                   "schedule": "serial" if side is None else "TTT-MLP on a second stream beside the other layers"},
         "roofline": roof,
         "per_layer": per_layer,
     }
