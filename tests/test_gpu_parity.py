@@ -366,6 +366,56 @@ def test_runs_on_a_side_stream():
     assert slice_err(host(out), oracle_full(x)[0]) <= BF16_TOL
 
 
+def test_layers_concurrent_on_two_streams_match_serial():
+    """The layer suite's schedule: TTT-MLP on a second stream while the three TTT-Linear layers run
+    on the main stream (each call with its own workspace). Outputs are bit-identical to the same
+    calls made one after another, and within the bar of the oracle."""
+    lib = T()
+    wls = [W["hvit3t_stage1_fullbatch"].with_(B=8, N=3136, seed=141),
+           W["vittt_bidir_1280"].with_(B=2, N=1600, seed=142),
+           W["ttt_linear_causal_16k"].with_(B=1, N=2048, H=4, seed=143),
+           W["ttt_mlp_causal_8k"].with_(B=1, N=1024, H=4, seed=144)]
+    xs = [synth.make_inputs(wl) for wl in wls]
+    calls = []
+    for wl, x in zip(wls, xs):
+        q, k, v = dev(x.q, "bf16"), dev(x.k, "bf16"), dev(x.v, "bf16")
+        op = {"fullbatch": lib.TTT_OP_FULLBATCH, "bidir": lib.TTT_OP_BIDIR, "causal": lib.TTT_OP_CAUSAL,
+              "mlp": lib.TTT_OP_MLP}[wl.op]
+        need = lib.ttt_workspace_size(op, lib.TTT_BF16, wl.B, wl.H, wl.N, wl.D, wl.Dh, wl.chunk)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+        o = torch.empty_like(q)
+        if wl.op == "mlp":
+            w1, w2 = torch.from_numpy(x.w1).cuda(), torch.from_numpy(x.w2).cuda()
+            calls.append(lambda q=q, k=k, v=v, w1=w1, w2=w2, o=o, ws=ws, wl=wl: lib.ttt_mlp_forward(
+                q, k, v, w1, w2, wl.chunk, wl.eta, o=o, workspace=ws))
+        else:
+            w0 = torch.from_numpy(x.w0).cuda()
+            fn = {"fullbatch": lambda q, k, v, w0, wl, **kw: lib.ttt_forward_fullbatch(q, k, v, w0, wl.eta, **kw),
+                  "bidir": lambda q, k, v, w0, wl, **kw: lib.ttt_forward_chunked_bidir(q, k, v, w0, wl.chunk,
+                                                                                      wl.eta, **kw),
+                  "causal": lambda q, k, v, w0, wl, **kw: lib.ttt_forward_chunked_causal(q, k, v, w0, wl.chunk,
+                                                                                        wl.eta, **kw)}[wl.op]
+            calls.append(lambda q=q, k=k, v=v, w0=w0, o=o, ws=ws, wl=wl, fn=fn: fn(q, k, v, w0, wl, o=o,
+                                                                                  workspace=ws))
+    serial = []
+    for c in calls:
+        serial.append(host(c()))
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+    for _ in range(2):
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            outs_mlp = calls[3]()
+        outs = [c() for c in calls[:3]]
+        main.wait_stream(side)
+        torch.cuda.synchronize()
+        for got, ref in zip([host(t) for t in outs] + [host(outs_mlp)], serial):
+            assert np.array_equal(got, ref)
+    for x, ref in zip(xs[:3], serial[:3]):
+        assert slice_err(ref, oracle_full(x)[0]) <= BF16_TOL
+
+
 @pytest.mark.parametrize("wl", [W["hvit3t_stage1_fullbatch"].with_(B=4, N=3136, seed=121),
                                 W["vit3s_fullbatch"].with_(B=3, N=196, H=6, seed=122),
                                 W["hvit3t_stage1_fullbatch"].with_(B=2, N=700, H=3, D=16, seed=123)],
