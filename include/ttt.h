@@ -15,7 +15,9 @@
  *   Inner states are always fp32, row-major, rows = input features: the linear model predicts
  *   k . W with W [D, D]; the MLP predicts GELU(k . W1) . W2 with W1 [D, Dh], W2 [Dh, D].
  *   An initial state pointer covers [H, ...] when its batch stride is 0 (one state shared by
- *   all batch elements) or [B, H, ...] when the stride is H * (elements of one head's state).
+ *   all batch elements) or [B, H, ...] when the stride (in elements) is at least
+ *   H * (elements of one head's state) and a multiple of 4, which keeps each batch element's
+ *   states 16-byte aligned.
  * Loss and step.  Per token l(W) = 1/2 ||f_W(k) - v||^2; a step over n tokens is
  *   W <- W - (eta/n) * sum of the n per-token gradients (gradient-descent update rule of the
  *   Vision-TTT summary on gist.science, "Methodologie" item 1; mini-batches of item 3).
@@ -29,7 +31,7 @@
  * Errors.  Every argument is validated before anything is enqueued; on error nothing is
  *   enqueued and no output is touched.
  *     TTT_ERR_INVALID      null pointer, non-positive size, N not a multiple of chunk,
- *                          misaligned pointer, overlapping output, non-finite eta
+ *                          misaligned pointer or batch stride, overlapping output, non-finite eta
  *     TTT_ERR_UNSUPPORTED  D not in {16, 32, 64}; chunk not in {16, 32, 64};
  *                          TTT-MLP with (D, Dh) other than (64, 256); TTT-MLP with fp32 I/O
  *     TTT_ERR_WORKSPACE    workspace_bytes < ttt_workspace_size(...)
@@ -43,7 +45,9 @@
  *   accumulator in fp32, and feeds 16-bit operands to the matrix cores: bf16, except in
  *   ttt_mlp_forward's products on the W2 side (hidden activations, W2, residuals), which take
  *   fp16 operands (more mantissa bits; those values stay far inside fp16's range).
- * Threads.  Entry points are reentrant and keep no global state.
+ * Threads.  Entry points are reentrant. The only state kept between calls is a per-device cache
+ *   of kernel occupancy figures (the chunked scans size their segment plan from it), filled on a
+ *   device's first call through atomics.
  */
 #ifndef TTT_H_
 #define TTT_H_
@@ -114,7 +118,8 @@ ttt_status ttt_forward_chunked_bidir(ttt_dtype dt, int B, int H, int N, int D, i
  * state (W1_s, W2_s): token i is read out with (W1_s, W2_s) - (eta/b) * sum_{j <= i in c} of the
  * per-token gradients at the start state; the chunk hands on the state after all b gradients.
  * w1_0: fp32 [H, D, Dh] (stride 0) or [B, H, D, Dh]; w2_0: fp32 [H, Dh, D] or [B, H, Dh, D];
- * w_batch_stride applies to both in units of one head's W1 (D*Dh == Dh*D) elements times H.
+ * w_batch_stride: elements between consecutive batch elements' states, 0 or at least H*D*Dh (a
+ * multiple of 4); it applies to both w1_0 and w2_0, which hold D*Dh elements per head.
  * w1_out / w2_out (nullable): fp32 [B, H, D, Dh] / [B, H, Dh, D] end states.
  */
 ttt_status ttt_mlp_forward(ttt_dtype dt, int B, int H, int N, int D, int Dh, int chunk, float eta,

@@ -52,7 +52,9 @@ ttt_status check_linear(ttt_op op, ttt_dtype dt, int B, int H, int N, int D, int
   }
   if ((long long)B * H > 65535) return TTT_ERR_UNSUPPORTED;
   const long long head = (long long)H * D * D;
-  if (w0s != 0 && w0s < head) return TTT_ERR_INVALID;
+  // A per-batch stride keeps every batch element's states 16-byte aligned, as the kernels' vector
+  // loads of them require.
+  if (w0s != 0 && (w0s < head || w0s % 4 != 0)) return TTT_ERR_INVALID;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(w0))
     return TTT_ERR_INVALID;
   if (w_out && !aligned16(w_out)) return TTT_ERR_INVALID;
@@ -165,7 +167,7 @@ ttt_status ttt_mlp_forward(ttt_dtype dt, int B, int H, int N, int D, int Dh, int
   if (dt != TTT_BF16 || D != 64 || Dh != 256 || chunk != 16) return TTT_ERR_UNSUPPORTED;
   if (N % chunk != 0) return TTT_ERR_INVALID;
   const long long head = (long long)H * D * Dh;
-  if (w_batch_stride != 0 && w_batch_stride < head) return TTT_ERR_INVALID;
+  if (w_batch_stride != 0 && (w_batch_stride < head || w_batch_stride % 4 != 0)) return TTT_ERR_INVALID;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(w1_0) ||
       !aligned16(w2_0))
     return TTT_ERR_INVALID;

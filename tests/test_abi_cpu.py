@@ -90,6 +90,7 @@ def _fullbatch(dt=T.TTT_BF16, B=1, H=1, N=64, D=64, eta=1.0, q=0, k=1, v=2, w0=3
     (dict(ws=None), 3),          # workspace needed but missing
     (dict(ws_bytes=16), 3),      # workspace too small
     (dict(w0s=7), 1),            # batch stride smaller than one batch of states
+    (dict(B=2, w0s=64 * 64 + 2), 1),  # batch stride that misaligns the second batch's states
 ])
 def test_fullbatch_validation_rejects_before_launch(kw, expect):
     assert _fullbatch(**kw) == expect
@@ -123,8 +124,8 @@ def test_chunked_validation(fn):
 
 def test_mlp_validation():
     lib = T.load_library()
-    call = lambda dt=T.TTT_BF16, D=64, Dh=256, chunk=16, N=64, o=4: lib.ttt_mlp_forward(  # noqa: E731
-        dt, 1, 1, N, D, Dh, chunk, 1.0, _p(0), _p(1), _p(2), _p(3), _p(6), 0,
+    call = lambda dt=T.TTT_BF16, D=64, Dh=256, chunk=16, N=64, o=4, wbs=0: lib.ttt_mlp_forward(  # noqa: E731
+        dt, 2, 1, N, D, Dh, chunk, 1.0, _p(0), _p(1), _p(2), _p(3), _p(6), wbs,
         None if o is None else _p(o), None, None, None, 0, None)
     assert call(o=None) == 1
     assert call(dt=T.TTT_F32) == 2
@@ -133,6 +134,8 @@ def test_mlp_validation():
     assert call(chunk=32) == 2
     assert call(N=40) == 1
     assert call(o=0) == 1                 # output aliases q
+    assert call(wbs=100) == 1             # batch stride below one batch of states
+    assert call(wbs=64 * 256 + 2) == 1    # batch stride that misaligns the second batch's states
 
 
 def test_binding_fails_loudly_without_gpu_tensors():
