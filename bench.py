@@ -235,11 +235,12 @@ def main() -> int:
     side = torch.cuda.Stream() if "ttt_mlp_causal_8k" in layers and len(layers) > 1 and not args.serial else None
     layer_stream = {n: (side if side is not None and n == "ttt_mlp_causal_8k" else stream) for n in layers}
     order = sorted(layers, key=lambda n: layer_stream[n] is stream)  # the side-stream launch first
-    main_done, side_done = torch.cuda.Event(), torch.cuda.Event()
+    main_done = torch.cuda.Event()
+    side_done = [torch.cuda.Event()]  # the side stream's last recorded event
 
     def step(marks=None, layer=None):
         if side is not None:
-            stream.wait_event(side_done)  # both as last recorded: the previous step's work on each stream
+            stream.wait_event(side_done[0])  # both as last recorded: the previous step's work on each stream
             side.wait_event(main_done)
         for n in order:
             st = layer_stream[n]
@@ -250,7 +251,11 @@ def main() -> int:
                 if marks is not None and n == layer:
                     marks[1].record(st)
         if side is not None:
-            side_done.record(side)
+            if marks is not None and layer_stream[layer] is side:
+                side_done[0] = marks[1]  # the timing event after the side stream's layer also marks its end
+            else:
+                side_done[0] = torch.cuda.Event()
+                side_done[0].record(side)
             main_done.record(stream)
 
     for _ in range(args.warmup):
