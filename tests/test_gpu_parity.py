@@ -201,13 +201,13 @@ def test_end_states(wl):
 # Full-batch split plans: one group with many splits, waves sharing a (head, row block) task when
 # a group has fewer than four, splits longer than the register sets (which refill them).
 FB_PLANS = [
-    W["hvit3t_stage1_fullbatch"].with_(B=1, N=2597, seed=71),           # one group, 41 splits
-    W["vit3s_fullbatch"].with_(B=1, N=5000, H=1, seed=72),              # D = 64, 79 splits
+    W["hvit3t_stage1_fullbatch"].with_(B=1, N=2597, seed=71),           # one group, 14 splits of 3 tiles
+    W["vit3s_fullbatch"].with_(B=1, N=5000, H=1, seed=72),              # D = 64, 16 splits of 5 tiles
     W["hvit3t_stage1_fullbatch"].with_(B=2, N=700, H=3, seed=73),       # one head per group: 2 waves per task
     W["hvit3t_stage1_fullbatch"].with_(B=1, N=900, H=1, D=16, seed=74), # one 16-wide head: 4 waves per task
     W["hvit3t_stage1_fullbatch"].with_(B=2, N=300, H=4, D=16, seed=75), # four heads per 128-byte row
     W["vit3s_fullbatch"].with_(B=100, N=600, seed=76),                  # D = 64 splits of 4 tiles, 2 sets
-    W["hvit3t_stage1_fullbatch"].with_(B=1, N=262144, seed=77),         # split cap (256): 16 tiles a split
+    W["hvit3t_stage1_fullbatch"].with_(B=1, N=262144, seed=77),         # split cap (16): 256 tiles a split
     W["vit3s_fullbatch"].with_(B=1, N=100000, H=1, seed=78),            # D = 64 at the split cap
 ]
 
