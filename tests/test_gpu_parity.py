@@ -112,6 +112,9 @@ SMALL = [
     W["ttt_linear_causal_16k"].with_(B=1, N=128, H=2, D=32, chunk=16, dtype="fp32", seed=45),
     W["ttt_mlp_causal_8k"].with_(B=1, N=128, H=2, seed=51),
     W["ttt_mlp_causal_8k"].with_(B=2, N=16, H=1, seed=52),
+    # odd chunk counts: the two-step loop body runs and the last step is peeled
+    W["ttt_mlp_causal_8k"].with_(B=1, N=48, H=2, seed=53),
+    W["ttt_mlp_causal_8k"].with_(B=1, N=80, H=3, seed=54),
 ]
 
 # Chunked cases long enough to be split into several segments (compose + prefix + rescan),
