@@ -30,11 +30,14 @@ if ROOT not in sys.path:
 SUITE = ["hvit3t_stage1_fullbatch", "vittt_bidir_1280", "ttt_linear_causal_16k", "ttt_mlp_causal_8k"]
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, TFLOP/s
-KERNEL_SOURCES = {              # kernel sources of each layer (for the traffic-counter freshness check)
-    "fullbatch": ["test_sequence_layers_amd/csrc/fullbatch.hip", "test_sequence_layers_amd/csrc/device.hpp"],
-    "bidir": ["test_sequence_layers_amd/csrc/chunked.hip", "test_sequence_layers_amd/csrc/device.hpp"],
-    "causal": ["test_sequence_layers_amd/csrc/chunked.hip", "test_sequence_layers_amd/csrc/device.hpp"],
-    "mlp": ["test_sequence_layers_amd/csrc/mlp.hip", "test_sequence_layers_amd/csrc/device.hpp"],
+# Kernel sources and the build script (compiler flags) of each layer, for the traffic-counter
+# freshness check: a change to any of them makes the stored counters stale.
+_BUILD = "test_sequence_layers_amd/build.py"
+KERNEL_SOURCES = {
+    "fullbatch": ["test_sequence_layers_amd/csrc/fullbatch.hip", "test_sequence_layers_amd/csrc/device.hpp", _BUILD],
+    "bidir": ["test_sequence_layers_amd/csrc/chunked.hip", "test_sequence_layers_amd/csrc/device.hpp", _BUILD],
+    "causal": ["test_sequence_layers_amd/csrc/chunked.hip", "test_sequence_layers_amd/csrc/device.hpp", _BUILD],
+    "mlp": ["test_sequence_layers_amd/csrc/mlp.hip", "test_sequence_layers_amd/csrc/device.hpp", _BUILD],
 }
 
 
