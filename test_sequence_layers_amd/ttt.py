@@ -66,6 +66,9 @@ def ttt_workspace_size(op: int, dtype: int, B: int, H: int, N: int, D: int, Dh: 
 
 
 # ------------------------------------------------------------------------------------ helpers
+# The binding is the only layer that sees tensor shapes: it checks every tensor against the layout
+# the C ABI assumes (include/ttt.h) before calling it, so that a wrongly shaped output or state can
+# never make a kernel write past its buffer. Everything below is argument marshalling only.
 def _torch():
     import torch  # imported lazily so that the CPU-only checks need no GPU
 
@@ -85,41 +88,64 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _stream(stream):
+def _stream(stream, device):
     torch = _torch()
-    s = torch.cuda.current_stream() if stream is None else stream
+    s = torch.cuda.current_stream(device) if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check_tensor(name, t, shape, dtype, device):
+    """t must be a contiguous device tensor of exactly this shape and dtype, on `device`."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, q on {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must have dtype {dtype}, not {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
 
 
 def _check_io(q, k, v):
     torch = _torch()
+    if not isinstance(q, torch.Tensor) or not q.is_cuda:
+        raise TypeError("q must be a CUDA (HIP) tensor")
+    if q.dim() != 4:
+        raise ValueError("q must be [B, N, H, D]")
+    _dtype_code(q)
     for name, t in (("q", q), ("k", k), ("v", v)):
-        if not isinstance(t, torch.Tensor) or not t.is_cuda:
-            raise TypeError(f"{name} must be a CUDA (HIP) tensor")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous [B, N, H, D]")
-        if t.dim() != 4 or t.shape != q.shape or t.dtype != q.dtype:
-            raise ValueError(f"{name} must match q's shape [B, N, H, D] and dtype")
+        _check_tensor(name, t, q.shape, q.dtype, q.device)
 
 
-def _state_stride(w, B: int, H: int, per_head: int) -> int:
+def _state_stride(name, w, B: int, H: int, rows: int, cols: int, device) -> int:
+    """Batch stride (elements) of an initial state [H, rows, cols] (shared, stride 0) or
+    [B, H, rows, cols] (one per batch element)."""
     torch = _torch()
-    if w.dtype != torch.float32 or not w.is_cuda or not w.is_contiguous():
-        raise ValueError("inner states must be contiguous fp32 device tensors")
-    if w.dim() == 3:
-        if w.shape[0] != H:
-            raise ValueError("state of shape [H, ...] expected")
+    if isinstance(w, torch.Tensor) and w.dim() == 3:
+        _check_tensor(name, w, (H, rows, cols), torch.float32, device)
         return 0
-    if w.dim() == 4 and w.shape[0] == B and w.shape[1] == H:
-        return H * per_head
-    raise ValueError("state must be [H, r, c] or [B, H, r, c]")
+    _check_tensor(name, w, (B, H, rows, cols), torch.float32, device)
+    return H * rows * cols
 
 
-def _workspace(op, dt, B, H, N, D, Dh, chunk, workspace):
+def _check_out(name, t, shape, dtype, device):
+    if t is not None:
+        _check_tensor(name, t, shape, dtype, device)
+
+
+def _workspace(op, dt, B, H, N, D, Dh, chunk, workspace, device):
     torch = _torch()
     need = ttt_workspace_size(op, dt, B, H, N, D, Dh, chunk)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device="cuda")
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    if workspace is not None:
+        if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda or workspace.device != device:
+            raise ValueError(f"workspace must be a device tensor on {device}")
+        if not workspace.is_contiguous():
+            raise ValueError("workspace must be contiguous")
     size = 0 if workspace is None else workspace.numel() * workspace.element_size()
     return workspace, size
 
@@ -129,69 +155,76 @@ def _raise(status, where):
         raise TTTError(status, where)
 
 
-# ------------------------------------------------------------------------------- entry points
-def ttt_forward_fullbatch(q, k, v, w0, eta: float = 1.0, *, o=None, w_out=None, workspace=None, stream=None):
-    """O = Q W*, W* = W0 - (eta/N) K^T (K W0 - V) per (b, h). Returns o."""
+def _linear(op, fn_name, q, k, v, w0, chunk, eta, o, w_out, workspace, stream):
     lib = load_library()
     _check_io(q, k, v)
+    torch = _torch()
     B, N, H, D = q.shape
+    dev = q.device
     dt = _dtype_code(q)
-    stride = _state_stride(w0, B, H, D * D)
-    o = _torch().empty_like(q) if o is None else o
-    ws, ws_size = _workspace(TTT_OP_FULLBATCH, dt, B, H, N, D, 0, 0, workspace)
-    st = lib.ttt_forward_fullbatch(dt, B, H, N, D, float(eta), _ptr(q), _ptr(k), _ptr(v), _ptr(w0), stride,
-                                   _ptr(o), _ptr(w_out), _ptr(ws), ws_size, _stream(stream))
-    _raise(st, "ttt_forward_fullbatch")
+    stride = _state_stride("w0", w0, B, H, D, D, dev)
+    _check_out("o", o, q.shape, q.dtype, dev)
+    _check_out("w_out", w_out, ((2,) if op == TTT_OP_BIDIR else ()) + (B, H, D, D), torch.float32, dev)
+    with torch.cuda.device(dev):
+        o = torch.empty_like(q) if o is None else o
+        ws, ws_size = _workspace(op, dt, B, H, N, D, 0, chunk, workspace, dev)
+        args = [dt, B, H, N, D] + ([] if op == TTT_OP_FULLBATCH else [int(chunk)])
+        st = getattr(lib, fn_name)(*args, float(eta), _ptr(q), _ptr(k), _ptr(v), _ptr(w0), stride, _ptr(o),
+                                   _ptr(w_out), _ptr(ws), ws_size, _stream(stream, dev))
+    _raise(st, fn_name)
     return o
+
+
+# ------------------------------------------------------------------------------- entry points
+def ttt_forward_fullbatch(q, k, v, w0, eta: float = 1.0, *, o=None, w_out=None, workspace=None, stream=None):
+    """O = Q W*, W* = W0 - (eta/N) K^T (K W0 - V) per (b, h). Returns o.
+
+    q, k, v, o: [B, N, H, D] bf16 or fp32; w0: fp32 [H, D, D] or [B, H, D, D]; w_out: fp32 [B, H, D, D]."""
+    return _linear(TTT_OP_FULLBATCH, "ttt_forward_fullbatch", q, k, v, w0, 0, eta, o, w_out, workspace, stream)
 
 
 def ttt_forward_chunked_causal(q, k, v, w0, chunk: int, eta: float = 1.0, *, o=None, w_out=None, workspace=None,
                                stream=None):
-    """Causal mini-batch TTT-Linear. Returns o."""
-    lib = load_library()
-    _check_io(q, k, v)
-    B, N, H, D = q.shape
-    dt = _dtype_code(q)
-    stride = _state_stride(w0, B, H, D * D)
-    o = _torch().empty_like(q) if o is None else o
-    ws, ws_size = _workspace(TTT_OP_CAUSAL, dt, B, H, N, D, 0, chunk, workspace)
-    st = lib.ttt_forward_chunked_causal(dt, B, H, N, D, int(chunk), float(eta), _ptr(q), _ptr(k), _ptr(v),
-                                        _ptr(w0), stride, _ptr(o), _ptr(w_out), _ptr(ws), ws_size, _stream(stream))
-    _raise(st, "ttt_forward_chunked_causal")
-    return o
+    """Causal mini-batch TTT-Linear. Returns o. w_out: fp32 [B, H, D, D] end state."""
+    return _linear(TTT_OP_CAUSAL, "ttt_forward_chunked_causal", q, k, v, w0, chunk, eta, o, w_out, workspace,
+                   stream)
 
 
 def ttt_forward_chunked_bidir(q, k, v, w0, chunk: int, eta: float = 1.0, *, o=None, w_out=None, workspace=None,
                               stream=None):
-    """Bidirectional chunked scan (forward + reversed-sequence scans, summed). Returns o."""
-    lib = load_library()
-    _check_io(q, k, v)
-    B, N, H, D = q.shape
-    dt = _dtype_code(q)
-    stride = _state_stride(w0, B, H, D * D)
-    o = _torch().empty_like(q) if o is None else o
-    ws, ws_size = _workspace(TTT_OP_BIDIR, dt, B, H, N, D, 0, chunk, workspace)
-    st = lib.ttt_forward_chunked_bidir(dt, B, H, N, D, int(chunk), float(eta), _ptr(q), _ptr(k), _ptr(v),
-                                       _ptr(w0), stride, _ptr(o), _ptr(w_out), _ptr(ws), ws_size, _stream(stream))
-    _raise(st, "ttt_forward_chunked_bidir")
-    return o
+    """Bidirectional chunked scan (forward + reversed-sequence scans, summed). Returns o.
+    w_out: fp32 [2, B, H, D, D] (forward end state, reverse end state)."""
+    return _linear(TTT_OP_BIDIR, "ttt_forward_chunked_bidir", q, k, v, w0, chunk, eta, o, w_out, workspace,
+                   stream)
 
 
 def ttt_mlp_forward(q, k, v, w1, w2, chunk: int, eta: float = 1.0, *, o=None, w1_out=None, w2_out=None,
                     workspace=None, stream=None):
-    """Causal mini-batch TTT-MLP, f(x) = GELU(x W1) W2. Returns o."""
+    """Causal mini-batch TTT-MLP, f(x) = GELU(x W1) W2. Returns o.
+
+    w1: fp32 [H, D, Dh] or [B, H, D, Dh]; w2: fp32 [H, Dh, D] or [B, H, Dh, D] (batched like w1);
+    w1_out / w2_out: fp32 [B, H, D, Dh] / [B, H, Dh, D] end states."""
     lib = load_library()
     _check_io(q, k, v)
+    torch = _torch()
     B, N, H, D = q.shape
+    dev = q.device
     dt = _dtype_code(q)
-    Dh = w1.shape[-1]
-    stride = _state_stride(w1, B, H, D * Dh)
-    if _state_stride(w2, B, H, D * Dh) != stride:
+    if not isinstance(w1, torch.Tensor) or w1.dim() not in (3, 4):
+        raise ValueError("w1 must be [H, D, Dh] or [B, H, D, Dh]")
+    Dh = int(w1.shape[-1])
+    stride = _state_stride("w1", w1, B, H, D, Dh, dev)
+    if w2.dim() != w1.dim():
         raise ValueError("w1 and w2 must both be shared over the batch or both per batch element")
-    o = _torch().empty_like(q) if o is None else o
-    ws, ws_size = _workspace(TTT_OP_MLP, dt, B, H, N, D, Dh, chunk, workspace)
-    st = lib.ttt_mlp_forward(dt, B, H, N, D, Dh, int(chunk), float(eta), _ptr(q), _ptr(k), _ptr(v), _ptr(w1),
-                             _ptr(w2), stride, _ptr(o), _ptr(w1_out), _ptr(w2_out), _ptr(ws), ws_size,
-                             _stream(stream))
+    _state_stride("w2", w2, B, H, Dh, D, dev)
+    _check_out("o", o, q.shape, q.dtype, dev)
+    _check_out("w1_out", w1_out, (B, H, D, Dh), torch.float32, dev)
+    _check_out("w2_out", w2_out, (B, H, Dh, D), torch.float32, dev)
+    with torch.cuda.device(dev):
+        o = torch.empty_like(q) if o is None else o
+        ws, ws_size = _workspace(TTT_OP_MLP, dt, B, H, N, D, Dh, chunk, workspace, dev)
+        st = lib.ttt_mlp_forward(dt, B, H, N, D, Dh, int(chunk), float(eta), _ptr(q), _ptr(k), _ptr(v), _ptr(w1),
+                                 _ptr(w2), stride, _ptr(o), _ptr(w1_out), _ptr(w2_out), _ptr(ws), ws_size,
+                                 _stream(stream, dev))
     _raise(st, "ttt_mlp_forward")
     return o

@@ -143,3 +143,84 @@ def test_binding_fails_loudly_without_gpu_tensors():
     x = torch.zeros(1, 16, 1, 16)
     with pytest.raises(TypeError):
         T.ttt_forward_fullbatch(x, x, x, torch.zeros(1, 16, 16))
+
+
+# ------------------------------------------------------------------ binding checks (no launch)
+# The Python binding checks every tensor against the layout the C ABI assumes before it calls the
+# library. These run on CPU with fake CUDA tensors (shape, dtype and device only, no storage); the
+# library handle is replaced by one that fails the test if any entry point is reached.
+class _NoCalls:
+    def __getattr__(self, name):
+        raise AssertionError(f"the binding reached the library ({name}) with invalid arguments")
+
+
+@pytest.fixture
+def fake_cuda(monkeypatch):
+    torch = pytest.importorskip("torch")
+    from torch._subclasses.fake_tensor import FakeTensorMode
+
+    monkeypatch.setattr(binding, "_lib", _NoCalls())
+    mode = FakeTensorMode()
+
+    def make(*shape, dtype=torch.bfloat16):
+        with mode:
+            return torch.empty(*shape, dtype=dtype, device="cuda")
+
+    return torch, make
+
+
+def _linear_cases(torch, make):
+    B, N, H, D = 2, 64, 3, 32
+    q = make(B, N, H, D)
+    w0 = make(H, D, D, dtype=torch.float32)
+    f32 = torch.float32
+    return q, w0, [
+        ("o wrong shape", dict(o=make(B, N, H, 16))),
+        ("o wrong dtype", dict(o=make(B, N, H, D, dtype=f32))),
+        ("w_out wrong shape", dict(w_out=make(B, H, D, 16, dtype=f32))),
+        ("w_out wrong dtype", dict(w_out=make(B, H, D, D))),
+        ("w_out of one direction only (bidir needs two)", dict(w_out=make(B, H, D, D, dtype=f32), bidir_only=True)),
+        ("w0 wrong trailing dims", dict(w0=make(H, D, 16, dtype=f32))),
+        ("w0 wrong dtype", dict(w0=make(H, D, D))),
+        ("w0 wrong batch", dict(w0=make(B + 1, H, D, D, dtype=f32))),
+        ("k wrong shape", dict(k=make(B, N, H, 16))),
+        ("v wrong dtype", dict(v=make(B, N, H, D, dtype=f32))),
+        ("o transposed view", dict(o=make(B, H, N, D).transpose(1, 2))),
+    ]
+
+
+@pytest.mark.parametrize("fn", ["ttt_forward_fullbatch", "ttt_forward_chunked_causal", "ttt_forward_chunked_bidir"])
+def test_binding_rejects_bad_tensors_before_launch(fake_cuda, fn):
+    torch, make = fake_cuda
+    q, w0, cases = _linear_cases(torch, make)
+    f = getattr(T, fn)
+    for what, kw in cases:
+        if kw.pop("bidir_only", False) and fn != "ttt_forward_chunked_bidir":
+            continue
+        args = dict(q=q, k=kw.pop("k", q), v=kw.pop("v", q), w0=kw.pop("w0", w0))
+        call = (lambda: f(args["q"], args["k"], args["v"], args["w0"], 1.0, **kw)) if fn == "ttt_forward_fullbatch" \
+            else (lambda: f(args["q"], args["k"], args["v"], args["w0"], 16, 1.0, **kw))
+        with pytest.raises((ValueError, TypeError)):
+            call()
+        print("rejected:", what)
+
+
+def test_binding_rejects_bad_mlp_tensors_before_launch(fake_cuda):
+    torch, make = fake_cuda
+    f32 = torch.float32
+    B, N, H, D, Dh = 2, 64, 3, 64, 256
+    q = make(B, N, H, D)
+    w1, w2 = make(H, D, Dh, dtype=f32), make(H, Dh, D, dtype=f32)
+    cases = [
+        dict(w1=make(H, D, 128, dtype=f32)),                      # hidden widths disagree with w2
+        dict(w2=make(H, D, Dh, dtype=f32)),                       # w2 transposed
+        dict(w2=make(B, H, Dh, D, dtype=f32)),                    # batched w2 with shared w1
+        dict(o=make(B, N, H, 32)),
+        dict(w1_out=make(B, H, Dh, D, dtype=f32)),
+        dict(w2_out=make(H, Dh, D, dtype=f32)),
+        dict(w2_out=make(B, H, Dh, D)),
+    ]
+    for kw in cases:
+        a1, a2 = kw.pop("w1", w1), kw.pop("w2", w2)
+        with pytest.raises((ValueError, TypeError)):
+            T.ttt_mlp_forward(q, q, q, a1, a2, 16, 1.0, **kw)
