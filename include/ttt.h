@@ -44,7 +44,8 @@
  *   TTT_BF16 reads and writes bf16 (round-to-nearest-even on output), keeps the state and every
  *   accumulator in fp32, and feeds 16-bit operands to the matrix cores: bf16, except in
  *   ttt_mlp_forward's products on the W2 side (hidden activations, W2, residuals), which take
- *   fp16 operands (more mantissa bits; those values stay far inside fp16's range).
+ *   fp16 operands (more mantissa bits) while the values converted stay inside the ranges that
+ *   ttt_mlp_forward states; chains whose values leave them are recomputed with bf16 operands.
  * Threads.  Entry points are reentrant. The only state kept between calls is a per-device cache
  *   of kernel occupancy figures (the chunked scans size their segment plan from it), filled on a
  *   device's first call through atomics.
@@ -121,6 +122,13 @@ ttt_status ttt_forward_chunked_bidir(ttt_dtype dt, int B, int H, int N, int D, i
  * w_batch_stride: elements between consecutive batch elements' states, 0 or at least H*D*Dh (a
  * multiple of 4); it applies to both w1_0 and w2_0, which hold D*Dh elements per head.
  * w1_out / w2_out (nullable): fp32 [B, H, D, Dh] / [B, H, Dh, D] end states.
+ * Operand ranges (bf16 I/O): the products on the W2 side take fp16 operands while, per wave and
+ * chunk, the largest |hidden pre-activation| is in [2^-10, sqrt 2] (else the GELU outputs must
+ * stay within 32 in magnitude), the largest |(eta/b) residual| is at most 2^15 and the W2
+ * state's largest magnitude (checked every 32 chunks) is in [2^-10, 2^15], all-zero values being
+ * exact. A (batch, head) chain that leaves these ranges is recomputed by a second kernel with bf16
+ * operands (fp32's exponent range); the workspace then holds, as its first B*H ints, 1 for each
+ * recomputed chain and 0 for the others.
  */
 ttt_status ttt_mlp_forward(ttt_dtype dt, int B, int H, int N, int D, int Dh, int chunk, float eta,
                            const void* q, const void* k, const void* v,

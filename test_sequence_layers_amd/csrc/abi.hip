@@ -3,6 +3,7 @@
 #include <math.h>
 #include <stdint.h>
 
+
 #include "../../include/ttt.h"
 #include "internal.hpp"
 
@@ -35,11 +36,12 @@ size_t state_bytes(int B, int H, size_t per_head, long long stride) {
   return ((size_t)(B - 1) * (size_t)stride + one) * sizeof(float);
 }
 
-// Common validation of the TTT-Linear entry points. Returns TTT_OK or the first failure.
+// Common validation of the TTT-Linear entry points. Returns TTT_OK or the first failure. With
+// check_ws false the workspace arguments are ignored (the caller supplies scratch of its own).
 ttt_status check_linear(ttt_op op, ttt_dtype dt, int B, int H, int N, int D, int chunk,
                         float eta, const void* q, const void* k, const void* v, const float* w0,
                         long long w0s, const void* o, const float* w_out, const void* ws,
-                        size_t ws_bytes) {
+                        size_t ws_bytes, bool check_ws = true) {
   if (dt != TTT_F32 && dt != TTT_BF16) return TTT_ERR_INVALID;
   if (B <= 0 || H <= 0 || N <= 0 || D <= 0) return TTT_ERR_INVALID;
   if (!isfinite(eta)) return TTT_ERR_INVALID;
@@ -71,7 +73,7 @@ ttt_status check_linear(ttt_op op, ttt_dtype dt, int B, int H, int N, int D, int
       return TTT_ERR_INVALID;
   }
   const size_t need = ttt_workspace_size(op, dt, B, H, N, D, 0, chunk);
-  if (need > 0) {
+  if (check_ws && need > 0) {
     if (!ws || ws_bytes < need) return TTT_ERR_WORKSPACE;
     if (!aligned16(ws)) return TTT_ERR_INVALID;
     const Range rws = range_of(ws, need);
@@ -190,7 +192,14 @@ ttt_status ttt_mlp_forward(ttt_dtype dt, int B, int H, int N, int D, int Dh, int
   }
   if (w1_out && w2_out && overlaps(outs[0], outs[1])) return TTT_ERR_INVALID;
   const size_t need = ttt_workspace_size(TTT_OP_MLP, dt, B, H, N, D, Dh, chunk);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return TTT_ERR_WORKSPACE;
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return TTT_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return TTT_ERR_INVALID;
+    const Range rws = range_of(workspace, need);
+    if (overlaps(rws, rq) || overlaps(rws, rk) || overlaps(rws, rv) || overlaps(rws, ro) ||
+        overlaps(rws, r1) || overlaps(rws, r2) || overlaps(rws, outs[0]) || overlaps(rws, outs[1]))
+      return TTT_ERR_INVALID;
+  }
   return from_hip(ttt::mlp_launch(B, H, N, D, Dh, chunk, eta, q, k, v, w1_0, w2_0,
                                   w_batch_stride, o, w1_out, w2_out, workspace,
                                   static_cast<hipStream_t>(stream)));

@@ -24,11 +24,26 @@
 // so results are deterministic. The steps between the first and the last have both a read-out
 // and a forward, known at compile time, so that their products and GELUs share basic blocks and
 // interleave. E is kept as -a E (a = eta / b), so that -a D1 and the weight updates' operands come
-// out of the products with the right sign (no separate negations). Operand precision: the
-// products on the W1 side (inputs K, Q and D1) take bf16 operands, those on the W2 side (X2, W2,
-// E, X2 X2^T) fp16 ones, which the packed fp16 GELU path produces directly; all accumulate in fp32. Two workgroup barriers per
+// out of the products with the right sign (no separate negations). Two workgroup barriers per
 // chunk; K, V, Q are staged through a four-deep LDS ring: each chunk's global loads are issued
 // three chunks ahead into one of two alternating register sets and stored to LDS two chunks ahead.
+//
+// Operand precision. The products on the W1 side (inputs K, Q and D1) take bf16 operands. Those
+// on the W2 side (X2, X2q, W2, E and X2q X2^T) take fp16 operands in the first launch: three more
+// mantissa bits than bf16, and the packed fp16 GELU path produces them directly. fp16 covers
+// magnitudes 2^-14 .. 65504 at full precision, so that launch checks, per wave and step, the
+// values it converts: the hidden pre-activations (largest magnitude in [2^-10, sqrt 2] for the
+// polynomial GELU, GELU outputs at most 32 in magnitude otherwise, so that the 32-unit sums of
+// X2q X2^T stay below 32768), the -a E tiles (largest magnitude at most 2^15) and, every 32
+// chunks, the W2 slice (largest magnitude in [2^-10, 2^15]); all-zero tiles are exact. -a E has no
+// lower bound: it only enters as a correction added to a term without it (the W2 update to W2,
+// the read-out's correction to X2q W2, through D1 the W1 update to W1), so its rounding error below
+// fp16's normal range (at most 2^-25 a value) stays negligible beside them when a = eta / b is
+// small, and inputs or weights small enough to make those terms small too fail the other checks.
+// A (batch,
+// head) chain that fails any check is flagged in the workspace, and a second launch recomputes
+// exactly the flagged chains with bf16 operands on the W2 side (bf16 has fp32's exponent range)
+// and the fp32 GELU; every other chain returns at once. All products accumulate in fp32.
 //
 // No 16x16x16 product accumulates onto the result of a 16x16x32 product: on gfx950 such a
 // mixed-shape accumulator chain was measured to read a stale accumulator (wrong results that
@@ -61,8 +76,8 @@ constexpr float kLog2InvSqrt2Pi = -1.32574806473615935f;   // log2(1 / sqrt(2 pi
 
 // GELU(x) = x Phi(x) with Phi(x) = (1 + erf(x / sqrt 2)) / 2 (exact erf form) and
 // GELU'(x) = Phi(x) + x phi(x), phi the standard normal density.
-// Fast path, used when every argument of the wave's GELUs in a chunk step has x^2 <= 2
-// (|x / sqrt 2| <= 1): erf(u) = u P(u^2)
+// Fast path, used when every argument of the wave's GELUs in a chunk step has |x| <= sqrt 2
+// (rounded down to fp16, so x^2 <= 2 and |x / sqrt 2| <= 1): erf(u) = u P(u^2)
 // with P the degree-3 least-squares polynomial for erf(u)/u on u^2 in [0, 1] (fitted on Chebyshev
 // nodes; max abs error of erf 2.7e-5 in fp32 Horner form), so Phi(x) = 1/2 + x R(x^2) with
 // R(t) = P(t / 2) / (2 sqrt 2). It runs in packed fp16 (below); its GELU and GELU' stay within
@@ -70,15 +85,10 @@ constexpr float kLog2InvSqrt2Pi = -1.32574806473615935f;   // log2(1 / sqrt(2 pi
 // library erf and exp2.
 constexpr float kErfP[4] = {1.128350616f, -0.3751908541f, 0.1079747304f, -0.0184600465f};
 constexpr float kInvTwoSqrt2 = 0.35355339059327376220f;
+constexpr float kSqrt2h = 1.4140625f;  // sqrt 2 rounded down to fp16: the fast path's bound on |x|
 constexpr float kR0 = kErfP[0] * kInvTwoSqrt2, kR1 = kErfP[1] * kInvTwoSqrt2 / 2.f,
                 kR2 = kErfP[2] * kInvTwoSqrt2 / 4.f, kR3 = kErfP[3] * kInvTwoSqrt2 / 8.f;
 
-__device__ __forceinline__ float cdf_fast(float x, float t) {  // t = x * x <= 2
-  float r = fmaf(kR3, t, kR2);
-  r = fmaf(r, t, kR1);
-  r = fmaf(r, t, kR0);
-  return fmaf(x, r, 0.5f);
-}
 __device__ __forceinline__ float cdf_lib(float x) { return 0.5f * (1.f + erff(x * kInvSqrt2)); }
 
 __device__ __forceinline__ bf16x8 cat_tiles(f32x4 lo, f32x4 hi) {
@@ -87,7 +97,8 @@ __device__ __forceinline__ bf16x8 cat_tiles(f32x4 lo, f32x4 hi) {
 
 // fp16 operands for the products on the W2 side (X2, W2, E and the X2 X2^T terms): three more
 // mantissa bits than bf16, and the packed fp16 arithmetic of the fast GELU path yields them
-// directly (no conversions). Their range (|x| < 65504) is far above these activations.
+// directly (no conversions). The kernel checks that the values it converts stay inside fp16's
+// range (header comment).
 typedef _Float16 f16;
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
@@ -116,6 +127,45 @@ __device__ __forceinline__ f16x4 tile_tr_h(const f16* base, int pitch, int l) { 
   return __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p));
 }
 
+// The operand type of the products on the W2 side: fp16 (first launch) or bf16 (recomputation of
+// the chains whose values left fp16's range).
+template <bool F16>
+struct W2Side;
+template <>
+struct W2Side<true> {
+  typedef f16 elem;
+  typedef f16x4 x4;
+  typedef f16x8 x8;
+  static __device__ __forceinline__ f32x4 mma32(x8 a, x8 b, f32x4 c) { return mmah32(a, b, c); }
+  static __device__ __forceinline__ f32x4 mma16(x4 a, x4 b, f32x4 c) { return mmah16(a, b, c); }
+  static __device__ __forceinline__ x4 cvt(f32x4 x) { return to_f16x4(x); }
+  static __device__ __forceinline__ x8 cat(x4 lo, x4 hi) { return cat8h(lo, hi); }
+  static __device__ __forceinline__ x4 ld(const elem* p) { return ld4h(p); }
+  static __device__ __forceinline__ x4 tr(const elem* base, int pitch, int l) { return tile_tr_h(base, pitch, l); }
+};
+template <>
+struct W2Side<false> {
+  typedef bf16 elem;
+  typedef bf16x4 x4;
+  typedef bf16x8 x8;
+  static __device__ __forceinline__ f32x4 mma32(x8 a, x8 b, f32x4 c) { return ttt::mma32(a, b, c); }
+  static __device__ __forceinline__ f32x4 mma16(x4 a, x4 b, f32x4 c) { return ttt::mma16(a, b, c); }
+  static __device__ __forceinline__ x4 cvt(f32x4 x) { return to_bf16x4(x); }
+  static __device__ __forceinline__ x8 cat(x4 lo, x4 hi) { return cat8(lo, hi); }
+  static __device__ __forceinline__ x4 ld(const elem* p) { return ld4(p); }
+  static __device__ __forceinline__ x4 tr(const elem* base, int pitch, int l) { return tile_tr(base, pitch, l); }
+};
+
+// Largest magnitude among the four values (NaN compares as not in any range below).
+__device__ __forceinline__ float absmax4(f32x4 x) {
+  return fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
+}
+// True when, over the wave, the largest magnitude m (one per lane) is outside [lo, hi] while not all
+// values are zero, or is not a number.
+__device__ __forceinline__ bool wave_out_of_range(float m, float lo, float hi) {
+  return __any(!(m <= hi)) || (__any(m > 0.f) && !__any(m >= lo));
+}
+
 // Fast GELU path in packed fp16 (|x| <= sqrt 2): Phi(x) = 1/2 + x R(t) as above, and
 // GELU'(x) = 1/2 + x S(t), t = x^2, with S the degree-3 least-squares polynomial for
 // (Phi(x) - 1/2) / x + phi(x) on t in [0, 2] (Chebyshev nodes; max abs error of GELU' 1.2e-4).
@@ -141,20 +191,34 @@ __device__ __forceinline__ void st16_lds8(bf16* p, uint4 v) {
   reinterpret_cast<uint2*>(p)[1] = make_uint2(v.z, v.w);
 }
 
+// F16: first launch (fp16 operands on the W2 side, range checks; writes flags[bh] = 1 when a check
+// failed, else 0). !F16: recomputation with bf16 operands of the chains whose flag is set.
+template <bool F16>
 __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ w1, const float* __restrict__ w2, long long wbs, int H, int N,
-    float a, bf16* __restrict__ o, float* __restrict__ w1_out, float* __restrict__ w2_out) {
+    float a, bf16* __restrict__ o, float* __restrict__ w1_out, float* __restrict__ w2_out,
+    int* __restrict__ flags) {
+  using S = W2Side<F16>;
+  using x4 = typename S::x4;
+  using x8 = typename S::x8;
+  using GpT = typename std::conditional<F16, f16x4, f32x4>::type;  // GELU'(Z1) tiles
   __shared__ __align__(16) bf16 sKVQ[kRing][3][kCh * kP];
-  __shared__ __align__(16) f16 sE[2][kCh * kP];            // -a E [token][out] (fp16)
+  __shared__ __align__(16) typename S::elem sE[2][kCh * kP];  // -a E [token][out]
   __shared__ __align__(16) f32x4 sRed[kWaves * kSlots * 64];  // lane-private partial tiles
+  __shared__ int sBad;
 
   const int bh = blockIdx.x, b = bh / H, h = bh % H;
+  if constexpr (!F16) {
+    if (flags[bh] == 0) return;  // this chain's fp16 result stands
+  }
   const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
   const long long ts = (long long)H * kD;
   const float* W1g = w1 + b * wbs + (long long)h * kD * kDh;
   const float* W2g = w2 + b * wbs + (long long)h * kDh * kD;
   const int hid0 = kHw * w;
+  bool bad = false;  // wave-uniform: a value converted to fp16 left the checked range
+  if (F16 && threadIdx.x == 0) sBad = 0;
 
   // W1t[m][n]:  W1[16m + 4g + j][hid0 + 16n + r]   (rows: features, cols: hidden)
   // W2t[n][o]:  W2[hid0 + 16n + 4g + j][16o + r]   (rows: hidden,   cols: outputs)
@@ -167,8 +231,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
         W2t[n][m][j] = W2g[(hid0 + 16 * n + 4 * g + j) * kD + 16 * m + r];
         W2x[m][n][j] = W2g[(hid0 + 16 * n + r) * kD + 16 * m + 4 * g + j];
       }
-  f16x4 ident;  // identity tile as the B operand: lane holds I[4g + i][r]
-  for (int i = 0; i < 4; ++i) ident[i] = (f16)(4 * g + i == r ? 1.f : 0.f);
+  x4 ident;  // identity tile as the B operand: lane holds I[4g + i][r]
+  for (int i = 0; i < 4; ++i) ident[i] = (typename S::elem)(4 * g + i == r ? 1.f : 0.f);
 
   const int C = N / kCh;
   const long long head0 = (long long)b * N * ts + (long long)h * kD;
@@ -185,9 +249,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
   __syncthreads();
 
   bf16x4 d1p[kNh];  // -a D1 of the previous chunk, [token][hidden] tiles
-  f16x8 x2tp;       // X2^T of the previous chunk, [hidden][token] tiles (both, c-layout k map)
+  x8 x2tp;          // X2^T of the previous chunk, [hidden][token] tiles (both, c-layout k map)
   for (int n = 0; n < kNh; ++n) d1p[n] = bf16x4{};
-  x2tp = f16x8{};
+  x2tp = x8{};
 
   // One chunk step: forward of chunk c, read-out of chunk c - 1. pf_cur holds chunk c + 2 (loaded
   // one step earlier); chunk c + 3 is loaded into pf_next.
@@ -199,8 +263,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
     const bf16* sV = sKVQ[c % kRing][1];
     const bf16* sKp = sKVQ[(c + kRing - 1) % kRing][0];  // chunk c - 1
     const bf16* sQp = sKVQ[(c + kRing - 1) % kRing][2];
-    f16* sEc = sE[c & 1];
-    const f16* sEp = sE[(c + 1) & 1];  // -a E of chunk c - 1
+    typename S::elem* sEc = sE[c & 1];
+    const typename S::elem* sEp = sE[(c + 1) & 1];  // -a E of chunk c - 1
 
     // ---------------- phase 1: products with the current weights. The read-out of chunk c - 1
     // and the forward of chunk c are independent; their products, GELUs and remaining products
@@ -210,7 +274,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
       for (int n = 0; n < kNh; ++n) w1b[ks][n] = cat_tiles(W1t[2 * ks][n], W1t[2 * ks + 1][n]);
     f32x4 Z1q[kNh];  // read-out: Z1q^T [hidden][token]
     f32x4 Z1[kNh];   // forward: Z1 [token][hidden]
-    f16x4 x2qh[kNh], x2b[kNh], gph[kNh];  // GELU(Z1q), GELU(Z1), GELU'(Z1) as fp16 tiles
+    x4 x2qh[kNh], x2b[kNh];  // GELU(Z1q), GELU(Z1) as W2-side operand tiles
+    GpT gph[kNh];            // GELU'(Z1)
     if constexpr (rd) {
       // M[t'][t] = k_t' . q_t of chunk c - 1, kept for t' > t.
       f32x4 mt = zero4();
@@ -242,79 +307,100 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
         Z1[n] = z;
       }
     }
-    {  // GELU of both chains, one fast-path decision for the wave
-      f16x4 zq[kNh], zf[kNh], tq[kNh], tf[kNh];
-      f16x4 tm = splat(0.f);
+    // GELU of both chains. fp32 with the library erf, for the recomputation, or when a hidden
+    // pre-activation of the wave's step exceeds sqrt 2 in magnitude; otherwise the packed fp16
+    // polynomials.
+    auto gelu_lib = [&](auto& xq_out, auto& xf_out, auto& gp_out, float& xm) {
       for (int n = 0; n < kNh; ++n) {
+        f32x4 xq, xf, gp;
+        for (int j = 0; j < 4; ++j) {
+          if constexpr (rd) xq[j] = Z1q[n][j] * cdf_lib(Z1q[n][j]);
+          if constexpr (fwd) {
+            const float x = Z1[n][j], cdf = cdf_lib(x);
+            xf[j] = x * cdf;
+            gp[j] = fmaf(x, __builtin_amdgcn_exp2f(fmaf(x * x, kNegHalfLog2e, kLog2InvSqrt2Pi)), cdf);
+          }
+        }
         if constexpr (rd) {
-          zq[n] = to_f16x4(Z1q[n]);
-          tq[n] = zq[n] * zq[n];
-          tm = __builtin_elementwise_max(tm, tq[n]);
+          xq_out[n] = S::cvt(xq);
+          xm = fmaxf(xm, absmax4(xq));
         }
         if constexpr (fwd) {
-          zf[n] = to_f16x4(Z1[n]);
-          tf[n] = zf[n] * zf[n];
-          tm = __builtin_elementwise_max(tm, tf[n]);
+          xf_out[n] = S::cvt(xf);
+          xm = fmaxf(xm, absmax4(xf));
+          if constexpr (F16) gp_out[n] = to_f16x4(gp);
+          else gp_out[n] = gp;
         }
       }
-      const float tmax = fmaxf(fmaxf((float)tm[0], (float)tm[1]), fmaxf((float)tm[2], (float)tm[3]));
-      if (!__any(!(tmax <= 2.f))) {
-        for (int n = 0; n < kNh; ++n) {
-          if constexpr (rd) x2qh[n] = zq[n] * cdf_fast_h(zq[n], tq[n]);
-          if constexpr (fwd) {
-            x2b[n] = zf[n] * cdf_fast_h(zf[n], tf[n]);
-            gph[n] = slope_fast_h(zf[n], tf[n]);
-          }
-        }
-      } else {  // fp32 with the library erf
-        for (int n = 0; n < kNh; ++n) {
-          f32x4 xq, xf, gp;
-          for (int j = 0; j < 4; ++j) {
-            if constexpr (rd) xq[j] = Z1q[n][j] * cdf_lib(Z1q[n][j]);
-            if constexpr (fwd) {
-              const float x = Z1[n][j], cdf = cdf_lib(x);
-              xf[j] = x * cdf;
-              gp[j] = fmaf(x, __builtin_amdgcn_exp2f(fmaf(x * x, kNegHalfLog2e, kLog2InvSqrt2Pi)), cdf);
-            }
-          }
-          if constexpr (rd) x2qh[n] = to_f16x4(xq);
-          if constexpr (fwd) {
-            x2b[n] = to_f16x4(xf);
-            gph[n] = to_f16x4(gp);
-          }
-        }
+    };
+    if constexpr (F16) {
+      float zm = 0.f;  // largest |pre-activation| of the lane
+      for (int n = 0; n < kNh; ++n) {
+        if constexpr (rd) zm = fmaxf(zm, absmax4(Z1q[n]));
+        if constexpr (fwd) zm = fmaxf(zm, absmax4(Z1[n]));
       }
+      // Below 2^-10 the GELU outputs would sit near fp16's subnormal range.
+      bad |= __any(zm > 0.f) && !__any(zm >= 0x1p-10f);
+      if (!__any(!(zm <= kSqrt2h))) {
+        for (int n = 0; n < kNh; ++n) {
+          if constexpr (rd) {
+            const f16x4 zq = to_f16x4(Z1q[n]), tq = zq * zq;
+            x2qh[n] = zq * cdf_fast_h(zq, tq);
+          }
+          if constexpr (fwd) {
+            const f16x4 zf = to_f16x4(Z1[n]), tf = zf * zf;
+            x2b[n] = zf * cdf_fast_h(zf, tf);
+            gph[n] = slope_fast_h(zf, tf);
+          }
+        }
+      } else {
+        float xm = 0.f;
+        gelu_lib(x2qh, x2b, gph, xm);
+        // |X2|, |X2q| <= 32 keeps them and the 32-unit sums of X2q X2^T inside fp16.
+        bad |= __any(!(xm <= 32.f));
+      }
+    } else {
+      float xm = 0.f;
+      gelu_lib(x2qh, x2b, gph, xm);
     }
-    f16x8 x2q;
-    f16x4 n2b;
+    x8 x2q;
+    x4 n2b;
     if constexpr (rd) {
-      x2q = cat8h(x2qh[0], x2qh[1]);
+      x2q = S::cat(x2qh[0], x2qh[1]);
       // (with the previous chunk's X2^T, before the forward below replaces it)
-      f32x4 n2 = mmah32(x2tp, x2q, zero4());  // [t'][t] = sum_h X2[t'][h] X2q[t][h]
+      f32x4 n2 = S::mma32(x2tp, x2q, zero4());  // [t'][t] = sum_h X2[t'][h] X2q[t][h]
       for (int j = 0; j < 4; ++j) n2[j] = 4 * g + j <= r ? 0.f : -n2[j];
-      n2b = to_f16x4(n2);  // (-a is in the stored E)
+      n2b = S::cvt(n2);  // (-a is in the stored E)
     }
     if constexpr (fwd) {
       f32x4 xt[kNh];
-      for (int n = 0; n < kNh; ++n) xt[n] = mmah16(x2b[n], ident, zero4());  // X2^T [hidden][token]
-      x2tp = cat_tiles_h(xt[0], xt[1]);
+      for (int n = 0; n < kNh; ++n) xt[n] = S::mma16(x2b[n], ident, zero4());  // X2^T [hidden][token]
+      x2tp = S::cat(S::cvt(xt[0]), S::cvt(xt[1]));
     }
-    f16x8 w2a[4];  // W2^T tiles (k = this wave's hidden units), for both products below
-    for (int o2 = 0; o2 < 4; ++o2) w2a[o2] = cat_tiles_h(W2t[0][o2], W2t[1][o2]);
+    x8 w2a[4];  // W2^T tiles (k = this wave's hidden units), for both products below
+    for (int o2 = 0; o2 < 4; ++o2) w2a[o2] = S::cat(S::cvt(W2t[0][o2]), S::cvt(W2t[1][o2]));
     if constexpr (rd) {
       // This wave's share of O^T [out][token]: W2^T X2q^T over its hidden units, plus
       // (a E)^T striu(X2q X2^T)^T = (-a E)^T (-striu(X2q X2^T))^T with X2q X2^T summed over the
       // same units (t' > t kept), the latter as a 16x16x32 product with a zero upper k half
       // (same-shape chain).
       for (int o2 = 0; o2 < 4; ++o2) {
-        const f32x4 ow = mmah32(w2a[o2], x2q, zero4());
+        const f32x4 ow = S::mma32(w2a[o2], x2q, zero4());
         sRed[(w * kSlots + 4 + o2) * 64 + l] =
-            mmah32(cat8h(tile_tr_h(&sEp[16 * o2], kP, l), f16x4{}), cat8h(n2b, f16x4{}), ow);  // A = (-a E)^T
+            S::mma32(S::cat(S::tr(&sEp[16 * o2], kP, l), x4{}), S::cat(n2b, x4{}), ow);  // A = (-a E)^T
       }
     }
     if constexpr (fwd) {
       // Z2^T partial [out][token] over this wave's hidden units.
-      for (int o2 = 0; o2 < 4; ++o2) sRed[(w * kSlots + o2) * 64 + l] = mmah32(w2a[o2], x2tp, zero4());
+      for (int o2 = 0; o2 < 4; ++o2) sRed[(w * kSlots + o2) * 64 + l] = S::mma32(w2a[o2], x2tp, zero4());
+    }
+    if constexpr (F16 && fwd) {
+      if ((c & 31) == 0) {  // the W2 slice, every 32 chunks (here, where the barrier ends the block)
+        float wm = 0.f;
+        for (int n = 0; n < kNh; ++n)
+          for (int o2 = 0; o2 < 4; ++o2) wm = fmaxf(wm, absmax4(W2t[n][o2]));
+        bad |= wave_out_of_range(wm, 0x1p-10f, 0x1p15f);
+      }
     }
     __syncthreads();
 
@@ -330,7 +416,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
       for (int ww = 1; ww < kWaves; ++ww) s = s + pt[ww];
       f32x4 e;
       for (int j = 0; j < 4; ++j) e[j] = a * ((float)vv[j] - s[j]);
-      *reinterpret_cast<f16x4*>(&sEc[r * kP + 16 * w + 4 * g]) = to_f16x4(e);
+      if constexpr (F16) bad |= __any(!(absmax4(e) <= 0x1p15f));
+      *reinterpret_cast<x4*>(&sEc[r * kP + 16 * w + 4 * g]) = S::cvt(e);
     }
     if (rd && w >= 4) {  // O^T tile of chunk c - 1 = sum of the waves' shares
       const int o4 = w - 4;
@@ -347,14 +434,15 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
     // ---------------- phase 3: backward and state update of chunk c
     if (fwd) {
       // -a dX2 [token][hidden] = (-a E) W2^T: A = -a E rows (c-layout k map), B = W2x tiles.
-      f16x8 ea[2];
+      x8 ea[2];
       for (int ko = 0; ko < 2; ++ko) {
-        const f16* pe = &sEc[r * kP + 32 * ko + 4 * g];
-        ea[ko] = cat8h(ld4h(pe), ld4h(pe + 16));
+        const typename S::elem* pe = &sEc[r * kP + 32 * ko + 4 * g];
+        ea[ko] = S::cat(S::ld(pe), S::ld(pe + 16));
       }
       for (int n = 0; n < kNh; ++n) {
         f32x4 acc = zero4();
-        for (int ko = 0; ko < 2; ++ko) acc = mmah32(ea[ko], cat_tiles_h(W2x[2 * ko][n], W2x[2 * ko + 1][n]), acc);
+        for (int ko = 0; ko < 2; ++ko)
+          acc = S::mma32(ea[ko], S::cat(S::cvt(W2x[2 * ko][n]), S::cvt(W2x[2 * ko + 1][n])), acc);
         f32x4 d1;  // -a D1
         for (int j = 0; j < 4; ++j) d1[j] = acc[j] * (float)gph[n][j];
         d1p[n] = to_bf16x4(d1);
@@ -366,10 +454,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
       }
       // W2 += X2^T (-a E) and W2^T += (-a E)^T X2: -a E's transposed tiles give both operands.
       for (int o2 = 0; o2 < 4; ++o2) {
-        const f16x4 e = tile_tr_h(&sEc[16 * o2], kP, l);
+        const x4 e = S::tr(&sEc[16 * o2], kP, l);
         for (int n = 0; n < kNh; ++n) {
-          W2t[n][o2] = mmah16(x2b[n], e, W2t[n][o2]);
-          W2x[o2][n] = mmah16(e, x2b[n], W2x[o2][n]);
+          W2t[n][o2] = S::mma16(x2b[n], e, W2t[n][o2]);
+          W2x[o2][n] = S::mma16(e, x2b[n], W2x[o2][n]);
         }
       }
     }
@@ -405,19 +493,30 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
       for (int o2 = 0; o2 < 4; ++o2)
         for (int j = 0; j < 4; ++j) dst[(hid0 + 16 * n + 4 * g + j) * kD + 16 * o2 + r] = W2t[n][o2][j];
   }
+  if constexpr (F16) {
+    if (bad && l == 0) sBad = 1;  // (every writer stores the same value)
+    __syncthreads();
+    if (threadIdx.x == 0) flags[bh] = sBad;
+  }
 }
 
 }  // namespace
 
-size_t mlp_workspace_bytes(int, int, int, int, int, int) { return 0; }
+// One flag per (batch, head) chain.
+size_t mlp_workspace_bytes(int B, int H, int, int, int, int) { return (size_t)B * H * sizeof(int); }
 
 hipError_t mlp_launch(int B, int H, int N, int D, int Dh, int chunk, float eta, const void* q,
                       const void* k, const void* v, const float* w1, const float* w2,
-                      long long wbs, void* o, float* w1_out, float* w2_out, void*, hipStream_t st) {
+                      long long wbs, void* o, float* w1_out, float* w2_out, void* ws, hipStream_t st) {
   if (D != kD || Dh != kDh || chunk != kCh) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(mlp_fwd_bf16, dim3(B * H), dim3(kWaves * 64), 0, st, (const bf16*)q, (const bf16*)k,
-                     (const bf16*)v, w1, w2, wbs, H, N, eta / (float)chunk, (bf16*)o, w1_out,
-                     w2_out);
+  int* flags = static_cast<int*>(ws);
+  const float a = eta / (float)chunk;
+  hipLaunchKernelGGL(mlp_fwd_bf16<true>, dim3(B * H), dim3(kWaves * 64), 0, st, (const bf16*)q,
+                     (const bf16*)k, (const bf16*)v, w1, w2, wbs, H, N, a, (bf16*)o, w1_out, w2_out,
+                     flags);
+  hipLaunchKernelGGL(mlp_fwd_bf16<false>, dim3(B * H), dim3(kWaves * 64), 0, st, (const bf16*)q,
+                     (const bf16*)k, (const bf16*)v, w1, w2, wbs, H, N, a, (bf16*)o, w1_out, w2_out,
+                     flags);
   return hipGetLastError();
 }
 
