@@ -46,9 +46,9 @@
  *   ttt_mlp_forward's products on the W2 side (hidden activations, W2, residuals), which take
  *   fp16 operands (more mantissa bits) while the values converted stay inside the ranges that
  *   ttt_mlp_forward states; chains whose values leave them are recomputed with bf16 operands.
- * Threads.  Entry points are reentrant. The only state kept between calls is a per-device cache
- *   of kernel occupancy figures (the chunked scans size their segment plan from it), filled on a
- *   device's first call through atomics.
+ * Threads.  Entry points are reentrant and keep no state between calls. How a call splits its work
+ *   (token splits, scan segments) is a function of its sizes only, never of the device it runs
+ *   on, so workspace sizes and results are the same on every device.
  */
 #ifndef TTT_H_
 #define TTT_H_

@@ -29,8 +29,6 @@
 // Inside every kernel, wave w owns columns [16w, 16w + 16) of its state (the columns of W are
 // independent regressions), held in MFMA accumulator layout; the chunk's K, V, Q are staged
 // through LDS with the next chunk prefetched into registers.
-#include <atomic>
-
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -649,63 +647,43 @@ struct ChunkPlan {
   int S, L;  // segments per (b, h) and chunks per segment
 };
 
-// Resident workgroups of the segment kernels, for the current device. The compose and scan
-// kernels walk their segment's chunks one after another (latency-bound), so the plan sizes the
-// grid to be resident in one round: a partial second round would double their time. Queried once
-// per (kernel, device) and cached; without a usable device the defaults of MI355X apply
-// (256 CUs, 2 workgroups per CU).
-struct Residency {
-  int cus, per_cu;
-};
-constexpr int kMaxDevices = 64;
+// Resident workgroups of the segment kernels. The compose and scan kernels walk their segment's
+// chunks one after another (latency-bound), so the plan sizes the grid to be resident in one round:
+// a partial second round would double their time. The plan is a pure function of the call's sizes
+// and of fixed constants, never of the device the call runs on, so that the workspace size and the
+// rounding path (the output bits) are the same everywhere:
+//  - kPlanCUs: the 256 compute units of an MI355X (a device with fewer only runs the grid in more
+//    rounds);
+//  - the waves per SIMD each compiled kernel sustains on gfx950, the compiler's occupancy figure
+//    (it accounts for the kernel's VGPR and LDS use), indexed [log2(D / 16)][log2(CH / 16)][bidir];
+//    tests/test_codegen.py checks these tables against the compiler's resource report of the
+//    current sources.
+// A kernel of w waves per workgroup then keeps floor(4 * occupancy / w) workgroups on a CU (at most
+// kMaxGroupsPerCU), and the plan takes the smaller figure of compose and scan.
+constexpr int kPlanCUs = 256;
+constexpr int kMaxGroupsPerCU = 16;
+constexpr int kComposeOcc[3][3][2] = {{{8, 8}, {8, 8}, {7, 6}},   // D = 16: CH = 16, 32, 64
+                                      {{8, 8}, {8, 8}, {7, 5}},   // D = 32
+                                      {{8, 6}, {7, 5}, {6, 4}}};  // D = 64
+constexpr int kScanOcc[3][3][2] = {{{7, 1}, {4, 1}, {2, 1}},
+                                   {{7, 1}, {4, 1}, {2, 1}},
+                                   {{5, 1}, {4, 1}, {2, 1}}};
 
-template <class Kernel>
-int cached_per_cu(Kernel kernel, int threads, int dev, std::atomic<int>* cache) {
-  int v = cache[dev].load(std::memory_order_relaxed);
-  if (v > 0) return v;
-  int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n < 1) {
-    (void)hipGetLastError();
-    n = 2;
-  }
-  cache[dev].store(n, std::memory_order_relaxed);
-  return n;
-}
-
-int device_cus(int dev) {
-  static std::atomic<int> cache[kMaxDevices];
-  int v = cache[dev].load(std::memory_order_relaxed);
-  if (v > 0) return v;
-  int n = 0;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) {
-    (void)hipGetLastError();
-    n = 256;
-  }
-  cache[dev].store(n, std::memory_order_relaxed);
-  return n;
-}
+constexpr int log2_16(int x) { return x == 16 ? 0 : (x == 32 ? 1 : 2); }
 
 template <int D, int CH>
-Residency residency(bool bidir) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
-    (void)hipGetLastError();
-    return Residency{256, 2};
-  }
-  static std::atomic<int> c_comp[2][kMaxDevices], c_scan[2][kMaxDevices];
-  const int comp = bidir ? cached_per_cu(chunk_compose_bf16<D, CH, true>, D / 8 * 64, dev, c_comp[1])
-                         : cached_per_cu(chunk_compose_bf16<D, CH, false>, D / 8 * 64, dev, c_comp[0]);
-  const int scan = bidir ? cached_per_cu(chunk_scan_bf16<D, CH, kBidir>, D / 16 * 64, dev, c_scan[1])
-                         : cached_per_cu(chunk_scan_bf16<D, CH, kCausal>, D / 16 * 64, dev, c_scan[0]);
-  return Residency{device_cus(dev), comp < scan ? comp : scan};
+int groups_per_cu(bool bidir) {
+  const int comp = 4 * kComposeOcc[log2_16(D)][log2_16(CH)][bidir] / (D / 8);
+  const int scan = 4 * kScanOcc[log2_16(D)][log2_16(CH)][bidir] / (D / 16);
+  const int n = comp < scan ? comp : scan;
+  return n < 1 ? 1 : (n > kMaxGroupsPerCU ? kMaxGroupsPerCU : n);
 }
 
 template <int D, int CH>
 ChunkPlan chunk_plan_dc(bool bidir, int B, int H, int N) {
   const int C = N / CH;
   const int BH = B * H;
-  const Residency res = residency<D, CH>(bidir);
-  const int slots = res.cus * res.per_cu;  // workgroups resident at once
+  const int slots = kPlanCUs * groups_per_cu<D, CH>(bidir);  // workgroups resident at once
   int S = slots / BH;                       // segments per (b, h): one resident round
   if (S > C / 4) S = C / 4;                 // keep at least 4 chunks per segment
   if (S < 1) S = 1;

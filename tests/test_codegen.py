@@ -158,3 +158,44 @@ def test_mlp_fast_gelu_in_fp16():
     assert np.abs(gelu - xd * ndtr(xd)).max() < 1.5e-3
     assert np.abs(slope - (ndtr(xd) + xd * phi)).max() < 1.5e-3
 
+
+
+def _occ_table(src, name):
+    m = re.search(name + r"\[3\]\[3\]\[2\]\s*=\s*\{(.*?)\};", src, flags=re.S)
+    assert m, f"{name} not found"
+    body = re.sub(r"//[^\n]*", "", m.group(1))
+    vals = [int(x) for x in re.findall(r"\d+", body)]
+    assert len(vals) == 18
+    return {(d, c, b): vals[(i * 3 + j) * 2 + b] for i, d in enumerate((16, 32, 64)) for j, c in enumerate((16, 32, 64))
+            for b in (0, 1)}
+
+
+@pytest.mark.skipif(HIPCC is None, reason="hipcc not available")
+def test_chunk_plan_occupancy_tables_match_the_compiled_kernels(tmp_path):
+    """The chunked scans size their segment plan from fixed tables of the waves per SIMD that each
+    compiled compose / scan kernel sustains (so that the plan does not depend on the device a call
+    runs on). Those tables must equal the compiler's occupancy report for the current sources."""
+    src_path = os.path.join(B.CSRC, "chunked.hip")
+    src = open(src_path).read()
+    compose, scan = _occ_table(src, "kComposeOcc"), _occ_table(src, "kScanOcc")
+    cmd = [HIPCC, *[f for f in B.flags_for("chunked.hip") if f != "-fPIC"], "--cuda-device-only", "-c", src_path,
+           "-o", str(tmp_path / "c.o"), "-Rpass-analysis=kernel-resource-usage"]
+    p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    assert p.returncode == 0, p.stdout[-2000:]
+    found = {}
+    kernel = None
+    for line in p.stdout.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            kernel = m.group(1)
+            continue
+        m = re.search(r"Occupancy \[waves/SIMD\]: (\d+)", line)
+        if m and kernel:
+            k = re.search(r"(chunk_compose_bf16|chunk_scan_bf16)ILi(\d+)ELi(\d+)EL([bi])(\d)E", kernel)
+            if k:
+                found[(k.group(1), int(k.group(2)), int(k.group(3)), int(k.group(5)))] = int(m.group(1))
+    assert len(found) == 36, sorted(found)
+    for (kind, d, c, bidir), occ in found.items():
+        table = compose if kind == "chunk_compose_bf16" else scan
+        assert table[(d, c, bidir)] == occ, f"{kind}<{d}, {c}, {'bidir' if bidir else 'causal'}>: table " \
+                                             f"{table[(d, c, bidir)]}, compiler {occ}"
