@@ -6,6 +6,10 @@ One step = one forward of every layer variant of the library, each at its refere
   * bidirectional chunked scan, Vision-TTT at 1280x1280 / 16-px patches: B=8, N=6400, 3 x 64, b=64
   * causal TTT-Linear language layer: B=2, N=16384, 12 x 64, b=16
   * causal TTT-MLP language layer: B=4, N=8192, 12 x 64, hidden 256, b=16
+The metric's N = 3136 / 6400 / 16384 are the first three (`metric_layers` in the output: their cold
+per-layer tokens/s and fraction of the 8 TB/s HBM peak). Per-layer figures are timed with each
+layer alone and its inputs rotated over copies totalling more than 1 GiB, so that every call
+reads them from HBM (cold); the warm figures (same inputs back to back) are reported beside them.
 Inputs are synthetic (seeded i.i.d. Gaussians of those shapes) and resident in HBM before the
 timed region. The four layers' inputs (584 MB) exceed the 256 MB Infinity Cache, so every layer
 starts with its inputs evicted by the other three. Within a step the TTT-MLP layer, whose 48
@@ -23,6 +27,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
@@ -30,6 +36,7 @@ if ROOT not in sys.path:
 SUITE = ["hvit3t_stage1_fullbatch", "vittt_bidir_1280", "ttt_linear_causal_16k", "ttt_mlp_causal_8k"]
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, TFLOP/s
+ROTATE_BYTES = 1200 * 2 ** 20   # cold per-layer timing: input copies rotated over more than this
 # Kernel sources and the build script (compiler flags) of each layer, for the traffic-counter
 # freshness check: a change to any of them makes the stored counters stale.
 _BUILD = "test_sequence_layers_amd/build.py"
@@ -105,41 +112,88 @@ def make_call(T, wl, d, torch):
                                      workspace=ws)
 
 
-def cpu_baseline(inputs) -> dict:
-    """The fp64 oracle, single-threaded, on a bounded sample of every layer (a subset of the
-    independent (batch, head) pairs), scaled to the whole suite step."""
+# CPU baseline sample: per layer, the (batch, head) slices the oracle runs, as tasks of
+# (batches, heads); each task's time is scaled by the layer's pair count over the pairs sampled
+# from that layer.
+CPU_SAMPLE = {
+    "hvit3t_stage1_fullbatch": [(8, 2)] * 2,   # 16 of 64 batches
+    "vittt_bidir_1280": [(1, 3)] * 2,          # 2 of 8 batches
+    "ttt_linear_causal_16k": [(1, 1)] * 4,     # 4 of 24 (batch, head) pairs
+    "ttt_mlp_causal_8k": [(1, 1)] * 8,         # 8 of 48 (batch, head) pairs
+}
+
+
+def _oracle_task(args):
+    """One oracle call on a (batch, head) slice, single-threaded; returns its duration (s)."""
     from threadpoolctl import threadpool_limits
 
     from oracle import ttt_oracle as O
 
-    samples = {"hvit3t_stage1_fullbatch": (64, 2), "vittt_bidir_1280": (8, 3), "ttt_linear_causal_16k": (2, 12),
-               "ttt_mlp_causal_8k": (1, 12)}  # (batches, heads) of each layer that the oracle runs (about 10 s)
-    total_s = 0.0
-    desc = []
+    op, eta, chunk, q, k, v, states = args
     with threadpool_limits(limits=1):
-        for name in SUITE:
-            x = inputs[name]
-            wl = x.wl
-            nb, nh = samples[name]
-            sl = (slice(0, nb), slice(None), slice(0, nh))
-            q, k, v = x.q64[sl], x.k64[sl], x.v64[sl]
+        t0 = time.perf_counter()
+        if op == "fullbatch":
+            O.fullbatch(q, k, v, states[0], eta)
+        elif op == "bidir":
+            O.chunked_bidir(q, k, v, states[0], eta, chunk)
+        elif op == "causal":
+            O.chunked_causal(q, k, v, states[0], eta, chunk)
+        else:
+            O.mlp_causal(q, k, v, states[0], states[1], eta, chunk)
+        return time.perf_counter() - t0
+
+
+def cpu_workers() -> int:
+    """Host cores for the oracle: OMP_NUM_THREADS (the machine's CPU share) or the core count, at most 16."""
+    n = int(os.environ.get("OMP_NUM_THREADS") or 0) or (os.cpu_count() or 1)
+    return max(1, min(16, n, os.cpu_count() or 1))
+
+
+def cpu_baseline(inputs, runs: int = 3) -> dict:
+    """The fp64 oracle as it stands, on the host's cores: a bounded sample of (batch, head) slices of
+    every layer (CPU_SAMPLE), one single-threaded task per slice, spread over a pool of worker
+    processes. Each run's time for the whole suite step is the sum over tasks of (task time x the
+    layer's pairs / the pairs sampled from that layer), divided by the worker count (the slices are independent, so
+    the full step would keep every core busy). One warm-up run, then the median of `runs`."""
+    import multiprocessing as mp
+    import statistics
+    from concurrent.futures import ProcessPoolExecutor
+
+    tasks, scales, desc = [], [], []
+    for name in SUITE:
+        if name not in inputs:
+            continue
+        x = inputs[name]
+        wl = x.wl
+        hb = 0
+        n_pairs = sum(nb * nh for nb, nh in CPU_SAMPLE[name])
+        for nb, nh in CPU_SAMPLE[name]:
+            # consecutive tasks take consecutive heads, then the next batches
+            b0, h0 = (hb // wl.H) * nb % wl.B, hb % wl.H
+            hb += nh
+            sl = (slice(b0, b0 + nb), slice(None), slice(h0, h0 + nh))
+            st = (x.w1[h0:h0 + nh], x.w2[h0:h0 + nh]) if wl.op == "mlp" else (x.w0[h0:h0 + nh],)
+            tasks.append((wl.op, wl.eta, wl.chunk, np.ascontiguousarray(x.q64[sl]), np.ascontiguousarray(x.k64[sl]),
+                          np.ascontiguousarray(x.v64[sl]), st))
+            scales.append(wl.B * wl.H / n_pairs)
+        desc.append(f"{name}: {n_pairs} of {wl.B * wl.H} (batch, head) pairs")
+    cores = cpu_workers()
+    ests, walls = [], []
+    with ProcessPoolExecutor(max_workers=cores, mp_context=mp.get_context("spawn")) as ex:
+        for run in range(runs + 1):
             t0 = time.perf_counter()
-            if wl.op == "fullbatch":
-                O.fullbatch(q, k, v, x.w0[:nh], wl.eta)
-            elif wl.op == "bidir":
-                O.chunked_bidir(q, k, v, x.w0[:nh], wl.eta, wl.chunk)
-            elif wl.op == "causal":
-                O.chunked_causal(q, k, v, x.w0[:nh], wl.eta, wl.chunk)
-            else:
-                O.mlp_causal(q, k, v, x.w1[:nh], x.w2[:nh], wl.eta, wl.chunk)
-            dt = time.perf_counter() - t0
-            scale = (wl.B * wl.H) / (nb * nh)
-            total_s += dt * scale
-            desc.append(f"{name}: {nb}x{nh} of {wl.B}x{wl.H} (batch x head) pairs in {dt:.2f} s")
-    tokens = sum(inputs[n].wl.tokens for n in SUITE)
-    return {"value": tokens / total_s, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": "fp64 numpy oracle, one thread; " + "; ".join(desc) +
-                      "; each layer's time scaled by its (batch, head) count"}
+            durs = list(ex.map(_oracle_task, tasks))
+            walls.append(time.perf_counter() - t0)
+            ests.append(sum(d * sc for d, sc in zip(durs, scales)) / cores)
+    step_s = statistics.median(ests[1:])
+    tokens = sum(inputs[n].wl.tokens for n in SUITE if n in inputs)
+    return {"value": tokens / step_s, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": (f"fp64 numpy oracle, {cores} worker processes of one thread each; "
+                       + "; ".join(desc) + f"; {len(tasks)} single-threaded tasks per run, each task's time "
+                       f"scaled by its layer's pair count over the pairs sampled from it, the sum divided by "
+                       f"{cores}; one warm-up run, then the "
+                       f"median of {runs} (suite step {step_s:.2f} s; sample wall times "
+                       + ", ".join(f"{w:.2f}" for w in walls[1:]) + " s)")}
 
 
 def copy_calibration(torch, reps: int = 5) -> None:
@@ -204,6 +258,8 @@ def main() -> int:
     ap.add_argument("--serial", action="store_true", help="run the layers of a step one after another on one stream")
     ap.add_argument("--layers", default=",".join(SUITE), help="comma-separated subset of the suite (profiling)")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--per-layer-only", action="store_true",
+                    help="only the per-layer cold and warm timings, one JSON line per layer (profiling)")
     ap.add_argument("--write-traffic", metavar="PMC_DIR", help="write profiles/traffic_<op>.json from counter runs")
     args = ap.parse_args()
     if args.write_traffic:
@@ -265,22 +321,39 @@ def main() -> int:
         step()
     torch.cuda.synchronize()
 
-    # Per-layer times: each layer alone, `reps` back-to-back calls between one pair of events (the
-    # events' own cost amortised over the calls). A short spin kernel first lets the host queue
-    # the calls ahead of the GPU, so that launch overhead on the host does not show in the time.
-    reps = max(args.steps, 10)
-    layer_ms = {}
+    # Per-layer times, each layer alone, many calls between one pair of events on the stream the
+    # kernels run on (the events' own cost amortised over the calls); a short spin kernel first lets
+    # the host queue the calls ahead of the GPU, so that launch overhead on the host does not show.
+    #  * cold: the calls rotate over copies of the layer's inputs and outputs totalling more than
+    #    1 GiB, so each call finds its inputs evicted from the 256 MB Infinity Cache;
+    #  * warm: back-to-back calls on one set of inputs (they fit in the Infinity Cache).
+    layer_ms, layer_ms_warm, rot_sets = {}, {}, {}
     for n in layers:
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        calls[n]()
-        if hasattr(torch.cuda, "_sleep"):
-            torch.cuda._sleep(1_000_000)
-        e0.record(stream)
-        for _ in range(reps):
-            calls[n]()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        layer_ms[n] = e0.elapsed_time(e1) / reps
+        wl = inputs[n].wl
+        nsets = max(2, -(-ROTATE_BYTES // wl.io_bytes))
+        sets = [dev[n]] + [{key: (t.clone() if key in ("q", "k", "v") else (torch.empty_like(t) if key == "o" else t))
+                            for key, t in dev[n].items()} for _ in range(nsets - 1)]
+        rcalls = [calls[n]] + [make_call(T, wl, d, torch) for d in sets[1:]]
+        rot_sets[n] = nsets
+        for label, seq in (("cold", [rcalls[i % nsets] for i in range(max(args.steps, 3 * nsets))]),
+                           ("warm", [calls[n]] * max(args.steps, 10))):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            for c in rcalls:
+                c()
+            if hasattr(torch.cuda, "_sleep"):
+                torch.cuda._sleep(1_000_000)
+            e0.record(stream)
+            for c in seq:
+                c()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            (layer_ms if label == "cold" else layer_ms_warm)[n] = e0.elapsed_time(e1) / len(seq)
+        del sets, rcalls
+    if args.per_layer_only:
+        for n in layers:
+            print(json.dumps({"layer": n, "ms_cold": layer_ms[n], "ms_warm": layer_ms_warm[n],
+                              "rotated_input_sets": rot_sets[n]}))
+        return 0
     dom = max(layers, key=lambda n: layer_ms[n])
 
     # Timed region: whole steps; one pair of events per step brackets the dominant layer's launch,
@@ -305,6 +378,9 @@ def main() -> int:
             "ms": round(layer_ms[n], 5), "tokens_per_s": wl.tokens / s,
             "alg_GBs": wl.io_bytes / s / 1e9, "hbm_frac": wl.io_bytes / s / 1e9 / PEAK_HBM_GBS,
             "alg_TFLOPs": alg_flops(wl) / s / 1e12, "mfma_frac": alg_flops(wl) / s / 1e12 / PEAK_BF16_TFLOPS,
+            "timing": f"cold: inputs rotated over {rot_sets[n]} copies (> 1 GiB)",
+            "ms_warm": round(layer_ms_warm[n], 5),
+            "hbm_frac_warm": wl.io_bytes / (layer_ms_warm[n] / 1000.0) / 1e9 / PEAK_HBM_GBS,
         }
     wl = inputs[dom].wl
     s = dom_ms / 1000.0
@@ -337,6 +413,10 @@ def main() -> int:
                    "schedule": "serial" if side is None else "TTT-MLP on a second stream beside the other layers"},
         "roofline": roof,
         "per_layer": per_layer,
+        "metric_layers": {str(inputs[n].wl.N): {"layer": n, "tokens_per_s": per_layer[n]["tokens_per_s"],
+                                                 "hbm_frac": per_layer[n]["hbm_frac"]}
+                          for n in ("hvit3t_stage1_fullbatch", "vittt_bidir_1280", "ttt_linear_causal_16k")
+                          if n in per_layer},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inputs)
