@@ -136,6 +136,25 @@ ttt_status ttt_mlp_forward(ttt_dtype dt, int B, int H, int N, int D, int Dh, int
                            void* o, float* w1_out, float* w2_out,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): ttt_forward_fullbatch without a workspace argument.
+ * Its scratch is a static device array of TTT_NOALLOC_SCRATCH_BYTES per device, which each device
+ * the library runs on holds until the process ends; nothing is allocated or freed by the call.
+ * Results are bit-identical to ttt_forward_fullbatch's. Every argument is validated as there;
+ * calls whose ttt_workspace_size(TTT_OP_FULLBATCH, ...) exceeds TTT_NOALLOC_SCRATCH_BYTES return
+ * TTT_ERR_WORKSPACE with nothing enqueued. `stream` must belong to the current device, whose
+ * scratch is used; its address is looked up on the first call on that device (TTT_ERR_HIP if
+ * that fails). All calls on one device share its scratch and keep no state in it between calls:
+ * calls that overlap in time on one device (different streams, or host threads without ordering)
+ * race on it and must not be made.
+ */
+#define TTT_NOALLOC_SCRATCH_BYTES (32u << 20)
+ttt_status ttt_forward_fullbatch_noalloc(ttt_dtype dt, int B, int H, int N, int D, float eta,
+                                         const void* q, const void* k, const void* v,
+                                         const float* w0, long long w0_batch_stride,
+                                         void* o, float* w_out, void* stream);
+
 /* Bytes of workspace an entry point needs for these sizes (0 when none; chunk and Dh are
  * ignored where they do not apply). Returns 0 also for unsupported sizes. */
 size_t ttt_workspace_size(ttt_op op, ttt_dtype dt, int B, int H, int N, int D, int Dh, int chunk);

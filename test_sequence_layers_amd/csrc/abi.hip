@@ -3,6 +3,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
 
 #include "../../include/ttt.h"
 #include "internal.hpp"
@@ -87,6 +88,35 @@ ttt_status check_linear(ttt_op op, ttt_dtype dt, int B, int H, int N, int D, int
 }
 
 ttt_status from_hip(hipError_t e) { return e == hipSuccess ? TTT_OK : TTT_ERR_HIP; }
+
+// Scratch of ttt_forward_fullbatch_noalloc: one static array per device, never allocated or freed
+// by the library (each device holds it until the process ends). In host code `scratch` only names
+// the symbol; its device address is looked up once per device with that device current, and only
+// that address is ever handed to kernels.
+__device__ __align__(256) unsigned char scratch[TTT_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];  // device address of `scratch`, per device (null until looked up)
+
+// Device address of the current device's scratch, or null if it cannot be had.
+void* scratch_of_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch[dev] = p;
+  }
+  return g_scratch[dev];
+}
 
 }  // namespace
 
@@ -203,6 +233,21 @@ ttt_status ttt_mlp_forward(ttt_dtype dt, int B, int H, int N, int D, int Dh, int
   return from_hip(ttt::mlp_launch(B, H, N, D, Dh, chunk, eta, q, k, v, w1_0, w2_0,
                                   w_batch_stride, o, w1_out, w2_out, workspace,
                                   static_cast<hipStream_t>(stream)));
+}
+
+ttt_status ttt_forward_fullbatch_noalloc(ttt_dtype dt, int B, int H, int N, int D, float eta,
+                                         const void* q, const void* k, const void* v,
+                                         const float* w0, long long w0_batch_stride, void* o,
+                                         float* w_out, void* stream) {
+  const ttt_status st = check_linear(TTT_OP_FULLBATCH, dt, B, H, N, D, 0, eta, q, k, v, w0,
+                                     w0_batch_stride, o, w_out, nullptr, 0, false);
+  if (st != TTT_OK) return st;
+  const size_t need = ttt_workspace_size(TTT_OP_FULLBATCH, dt, B, H, N, D, 0, 0);
+  if (need > (size_t)TTT_NOALLOC_SCRATCH_BYTES) return TTT_ERR_WORKSPACE;
+  void* ws = scratch_of_current_device();
+  if (!ws) return TTT_ERR_HIP;
+  return from_hip(ttt::fb_launch(dt == TTT_BF16, B, H, N, D, eta, q, k, v, w0, w0_batch_stride,
+                                 o, w_out, ws, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

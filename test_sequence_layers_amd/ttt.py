@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(HERE, "libttt.so")
 TTT_OK, TTT_ERR_INVALID, TTT_ERR_UNSUPPORTED, TTT_ERR_WORKSPACE, TTT_ERR_HIP = range(5)
 TTT_F32, TTT_BF16 = 0, 1
 TTT_OP_FULLBATCH, TTT_OP_CAUSAL, TTT_OP_BIDIR, TTT_OP_MLP = range(4)
+TTT_NOALLOC_SCRATCH_BYTES = 32 << 20  # static scratch of ttt_forward_fullbatch_noalloc, per device
 
 # Every symbol include/ttt.h declares, with its ctypes signature.
 _c_int, _c_float, _c_ll, _vp, _sz = ctypes.c_int, ctypes.c_float, ctypes.c_longlong, ctypes.c_void_p, ctypes.c_size_t
@@ -27,6 +28,8 @@ SIGNATURES = {
                                            _vp, _c_ll, _vp, _vp, _vp, _sz, _vp]),
     "ttt_mlp_forward": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _vp, _vp, _vp,
                                  _vp, _vp, _c_ll, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "ttt_forward_fullbatch_noalloc": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _vp, _vp, _vp, _vp,
+                                               _c_ll, _vp, _vp, _vp]),
     "ttt_workspace_size": (_sz, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
     "ttt_status_string": (ctypes.c_char_p, [_c_int]),
 }
@@ -181,6 +184,25 @@ def ttt_forward_fullbatch(q, k, v, w0, eta: float = 1.0, *, o=None, w_out=None, 
 
     q, k, v, o: [B, N, H, D] bf16 or fp32; w0: fp32 [H, D, D] or [B, H, D, D]; w_out: fp32 [B, H, D, D]."""
     return _linear(TTT_OP_FULLBATCH, "ttt_forward_fullbatch", q, k, v, w0, 0, eta, o, w_out, workspace, stream)
+
+
+def ttt_forward_fullbatch_noalloc(q, k, v, w0, eta: float = 1.0, *, o, w_out=None, stream=None):
+    """ttt_forward_fullbatch for callers that cannot allocate: the library's static per-device scratch
+    replaces the workspace, and the caller passes the output `o`. Returns o."""
+    lib = load_library()
+    _check_io(q, k, v)
+    torch = _torch()
+    B, N, H, D = q.shape
+    dev = q.device
+    dt = _dtype_code(q)
+    stride = _state_stride("w0", w0, B, H, D, D, dev)
+    _check_tensor("o", o, q.shape, q.dtype, dev)
+    _check_out("w_out", w_out, (B, H, D, D), torch.float32, dev)
+    with torch.cuda.device(dev):
+        st = lib.ttt_forward_fullbatch_noalloc(dt, B, H, N, D, float(eta), _ptr(q), _ptr(k), _ptr(v), _ptr(w0),
+                                               stride, _ptr(o), _ptr(w_out), _stream(stream, dev))
+    _raise(st, "ttt_forward_fullbatch_noalloc")
+    return o
 
 
 def ttt_forward_chunked_causal(q, k, v, w0, chunk: int, eta: float = 1.0, *, o=None, w_out=None, workspace=None,

@@ -25,7 +25,23 @@ def _declared_functions():
 def test_header_declares_the_entry_points():
     assert _declared_functions() == sorted([
         "ttt_forward_fullbatch", "ttt_forward_chunked_causal", "ttt_forward_chunked_bidir", "ttt_mlp_forward",
-        "ttt_workspace_size", "ttt_status_string"])
+        "ttt_workspace_size", "ttt_status_string", "ttt_forward_fullbatch_noalloc"])
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch_before_any_device_call():
+    """The no-alloc full-batch entry point validates everything, the scratch size included, before
+    it touches the device (so this runs without a GPU), and reports calls too large for its static
+    scratch as a workspace error."""
+    lib = T.load_library()
+    B, H, D = 4096, 6, 64  # 256-group plan: one split per group, 2 * 6 * 64 * 64 * 4 bytes each
+    assert T.ttt_workspace_size(T.TTT_OP_FULLBATCH, T.TTT_BF16, B, H, 196, D) > T.TTT_NOALLOC_SCRATCH_BYTES
+    call = lambda B=B, o=4, N=196: lib.ttt_forward_fullbatch_noalloc(T.TTT_BF16, B, H, N, D, 1.0, _p(0), _p(1),  # noqa: E731
+                                                                     _p(2), _p(3), 0, None if o is None else _p(o),
+                                                                     None, None)
+    assert call() == binding.TTT_ERR_WORKSPACE
+    assert call(o=None) == binding.TTT_ERR_INVALID
+    assert call(o=0) == binding.TTT_ERR_INVALID  # output aliases q
+    assert call(N=0) == binding.TTT_ERR_INVALID
 
 
 def test_library_exports_every_declared_symbol():
