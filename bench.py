@@ -37,6 +37,7 @@ SUITE = ["hvit3t_stage1_fullbatch", "vittt_bidir_1280", "ttt_linear_causal_16k",
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, TFLOP/s
 ROTATE_BYTES = 1200 * 2 ** 20   # cold per-layer timing: input copies rotated over more than this
+SPIN_CYCLES = 25_000_000        # GPU spin before a timed sequence of calls, so the host queues them all
 # Kernel sources and the build script (compiler flags) of each layer, for the traffic-counter
 # freshness check: a change to any of them makes the stored counters stale.
 _BUILD = "test_sequence_layers_amd/build.py"
@@ -249,6 +250,46 @@ def write_traffic(pmc_dir: str) -> int:
     return 0
 
 
+def extra_legs(T, torch, inputs, dev, time_rotated) -> dict:
+    """Legs outside the suite step, each timed like the layers (cold, inputs rotated over > 1 GiB):
+      * dwconv_kv_vittt_1280: the Vision-TTT Conv2d preprocessing, a depth-wise 3x3 convolution of
+        K and of V over the 80 x 80 token grid (8 images, C = 3 x 64), bf16;
+      * vittt_bidir_1280_with_dwconv: that preprocessing followed by the bidirectional scan."""
+    name = "vittt_bidir_1280"
+    if name not in inputs:
+        return {}
+    wl = inputs[name].wl
+    Hi = Wi = 80
+    C = wl.H * wl.D
+    rs = np.random.default_rng(4242)
+    wk, wv = [torch.from_numpy((rs.standard_normal((C, 3, 3)) / 3.0).astype(np.float32)).cuda() for _ in range(2)]
+    bk, bv = [torch.from_numpy((rs.standard_normal(C) * 0.05).astype(np.float32)).cuda() for _ in range(2)]
+    need = T.ttt_workspace_size(T.TTT_OP_BIDIR, T.TTT_BF16, wl.B, wl.H, wl.N, wl.D, 0, wl.chunk)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    kc, vc = torch.empty_like(dev[name]["k"]), torch.empty_like(dev[name]["v"])
+
+    def conv(d):
+        return lambda: (T.ttt_dwconv3x3(d["k"], wk, bk, height=Hi, width=Wi, y=kc),
+                        T.ttt_dwconv3x3(d["v"], wv, bv, height=Hi, width=Wi, y=vc))
+
+    def chain(d):
+        def run():
+            conv(d)()
+            T.ttt_forward_chunked_bidir(d["q"], kc, vc, d["w0"], wl.chunk, wl.eta, o=d["o"], workspace=ws)
+        return run
+
+    conv_bytes = 4 * wl.B * wl.N * C * 2          # read K and V, write both convolved
+    out = {}
+    for leg, make, nbytes in (("dwconv_kv_vittt_1280", conv, conv_bytes),
+                              ("vittt_bidir_1280_with_dwconv", chain, conv_bytes + wl.io_bytes)):
+        cold, warm, nsets = time_rotated(make, dev[name], nbytes)
+        s = cold / 1000.0
+        out[leg] = {"ms": round(cold, 5), "ms_warm": round(warm, 5), "tokens_per_s": wl.tokens / s,
+                    "alg_bytes": nbytes, "alg_GBs": nbytes / s / 1e9, "hbm_frac": nbytes / s / 1e9 / PEAK_HBM_GBS,
+                    "timing": f"cold: inputs rotated over {nsets} copies (> 1 GiB)"}
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -258,6 +299,7 @@ def main() -> int:
     ap.add_argument("--serial", action="store_true", help="run the layers of a step one after another on one stream")
     ap.add_argument("--layers", default=",".join(SUITE), help="comma-separated subset of the suite (profiling)")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--no-extra-legs", action="store_true", help="skip the legs outside the suite step")
     ap.add_argument("--per-layer-only", action="store_true",
                     help="only the per-layer cold and warm timings, one JSON line per layer (profiling)")
     ap.add_argument("--write-traffic", metavar="PMC_DIR", help="write profiles/traffic_<op>.json from counter runs")
@@ -322,33 +364,39 @@ def main() -> int:
     torch.cuda.synchronize()
 
     # Per-layer times, each layer alone, many calls between one pair of events on the stream the
-    # kernels run on (the events' own cost amortised over the calls); a short spin kernel first lets
-    # the host queue the calls ahead of the GPU, so that launch overhead on the host does not show.
+    # kernels run on (the events' own cost amortised over the calls); a spin kernel first lets the
+    # host queue all the calls ahead of the GPU, so that host time per call does not show.
     #  * cold: the calls rotate over copies of the layer's inputs and outputs totalling more than
     #    1 GiB, so each call finds its inputs evicted from the 256 MB Infinity Cache;
     #  * warm: back-to-back calls on one set of inputs (they fit in the Infinity Cache).
-    layer_ms, layer_ms_warm, rot_sets = {}, {}, {}
-    for n in layers:
-        wl = inputs[n].wl
-        nsets = max(2, -(-ROTATE_BYTES // wl.io_bytes))
-        sets = [dev[n]] + [{key: (t.clone() if key in ("q", "k", "v") else (torch.empty_like(t) if key == "o" else t))
-                            for key, t in dev[n].items()} for _ in range(nsets - 1)]
-        rcalls = [calls[n]] + [make_call(T, wl, d, torch) for d in sets[1:]]
-        rot_sets[n] = nsets
+    def time_rotated(make, d0, io_bytes):
+        """(cold ms, warm ms, input sets) of the calls make(d) builds, d rotating over copies of d0."""
+        nsets = max(2, -(-ROTATE_BYTES // io_bytes))
+        sets = [d0] + [{key: (t.clone() if key in ("q", "k", "v") else (torch.empty_like(t) if key == "o" else t))
+                        for key, t in d0.items()} for _ in range(nsets - 1)]
+        rcalls = [make(d) for d in sets]
+        res = {}
         for label, seq in (("cold", [rcalls[i % nsets] for i in range(max(args.steps, 3 * nsets))]),
-                           ("warm", [calls[n]] * max(args.steps, 10))):
+                           ("warm", [rcalls[0]] * max(args.steps, 10))):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             for c in rcalls:
                 c()
-            if hasattr(torch.cuda, "_sleep"):
-                torch.cuda._sleep(1_000_000)
+            if hasattr(torch.cuda, "_sleep"):  # (about 10 ms: the binding takes ~20 us of host time a call)
+                torch.cuda._sleep(SPIN_CYCLES)
             e0.record(stream)
             for c in seq:
                 c()
             e1.record(stream)
             torch.cuda.synchronize()
-            (layer_ms if label == "cold" else layer_ms_warm)[n] = e0.elapsed_time(e1) / len(seq)
-        del sets, rcalls
+            res[label] = e0.elapsed_time(e1) / len(seq)
+        return res["cold"], res["warm"], nsets
+
+    layer_ms, layer_ms_warm, rot_sets = {}, {}, {}
+    for n in layers:
+        wl = inputs[n].wl
+        layer_ms[n], layer_ms_warm[n], rot_sets[n] = time_rotated(
+            lambda d, wl=wl: make_call(T, wl, d, torch), dev[n], wl.io_bytes)
+    extra = {} if args.no_extra_legs else extra_legs(T, torch, inputs, dev, time_rotated)
     if args.per_layer_only:
         for n in layers:
             print(json.dumps({"layer": n, "ms_cold": layer_ms[n], "ms_warm": layer_ms_warm[n],
@@ -413,6 +461,7 @@ def main() -> int:
                    "schedule": "serial" if side is None else "TTT-MLP on a second stream beside the other layers"},
         "roofline": roof,
         "per_layer": per_layer,
+        "extra_legs": extra,
         "metric_layers": {str(inputs[n].wl.N): {"layer": n, "tokens_per_s": per_layer[n]["tokens_per_s"],
                                                  "hbm_frac": per_layer[n]["hbm_frac"]}
                           for n in ("hvit3t_stage1_fullbatch", "vittt_bidir_1280", "ttt_linear_causal_16k")

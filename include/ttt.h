@@ -33,7 +33,7 @@
  *     TTT_ERR_INVALID      null pointer, non-positive size, N not a multiple of chunk,
  *                          misaligned pointer or batch stride, overlapping output, non-finite eta
  *     TTT_ERR_UNSUPPORTED  D not in {16, 32, 64}; chunk not in {16, 32, 64};
- *                          TTT-MLP with (D, Dh) other than (64, 256); TTT-MLP with fp32 I/O
+ *                          TTT-MLP with Dh not a multiple of 64 in [64, 1024]
  *     TTT_ERR_WORKSPACE    workspace_bytes < ttt_workspace_size(...)
  *     TTT_ERR_HIP          a HIP launch error reported right after enqueueing
  * Workspace.  Scratch device memory of at least ttt_workspace_size(...) bytes (may be NULL when
@@ -122,19 +122,38 @@ ttt_status ttt_forward_chunked_bidir(ttt_dtype dt, int B, int H, int N, int D, i
  * w_batch_stride: elements between consecutive batch elements' states, 0 or at least H*D*Dh (a
  * multiple of 4); it applies to both w1_0 and w2_0, which hold D*Dh elements per head.
  * w1_out / w2_out (nullable): fp32 [B, H, D, Dh] / [B, H, Dh, D] end states.
- * Operand ranges (bf16 I/O): the products on the W2 side take fp16 operands while, per wave and
- * chunk, the largest |hidden pre-activation| is in [2^-10, sqrt 2] (else the GELU outputs must
- * stay within 32 in magnitude), the largest |(eta/b) residual| is at most 2^15 and the W2
- * state's largest magnitude (checked every 32 chunks) is in [2^-10, 2^15], all-zero values being
- * exact. A (batch, head) chain that leaves these ranges is recomputed by a second kernel with bf16
- * operands (fp32's exponent range); the workspace then holds, as its first B*H ints, 1 for each
- * recomputed chain and 0 for the others.
+ * Sizes: D in {16, 32, 64}, Dh a multiple of 64 in [64, 1024], chunk in {16, 32, 64}. bf16 I/O with
+ * (D, Dh, chunk) = (64, 256, 16) runs on the matrix cores with the state held in registers; every
+ * other size, and fp32 I/O, runs in plain fp32 arithmetic with the state in the workspace.
+ * Operand ranges (bf16 I/O, (D, Dh, chunk) = (64, 256, 16)): the products on the W2 side take
+ * fp16 operands while the hidden pre-activations stay at least 2^-10 in magnitude (per lane of a
+ * wave and chunk, unless all zero) and either within sqrt 2 or with GELU outputs within 32, the W2
+ * state's largest magnitude (checked every 32 chunks and at the end) is in [2^-10, 2^15], and the
+ * state stays finite. A (batch, head) chain that leaves these ranges is recomputed by a second
+ * kernel with bf16 operands (fp32's exponent range); the workspace then holds, as its first B*H
+ * ints, 1 for each recomputed chain and 0 for the others.
+ * Precision: TTT_F32 keeps everything in fp32 (no reduced-precision operands).
  */
 ttt_status ttt_mlp_forward(ttt_dtype dt, int B, int H, int N, int D, int Dh, int chunk, float eta,
                            const void* q, const void* k, const void* v,
                            const float* w1_0, const float* w2_0, long long w_batch_stride,
                            void* o, float* w1_out, float* w2_out,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Depth-wise 3x3 convolution over the token grid, the Conv2d preprocessing applied to a scan's
+ * training data before the scan (Vision-TTT summary on gist.science, "Methodologie" item 2) and
+ * ViT^3's depth-wise branch (ViT^3 review on techloop.online, "TTT Block" section). x and y are
+ * [B, height * width, C] (tokens in raster order, channels contiguous: the [B, N, H, D] layout of
+ * q, k, v with C = H * D) of dtype dt; weight fp32 [C, 3, 3]; bias fp32 [C] or NULL. With zero
+ * padding of one token on each side,
+ *   y[b, i, j, c] = bias[c] + sum_{u, v = 0..2} weight[c, u, v] x[b, i + u - 1, j + v - 1, c]
+ * (cross-correlation, as convolution layers compute it), accumulated in fp32 and rounded to dt.
+ * C must be a multiple of 4 and one image row (width * C elements) at most 2^31 - 1 bytes; x, y and
+ * weight 16-byte aligned, bias 4-byte aligned; y must not overlap x, weight or bias. No workspace.
+ */
+ttt_status ttt_dwconv3x3(ttt_dtype dt, int B, int height, int width, int C, const void* x,
+                         const float* weight, const float* bias, void* y, void* stream);
 
 /*
  * For callers that cannot allocate device memory (code under HIP graph capture, tight serving

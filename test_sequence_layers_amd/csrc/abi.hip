@@ -134,8 +134,8 @@ size_t ttt_workspace_size(ttt_op op, ttt_dtype dt, int B, int H, int N, int D, i
       if (!supported_chunk(chunk) || N % chunk != 0) return 0;
       return round_up(ttt::chunked_workspace_bytes(op == TTT_OP_BIDIR, bf, B, H, N, D, chunk), 256);
     case TTT_OP_MLP:
-      if (chunk <= 0 || N % chunk != 0) return 0;
-      return round_up(ttt::mlp_workspace_bytes(B, H, N, D, Dh, chunk), 256);
+      if (!ttt::mlp_supported(D, Dh, chunk) || N % chunk != 0) return 0;
+      return round_up(ttt::mlp_workspace_bytes(bf, B, H, N, D, Dh, chunk), 256);
   }
   return 0;
 }
@@ -196,7 +196,7 @@ ttt_status ttt_mlp_forward(ttt_dtype dt, int B, int H, int N, int D, int Dh, int
   if (B <= 0 || H <= 0 || N <= 0 || D <= 0 || Dh <= 0 || chunk <= 0) return TTT_ERR_INVALID;
   if (!isfinite(eta)) return TTT_ERR_INVALID;
   if (!q || !k || !v || !w1_0 || !w2_0 || !o) return TTT_ERR_INVALID;
-  if (dt != TTT_BF16 || D != 64 || Dh != 256 || chunk != 16) return TTT_ERR_UNSUPPORTED;
+  if (!ttt::mlp_supported(D, Dh, chunk)) return TTT_ERR_UNSUPPORTED;
   if (N % chunk != 0) return TTT_ERR_INVALID;
   const long long head = (long long)H * D * Dh;
   if (w_batch_stride != 0 && (w_batch_stride < head || w_batch_stride % 4 != 0)) return TTT_ERR_INVALID;
@@ -230,9 +230,30 @@ ttt_status ttt_mlp_forward(ttt_dtype dt, int B, int H, int N, int D, int Dh, int
         overlaps(rws, r1) || overlaps(rws, r2) || overlaps(rws, outs[0]) || overlaps(rws, outs[1]))
       return TTT_ERR_INVALID;
   }
-  return from_hip(ttt::mlp_launch(B, H, N, D, Dh, chunk, eta, q, k, v, w1_0, w2_0,
+  return from_hip(ttt::mlp_launch(dt == TTT_BF16, B, H, N, D, Dh, chunk, eta, q, k, v, w1_0, w2_0,
                                   w_batch_stride, o, w1_out, w2_out, workspace,
                                   static_cast<hipStream_t>(stream)));
+}
+
+ttt_status ttt_dwconv3x3(ttt_dtype dt, int B, int height, int width, int C, const void* x,
+                         const float* weight, const float* bias, void* y, void* stream) {
+  if (dt != TTT_F32 && dt != TTT_BF16) return TTT_ERR_INVALID;
+  if (B <= 0 || height <= 0 || width <= 0 || C <= 0) return TTT_ERR_INVALID;
+  if (!x || !weight || !y) return TTT_ERR_INVALID;
+  if (C % 4 != 0) return TTT_ERR_UNSUPPORTED;
+  // (one image row's bytes must fit the 32-bit range of a buffer resource)
+  if (B > 65535 || height > 65535 || (long long)width * C * elem_size(dt) > 0x7fffffffll)
+    return TTT_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(weight) ||
+      (bias && (reinterpret_cast<uintptr_t>(bias) & 3u)))
+    return TTT_ERR_INVALID;
+  const size_t act = (size_t)B * height * width * C * elem_size(dt);
+  const Range ry = range_of(y, act);
+  if (overlaps(ry, range_of(x, act)) || overlaps(ry, range_of(weight, (size_t)C * 9 * sizeof(float))) ||
+      (bias && overlaps(ry, range_of(bias, (size_t)C * sizeof(float)))))
+    return TTT_ERR_INVALID;
+  return from_hip(ttt::dwconv_launch(dt == TTT_BF16, B, height, width, C, x, weight, bias, y,
+                                     static_cast<hipStream_t>(stream)));
 }
 
 ttt_status ttt_forward_fullbatch_noalloc(ttt_dtype dt, int B, int H, int N, int D, float eta,

@@ -27,10 +27,15 @@ hipError_t chunked_launch(bool bidir, bool bf16_io, int B, int H, int N, int D, 
                           long long w0_bstride, void* o, float* w_out, void* ws, hipStream_t st);
 
 // ---- TTT-MLP --------------------------------------------------------------------------------
-size_t mlp_workspace_bytes(int B, int H, int N, int D, int Dh, int chunk);
-hipError_t mlp_launch(int B, int H, int N, int D, int Dh, int chunk, float eta, const void* q,
-                      const void* k, const void* v, const float* w1, const float* w2,
-                      long long w_bstride, void* o, float* w1_out, float* w2_out, void* ws,
-                      hipStream_t st);
+bool mlp_supported(int D, int Dh, int chunk);
+size_t mlp_workspace_bytes(bool bf16_io, int B, int H, int N, int D, int Dh, int chunk);
+hipError_t mlp_launch(bool bf16_io, int B, int H, int N, int D, int Dh, int chunk, float eta,
+                      const void* q, const void* k, const void* v, const float* w1,
+                      const float* w2, long long w_bstride, void* o, float* w1_out,
+                      float* w2_out, void* ws, hipStream_t st);
+
+// ---- depth-wise 3x3 convolution over the token grid ------------------------------------------
+hipError_t dwconv_launch(bool bf16_io, int B, int Hi, int Wi, int C, const void* x,
+                         const float* w, const float* bias, void* y, hipStream_t st);
 
 }  // namespace ttt

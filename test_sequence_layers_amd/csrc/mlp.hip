@@ -32,12 +32,14 @@
 // on the W2 side (X2, X2q, W2, E and X2q X2^T) take fp16 operands in the first launch: three more
 // mantissa bits than bf16, and the packed fp16 GELU path produces them directly. fp16 covers
 // magnitudes 2^-14 .. 65504 at full precision, so that launch checks, per wave and step, the
-// values it converts: the hidden pre-activations (largest magnitude in [2^-10, sqrt 2] for the
-// polynomial GELU, GELU outputs at most 32 in magnitude otherwise, so that the 32-unit sums of
-// X2q X2^T stay below 32768), the -a E tiles (largest magnitude at most 2^15) and, every 32
-// chunks, the W2 slice (largest magnitude in [2^-10, 2^15]); all-zero tiles are exact. -a E has no
-// lower bound: it only enters as a correction added to a term without it (the W2 update to W2,
-// the read-out's correction to X2q W2, through D1 the W1 update to W1), so its rounding error below
+// values it converts: the hidden pre-activations (each lane's largest magnitude at least 2^-10
+// unless all are zero, and at most sqrt 2 for the polynomial GELU; GELU outputs at most 32 in
+// magnitude otherwise, so that the 32-unit sums of X2q X2^T stay below 32768) and, every 32 chunks
+// and at the end, the W2 slice (largest magnitude in [2^-10, 2^15], or zero). The -a E tiles are
+// not checked in the steps: an fp16 overflow there turns the W2 update and, through D1, the W1
+// update into inf or NaN, which a final check of the whole state catches. Nor do they need a lower
+// bound: -a E only enters as a correction added to a term without it (the W2 update to W2, the
+// read-out's correction to X2q W2, through D1 the W1 update to W1), so its rounding error below
 // fp16's normal range (at most 2^-25 a value) stays negligible beside them when a = eta / b is
 // small, and inputs or weights small enough to make those terms small too fail the other checks.
 // A (batch,
@@ -86,6 +88,8 @@ constexpr float kLog2InvSqrt2Pi = -1.32574806473615935f;   // log2(1 / sqrt(2 pi
 constexpr float kErfP[4] = {1.128350616f, -0.3751908541f, 0.1079747304f, -0.0184600465f};
 constexpr float kInvTwoSqrt2 = 0.35355339059327376220f;
 constexpr float kSqrt2h = 1.4140625f;  // sqrt 2 rounded down to fp16: the fast path's bound on |x|
+constexpr uint32_t kZLoBits = 0x3A800000u;  // float bits of 2^-10
+constexpr uint32_t kZHiBits = 0x3FB50000u;  // float bits of 1.4140625
 constexpr float kR0 = kErfP[0] * kInvTwoSqrt2, kR1 = kErfP[1] * kInvTwoSqrt2 / 2.f,
                 kR2 = kErfP[2] * kInvTwoSqrt2 / 4.f, kR3 = kErfP[3] * kInvTwoSqrt2 / 8.f;
 
@@ -339,9 +343,12 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
         if constexpr (rd) zm = fmaxf(zm, absmax4(Z1q[n]));
         if constexpr (fwd) zm = fmaxf(zm, absmax4(Z1[n]));
       }
-      // Below 2^-10 the GELU outputs would sit near fp16's subnormal range.
-      bad |= __any(zm > 0.f) && !__any(zm >= 0x1p-10f);
-      if (!__any(!(zm <= kSqrt2h))) {
+      // Polynomial path when every lane's largest |pre-activation| is in [2^-10, sqrt 2]: one
+      // unsigned compare of the float bits (monotonic for non-negative floats; NaN fails it).
+      // Below 2^-10 the GELU outputs would sit near fp16's subnormal range, so the other path
+      // flags such lanes (all-zero lanes are exact).
+      const bool poly = __float_as_uint(zm) - kZLoBits <= kZHiBits - kZLoBits;
+      if (!__any(!poly)) {
         for (int n = 0; n < kNh; ++n) {
           if constexpr (rd) {
             const f16x4 zq = to_f16x4(Z1q[n]), tq = zq * zq;
@@ -357,7 +364,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
         float xm = 0.f;
         gelu_lib(x2qh, x2b, gph, xm);
         // |X2|, |X2q| <= 32 keeps them and the 32-unit sums of X2q X2^T inside fp16.
-        bad |= __any(!(xm <= 32.f));
+        bad |= __any(!(xm <= 32.f)) || __any(zm > 0.f && zm < 0x1p-10f);
       }
     } else {
       float xm = 0.f;
@@ -416,7 +423,6 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
       for (int ww = 1; ww < kWaves; ++ww) s = s + pt[ww];
       f32x4 e;
       for (int j = 0; j < 4; ++j) e[j] = a * ((float)vv[j] - s[j]);
-      if constexpr (F16) bad |= __any(!(absmax4(e) <= 0x1p15f));
       *reinterpret_cast<x4*>(&sEc[r * kP + 16 * w + 4 * g]) = S::cvt(e);
     }
     if (rd && w >= 4) {  // O^T tile of chunk c - 1 = sum of the waves' shares
@@ -494,23 +500,197 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
         for (int j = 0; j < 4; ++j) dst[(hid0 + 16 * n + 4 * g + j) * kD + 16 * o2 + r] = W2t[n][o2][j];
   }
   if constexpr (F16) {
+    // The state must have stayed finite and W2 in range: an fp16 overflow of a -a E tile (whose
+    // values the steps do not check) reaches W2 through its update and W1 through D1 as inf or NaN.
+    float sm = 0.f, wm = 0.f;
+    for (int m = 0; m < 4; ++m)
+      for (int n = 0; n < kNh; ++n) {
+        sm = fmaxf(sm, absmax4(W1t[m][n]));
+        sm = fmaxf(sm, absmax4(W2x[m][n]));
+        wm = fmaxf(wm, absmax4(W2t[n][m]));
+      }
+    bad |= wave_out_of_range(wm, 0x1p-10f, 0x1p15f) || __any(!(sm <= 3.0e38f));
     if (bad && l == 0) sBad = 1;  // (every writer stores the same value)
     __syncthreads();
     if (threadIdx.x == 0) flags[bh] = sBad;
   }
 }
 
+
+// ---------------------------------------------------------------- any size, fp32 arithmetic
+// The same layer for every other supported size (D in {16, 32, 64}, Dh a multiple of 64 up to
+// 1024, b in {16, 32, 64}) and for fp32 I/O, in plain fp32 FMA arithmetic (the exact erf GELU of
+// the C library), one workgroup per (batch, head). Each chunk is computed from its start state
+// (W1, W2) in the dual form of the per-token read-out:
+//   Z1 = K W1, X2 = GELU(Z1), E = X2 W2 - V, D1 = (E W2^T) * GELU'(Z1)
+//   Z1q = Q W1 - a tril(Q K^T) D1, X2q = GELU(Z1q), O = X2q W2 - a tril(X2q X2^T) E
+//   W1 -= a K^T D1, W2 -= a X2^T E
+// (tril keeps j <= i, so token i sees the gradients of tokens j <= i). The state and the
+// [b, Dh] intermediates live in the workspace (per chain 2 D Dh + 4 b Dh floats), the chunk's
+// K, V, Q, E and the two masked b x b products in LDS.
+constexpr int kGenThreads = 256;
+constexpr int kGenMaxD = 64, kGenMaxCh = 64;
+
+__device__ __forceinline__ float gelu_f32(float x) { return x * cdf_lib(x); }
+__device__ __forceinline__ float gelu_prime_f32(float x) {
+  return cdf_lib(x) + x * expf(-0.5f * x * x) * 0.39894228040143267794f;  // Phi(x) + x phi(x)
+}
+template <class T>
+__device__ __forceinline__ float load_io(const T* p) { return (float)*p; }
+template <class T>
+__device__ __forceinline__ void store_io(T* p, float v) { *p = (T)v; }
+
+template <class T>
+__global__ __launch_bounds__(kGenThreads) void mlp_fwd_generic(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const float* __restrict__ w1, const float* __restrict__ w2, long long wbs, int H, int N, int D,
+    int Dh, int CH, float a, T* __restrict__ o, float* __restrict__ w1_out,
+    float* __restrict__ w2_out, float* __restrict__ ws) {
+  __shared__ float sK[kGenMaxCh][kGenMaxD + 1], sV[kGenMaxCh][kGenMaxD + 1], sQ[kGenMaxCh][kGenMaxD + 1];
+  __shared__ float sE[kGenMaxCh][kGenMaxD + 1];
+  __shared__ float sM[kGenMaxCh][kGenMaxCh + 1], sN2[kGenMaxCh][kGenMaxCh + 1];
+  const int bh = blockIdx.x, b = bh / H, h = bh % H, tid = threadIdx.x;
+  const long long DDh = (long long)D * Dh, BDh = (long long)CH * Dh;
+  float* W1 = ws + (long long)bh * (2 * DDh + 4 * BDh);
+  float* W2 = W1 + DDh;
+  float* Z1 = W2 + DDh;  // then Z1q / X2q
+  float* X2 = Z1 + BDh;
+  float* GP = X2 + BDh;
+  float* D1 = GP + BDh;
+  const float* W1g = w1 + b * wbs + (long long)h * DDh;
+  const float* W2g = w2 + b * wbs + (long long)h * DDh;
+  for (long long e = tid; e < DDh; e += kGenThreads) {
+    W1[e] = W1g[e];
+    W2[e] = W2g[e];
+  }
+  const long long ts = (long long)H * D;
+  const long long head0 = (long long)b * N * ts + (long long)h * D;
+  __syncthreads();
+  for (int c0 = 0; c0 < N; c0 += CH) {
+    for (int e = tid; e < CH * D; e += kGenThreads) {
+      const int t = e / D, f = e % D;
+      const long long off = head0 + (long long)(c0 + t) * ts + f;
+      sK[t][f] = load_io(k + off);
+      sV[t][f] = load_io(v + off);
+      sQ[t][f] = load_io(q + off);
+    }
+    __syncthreads();
+    // Z1 = K W1, X2 = GELU(Z1), GP = GELU'(Z1); M = tril(Q K^T)
+    for (long long e = tid; e < BDh; e += kGenThreads) {
+      const int t = (int)(e / Dh), j = (int)(e % Dh);
+      float z = 0.f;
+      for (int f = 0; f < D; ++f) z = fmaf(sK[t][f], W1[(long long)f * Dh + j], z);
+      X2[e] = gelu_f32(z);
+      GP[e] = gelu_prime_f32(z);
+    }
+    for (int e = tid; e < CH * CH; e += kGenThreads) {
+      const int i = e / CH, j = e % CH;
+      float m = 0.f;
+      if (j <= i)
+        for (int f = 0; f < D; ++f) m = fmaf(sQ[i][f], sK[j][f], m);
+      sM[i][j] = m;
+    }
+    __syncthreads();
+    // E = X2 W2 - V
+    for (int e = tid; e < CH * D; e += kGenThreads) {
+      const int t = e / D, f = e % D;
+      float z = -sV[t][f];
+      for (int j = 0; j < Dh; ++j) z = fmaf(X2[(long long)t * Dh + j], W2[(long long)j * D + f], z);
+      sE[t][f] = z;
+    }
+    __syncthreads();
+    // D1 = (E W2^T) * GP
+    for (long long e = tid; e < BDh; e += kGenThreads) {
+      const int t = (int)(e / Dh), j = (int)(e % Dh);
+      float g = 0.f;
+      for (int f = 0; f < D; ++f) g = fmaf(sE[t][f], W2[(long long)j * D + f], g);
+      D1[e] = g * GP[e];
+    }
+    __syncthreads();
+    // Z1q = Q W1 - a M D1, X2q = GELU(Z1q) (into Z1)
+    for (long long e = tid; e < BDh; e += kGenThreads) {
+      const int t = (int)(e / Dh), j = (int)(e % Dh);
+      float z = 0.f, corr = 0.f;
+      for (int f = 0; f < D; ++f) z = fmaf(sQ[t][f], W1[(long long)f * Dh + j], z);
+      for (int u = 0; u <= t; ++u) corr = fmaf(sM[t][u], D1[(long long)u * Dh + j], corr);
+      Z1[e] = gelu_f32(fmaf(-a, corr, z));
+    }
+    __syncthreads();
+    // N2 = tril(X2q X2^T)
+    for (int e = tid; e < CH * CH; e += kGenThreads) {
+      const int i = e / CH, j = e % CH;
+      float m = 0.f;
+      if (j <= i)
+        for (int u = 0; u < Dh; ++u) m = fmaf(Z1[(long long)i * Dh + u], X2[(long long)j * Dh + u], m);
+      sN2[i][j] = m;
+    }
+    __syncthreads();
+    // O = X2q W2 - a N2 E
+    for (int e = tid; e < CH * D; e += kGenThreads) {
+      const int t = e / D, f = e % D;
+      float z = 0.f, corr = 0.f;
+      for (int j = 0; j < Dh; ++j) z = fmaf(Z1[(long long)t * Dh + j], W2[(long long)j * D + f], z);
+      for (int u = 0; u <= t; ++u) corr = fmaf(sN2[t][u], sE[u][f], corr);
+      store_io(o + head0 + (long long)(c0 + t) * ts + f, fmaf(-a, corr, z));
+    }
+    // W1 -= a K^T D1, W2 -= a X2^T E (the read-out above used the start state)
+    __syncthreads();
+    for (long long e = tid; e < DDh; e += kGenThreads) {
+      const int f = (int)(e / Dh), j = (int)(e % Dh);
+      float g = 0.f;
+      for (int t = 0; t < CH; ++t) g = fmaf(sK[t][f], D1[(long long)t * Dh + j], g);
+      W1[e] = fmaf(-a, g, W1[e]);
+    }
+    for (long long e = tid; e < DDh; e += kGenThreads) {
+      const int j = (int)(e / D), f = (int)(e % D);
+      float g = 0.f;
+      for (int t = 0; t < CH; ++t) g = fmaf(X2[(long long)t * Dh + j], sE[t][f], g);
+      W2[e] = fmaf(-a, g, W2[e]);
+    }
+    __syncthreads();
+  }
+  if (w1_out)
+    for (long long e = tid; e < DDh; e += kGenThreads) w1_out[(long long)bh * DDh + e] = W1[e];
+  if (w2_out)
+    for (long long e = tid; e < DDh; e += kGenThreads) w2_out[(long long)bh * DDh + e] = W2[e];
+}
+
 }  // namespace
 
-// One flag per (batch, head) chain.
-size_t mlp_workspace_bytes(int B, int H, int, int, int, int) { return (size_t)B * H * sizeof(int); }
+bool mlp_fast_path(bool bf16_io, int D, int Dh, int chunk) {
+  return bf16_io && D == kD && Dh == kDh && chunk == kCh;
+}
 
-hipError_t mlp_launch(int B, int H, int N, int D, int Dh, int chunk, float eta, const void* q,
-                      const void* k, const void* v, const float* w1, const float* w2,
-                      long long wbs, void* o, float* w1_out, float* w2_out, void* ws, hipStream_t st) {
-  if (D != kD || Dh != kDh || chunk != kCh) return hipErrorInvalidValue;
-  int* flags = static_cast<int*>(ws);
+bool mlp_supported(int D, int Dh, int chunk) {
+  if (D != 16 && D != 32 && D != 64) return false;
+  if (chunk != 16 && chunk != 32 && chunk != 64) return false;
+  return Dh >= 64 && Dh <= 1024 && Dh % 64 == 0;
+}
+
+// Fast path: one flag per (batch, head) chain. Otherwise the state and intermediates per chain.
+size_t mlp_workspace_bytes(bool bf16_io, int B, int H, int, int D, int Dh, int chunk) {
+  if (mlp_fast_path(bf16_io, D, Dh, chunk)) return (size_t)B * H * sizeof(int);
+  return (size_t)B * H * (2 * (size_t)D * Dh + 4 * (size_t)chunk * Dh) * sizeof(float);
+}
+
+hipError_t mlp_launch(bool bf16_io, int B, int H, int N, int D, int Dh, int chunk, float eta,
+                      const void* q, const void* k, const void* v, const float* w1,
+                      const float* w2, long long wbs, void* o, float* w1_out, float* w2_out,
+                      void* ws, hipStream_t st) {
   const float a = eta / (float)chunk;
+  if (!mlp_fast_path(bf16_io, D, Dh, chunk)) {
+    if (!mlp_supported(D, Dh, chunk)) return hipErrorInvalidValue;
+    if (bf16_io)
+      hipLaunchKernelGGL(mlp_fwd_generic<bf16>, dim3(B * H), dim3(kGenThreads), 0, st, (const bf16*)q,
+                         (const bf16*)k, (const bf16*)v, w1, w2, wbs, H, N, D, Dh, chunk, a, (bf16*)o,
+                         w1_out, w2_out, static_cast<float*>(ws));
+    else
+      hipLaunchKernelGGL(mlp_fwd_generic<float>, dim3(B * H), dim3(kGenThreads), 0, st, (const float*)q,
+                         (const float*)k, (const float*)v, w1, w2, wbs, H, N, D, Dh, chunk, a, (float*)o,
+                         w1_out, w2_out, static_cast<float*>(ws));
+    return hipGetLastError();
+  }
+  int* flags = static_cast<int*>(ws);
   hipLaunchKernelGGL(mlp_fwd_bf16<true>, dim3(B * H), dim3(kWaves * 64), 0, st, (const bf16*)q,
                      (const bf16*)k, (const bf16*)v, w1, w2, wbs, H, N, a, (bf16*)o, w1_out, w2_out,
                      flags);

@@ -30,6 +30,7 @@ SIGNATURES = {
                                  _vp, _vp, _c_ll, _vp, _vp, _vp, _vp, _sz, _vp]),
     "ttt_forward_fullbatch_noalloc": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _vp, _vp, _vp, _vp,
                                                _c_ll, _vp, _vp, _vp]),
+    "ttt_dwconv3x3": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp]),
     "ttt_workspace_size": (_sz, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
     "ttt_status_string": (ctypes.c_char_p, [_c_int]),
 }
@@ -250,3 +251,29 @@ def ttt_mlp_forward(q, k, v, w1, w2, chunk: int, eta: float = 1.0, *, o=None, w1
                                  _stream(stream, dev))
     _raise(st, "ttt_mlp_forward")
     return o
+
+
+def ttt_dwconv3x3(x, weight, bias=None, *, height: int, width: int, y=None, stream=None):
+    """Depth-wise 3x3 convolution over the token grid. x: [B, height * width, C] or [B, N, H, D]
+    (then C = H * D) bf16 or fp32; weight fp32 [C, 3, 3]; bias fp32 [C] or None. Returns y (x's shape)."""
+    lib = load_library()
+    torch = _torch()
+    if not isinstance(x, torch.Tensor) or not x.is_cuda:
+        raise TypeError("x must be a CUDA (HIP) tensor")
+    dev = x.device
+    dt = _dtype_code(x)
+    if x.dim() not in (3, 4) or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [B, N, C] or [B, N, H, D] tensor")
+    B, N = int(x.shape[0]), int(x.shape[1])
+    C = int(x.numel() // max(B * N, 1))
+    if N != height * width:
+        raise ValueError(f"{N} tokens are not a {height} x {width} grid")
+    _check_tensor("weight", weight, (C, 3, 3), torch.float32, dev)
+    _check_out("bias", bias, (C,), torch.float32, dev)
+    _check_out("y", y, x.shape, x.dtype, dev)
+    with torch.cuda.device(dev):
+        y = torch.empty_like(x) if y is None else y
+        st = lib.ttt_dwconv3x3(dt, B, int(height), int(width), C, _ptr(x), _ptr(weight), _ptr(bias), _ptr(y),
+                               _stream(stream, dev))
+    _raise(st, "ttt_dwconv3x3")
+    return y

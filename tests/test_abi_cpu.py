@@ -19,13 +19,29 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _declared_functions():
     src = open(os.path.join(ROOT, "include", "ttt.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(ttt_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(ttt_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_header_declares_the_entry_points():
     assert _declared_functions() == sorted([
         "ttt_forward_fullbatch", "ttt_forward_chunked_causal", "ttt_forward_chunked_bidir", "ttt_mlp_forward",
-        "ttt_workspace_size", "ttt_status_string", "ttt_forward_fullbatch_noalloc"])
+        "ttt_workspace_size", "ttt_status_string", "ttt_forward_fullbatch_noalloc", "ttt_dwconv3x3"])
+
+
+def test_dwconv_validation_rejects_before_launch():
+    lib = T.load_library()
+    call = lambda dt=T.TTT_BF16, B=1, Hi=4, Wi=4, C=64, x=0, w=1, b=2, y=3: lib.ttt_dwconv3x3(  # noqa: E731
+        dt, B, Hi, Wi, C, None if x is None else _p(x), None if w is None else _p(w), None if b is None else _p(b),
+        None if y is None else _p(y), None)
+    assert call(x=None) == 1
+    assert call(y=None) == 1
+    assert call(w=None) == 1
+    assert call(B=0) == 1
+    assert call(dt=5) == 1
+    assert call(C=62) == 2               # channels not a multiple of 4
+    assert call(y=0) == 1                # output overlaps the input
+    st = lib.ttt_dwconv3x3(T.TTT_BF16, 1, 4, 4, 64, ctypes.c_void_p(FAKE + 8), _p(1), None, _p(3), None)
+    assert st == 1                       # misaligned input
 
 
 def test_noalloc_rejects_calls_beyond_its_scratch_before_any_device_call():
@@ -144,10 +160,17 @@ def test_mlp_validation():
         dt, 2, 1, N, D, Dh, chunk, 1.0, _p(0), _p(1), _p(2), _p(3), _p(6), wbs,
         None if o is None else _p(o), None, None, None, 0, None)
     assert call(o=None) == 1
-    assert call(dt=T.TTT_F32) == 2
-    assert call(D=32) == 2
-    assert call(Dh=128) == 2
-    assert call(chunk=32) == 2
+    # supported sizes and dtypes get as far as the (missing) workspace
+    assert call() == 3
+    assert call(dt=T.TTT_F32) == 3
+    assert call(D=32) == 3
+    assert call(Dh=128) == 3
+    assert call(Dh=1024) == 3
+    assert call(chunk=32, N=64) == 3
+    assert call(D=48) == 2
+    assert call(Dh=100) == 2
+    assert call(Dh=2048) == 2
+    assert call(chunk=8) == 2
     assert call(N=40) == 1
     assert call(o=0) == 1                 # output aliases q
     assert call(wbs=100) == 1             # batch stride below one batch of states

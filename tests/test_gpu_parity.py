@@ -127,6 +127,14 @@ SMALL = [
     # odd chunk counts: the two-step loop body runs and the last step is peeled
     W["ttt_mlp_causal_8k"].with_(B=1, N=48, H=2, seed=53),
     W["ttt_mlp_causal_8k"].with_(B=1, N=80, H=3, seed=54),
+    # TTT-MLP sizes and dtypes outside the matrix-core path (plain fp32 arithmetic)
+    W["ttt_mlp_causal_8k"].with_(B=1, N=64, H=2, dtype="fp32", seed=55),
+    W["ttt_mlp_causal_8k"].with_(B=2, N=96, H=1, chunk=32, dtype="fp32", seed=56),
+    W["ttt_mlp_causal_8k"].with_(B=1, N=128, H=2, chunk=64, dtype="fp32", seed=57),
+    W["ttt_mlp_causal_8k"].with_(B=1, N=128, H=2, chunk=64, seed=58),
+    W["ttt_mlp_causal_8k"].with_(B=1, N=96, H=3, D=32, Dh=128, chunk=32, seed=59),
+    W["ttt_mlp_causal_8k"].with_(B=1, N=64, H=2, D=16, Dh=512, chunk=16, dtype="fp32", seed=60),
+    W["ttt_mlp_causal_8k"].with_(B=1, N=64, H=2, Dh=1024, chunk=16, seed=61),
 ]
 
 # Chunked cases long enough to be split into several segments (compose + prefix + rescan),
@@ -262,13 +270,17 @@ def test_fullbatch_split_plans(wl):
     assert np.abs(st[0] - ref_w).max() / np.abs(ref_w).max() <= BF16_TOL
 
 
-def test_mlp_end_states():
-    wl = W["ttt_mlp_causal_8k"].with_(B=1, N=64, H=2, seed=64)
+@pytest.mark.parametrize("wl", [W["ttt_mlp_causal_8k"].with_(B=1, N=64, H=2, seed=64),
+                                W["ttt_mlp_causal_8k"].with_(B=2, N=64, H=2, chunk=32, dtype="fp32", seed=69),
+                                W["ttt_mlp_causal_8k"].with_(B=1, N=64, H=1, D=32, Dh=192, dtype="fp32", seed=70)],
+                         ids=lambda w: f"{w.dtype}-D{w.D}Dh{w.Dh}c{w.chunk}")
+def test_mlp_end_states(wl):
+    print(f"mlp end states {wl.dtype} D={wl.D} Dh={wl.Dh} b={wl.chunk}", flush=True)
     x = synth.make_inputs(wl)
     _, s1, s2 = run_gpu(x, want_state=True)
     _, r1, r2 = oracle_full(x)
-    assert np.abs(s1 - r1).max() / np.abs(r1).max() <= BF16_TOL
-    assert np.abs(s2 - r2).max() / np.abs(r2).max() <= BF16_TOL
+    assert np.abs(s1 - r1).max() / np.abs(r1).max() <= tol(wl)
+    assert np.abs(s2 - r2).max() / np.abs(r2).max() <= tol(wl)
 
 
 def test_mlp_activations_beyond_fp16_products():
