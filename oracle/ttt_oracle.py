@@ -31,7 +31,8 @@ widened to float64 here); inner states are [H, ...] (shared over the batch) or
 
 Parity status: every function here is pinned by tests/test_oracle_pins.py
 (closed forms, special cases, finite differences, autograd, exact rational
-arithmetic). None is "parity unpinned".
+arithmetic) and tests/test_oracle_pins_epochs.py (fullbatch_epochs: closed form
+with orthogonal keys, convergence to least squares). None is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -92,6 +93,25 @@ def fullbatch(q, k, v, w0, eta: float):
     E = K @ W0 - V                       # residuals f_W0(k_j) - v_j, one row per token
     G = _t(K) @ E                        # sum_j of per-token gradients k_j^T e_j
     W = W0 - (eta / N) * G
+    return _bnhd(Q @ W), W
+
+
+def fullbatch_epochs(q, k, v, w0, eta: float, epochs: int):
+    """Several full-batch epochs of the inner training before the read-out.
+
+    ViT^3 review (techloop.online), design-space study: how many epochs one inner update runs is
+    one of the studied choices (single epoch is the one the final models keep). Epoch e takes one
+    full-batch gradient step from the previous epoch's weights:
+        W_{e+1} = W_e - (eta/N) K^T (K W_e - V),   W_0 = W0,   O = Q W_epochs.
+    Returns (O [B,N,H,D], W_epochs [B,H,D,D]).
+    """
+    if epochs < 1:
+        raise ValueError("at least one epoch")
+    Q, K, V = _bhnd(q), _bhnd(k), _bhnd(v)
+    B, H, N, _ = Q.shape
+    W = _state(w0, B, H)
+    for _ in range(epochs):
+        W = W - (eta / N) * (_t(K) @ (K @ W - V))
     return _bnhd(Q @ W), W
 
 
