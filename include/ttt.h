@@ -84,6 +84,20 @@ ttt_status ttt_forward_fullbatch(ttt_dtype dt, int B, int H, int N, int D, float
                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Several full-batch epochs before the read-out (ViT^3 review on techloop.online, design-space
+ * study: how many epochs one inner update runs). Per (b, h), from W_0 = W0:
+ *   W_{e+1} = W_e - (eta/N) K^T (K W_e - V)   for e < epochs,   O = Q W_epochs.
+ * epochs = 1 is ttt_forward_fullbatch. The epochs reuse the one pass over K and V (K^T K and K^T V
+ * are summed once), so their cost is a few d x d products per (b, h). epochs < 1 is
+ * TTT_ERR_INVALID, above 256 TTT_ERR_UNSUPPORTED. Workspace as for ttt_forward_fullbatch.
+ */
+ttt_status ttt_forward_fullbatch_epochs(ttt_dtype dt, int B, int H, int N, int D, int epochs,
+                                        float eta, const void* q, const void* k, const void* v,
+                                        const float* w0, long long w0_batch_stride,
+                                        void* o, float* w_out,
+                                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Causal mini-batch TTT-Linear (TTT-Linear / TTT-MLP abstract; mini-batches of b = chunk tokens,
  * Vision-TTT summary "Methodologie" item 3). Per (b, h), for consecutive chunks c of b tokens
  * with start state W_s:

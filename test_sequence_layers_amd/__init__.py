@@ -1,7 +1,8 @@
 """MI355X-native TTT-layer forward library (HIP kernels for gfx950 behind a C ABI).
 
 The entry points mirror include/ttt.h: ttt_forward_fullbatch, ttt_forward_chunked_causal,
-ttt_forward_chunked_bidir, ttt_mlp_forward, ttt_workspace_size, and ttt_forward_fullbatch_noalloc
+ttt_forward_chunked_bidir, ttt_mlp_forward, ttt_workspace_size, ttt_forward_fullbatch_epochs
+(several full-batch epochs), and ttt_forward_fullbatch_noalloc
 (full-batch with the library's static scratch instead of a workspace, for callers that cannot
 allocate), and ttt_dwconv3x3 (the depth-wise 3x3 convolution over the token grid that precedes a
 scan or runs beside it).
@@ -9,4 +10,4 @@ scan or runs beside it).
 from .ttt import (  # noqa: F401
     TTT_BF16, TTT_F32, TTT_NOALLOC_SCRATCH_BYTES, TTT_OP_BIDIR, TTT_OP_CAUSAL, TTT_OP_FULLBATCH, TTT_OP_MLP,
     TTTError, load_library, status_string, ttt_forward_chunked_bidir, ttt_forward_chunked_causal,
-    ttt_dwconv3x3, ttt_forward_fullbatch, ttt_forward_fullbatch_noalloc, ttt_mlp_forward, ttt_workspace_size)
+    ttt_dwconv3x3, ttt_forward_fullbatch, ttt_forward_fullbatch_epochs, ttt_forward_fullbatch_noalloc, ttt_mlp_forward, ttt_workspace_size)

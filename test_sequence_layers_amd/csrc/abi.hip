@@ -155,11 +155,23 @@ ttt_status ttt_forward_fullbatch(ttt_dtype dt, int B, int H, int N, int D, float
                                  const void* q, const void* k, const void* v, const float* w0,
                                  long long w0_batch_stride, void* o, float* w_out,
                                  void* workspace, size_t workspace_bytes, void* stream) {
+  return ttt_forward_fullbatch_epochs(dt, B, H, N, D, 1, eta, q, k, v, w0, w0_batch_stride, o,
+                                      w_out, workspace, workspace_bytes, stream);
+}
+
+ttt_status ttt_forward_fullbatch_epochs(ttt_dtype dt, int B, int H, int N, int D, int epochs,
+                                        float eta, const void* q, const void* k, const void* v,
+                                        const float* w0, long long w0_batch_stride, void* o,
+                                        float* w_out, void* workspace, size_t workspace_bytes,
+                                        void* stream) {
   const ttt_status st = check_linear(TTT_OP_FULLBATCH, dt, B, H, N, D, 0, eta, q, k, v, w0,
                                      w0_batch_stride, o, w_out, workspace, workspace_bytes);
   if (st != TTT_OK) return st;
-  return from_hip(ttt::fb_launch(dt == TTT_BF16, B, H, N, D, eta, q, k, v, w0, w0_batch_stride,
-                                 o, w_out, workspace, static_cast<hipStream_t>(stream)));
+  if (epochs < 1) return TTT_ERR_INVALID;
+  if (epochs > 256) return TTT_ERR_UNSUPPORTED;
+  return from_hip(ttt::fb_launch(dt == TTT_BF16, B, H, N, D, epochs, eta, q, k, v, w0,
+                                 w0_batch_stride, o, w_out, workspace,
+                                 static_cast<hipStream_t>(stream)));
 }
 
 ttt_status ttt_forward_chunked_causal(ttt_dtype dt, int B, int H, int N, int D, int chunk,
@@ -267,8 +279,8 @@ ttt_status ttt_forward_fullbatch_noalloc(ttt_dtype dt, int B, int H, int N, int 
   if (need > (size_t)TTT_NOALLOC_SCRATCH_BYTES) return TTT_ERR_WORKSPACE;
   void* ws = scratch_of_current_device();
   if (!ws) return TTT_ERR_HIP;
-  return from_hip(ttt::fb_launch(dt == TTT_BF16, B, H, N, D, eta, q, k, v, w0, w0_batch_stride,
-                                 o, w_out, ws, static_cast<hipStream_t>(stream)));
+  return from_hip(ttt::fb_launch(dt == TTT_BF16, B, H, N, D, 1, eta, q, k, v, w0,
+                                 w0_batch_stride, o, w_out, ws, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

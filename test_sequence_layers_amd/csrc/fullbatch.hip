@@ -17,7 +17,12 @@
 // HBM traffic is the algorithmic Q, K, V read plus the O write; the split records are two d x d
 // fp32 matrices per split and stay in L2 / Infinity Cache.
 //
-// fp32 I/O: three plain-FMA launches (partial gradients, fixed-order reduction, read-out).
+// fp32 I/O: three plain-FMA launches (the splits' K^T K and K^T V, a fixed-order reduction that
+// also runs the epochs, read-out).
+//
+// Several epochs (ViT^3 review, design-space study: epochs per inner update) reuse the same sums:
+// epoch e takes W_{e+1} = W_e - (eta/N) ((K^T K) W_e - K^T V), a few small products per (b, h)
+// in the read-out kernel, with no further pass over K and V.
 #include <type_traits>
 
 #include "device.hpp"
@@ -90,14 +95,16 @@ __device__ __forceinline__ int wstar_operand_offset(int hl, int row, int col) {
          row % E;
 }
 
-// Row block m of W* = W0 - scale ((K^T K) W0 - K^T V) for head hl of a group, from the summed
-// accumulator tiles acc[0 .. NT) = (c, m) of K^T K and acc[NT .. 2NT) = (m, n) of K^T V. By
-// symmetry, tile (c, m) of K^T K in accumulator layout is the A operand of rows 16m.. and k block
-// c. (The 16x16x16 products keep their own accumulators: they must not take a 16x16x32 result as
-// their accumulator input.) Writes the read-out operands and, if w_out is set, W* in fp32.
+// Row block m of W1 = W0 - scale ((K^T K) W0 - K^T V) for head hl of a group (one epoch from W0),
+// from the summed accumulator tiles acc[0 .. NT) = (c, m) of K^T K and acc[NT .. 2NT) = (m, n) of
+// K^T V. By symmetry, tile (c, m) of K^T K in accumulator layout is the A operand of rows 16m..
+// and k block c. (The 16x16x16 products keep their own accumulators: they must not take a
+// 16x16x32 result as their accumulator input.) Writes, where set, the read-out operands, W1 in
+// fp32 to w_out and W1 in fp32 to wnext (the next epoch's W0, same layout as W0).
 template <int D>
 __device__ __forceinline__ void wstar_rows(const f32x4* acc, int hl, int m, const float* W0,
-                                           float scale, bf16* wop_grp, float* w_out, int r, int g) {
+                                           float scale, bf16* wop_grp, float* w_out, float* wnext,
+                                           int r, int g) {
   constexpr int NT = D / 16;
   bf16x4 ka[NT];
   for (int c = 0; c < NT; ++c) ka[c] = to_bf16x4(acc[c]);
@@ -111,8 +118,9 @@ __device__ __forceinline__ void wstar_rows(const f32x4* acc, int hl, int m, cons
     for (int j = 0; j < 4; ++j) {  // W*[16m + 4g + j][16n + r]
       const int row = 16 * m + 4 * g + j, col = 16 * n + r;
       const float wv = W0[row * D + col] - scale * (gw[j] - acc[NT + n][j]);
-      wop_grp[wstar_operand_offset<D>(hl, row, col)] = (bf16)wv;
+      if (wop_grp) wop_grp[wstar_operand_offset<D>(hl, row, col)] = (bf16)wv;
       if (w_out) w_out[row * D + col] = wv;
+      if (wnext) wnext[row * D + col] = wv;
     }
   }
 }
@@ -246,8 +254,8 @@ constexpr int kReadSets = 4;
 template <int D, int HG>
 __global__ __launch_bounds__(kThreads) void fb_readout_bf16(
     const bf16* __restrict__ q, const float* __restrict__ partial, const float* __restrict__ w0,
-    long long w0_bstride, int H, int N, int S, int tps, float scale, bf16* __restrict__ o,
-    float* __restrict__ w_out) {
+    long long w0_bstride, int H, int N, int S, int tps, float scale, int epochs,
+    bf16* __restrict__ o, float* __restrict__ w_out) {
   using G = Geo<D, HG>;
   constexpr int NT = D / 16, E = kOpElems<D>, KS = D / (4 * E);
   constexpr long long DD = (long long)D * D;
@@ -258,6 +266,7 @@ __global__ __launch_bounds__(kThreads) void fb_readout_bf16(
   __shared__ __align__(16) bf16 sQ[4][16 * G::P];
   __shared__ __align__(16) bf16 sO[4][16 * G::P];
   __shared__ __align__(16) float sW0[HG * D * D];
+  __shared__ __align__(16) float sW1[HG * D * D];  // the other epoch buffer
   __shared__ __align__(16) bf16 sWop[HG * D * D];
   __shared__ f32x4 sSum[(4 - TASKS) > 0 ? (4 - TASKS) : 1][T2][64];
   const int item = xcd_item(blockIdx.x, gridDim.x);
@@ -321,14 +330,26 @@ __global__ __launch_bounds__(kThreads) void fb_readout_bf16(
         for (int t = 0; t < T2; ++t) sSum[w - TASKS][t][l] = acc[t];
     }
     __syncthreads();
-    if (tw == 0) {
-      if constexpr (WPT > 1)
+    if constexpr (WPT > 1) {
+      if (tw == 0)
         for (int u = 1; u < WPT; ++u)
           for (int t = 0; t < T2; ++t) acc[t] += sSum[(u - 1) * TASKS + task][t][l];
-      wstar_rows<D>(acc, hl, m, sW0 + hl * DD, scale, sWop,
-                    (w_out && s == 0) ? w_out + ((long long)b * H + h0 + hl) * DD : nullptr, r, g);
     }
-    __syncthreads();
+    // Epoch e: W_{e+1} = W_e - scale ((K^T K) W_e - K^T V), between the two LDS buffers; the last
+    // epoch writes the read-out operands (and w_out, from split 0's workgroup).
+    float* wcur = sW0;
+    float* wnxt = sW1;
+    for (int e = 0; e < epochs; ++e) {
+      const bool last = e + 1 == epochs;
+      if (tw == 0)
+        wstar_rows<D>(acc, hl, m, wcur + hl * DD, scale, last ? sWop : nullptr,
+                      (last && w_out && s == 0) ? w_out + ((long long)b * H + h0 + hl) * DD : nullptr,
+                      last ? nullptr : wnxt + hl * DD, r, g);
+      __syncthreads();
+      float* t = wcur;
+      wcur = wnxt;
+      wnxt = t;
+    }
   }
   using Op = typename std::conditional<(D >= 32), bf16x8, bf16x4>::type;
   Op wa[HG][NT][KS];  // A operands W*^T
@@ -371,22 +392,19 @@ __global__ __launch_bounds__(kThreads) void fb_readout_bf16(
 }
 
 // ---------------------------------------------------------------- fp32 I/O, plain FMA
+// Per (b, h, split): the split's K^T K and K^T V (plain fp32 FMA), as in the bf16 path.
 template <int D>
 __global__ __launch_bounds__(kThreads) void fb_partial_f32(const float* __restrict__ k,
-                                                           const float* __restrict__ v,
-                                                           const float* __restrict__ w0,
-                                                           long long w0_bstride, int H, int N,
-                                                           int tps, int S,
+                                                           const float* __restrict__ v, int H,
+                                                           int N, int tps, int S,
                                                            float* __restrict__ partial) {
-  __shared__ float sK[kTileF][D + 1], sE[kTileF][D + 1], sW[D][D + 1];
+  __shared__ float sK[kTileF][D + 1], sV[kTileF][D + 1];
   constexpr int PER = (D * D + kThreads - 1) / kThreads;
   const int s = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H;
   const int n0 = s * tps, n1 = min(N, n0 + tps);
   const long long ts = (long long)H * D;
-  const float* W0 = w0 + b * w0_bstride + (long long)h * D * D;
-  for (int e = threadIdx.x; e < D * D; e += kThreads) sW[e / D][e % D] = W0[e];
-  float G[PER];
-  for (int u = 0; u < PER; ++u) G[u] = 0.f;
+  float kk[PER], kv[PER];
+  for (int u = 0; u < PER; ++u) kk[u] = kv[u] = 0.f;
   for (int t0 = n0; t0 < n1; t0 += kTileF) {
     __syncthreads();
     for (int e = threadIdx.x; e < kTileF * D; e += kThreads) {
@@ -394,31 +412,30 @@ __global__ __launch_bounds__(kThreads) void fb_partial_f32(const float* __restri
       const bool ok = t0 + t < n1;
       const long long off = ((long long)b * N + t0 + t) * ts + (long long)h * D + c;
       sK[t][c] = ok ? k[off] : 0.f;
-      sE[t][c] = ok ? v[off] : 0.f;
-    }
-    __syncthreads();
-    // E = K W0 - V, in place over the V tile (each thread touches only its own elements).
-    for (int e = threadIdx.x; e < kTileF * D; e += kThreads) {
-      const int t = e / D, c = e % D;
-      float acc = -sE[t][c];
-      for (int i = 0; i < D; ++i) acc = fmaf(sK[t][i], sW[i][c], acc);
-      sE[t][c] = acc;
+      sV[t][c] = ok ? v[off] : 0.f;
     }
     __syncthreads();
     for (int u = 0; u < PER; ++u) {
       const int e = threadIdx.x + kThreads * u;
       if (e < D * D) {
         const int i = e / D, c = e % D;
-        float acc = G[u];
-        for (int t = 0; t < kTileF; ++t) acc = fmaf(sK[t][i], sE[t][c], acc);
-        G[u] = acc;
+        float a = kk[u], bb = kv[u];
+        for (int t = 0; t < kTileF; ++t) {
+          a = fmaf(sK[t][i], sK[t][c], a);
+          bb = fmaf(sK[t][i], sV[t][c], bb);
+        }
+        kk[u] = a;
+        kv[u] = bb;
       }
     }
   }
-  float* out = partial + ((long long)bh * S + s) * D * D;
+  float* out = partial + ((long long)bh * S + s) * 2 * D * D;
   for (int u = 0; u < PER; ++u) {
     const int e = threadIdx.x + kThreads * u;
-    if (e < D * D) out[e] = G[u];
+    if (e < D * D) {
+      out[e] = kk[u];
+      out[D * D + e] = kv[u];
+    }
   }
 }
 
@@ -449,20 +466,44 @@ __global__ __launch_bounds__(kThreads) void fb_readout_f32(const float* __restri
   }
 }
 
-// ---------------------------------------------------------------- shared reduction
-__global__ __launch_bounds__(kThreads) void fb_reduce(const float* __restrict__ partial, int S,
-                                                      const float* __restrict__ w0,
-                                                      long long w0_bstride, int H, int D,
-                                                      float scale, float* __restrict__ wstar,
-                                                      float* __restrict__ w_out) {
+// ---------------------------------------------------------------- fp32 reduction and epochs
+// Per (b, h): sums the splits' K^T K and K^T V in a fixed order, then runs the epochs
+// W <- W - scale ((K^T K) W - K^T V) from W0 in LDS.
+template <int D>
+__global__ __launch_bounds__(kThreads) void fb_reduce_f32(const float* __restrict__ partial, int S,
+                                                          const float* __restrict__ w0,
+                                                          long long w0_bstride, int H, float scale,
+                                                          int epochs, float* __restrict__ wstar,
+                                                          float* __restrict__ w_out) {
+  __shared__ float sKK[D][D + 1], sKV[D][D + 1], sW[2][D][D + 1];
   const int bh = blockIdx.x, b = bh / H, h = bh % H;
   const long long dd = (long long)D * D;
   const float* W0 = w0 + b * w0_bstride + h * dd;
-  const float* pp = partial + bh * S * dd;
+  const float* pp = partial + (long long)bh * S * 2 * dd;
   for (int e = threadIdx.x; e < D * D; e += kThreads) {
-    float acc = 0.f;
-    for (int s = 0; s < S; ++s) acc += pp[s * dd + e];
-    const float wv = W0[e] - scale * acc;
+    float a = 0.f, c = 0.f;
+    for (int s = 0; s < S; ++s) {
+      a += pp[s * 2 * dd + e];
+      c += pp[s * 2 * dd + dd + e];
+    }
+    sKK[e / D][e % D] = a;
+    sKV[e / D][e % D] = c;
+    sW[0][e / D][e % D] = W0[e];
+  }
+  __syncthreads();
+  int cur = 0;
+  for (int ep = 0; ep < epochs; ++ep) {
+    for (int e = threadIdx.x; e < D * D; e += kThreads) {
+      const int i = e / D, c = e % D;
+      float gw = 0.f;
+      for (int kq = 0; kq < D; ++kq) gw = fmaf(sKK[i][kq], sW[cur][kq][c], gw);
+      sW[cur ^ 1][i][c] = sW[cur][i][c] - scale * (gw - sKV[i][c]);
+    }
+    __syncthreads();
+    cur ^= 1;
+  }
+  for (int e = threadIdx.x; e < D * D; e += kThreads) {
+    const float wv = sW[cur][e / D][e % D];
     wstar[bh * dd + e] = wv;
     if (w_out) w_out[bh * dd + e] = wv;
   }
@@ -500,9 +541,9 @@ FbPlan plan_splits(int groups, int N, int sets) {
 }
 
 template <int D, int HG>
-hipError_t launch_bf16(int B, int H, int N, float eta, const void* q, const void* k, const void* v,
-                       const float* w0, long long w0s, void* o, float* w_out, void* ws,
-                       hipStream_t st) {
+hipError_t launch_bf16(int B, int H, int N, int epochs, float eta, const void* q, const void* k,
+                       const void* v, const float* w0, long long w0s, void* o, float* w_out,
+                       void* ws, hipStream_t st) {
   const int groups = B * (H / HG);
   const FbPlan pl = plan_splits(groups, N, tile_sets(D));
   float* partial = static_cast<float*>(ws);
@@ -511,23 +552,24 @@ hipError_t launch_bf16(int B, int H, int N, float eta, const void* q, const void
   hipLaunchKernelGGL((fb_partial_bf16<D, HG>), dim3(items), dim3(kThreads), 0, st, (const bf16*)k,
                      (const bf16*)v, w0, w0s, H, N, pl.splits, pl.tokens_per_split, partial);
   hipLaunchKernelGGL((fb_readout_bf16<D, HG>), dim3(items), dim3(kThreads), 0, st, (const bf16*)q,
-                     partial, w0, w0s, H, N, pl.splits, pl.tokens_per_split, scale, (bf16*)o, w_out);
+                     partial, w0, w0s, H, N, pl.splits, pl.tokens_per_split, scale, epochs, (bf16*)o,
+                     w_out);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_f32(int B, int H, int N, float eta, const void* q, const void* k, const void* v,
-                      const float* w0, long long w0s, void* o, float* w_out, void* ws,
-                      hipStream_t st) {
+hipError_t launch_f32(int B, int H, int N, int epochs, float eta, const void* q, const void* k,
+                      const void* v, const float* w0, long long w0s, void* o, float* w_out,
+                      void* ws, hipStream_t st) {
   const int BH = B * H;
   const FbPlan pl = plan_splits(BH, N, 1);
   float* partial = static_cast<float*>(ws);
-  float* wstar = partial + (size_t)BH * pl.splits * D * D;
+  float* wstar = partial + (size_t)BH * pl.splits * 2 * D * D;
   const dim3 grid(pl.splits, BH);
   hipLaunchKernelGGL(fb_partial_f32<D>, grid, dim3(kThreads), 0, st, (const float*)k,
-                     (const float*)v, w0, w0s, H, N, pl.tokens_per_split, pl.splits, partial);
-  hipLaunchKernelGGL(fb_reduce, dim3(BH), dim3(kThreads), 0, st, partial, pl.splits, w0, w0s, H,
-                     D, eta / (float)N, wstar, w_out);
+                     (const float*)v, H, N, pl.tokens_per_split, pl.splits, partial);
+  hipLaunchKernelGGL(fb_reduce_f32<D>, dim3(BH), dim3(kThreads), 0, st, partial, pl.splits, w0, w0s,
+                     H, eta / (float)N, epochs, wstar, w_out);
   hipLaunchKernelGGL(fb_readout_f32<D>, grid, dim3(kThreads), 0, st, (const float*)q, wstar, H,
                      N, pl.tokens_per_split, (float*)o);
   return hipGetLastError();
@@ -543,7 +585,7 @@ size_t fb_workspace_bytes(bool bf16_io, int B, int H, int N, int D) {
   const size_t dd = (size_t)D * D * sizeof(float);
   if (!bf16_io) {
     const FbPlan p = plan_splits(B * H, N, 1);
-    return (size_t)B * H * p.splits * dd + (size_t)B * H * dd;
+    return (size_t)B * H * p.splits * 2 * dd + (size_t)B * H * dd;
   }
   const int hg = head_group(H, D);
   const int groups = B * (H / hg);
@@ -551,25 +593,26 @@ size_t fb_workspace_bytes(bool bf16_io, int B, int H, int N, int D) {
   return (size_t)groups * p.splits * 2 * hg * dd;
 }
 
-hipError_t fb_launch(bool bf16_io, int B, int H, int N, int D, float eta, const void* q,
-                     const void* k, const void* v, const float* w0, long long w0s, void* o,
-                     float* w_out, void* ws, hipStream_t st) {
+hipError_t fb_launch(bool bf16_io, int B, int H, int N, int D, int epochs, float eta,
+                     const void* q, const void* k, const void* v, const float* w0, long long w0s,
+                     void* o, float* w_out, void* ws, hipStream_t st) {
+  const int E = epochs;
   if (!bf16_io) {
     switch (D) {
-      case 16: return launch_f32<16>(B, H, N, eta, q, k, v, w0, w0s, o, w_out, ws, st);
-      case 32: return launch_f32<32>(B, H, N, eta, q, k, v, w0, w0s, o, w_out, ws, st);
-      case 64: return launch_f32<64>(B, H, N, eta, q, k, v, w0, w0s, o, w_out, ws, st);
+      case 16: return launch_f32<16>(B, H, N, E, eta, q, k, v, w0, w0s, o, w_out, ws, st);
+      case 32: return launch_f32<32>(B, H, N, E, eta, q, k, v, w0, w0s, o, w_out, ws, st);
+      case 64: return launch_f32<64>(B, H, N, E, eta, q, k, v, w0, w0s, o, w_out, ws, st);
       default: return hipErrorInvalidValue;
     }
   }
   const int hg = head_group(H, D);
   switch (D * 8 + hg) {
-    case 64 * 8 + 1: return launch_bf16<64, 1>(B, H, N, eta, q, k, v, w0, w0s, o, w_out, ws, st);
-    case 32 * 8 + 2: return launch_bf16<32, 2>(B, H, N, eta, q, k, v, w0, w0s, o, w_out, ws, st);
-    case 32 * 8 + 1: return launch_bf16<32, 1>(B, H, N, eta, q, k, v, w0, w0s, o, w_out, ws, st);
-    case 16 * 8 + 4: return launch_bf16<16, 4>(B, H, N, eta, q, k, v, w0, w0s, o, w_out, ws, st);
-    case 16 * 8 + 2: return launch_bf16<16, 2>(B, H, N, eta, q, k, v, w0, w0s, o, w_out, ws, st);
-    case 16 * 8 + 1: return launch_bf16<16, 1>(B, H, N, eta, q, k, v, w0, w0s, o, w_out, ws, st);
+    case 64 * 8 + 1: return launch_bf16<64, 1>(B, H, N, E, eta, q, k, v, w0, w0s, o, w_out, ws, st);
+    case 32 * 8 + 2: return launch_bf16<32, 2>(B, H, N, E, eta, q, k, v, w0, w0s, o, w_out, ws, st);
+    case 32 * 8 + 1: return launch_bf16<32, 1>(B, H, N, E, eta, q, k, v, w0, w0s, o, w_out, ws, st);
+    case 16 * 8 + 4: return launch_bf16<16, 4>(B, H, N, E, eta, q, k, v, w0, w0s, o, w_out, ws, st);
+    case 16 * 8 + 2: return launch_bf16<16, 2>(B, H, N, E, eta, q, k, v, w0, w0s, o, w_out, ws, st);
+    case 16 * 8 + 1: return launch_bf16<16, 1>(B, H, N, E, eta, q, k, v, w0, w0s, o, w_out, ws, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -16,9 +16,9 @@ struct FbPlan {
 };
 FbPlan fb_plan(int B, int H, int N, int D);
 size_t fb_workspace_bytes(bool bf16_io, int B, int H, int N, int D);
-hipError_t fb_launch(bool bf16_io, int B, int H, int N, int D, float eta, const void* q,
-                     const void* k, const void* v, const float* w0, long long w0_bstride, void* o,
-                     float* w_out, void* ws, hipStream_t st);
+hipError_t fb_launch(bool bf16_io, int B, int H, int N, int D, int epochs, float eta,
+                     const void* q, const void* k, const void* v, const float* w0,
+                     long long w0_bstride, void* o, float* w_out, void* ws, hipStream_t st);
 
 // ---- chunked TTT-Linear (causal and bidirectional) ------------------------------------------
 size_t chunked_workspace_bytes(bool bidir, bool bf16_io, int B, int H, int N, int D, int chunk);

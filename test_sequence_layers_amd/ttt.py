@@ -22,6 +22,8 @@ _c_int, _c_float, _c_ll, _vp, _sz = ctypes.c_int, ctypes.c_float, ctypes.c_longl
 SIGNATURES = {
     "ttt_forward_fullbatch": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _vp, _vp, _vp, _vp, _c_ll,
                                        _vp, _vp, _vp, _sz, _vp]),
+    "ttt_forward_fullbatch_epochs": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _vp, _vp,
+                                              _vp, _vp, _c_ll, _vp, _vp, _vp, _sz, _vp]),
     "ttt_forward_chunked_causal": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _vp, _vp, _vp,
                                             _vp, _c_ll, _vp, _vp, _vp, _sz, _vp]),
     "ttt_forward_chunked_bidir": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _vp, _vp, _vp,
@@ -159,7 +161,7 @@ def _raise(status, where):
         raise TTTError(status, where)
 
 
-def _linear(op, fn_name, q, k, v, w0, chunk, eta, o, w_out, workspace, stream):
+def _linear(op, fn_name, q, k, v, w0, chunk, eta, o, w_out, workspace, stream, epochs=None):
     lib = load_library()
     _check_io(q, k, v)
     torch = _torch()
@@ -172,7 +174,8 @@ def _linear(op, fn_name, q, k, v, w0, chunk, eta, o, w_out, workspace, stream):
     with torch.cuda.device(dev):
         o = torch.empty_like(q) if o is None else o
         ws, ws_size = _workspace(op, dt, B, H, N, D, 0, chunk, workspace, dev)
-        args = [dt, B, H, N, D] + ([] if op == TTT_OP_FULLBATCH else [int(chunk)])
+        args = [dt, B, H, N, D] + ([] if op == TTT_OP_FULLBATCH else [int(chunk)]) + \
+            ([] if epochs is None else [int(epochs)])
         st = getattr(lib, fn_name)(*args, float(eta), _ptr(q), _ptr(k), _ptr(v), _ptr(w0), stride, _ptr(o),
                                    _ptr(w_out), _ptr(ws), ws_size, _stream(stream, dev))
     _raise(st, fn_name)
@@ -185,6 +188,13 @@ def ttt_forward_fullbatch(q, k, v, w0, eta: float = 1.0, *, o=None, w_out=None, 
 
     q, k, v, o: [B, N, H, D] bf16 or fp32; w0: fp32 [H, D, D] or [B, H, D, D]; w_out: fp32 [B, H, D, D]."""
     return _linear(TTT_OP_FULLBATCH, "ttt_forward_fullbatch", q, k, v, w0, 0, eta, o, w_out, workspace, stream)
+
+
+def ttt_forward_fullbatch_epochs(q, k, v, w0, epochs: int, eta: float = 1.0, *, o=None, w_out=None, workspace=None,
+                                 stream=None):
+    """`epochs` full-batch steps W <- W - (eta/N) K^T (K W - V) from W0, then O = Q W. Returns o."""
+    return _linear(TTT_OP_FULLBATCH, "ttt_forward_fullbatch_epochs", q, k, v, w0, 0, eta, o, w_out, workspace,
+                   stream, epochs=epochs)
 
 
 def ttt_forward_fullbatch_noalloc(q, k, v, w0, eta: float = 1.0, *, o, w_out=None, stream=None):

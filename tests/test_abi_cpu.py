@@ -25,7 +25,17 @@ def _declared_functions():
 def test_header_declares_the_entry_points():
     assert _declared_functions() == sorted([
         "ttt_forward_fullbatch", "ttt_forward_chunked_causal", "ttt_forward_chunked_bidir", "ttt_mlp_forward",
-        "ttt_workspace_size", "ttt_status_string", "ttt_forward_fullbatch_noalloc", "ttt_dwconv3x3"])
+        "ttt_workspace_size", "ttt_status_string", "ttt_forward_fullbatch_noalloc", "ttt_dwconv3x3",
+        "ttt_forward_fullbatch_epochs"])
+
+
+def test_fullbatch_epochs_validation():
+    lib = T.load_library()
+    call = lambda e: lib.ttt_forward_fullbatch_epochs(T.TTT_BF16, 1, 1, 64, 64, e, 1.0, _p(0), _p(1), _p(2), _p(3),  # noqa: E731
+                                                      0, _p(4), None, _p(5), 1 << 30, None)
+    assert call(0) == 1
+    assert call(-3) == 1
+    assert call(257) == 2
 
 
 def test_dwconv_validation_rejects_before_launch():

@@ -554,3 +554,35 @@ def test_fullbatch_workspace_reuse_with_new_inputs():
         out = host(lib.ttt_forward_fullbatch(q, k, v, torch.from_numpy(x.w0).cuda(), wl.eta, workspace=ws))
         torch.cuda.synchronize()
         assert slice_err(out, oracle_full(x)[0]) <= BF16_TOL
+
+
+# ------------------------------------------------------------------ several full-batch epochs
+EPOCH_CASES = [
+    (W["hvit3t_stage1_fullbatch"].with_(B=2, N=700, seed=161), 3),          # 2 heads of 32 per group
+    (W["vit3s_fullbatch"].with_(B=3, N=196, seed=162), 2),                   # one head of 64 per group
+    (W["hvit3t_stage1_fullbatch"].with_(B=1, N=900, H=1, D=16, seed=163), 5),  # 4 waves per task
+    (W["fullbatch_tiny_fp32"].with_(B=2, N=300, H=3, D=32, seed=164), 4),    # fp32: 1e-4 bar
+    (W["fullbatch_tiny_fp32"].with_(B=1, N=77, H=2, D=64, seed=165), 1),
+    (W["hvit3t_stage1_fullbatch"], 3),                                       # full size
+]
+
+
+@pytest.mark.parametrize("wl,epochs", EPOCH_CASES, ids=lambda v: f"{v.dtype}-B{v.B}N{v.N}H{v.H}D{v.D}"
+                         if hasattr(v, "dtype") else f"E{v}")
+def test_fullbatch_epochs_parity(wl, epochs):
+    lib = T()
+    print(f"epochs {epochs}: {wl.dtype} B={wl.B} N={wl.N} H={wl.H} D={wl.D}", flush=True)
+    x = synth.make_inputs(wl)
+    q, k, v = dev(x.q, wl.dtype), dev(x.k, wl.dtype), dev(x.v, wl.dtype)
+    w0 = torch.from_numpy(x.w0).cuda()
+    so = torch.full((wl.B, wl.H, wl.D, wl.D), float("nan"), device="cuda")
+    out = lib.ttt_forward_fullbatch_epochs(q, k, v, w0, epochs, wl.eta, w_out=so)
+    torch.cuda.synchronize()
+    ref_o, ref_w = O.fullbatch_epochs(x.q64, x.k64, x.v64, x.w0, wl.eta, epochs)
+    assert report(f"epochs={epochs}", host(out), ref_o) <= tol(wl)
+    st = so.cpu().numpy()
+    assert np.abs(st - ref_w).max() / np.abs(ref_w).max() <= tol(wl)
+    if epochs == 1:  # the same kernels and plan as ttt_forward_fullbatch
+        ref1 = lib.ttt_forward_fullbatch(q, k, v, w0, wl.eta)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref1)
