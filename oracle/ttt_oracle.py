@@ -32,7 +32,9 @@ widened to float64 here); inner states are [H, ...] (shared over the batch) or
 Parity status: every function here is pinned by tests/test_oracle_pins.py
 (closed forms, special cases, finite differences, autograd, exact rational
 arithmetic) and tests/test_oracle_pins_epochs.py (fullbatch_epochs: closed form
-with orthogonal keys, convergence to least squares). None is "parity unpinned".
+with orthogonal keys, convergence to least squares) and tests/test_oracle_pins_vjp.py
+(fullbatch_vjp: finite differences, torch autograd, eta = 0). None is "parity
+unpinned".
 """
 from __future__ import annotations
 
@@ -94,6 +96,32 @@ def fullbatch(q, k, v, w0, eta: float):
     G = _t(K) @ E                        # sum_j of per-token gradients k_j^T e_j
     W = W0 - (eta / N) * G
     return _bnhd(Q @ W), W
+
+
+def fullbatch_vjp(q, k, v, w0, eta: float, d_o):
+    """Gradients of the full-batch layer for the outer training loop: given dO = dL/dO, returns
+    (dL/dq, dL/dk, dL/dv, dL/dW0) of the one-step forward above, in closed form (the pages'
+    authors likewise derive the inner gradient by hand rather than by autograd: ViT^3 review,
+    section on the official code). With s = eta/N, E = K W0 - V, W* = W0 - s K^T E and
+    G = Q^T dO = dL/dW*:
+        dQ  = dO W*^T
+        dW0 = (I - s K^T K) G                 (dW*/dW0 = I - s K^T K, symmetric)
+        dV  = s K G                            (W* depends on V through s K^T V)
+        dK  = -s (E G^T + K G W0^T)            (from d(K^T (K W0 - V)) = dK^T E + K^T dK W0)
+    Inputs as for fullbatch, d_o [B,N,H,D]. Returns ([B,N,H,D] x 3, [B,H,D,D]).
+    """
+    Q, K, V, dO = _bhnd(q), _bhnd(k), _bhnd(v), _bhnd(d_o)
+    B, H, N, D = Q.shape
+    W0 = _state(w0, B, H)
+    s = eta / N
+    E = K @ W0 - V
+    Ws = W0 - s * (_t(K) @ E)
+    G = _t(Q) @ dO
+    dQ = dO @ _t(Ws)
+    dW0 = G - s * (_t(K) @ (K @ G))
+    dV = s * (K @ G)
+    dK = -s * (E @ _t(G) + K @ G @ _t(W0))
+    return _bnhd(dQ), _bnhd(dK), _bnhd(dV), dW0
 
 
 def fullbatch_epochs(q, k, v, w0, eta: float, epochs: int):
