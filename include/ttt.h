@@ -69,7 +69,13 @@ typedef enum {
 
 typedef enum { TTT_F32 = 0, TTT_BF16 = 1 } ttt_dtype;
 
-typedef enum { TTT_OP_FULLBATCH = 0, TTT_OP_CAUSAL = 1, TTT_OP_BIDIR = 2, TTT_OP_MLP = 3 } ttt_op;
+typedef enum {
+  TTT_OP_FULLBATCH = 0,
+  TTT_OP_CAUSAL = 1,
+  TTT_OP_BIDIR = 2,
+  TTT_OP_MLP = 3,
+  TTT_OP_FULLBATCH_BWD = 4
+} ttt_op;
 
 /*
  * Single-epoch, full-batch inner step (ViT^3 review on techloop.online, design-space study: one
@@ -82,6 +88,22 @@ ttt_status ttt_forward_fullbatch(ttt_dtype dt, int B, int H, int N, int D, float
                                  const float* w0, long long w0_batch_stride,
                                  void* o, float* w_out,
                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward pass of ttt_forward_fullbatch for the outer training loop: given d_o = dL/dO, the
+ * gradients of L with respect to q, k, v and W0, in closed form (the pages' authors also write
+ * the inner gradient by hand: ViT^3 review on techloop.online, section on the official code).
+ * With s = eta/N, W* as in the forward, G = Q^T dO and M = W0 G^T + G W0^T, per (b, h):
+ *   dQ = dO W*^T,   dK = -s (K M - V G^T),   dV = s K G,   dW0 = G - s (K^T K) G.
+ * d_o, d_q, d_k, d_v: [B, N, H, D] of dtype dt; d_w0: fp32 [B, H, D, D], per batch element even
+ * when W0 is shared (w0_batch_stride 0): the caller then sums it over the batch. Outputs must not
+ * overlap any input or each other. Workspace: ttt_workspace_size(TTT_OP_FULLBATCH_BWD, ...).
+ */
+ttt_status ttt_backward_fullbatch(ttt_dtype dt, int B, int H, int N, int D, float eta,
+                                  const void* q, const void* k, const void* v,
+                                  const float* w0, long long w0_batch_stride, const void* d_o,
+                                  void* d_q, void* d_k, void* d_v, float* d_w0,
+                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Several full-batch epochs before the read-out (ViT^3 review on techloop.online, design-space

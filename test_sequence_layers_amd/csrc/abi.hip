@@ -129,6 +129,8 @@ size_t ttt_workspace_size(ttt_op op, ttt_dtype dt, int B, int H, int N, int D, i
   switch (op) {
     case TTT_OP_FULLBATCH:
       return round_up(ttt::fb_workspace_bytes(bf, B, H, N, D), 256);
+    case TTT_OP_FULLBATCH_BWD:
+      return round_up(ttt::fbb_workspace_bytes(bf, B, H, N, D), 256);
     case TTT_OP_CAUSAL:
     case TTT_OP_BIDIR:
       if (!supported_chunk(chunk) || N % chunk != 0) return 0;
@@ -172,6 +174,42 @@ ttt_status ttt_forward_fullbatch_epochs(ttt_dtype dt, int B, int H, int N, int D
   return from_hip(ttt::fb_launch(dt == TTT_BF16, B, H, N, D, epochs, eta, q, k, v, w0,
                                  w0_batch_stride, o, w_out, workspace,
                                  static_cast<hipStream_t>(stream)));
+}
+
+ttt_status ttt_backward_fullbatch(ttt_dtype dt, int B, int H, int N, int D, float eta,
+                                  const void* q, const void* k, const void* v, const float* w0,
+                                  long long w0_batch_stride, const void* d_o, void* d_q,
+                                  void* d_k, void* d_v, float* d_w0, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  // The forward's checks cover q, k, v, w0 and one [B, N, H, D] output (d_q here); the rest below.
+  ttt_status st = check_linear(TTT_OP_FULLBATCH, dt, B, H, N, D, 0, eta, q, k, v, w0,
+                               w0_batch_stride, d_q, nullptr, nullptr, 0, false);
+  if (st != TTT_OK) return st;
+  if (!d_o || !d_k || !d_v || !d_w0) return TTT_ERR_INVALID;
+  if (!aligned16(d_o) || !aligned16(d_k) || !aligned16(d_v) || !aligned16(d_w0))
+    return TTT_ERR_INVALID;
+  const size_t act = (size_t)B * N * H * D * elem_size(dt);
+  const Range ins[5] = {range_of(q, act), range_of(k, act), range_of(v, act), range_of(d_o, act),
+                        range_of(w0, state_bytes(B, H, (size_t)D * D, w0_batch_stride))};
+  const Range outs[4] = {range_of(d_q, act), range_of(d_k, act), range_of(d_v, act),
+                         range_of(d_w0, (size_t)B * H * D * D * sizeof(float))};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 5; ++j)
+      if (overlaps(outs[i], ins[j])) return TTT_ERR_INVALID;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], outs[j])) return TTT_ERR_INVALID;
+  }
+  const size_t need = ttt_workspace_size(TTT_OP_FULLBATCH_BWD, dt, B, H, N, D, 0, 0);
+  if (!workspace || workspace_bytes < need) return TTT_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return TTT_ERR_INVALID;
+  const Range rws = range_of(workspace, need);
+  for (int j = 0; j < 5; ++j)
+    if (overlaps(rws, ins[j])) return TTT_ERR_INVALID;
+  for (int i = 0; i < 4; ++i)
+    if (overlaps(rws, outs[i])) return TTT_ERR_INVALID;
+  return from_hip(ttt::fbb_launch(dt == TTT_BF16, B, H, N, D, eta, q, k, v, w0, w0_batch_stride,
+                                  d_o, d_q, d_k, d_v, d_w0, workspace,
+                                  static_cast<hipStream_t>(stream)));
 }
 
 ttt_status ttt_forward_chunked_causal(ttt_dtype dt, int B, int H, int N, int D, int chunk,

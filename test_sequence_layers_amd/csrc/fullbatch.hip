@@ -575,6 +575,255 @@ hipError_t launch_f32(int B, int H, int N, int epochs, float eta, const void* q,
   return hipGetLastError();
 }
 
+
+// ---------------------------------------------------------------- backward (outer-loop gradients)
+// Given dO, the gradients of the one-step layer (closed form; the pages' authors likewise write
+// the inner gradient by hand, ViT^3 review, section on the official code). With s = eta/N,
+// W* = W0 - s ((K^T K) W0 - K^T V), G = Q^T dO and M = W0 G^T + G W0^T:
+//   dQ = dO W*^T,   dV = s K G,   dK = -s (K M - V G^T),   dW0 = G - s (K^T K) G.
+// Three launches after the sums (the partial kernels above, run on (K, V) for K^T K and K^T V
+// and on (Q, dO), whose second product is G):
+//   fbb_finish: per (b, h), the fixed-order sums of the split records, then W*, dW0 and M in
+//               LDS (plain fp32), written out as the token kernel's four operand matrices
+//               A_q = W*, A_v = s G^T, A_k1 = -s M, A_k2 = s G (bf16 MFMA tiles, or fp32);
+//   fbb_tokens: per 16-token tile, dQ^T = A_q dO^T, dV^T = A_v K^T, dK^T = A_k1 K^T + A_k2 V^T.
+constexpr int kBwdMats = 4;
+
+// Element (i, j) of the summed K^T K (which = 0) or K^T V (which = 1) of head hl of a group, from
+// the bf16 path's split records (per task (head, row block m): tiles (c, m) of K^T K, then
+// (m, n) of K^T V, in accumulator lane order).
+template <int D, int HG>
+__device__ __forceinline__ float record_sum_bf16(const float* rec, int S, int hl, int which, int i,
+                                                 int j) {
+  constexpr int NT = D / 16;
+  int task, t;
+  if (which == 0) {  // tile (c = i / 16, m = j / 16): rows of K^T K 16c + 4g + jj, column 16m + r
+    task = hl * NT + j / 16;
+    t = i / 16;
+  } else {           // tile (m = i / 16, n = j / 16)
+    task = hl * NT + i / 16;
+    t = NT + j / 16;
+  }
+  const int r = j % 16, g = (i % 16) / 4, jj = i % 4;
+  const long long off = (long long)task * (2 * NT * 256) + (t * 64 + r + 16 * g) * 4 + jj;
+  float acc = 0.f;
+  for (int sp = 0; sp < S; ++sp) acc += rec[(long long)sp * (2 * HG * D * D) + off];
+  return acc;
+}
+
+// One workgroup per (b, h). rec_kv / rec_qd: the group's split records (bf16 path) or the
+// (b, h)'s (fp32 path: per split K^T K then K^T V, row-major). ops: the four operand matrices.
+template <int D, int HG, bool BF16>
+__global__ __launch_bounds__(kThreads) void fbb_finish(const float* __restrict__ rec_kv,
+                                                       const float* __restrict__ rec_qd,
+                                                       const float* __restrict__ w0,
+                                                       long long w0_bstride, int H, int S,
+                                                       float s_eta, void* __restrict__ ops,
+                                                       float* __restrict__ d_w0) {
+  __shared__ float sKK[D][D + 1], sKV[D][D + 1], sG[D][D + 1], sW0[D][D + 1];
+  const int bh = blockIdx.x, b = bh / H, h = bh % H;
+  const long long DD = (long long)D * D;
+  const float* W0 = w0 + b * w0_bstride + h * DD;
+  for (int e = threadIdx.x; e < D * D; e += kThreads) {
+    const int i = e / D, j = e % D;
+    float kk, kv, gq;
+    if constexpr (BF16) {
+      const int grp = b * (H / HG) + h / HG, hl = h % HG;
+      const float* rk = rec_kv + (long long)grp * S * (2 * HG * DD);
+      const float* rq = rec_qd + (long long)grp * S * (2 * HG * DD);
+      kk = record_sum_bf16<D, HG>(rk, S, hl, 0, i, j);
+      kv = record_sum_bf16<D, HG>(rk, S, hl, 1, i, j);
+      gq = record_sum_bf16<D, HG>(rq, S, hl, 1, i, j);
+    } else {
+      kk = kv = gq = 0.f;
+      for (int sp = 0; sp < S; ++sp) {
+        const long long base = ((long long)bh * S + sp) * 2 * DD;
+        kk += rec_kv[base + e];
+        kv += rec_kv[base + DD + e];
+        gq += rec_qd[base + DD + e];
+      }
+    }
+    sKK[i][j] = kk;
+    sKV[i][j] = kv;
+    sG[i][j] = gq;
+    sW0[i][j] = W0[e];
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < D * D; e += kThreads) {
+    const int i = e / D, j = e % D;
+    float kw = 0.f, kg = 0.f, m = 0.f;
+    for (int c = 0; c < D; ++c) {
+      kw = fmaf(sKK[i][c], sW0[c][j], kw);
+      kg = fmaf(sKK[i][c], sG[c][j], kg);
+      m = fmaf(sW0[i][c], sG[j][c], fmaf(sG[i][c], sW0[j][c], m));
+    }
+    const float ws = sW0[i][j] - s_eta * (kw - sKV[i][j]);
+    d_w0[(long long)bh * DD + e] = sG[i][j] - s_eta * kg;
+    // A_q = W*, A_v = s G^T, A_k1 = -s M, A_k2 = s G, element (row i, k = j)
+    const float a[kBwdMats] = {ws, s_eta * sG[j][i], -s_eta * m, s_eta * sG[i][j]};
+    for (int mat = 0; mat < kBwdMats; ++mat) {
+      if constexpr (BF16) {
+        // operand tile (column tile n = i / 16, k step ks), lane r + 16 g, element ii
+        constexpr int E = D >= 32 ? 8 : 4, KS = D >= 32 ? D / 32 : 1;
+        const int n = i / 16, r = i % 16, ks = j / (4 * E), g = (j % (4 * E)) / E, ii = j % E;
+        bf16* dst = static_cast<bf16*>(ops) + (long long)bh * kBwdMats * DD + mat * DD;
+        dst[((n * KS + ks) * 64 + r + 16 * g) * E + ii] = (bf16)a[mat];
+      } else {
+        static_cast<float*>(ops)[(long long)bh * kBwdMats * DD + mat * DD + e] = a[mat];
+      }
+    }
+  }
+}
+
+// bf16: one workgroup per (256-token block, b, h); wave w handles 16-token tiles w, w + 4, ... of
+// the block. Operands of the four matrices are staged in LDS (lane order); each tile's dO, K, V
+// rows are the B operands (lane (r, g): token r, features 8g.. of a 32-feature k step, one 16-byte
+// load), and the results come out transposed (lane (r, g): 4 adjacent output features of token r,
+// one 8-byte store).
+constexpr int kBwdTok = 256;
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void fbb_tokens_bf16(
+    const bf16* __restrict__ d_o, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ ops, int H, int N, bf16* __restrict__ d_q, bf16* __restrict__ d_k,
+    bf16* __restrict__ d_v) {
+  constexpr int NT = D / 16, E = D >= 32 ? 8 : 4, KS = D >= 32 ? D / 32 : 1;
+  constexpr int DD = D * D;
+  typedef typename std::conditional<(D >= 32), bf16x8, bf16x4>::type Op;
+  __shared__ __align__(16) bf16 sOps[kBwdMats * DD];
+  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
+  const bf16* src = ops + (long long)bh * kBwdMats * DD;
+  for (int e = threadIdx.x * 8; e < kBwdMats * DD; e += kThreads * 8)
+    *reinterpret_cast<uint4*>(&sOps[e]) = *reinterpret_cast<const uint4*>(&src[e]);
+  __syncthreads();
+  const long long ts = (long long)H * D;
+  const long long head0 = (long long)b * N * ts + (long long)h * D;
+  auto mma = [](Op a, Op bb, f32x4 c) {
+    if constexpr (D >= 32) return mma32(a, bb, c);
+    else return mma16(a, bb, c);
+  };
+  auto aop = [&](int mat, int n, int ks) {
+    return *reinterpret_cast<const Op*>(&sOps[mat * DD + ((n * KS + ks) * 64 + l) * E]);
+  };
+  for (int tile = w; tile * 16 < kBwdTok; tile += 4) {
+    const int t0 = blockIdx.x * kBwdTok + tile * 16;
+    if (t0 >= N) break;
+    const bool ok = t0 + r < N;
+    const long long row = head0 + (long long)(t0 + r) * ts;
+    Op xo[KS], xk[KS], xv[KS];
+    for (int ks = 0; ks < KS; ++ks) {
+      const int col = ks * 4 * E + E * g;
+      xo[ks] = ok ? *reinterpret_cast<const Op*>(d_o + row + col) : Op{};
+      xk[ks] = ok ? *reinterpret_cast<const Op*>(k + row + col) : Op{};
+      xv[ks] = ok ? *reinterpret_cast<const Op*>(v + row + col) : Op{};
+    }
+    for (int n = 0; n < NT; ++n) {
+      f32x4 aq = zero4(), av = zero4(), ak = zero4();
+      for (int ks = 0; ks < KS; ++ks) {
+        aq = mma(aop(0, n, ks), xo[ks], aq);
+        av = mma(aop(1, n, ks), xk[ks], av);
+        ak = mma(aop(2, n, ks), xk[ks], ak);
+        ak = mma(aop(3, n, ks), xv[ks], ak);
+      }
+      if (ok) {
+        const long long o = row + 16 * n + 4 * g;
+        *reinterpret_cast<bf16x4*>(d_q + o) = to_bf16x4(aq);
+        *reinterpret_cast<bf16x4*>(d_v + o) = to_bf16x4(av);
+        *reinterpret_cast<bf16x4*>(d_k + o) = to_bf16x4(ak);
+      }
+    }
+  }
+}
+
+// fp32: plain FMA, one workgroup per (256-token block, b, h); the matrices in LDS.
+template <int D>
+__global__ __launch_bounds__(kThreads) void fbb_tokens_f32(
+    const float* __restrict__ d_o, const float* __restrict__ k, const float* __restrict__ v,
+    const float* __restrict__ ops, int H, int N, float* __restrict__ d_q, float* __restrict__ d_k,
+    float* __restrict__ d_v) {
+  __shared__ float sA[kBwdMats][D][D + 1];
+  __shared__ float sX[3][kTileF][D + 1];
+  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  const float* src = ops + (long long)bh * kBwdMats * D * D;
+  for (int e = threadIdx.x; e < kBwdMats * D * D; e += kThreads) sA[e / (D * D)][(e / D) % D][e % D] = src[e];
+  const long long ts = (long long)H * D;
+  const long long head0 = (long long)b * N * ts + (long long)h * D;
+  for (int t0 = blockIdx.x * kBwdTok; t0 < min(N, (int)(blockIdx.x + 1) * kBwdTok); t0 += kTileF) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < kTileF * D; e += kThreads) {
+      const int t = e / D, c = e % D;
+      const bool ok = t0 + t < N;
+      const long long off = head0 + (long long)(t0 + t) * ts + c;
+      sX[0][t][c] = ok ? d_o[off] : 0.f;
+      sX[1][t][c] = ok ? k[off] : 0.f;
+      sX[2][t][c] = ok ? v[off] : 0.f;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < kTileF * D; e += kThreads) {
+      const int t = e / D, i = e % D;
+      if (t0 + t >= N) continue;
+      float q = 0.f, vv = 0.f, kk = 0.f;
+      for (int j = 0; j < D; ++j) {
+        q = fmaf(sA[0][i][j], sX[0][t][j], q);
+        vv = fmaf(sA[1][i][j], sX[1][t][j], vv);
+        kk = fmaf(sA[2][i][j], sX[1][t][j], fmaf(sA[3][i][j], sX[2][t][j], kk));
+      }
+      const long long off = head0 + (long long)(t0 + t) * ts + i;
+      d_q[off] = q;
+      d_v[off] = vv;
+      d_k[off] = kk;
+    }
+  }
+}
+
+template <int D, int HG>
+hipError_t launch_bwd_bf16(int B, int H, int N, float eta, const void* q, const void* k,
+                           const void* v, const float* w0, long long w0s, const void* d_o,
+                           void* d_q, void* d_k, void* d_v, float* d_w0, void* ws,
+                           hipStream_t st) {
+  const int groups = B * (H / HG);
+  const FbPlan pl = plan_splits(groups, N, tile_sets(D));
+  const size_t rec = (size_t)groups * pl.splits * 2 * HG * D * D;  // floats per record set
+  float* rkv = static_cast<float*>(ws);
+  float* rqd = rkv + rec;
+  bf16* ops = reinterpret_cast<bf16*>(rqd + rec);
+  const int items = groups * pl.splits;
+  hipLaunchKernelGGL((fb_partial_bf16<D, HG>), dim3(items), dim3(kThreads), 0, st, (const bf16*)k,
+                     (const bf16*)v, w0, w0s, H, N, pl.splits, pl.tokens_per_split, rkv);
+  hipLaunchKernelGGL((fb_partial_bf16<D, HG>), dim3(items), dim3(kThreads), 0, st, (const bf16*)q,
+                     (const bf16*)d_o, w0, w0s, H, N, pl.splits, pl.tokens_per_split, rqd);
+  hipLaunchKernelGGL((fbb_finish<D, HG, true>), dim3(B * H), dim3(kThreads), 0, st, rkv, rqd, w0, w0s,
+                     H, pl.splits, eta / (float)N, (void*)ops, d_w0);
+  hipLaunchKernelGGL((fbb_tokens_bf16<D>), dim3((N + kBwdTok - 1) / kBwdTok, B * H), dim3(kThreads), 0,
+                     st, (const bf16*)d_o, (const bf16*)k, (const bf16*)v, (const bf16*)ops, H, N,
+                     (bf16*)d_q, (bf16*)d_k, (bf16*)d_v);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_bwd_f32(int B, int H, int N, float eta, const void* q, const void* k,
+                          const void* v, const float* w0, long long w0s, const void* d_o,
+                          void* d_q, void* d_k, void* d_v, float* d_w0, void* ws, hipStream_t st) {
+  const int BH = B * H;
+  const FbPlan pl = plan_splits(BH, N, 1);
+  const size_t rec = (size_t)BH * pl.splits * 2 * D * D;
+  float* rkv = static_cast<float*>(ws);
+  float* rqd = rkv + rec;
+  float* ops = rqd + rec;
+  const dim3 grid(pl.splits, BH);
+  hipLaunchKernelGGL(fb_partial_f32<D>, grid, dim3(kThreads), 0, st, (const float*)k, (const float*)v,
+                     H, N, pl.tokens_per_split, pl.splits, rkv);
+  hipLaunchKernelGGL(fb_partial_f32<D>, grid, dim3(kThreads), 0, st, (const float*)q, (const float*)d_o,
+                     H, N, pl.tokens_per_split, pl.splits, rqd);
+  hipLaunchKernelGGL((fbb_finish<D, 1, false>), dim3(BH), dim3(kThreads), 0, st, rkv, rqd, w0, w0s, H,
+                     pl.splits, eta / (float)N, (void*)ops, d_w0);
+  hipLaunchKernelGGL(fbb_tokens_f32<D>, dim3((N + kBwdTok - 1) / kBwdTok, BH), dim3(kThreads), 0, st,
+                     (const float*)d_o, (const float*)k, (const float*)v, (const float*)ops, H, N,
+                     (float*)d_q, (float*)d_k, (float*)d_v);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 FbPlan fb_plan(int B, int H, int N, int D) {
@@ -613,6 +862,46 @@ hipError_t fb_launch(bool bf16_io, int B, int H, int N, int D, int epochs, float
     case 16 * 8 + 4: return launch_bf16<16, 4>(B, H, N, E, eta, q, k, v, w0, w0s, o, w_out, ws, st);
     case 16 * 8 + 2: return launch_bf16<16, 2>(B, H, N, E, eta, q, k, v, w0, w0s, o, w_out, ws, st);
     case 16 * 8 + 1: return launch_bf16<16, 1>(B, H, N, E, eta, q, k, v, w0, w0s, o, w_out, ws, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+size_t fbb_workspace_bytes(bool bf16_io, int B, int H, int N, int D) {
+  const size_t dd = (size_t)D * D;
+  if (!bf16_io) {
+    const FbPlan p = plan_splits(B * H, N, 1);
+    return (2 * (size_t)B * H * p.splits * 2 * dd + (size_t)B * H * kBwdMats * dd) * sizeof(float);
+  }
+  const int hg = head_group(H, D);
+  const int groups = B * (H / hg);
+  const FbPlan p = plan_splits(groups, N, tile_sets(D));
+  return 2 * (size_t)groups * p.splits * 2 * hg * dd * sizeof(float) + (size_t)B * H * kBwdMats * dd * 2;
+}
+
+hipError_t fbb_launch(bool bf16_io, int B, int H, int N, int D, float eta, const void* q,
+                      const void* k, const void* v, const float* w0, long long w0s,
+                      const void* d_o, void* d_q, void* d_k, void* d_v, float* d_w0, void* ws,
+                      hipStream_t st) {
+  if (!bf16_io) {
+    switch (D) {
+      case 16: return launch_bwd_f32<16>(B, H, N, eta, q, k, v, w0, w0s, d_o, d_q, d_k, d_v, d_w0, ws, st);
+      case 32: return launch_bwd_f32<32>(B, H, N, eta, q, k, v, w0, w0s, d_o, d_q, d_k, d_v, d_w0, ws, st);
+      case 64: return launch_bwd_f32<64>(B, H, N, eta, q, k, v, w0, w0s, d_o, d_q, d_k, d_v, d_w0, ws, st);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  const int hg = head_group(H, D);
+  switch (D * 8 + hg) {
+#define TTT_BWD(DV, HGV)                                                                          \
+  case DV * 8 + HGV:                                                                             \
+    return launch_bwd_bf16<DV, HGV>(B, H, N, eta, q, k, v, w0, w0s, d_o, d_q, d_k, d_v, d_w0, ws, st);
+    TTT_BWD(64, 1)
+    TTT_BWD(32, 2)
+    TTT_BWD(32, 1)
+    TTT_BWD(16, 4)
+    TTT_BWD(16, 2)
+    TTT_BWD(16, 1)
+#undef TTT_BWD
     default: return hipErrorInvalidValue;
   }
 }

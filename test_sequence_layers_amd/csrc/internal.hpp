@@ -20,6 +20,12 @@ hipError_t fb_launch(bool bf16_io, int B, int H, int N, int D, int epochs, float
                      const void* q, const void* k, const void* v, const float* w0,
                      long long w0_bstride, void* o, float* w_out, void* ws, hipStream_t st);
 
+size_t fbb_workspace_bytes(bool bf16_io, int B, int H, int N, int D);
+hipError_t fbb_launch(bool bf16_io, int B, int H, int N, int D, float eta, const void* q,
+                      const void* k, const void* v, const float* w0, long long w0_bstride,
+                      const void* d_o, void* d_q, void* d_k, void* d_v, float* d_w0, void* ws,
+                      hipStream_t st);
+
 // ---- chunked TTT-Linear (causal and bidirectional) ------------------------------------------
 size_t chunked_workspace_bytes(bool bidir, bool bf16_io, int B, int H, int N, int D, int chunk);
 hipError_t chunked_launch(bool bidir, bool bf16_io, int B, int H, int N, int D, int chunk,

@@ -26,7 +26,23 @@ def test_header_declares_the_entry_points():
     assert _declared_functions() == sorted([
         "ttt_forward_fullbatch", "ttt_forward_chunked_causal", "ttt_forward_chunked_bidir", "ttt_mlp_forward",
         "ttt_workspace_size", "ttt_status_string", "ttt_forward_fullbatch_noalloc", "ttt_dwconv3x3",
-        "ttt_forward_fullbatch_epochs"])
+        "ttt_forward_fullbatch_epochs", "ttt_backward_fullbatch"])
+
+
+def test_backward_validation_rejects_before_launch():
+    lib = T.load_library()
+    call = lambda do=5, dq=6, dk=7, dv=8, dw=9, ws=10, wsb=1 << 30, D=64: lib.ttt_backward_fullbatch(  # noqa: E731
+        T.TTT_BF16, 1, 1, 64, D, 1.0, _p(0), _p(1), _p(2), _p(3), 0, None if do is None else _p(do),
+        None if dq is None else _p(dq), None if dk is None else _p(dk), None if dv is None else _p(dv),
+        None if dw is None else _p(dw), None if ws is None else _p(ws), wsb, None)
+    assert call(do=None) == 1
+    assert call(dw=None) == 1
+    assert call(dk=0) == 1               # a gradient output overlaps q
+    assert call(dv=6) == 1               # two outputs overlap
+    assert call(ws=None) == 3
+    assert call(wsb=16) == 3
+    assert call(D=48) == 2
+    assert T.ttt_workspace_size(T.TTT_OP_FULLBATCH_BWD, T.TTT_BF16, 64, 2, 3136, 32) > 0
 
 
 def test_fullbatch_epochs_validation():
