@@ -31,7 +31,8 @@ widened to float64 here); inner states are [H, ...] (shared over the batch) or
 
 Parity status: every function here is pinned by tests/test_oracle_pins.py
 (closed forms, special cases, finite differences, autograd, exact rational
-arithmetic) and tests/test_oracle_pins_epochs.py (fullbatch_epochs: closed form
+arithmetic; chunked_bidir_2d and grid_transpose in test_oracle_pins_2d.py) and
+tests/test_oracle_pins_epochs.py (fullbatch_epochs: closed form
 with orthogonal keys, convergence to least squares) and tests/test_oracle_pins_vjp.py
 (fullbatch_vjp: finite differences, torch autograd, eta = 0). None is "parity
 unpinned".
@@ -175,6 +176,32 @@ def chunked_bidir(q, k, v, w0, eta: float, chunk: int):
     rev = slice(None, None, -1)
     Or, Wr = _scan_noncausal(Q[:, :, rev], K[:, :, rev], V[:, :, rev], W0, eta, chunk)
     return _bnhd(Of + Or[:, :, rev]), Wf, Wr
+
+
+def grid_transpose(x, height: int, width: int):
+    """[B, height * width, ...] tokens in raster order -> the same tokens in column order (the
+    raster order of the transposed [width, height] grid)."""
+    x = np.asarray(x)
+    B = x.shape[0]
+    rest = x.shape[2:]
+    return np.ascontiguousarray(np.swapaxes(x.reshape((B, height, width) + rest), 1, 2).reshape((B, height * width) + rest))
+
+
+def chunked_bidir_2d(q, k, v, w0, eta: float, chunk: int, height: int, width: int):
+    """Bidirectional scans in raster order and in column order, summed.
+
+    The Vision-TTT summary (gist.science, "De Oplossing": the bidirectional scanner reads the image
+    left to right, right to left, and top to bottom) adds a column scan to the raster scans. Read
+    here as: the bidirectional scan of chunked_bidir over the tokens in raster order, plus the same
+    over the tokens in column order (top to bottom, column by column), its outputs put back in
+    raster order; all four directions start from the same W0.
+    Returns (O, [raster fwd end, raster rev end, column fwd end, column rev end]).
+    """
+    O1, Wf1, Wr1 = chunked_bidir(q, k, v, w0, eta, chunk)
+    qt, kt, vt = (grid_transpose(t, height, width) for t in (q, k, v))
+    O2t, Wf2, Wr2 = chunked_bidir(qt, kt, vt, w0, eta, chunk)
+    O2 = grid_transpose(O2t, width, height)
+    return O1 + O2, [Wf1, Wr1, Wf2, Wr2]
 
 
 # --------------------------------------------------------------------------------------------
