@@ -254,7 +254,11 @@ def extra_legs(T, torch, inputs, dev, time_rotated) -> dict:
     """Legs outside the suite step, each timed like the layers (cold, inputs rotated over > 1 GiB):
       * dwconv_kv_vittt_1280: the Vision-TTT Conv2d preprocessing, a depth-wise 3x3 convolution of
         K and of V over the 80 x 80 token grid (8 images, C = 3 x 64), bf16;
-      * vittt_bidir_1280_with_dwconv: that preprocessing followed by the bidirectional scan."""
+      * vittt_bidir_1280_with_dwconv: that preprocessing followed by the bidirectional scan;
+      * vittt_bidir2d_1280: the raster- plus column-order bidirectional scans of the 80 x 80 grid
+        (algorithmic bytes: q, k, v read and o written once);
+      * fullbatch_backward_hvit3t_stage1: the full-batch layer's backward pass (dQ, dK, dV, dW0) at
+        the H-ViT^3-T stage-1 shape, bf16."""
     name = "vittt_bidir_1280"
     if name not in inputs:
         return {}
@@ -280,8 +284,38 @@ def extra_legs(T, torch, inputs, dev, time_rotated) -> dict:
 
     conv_bytes = 4 * wl.B * wl.N * C * 2          # read K and V, write both convolved
     out = {}
+    fb = "hvit3t_stage1_fullbatch"
+    if fb in inputs:  # the full-batch layer's backward pass at the H-ViT^3-T stage-1 shape
+        fw = inputs[fb].wl
+        rs2 = np.random.default_rng(4343)
+        d_o = torch.from_numpy((rs2.standard_normal((fw.B, fw.N, fw.H, fw.D)) / np.sqrt(fw.D)).astype(np.float32)
+                               ).cuda().to(torch.bfloat16)
+        need_b = T.ttt_workspace_size(T.TTT_OP_FULLBATCH_BWD, T.TTT_BF16, fw.B, fw.H, fw.N, fw.D)
+        wsb = torch.empty(need_b, dtype=torch.uint8, device="cuda")
+        grads = [torch.empty_like(dev[fb]["q"]) for _ in range(3)]
+        dw0 = torch.empty((fw.B, fw.H, fw.D, fw.D), dtype=torch.float32, device="cuda")
+
+        def bwd(d):
+            return lambda: T.ttt_backward_fullbatch(d["q"], d["k"], d["v"], d["w0"], d_o, fw.eta, d_q=grads[0],
+                                                    d_k=grads[1], d_v=grads[2], d_w0=dw0, workspace=wsb)
+
+        nb = 7 * fw.B * fw.N * fw.H * fw.D * 2    # read q, k, v, dO; write dq, dk, dv
+        cold, warm, nsets = time_rotated(bwd, dev[fb], nb)
+        sec = cold / 1000.0
+        out["fullbatch_backward_hvit3t_stage1"] = {
+            "ms": round(cold, 5), "ms_warm": round(warm, 5), "tokens_per_s": fw.tokens / sec, "alg_bytes": nb,
+            "alg_GBs": nb / sec / 1e9, "hbm_frac": nb / sec / 1e9 / PEAK_HBM_GBS,
+            "timing": f"cold: inputs rotated over {nsets} copies (> 1 GiB); dO fixed"}
+    need2 = T.ttt_workspace_size(T.TTT_OP_BIDIR2D, T.TTT_BF16, wl.B, wl.H, wl.N, wl.D, 0, wl.chunk)
+    ws2 = torch.empty(need2, dtype=torch.uint8, device="cuda")
+
+    def scan2d(d):
+        return lambda: T.ttt_forward_chunked_bidir2d(d["q"], d["k"], d["v"], d["w0"], wl.chunk, Hi, Wi, wl.eta,
+                                                     o=d["o"], workspace=ws2)
+
     for leg, make, nbytes in (("dwconv_kv_vittt_1280", conv, conv_bytes),
-                              ("vittt_bidir_1280_with_dwconv", chain, conv_bytes + wl.io_bytes)):
+                              ("vittt_bidir_1280_with_dwconv", chain, conv_bytes + wl.io_bytes),
+                              ("vittt_bidir2d_1280", scan2d, wl.io_bytes)):
         cold, warm, nsets = time_rotated(make, dev[name], nbytes)
         s = cold / 1000.0
         out[leg] = {"ms": round(cold, 5), "ms_warm": round(warm, 5), "tokens_per_s": wl.tokens / s,

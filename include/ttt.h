@@ -74,7 +74,8 @@ typedef enum {
   TTT_OP_CAUSAL = 1,
   TTT_OP_BIDIR = 2,
   TTT_OP_MLP = 3,
-  TTT_OP_FULLBATCH_BWD = 4
+  TTT_OP_FULLBATCH_BWD = 4,
+  TTT_OP_BIDIR2D = 5
 } ttt_op;
 
 /*
@@ -148,6 +149,22 @@ ttt_status ttt_forward_chunked_bidir(ttt_dtype dt, int B, int H, int N, int D, i
                                      const float* w0, long long w0_batch_stride,
                                      void* o, float* w_out,
                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * 2-D bidirectional layer: the bidirectional scan of ttt_forward_chunked_bidir over the tokens in
+ * raster order plus the same scan over the tokens in column order (top to bottom, column by
+ * column: the Vision-TTT summary on gist.science, "De Oplossing", has the scanner read the image
+ * top to bottom as well), summed; all four directions start from W0. The N = height * width
+ * tokens of each batch element are an image in raster order (token i * width + j is pixel (i, j)).
+ * w_out (nullable): fp32 [4, B, H, D, D]: raster forward end, raster reverse end, column forward
+ * end, column reverse end. Workspace: ttt_workspace_size(TTT_OP_BIDIR2D, ..., N, D, 0, chunk) with
+ * N = height * width (the inputs and output in column order, and the scans' workspace).
+ */
+ttt_status ttt_forward_chunked_bidir2d(ttt_dtype dt, int B, int H, int height, int width, int D,
+                                       int chunk, float eta, const void* q, const void* k,
+                                       const void* v, const float* w0, long long w0_batch_stride,
+                                       void* o, float* w_out,
+                                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Causal mini-batch TTT-MLP (TTT-Linear / TTT-MLP abstract: the hidden state is a two-layer

@@ -135,6 +135,11 @@ size_t ttt_workspace_size(ttt_op op, ttt_dtype dt, int B, int H, int N, int D, i
     case TTT_OP_BIDIR:
       if (!supported_chunk(chunk) || N % chunk != 0) return 0;
       return round_up(ttt::chunked_workspace_bytes(op == TTT_OP_BIDIR, bf, B, H, N, D, chunk), 256);
+    case TTT_OP_BIDIR2D: {
+      if (!supported_chunk(chunk) || N % chunk != 0) return 0;
+      const size_t act = round_up((size_t)B * N * H * D * elem_size(dt), 256);
+      return 4 * act + round_up(ttt::chunked_workspace_bytes(true, bf, B, H, N, D, chunk), 256);
+    }
     case TTT_OP_MLP:
       if (!ttt::mlp_supported(D, Dh, chunk) || N % chunk != 0) return 0;
       return round_up(ttt::mlp_workspace_bytes(bf, B, H, N, D, Dh, chunk), 256);
@@ -236,6 +241,59 @@ ttt_status ttt_forward_chunked_bidir(ttt_dtype dt, int B, int H, int N, int D, i
   return from_hip(ttt::chunked_launch(true, dt == TTT_BF16, B, H, N, D, chunk, eta, q, k, v, w0,
                                       w0_batch_stride, o, w_out, workspace,
                                       static_cast<hipStream_t>(stream)));
+}
+
+ttt_status ttt_forward_chunked_bidir2d(ttt_dtype dt, int B, int H, int height, int width, int D,
+                                       int chunk, float eta, const void* q, const void* k,
+                                       const void* v, const float* w0, long long w0_batch_stride,
+                                       void* o, float* w_out, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  if (height <= 0 || width <= 0) return TTT_ERR_INVALID;
+  if ((long long)height * width > 0x7fffffffll) return TTT_ERR_UNSUPPORTED;
+  const int N = height * width;
+  // The bidirectional checks cover the inputs, o and the first two w_out states; the column scan
+  // writes the other two.
+  ttt_status st = check_linear(TTT_OP_BIDIR, dt, B, H, N, D, chunk, eta, q, k, v, w0,
+                               w0_batch_stride, o, w_out, nullptr, 0, false);
+  if (st != TTT_OK) return st;
+  const size_t act = (size_t)B * N * H * D * elem_size(dt);
+  const size_t dd = (size_t)B * H * D * D;
+  const Range rq = range_of(q, act), rk = range_of(k, act), rv = range_of(v, act);
+  const Range rw0 = range_of(w0, state_bytes(B, H, (size_t)D * D, w0_batch_stride));
+  if (w_out) {
+    const Range rwo = range_of(w_out, 4 * dd * sizeof(float));
+    if (overlaps(rwo, rq) || overlaps(rwo, rk) || overlaps(rwo, rv) || overlaps(rwo, rw0) ||
+        overlaps(rwo, range_of(o, act)))
+      return TTT_ERR_INVALID;
+  }
+  const size_t need = ttt_workspace_size(TTT_OP_BIDIR2D, dt, B, H, N, D, 0, chunk);
+  if (!workspace || workspace_bytes < need) return TTT_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return TTT_ERR_INVALID;
+  const Range rws = range_of(workspace, need);
+  if (overlaps(rws, rq) || overlaps(rws, rk) || overlaps(rws, rv) || overlaps(rws, rw0) ||
+      overlaps(rws, range_of(o, act)) || (w_out && overlaps(rws, range_of(w_out, 4 * dd * 4))))
+    return TTT_ERR_INVALID;
+  // Workspace: q, k, v and the output in column order, then the scans' own workspace.
+  char* wsb = static_cast<char*>(workspace);
+  const size_t actp = round_up(act, 256);
+  void* qt = wsb;
+  void* kt = wsb + actp;
+  void* vt = wsb + 2 * actp;
+  void* ot = wsb + 3 * actp;
+  void* scan_ws = wsb + 4 * actp;
+  const bool bf = dt == TTT_BF16;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const void* srcs[3] = {q, k, v};
+  void* dsts[3] = {qt, kt, vt};
+  hipError_t e = ttt::gather_columns_launch(bf, B, height, width, H * D, srcs, dsts, 3, s);
+  if (e == hipSuccess)
+    e = ttt::chunked_launch(true, bf, B, H, N, D, chunk, eta, q, k, v, w0, w0_batch_stride, o, w_out,
+                            scan_ws, s);
+  if (e == hipSuccess)
+    e = ttt::chunked_launch(true, bf, B, H, N, D, chunk, eta, qt, kt, vt, w0, w0_batch_stride, ot,
+                            w_out ? w_out + 2 * dd : nullptr, scan_ws, s);
+  if (e == hipSuccess) e = ttt::add_columns_launch(bf, B, height, width, H * D, ot, o, s);
+  return from_hip(e);
 }
 
 ttt_status ttt_mlp_forward(ttt_dtype dt, int B, int H, int N, int D, int Dh, int chunk, float eta,

@@ -40,6 +40,13 @@ hipError_t mlp_launch(bool bf16_io, int B, int H, int N, int D, int Dh, int chun
                       const float* w2, long long w_bstride, void* o, float* w1_out,
                       float* w2_out, void* ws, hipStream_t st);
 
+// ---- token-grid permutations (column order) ---------------------------------------------------
+hipError_t gather_columns_launch(bool bf16_io, int B, int Hg, int Wg, int C,
+                                 const void* const src[3], void* const dst[3], int count,
+                                 hipStream_t st);
+hipError_t add_columns_launch(bool bf16_io, int B, int Hg, int Wg, int C, const void* ot, void* o,
+                              hipStream_t st);
+
 // ---- depth-wise 3x3 convolution over the token grid ------------------------------------------
 hipError_t dwconv_launch(bool bf16_io, int B, int Hi, int Wi, int C, const void* x,
                          const float* w, const float* bias, void* y, hipStream_t st);

@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(HERE, "libttt.so")
 
 TTT_OK, TTT_ERR_INVALID, TTT_ERR_UNSUPPORTED, TTT_ERR_WORKSPACE, TTT_ERR_HIP = range(5)
 TTT_F32, TTT_BF16 = 0, 1
-TTT_OP_FULLBATCH, TTT_OP_CAUSAL, TTT_OP_BIDIR, TTT_OP_MLP, TTT_OP_FULLBATCH_BWD = range(5)
+TTT_OP_FULLBATCH, TTT_OP_CAUSAL, TTT_OP_BIDIR, TTT_OP_MLP, TTT_OP_FULLBATCH_BWD, TTT_OP_BIDIR2D = range(6)
 TTT_NOALLOC_SCRATCH_BYTES = 32 << 20  # static scratch of ttt_forward_fullbatch_noalloc, per device
 
 # Every symbol include/ttt.h declares, with its ctypes signature.
@@ -26,6 +26,8 @@ SIGNATURES = {
                                               _vp, _vp, _c_ll, _vp, _vp, _vp, _sz, _vp]),
     "ttt_backward_fullbatch": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _vp, _vp, _vp, _vp, _c_ll,
                                         _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "ttt_forward_chunked_bidir2d": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _vp,
+                                             _vp, _vp, _vp, _c_ll, _vp, _vp, _vp, _sz, _vp]),
     "ttt_forward_chunked_causal": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _vp, _vp, _vp,
                                             _vp, _c_ll, _vp, _vp, _vp, _sz, _vp]),
     "ttt_forward_chunked_bidir": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _vp, _vp, _vp,
@@ -259,6 +261,31 @@ def ttt_forward_chunked_bidir(q, k, v, w0, chunk: int, eta: float = 1.0, *, o=No
     w_out: fp32 [2, B, H, D, D] (forward end state, reverse end state)."""
     return _linear(TTT_OP_BIDIR, "ttt_forward_chunked_bidir", q, k, v, w0, chunk, eta, o, w_out, workspace,
                    stream)
+
+
+def ttt_forward_chunked_bidir2d(q, k, v, w0, chunk: int, height: int, width: int, eta: float = 1.0, *, o=None,
+                                w_out=None, workspace=None, stream=None):
+    """Bidirectional scans in raster order and in column order of the height x width token grid,
+    summed. w_out: fp32 [4, B, H, D, D]. Returns o."""
+    lib = load_library()
+    _check_io(q, k, v)
+    torch = _torch()
+    B, N, H, D = q.shape
+    if N != height * width:
+        raise ValueError(f"{N} tokens are not a {height} x {width} grid")
+    dev = q.device
+    dt = _dtype_code(q)
+    stride = _state_stride("w0", w0, B, H, D, D, dev)
+    _check_out("o", o, q.shape, q.dtype, dev)
+    _check_out("w_out", w_out, (4, B, H, D, D), torch.float32, dev)
+    with torch.cuda.device(dev):
+        o = torch.empty_like(q) if o is None else o
+        ws, ws_size = _workspace(TTT_OP_BIDIR2D, dt, B, H, N, D, 0, chunk, workspace, dev)
+        st = lib.ttt_forward_chunked_bidir2d(dt, B, H, int(height), int(width), D, int(chunk), float(eta), _ptr(q),
+                                             _ptr(k), _ptr(v), _ptr(w0), stride, _ptr(o), _ptr(w_out), _ptr(ws),
+                                             ws_size, _stream(stream, dev))
+    _raise(st, "ttt_forward_chunked_bidir2d")
+    return o
 
 
 def ttt_mlp_forward(q, k, v, w1, w2, chunk: int, eta: float = 1.0, *, o=None, w1_out=None, w2_out=None,

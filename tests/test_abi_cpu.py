@@ -26,7 +26,23 @@ def test_header_declares_the_entry_points():
     assert _declared_functions() == sorted([
         "ttt_forward_fullbatch", "ttt_forward_chunked_causal", "ttt_forward_chunked_bidir", "ttt_mlp_forward",
         "ttt_workspace_size", "ttt_status_string", "ttt_forward_fullbatch_noalloc", "ttt_dwconv3x3",
-        "ttt_forward_fullbatch_epochs", "ttt_backward_fullbatch"])
+        "ttt_forward_fullbatch_epochs", "ttt_backward_fullbatch", "ttt_forward_chunked_bidir2d"])
+
+
+def test_bidir2d_validation_rejects_before_launch():
+    lib = T.load_library()
+    call = lambda hg=8, wg=8, chunk=16, ws=5, wsb=1 << 30, o=4, wout=None: lib.ttt_forward_chunked_bidir2d(  # noqa: E731
+        T.TTT_BF16, 1, 1, hg, wg, 64, chunk, 1.0, _p(0), _p(1), _p(2), _p(3), 0, None if o is None else _p(o),
+        None if wout is None else _p(wout), None if ws is None else _p(ws), wsb, None)
+    assert call(hg=0) == 1
+    assert call(o=None) == 1
+    assert call(chunk=24) == 2
+    assert call(hg=5, wg=5) == 1          # 25 tokens: not a multiple of the chunk
+    assert call(ws=None) == 3
+    assert call(wsb=64) == 3
+    assert call(wout=1) == 1              # end states overlap k
+    assert T.ttt_workspace_size(T.TTT_OP_BIDIR2D, T.TTT_BF16, 8, 3, 6400, 64, 0, 64) > \
+        4 * 8 * 6400 * 3 * 64 * 2
 
 
 def test_backward_validation_rejects_before_launch():

@@ -586,3 +586,30 @@ def test_fullbatch_epochs_parity(wl, epochs):
         ref1 = lib.ttt_forward_fullbatch(q, k, v, w0, wl.eta)
         torch.cuda.synchronize()
         assert torch.equal(out, ref1)
+
+
+# ------------------------------------------------------------------ 2-D bidirectional scans
+BIDIR2D_CASES = [
+    (W["vittt_bidir_1280"].with_(B=2, seed=181), 80, 80),                        # Vision-TTT 1280^2 grid
+    (W["vittt_bidir_1280"].with_(B=1, N=24 * 40, H=2, D=32, chunk=16, seed=182), 24, 40),
+    (W["vittt_bidir_1280"].with_(B=2, N=12 * 16, H=1, D=16, chunk=32, seed=183), 12, 16),  # chunks span columns
+    (W["vittt_bidir_1280"].with_(B=1, N=8 * 16, H=2, D=64, chunk=16, dtype="fp32", seed=184), 8, 16),
+]
+
+
+@pytest.mark.parametrize("wl,hg,wg", BIDIR2D_CASES, ids=lambda v: f"{v.dtype}-B{v.B}H{v.H}D{v.D}c{v.chunk}"
+                         if hasattr(v, "dtype") else str(v))
+def test_bidir2d_parity(wl, hg, wg):
+    lib = T()
+    print(f"bidir2d {wl.dtype} B={wl.B} {hg}x{wg} H={wl.H} D={wl.D} b={wl.chunk}", flush=True)
+    x = synth.make_inputs(wl)
+    q, k, v = dev(x.q, wl.dtype), dev(x.k, wl.dtype), dev(x.v, wl.dtype)
+    so = torch.full((4, wl.B, wl.H, wl.D, wl.D), float("nan"), device="cuda")
+    out = lib.ttt_forward_chunked_bidir2d(q, k, v, torch.from_numpy(x.w0).cuda(), wl.chunk, hg, wg, wl.eta,
+                                          w_out=so)
+    torch.cuda.synchronize()
+    ref_o, ref_w = O.chunked_bidir_2d(x.q64, x.k64, x.v64, x.w0, wl.eta, wl.chunk, hg, wg)
+    assert report("bidir2d", host(out), ref_o) <= tol(wl)
+    st = so.cpu().numpy()
+    for i in range(4):
+        assert np.abs(st[i] - ref_w[i]).max() / np.abs(ref_w[i]).max() <= tol(wl), i
