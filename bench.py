@@ -258,7 +258,9 @@ def extra_legs(T, torch, inputs, dev, time_rotated) -> dict:
       * vittt_bidir2d_1280: the raster- plus column-order bidirectional scans of the 80 x 80 grid
         (algorithmic bytes: q, k, v read and o written once);
       * fullbatch_backward_hvit3t_stage1: the full-batch layer's backward pass (dQ, dK, dV, dW0) at
-        the H-ViT^3-T stage-1 shape, bf16."""
+        the H-ViT^3-T stage-1 shape, bf16;
+      * block_epilogue_hvit3t_stage1: the ViT^3 block epilogue over that layer's 200,704 tokens
+        (C = C_out = 64), bf16."""
     name = "vittt_bidir_1280"
     if name not in inputs:
         return {}
@@ -299,6 +301,25 @@ def extra_legs(T, torch, inputs, dev, time_rotated) -> dict:
             return lambda: T.ttt_backward_fullbatch(d["q"], d["k"], d["v"], d["w0"], d_o, fw.eta, d_q=grads[0],
                                                     d_k=grads[1], d_v=grads[2], d_w0=dw0, workspace=wsb)
 
+        # the ViT^3 block epilogue at this width: [O * sigmoid(G), X] Wo^T + b over the layer's tokens
+        Mt, Ct = fw.B * fw.N, fw.H * fw.D
+        ep_in = {key: torch.from_numpy((rs2.standard_normal((Mt, Ct)) * 0.3).astype(np.float32)).cuda()
+                 .to(torch.bfloat16) for key in ("q", "k", "v")}
+        wpj = torch.from_numpy((rs2.standard_normal((Ct, 2 * Ct)) / np.sqrt(2 * Ct)).astype(np.float32)).cuda() \
+            .to(torch.bfloat16)
+        bpj = torch.zeros(Ct, dtype=torch.float32, device="cuda")
+        yep = torch.empty((Mt, Ct), dtype=torch.bfloat16, device="cuda")
+
+        def epi(d):
+            return lambda: T.ttt_block_epilogue(d["q"], d["k"], d["v"], wpj, bpj, y=yep)
+
+        nbe = 4 * Mt * Ct * 2                      # read O, G, X; write y
+        cold, warm, nsets = time_rotated(epi, ep_in, nbe)
+        sec = cold / 1000.0
+        out["block_epilogue_hvit3t_stage1"] = {
+            "ms": round(cold, 5), "ms_warm": round(warm, 5), "tokens_per_s": Mt / sec, "alg_bytes": nbe,
+            "alg_GBs": nbe / sec / 1e9, "hbm_frac": nbe / sec / 1e9 / PEAK_HBM_GBS,
+            "timing": f"cold: inputs rotated over {nsets} copies (> 1 GiB); M = {Mt} tokens, C = C_out = {Ct}"}
         nb = 7 * fw.B * fw.N * fw.H * fw.D * 2    # read q, k, v, dO; write dq, dk, dv
         cold, warm, nsets = time_rotated(bwd, dev[fb], nb)
         sec = cold / 1000.0

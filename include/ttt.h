@@ -209,6 +209,21 @@ ttt_status ttt_dwconv3x3(ttt_dtype dt, int B, int height, int width, int C, cons
                          const float* weight, const float* bias, void* y, void* stream);
 
 /*
+ * ViT^3 block epilogue (ViT^3 review on techloop.online, "TTT Block" section and the section on the
+ * official code: a GLU-style main branch and a 3x3 depth-wise convolution branch in parallel, their
+ * outputs concatenated and projected back to the block's width). Per token m:
+ *   y[m] = [o[m] * sigmoid(gate[m]), xconv[m]] w_proj^T + bias
+ * o, gate, xconv: [M, C] (e.g. M = B * N tokens of the TTT layer's output, its gate, and the
+ * convolution branch from ttt_dwconv3x3); w_proj: [C_out, 2C] (a linear layer's [out, in] layout),
+ * all of dtype dt; bias fp32 [C_out] or NULL; y: [M, C_out] of dtype dt. bf16 accumulates in fp32
+ * on the matrix cores (the gated values are rounded to bf16 as operands). C must be a multiple of
+ * 32, C_out of 64; pointers 16-byte aligned (bias 4-byte); y must not overlap an input.
+ */
+ttt_status ttt_block_epilogue(ttt_dtype dt, int M, int C, int C_out, const void* o,
+                              const void* gate, const void* xconv, const void* w_proj,
+                              const float* bias, void* y, void* stream);
+
+/*
  * For callers that cannot allocate device memory (code under HIP graph capture, tight serving
  * loops, harnesses that forbid allocation): ttt_forward_fullbatch without a workspace argument.
  * Its scratch is a static device array of TTT_NOALLOC_SCRATCH_BYTES per device, which each device

@@ -13,7 +13,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libttt.so")
-SOURCES = ["abi.hip", "fullbatch.hip", "chunked.hip", "mlp.hip", "dwconv.hip", "grid.hip"]
+SOURCES = ["abi.hip", "fullbatch.hip", "chunked.hip", "mlp.hip", "dwconv.hip", "grid.hip", "epilogue.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed fp32 ops are disabled for all device code: hipcc would otherwise form v_pk_* fp32

@@ -364,6 +364,28 @@ ttt_status ttt_dwconv3x3(ttt_dtype dt, int B, int height, int width, int C, cons
                                      static_cast<hipStream_t>(stream)));
 }
 
+ttt_status ttt_block_epilogue(ttt_dtype dt, int M, int C, int C_out, const void* o,
+                              const void* gate, const void* xconv, const void* w_proj,
+                              const float* bias, void* y, void* stream) {
+  if (dt != TTT_F32 && dt != TTT_BF16) return TTT_ERR_INVALID;
+  if (M <= 0 || C <= 0 || C_out <= 0) return TTT_ERR_INVALID;
+  if (!o || !gate || !xconv || !w_proj || !y) return TTT_ERR_INVALID;
+  if (C % 32 != 0 || C_out % 64 != 0 || C > 4096 || C_out > 65535 * 64) return TTT_ERR_UNSUPPORTED;
+  if ((long long)M * (C > C_out ? C : C_out) > (1ll << 40)) return TTT_ERR_UNSUPPORTED;
+  if (!aligned16(o) || !aligned16(gate) || !aligned16(xconv) || !aligned16(w_proj) || !aligned16(y) ||
+      (bias && (reinterpret_cast<uintptr_t>(bias) & 3u)))
+    return TTT_ERR_INVALID;
+  const size_t es = elem_size(dt);
+  const Range ry = range_of(y, (size_t)M * C_out * es);
+  if (overlaps(ry, range_of(o, (size_t)M * C * es)) || overlaps(ry, range_of(gate, (size_t)M * C * es)) ||
+      overlaps(ry, range_of(xconv, (size_t)M * C * es)) ||
+      overlaps(ry, range_of(w_proj, (size_t)C_out * 2 * C * es)) ||
+      (bias && overlaps(ry, range_of(bias, (size_t)C_out * sizeof(float)))))
+    return TTT_ERR_INVALID;
+  return from_hip(ttt::epilogue_launch(dt == TTT_BF16, M, C, C_out, o, gate, xconv, w_proj, bias, y,
+                                       static_cast<hipStream_t>(stream)));
+}
+
 ttt_status ttt_forward_fullbatch_noalloc(ttt_dtype dt, int B, int H, int N, int D, float eta,
                                          const void* q, const void* k, const void* v,
                                          const float* w0, long long w0_batch_stride, void* o,

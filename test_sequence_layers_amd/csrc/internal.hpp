@@ -47,6 +47,11 @@ hipError_t gather_columns_launch(bool bf16_io, int B, int Hg, int Wg, int C,
 hipError_t add_columns_launch(bool bf16_io, int B, int Hg, int Wg, int C, const void* ot, void* o,
                               hipStream_t st);
 
+// ---- ViT^3 block epilogue ---------------------------------------------------------------------
+hipError_t epilogue_launch(bool bf16_io, int M, int C, int Cout, const void* o, const void* gate,
+                           const void* xc, const void* wo, const float* bias, void* y,
+                           hipStream_t st);
+
 // ---- depth-wise 3x3 convolution over the token grid ------------------------------------------
 hipError_t dwconv_launch(bool bf16_io, int B, int Hi, int Wi, int C, const void* x,
                          const float* w, const float* bias, void* y, hipStream_t st);

@@ -37,6 +37,7 @@ SIGNATURES = {
     "ttt_forward_fullbatch_noalloc": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _vp, _vp, _vp, _vp,
                                                _c_ll, _vp, _vp, _vp]),
     "ttt_dwconv3x3": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp]),
+    "ttt_block_epilogue": (_c_int, [_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "ttt_workspace_size": (_sz, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
     "ttt_status_string": (ctypes.c_char_p, [_c_int]),
 }
@@ -343,4 +344,33 @@ def ttt_dwconv3x3(x, weight, bias=None, *, height: int, width: int, y=None, stre
         st = lib.ttt_dwconv3x3(dt, B, int(height), int(width), C, _ptr(x), _ptr(weight), _ptr(bias), _ptr(y),
                                _stream(stream, dev))
     _raise(st, "ttt_dwconv3x3")
+    return y
+
+
+def ttt_block_epilogue(o, gate, xconv, w_proj, bias=None, *, y=None, stream=None):
+    """y = [o * sigmoid(gate), xconv] w_proj^T + bias per token. o, gate, xconv: [..., C] (the
+    leading dims are the tokens); w_proj [C_out, 2C] of the same dtype; bias fp32 [C_out] or None.
+    Returns y [..., C_out]."""
+    lib = load_library()
+    torch = _torch()
+    if not isinstance(o, torch.Tensor) or not o.is_cuda:
+        raise TypeError("o must be a CUDA (HIP) tensor")
+    dev = o.device
+    dt = _dtype_code(o)
+    C = int(o.shape[-1])
+    M = int(o.numel() // C)
+    for name, t in (("o", o), ("gate", gate), ("xconv", xconv)):
+        _check_tensor(name, t, o.shape, o.dtype, dev)
+    if w_proj.dim() != 2 or int(w_proj.shape[1]) != 2 * C:
+        raise ValueError("w_proj must be [C_out, 2C]")
+    Co = int(w_proj.shape[0])
+    _check_tensor("w_proj", w_proj, (Co, 2 * C), o.dtype, dev)
+    _check_out("bias", bias, (Co,), torch.float32, dev)
+    out_shape = tuple(o.shape[:-1]) + (Co,)
+    _check_out("y", y, out_shape, o.dtype, dev)
+    with torch.cuda.device(dev):
+        y = torch.empty(out_shape, dtype=o.dtype, device=dev) if y is None else y
+        st = lib.ttt_block_epilogue(dt, M, C, Co, _ptr(o), _ptr(gate), _ptr(xconv), _ptr(w_proj), _ptr(bias), _ptr(y),
+                                    _stream(stream, dev))
+    _raise(st, "ttt_block_epilogue")
     return y

@@ -26,7 +26,20 @@ def test_header_declares_the_entry_points():
     assert _declared_functions() == sorted([
         "ttt_forward_fullbatch", "ttt_forward_chunked_causal", "ttt_forward_chunked_bidir", "ttt_mlp_forward",
         "ttt_workspace_size", "ttt_status_string", "ttt_forward_fullbatch_noalloc", "ttt_dwconv3x3",
-        "ttt_forward_fullbatch_epochs", "ttt_backward_fullbatch", "ttt_forward_chunked_bidir2d"])
+        "ttt_forward_fullbatch_epochs", "ttt_backward_fullbatch", "ttt_forward_chunked_bidir2d",
+        "ttt_block_epilogue"])
+
+
+def test_block_epilogue_validation():
+    lib = T.load_library()
+    call = lambda C=64, Co=64, y=4, o=0: lib.ttt_block_epilogue(T.TTT_BF16, 128, C, Co, None if o is None else _p(o),  # noqa: E731
+                                                               _p(1), _p(2), _p(3), None, None if y is None else _p(y),
+                                                               None)
+    assert call(o=None) == 1
+    assert call(y=None) == 1
+    assert call(C=48) == 2
+    assert call(Co=96) == 2
+    assert call(y=0) == 1
 
 
 def test_bidir2d_validation_rejects_before_launch():
