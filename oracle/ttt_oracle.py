@@ -34,7 +34,9 @@ Parity status: every function here is pinned by tests/test_oracle_pins.py
 arithmetic; chunked_bidir_2d and grid_transpose in test_oracle_pins_2d.py) and
 tests/test_oracle_pins_epochs.py (fullbatch_epochs: closed form
 with orthogonal keys, convergence to least squares) and tests/test_oracle_pins_vjp.py
-(fullbatch_vjp: finite differences, torch autograd, eta = 0). None is "parity
+(fullbatch_vjp: finite differences, torch autograd, eta = 0) and
+tests/test_oracle_pins_chunked_vjp.py (chunked_causal_vjp, chunked_bidir_vjp: finite differences,
+torch autograd of the dual form, eta = 0, one chunk = the full-batch gradients). None is "parity
 unpinned".
 """
 from __future__ import annotations
@@ -231,6 +233,85 @@ def chunked_causal(q, k, v, w0, eta: float, chunk: int):
             O[:, :, i:i + 1] = qi @ (Ws - a * S)     # token i's own weights
         W = Ws - a * S
     return _bnhd(O), W
+
+
+def _scan_vjp(Q, K, V, W0, dO, eta: float, b: int, causal: bool):
+    """Reverse mode through the primal mini-batch loop of one scan direction ([B, H, N, D] arrays,
+    tokens in the scan's order).
+
+    Forward, per chunk with start state W_s and a = eta/b: e_j = k_j W_s - v_j, S_i = sum over the
+    chunk's tokens j <= i (causal) or all of them (read-out after the update) of k_j^T e_j,
+    o_i = q_i (W_s - a S_i), and the chunk hands W_s - a S_last on. Backward, chunks last to first,
+    with lam = dL/d(state handed on) (zero after the last chunk):
+        dq_i   = do_i (W_s - a S_i)^T
+        Gam_j  = -a (lam + sum of q_i^T do_i over the outputs i whose S_i contains token j)
+        de_j   = k_j Gam_j                 (S_i holds k_j^T e_j)
+        dk_j   = e_j Gam_j^T + de_j W_s^T  (through k_j^T e_j and through e_j = k_j W_s - v_j)
+        dv_j   = -de_j
+        lam   <- lam + sum_i q_i^T do_i + sum_j k_j^T de_j   (= dL/dW_s)
+    Returns (dQ, dK, dV, dW0) with dW0 [B, H, D, D]."""
+    B, H, N, D = Q.shape
+    a = eta / b
+    starts = []
+    W = W0.copy()
+    for c0 in range(0, N, b):  # forward pass: every chunk's start state
+        starts.append(W)
+        Kc, Vc = K[:, :, c0:c0 + b], V[:, :, c0:c0 + b]
+        W = W - a * (_t(Kc) @ (Kc @ W - Vc))
+    dQ, dK, dV = np.zeros_like(Q), np.zeros_like(K), np.zeros_like(V)
+    lam = np.zeros_like(W0)
+    for ci in range(N // b - 1, -1, -1):
+        c0 = ci * b
+        Ws = starts[ci]
+        rows = [c0 + i for i in range(b)]
+        e = {j: K[:, :, j:j + 1] @ Ws - V[:, :, j:j + 1] for j in rows}
+        qdo = {i: _t(Q[:, :, i:i + 1]) @ dO[:, :, i:i + 1] for i in rows}
+        S = np.zeros_like(Ws)
+        total_qdo = sum(qdo.values())
+        for i in rows:  # read-out weights of each output
+            S = S + _t(K[:, :, i:i + 1]) @ e[i]
+            Wi = Ws - a * (S if causal else _t(K[:, :, c0:c0 + b]) @ (K[:, :, c0:c0 + b] @ Ws - V[:, :, c0:c0 + b]))
+            dQ[:, :, i:i + 1] = dO[:, :, i:i + 1] @ _t(Wi)
+        lam_prev = lam + total_qdo
+        later = np.zeros_like(Ws)  # sum of q_i^T do_i over outputs i >= j (causal)
+        for j in reversed(rows):
+            later = later + qdo[j]
+            Gam = -a * (lam + (later if causal else total_qdo))
+            kj = K[:, :, j:j + 1]
+            de = kj @ Gam
+            dK[:, :, j:j + 1] = e[j] @ _t(Gam) + de @ _t(Ws)
+            dV[:, :, j:j + 1] = -de
+            lam_prev = lam_prev + _t(kj) @ de
+        lam = lam_prev
+    return dQ, dK, dV, lam
+
+
+def chunked_causal_vjp(q, k, v, w0, eta: float, chunk: int, d_o):
+    """Gradients of the causal chunked TTT-Linear layer (chunked_causal) for the outer training
+    loop: (dL/dq, dL/dk, dL/dv, dL/dW0) for L = <dO, O>, by reverse mode through the primal loop
+    (the pages' authors derive the inner gradient by hand: ViT^3 review, section on the official
+    code; the outer gradient here follows the same closed-form style). dW0 is per batch element
+    [B, H, D, D]; a W0 shared over the batch gets the sum over B."""
+    Q, K, V, dO = _bhnd(q), _bhnd(k), _bhnd(v), _bhnd(d_o)
+    B, H, N, D = Q.shape
+    _check_chunk(N, chunk)
+    dQ, dK, dV, dW0 = _scan_vjp(Q, K, V, _state(w0, B, H), dO, eta, chunk, causal=True)
+    return _bnhd(dQ), _bnhd(dK), _bnhd(dV), dW0
+
+
+def chunked_bidir_vjp(q, k, v, w0, eta: float, chunk: int, d_o):
+    """Gradients of the bidirectional scan (chunked_bidir): the forward scan's and the reversed
+    scan's gradients summed (both read the same q, k, v, W0 and receive the same dO, the reversed
+    one in its own token order). Returns (dq, dk, dv [B,N,H,D], dW0 [B,H,D,D])."""
+    Q, K, V, dO = _bhnd(q), _bhnd(k), _bhnd(v), _bhnd(d_o)
+    B, H, N, D = Q.shape
+    _check_chunk(N, chunk)
+    W0 = _state(w0, B, H)
+    gf = _scan_vjp(Q, K, V, W0, dO, eta, chunk, causal=False)
+    rev = slice(None, None, -1)
+    gr = _scan_vjp(Q[:, :, rev], K[:, :, rev], V[:, :, rev], W0, dO[:, :, rev], eta, chunk, causal=False)
+    grads = [_bnhd(f + r[:, :, rev]) for f, r in zip(gf[:3], gr[:3])]
+    return grads[0], grads[1], grads[2], gf[3] + gr[3]
 
 
 def gelu(x):
