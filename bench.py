@@ -260,7 +260,10 @@ def extra_legs(T, torch, inputs, dev, time_rotated) -> dict:
       * fullbatch_backward_hvit3t_stage1: the full-batch layer's backward pass (dQ, dK, dV, dW0) at
         the H-ViT^3-T stage-1 shape, bf16;
       * block_epilogue_hvit3t_stage1: the ViT^3 block epilogue over that layer's 200,704 tokens
-        (C = C_out = 64), bf16."""
+        (C = C_out = 64), bf16;
+      * causal_backward_16k, bidir_backward_vittt_1280: the backward passes (dQ, dK, dV, dW0) of the
+        causal TTT-Linear layer (2 x 16384 x 12 x 64, b = 16) and of the Vision-TTT bidirectional
+        scan (8 x 6400 x 3 x 64, b = 64), bf16."""
     name = "vittt_bidir_1280"
     if name not in inputs:
         return {}
@@ -327,6 +330,32 @@ def extra_legs(T, torch, inputs, dev, time_rotated) -> dict:
             "ms": round(cold, 5), "ms_warm": round(warm, 5), "tokens_per_s": fw.tokens / sec, "alg_bytes": nb,
             "alg_GBs": nb / sec / 1e9, "hbm_frac": nb / sec / 1e9 / PEAK_HBM_GBS,
             "timing": f"cold: inputs rotated over {nsets} copies (> 1 GiB); dO fixed"}
+    # backward passes of the chunked layers at their full sizes (dO fixed, inputs rotated)
+    for lname, leg, op, fn in (("ttt_linear_causal_16k", "causal_backward_16k", T.TTT_OP_CAUSAL_BWD,
+                                T.ttt_backward_chunked_causal),
+                               ("vittt_bidir_1280", "bidir_backward_vittt_1280", T.TTT_OP_BIDIR_BWD,
+                                T.ttt_backward_chunked_bidir)):
+        if lname not in inputs:
+            continue
+        cw = inputs[lname].wl
+        rs3 = np.random.default_rng(4444)
+        d_oc = torch.from_numpy((rs3.standard_normal((cw.B, cw.N, cw.H, cw.D)) / np.sqrt(cw.D)).astype(np.float32)
+                                ).cuda().to(torch.bfloat16)
+        wsc = torch.empty(max(T.ttt_workspace_size(op, T.TTT_BF16, cw.B, cw.H, cw.N, cw.D, 0, cw.chunk), 1),
+                          dtype=torch.uint8, device="cuda")
+        gc = [torch.empty_like(dev[lname]["q"]) for _ in range(3)]
+        dw0c = torch.empty((cw.B, cw.H, cw.D, cw.D), dtype=torch.float32, device="cuda")
+
+        def cbwd(d, cw=cw, fn=fn, d_oc=d_oc, wsc=wsc, gc=gc, dw0c=dw0c):
+            return lambda: fn(d["q"], d["k"], d["v"], d["w0"], d_oc, cw.chunk, cw.eta, d_q=gc[0], d_k=gc[1],
+                              d_v=gc[2], d_w0=dw0c, workspace=wsc)
+
+        nbc = 7 * cw.B * cw.N * cw.H * cw.D * 2   # read q, k, v, dO; write dq, dk, dv
+        cold, warm, nsets = time_rotated(cbwd, dev[lname], nbc)
+        sec = cold / 1000.0
+        out[leg] = {"ms": round(cold, 5), "ms_warm": round(warm, 5), "tokens_per_s": cw.tokens / sec,
+                    "alg_bytes": nbc, "alg_GBs": nbc / sec / 1e9, "hbm_frac": nbc / sec / 1e9 / PEAK_HBM_GBS,
+                    "timing": f"cold: inputs rotated over {nsets} copies (> 1 GiB); dO fixed"}
     need2 = T.ttt_workspace_size(T.TTT_OP_BIDIR2D, T.TTT_BF16, wl.B, wl.H, wl.N, wl.D, 0, wl.chunk)
     ws2 = torch.empty(need2, dtype=torch.uint8, device="cuda")
 

@@ -75,7 +75,9 @@ typedef enum {
   TTT_OP_BIDIR = 2,
   TTT_OP_MLP = 3,
   TTT_OP_FULLBATCH_BWD = 4,
-  TTT_OP_BIDIR2D = 5
+  TTT_OP_BIDIR2D = 5,
+  TTT_OP_CAUSAL_BWD = 6,
+  TTT_OP_BIDIR_BWD = 7
 } ttt_op;
 
 /*
@@ -136,6 +138,28 @@ ttt_status ttt_forward_chunked_causal(ttt_dtype dt, int B, int H, int N, int D, 
                                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Backward pass of ttt_forward_chunked_causal for the outer training loop: given d_o = dL/dO, the
+ * gradients of L with respect to q, k, v and W0 (closed form, in the style of the hand-written
+ * inner gradient of the ViT^3 review on techloop.online, section on the official code). Per chunk
+ * with start state W, a = eta/b, E = K W - V, S = tril(Q K^T) and lam = dL/d(the state the chunk
+ * hands on):
+ *   dE = -a (S^T dO + K lam),   dS = -a tril(dO E^T),
+ *   dQ = dO W^T + dS K,   dK = dE W^T + dS^T Q - a E lam^T,   dV = -dE,
+ *   dL/dW (for the chunk before) = lam + Q^T dO + K^T dE.
+ * Arguments as for ttt_backward_fullbatch plus chunk (16, 32 or 64, dividing N): d_o, d_q, d_k,
+ * d_v [B, N, H, D] of dtype dt; d_w0 fp32 [B, H, D, D] per batch element (summed by the caller
+ * when W0 is shared). No gradient flows in through the end state (w_out of the forward). Outputs
+ * must not overlap any input or each other. Workspace: ttt_workspace_size(TTT_OP_CAUSAL_BWD, ...,
+ * chunk), which may be 0 (then workspace may be NULL).
+ */
+ttt_status ttt_backward_chunked_causal(ttt_dtype dt, int B, int H, int N, int D, int chunk,
+                                       float eta, const void* q, const void* k, const void* v,
+                                       const float* w0, long long w0_batch_stride,
+                                       const void* d_o, void* d_q, void* d_k, void* d_v,
+                                       float* d_w0, void* workspace, size_t workspace_bytes,
+                                       void* stream);
+
+/*
  * Bidirectional chunked scan (Vision-TTT summary on gist.science, "Methodologie" item 2: tokens
  * are scanned forwards and backwards; item 3: mini-batches). Per (b, h): a forward scan over
  * chunks of b tokens, W_c = W_{c-1} - (eta/b) K_c^T (K_c W_{c-1} - V_c) from W_{-1} = W0, reads
@@ -149,6 +173,22 @@ ttt_status ttt_forward_chunked_bidir(ttt_dtype dt, int B, int H, int N, int D, i
                                      const float* w0, long long w0_batch_stride,
                                      void* o, float* w_out,
                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward pass of ttt_forward_chunked_bidir: the gradients of both scans summed (each reads the
+ * same q, k, v and W0 and receives the same d_o). Each scan reads out after its chunk's update, so
+ * per chunk (in that scan's order) with lam' = lam + Q^T dO and W_c the state after the chunk:
+ *   dE = -a K lam',   dQ = dO W_c^T,   dK = dE W^T - a E lam'^T,   dV = -dE,
+ *   dL/dW (for the chunk before) = lam' + K^T dE.
+ * Arguments, layouts and errors as for ttt_backward_chunked_causal; workspace:
+ * ttt_workspace_size(TTT_OP_BIDIR_BWD, ..., chunk) (nonzero: it holds one scan's partial sums).
+ */
+ttt_status ttt_backward_chunked_bidir(ttt_dtype dt, int B, int H, int N, int D, int chunk,
+                                      float eta, const void* q, const void* k, const void* v,
+                                      const float* w0, long long w0_batch_stride,
+                                      const void* d_o, void* d_q, void* d_k, void* d_v,
+                                      float* d_w0, void* workspace, size_t workspace_bytes,
+                                      void* stream);
 
 /*
  * 2-D bidirectional layer: the bidirectional scan of ttt_forward_chunked_bidir over the tokens in

@@ -268,9 +268,10 @@ def _scan_vjp(Q, K, V, W0, dO, eta: float, b: int, causal: bool):
         qdo = {i: _t(Q[:, :, i:i + 1]) @ dO[:, :, i:i + 1] for i in rows}
         S = np.zeros_like(Ws)
         total_qdo = sum(qdo.values())
+        S_all = sum(_t(K[:, :, j:j + 1]) @ e[j] for j in rows)
         for i in rows:  # read-out weights of each output
             S = S + _t(K[:, :, i:i + 1]) @ e[i]
-            Wi = Ws - a * (S if causal else _t(K[:, :, c0:c0 + b]) @ (K[:, :, c0:c0 + b] @ Ws - V[:, :, c0:c0 + b]))
+            Wi = Ws - a * (S if causal else S_all)
             dQ[:, :, i:i + 1] = dO[:, :, i:i + 1] @ _t(Wi)
         lam_prev = lam + total_qdo
         later = np.zeros_like(Ws)  # sum of q_i^T do_i over outputs i >= j (causal)

@@ -89,6 +89,44 @@ ttt_status check_linear(ttt_op op, ttt_dtype dt, int B, int H, int N, int D, int
 
 ttt_status from_hip(hipError_t e) { return e == hipSuccess ? TTT_OK : TTT_ERR_HIP; }
 
+// Validation of the backward entry points: the forward's checks of q, k, v, w0 and one
+// [B, N, H, D] output (d_q), then d_o, the other outputs, the workspace and every overlap.
+ttt_status check_backward(ttt_op op, ttt_dtype dt, int B, int H, int N, int D, int chunk,
+                          float eta, const void* q, const void* k, const void* v, const float* w0,
+                          long long w0s, const void* d_o, const void* d_q, const void* d_k,
+                          const void* d_v, const float* d_w0, const void* ws, size_t ws_bytes) {
+  const ttt_op fwd = op == TTT_OP_FULLBATCH_BWD ? TTT_OP_FULLBATCH
+                                                : (op == TTT_OP_CAUSAL_BWD ? TTT_OP_CAUSAL : TTT_OP_BIDIR);
+  ttt_status st = check_linear(fwd, dt, B, H, N, D, chunk, eta, q, k, v, w0, w0s, d_q, nullptr,
+                               nullptr, 0, false);
+  if (st != TTT_OK) return st;
+  if (!d_o || !d_k || !d_v || !d_w0) return TTT_ERR_INVALID;
+  if (!aligned16(d_o) || !aligned16(d_k) || !aligned16(d_v) || !aligned16(d_w0))
+    return TTT_ERR_INVALID;
+  const size_t act = (size_t)B * N * H * D * elem_size(dt);
+  const Range ins[5] = {range_of(q, act), range_of(k, act), range_of(v, act), range_of(d_o, act),
+                        range_of(w0, state_bytes(B, H, (size_t)D * D, w0s))};
+  const Range outs[4] = {range_of(d_q, act), range_of(d_k, act), range_of(d_v, act),
+                         range_of(d_w0, (size_t)B * H * D * D * sizeof(float))};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 5; ++j)
+      if (overlaps(outs[i], ins[j])) return TTT_ERR_INVALID;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], outs[j])) return TTT_ERR_INVALID;
+  }
+  const size_t need = ttt_workspace_size(op, dt, B, H, N, D, 0, chunk);
+  if (need > 0) {
+    if (!ws || ws_bytes < need) return TTT_ERR_WORKSPACE;
+    if (!aligned16(ws)) return TTT_ERR_INVALID;
+    const Range rws = range_of(ws, need);
+    for (int j = 0; j < 5; ++j)
+      if (overlaps(rws, ins[j])) return TTT_ERR_INVALID;
+    for (int i = 0; i < 4; ++i)
+      if (overlaps(rws, outs[i])) return TTT_ERR_INVALID;
+  }
+  return TTT_OK;
+}
+
 // Scratch of ttt_forward_fullbatch_noalloc: one static array per device, never allocated or freed
 // by the library (each device holds it until the process ends). In host code `scratch` only names
 // the symbol; its device address is looked up once per device with that device current, and only
@@ -131,6 +169,10 @@ size_t ttt_workspace_size(ttt_op op, ttt_dtype dt, int B, int H, int N, int D, i
       return round_up(ttt::fb_workspace_bytes(bf, B, H, N, D), 256);
     case TTT_OP_FULLBATCH_BWD:
       return round_up(ttt::fbb_workspace_bytes(bf, B, H, N, D), 256);
+    case TTT_OP_CAUSAL_BWD:
+    case TTT_OP_BIDIR_BWD:
+      if (!supported_chunk(chunk) || N % chunk != 0) return 0;
+      return round_up(ttt::chunked_bwd_workspace_bytes(op == TTT_OP_BIDIR_BWD, bf, B, H, N, D, chunk), 256);
     case TTT_OP_CAUSAL:
     case TTT_OP_BIDIR:
       if (!supported_chunk(chunk) || N % chunk != 0) return 0;
@@ -186,35 +228,43 @@ ttt_status ttt_backward_fullbatch(ttt_dtype dt, int B, int H, int N, int D, floa
                                   long long w0_batch_stride, const void* d_o, void* d_q,
                                   void* d_k, void* d_v, float* d_w0, void* workspace,
                                   size_t workspace_bytes, void* stream) {
-  // The forward's checks cover q, k, v, w0 and one [B, N, H, D] output (d_q here); the rest below.
-  ttt_status st = check_linear(TTT_OP_FULLBATCH, dt, B, H, N, D, 0, eta, q, k, v, w0,
-                               w0_batch_stride, d_q, nullptr, nullptr, 0, false);
+  const ttt_status st = check_backward(TTT_OP_FULLBATCH_BWD, dt, B, H, N, D, 0, eta, q, k, v, w0,
+                                       w0_batch_stride, d_o, d_q, d_k, d_v, d_w0, workspace,
+                                       workspace_bytes);
   if (st != TTT_OK) return st;
-  if (!d_o || !d_k || !d_v || !d_w0) return TTT_ERR_INVALID;
-  if (!aligned16(d_o) || !aligned16(d_k) || !aligned16(d_v) || !aligned16(d_w0))
-    return TTT_ERR_INVALID;
-  const size_t act = (size_t)B * N * H * D * elem_size(dt);
-  const Range ins[5] = {range_of(q, act), range_of(k, act), range_of(v, act), range_of(d_o, act),
-                        range_of(w0, state_bytes(B, H, (size_t)D * D, w0_batch_stride))};
-  const Range outs[4] = {range_of(d_q, act), range_of(d_k, act), range_of(d_v, act),
-                         range_of(d_w0, (size_t)B * H * D * D * sizeof(float))};
-  for (int i = 0; i < 4; ++i) {
-    for (int j = 0; j < 5; ++j)
-      if (overlaps(outs[i], ins[j])) return TTT_ERR_INVALID;
-    for (int j = i + 1; j < 4; ++j)
-      if (overlaps(outs[i], outs[j])) return TTT_ERR_INVALID;
-  }
-  const size_t need = ttt_workspace_size(TTT_OP_FULLBATCH_BWD, dt, B, H, N, D, 0, 0);
-  if (!workspace || workspace_bytes < need) return TTT_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return TTT_ERR_INVALID;
-  const Range rws = range_of(workspace, need);
-  for (int j = 0; j < 5; ++j)
-    if (overlaps(rws, ins[j])) return TTT_ERR_INVALID;
-  for (int i = 0; i < 4; ++i)
-    if (overlaps(rws, outs[i])) return TTT_ERR_INVALID;
   return from_hip(ttt::fbb_launch(dt == TTT_BF16, B, H, N, D, eta, q, k, v, w0, w0_batch_stride,
                                   d_o, d_q, d_k, d_v, d_w0, workspace,
                                   static_cast<hipStream_t>(stream)));
+}
+
+ttt_status ttt_backward_chunked_causal(ttt_dtype dt, int B, int H, int N, int D, int chunk,
+                                       float eta, const void* q, const void* k, const void* v,
+                                       const float* w0, long long w0_batch_stride,
+                                       const void* d_o, void* d_q, void* d_k, void* d_v,
+                                       float* d_w0, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  const ttt_status st = check_backward(TTT_OP_CAUSAL_BWD, dt, B, H, N, D, chunk, eta, q, k, v, w0,
+                                       w0_batch_stride, d_o, d_q, d_k, d_v, d_w0, workspace,
+                                       workspace_bytes);
+  if (st != TTT_OK) return st;
+  return from_hip(ttt::chunked_bwd_launch(false, dt == TTT_BF16, B, H, N, D, chunk, eta, q, k, v,
+                                          w0, w0_batch_stride, d_o, d_q, d_k, d_v, d_w0,
+                                          workspace, static_cast<hipStream_t>(stream)));
+}
+
+ttt_status ttt_backward_chunked_bidir(ttt_dtype dt, int B, int H, int N, int D, int chunk,
+                                      float eta, const void* q, const void* k, const void* v,
+                                      const float* w0, long long w0_batch_stride,
+                                      const void* d_o, void* d_q, void* d_k, void* d_v,
+                                      float* d_w0, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  const ttt_status st = check_backward(TTT_OP_BIDIR_BWD, dt, B, H, N, D, chunk, eta, q, k, v, w0,
+                                       w0_batch_stride, d_o, d_q, d_k, d_v, d_w0, workspace,
+                                       workspace_bytes);
+  if (st != TTT_OK) return st;
+  return from_hip(ttt::chunked_bwd_launch(true, dt == TTT_BF16, B, H, N, D, chunk, eta, q, k, v,
+                                          w0, w0_batch_stride, d_o, d_q, d_k, d_v, d_w0,
+                                          workspace, static_cast<hipStream_t>(stream)));
 }
 
 ttt_status ttt_forward_chunked_causal(ttt_dtype dt, int B, int H, int N, int D, int chunk,

@@ -95,7 +95,7 @@ constexpr int max_seg_len() { return kRevLdsBytes / (D * D * 2); }
 // the tensor of a piece is the same across the wave, and choosing its base pointer is scalar work.
 template <int D, int CH, int NTH, int NTS, int G, int P>
 struct ChunkStager {
-  static_assert(NTH % G == 0 && NTS >= 1 && NTS <= 3, "staging geometry");
+  static_assert(NTH % G == 0 && NTS >= 1 && NTS <= 4, "staging geometry");
   static constexpr int CPR = D / 8;  // 16-byte pieces per row
   static constexpr int TILE = CH * CPR;
   static constexpr int PIECES = NTS * TILE;
@@ -118,18 +118,19 @@ struct ChunkStager {
   __device__ __forceinline__ bool valid(int i) const {
     return PIECES % GT == 0 || (int)(threadIdx.x % GT) + i * GT < PIECES;
   }
-  // t0, t1, t2: the chunk's first row in each tensor.
-  __device__ __forceinline__ void load(const bf16* t0, const bf16* t1, const bf16* t2) {
+  // t0 .. t3: the chunk's first row in each tensor (unused ones may be null).
+  __device__ __forceinline__ void load(const bf16* t0, const bf16* t1, const bf16* t2,
+                                       const bf16* t3 = nullptr) {
     for (int i = 0; i < PER; ++i)
       if (valid(i)) {
-        const bf16* src = sel[i] == 0 ? t0 : (sel[i] == 1 ? t1 : t2);
+        const bf16* src = sel[i] == 0 ? t0 : (sel[i] == 1 ? t1 : (sel[i] == 2 ? t2 : t3));
         v[i] = ld16(src + goff[i]);
       }
   }
-  __device__ __forceinline__ void store(bf16* d0, bf16* d1, bf16* d2) const {
+  __device__ __forceinline__ void store(bf16* d0, bf16* d1, bf16* d2, bf16* d3 = nullptr) const {
     for (int i = 0; i < PER; ++i)
       if (valid(i)) {
-        bf16* dst = sel[i] == 0 ? d0 : (sel[i] == 1 ? d1 : d2);
+        bf16* dst = sel[i] == 0 ? d0 : (sel[i] == 1 ? d1 : (sel[i] == 2 ? d2 : d3));
         st16_lds8(dst + loff[i], v[i]);
       }
   }
@@ -313,7 +314,10 @@ __global__ __launch_bounds__(D / 8 * 64) void chunk_compose_bf16(
 // ---------------------------------------------------------------- 2. prefix over segments
 // The columns of W are independent regressions, so the fold over the segment maps,
 // W[:, cols] <- W[:, cols] + (-Dev) W[:, cols] + R[:, cols], runs as one single-wave workgroup
-// per (b, h, direction, 16-column tile), storing each segment's entry state. Its speed is the
+// per (b, h, record slot, 16-column tile), storing each segment's entry state. A segment carries
+// NREC map records: even slots are folded first segment to last, odd slots last to first; slots
+// below n_init start from W0, the others from zero (the backward pass folds its adjoint maps,
+// which start from a zero gradient, beside the forward maps). Its speed is the
 // latency of one step (a few dependent products), so there is no LDS and no barrier: each lane
 // loads its own operands of a map record (rows of -Dev, its R entries) straight into registers,
 // kPrefixSets steps ahead, rotating through kPrefixSets register sets.
@@ -339,27 +343,28 @@ struct PrefixOperands {
   }
 };
 
-template <int D, bool BIDIR>
+template <int D, int NREC>
 __global__ __launch_bounds__(64) void chunk_prefix(const float* __restrict__ w0,
-                                                   long long w0_bstride, int H, int S,
+                                                   long long w0_bstride, int n_init, int H, int S,
                                                    const float* __restrict__ comp,
                                                    float* __restrict__ win) {
   constexpr int NT = D / 16;
   constexpr long long DD = (long long)D * D;
-  const int bh = blockIdx.x, dir = blockIdx.y, col = blockIdx.z, b = bh / H, h = bh % H;
+  const int bh = blockIdx.x, slot = blockIdx.y, col = blockIdx.z, b = bh / H, h = bh % H;
   const int BH = gridDim.x;
   const int l = threadIdx.x, r = l & 15, g = l >> 4;
-  const int nrec = BIDIR ? 2 : 1;
+  const bool rev = slot & 1;
   auto record = [&](int i) {  // map record of the i-th fold step
-    const int s = dir == 0 ? i : S - 1 - i;
-    return comp + (((long long)bh * S + s) * nrec + dir) * kMapFloats<D>;
+    const int s = rev ? S - 1 - i : i;
+    return comp + (((long long)bh * S + s) * NREC + slot) * kMapFloats<D>;
   };
 
   const float* W0 = w0 + b * w0_bstride + h * DD;
   f32x4 W[NT];  // W[16m + 4g + j][16 col + r]
   for (int m = 0; m < NT; ++m)
-    for (int j = 0; j < 4; ++j) W[m][j] = W0[(16 * m + 4 * g + j) * D + 16 * col + r];
-  float* dst_base = win + ((long long)dir * BH + bh) * S * DD;
+    for (int j = 0; j < 4; ++j)
+      W[m][j] = slot < n_init ? W0[(16 * m + 4 * g + j) * D + 16 * col + r] : 0.f;
+  float* dst_base = win + ((long long)slot * BH + bh) * S * DD;
   const int steps = S - 1;  // maps applied: segments 0 .. S-2 in fold order
   PrefixOperands<D> set0, set1, set2, set3;
   set0.load(record(0), col, l);
@@ -367,7 +372,7 @@ __global__ __launch_bounds__(64) void chunk_prefix(const float* __restrict__ w0,
   set2.load(record(min(2, S - 1)), col, l);
   set3.load(record(min(3, S - 1)), col, l);
   auto store = [&](int i) {  // entry state of the i-th segment in fold order
-    float* dst = dst_base + (dir == 0 ? i : S - 1 - i) * DD;
+    float* dst = dst_base + (rev ? S - 1 - i : i) * DD;
     for (int m = 0; m < NT; ++m) *reinterpret_cast<f32x4*>(dst + state_tile<D>(col, m, l)) = W[m];
   };
   auto step = [&](int i, PrefixOperands<D>& op) {  // applies map i, stores entry state i + 1
@@ -723,12 +728,12 @@ hipError_t launch_bf16(bool bidir, int B, int H, int N, float a, const void* q, 
     if (bidir) {
       hipLaunchKernelGGL((chunk_compose_bf16<D, CH, true>), dim3(pl.S, BH), dim3(D / 8 * 64), 0, st,
                          (const bf16*)k, (const bf16*)v, H, N, a, pl.S, pl.L, comp);
-      hipLaunchKernelGGL((chunk_prefix<D, true>), dim3(BH, 2, D / 16), dim3(64), 0, st, w0, w0s, H,
+      hipLaunchKernelGGL((chunk_prefix<D, 2>), dim3(BH, 2, D / 16), dim3(64), 0, st, w0, w0s, 2, H,
                          pl.S, comp, win);
     } else {
       hipLaunchKernelGGL((chunk_compose_bf16<D, CH, false>), dim3(pl.S, BH), dim3(D / 8 * 64), 0,
                          st, (const bf16*)k, (const bf16*)v, H, N, a, pl.S, pl.L, comp);
-      hipLaunchKernelGGL((chunk_prefix<D, false>), dim3(BH, 1, D / 16), dim3(64), 0, st, w0, w0s,
+      hipLaunchKernelGGL((chunk_prefix<D, 1>), dim3(BH, 1, D / 16), dim3(64), 0, st, w0, w0s, 1,
                          H, pl.S, comp, win);
     }
   }
@@ -777,6 +782,667 @@ hipError_t launch_bf16_d(bool bidir, int B, int H, int N, int CH, float a, const
   }
 }
 
+// ================================================================ backward (outer-loop gradients)
+// Gradients of the chunked layers for the outer training loop (the pages' authors write the inner
+// gradient by hand rather than by autograd: ViT^3 review, section on the official code; the outer
+// gradient here is derived in the same closed-form style). One scan direction, chunk c in the
+// scan's order with start state W (= W_{c-1}), a = eta/b, E = K W - V and the read-out
+//   O = Q W - a (M o Q K^T) E,   M = tril (causal) or all ones (read-out after the chunk's update,
+//                                    i.e. O = Q W_c with W_c = W - a K^T E),
+// and lam = dL/dW_c from the chunks after c (zero after the last). Then
+//   dE = -a (S^T dO + K lam),  S = M o (Q K^T)      dS = -a M o (dO E^T)
+//   dQ = dO W^T + dS K        dK = dE W^T + dS^T Q - a E lam^T        dV = -dE
+//   dL/dW_{c-1} = lam + Q^T dO + K^T dE.
+// For the read-out after the update the same reads, with lam' = lam + Q^T dO:
+//   dE = -a K lam',  dQ = dO W_c^T,  dK = dE W^T - a E lam'^T,  dL/dW_{c-1} = lam' + K^T dE.
+// The adjoint step lam -> A_c lam + U_c is affine with the forward map's linear part A_c =
+// I - a K^T K (symmetric), so a segment's adjoint map is the forward composite transposed plus an
+// offset, and the prefix fold carries the adjoints beside the forward states:
+//   1. chunk_compose_bwd: per (segment, b, h), the forward map (as in the forward pass) and the
+//      adjoint offsets: for a forward-ordered scan U = sum_c P_{c-1}^T U_c (P_{c-1} the forward
+//      composite before chunk c; U_c = (Q_c - a S_c K_c)^T dO_c, which is (Q_c A_c)^T dO_c for the
+//      all-ones mask); for the reversed scan of the bidirectional layer, whose adjoint runs over
+//      the chunks in forward order, mu <- A_c (mu + Q_c^T dO_c).
+//   2. chunk_prefix over the records: forward entry states and adjoints at every segment's end.
+//   3. chunk_bwd_scan: per (segment, b, h), the forward states over the segment into an LDS ring
+//      (bf16, the operand precision), then the chunks in reverse scan order with the formulas
+//      above. The bidirectional layer runs it once per direction: the reversed scan writes fp32
+//      partial gradients, the forward scan adds them before rounding.
+
+// Record slots of the backward (a segment's maps): causal: 0 forward map, 1 adjoint map;
+// bidirectional: 0 forward, 1 reversed-scan forward, 2 reversed-scan adjoint, 3 forward adjoint.
+// Even slots are folded first segment to last, odd slots last to first.
+
+// Y^T[16 cols x 16 rows] = W[:, col0..col0+15]^T X_rows^T with W a row-major bf16 tile in LDS
+// (row pitch PW): lane (r, g) gets sum_k W[k][col0 + 4g + j] X[row0 + r][k]. The A operand (W's
+// columns) comes from LDS transpose reads.
+template <int D, int P, int PW>
+__device__ __forceinline__ f32x4 ldsstate_times_rows(const bf16* Wl, int col0, const bf16* X,
+                                                     int row0, f32x4 acc, int r, int g, int l) {
+  if constexpr (D >= 32) {
+    for (int ks = 0; ks < D / 32; ++ks) {
+      const bf16* p = X + (row0 + r) * P + 32 * ks + 4 * g;
+      acc = mma32(cat8(tile_tr(&Wl[(32 * ks) * PW + col0], PW, l), tile_tr(&Wl[(32 * ks + 16) * PW + col0], PW, l)),
+                  cat8(ld4(p), ld4(p + 16)), acc);
+    }
+  } else {
+    acc = mma16(tile_tr(&Wl[col0], PW, l), ld4(X + (row0 + r) * P + 4 * g), acc);
+  }
+  return acc;
+}
+
+// C[16 x 16] += A_rows(arow0..) . B_rows(brow0..)^T, contraction over the D features: lane (r, g)
+// gets sum_k A[arow0 + 4g + j][k] B[brow0 + r][k] (A and B row-major bf16 in LDS).
+template <int D, int PA, int PB>
+__device__ __forceinline__ f32x4 rows_dot_rows(const bf16* A, int arow0, const bf16* Bm, int brow0,
+                                               f32x4 acc, int r, int g) {
+  if constexpr (D >= 32) {
+    for (int ks = 0; ks < D / 32; ++ks) {
+      const bf16* pa = A + (arow0 + r) * PA + 32 * ks + 4 * g;
+      const bf16* pb = Bm + (brow0 + r) * PB + 32 * ks + 4 * g;
+      acc = mma32(cat8(ld4(pa), ld4(pa + 16)), cat8(ld4(pb), ld4(pb + 16)), acc);
+    }
+  } else {
+    acc = mma16(ld4(A + (arow0 + r) * PA + 4 * g), ld4(Bm + (brow0 + r) * PB + 4 * g), acc);
+  }
+  return acc;
+}
+
+// X[:, 16col..] += A^T B[:, 16col..] over the chunk's tokens, A and B [CH x D] tiles in LDS (A^T
+// and B both by transpose reads). 16-token chunks use 16x16x16 products, longer ones 16x16x32
+// (the same shapes as update_state, so the two may accumulate into the same registers).
+template <int D, int NP, int P>
+__device__ __forceinline__ void add_at_b(f32x4* X, const bf16* A, const bf16* Bm, int col, int l) {
+  if constexpr (NP == 1) {
+    const bf16x4 bt = tile_tr(&Bm[16 * col], P, l);
+    for (int m = 0; m < D / 16; ++m) X[m] = mma16(tile_tr(&A[16 * m], P, l), bt, X[m]);
+  } else {
+    for (int p = 0; p < NP; p += 2) {
+      const bf16x8 bt = cat8(tile_tr(&Bm[16 * p * P + 16 * col], P, l), tile_tr(&Bm[16 * (p + 1) * P + 16 * col], P, l));
+      for (int m = 0; m < D / 16; ++m)
+        X[m] = mma32(cat8(tile_tr(&A[16 * p * P + 16 * m], P, l), tile_tr(&A[16 * (p + 1) * P + 16 * m], P, l)), bt, X[m]);
+    }
+  }
+}
+
+// Acc[n] (row tile col, column tile n) += Z^T B[:, 16n..], Z the [CH x 16] C-layout tiles of one
+// wave (rows = tokens), B a [CH x D] LDS tile: the R_rev accumulation pattern of the compose.
+template <int D, int NP, int P>
+__device__ __forceinline__ void add_zt_b(f32x4* Acc, const f32x4* Z, const bf16* Bm, float scale,
+                                         int l) {
+  if constexpr (NP == 1) {
+    const bf16x4 za = to_bf16x4_scaled(Z[0], scale);
+    for (int n = 0; n < D / 16; ++n) Acc[n] = mma16(za, tile_tr(&Bm[16 * n], P, l), Acc[n]);
+  } else {
+    for (int p = 0; p < NP; p += 2) {
+      const bf16x8 za = cat8(to_bf16x4_scaled(Z[p], scale), to_bf16x4_scaled(Z[p + 1], scale));
+      for (int n = 0; n < D / 16; ++n)
+        Acc[n] = mma32(za, cat8(tile_tr(&Bm[16 * p * P + 16 * n], P, l), tile_tr(&Bm[16 * (p + 1) * P + 16 * n], P, l)), Acc[n]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- B1. compose (backward)
+// Waves: role 0 holds P columns [16col, 16col + 16) (from I) and accumulates row tile col of the
+// forward scan's adjoint offset (and, bidirectional, of R_rev); role 1 holds R columns (from 0);
+// role 2 (bidirectional) holds columns of the reversed scan's adjoint offset.
+template <int D, int CH, bool BIDIR>
+__global__ __launch_bounds__((BIDIR ? 3 : 2) * (D / 16) * 64) void chunk_compose_bwd_bf16(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ d_o, int H, int N, float a, int S, int L, float* __restrict__ comp) {
+  constexpr int P = lds_pitch<D>(), NT = D / 16, NP = CH / 16, NTH = (BIDIR ? 3 : 2) * NT * 64;
+  constexpr int NREC = BIDIR ? 4 : 2;
+  constexpr long long DD = (long long)D * D;
+  __shared__ __align__(16) bf16 sKb[2][CH * P];
+  __shared__ __align__(16) bf16 sVb[2][CH * P];
+  __shared__ __align__(16) bf16 sQb[2][CH * P];
+  __shared__ __align__(16) bf16 sDb[2][CH * P];
+
+  const int s = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H;
+  const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
+  const int role = w / NT, col = w % NT;
+  const int C = N / CH;
+  const int lo = s * L, hi = min(C, lo + L);
+  const long long ts = (long long)H * D;
+  const long long head0 = (long long)b * N * ts + (long long)h * D;
+
+  f32x4 X[NT], RR[NT], UT[NT];
+  for (int m = 0; m < NT; ++m)
+    for (int j = 0; j < 4; ++j) {
+      X[m][j] = (role == 0 && 16 * m + 4 * g + j == 16 * col + r) ? 1.f : 0.f;
+      RR[m][j] = 0.f;
+      UT[m][j] = 0.f;
+    }
+
+  constexpr int G = stage_groups<CH>();
+  ChunkStager<D, CH, NTH, 4, G, P> st(ts);
+  const long long cs = (long long)CH * ts;
+  const bf16* kn = k + head0 + lo * cs;
+  const bf16* vn = v + head0 + lo * cs;
+  const bf16* qn = q + head0 + lo * cs;
+  const bf16* dn = d_o + head0 + lo * cs;
+  for (int j = 0; j < G; ++j, kn += cs, vn += cs, qn += cs, dn += cs)
+    if (lo + j < hi && st.mine(j)) st.load(kn, vn, qn, dn);
+  for (int c = lo; c < hi; ++c, kn += cs, vn += cs, qn += cs, dn += cs) {
+    bf16* sK = sKb[(c - lo) & 1];
+    bf16* sV = sVb[(c - lo) & 1];
+    bf16* sQ = sQb[(c - lo) & 1];
+    bf16* sD = sDb[(c - lo) & 1];
+    if (st.mine(c - lo)) {
+      st.store(sK, sV, sQ, sD);
+      if (c + G < hi) st.load(kn, vn, qn, dn);
+    }
+    __syncthreads();
+    f32x4 Y[NP];
+    if (role == 0) {
+      residuals<D, NP, P>(Y, X, sK, sV, -1, r, g, l);  // K_c P_{c-1}
+      f32x4 Z[NP];
+      if constexpr (!BIDIR) {
+        // Z = Q_c P_{c-1} - a tril(Q_c K_c^T) K_c P_{c-1}
+        for (int p = 0; p < NP; ++p) {
+          const f32x4 zq = rows_times_state<D, P>(sQ, 16 * p, X, zero4(), r, g);
+          f32x4 acc = zero4();
+          for (int pp = 0; pp <= p; ++pp) {
+            // pt[t' = 16pp + 4g + j][t = 16p + r] = k_t' . q_t: the A operand S[t][t']
+            f32x4 pt = rows_dot_rows<D, P, P>(sK, 16 * pp, sQ, 16 * p, zero4(), r, g);
+            if (pp == p)
+              for (int j = 0; j < 4; ++j)
+                if (4 * g + j > r) pt[j] = 0.f;
+            acc = mma16(to_bf16x4_scaled(pt, -a), to_bf16x4(Y[pp]), acc);
+          }
+          Z[p] = zq + acc;
+        }
+        add_zt_b<D, NP, P>(UT, Z, sD, 1.f, l);
+        update_state<D, NP, P>(X, Y, sK, a, l);
+      } else {
+        add_zt_b<D, NP, P>(RR, Y, sV, a, l);  // R_rev += a (K_c P_{c-1})^T V_c
+        update_state<D, NP, P>(X, Y, sK, a, l);
+        for (int p = 0; p < NP; ++p) Z[p] = rows_times_state<D, P>(sQ, 16 * p, X, zero4(), r, g);
+        add_zt_b<D, NP, P>(UT, Z, sD, 1.f, l);  // U += (Q_c P_c)^T dO_c
+      }
+    } else if (role == 1) {
+      residuals<D, NP, P>(Y, X, sK, sV, col, r, g, l);
+      update_state<D, NP, P>(X, Y, sK, a, l);
+    } else {  // mu <- A_c (mu + Q_c^T dO_c)
+      add_at_b<D, NP, P>(X, sQ, sD, col, l);
+      residuals<D, NP, P>(Y, X, sK, sV, -1, r, g, l);
+      update_state<D, NP, P>(X, Y, sK, a, l);
+    }
+  }
+
+  float* rec = comp + ((long long)bh * S + s) * NREC * kMapFloats<D>;
+  auto ndev = [&](int slot) { return reinterpret_cast<bf16*>(rec + slot * kMapFloats<D>); };
+  auto roff = [&](int slot) { return rec + slot * kMapFloats<D> + DD / 2; };
+  if (role == 0) {
+    for (int m = 0; m < NT; ++m)
+      for (int j = 0; j < 4; ++j) {
+        const int row = 16 * m + 4 * g + j, cc = 16 * col + r;
+        const bf16 nd = (bf16)(X[m][j] - (row == cc ? 1.f : 0.f));  // -Dev = P - I
+        ndev(0)[dev_offset<D>(row, cc)] = nd;
+        ndev(1)[dev_offset<D>(cc, row)] = nd;
+        if constexpr (BIDIR) {
+          ndev(2)[dev_offset<D>(row, cc)] = nd;
+          ndev(3)[dev_offset<D>(cc, row)] = nd;
+        }
+      }
+    // UT[n] / RR[n]: tile (column tile n, row tile col) of the offsets
+    for (int n = 0; n < NT; ++n)
+      *reinterpret_cast<f32x4*>(roff(BIDIR ? 3 : 1) + state_tile<D>(n, col, l)) = UT[n];
+    if constexpr (BIDIR)
+      for (int n = 0; n < NT; ++n) *reinterpret_cast<f32x4*>(roff(1) + state_tile<D>(n, col, l)) = RR[n];
+  } else {
+    float* dst = roff(role == 1 ? 0 : 2);
+    for (int m = 0; m < NT; ++m) *reinterpret_cast<f32x4*>(dst + state_tile<D>(col, m, l)) = X[m];
+  }
+}
+
+// ---------------------------------------------------------------- B3. segment scan (backward)
+// LDS of the backward scan: five [CH x D] tiles (K; V, then E; Q; dO; dE), -a lam (row-major) and
+// the ring of the segment's forward states. The ring takes what a budget leaves (two workgroups
+// per CU for chunks of up to 32 tokens, one for 64): it bounds the chunks per segment.
+template <int D, int CH>
+constexpr int bwd_fixed_lds() { return (5 * CH + D) * lds_pitch<D>() * 2; }
+template <int D, int CH>
+constexpr int bwd_ring() {
+  constexpr int budget = CH <= 32 ? 80 * 1024 : 156 * 1024;
+  constexpr int n = (budget - bwd_fixed_lds<D, CH>()) / (D * lds_pitch<D>() * 2);
+  return n > 17 ? 17 : n;
+}
+
+// Output modes: write bf16; write fp32 partials (reversed scan of the bidirectional layer); add the
+// partials and write bf16 (its forward scan, launched after).
+enum BwdOut { kOutBf16 = 0, kOutPartial = 1, kOutAddPartial = 2 };
+
+template <int D, int CH, bool CAUSAL>
+__global__ __launch_bounds__(D / 16 * 64) void chunk_bwd_scan_bf16(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ d_o, const float* __restrict__ w0, long long w0_bstride, int H, int N,
+    float a, int S, int L, const float* __restrict__ win, int dir, int fwd_slot, int adj_slot,
+    int out_mode, float* __restrict__ part, bf16* __restrict__ dq, bf16* __restrict__ dk,
+    bf16* __restrict__ dv, float* __restrict__ d_w0) {
+  constexpr int P = lds_pitch<D>(), PW = P;
+  constexpr int NT = D / 16, NP = CH / 16, NTH = NT * 64;
+  constexpr int RING = bwd_ring<D, CH>();
+  constexpr long long DD = (long long)D * D;
+  __shared__ __align__(16) bf16 sK[CH * P];
+  __shared__ __align__(16) bf16 sV[CH * P];  // V in the states pass, E in the gradient pass
+  __shared__ __align__(16) bf16 sQ[CH * P];
+  __shared__ __align__(16) bf16 sD[CH * P];
+  __shared__ __align__(16) bf16 sDE[CH * P];
+  __shared__ __align__(16) bf16 sL[D * PW];
+  __shared__ __align__(16) bf16 ring[RING][D * PW];
+  bf16* const sE = sV;
+
+  const int s = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H;
+  const int BH = gridDim.y;
+  const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
+  const int C = N / CH;
+  const int lo = s * L, hi = min(C, lo + L), n = hi - lo;
+  const long long ts = (long long)H * D;
+  const long long head0 = (long long)b * N * ts + (long long)h * D;
+  const long long cs = (long long)CH * ts;
+  // chunk at scan position pos of this segment
+  auto chunk_at = [&](int pos) { return dir == 0 ? lo + pos : hi - 1 - pos; };
+  const long long step = dir == 0 ? cs : -cs;  // pointer step to the next scan position
+
+  auto entry = [&](int slot, f32x4* X) {
+    if (S == 1) {
+      const float* src = w0 + b * w0_bstride + h * DD;
+      for (int m = 0; m < NT; ++m)
+        for (int j = 0; j < 4; ++j) X[m][j] = slot == fwd_slot ? src[(16 * m + 4 * g + j) * D + 16 * w + r] : 0.f;
+    } else {
+      const float* src = win + (((long long)slot * BH + bh) * S + s) * DD;
+      for (int m = 0; m < NT; ++m) X[m] = *reinterpret_cast<const f32x4*>(src + state_tile<D>(w, m, l));
+    }
+  };
+  auto put_state = [&](bf16* dst, const f32x4* X, float scale) {  // row-major bf16, this wave's columns
+    for (int m = 0; m < NT; ++m)
+      for (int j = 0; j < 4; ++j) dst[(16 * m + 4 * g + j) * PW + 16 * w + r] = (bf16)(X[m][j] * scale);
+  };
+  constexpr int G = stage_groups<CH>();
+
+  // ---- states pass: the segment's chunks in scan order from its entry state
+  f32x4 W[NT];
+  entry(fwd_slot, W);
+  __builtin_amdgcn_s_waitcnt(0);
+  {
+    ChunkStager<D, CH, NTH, 2, G, P> sa(ts);
+    const bf16* kn = k + head0 + chunk_at(0) * cs;
+    const bf16* vn = v + head0 + chunk_at(0) * cs;
+    for (int j = 0; j < G; ++j, kn += step, vn += step)
+      if (j < n && sa.mine(j)) sa.load(kn, vn, nullptr);
+    for (int pos = 0; pos < n; ++pos, kn += step, vn += step) {
+      __syncthreads();
+      if (sa.mine(pos)) {
+        sa.store(sK, sV, nullptr);
+        if (pos + G < n) sa.load(kn, vn, nullptr);
+      }
+      __syncthreads();
+      put_state(ring[pos], W, 1.f);
+      f32x4 E[NP];
+      residuals<D, NP, P>(E, W, sK, sV, w, r, g, l);
+      update_state<D, NP, P>(W, E, sK, a, l);
+    }
+    if (!CAUSAL) put_state(ring[n], W, 1.f);
+  }
+
+  // ---- gradient pass: the chunks in reverse scan order
+  f32x4 lam[NT];
+  entry(adj_slot, lam);
+  __builtin_amdgcn_s_waitcnt(0);
+  ChunkStager<D, CH, NTH, 4, G, P> sb(ts);
+  const bf16* kn = k + head0 + chunk_at(n - 1) * cs;
+  const bf16* vn = v + head0 + chunk_at(n - 1) * cs;
+  const bf16* qn = q + head0 + chunk_at(n - 1) * cs;
+  const bf16* dn = d_o + head0 + chunk_at(n - 1) * cs;
+  for (int j = 0; j < G; ++j, kn -= step, vn -= step, qn -= step, dn -= step)
+    if (j < n && sb.mine(j)) sb.load(kn, vn, qn, dn);
+  for (int it = 0; it < n; ++it, kn -= step, vn -= step, qn -= step, dn -= step) {
+    const int pos = n - 1 - it;
+    const long long tok0 = head0 + (long long)chunk_at(pos) * cs;
+    // V is staged into the E tile's buffer; each lane reads its own V values from there before
+    // overwriting them with E (same rows and columns).
+    __syncthreads();
+    if (sb.mine(it)) {
+      sb.store(sK, sV, sQ, sD);
+      if (it + G < n) sb.load(kn, vn, qn, dn);
+    }
+    __syncthreads();
+    const bf16* Wp = ring[pos];
+    const bf16* Wn = ring[CAUSAL ? pos : pos + 1];
+
+    // E^T and dE^T for this wave's 16 features: lane (r, g) holds features 16w + 4g + j of token
+    // 16p + r.
+    f32x4 Et[NP], dEt[NP];
+    for (int p = 0; p < NP; ++p) {
+      const bf16x4 vv = ld4(&sV[(16 * p + r) * P + 16 * w + 4 * g]);
+      f32x4 init;
+      for (int j = 0; j < 4; ++j) init[j] = -(float)vv[j];
+      Et[p] = ldsstate_times_rows<D, P, PW>(Wp, 16 * w, sK, 16 * p, init, r, g, l);
+    }
+    if (!CAUSAL) add_at_b<D, NP, P>(lam, sQ, sD, w, l);  // lam' = lam + Q^T dO
+    for (int p = 0; p < NP; ++p) {
+      const f32x4 kl = state_times_rows<D, P>(sK, 16 * p, lam, r, g);
+      f32x4 sd = zero4();
+      if constexpr (CAUSAL) {
+        // sum over t >= t' of S[t][t'] dO[t][col]: A = dO^T (tile pp), B[t][t'] = q_t . k_t'
+        for (int pp = p; pp < NP; ++pp) {
+          f32x4 st = rows_dot_rows<D, P, P>(sQ, 16 * pp, sK, 16 * p, zero4(), r, g);
+          if (pp == p)
+            for (int j = 0; j < 4; ++j)
+              if (r > 4 * g + j) st[j] = 0.f;
+          sd = mma16(tile_tr(&sD[16 * pp * P + 16 * w], P, l), to_bf16x4(st), sd);
+        }
+      }
+      dEt[p] = (kl + sd) * (-a);
+    }
+    for (int p = 0; p < NP; ++p) {
+      *reinterpret_cast<bf16x4*>(&sE[(16 * p + r) * P + 16 * w + 4 * g]) = to_bf16x4(Et[p]);
+      *reinterpret_cast<bf16x4*>(&sDE[(16 * p + r) * P + 16 * w + 4 * g]) = to_bf16x4(dEt[p]);
+    }
+    put_state(sL, lam, -a);
+    __syncthreads();
+
+    // Gradients of this wave's 16 features of every token, transposed (lane (r, g): features
+    // 16w + 4g + j of token 16p + r).
+    for (int p = 0; p < NP; ++p) {
+      f32x4 gq = rows_dot_rows<D, PW, P>(Wn, 16 * w, sD, 16 * p, zero4(), r, g);
+      f32x4 gk = rows_dot_rows<D, PW, P>(Wp, 16 * w, sDE, 16 * p, zero4(), r, g);
+      gk = rows_dot_rows<D, PW, P>(sL, 16 * w, sE, 16 * p, gk, r, g);
+      if constexpr (CAUSAL) {
+        f32x4 cq = zero4(), ck = zero4();
+        for (int pp = 0; pp <= p; ++pp) {  // dQ += dS K: B[t'][t] = -a E_t' . dO_t, t' <= t
+          f32x4 et = rows_dot_rows<D, P, P>(sE, 16 * pp, sD, 16 * p, zero4(), r, g);
+          if (pp == p)
+            for (int j = 0; j < 4; ++j)
+              if (4 * g + j > r) et[j] = 0.f;
+          cq = mma16(tile_tr(&sK[16 * pp * P + 16 * w], P, l), to_bf16x4_scaled(et, -a), cq);
+        }
+        for (int pp = p; pp < NP; ++pp) {  // dK += dS^T Q: B[t][t'] = -a dO_t . E_t', t' <= t
+          f32x4 de = rows_dot_rows<D, P, P>(sD, 16 * pp, sE, 16 * p, zero4(), r, g);
+          if (pp == p)
+            for (int j = 0; j < 4; ++j)
+              if (r > 4 * g + j) de[j] = 0.f;
+          ck = mma16(tile_tr(&sQ[16 * pp * P + 16 * w], P, l), to_bf16x4_scaled(de, -a), ck);
+        }
+        gq += cq;
+        gk += ck;
+      }
+      const f32x4 gv = -dEt[p];
+      const long long off = tok0 + (long long)(16 * p + r) * ts + 16 * w + 4 * g;
+      if (out_mode == kOutPartial) {
+        const long long act = (long long)gridDim.y / H * N * ts;  // elements of one [B, N, H, D] tensor
+        *reinterpret_cast<f32x4*>(part + off) = gq;
+        *reinterpret_cast<f32x4*>(part + act + off) = gk;
+        *reinterpret_cast<f32x4*>(part + 2 * act + off) = gv;
+      } else {
+        f32x4 oq = gq, ok = gk, ov = gv;
+        if (out_mode == kOutAddPartial) {
+          const long long act = (long long)gridDim.y / H * N * ts;
+          oq += *reinterpret_cast<const f32x4*>(part + off);
+          ok += *reinterpret_cast<const f32x4*>(part + act + off);
+          ov += *reinterpret_cast<const f32x4*>(part + 2 * act + off);
+        }
+        *reinterpret_cast<bf16x4*>(dq + off) = to_bf16x4(oq);
+        *reinterpret_cast<bf16x4*>(dk + off) = to_bf16x4(ok);
+        *reinterpret_cast<bf16x4*>(dv + off) = to_bf16x4(ov);
+      }
+    }
+    if (CAUSAL) add_at_b<D, NP, P>(lam, sQ, sD, w, l);
+    add_at_b<D, NP, P>(lam, sK, sDE, w, l);
+  }
+  // The segment holding the scan's first chunk ends the adjoint: dL/dW0 of this direction.
+  if (s == (dir == 0 ? 0 : S - 1)) {
+    float* dst = d_w0 + (long long)bh * DD;
+    for (int m = 0; m < NT; ++m)
+      for (int j = 0; j < 4; ++j) {
+        float* e = dst + (16 * m + 4 * g + j) * D + 16 * w + r;
+        *e = out_mode == kOutAddPartial ? *e + lam[m][j] : lam[m][j];
+      }
+  }
+}
+
+// ---------------------------------------------------------------- backward, fp32 I/O, plain FMA
+// One workgroup per (b, h) and scan direction pass; the states of the scan (C + 1 of them) go to
+// the workspace, the gradient pass reads them back. Same algebra as the bf16 kernels, in fp32.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void chunk_bwd_f32(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    const float* __restrict__ d_o, const float* __restrict__ w0, long long w0_bstride, int H,
+    int N, int CH, float a, int dir, float* __restrict__ states, bool accumulate,
+    float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ dv,
+    float* __restrict__ d_w0) {
+  constexpr int DP = D + 1;
+  __shared__ float sW[D * DP], sLam[D * DP];
+  __shared__ float sK[64 * DP], sQ[64 * DP], sD[64 * DP], sE[64 * DP], sDE[64 * DP];
+  __shared__ float sS[64 * 65];
+  const int bh = blockIdx.x, b = bh / H, h = bh % H, tid = threadIdx.x;
+  const int C = N / CH;
+  const long long ts = (long long)H * D, dd = (long long)D * D;
+  const long long head0 = (long long)b * N * ts + (long long)h * D;
+  float* st = states + (long long)bh * (C + 1) * dd;
+  auto chunk_at = [&](int pos) { return dir == 0 ? pos : C - 1 - pos; };
+  auto load_tile = [&](float* dst, const float* src, int c) {
+    for (int e = tid; e < CH * D; e += 256) dst[(e / D) * DP + e % D] = src[head0 + ((long long)c * CH + e / D) * ts + e % D];
+  };
+  const float* W0 = w0 + b * w0_bstride + h * dd;
+  for (int e = tid; e < D * D; e += 256) sW[(e / D) * DP + e % D] = W0[e];
+  __syncthreads();
+  // states pass
+  for (int pos = 0; pos < C; ++pos) {
+    const int c = chunk_at(pos);
+    for (int e = tid; e < D * D; e += 256) st[pos * dd + e] = sW[(e / D) * DP + e % D];
+    load_tile(sK, k, c);
+    __syncthreads();
+    for (int e = tid; e < CH * D; e += 256) {  // E = K W - V
+      const int t = e / D, j = e % D;
+      float acc = -v[head0 + ((long long)c * CH + t) * ts + j];
+      for (int kk = 0; kk < D; ++kk) acc = fmaf(sK[t * DP + kk], sW[kk * DP + j], acc);
+      sE[t * DP + j] = acc;
+    }
+    __syncthreads();
+    for (int e = tid; e < D * D; e += 256) {  // W -= a K^T E
+      const int i = e / D, j = e % D;
+      float acc = 0.f;
+      for (int t = 0; t < CH; ++t) acc = fmaf(sK[t * DP + i], sE[t * DP + j], acc);
+      sW[i * DP + j] = fmaf(-a, acc, sW[i * DP + j]);
+    }
+    __syncthreads();
+  }
+  for (int e = tid; e < D * D; e += 256) {
+    st[C * dd + e] = sW[(e / D) * DP + e % D];
+    sLam[(e / D) * DP + e % D] = 0.f;
+  }
+  __syncthreads();
+  // gradient pass
+  for (int pos = C - 1; pos >= 0; --pos) {
+    const int c = chunk_at(pos);
+    const float* Wp = st + pos * dd;
+    const float* Wn = st + (CAUSAL ? pos : pos + 1) * dd;
+    load_tile(sK, k, c);
+    load_tile(sQ, q, c);
+    load_tile(sD, d_o, c);
+    for (int e = tid; e < D * D; e += 256) sW[(e / D) * DP + e % D] = Wp[e];
+    __syncthreads();
+    for (int e = tid; e < CH * D; e += 256) {  // E = K W - V
+      const int t = e / D, j = e % D;
+      float acc = -v[head0 + ((long long)c * CH + t) * ts + j];
+      for (int kk = 0; kk < D; ++kk) acc = fmaf(sK[t * DP + kk], sW[kk * DP + j], acc);
+      sE[t * DP + j] = acc;
+    }
+    for (int e = tid; e < CH * CH; e += 256) {  // S[t][t'] = q_t . k_t' (masked below)
+      const int t = e / CH, u = e % CH;
+      float acc = 0.f;
+      for (int kk = 0; kk < D; ++kk) acc = fmaf(sQ[t * DP + kk], sK[u * DP + kk], acc);
+      sS[t * 65 + u] = acc;
+    }
+    if (!CAUSAL) {
+      for (int e = tid; e < D * D; e += 256) {  // lam' = lam + Q^T dO
+        const int i = e / D, j = e % D;
+        float acc = sLam[i * DP + j];
+        for (int t = 0; t < CH; ++t) acc = fmaf(sQ[t * DP + i], sD[t * DP + j], acc);
+        sLam[i * DP + j] = acc;
+      }
+    }
+    __syncthreads();
+    for (int e = tid; e < CH * D; e += 256) {  // dE = -a (S^T dO + K lam)
+      const int t = e / D, j = e % D;
+      float acc = 0.f;
+      for (int kk = 0; kk < D; ++kk) acc = fmaf(sK[t * DP + kk], sLam[kk * DP + j], acc);
+      if (CAUSAL)
+        for (int u = t; u < CH; ++u) acc = fmaf(sS[u * 65 + t], sD[u * DP + j], acc);
+      sDE[t * DP + j] = -a * acc;
+    }
+    __syncthreads();
+    if (CAUSAL) {
+      for (int e = tid; e < CH * CH; e += 256) {  // dS[t][t'] = -a dO_t . E_t', t' <= t
+        const int t = e / CH, u = e % CH;
+        float acc = 0.f;
+        if (u <= t)
+          for (int kk = 0; kk < D; ++kk) acc = fmaf(sD[t * DP + kk], sE[u * DP + kk], acc);
+        sS[t * 65 + u] = -a * acc;
+      }
+      __syncthreads();
+    }
+    for (int e = tid; e < CH * D; e += 256) {
+      const int t = e / D, i = e % D;
+      const long long off = head0 + ((long long)c * CH + t) * ts + i;
+      float gq = 0.f, gk = 0.f;
+      for (int j = 0; j < D; ++j) {
+        gq = fmaf(sD[t * DP + j], Wn[i * D + j], gq);
+        gk = fmaf(sDE[t * DP + j], sW[i * DP + j], gk);
+        gk = fmaf(-a * sE[t * DP + j], sLam[i * DP + j], gk);
+      }
+      if (CAUSAL) {
+        for (int u = 0; u <= t; ++u) gq = fmaf(sS[t * 65 + u], sK[u * DP + i], gq);
+        for (int u = t; u < CH; ++u) gk = fmaf(sS[u * 65 + t], sQ[u * DP + i], gk);
+      }
+      const float gv = -sDE[t * DP + i];
+      dq[off] = accumulate ? dq[off] + gq : gq;
+      dk[off] = accumulate ? dk[off] + gk : gk;
+      dv[off] = accumulate ? dv[off] + gv : gv;
+    }
+    __syncthreads();
+    for (int e = tid; e < D * D; e += 256) {  // lam <- lam (+ Q^T dO) + K^T dE
+      const int i = e / D, j = e % D;
+      float acc = sLam[i * DP + j];
+      for (int t = 0; t < CH; ++t) {
+        if (CAUSAL) acc = fmaf(sQ[t * DP + i], sD[t * DP + j], acc);
+        acc = fmaf(sK[t * DP + i], sDE[t * DP + j], acc);
+      }
+      sLam[i * DP + j] = acc;
+    }
+    __syncthreads();
+  }
+  float* dst = d_w0 + (long long)bh * dd;
+  for (int e = tid; e < D * D; e += 256) dst[e] = accumulate ? dst[e] + sLam[(e / D) * DP + e % D] : sLam[(e / D) * DP + e % D];
+}
+
+// ---------------------------------------------------------------- backward planning and launch
+struct BwdPlan {
+  int S, L;
+};
+
+template <int D, int CH>
+BwdPlan bwd_plan_dc(int N) {
+  const int C = N / CH;
+  const int lmax = bwd_ring<D, CH>() - 1;
+  int S = (C + lmax - 1) / lmax;
+  const int L = (C + S - 1) / S;
+  S = (C + L - 1) / L;
+  return BwdPlan{S, L};
+}
+
+template <int D>
+BwdPlan bwd_plan_d(int N, int CH) {
+  switch (CH) {
+    case 16: return bwd_plan_dc<D, 16>(N);
+    case 32: return bwd_plan_dc<D, 32>(N);
+    default: return bwd_plan_dc<D, 64>(N);
+  }
+}
+
+BwdPlan bwd_plan(int N, int D, int CH) {
+  switch (D) {
+    case 16: return bwd_plan_d<16>(N, CH);
+    case 32: return bwd_plan_d<32>(N, CH);
+    default: return bwd_plan_d<64>(N, CH);
+  }
+}
+
+template <int D, int CH>
+hipError_t launch_bwd_bf16(bool bidir, int B, int H, int N, float a, const void* q, const void* k,
+                           const void* v, const float* w0, long long w0s, const void* d_o,
+                           void* dq, void* dk, void* dv, float* d_w0, void* ws, hipStream_t st) {
+  const int BH = B * H;
+  const BwdPlan pl = bwd_plan(N, D, CH);
+  const int nrec = bidir ? 4 : 2;
+  const long long DD = (long long)D * D;
+  float* comp = static_cast<float*>(ws);
+  float* win = comp + (pl.S > 1 ? (long long)BH * pl.S * nrec * kMapFloats<D> : 0);
+  float* part = win + (pl.S > 1 ? (long long)nrec * BH * pl.S * DD : 0);
+  const bf16 *Q = (const bf16*)q, *K = (const bf16*)k, *V = (const bf16*)v, *DO = (const bf16*)d_o;
+  bf16 *GQ = (bf16*)dq, *GK = (bf16*)dk, *GV = (bf16*)dv;
+  const dim3 grid(pl.S, BH), block(D / 16 * 64);
+  if (!bidir) {
+    if (pl.S > 1) {
+      hipLaunchKernelGGL((chunk_compose_bwd_bf16<D, CH, false>), dim3(pl.S, BH), dim3(2 * D / 16 * 64), 0,
+                         st, Q, K, V, DO, H, N, a, pl.S, pl.L, comp);
+      hipLaunchKernelGGL((chunk_prefix<D, 2>), dim3(BH, 2, D / 16), dim3(64), 0, st, w0, w0s, 1, H,
+                         pl.S, comp, win);
+    }
+    hipLaunchKernelGGL((chunk_bwd_scan_bf16<D, CH, true>), grid, block, 0, st, Q, K, V, DO, w0, w0s,
+                       H, N, a, pl.S, pl.L, win, 0, 0, 1, (int)kOutBf16, part, GQ, GK, GV, d_w0);
+    return hipGetLastError();
+  }
+  if (pl.S > 1) {
+    hipLaunchKernelGGL((chunk_compose_bwd_bf16<D, CH, true>), dim3(pl.S, BH), dim3(3 * D / 16 * 64), 0,
+                       st, Q, K, V, DO, H, N, a, pl.S, pl.L, comp);
+    hipLaunchKernelGGL((chunk_prefix<D, 4>), dim3(BH, 4, D / 16), dim3(64), 0, st, w0, w0s, 2, H,
+                       pl.S, comp, win);
+  }
+  // reversed scan: forward states in slot 1, its adjoints in slot 2; then the forward scan
+  hipLaunchKernelGGL((chunk_bwd_scan_bf16<D, CH, false>), grid, block, 0, st, Q, K, V, DO, w0, w0s,
+                     H, N, a, pl.S, pl.L, win, 1, 1, 2, (int)kOutPartial, part, GQ, GK, GV, d_w0);
+  hipLaunchKernelGGL((chunk_bwd_scan_bf16<D, CH, false>), grid, block, 0, st, Q, K, V, DO, w0, w0s,
+                     H, N, a, pl.S, pl.L, win, 0, 0, 3, (int)kOutAddPartial, part, GQ, GK, GV, d_w0);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_bwd_bf16_d(bool bidir, int B, int H, int N, int CH, float a, const void* q,
+                             const void* k, const void* v, const float* w0, long long w0s,
+                             const void* d_o, void* dq, void* dk, void* dv, float* d_w0, void* ws,
+                             hipStream_t st) {
+  switch (CH) {
+    case 16: return launch_bwd_bf16<D, 16>(bidir, B, H, N, a, q, k, v, w0, w0s, d_o, dq, dk, dv, d_w0, ws, st);
+    case 32: return launch_bwd_bf16<D, 32>(bidir, B, H, N, a, q, k, v, w0, w0s, d_o, dq, dk, dv, d_w0, ws, st);
+    case 64: return launch_bwd_bf16<D, 64>(bidir, B, H, N, a, q, k, v, w0, w0s, d_o, dq, dk, dv, d_w0, ws, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int D>
+hipError_t launch_bwd_f32(bool bidir, int B, int H, int N, int CH, float a, const void* q,
+                          const void* k, const void* v, const float* w0, long long w0s,
+                          const void* d_o, void* dq, void* dk, void* dv, float* d_w0, void* ws,
+                          hipStream_t st) {
+  const int BH = B * H;
+  float* states = static_cast<float*>(ws);
+  const float *Q = (const float*)q, *K = (const float*)k, *V = (const float*)v, *DO = (const float*)d_o;
+  float *GQ = (float*)dq, *GK = (float*)dk, *GV = (float*)dv;
+  if (!bidir) {
+    hipLaunchKernelGGL((chunk_bwd_f32<D, true>), dim3(BH), dim3(256), 0, st, Q, K, V, DO, w0, w0s, H,
+                       N, CH, a, 0, states, false, GQ, GK, GV, d_w0);
+  } else {
+    hipLaunchKernelGGL((chunk_bwd_f32<D, false>), dim3(BH), dim3(256), 0, st, Q, K, V, DO, w0, w0s, H,
+                       N, CH, a, 1, states, false, GQ, GK, GV, d_w0);
+    hipLaunchKernelGGL((chunk_bwd_f32<D, false>), dim3(BH), dim3(256), 0, st, Q, K, V, DO, w0, w0s, H,
+                       N, CH, a, 0, states, true, GQ, GK, GV, d_w0);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 size_t chunked_workspace_bytes(bool bidir, bool bf16_io, int B, int H, int N, int D, int chunk) {
@@ -809,6 +1475,41 @@ hipError_t chunked_launch(bool bidir, bool bf16_io, int B, int H, int N, int D, 
     case 16: return launch_f32<16>(bidir, B, H, N, chunk, a, q, k, v, w0, w0s, o, w_out, ws, st);
     case 32: return launch_f32<32>(bidir, B, H, N, chunk, a, q, k, v, w0, w0s, o, w_out, ws, st);
     case 64: return launch_f32<64>(bidir, B, H, N, chunk, a, q, k, v, w0, w0s, o, w_out, ws, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+size_t chunked_bwd_workspace_bytes(bool bidir, bool bf16_io, int B, int H, int N, int D, int chunk) {
+  const size_t BH = (size_t)B * H, DD = (size_t)D * D, C = (size_t)N / (size_t)chunk;
+  // fp32: the scan's C + 1 states per (b, h)
+  if (!bf16_io) return BH * (C + 1) * DD * sizeof(float);
+  const BwdPlan pl = bwd_plan(N, D, chunk);
+  const size_t nrec = bidir ? 4 : 2;
+  size_t bytes = 0;
+  if (pl.S > 1)  // map records (-Dev bf16 + offset fp32) and the folded states, per slot
+    bytes += BH * pl.S * nrec * (DD / 2 + DD) * sizeof(float) + nrec * BH * pl.S * DD * sizeof(float);
+  if (bidir)  // the reversed scan's fp32 partial dq, dk, dv
+    bytes += 3 * (size_t)B * N * H * D * sizeof(float);
+  return bytes;
+}
+
+hipError_t chunked_bwd_launch(bool bidir, bool bf16_io, int B, int H, int N, int D, int chunk,
+                              float eta, const void* q, const void* k, const void* v,
+                              const float* w0, long long w0s, const void* d_o, void* d_q,
+                              void* d_k, void* d_v, float* d_w0, void* ws, hipStream_t st) {
+  const float a = eta / (float)chunk;
+  if (bf16_io) {
+    switch (D) {
+      case 16: return launch_bwd_bf16_d<16>(bidir, B, H, N, chunk, a, q, k, v, w0, w0s, d_o, d_q, d_k, d_v, d_w0, ws, st);
+      case 32: return launch_bwd_bf16_d<32>(bidir, B, H, N, chunk, a, q, k, v, w0, w0s, d_o, d_q, d_k, d_v, d_w0, ws, st);
+      case 64: return launch_bwd_bf16_d<64>(bidir, B, H, N, chunk, a, q, k, v, w0, w0s, d_o, d_q, d_k, d_v, d_w0, ws, st);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  switch (D) {
+    case 16: return launch_bwd_f32<16>(bidir, B, H, N, chunk, a, q, k, v, w0, w0s, d_o, d_q, d_k, d_v, d_w0, ws, st);
+    case 32: return launch_bwd_f32<32>(bidir, B, H, N, chunk, a, q, k, v, w0, w0s, d_o, d_q, d_k, d_v, d_w0, ws, st);
+    case 64: return launch_bwd_f32<64>(bidir, B, H, N, chunk, a, q, k, v, w0, w0s, d_o, d_q, d_k, d_v, d_w0, ws, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -31,6 +31,11 @@ size_t chunked_workspace_bytes(bool bidir, bool bf16_io, int B, int H, int N, in
 hipError_t chunked_launch(bool bidir, bool bf16_io, int B, int H, int N, int D, int chunk,
                           float eta, const void* q, const void* k, const void* v, const float* w0,
                           long long w0_bstride, void* o, float* w_out, void* ws, hipStream_t st);
+size_t chunked_bwd_workspace_bytes(bool bidir, bool bf16_io, int B, int H, int N, int D, int chunk);
+hipError_t chunked_bwd_launch(bool bidir, bool bf16_io, int B, int H, int N, int D, int chunk,
+                              float eta, const void* q, const void* k, const void* v,
+                              const float* w0, long long w0_bstride, const void* d_o, void* d_q,
+                              void* d_k, void* d_v, float* d_w0, void* ws, hipStream_t st);
 
 // ---- TTT-MLP --------------------------------------------------------------------------------
 bool mlp_supported(int D, int Dh, int chunk);

@@ -14,7 +14,8 @@ LIB_PATH = os.path.join(HERE, "libttt.so")
 
 TTT_OK, TTT_ERR_INVALID, TTT_ERR_UNSUPPORTED, TTT_ERR_WORKSPACE, TTT_ERR_HIP = range(5)
 TTT_F32, TTT_BF16 = 0, 1
-TTT_OP_FULLBATCH, TTT_OP_CAUSAL, TTT_OP_BIDIR, TTT_OP_MLP, TTT_OP_FULLBATCH_BWD, TTT_OP_BIDIR2D = range(6)
+(TTT_OP_FULLBATCH, TTT_OP_CAUSAL, TTT_OP_BIDIR, TTT_OP_MLP, TTT_OP_FULLBATCH_BWD, TTT_OP_BIDIR2D, TTT_OP_CAUSAL_BWD,
+ TTT_OP_BIDIR_BWD) = range(8)
 TTT_NOALLOC_SCRATCH_BYTES = 32 << 20  # static scratch of ttt_forward_fullbatch_noalloc, per device
 
 # Every symbol include/ttt.h declares, with its ctypes signature.
@@ -26,6 +27,10 @@ SIGNATURES = {
                                               _vp, _vp, _c_ll, _vp, _vp, _vp, _sz, _vp]),
     "ttt_backward_fullbatch": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _vp, _vp, _vp, _vp, _c_ll,
                                         _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "ttt_backward_chunked_causal": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _vp, _vp, _vp,
+                                             _vp, _c_ll, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "ttt_backward_chunked_bidir": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _vp, _vp, _vp,
+                                            _vp, _c_ll, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "ttt_forward_chunked_bidir2d": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _vp,
                                              _vp, _vp, _vp, _c_ll, _vp, _vp, _vp, _sz, _vp]),
     "ttt_forward_chunked_causal": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _vp, _vp, _vp,
@@ -202,10 +207,7 @@ def ttt_forward_fullbatch_epochs(q, k, v, w0, epochs: int, eta: float = 1.0, *, 
                    stream, epochs=epochs)
 
 
-def ttt_backward_fullbatch(q, k, v, w0, d_o, eta: float = 1.0, *, d_q=None, d_k=None, d_v=None, d_w0=None,
-                           workspace=None, stream=None):
-    """Gradients (dq, dk, dv, dW0) of the full-batch layer for the outer loop, given d_o = dL/dO.
-    d_w0 is [B, H, D, D] per batch element (sum it over the batch when w0 is shared)."""
+def _backward(op, name, q, k, v, w0, d_o, chunk, eta, d_q, d_k, d_v, d_w0, workspace, stream):
     lib = load_library()
     _check_io(q, k, v)
     torch = _torch()
@@ -214,20 +216,44 @@ def ttt_backward_fullbatch(q, k, v, w0, d_o, eta: float = 1.0, *, d_q=None, d_k=
     dt = _dtype_code(q)
     stride = _state_stride("w0", w0, B, H, D, D, dev)
     _check_tensor("d_o", d_o, q.shape, q.dtype, dev)
-    for name, t in (("d_q", d_q), ("d_k", d_k), ("d_v", d_v)):
-        _check_out(name, t, q.shape, q.dtype, dev)
+    for nm, t in (("d_q", d_q), ("d_k", d_k), ("d_v", d_v)):
+        _check_out(nm, t, q.shape, q.dtype, dev)
     _check_out("d_w0", d_w0, (B, H, D, D), torch.float32, dev)
     with torch.cuda.device(dev):
         d_q = torch.empty_like(q) if d_q is None else d_q
         d_k = torch.empty_like(q) if d_k is None else d_k
         d_v = torch.empty_like(q) if d_v is None else d_v
         d_w0 = torch.empty((B, H, D, D), dtype=torch.float32, device=dev) if d_w0 is None else d_w0
-        ws, ws_size = _workspace(TTT_OP_FULLBATCH_BWD, dt, B, H, N, D, 0, 0, workspace, dev)
-        st = lib.ttt_backward_fullbatch(dt, B, H, N, D, float(eta), _ptr(q), _ptr(k), _ptr(v), _ptr(w0), stride,
-                                        _ptr(d_o), _ptr(d_q), _ptr(d_k), _ptr(d_v), _ptr(d_w0), _ptr(ws), ws_size,
-                                        _stream(stream, dev))
-    _raise(st, "ttt_backward_fullbatch")
+        ws, ws_size = _workspace(op, dt, B, H, N, D, 0, chunk, workspace, dev)
+        args = [dt, B, H, N, D] + ([int(chunk)] if op != TTT_OP_FULLBATCH_BWD else []) + [
+            float(eta), _ptr(q), _ptr(k), _ptr(v), _ptr(w0), stride, _ptr(d_o), _ptr(d_q), _ptr(d_k), _ptr(d_v),
+            _ptr(d_w0), _ptr(ws), ws_size, _stream(stream, dev)]
+        st = getattr(lib, name)(*args)
+    _raise(st, name)
     return d_q, d_k, d_v, d_w0
+
+
+def ttt_backward_fullbatch(q, k, v, w0, d_o, eta: float = 1.0, *, d_q=None, d_k=None, d_v=None, d_w0=None,
+                           workspace=None, stream=None):
+    """Gradients (dq, dk, dv, dW0) of the full-batch layer for the outer loop, given d_o = dL/dO.
+    d_w0 is [B, H, D, D] per batch element (sum it over the batch when w0 is shared)."""
+    return _backward(TTT_OP_FULLBATCH_BWD, "ttt_backward_fullbatch", q, k, v, w0, d_o, 0, eta, d_q, d_k, d_v, d_w0,
+                     workspace, stream)
+
+
+def ttt_backward_chunked_causal(q, k, v, w0, d_o, chunk: int, eta: float = 1.0, *, d_q=None, d_k=None, d_v=None,
+                                d_w0=None, workspace=None, stream=None):
+    """Gradients (dq, dk, dv, dW0) of the causal chunked layer given d_o = dL/dO (no gradient through
+    the end state). d_w0 is [B, H, D, D] per batch element."""
+    return _backward(TTT_OP_CAUSAL_BWD, "ttt_backward_chunked_causal", q, k, v, w0, d_o, chunk, eta, d_q, d_k, d_v,
+                     d_w0, workspace, stream)
+
+
+def ttt_backward_chunked_bidir(q, k, v, w0, d_o, chunk: int, eta: float = 1.0, *, d_q=None, d_k=None, d_v=None,
+                               d_w0=None, workspace=None, stream=None):
+    """Gradients (dq, dk, dv, dW0) of the bidirectional scan (both scans summed) given d_o = dL/dO."""
+    return _backward(TTT_OP_BIDIR_BWD, "ttt_backward_chunked_bidir", q, k, v, w0, d_o, chunk, eta, d_q, d_k, d_v,
+                     d_w0, workspace, stream)
 
 
 def ttt_forward_fullbatch_noalloc(q, k, v, w0, eta: float = 1.0, *, o, w_out=None, stream=None):

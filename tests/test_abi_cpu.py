@@ -27,7 +27,7 @@ def test_header_declares_the_entry_points():
         "ttt_forward_fullbatch", "ttt_forward_chunked_causal", "ttt_forward_chunked_bidir", "ttt_mlp_forward",
         "ttt_workspace_size", "ttt_status_string", "ttt_forward_fullbatch_noalloc", "ttt_dwconv3x3",
         "ttt_forward_fullbatch_epochs", "ttt_backward_fullbatch", "ttt_forward_chunked_bidir2d",
-        "ttt_block_epilogue"])
+        "ttt_block_epilogue", "ttt_backward_chunked_causal", "ttt_backward_chunked_bidir"])
 
 
 def test_block_epilogue_validation():
@@ -72,6 +72,37 @@ def test_backward_validation_rejects_before_launch():
     assert call(wsb=16) == 3
     assert call(D=48) == 2
     assert T.ttt_workspace_size(T.TTT_OP_FULLBATCH_BWD, T.TTT_BF16, 64, 2, 3136, 32) > 0
+
+
+@pytest.mark.parametrize("fn", ["ttt_backward_chunked_causal", "ttt_backward_chunked_bidir"])
+def test_chunked_backward_validation_rejects_before_launch(fn):
+    lib = T.load_library()
+    f = getattr(lib, fn)
+    call = lambda do=5, dq=6, dk=7, dv=8, dw=9, ws=10, wsb=1 << 30, D=64, N=1024, chunk=16: f(  # noqa: E731
+        T.TTT_BF16, 1, 1, N, D, chunk, 1.0, _p(0), _p(1), _p(2), _p(3), 0, None if do is None else _p(do),
+        None if dq is None else _p(dq), None if dk is None else _p(dk), None if dv is None else _p(dv),
+        None if dw is None else _p(dw), None if ws is None else _p(ws), wsb, None)
+    assert call(do=None) == 1
+    assert call(dw=None) == 1
+    assert call(dk=0) == 1               # a gradient output overlaps q
+    assert call(dv=6) == 1               # two outputs overlap
+    assert call(ws=None) == 3            # 1024 tokens of 16: several segments, workspace needed
+    assert call(wsb=16) == 3
+    assert call(D=48) == 2
+    assert call(chunk=24) == 2
+    assert call(N=1000) == 1             # not a multiple of the chunk
+    op = T.TTT_OP_CAUSAL_BWD if "causal" in fn else T.TTT_OP_BIDIR_BWD
+    assert T.ttt_workspace_size(op, T.TTT_BF16, 2, 12, 16384, 64, 0, 16) > 0
+    assert T.ttt_workspace_size(op, T.TTT_BF16, 2, 12, 16384, 64, 0, 24) == 0
+    # fp32: the scan's states, C + 1 per (b, h)
+    assert T.ttt_workspace_size(op, T.TTT_F32, 2, 3, 256, 32, 0, 16) == 2 * 3 * 17 * 32 * 32 * 4
+
+
+def test_chunked_backward_single_segment_needs_no_workspace():
+    """A causal sequence that fits one segment needs no workspace (the bidirectional one always holds
+    one scan's fp32 partial gradients)."""
+    assert T.ttt_workspace_size(T.TTT_OP_CAUSAL_BWD, T.TTT_BF16, 1, 1, 32, 64, 0, 16) == 0
+    assert T.ttt_workspace_size(T.TTT_OP_BIDIR_BWD, T.TTT_BF16, 1, 1, 32, 64, 0, 16) == 3 * 32 * 64 * 4
 
 
 def test_fullbatch_epochs_validation():
@@ -297,6 +328,34 @@ def test_binding_rejects_bad_tensors_before_launch(fake_cuda, fn):
         with pytest.raises((ValueError, TypeError)):
             call()
         print("rejected:", what)
+
+
+@pytest.mark.parametrize("fn", ["ttt_backward_fullbatch", "ttt_backward_chunked_causal",
+                                "ttt_backward_chunked_bidir"])
+def test_binding_rejects_bad_backward_tensors_before_launch(fake_cuda, fn):
+    torch, make = fake_cuda
+    f32 = torch.float32
+    B, N, H, D = 2, 64, 3, 32
+    q = make(B, N, H, D)
+    w0 = make(H, D, D, dtype=f32)
+    f = getattr(T, fn)
+    cases = [
+        dict(d_o=make(B, N, H, 16)),
+        dict(d_o=make(B, N, H, D, dtype=f32)),
+        dict(d_q=make(B, N, H, 16)),
+        dict(d_k=make(B, N, H, D, dtype=f32)),
+        dict(d_w0=make(H, D, D, dtype=f32)),             # per batch element: [B, H, D, D]
+        dict(d_w0=make(B, H, D, D)),                     # bf16 instead of fp32
+        dict(w0=make(H, D, 16, dtype=f32)),
+    ]
+    for kw in cases:
+        d_o = kw.pop("d_o", q)
+        a_w0 = kw.pop("w0", w0)
+        with pytest.raises((ValueError, TypeError)):
+            if fn == "ttt_backward_fullbatch":
+                f(q, q, q, a_w0, d_o, 1.0, **kw)
+            else:
+                f(q, q, q, a_w0, d_o, 16, 1.0, **kw)
 
 
 def test_binding_rejects_bad_mlp_tensors_before_launch(fake_cuda):
