@@ -571,80 +571,200 @@ __global__ __launch_bounds__(D / 16 * 64) void chunk_scan_bf16(
 }
 
 // ---------------------------------------------------------------- fp32 I/O, plain FMA
-// One workgroup per (b, h); the state lives in LDS and tokens are processed one by one in the
-// primal form (weights of each token materialised), in true fp32. The reverse scan of the
-// bidirectional variant stores its per-chunk states in the workspace.
-enum F32Mode { kF32Causal = 0, kF32ReverseStore = 1, kF32ForwardBoth = 2 };
+// The fp32 path takes the same decomposition as the bf16 kernels (the plan's segments, composed
+// maps stored as -Dev = P - I and R, the prefix fold, per-segment rescans with the dual-form causal
+// read-out), in fp32 FMA with workgroup-wide loops over LDS tiles, so that the fp32 parity bound
+// checks that algebra itself. Records hold -Dev and R in fp32 (kF32MapFloats per direction).
+template <int D>
+constexpr int kF32MapFloats = 2 * D * D;
+constexpr int kF32Threads = 256;
 
+// Y[t][j] = sum_k X[t][k] M[k][j] - (Vt ? Vt[t][j] : 0) for t < rows (LDS tiles, row pitch D + 1).
+template <int D>
+__device__ __forceinline__ void f32_rows_times(float* Y, const float* X, const float* M, const float* Vt,
+                                               int rows) {
+  constexpr int DP = D + 1;
+  for (int e = threadIdx.x; e < rows * D; e += kF32Threads) {
+    const int t = e / D, j = e % D;
+    float acc = Vt ? -Vt[t * DP + j] : 0.f;
+    for (int k = 0; k < D; ++k) acc = fmaf(X[t * DP + k], M[k * DP + j], acc);
+    Y[t * DP + j] = acc;
+  }
+}
+
+// M[i][j] += s sum_t X[t][i] Y[t][j] over t < rows.
+template <int D>
+__device__ __forceinline__ void f32_add_xt_y(float* M, const float* X, const float* Y, float s, int rows) {
+  constexpr int DP = D + 1;
+  for (int e = threadIdx.x; e < D * D; e += kF32Threads) {
+    const int i = e / D, j = e % D;
+    float acc = 0.f;
+    for (int t = 0; t < rows; ++t) acc = fmaf(X[t * DP + i], Y[t * DP + j], acc);
+    M[i * DP + j] = fmaf(s, acc, M[i * DP + j]);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void f32_load_rows(float* dst, const float* src, long long ts, int rows) {
+  constexpr int DP = D + 1;
+  for (int e = threadIdx.x; e < rows * D; e += kF32Threads) dst[(e / D) * DP + e % D] = src[(e / D) * ts + e % D];
+}
+
+// 1. compose: the segment's forward map W -> P W + R (and, bidirectional, the reversed scan's
+// offset R_rev = a sum_c (K_c P_{c-1})^T V_c), from P = I, R = 0.
+template <int D, bool BIDIR>
+__global__ __launch_bounds__(kF32Threads) void chunk_compose_f32(const float* __restrict__ k,
+                                                                 const float* __restrict__ v, int H,
+                                                                 int N, int CH, float a, int S, int L,
+                                                                 float* __restrict__ comp) {
+  constexpr int DP = D + 1;
+  __shared__ float sK[64 * DP], sV[64 * DP], sY[64 * DP], sYR[64 * DP];
+  __shared__ float sP[D * DP], sR[D * DP], sRR[BIDIR ? D * DP : 1];
+  const int s = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H, tid = threadIdx.x;
+  const int C = N / CH, lo = s * L, hi = min(C, lo + L);
+  const long long ts = (long long)H * D, head0 = (long long)b * N * ts + (long long)h * D;
+  for (int e = tid; e < D * D; e += kF32Threads) {
+    sP[(e / D) * DP + e % D] = (e / D == e % D) ? 1.f : 0.f;
+    sR[(e / D) * DP + e % D] = 0.f;
+    if (BIDIR) sRR[(e / D) * DP + e % D] = 0.f;
+  }
+  for (int c = lo; c < hi; ++c) {
+    __syncthreads();
+    f32_load_rows<D>(sK, k + head0 + (long long)c * CH * ts, ts, CH);
+    f32_load_rows<D>(sV, v + head0 + (long long)c * CH * ts, ts, CH);
+    __syncthreads();
+    f32_rows_times<D>(sY, sK, sP, nullptr, CH);  // K P
+    f32_rows_times<D>(sYR, sK, sR, sV, CH);      // K R - V
+    __syncthreads();
+    if (BIDIR) f32_add_xt_y<D>(sRR, sY, sV, a, CH);
+    f32_add_xt_y<D>(sP, sK, sY, -a, CH);
+    f32_add_xt_y<D>(sR, sK, sYR, -a, CH);
+  }
+  __syncthreads();
+  float* rec = comp + ((long long)bh * S + s) * (BIDIR ? 2 : 1) * kF32MapFloats<D>;
+  for (int e = tid; e < D * D; e += kF32Threads) {
+    const int i = e / D, j = e % D;
+    const float nd = sP[i * DP + j] - (i == j ? 1.f : 0.f);  // -Dev = P - I
+    rec[e] = nd;
+    rec[D * D + e] = sR[i * DP + j];
+    if (BIDIR) {
+      rec[kF32MapFloats<D> + j * D + i] = nd;  // -Dev_r = -Dev^T
+      rec[kF32MapFloats<D> + D * D + e] = sRR[i * DP + j];
+    }
+  }
+}
+
+// 2. prefix: per (b, h, direction), W <- W + (-Dev) W + R over the segments in fold order
+// (reversed for direction 1), storing every segment's entry state.
+template <int D, bool BIDIR>
+__global__ __launch_bounds__(kF32Threads) void chunk_prefix_f32(const float* __restrict__ w0,
+                                                                long long w0_bstride, int H, int S,
+                                                                const float* __restrict__ comp,
+                                                                float* __restrict__ win) {
+  constexpr int DP = D + 1;
+  __shared__ float sW[D * DP], sT[D * DP];
+  const int bh = blockIdx.x, dir = blockIdx.y, b = bh / H, h = bh % H, tid = threadIdx.x;
+  const int BH = gridDim.x;
+  const long long DD = (long long)D * D;
+  const float* W0 = w0 + b * w0_bstride + h * DD;
+  for (int e = tid; e < D * D; e += kF32Threads) sW[(e / D) * DP + e % D] = W0[e];
+  float* dst = win + ((long long)dir * BH + bh) * S * DD;
+  for (int i = 0; i < S; ++i) {
+    const int sg = dir == 0 ? i : S - 1 - i;
+    __syncthreads();
+    for (int e = tid; e < D * D; e += kF32Threads) dst[sg * DD + e] = sW[(e / D) * DP + e % D];
+    if (i == S - 1) break;
+    const float* rec = comp + ((long long)bh * S + sg) * (BIDIR ? 2 : 1) * kF32MapFloats<D> + dir * kF32MapFloats<D>;
+    for (int e = tid; e < D * D; e += kF32Threads) {
+      const int r = e / D, c = e % D;
+      float acc = rec[D * D + e];
+      for (int k2 = 0; k2 < D; ++k2) acc = fmaf(rec[r * D + k2], sW[k2 * DP + c], acc);
+      sT[r * DP + c] = acc;
+    }
+    __syncthreads();
+    for (int e = tid; e < D * D; e += kF32Threads) sW[(e / D) * DP + e % D] += sT[(e / D) * DP + e % D];
+  }
+}
+
+// 3. scan: per (segment, b, h), from the segment's entry state. Causal: O = Q W - a tril(Q K^T) E,
+// W <- W - a K^T E. Bidirectional: the reversed scan over the segment stores each W^r_c in
+// `rstates`, then the forward scan reads out O = Q (W^f_c + W^r_c).
 template <int D, int MODE>
-__global__ __launch_bounds__(256) void chunk_scan_f32(const float* __restrict__ q,
-                                                      const float* __restrict__ k,
-                                                      const float* __restrict__ v,
-                                                      const float* __restrict__ w0,
-                                                      long long w0_bstride, int H, int N, int CH,
-                                                      float a, float* __restrict__ states,
-                                                      float* __restrict__ o,
-                                                      float* __restrict__ w_out) {
-  __shared__ float sW[D][D + 1], sS[D][D + 1];
-  __shared__ float sk[D], sq[D], se[D];
-  constexpr int PER = (D * D + 255) / 256;
-  const int bh = blockIdx.x, b = bh / H, h = bh % H, tid = threadIdx.x;
-  const int C = N / CH;
-  const long long ts = (long long)H * D, dd = (long long)D * D;
-  const float* W0 = w0 + b * w0_bstride + h * dd;
-  for (int e = tid; e < D * D; e += 256) sW[e / D][e % D] = W0[e];
-  const long long head0 = (long long)b * N * ts + (long long)h * D;
-  float* st_bh = states ? states + bh * (long long)C * dd : nullptr;
-  for (int it = 0; it < C; ++it) {
-    const int c = (MODE == kF32ReverseStore) ? C - 1 - it : it;
-    for (int e = tid; e < D * D; e += 256) sS[e / D][e % D] = 0.f;
+__global__ __launch_bounds__(kF32Threads) void chunk_scan_dual_f32(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    const float* __restrict__ w0, long long w0_bstride, int H, int N, int CH, float a, int S, int L,
+    const float* __restrict__ win, float* __restrict__ rstates, float* __restrict__ o,
+    float* __restrict__ w_out) {
+  constexpr int DP = D + 1;
+  __shared__ float sK[64 * DP], sV[64 * DP], sQ[64 * DP], sE[64 * DP];
+  __shared__ float sW[D * DP], sS[64 * 65];
+  const int s = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H, tid = threadIdx.x;
+  const int BH = gridDim.y;
+  const int C = N / CH, lo = s * L, hi = min(C, lo + L);
+  const long long ts = (long long)H * D, head0 = (long long)b * N * ts + (long long)h * D;
+  const long long DD = (long long)D * D;
+  auto entry = [&](int dir) {
+    const float* src = S == 1 ? w0 + b * w0_bstride + h * DD : win + (((long long)dir * BH + bh) * S + s) * DD;
+    for (int e = tid; e < D * D; e += kF32Threads) sW[(e / D) * DP + e % D] = src[e];
+  };
+  auto step = [&](int c, bool with_q) {  // stage chunk c, E = K W - V, W <- W - a K^T E (after use)
     __syncthreads();
-    for (int i = 0; i < CH; ++i) {
-      const long long off = head0 + ((long long)c * CH + i) * ts;
-      if (tid < D) {
-        sk[tid] = k[off + tid];
-        sq[tid] = (MODE == kF32ReverseStore) ? 0.f : q[off + tid];
-      }
-      __syncthreads();
-      if (tid < D) {  // e = k W_s - v
-        float acc = -v[off + tid];
-        for (int j = 0; j < D; ++j) acc = fmaf(sk[j], sW[j][tid], acc);
-        se[tid] = acc;
-      }
-      __syncthreads();
-      for (int u = 0; u < PER; ++u) {  // S += k^T e
-        const int e = tid + 256 * u;
-        if (e < D * D) sS[e / D][e % D] = fmaf(sk[e / D], se[e % D], sS[e / D][e % D]);
-      }
-      __syncthreads();
-      if (MODE == kF32Causal && tid < D) {  // o_i = q_i (W_s - a S_i)
-        float acc = 0.f;
-        for (int j = 0; j < D; ++j) acc = fmaf(sq[j], fmaf(-a, sS[j][tid], sW[j][tid]), acc);
-        o[off + tid] = acc;
-      }
-      __syncthreads();
-    }
-    for (int e = tid; e < D * D; e += 256) sW[e / D][e % D] = fmaf(-a, sS[e / D][e % D], sW[e / D][e % D]);
+    f32_load_rows<D>(sK, k + head0 + (long long)c * CH * ts, ts, CH);
+    f32_load_rows<D>(sV, v + head0 + (long long)c * CH * ts, ts, CH);
+    if (with_q) f32_load_rows<D>(sQ, q + head0 + (long long)c * CH * ts, ts, CH);
     __syncthreads();
-    if (MODE == kF32ReverseStore)
-      for (int e = tid; e < D * D; e += 256) st_bh[c * dd + e] = sW[e / D][e % D];
-    if (MODE == kF32ForwardBoth) {
-      for (int e = tid; e < D * D; e += 256) sS[e / D][e % D] = sW[e / D][e % D] + st_bh[c * dd + e];
+    f32_rows_times<D>(sE, sK, sW, sV, CH);
+    __syncthreads();
+  };
+  float* rs_bh = MODE == kBidir ? rstates + (long long)bh * C * DD : nullptr;
+  if (MODE == kBidir) {
+    entry(1);
+    for (int c = hi - 1; c >= lo; --c) {
+      step(c, false);
+      f32_add_xt_y<D>(sW, sK, sE, -a, CH);
       __syncthreads();
-      for (int e = tid; e < CH * D; e += 256) {
-        const int i = e / D, col = e % D;
-        const long long off = head0 + ((long long)c * CH + i) * ts;
-        float acc = 0.f;
-        for (int j = 0; j < D; ++j) acc = fmaf(q[off + j], sS[j][col], acc);
-        o[off + col] = acc;
-      }
+      for (int e = tid; e < D * D; e += kF32Threads) rs_bh[c * DD + e] = sW[(e / D) * DP + e % D];
     }
     __syncthreads();
+    if (s == 0 && w_out)
+      for (int e = tid; e < D * D; e += kF32Threads) w_out[(long long)BH * DD + bh * DD + e] = sW[(e / D) * DP + e % D];
   }
-  if (w_out) {
-    float* dst = w_out + (MODE == kF32ReverseStore ? (long long)gridDim.x * dd : 0) + bh * dd;
-    for (int e = tid; e < D * D; e += 256) dst[e] = sW[e / D][e % D];
+  entry(0);
+  for (int c = lo; c < hi; ++c) {
+    step(c, true);
+    float* oc = o + head0 + (long long)c * CH * ts;
+    if (MODE == kCausal) {
+      for (int e = tid; e < CH * CH; e += kF32Threads) {  // S = tril(Q K^T)
+        const int t = e / CH, u = e % CH;
+        float acc = 0.f;
+        if (u <= t)
+          for (int kk = 0; kk < D; ++kk) acc = fmaf(sQ[t * DP + kk], sK[u * DP + kk], acc);
+        sS[t * 65 + u] = acc;
+      }
+      __syncthreads();
+      for (int e = tid; e < CH * D; e += kF32Threads) {  // O = Q W - a S E
+        const int t = e / D, j = e % D;
+        float qw = 0.f, se = 0.f;
+        for (int kk = 0; kk < D; ++kk) qw = fmaf(sQ[t * DP + kk], sW[kk * DP + j], qw);
+        for (int u = 0; u <= t; ++u) se = fmaf(sS[t * 65 + u], sE[u * DP + j], se);
+        oc[t * ts + j] = fmaf(-a, se, qw);
+      }
+      __syncthreads();
+      f32_add_xt_y<D>(sW, sK, sE, -a, CH);
+    } else {
+      f32_add_xt_y<D>(sW, sK, sE, -a, CH);
+      __syncthreads();
+      for (int e = tid; e < CH * D; e += kF32Threads) {  // O = Q (W^f_c + W^r_c)
+        const int t = e / D, j = e % D;
+        float acc = 0.f;
+        for (int kk = 0; kk < D; ++kk) acc = fmaf(sQ[t * DP + kk], sW[kk * DP + j] + rs_bh[c * DD + kk * D + j], acc);
+        oc[t * ts + j] = acc;
+      }
+    }
   }
+  __syncthreads();
+  if (s == S - 1 && w_out)
+    for (int e = tid; e < D * D; e += kF32Threads) w_out[bh * DD + e] = sW[(e / D) * DP + e % D];
 }
 
 // ---------------------------------------------------------------- planning and launch
@@ -754,19 +874,32 @@ hipError_t launch_f32(bool bidir, int B, int H, int N, int CH, float a, const vo
                       const void* k, const void* v, const float* w0, long long w0s, void* o,
                       float* w_out, void* ws, hipStream_t st) {
   const int BH = B * H;
-  if (!bidir) {
-    hipLaunchKernelGGL((chunk_scan_f32<D, kF32Causal>), dim3(BH), dim3(256), 0, st,
-                       (const float*)q, (const float*)k, (const float*)v, w0, w0s, H, N, CH, a,
-                       nullptr, (float*)o, w_out);
-  } else {
-    float* states = static_cast<float*>(ws);
-    hipLaunchKernelGGL((chunk_scan_f32<D, kF32ReverseStore>), dim3(BH), dim3(256), 0, st,
-                       (const float*)q, (const float*)k, (const float*)v, w0, w0s, H, N, CH, a,
-                       states, (float*)o, w_out);
-    hipLaunchKernelGGL((chunk_scan_f32<D, kF32ForwardBoth>), dim3(BH), dim3(256), 0, st,
-                       (const float*)q, (const float*)k, (const float*)v, w0, w0s, H, N, CH, a,
-                       states, (float*)o, w_out);
+  const ChunkPlan pl = chunk_plan(bidir, B, H, N, D, CH);
+  const long long DD = (long long)D * D;
+  const int ndir = bidir ? 2 : 1;
+  float* comp = static_cast<float*>(ws);
+  float* win = comp + (pl.S > 1 ? (long long)BH * pl.S * ndir * kF32MapFloats<D> : 0);
+  float* rstates = win + (pl.S > 1 ? (long long)ndir * BH * pl.S * DD : 0);
+  const float *Q = (const float*)q, *K = (const float*)k, *V = (const float*)v;
+  if (pl.S > 1) {
+    if (bidir) {
+      hipLaunchKernelGGL((chunk_compose_f32<D, true>), dim3(pl.S, BH), dim3(kF32Threads), 0, st, K, V, H, N, CH, a,
+                         pl.S, pl.L, comp);
+      hipLaunchKernelGGL((chunk_prefix_f32<D, true>), dim3(BH, 2), dim3(kF32Threads), 0, st, w0, w0s, H, pl.S,
+                         comp, win);
+    } else {
+      hipLaunchKernelGGL((chunk_compose_f32<D, false>), dim3(pl.S, BH), dim3(kF32Threads), 0, st, K, V, H, N, CH,
+                         a, pl.S, pl.L, comp);
+      hipLaunchKernelGGL((chunk_prefix_f32<D, false>), dim3(BH, 1), dim3(kF32Threads), 0, st, w0, w0s, H, pl.S,
+                         comp, win);
+    }
   }
+  if (bidir)
+    hipLaunchKernelGGL((chunk_scan_dual_f32<D, kBidir>), dim3(pl.S, BH), dim3(kF32Threads), 0, st, Q, K, V, w0,
+                       w0s, H, N, CH, a, pl.S, pl.L, win, rstates, (float*)o, w_out);
+  else
+    hipLaunchKernelGGL((chunk_scan_dual_f32<D, kCausal>), dim3(pl.S, BH), dim3(kF32Threads), 0, st, Q, K, V, w0,
+                       w0s, H, N, CH, a, pl.S, pl.L, win, rstates, (float*)o, w_out);
   return hipGetLastError();
 }
 
@@ -1447,12 +1580,15 @@ hipError_t launch_bwd_f32(bool bidir, int B, int H, int N, int CH, float a, cons
 
 size_t chunked_workspace_bytes(bool bidir, bool bf16_io, int B, int H, int N, int D, int chunk) {
   const size_t BH = (size_t)B * H, DD = (size_t)D * D;
-  if (!bf16_io) {
-    if (!bidir) return 0;
-    // fp32 path: reverse-scan state after every chunk, C * D * D fp32 per (b, h)
-    return BH * ((size_t)N / (size_t)chunk) * DD * sizeof(float);
-  }
   const ChunkPlan pl = chunk_plan(bidir, B, H, N, D, chunk);
+  if (!bf16_io) {
+    // fp32 path: map records (-Dev and R, fp32) and entry states per direction, and for the
+    // bidirectional scan the reversed scan's state after every chunk (C * D * D per (b, h))
+    const size_t ndir = bidir ? 2 : 1;
+    size_t bytes = pl.S > 1 ? BH * pl.S * ndir * 2 * DD * sizeof(float) + ndir * BH * pl.S * DD * sizeof(float) : 0;
+    if (bidir) bytes += BH * ((size_t)N / (size_t)chunk) * DD * sizeof(float);
+    return bytes;
+  }
   if (pl.S == 1) return 0;
   // segment map records (-Dev bf16 + R fp32, per direction) + entry states per direction
   const size_t ndir = bidir ? 2 : 1;
