@@ -1131,16 +1131,13 @@ __global__ __launch_bounds__((BIDIR ? 3 : 2) * (D / 16) * 64) void chunk_compose
 
 // ---------------------------------------------------------------- B3. segment scan (backward)
 // LDS of the backward scan: five [CH x D] tiles (K; V, then E; Q; dO; dE), -a lam (row-major) and
-// the ring of the segment's forward states. The ring takes what a budget leaves (two workgroups
-// per CU for chunks of up to 32 tokens, one for 64): it bounds the chunks per segment.
-template <int D, int CH>
-constexpr int bwd_fixed_lds() { return (5 * CH + D) * lds_pitch<D>() * 2; }
-template <int D, int CH>
-constexpr int bwd_ring() {
-  constexpr int budget = CH <= 32 ? 80 * 1024 : 156 * 1024;
-  constexpr int n = (budget - bwd_fixed_lds<D, CH>()) / (D * lds_pitch<D>() * 2);
-  return n > 17 ? 17 : n;
-}
+// two row-major state tiles (this chunk's start state and the next chunk's, which is this chunk's
+// end state). The segment's forward states go to a per-segment ring in the workspace as bf16
+// accumulator-layout tiles: each wave writes its own columns in the states pass and reads back
+// only what it wrote, so the ring needs no cross-wave ordering; segments are as long as the plan
+// wants, with no LDS bound.
+template <int D>
+constexpr long long kRingState = (long long)D * D;  // bf16 elements per state in the ring
 
 // Output modes: write bf16; write fp32 partials (reversed scan of the bidirectional layer); add the
 // partials and write bf16 (its forward scan, launched after).
@@ -1150,12 +1147,11 @@ template <int D, int CH, bool CAUSAL>
 __global__ __launch_bounds__(D / 16 * 64) void chunk_bwd_scan_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ d_o, const float* __restrict__ w0, long long w0_bstride, int H, int N,
-    float a, int S, int L, const float* __restrict__ win, int dir, int fwd_slot, int adj_slot,
-    int out_mode, float* __restrict__ part, bf16* __restrict__ dq, bf16* __restrict__ dk,
-    bf16* __restrict__ dv, float* __restrict__ d_w0) {
+    float a, int S, int L, const float* __restrict__ win, bf16* __restrict__ wring, int dir,
+    int fwd_slot, int adj_slot, int out_mode, float* __restrict__ part, bf16* __restrict__ dq,
+    bf16* __restrict__ dk, bf16* __restrict__ dv, float* __restrict__ d_w0) {
   constexpr int P = lds_pitch<D>(), PW = P;
   constexpr int NT = D / 16, NP = CH / 16, NTH = NT * 64;
-  constexpr int RING = bwd_ring<D, CH>();
   constexpr long long DD = (long long)D * D;
   __shared__ __align__(16) bf16 sK[CH * P];
   __shared__ __align__(16) bf16 sV[CH * P];  // V in the states pass, E in the gradient pass
@@ -1163,7 +1159,7 @@ __global__ __launch_bounds__(D / 16 * 64) void chunk_bwd_scan_bf16(
   __shared__ __align__(16) bf16 sD[CH * P];
   __shared__ __align__(16) bf16 sDE[CH * P];
   __shared__ __align__(16) bf16 sL[D * PW];
-  __shared__ __align__(16) bf16 ring[RING][D * PW];
+  __shared__ __align__(16) bf16 sW[2][D * PW];
   bf16* const sE = sV;
 
   const int s = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H;
@@ -1192,6 +1188,20 @@ __global__ __launch_bounds__(D / 16 * 64) void chunk_bwd_scan_bf16(
     for (int m = 0; m < NT; ++m)
       for (int j = 0; j < 4; ++j) dst[(16 * m + 4 * g + j) * PW + 16 * w + r] = (bf16)(X[m][j] * scale);
   };
+  // The segment's ring: state pos at ring_seg + pos * D * D, tile (wave w, row tile m) lane by lane.
+  bf16* const ring_seg = wring + ((long long)bh * S + s) * (L + 1) * kRingState<D>;
+  auto ring_put = [&](int pos, const f32x4* X) {
+    for (int m = 0; m < NT; ++m)
+      *reinterpret_cast<bf16x4*>(ring_seg + pos * kRingState<D> + ((w * NT + m) * 64 + l) * 4) = to_bf16x4(X[m]);
+  };
+  auto ring_get = [&](int pos, bf16x4* T) {
+    for (int m = 0; m < NT; ++m)
+      T[m] = *reinterpret_cast<const bf16x4*>(ring_seg + pos * kRingState<D> + ((w * NT + m) * 64 + l) * 4);
+  };
+  auto put_tiles = [&](bf16* dst, const bf16x4* T) {  // row-major, this wave's columns
+    for (int m = 0; m < NT; ++m)
+      for (int j = 0; j < 4; ++j) dst[(16 * m + 4 * g + j) * PW + 16 * w + r] = T[m][j];
+  };
   constexpr int G = stage_groups<CH>();
 
   // ---- states pass: the segment's chunks in scan order from its entry state
@@ -1211,12 +1221,12 @@ __global__ __launch_bounds__(D / 16 * 64) void chunk_bwd_scan_bf16(
         if (pos + G < n) sa.load(kn, vn, nullptr);
       }
       __syncthreads();
-      put_state(ring[pos], W, 1.f);
+      ring_put(pos, W);
       f32x4 E[NP];
       residuals<D, NP, P>(E, W, sK, sV, w, r, g, l);
       update_state<D, NP, P>(W, E, sK, a, l);
     }
-    if (!CAUSAL) put_state(ring[n], W, 1.f);
+    if (!CAUSAL) ring_put(n, W);
   }
 
   // ---- gradient pass: the chunks in reverse scan order
@@ -1230,9 +1240,20 @@ __global__ __launch_bounds__(D / 16 * 64) void chunk_bwd_scan_bf16(
   const bf16* dn = d_o + head0 + chunk_at(n - 1) * cs;
   for (int j = 0; j < G; ++j, kn -= step, vn -= step, qn -= step, dn -= step)
     if (j < n && sb.mine(j)) sb.load(kn, vn, qn, dn);
+  // State tiles: sW[it & 1] holds this chunk's start state; the other buffer, the previous
+  // iteration's start state, is this chunk's end state (read-out after the update). Each wave
+  // fetches its own ring tiles one chunk ahead.
+  bf16x4 wt[NT];
+  if (!CAUSAL) {
+    ring_get(n, wt);
+    put_tiles(sW[1], wt);
+  }
+  ring_get(n - 1, wt);
   for (int it = 0; it < n; ++it, kn -= step, vn -= step, qn -= step, dn -= step) {
     const int pos = n - 1 - it;
     const long long tok0 = head0 + (long long)chunk_at(pos) * cs;
+    bf16* const Wp = sW[it & 1];
+    const bf16* const Wn = CAUSAL ? Wp : sW[(it + 1) & 1];
     // V is staged into the E tile's buffer; each lane reads its own V values from there before
     // overwriting them with E (same rows and columns).
     __syncthreads();
@@ -1240,9 +1261,9 @@ __global__ __launch_bounds__(D / 16 * 64) void chunk_bwd_scan_bf16(
       sb.store(sK, sV, sQ, sD);
       if (it + G < n) sb.load(kn, vn, qn, dn);
     }
+    put_tiles(Wp, wt);
+    if (pos > 0) ring_get(pos - 1, wt);
     __syncthreads();
-    const bf16* Wp = ring[pos];
-    const bf16* Wn = ring[CAUSAL ? pos : pos + 1];
 
     // E^T and dE^T for this wave's 16 features: lane (r, g) holds features 16w + 4g + j of token
     // 16p + r.
@@ -1476,31 +1497,19 @@ struct BwdPlan {
   int S, L;
 };
 
-template <int D, int CH>
-BwdPlan bwd_plan_dc(int N) {
+// Segments as for the forward scans: the grid resident in one round (two workgroups of the segment
+// scan per CU: its LDS and registers allow two at d = 64), at least 4 chunks per segment.
+constexpr int kBwdGroupsPerCU = 2;
+
+BwdPlan bwd_plan(int B, int H, int N, int CH) {
   const int C = N / CH;
-  const int lmax = bwd_ring<D, CH>() - 1;
-  int S = (C + lmax - 1) / lmax;
+  const int BH = B * H;
+  int S = kPlanCUs * kBwdGroupsPerCU / BH;
+  if (S > C / 4) S = C / 4;
+  if (S < 1) S = 1;
   const int L = (C + S - 1) / S;
   S = (C + L - 1) / L;
   return BwdPlan{S, L};
-}
-
-template <int D>
-BwdPlan bwd_plan_d(int N, int CH) {
-  switch (CH) {
-    case 16: return bwd_plan_dc<D, 16>(N);
-    case 32: return bwd_plan_dc<D, 32>(N);
-    default: return bwd_plan_dc<D, 64>(N);
-  }
-}
-
-BwdPlan bwd_plan(int N, int D, int CH) {
-  switch (D) {
-    case 16: return bwd_plan_d<16>(N, CH);
-    case 32: return bwd_plan_d<32>(N, CH);
-    default: return bwd_plan_d<64>(N, CH);
-  }
 }
 
 template <int D, int CH>
@@ -1508,12 +1517,13 @@ hipError_t launch_bwd_bf16(bool bidir, int B, int H, int N, float a, const void*
                            const void* v, const float* w0, long long w0s, const void* d_o,
                            void* dq, void* dk, void* dv, float* d_w0, void* ws, hipStream_t st) {
   const int BH = B * H;
-  const BwdPlan pl = bwd_plan(N, D, CH);
+  const BwdPlan pl = bwd_plan(B, H, N, CH);
   const int nrec = bidir ? 4 : 2;
   const long long DD = (long long)D * D;
   float* comp = static_cast<float*>(ws);
   float* win = comp + (pl.S > 1 ? (long long)BH * pl.S * nrec * kMapFloats<D> : 0);
-  float* part = win + (pl.S > 1 ? (long long)nrec * BH * pl.S * DD : 0);
+  bf16* wring = reinterpret_cast<bf16*>(win + (pl.S > 1 ? (long long)nrec * BH * pl.S * DD : 0));
+  float* part = reinterpret_cast<float*>(wring + (long long)BH * pl.S * (pl.L + 1) * kRingState<D>);
   const bf16 *Q = (const bf16*)q, *K = (const bf16*)k, *V = (const bf16*)v, *DO = (const bf16*)d_o;
   bf16 *GQ = (bf16*)dq, *GK = (bf16*)dk, *GV = (bf16*)dv;
   const dim3 grid(pl.S, BH), block(D / 16 * 64);
@@ -1525,7 +1535,7 @@ hipError_t launch_bwd_bf16(bool bidir, int B, int H, int N, float a, const void*
                          pl.S, comp, win);
     }
     hipLaunchKernelGGL((chunk_bwd_scan_bf16<D, CH, true>), grid, block, 0, st, Q, K, V, DO, w0, w0s,
-                       H, N, a, pl.S, pl.L, win, 0, 0, 1, (int)kOutBf16, part, GQ, GK, GV, d_w0);
+                       H, N, a, pl.S, pl.L, win, wring, 0, 0, 1, (int)kOutBf16, part, GQ, GK, GV, d_w0);
     return hipGetLastError();
   }
   if (pl.S > 1) {
@@ -1536,9 +1546,9 @@ hipError_t launch_bwd_bf16(bool bidir, int B, int H, int N, float a, const void*
   }
   // reversed scan: forward states in slot 1, its adjoints in slot 2; then the forward scan
   hipLaunchKernelGGL((chunk_bwd_scan_bf16<D, CH, false>), grid, block, 0, st, Q, K, V, DO, w0, w0s,
-                     H, N, a, pl.S, pl.L, win, 1, 1, 2, (int)kOutPartial, part, GQ, GK, GV, d_w0);
+                     H, N, a, pl.S, pl.L, win, wring, 1, 1, 2, (int)kOutPartial, part, GQ, GK, GV, d_w0);
   hipLaunchKernelGGL((chunk_bwd_scan_bf16<D, CH, false>), grid, block, 0, st, Q, K, V, DO, w0, w0s,
-                     H, N, a, pl.S, pl.L, win, 0, 0, 3, (int)kOutAddPartial, part, GQ, GK, GV, d_w0);
+                     H, N, a, pl.S, pl.L, win, wring, 0, 0, 3, (int)kOutAddPartial, part, GQ, GK, GV, d_w0);
   return hipGetLastError();
 }
 
@@ -1619,11 +1629,12 @@ size_t chunked_bwd_workspace_bytes(bool bidir, bool bf16_io, int B, int H, int N
   const size_t BH = (size_t)B * H, DD = (size_t)D * D, C = (size_t)N / (size_t)chunk;
   // fp32: the scan's C + 1 states per (b, h)
   if (!bf16_io) return BH * (C + 1) * DD * sizeof(float);
-  const BwdPlan pl = bwd_plan(N, D, chunk);
+  const BwdPlan pl = bwd_plan(B, H, N, chunk);
   const size_t nrec = bidir ? 4 : 2;
   size_t bytes = 0;
   if (pl.S > 1)  // map records (-Dev bf16 + offset fp32) and the folded states, per slot
     bytes += BH * pl.S * nrec * (DD / 2 + DD) * sizeof(float) + nrec * BH * pl.S * DD * sizeof(float);
+  bytes += BH * pl.S * (pl.L + 1) * DD * 2;  // the segments' forward states, bf16
   if (bidir)  // the reversed scan's fp32 partial dq, dk, dv
     bytes += 3 * (size_t)B * N * H * D * sizeof(float);
   return bytes;

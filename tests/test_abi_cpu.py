@@ -98,11 +98,13 @@ def test_chunked_backward_validation_rejects_before_launch(fn):
     assert T.ttt_workspace_size(op, T.TTT_F32, 2, 3, 256, 32, 0, 16) == 2 * 3 * 17 * 32 * 32 * 4
 
 
-def test_chunked_backward_single_segment_needs_no_workspace():
-    """A causal sequence that fits one segment needs no workspace (the bidirectional one always holds
-    one scan's fp32 partial gradients)."""
-    assert T.ttt_workspace_size(T.TTT_OP_CAUSAL_BWD, T.TTT_BF16, 1, 1, 32, 64, 0, 16) == 0
-    assert T.ttt_workspace_size(T.TTT_OP_BIDIR_BWD, T.TTT_BF16, 1, 1, 32, 64, 0, 16) == 3 * 32 * 64 * 4
+def test_chunked_backward_workspace_holds_the_segment_states():
+    """The backward always keeps its segments' forward states (bf16, d x d each) in the workspace; a
+    single-segment causal sequence needs only those (C + 1 states), the bidirectional one also
+    holds one scan's fp32 partial gradients."""
+    ring = (2 + 1) * 64 * 64 * 2
+    assert T.ttt_workspace_size(T.TTT_OP_CAUSAL_BWD, T.TTT_BF16, 1, 1, 32, 64, 0, 16) == ring
+    assert T.ttt_workspace_size(T.TTT_OP_BIDIR_BWD, T.TTT_BF16, 1, 1, 32, 64, 0, 16) == ring + 3 * 32 * 64 * 4
 
 
 def test_fullbatch_epochs_validation():
