@@ -589,28 +589,6 @@ hipError_t launch_f32(int B, int H, int N, int epochs, float eta, const void* q,
 //   fbb_tokens: per 16-token tile, dQ^T = A_q dO^T, dV^T = A_v K^T, dK^T = A_k1 K^T + A_k2 V^T.
 constexpr int kBwdMats = 4;
 
-// Element (i, j) of the summed K^T K (which = 0) or K^T V (which = 1) of head hl of a group, from
-// the bf16 path's split records (per task (head, row block m): tiles (c, m) of K^T K, then
-// (m, n) of K^T V, in accumulator lane order).
-template <int D, int HG>
-__device__ __forceinline__ float record_sum_bf16(const float* rec, int S, int hl, int which, int i,
-                                                 int j) {
-  constexpr int NT = D / 16;
-  int task, t;
-  if (which == 0) {  // tile (c = i / 16, m = j / 16): rows of K^T K 16c + 4g + jj, column 16m + r
-    task = hl * NT + j / 16;
-    t = i / 16;
-  } else {           // tile (m = i / 16, n = j / 16)
-    task = hl * NT + i / 16;
-    t = NT + j / 16;
-  }
-  const int r = j % 16, g = (i % 16) / 4, jj = i % 4;
-  const long long off = (long long)task * (2 * NT * 256) + (t * 64 + r + 16 * g) * 4 + jj;
-  float acc = 0.f;
-  for (int sp = 0; sp < S; ++sp) acc += rec[(long long)sp * (2 * HG * D * D) + off];
-  return acc;
-}
-
 // One workgroup per (b, h). rec_kv / rec_qd: the group's split records (bf16 path) or the
 // (b, h)'s (fp32 path: per split K^T K then K^T V, row-major). ops: the four operand matrices.
 template <int D, int HG, bool BF16>
@@ -624,29 +602,61 @@ __global__ __launch_bounds__(kThreads) void fbb_finish(const float* __restrict__
   const int bh = blockIdx.x, b = bh / H, h = bh % H;
   const long long DD = (long long)D * D;
   const float* W0 = w0 + b * w0_bstride + h * DD;
-  for (int e = threadIdx.x; e < D * D; e += kThreads) {
-    const int i = e / D, j = e % D;
-    float kk, kv, gq;
-    if constexpr (BF16) {
-      const int grp = b * (H / HG) + h / HG, hl = h % HG;
-      const float* rk = rec_kv + (long long)grp * S * (2 * HG * DD);
-      const float* rq = rec_qd + (long long)grp * S * (2 * HG * DD);
-      kk = record_sum_bf16<D, HG>(rk, S, hl, 0, i, j);
-      kv = record_sum_bf16<D, HG>(rk, S, hl, 1, i, j);
-      gq = record_sum_bf16<D, HG>(rq, S, hl, 1, i, j);
-    } else {
-      kk = kv = gq = 0.f;
+  if constexpr (BF16) {
+    // The head's part of a split record is 2 d^2 contiguous floats (its tasks' tiles), laid out
+    // alike in every split: sum it in split order over 16-byte pieces (the loads of 8 splits in
+    // flight at once), then scatter each element to its (row, column).
+    constexpr int NT = D / 16, TASK = 2 * NT * 256, U = 8;
+    const int grp = b * (H / HG) + h / HG, hl = h % HG;
+    const long long rstride = 2LL * HG * DD;  // floats per split record of the group
+    const float* rk = rec_kv + (long long)grp * S * rstride + (long long)hl * 2 * DD;
+    const float* rq = rec_qd + (long long)grp * S * rstride + (long long)hl * 2 * DD;
+    for (int o4 = threadIdx.x; o4 < 2 * DD / 4; o4 += kThreads) {
+      f32x4 ak = zero4(), aq = zero4();
+      for (int sp0 = 0; sp0 < S; sp0 += U) {
+        f32x4 bk[U], bq[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (sp0 + u < S) {
+            bk[u] = *reinterpret_cast<const f32x4*>(rk + (sp0 + u) * rstride + 4 * o4);
+            bq[u] = *reinterpret_cast<const f32x4*>(rq + (sp0 + u) * rstride + 4 * o4);
+          }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (sp0 + u < S) {
+            ak += bk[u];
+            aq += bq[u];
+          }
+      }
+      // offset 4 o4 + jj: task tl, tile tt, lane r + 16 g, element jj (the record layout)
+      const int tl = (4 * o4) / TASK, rem = (4 * o4) % TASK, tt = rem / 256, lane = (rem % 256) / 4;
+      const int r = lane % 16, g = lane / 16;
+      for (int jj = 0; jj < 4; ++jj) {
+        if (tt < NT) {  // K^T K tile (c = tt, m = tl)
+          sKK[16 * tt + 4 * g + jj][16 * tl + r] = ak[jj];
+        } else {        // K^T V and Q^T dO tiles (m = tl, n = tt - NT)
+          sKV[16 * tl + 4 * g + jj][16 * (tt - NT) + r] = ak[jj];
+          sG[16 * tl + 4 * g + jj][16 * (tt - NT) + r] = aq[jj];
+        }
+      }
+    }
+    for (int e = threadIdx.x; e < D * D; e += kThreads) sW0[e / D][e % D] = W0[e];
+  }
+  if constexpr (!BF16) {  // per (b, h, split): K^T K then K^T V (or Q^T Q then Q^T dO), row-major
+    for (int e = threadIdx.x; e < D * D; e += kThreads) {
+      const int i = e / D, j = e % D;
+      float kk = 0.f, kv = 0.f, gq = 0.f;
       for (int sp = 0; sp < S; ++sp) {
         const long long base = ((long long)bh * S + sp) * 2 * DD;
         kk += rec_kv[base + e];
         kv += rec_kv[base + DD + e];
         gq += rec_qd[base + DD + e];
       }
+      sKK[i][j] = kk;
+      sKV[i][j] = kv;
+      sG[i][j] = gq;
+      sW0[i][j] = W0[e];
     }
-    sKK[i][j] = kk;
-    sKV[i][j] = kv;
-    sG[i][j] = gq;
-    sW0[i][j] = W0[e];
   }
   __syncthreads();
   for (int e = threadIdx.x; e < D * D; e += kThreads) {
