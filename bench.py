@@ -263,7 +263,9 @@ def extra_legs(T, torch, inputs, dev, time_rotated) -> dict:
         (C = C_out = 64), bf16;
       * causal_backward_16k, bidir_backward_vittt_1280: the backward passes (dQ, dK, dV, dW0) of the
         causal TTT-Linear layer (2 x 16384 x 12 x 64, b = 16) and of the Vision-TTT bidirectional
-        scan (8 x 6400 x 3 x 64, b = 64), bf16."""
+        scan (8 x 6400 x 3 x 64, b = 64), bf16;
+      * design-space variants: 4 full-batch epochs at the H-ViT^3-T stage-1 shape, the Vision-TTT scan
+        with b = 16, and a 4x wider inner MLP (Dh = 1024) at a reduced shape."""
     name = "vittt_bidir_1280"
     if name not in inputs:
         return {}
@@ -371,6 +373,59 @@ def extra_legs(T, torch, inputs, dev, time_rotated) -> dict:
         out[leg] = {"ms": round(cold, 5), "ms_warm": round(warm, 5), "tokens_per_s": wl.tokens / s,
                     "alg_bytes": nbytes, "alg_GBs": nbytes / s / 1e9, "hbm_frac": nbytes / s / 1e9 / PEAK_HBM_GBS,
                     "timing": f"cold: inputs rotated over {nsets} copies (> 1 GiB)"}
+    # design-space variants (ViT^3 review, design-space study; Vision-TTT's b = 16)
+    if fb in inputs:  # 4 full-batch epochs at the H-ViT^3-T stage-1 shape
+        fw = inputs[fb].wl
+        wse = torch.empty(max(T.ttt_workspace_size(T.TTT_OP_FULLBATCH, T.TTT_BF16, fw.B, fw.H, fw.N, fw.D), 1),
+                          dtype=torch.uint8, device="cuda")
+
+        def ep4(d, fw=fw, wse=wse):
+            return lambda: T.ttt_forward_fullbatch_epochs(d["q"], d["k"], d["v"], d["w0"], 4, fw.eta, o=d["o"],
+                                                          workspace=wse)
+
+        cold, warm, nsets = time_rotated(ep4, dev[fb], fw.io_bytes)
+        sec = cold / 1000.0
+        out["fullbatch_4_epochs_hvit3t_stage1"] = {
+            "ms": round(cold, 5), "ms_warm": round(warm, 5), "tokens_per_s": fw.tokens / sec,
+            "alg_bytes": fw.io_bytes, "alg_GBs": fw.io_bytes / sec / 1e9,
+            "hbm_frac": fw.io_bytes / sec / 1e9 / PEAK_HBM_GBS,
+            "timing": f"cold: inputs rotated over {nsets} copies (> 1 GiB); 4 epochs over one pass of K and V"}
+    # the Vision-TTT scan with b = 16 (its summary's mini-batch size), same tensors as the b = 64 layer
+    ws16 = torch.empty(max(T.ttt_workspace_size(T.TTT_OP_BIDIR, T.TTT_BF16, wl.B, wl.H, wl.N, wl.D, 0, 16), 1),
+                       dtype=torch.uint8, device="cuda")
+
+    def bidir16(d):
+        return lambda: T.ttt_forward_chunked_bidir(d["q"], d["k"], d["v"], d["w0"], 16, wl.eta, o=d["o"],
+                                                   workspace=ws16)
+
+    cold, warm, nsets = time_rotated(bidir16, dev[name], wl.io_bytes)
+    sec = cold / 1000.0
+    out["vittt_bidir_1280_b16"] = {
+        "ms": round(cold, 5), "ms_warm": round(warm, 5), "tokens_per_s": wl.tokens / sec,
+        "alg_bytes": wl.io_bytes, "alg_GBs": wl.io_bytes / sec / 1e9, "hbm_frac": wl.io_bytes / sec / 1e9 / PEAK_HBM_GBS,
+        "timing": f"cold: inputs rotated over {nsets} copies (> 1 GiB); mini-batches of 16 tokens"}
+    # a wider inner MLP (Dh = 1024, 4 x the suite's) on the plain fp32 path, at a reduced shape
+    from test_sequence_layers_amd import synth
+
+    mw = synth.WORKLOADS["ttt_mlp_causal_8k"].with_(B=1, N=1024, H=12, Dh=1024, seed=4545)
+    xm = synth.make_inputs(mw)
+    dm = to_device(xm, torch)
+    wsm = torch.empty(T.ttt_workspace_size(T.TTT_OP_MLP, T.TTT_BF16, mw.B, mw.H, mw.N, mw.D, mw.Dh, mw.chunk),
+                      dtype=torch.uint8, device="cuda")
+
+    def mlpw(d):
+        return lambda: T.ttt_mlp_forward(d["q"], d["k"], d["v"], d["w1"], d["w2"], mw.chunk, mw.eta, o=d["o"],
+                                         workspace=wsm)
+
+    # compute-bound (6 MB of I/O against 12 GFLOP): two input sets alternate instead of a 1 GiB rotation
+    cold, warm, nsets = time_rotated(mlpw, dm, ROTATE_BYTES)
+    sec = cold / 1000.0
+    flops = alg_flops(mw)
+    out["ttt_mlp_wide_dh1024_1x1024x12"] = {
+        "ms": round(cold, 5), "ms_warm": round(warm, 5), "tokens_per_s": mw.tokens / sec,
+        "alg_TFLOPs": flops / sec / 1e12, "mfma_frac": flops / sec / 1e12 / PEAK_BF16_TFLOPS,
+        "timing": f"{nsets} input sets alternating; B = 1, N = 1024, 12 heads of 64, Dh = 1024, b = 16 "
+                  "(plain fp32 arithmetic: the matrix-core kernel covers Dh = 256)"}
     return out
 
 

@@ -525,11 +525,16 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
 //   Z1 = K W1, X2 = GELU(Z1), E = X2 W2 - V, D1 = (E W2^T) * GELU'(Z1)
 //   Z1q = Q W1 - a tril(Q K^T) D1, X2q = GELU(Z1q), O = X2q W2 - a tril(X2q X2^T) E
 //   W1 -= a K^T D1, W2 -= a X2^T E
-// (tril keeps j <= i, so token i sees the gradients of tokens j <= i). The state and the
-// [b, Dh] intermediates live in the workspace (per chain 2 D Dh + 4 b Dh floats), the chunk's
-// K, V, Q, E and the two masked b x b products in LDS.
+// (tril keeps j <= i, so token i sees the gradients of tokens j <= i). The state lives in the
+// workspace; so do the [Dh, b] intermediates, stored hidden-unit-major so that a thread owning a
+// hidden unit reads and writes its b values contiguously. Work is laid out so that the state
+// streams once per pass: a thread owns hidden unit j for the passes over W1's column j and W2's row
+// j (Z1 and Q W1; D1, X2q and the W1 update; the W2 update), and the contractions over the hidden
+// units (E, O) give each thread an output feature and a share of the hidden units, the partial sums
+// reduced through LDS in a fixed order. The chunk's K, V, Q, E and the masked b x b products are in
+// LDS. Per chain the workspace holds 2 D Dh + 4 b Dh floats.
 constexpr int kGenThreads = 256;
-constexpr int kGenMaxD = 64, kGenMaxCh = 64;
+constexpr int kGenTB = 16;  // tokens per block of the E and O partial sums
 
 __device__ __forceinline__ float gelu_f32(float x) { return x * cdf_lib(x); }
 __device__ __forceinline__ float gelu_prime_f32(float x) {
@@ -540,23 +545,24 @@ __device__ __forceinline__ float load_io(const T* p) { return (float)*p; }
 template <class T>
 __device__ __forceinline__ void store_io(T* p, float v) { *p = (T)v; }
 
-template <class T>
+template <class T, int D, int CH>
 __global__ __launch_bounds__(kGenThreads) void mlp_fwd_generic(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const float* __restrict__ w1, const float* __restrict__ w2, long long wbs, int H, int N, int D,
-    int Dh, int CH, float a, T* __restrict__ o, float* __restrict__ w1_out,
-    float* __restrict__ w2_out, float* __restrict__ ws) {
-  __shared__ float sK[kGenMaxCh][kGenMaxD + 1], sV[kGenMaxCh][kGenMaxD + 1], sQ[kGenMaxCh][kGenMaxD + 1];
-  __shared__ float sE[kGenMaxCh][kGenMaxD + 1];
-  __shared__ float sM[kGenMaxCh][kGenMaxCh + 1], sN2[kGenMaxCh][kGenMaxCh + 1];
+    const float* __restrict__ w1, const float* __restrict__ w2, long long wbs, int H, int N, int Dh,
+    float a, T* __restrict__ o, float* __restrict__ w1_out, float* __restrict__ w2_out,
+    float* __restrict__ ws) {
+  constexpr int DP = D + 1, G = kGenThreads / D;  // G hidden-unit groups of the E / O partial sums
+  __shared__ float sK[CH * DP], sV[CH * DP], sQ[CH * DP], sE[CH * DP];
+  __shared__ float sM[CH * (CH + 1)], sN2[CH * (CH + 1)];
+  __shared__ float sPart[kGenThreads * (kGenTB + 1)];
   const int bh = blockIdx.x, b = bh / H, h = bh % H, tid = threadIdx.x;
   const long long DDh = (long long)D * Dh, BDh = (long long)CH * Dh;
-  float* W1 = ws + (long long)bh * (2 * DDh + 4 * BDh);
-  float* W2 = W1 + DDh;
-  float* Z1 = W2 + DDh;  // then Z1q / X2q
-  float* X2 = Z1 + BDh;
-  float* GP = X2 + BDh;
-  float* D1 = GP + BDh;
+  float* W1 = ws + (long long)bh * (2 * DDh + 4 * BDh);  // [D][Dh]
+  float* W2 = W1 + DDh;                                  // [Dh][D]
+  float* X2T = W2 + DDh;                                 // [Dh][CH]: GELU(Z1)
+  float* GPT = X2T + BDh;                                // [Dh][CH]: GELU'(Z1)
+  float* XQT = GPT + BDh;                                // [Dh][CH]: Q W1, then X2q
+  float* D1T = XQT + BDh;                                // [Dh][CH]: D1
   const float* W1g = w1 + b * wbs + (long long)h * DDh;
   const float* W2g = w2 + b * wbs + (long long)h * DDh;
   for (long long e = tid; e < DDh; e += kGenThreads) {
@@ -565,87 +571,140 @@ __global__ __launch_bounds__(kGenThreads) void mlp_fwd_generic(
   }
   const long long ts = (long long)H * D;
   const long long head0 = (long long)b * N * ts + (long long)h * D;
+  const int f = tid % D, jg = tid / D;  // output feature and hidden-unit group of the partial sums
+
+  // P[t][f] = sum_j XT[j][tb + t] W2[j][f] over the chunk's tokens tb .. tb + 15, reduced over the
+  // groups in order; calls out(t, f, value) for each.
+  auto hidden_contraction = [&](const float* XT, auto out) {
+    for (int tb = 0; tb < CH; tb += kGenTB) {
+      float acc[kGenTB];
+#pragma unroll
+      for (int t = 0; t < kGenTB; ++t) acc[t] = 0.f;
+      for (int j = jg; j < Dh; j += G) {
+        const float w = W2[(long long)j * D + f];
+        const f32x4* x = reinterpret_cast<const f32x4*>(XT + (long long)j * CH + tb);
+#pragma unroll
+        for (int t4 = 0; t4 < kGenTB / 4; ++t4) {
+          const f32x4 xv = x[t4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) acc[4 * t4 + u] = fmaf(xv[u], w, acc[4 * t4 + u]);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < kGenTB; ++t) sPart[tid * (kGenTB + 1) + t] = acc[t];
+      __syncthreads();
+      for (int e = tid; e < kGenTB * D; e += kGenThreads) {
+        const int t = e / D, ff = e % D;
+        float sum = 0.f;
+        for (int g = 0; g < G; ++g) sum += sPart[(g * D + ff) * (kGenTB + 1) + t];
+        out(tb + t, ff, sum);
+      }
+      __syncthreads();
+    }
+  };
+
   __syncthreads();
   for (int c0 = 0; c0 < N; c0 += CH) {
     for (int e = tid; e < CH * D; e += kGenThreads) {
-      const int t = e / D, f = e % D;
-      const long long off = head0 + (long long)(c0 + t) * ts + f;
-      sK[t][f] = load_io(k + off);
-      sV[t][f] = load_io(v + off);
-      sQ[t][f] = load_io(q + off);
+      const int t = e / D, ff = e % D;
+      const long long off = head0 + (long long)(c0 + t) * ts + ff;
+      sK[t * DP + ff] = load_io(k + off);
+      sV[t * DP + ff] = load_io(v + off);
+      sQ[t * DP + ff] = load_io(q + off);
     }
     __syncthreads();
-    // Z1 = K W1, X2 = GELU(Z1), GP = GELU'(Z1); M = tril(Q K^T)
-    for (long long e = tid; e < BDh; e += kGenThreads) {
-      const int t = (int)(e / Dh), j = (int)(e % Dh);
-      float z = 0.f;
-      for (int f = 0; f < D; ++f) z = fmaf(sK[t][f], W1[(long long)f * Dh + j], z);
-      X2[e] = gelu_f32(z);
-      GP[e] = gelu_prime_f32(z);
+    // Z1 = K W1 (X2, GELU'), Q W1, column by column of W1; M = tril(Q K^T)
+    for (int j = tid; j < Dh; j += kGenThreads) {
+      float wc[D];
+#pragma unroll
+      for (int ff = 0; ff < D; ++ff) wc[ff] = W1[(long long)ff * Dh + j];
+#pragma unroll 1
+      for (int t = 0; t < CH; ++t) {
+        float z = 0.f, zq = 0.f;
+#pragma unroll
+        for (int ff = 0; ff < D; ++ff) {
+          z = fmaf(sK[t * DP + ff], wc[ff], z);
+          zq = fmaf(sQ[t * DP + ff], wc[ff], zq);
+        }
+        X2T[(long long)j * CH + t] = gelu_f32(z);
+        GPT[(long long)j * CH + t] = gelu_prime_f32(z);
+        XQT[(long long)j * CH + t] = zq;
+      }
     }
     for (int e = tid; e < CH * CH; e += kGenThreads) {
-      const int i = e / CH, j = e % CH;
+      const int i = e / CH, u = e % CH;
       float m = 0.f;
-      if (j <= i)
-        for (int f = 0; f < D; ++f) m = fmaf(sQ[i][f], sK[j][f], m);
-      sM[i][j] = m;
+      if (u <= i)
+        for (int ff = 0; ff < D; ++ff) m = fmaf(sQ[i * DP + ff], sK[u * DP + ff], m);
+      sM[i * (CH + 1) + u] = m;
     }
     __syncthreads();
     // E = X2 W2 - V
-    for (int e = tid; e < CH * D; e += kGenThreads) {
-      const int t = e / D, f = e % D;
-      float z = -sV[t][f];
-      for (int j = 0; j < Dh; ++j) z = fmaf(X2[(long long)t * Dh + j], W2[(long long)j * D + f], z);
-      sE[t][f] = z;
-    }
-    __syncthreads();
-    // D1 = (E W2^T) * GP
-    for (long long e = tid; e < BDh; e += kGenThreads) {
-      const int t = (int)(e / Dh), j = (int)(e % Dh);
-      float g = 0.f;
-      for (int f = 0; f < D; ++f) g = fmaf(sE[t][f], W2[(long long)j * D + f], g);
-      D1[e] = g * GP[e];
-    }
-    __syncthreads();
-    // Z1q = Q W1 - a M D1, X2q = GELU(Z1q) (into Z1)
-    for (long long e = tid; e < BDh; e += kGenThreads) {
-      const int t = (int)(e / Dh), j = (int)(e % Dh);
-      float z = 0.f, corr = 0.f;
-      for (int f = 0; f < D; ++f) z = fmaf(sQ[t][f], W1[(long long)f * Dh + j], z);
-      for (int u = 0; u <= t; ++u) corr = fmaf(sM[t][u], D1[(long long)u * Dh + j], corr);
-      Z1[e] = gelu_f32(fmaf(-a, corr, z));
+    hidden_contraction(X2T, [&](int t, int ff, float sum) { sE[t * DP + ff] = sum - sV[t * DP + ff]; });
+    // per hidden unit j: D1 = (E W2^T) * GELU'(Z1); X2q = GELU(Q W1 - a M D1); W1[:, j] -= a K^T D1
+    for (int j = tid; j < Dh; j += kGenThreads) {
+      float* d1 = D1T + (long long)j * CH;
+      float* xq = XQT + (long long)j * CH;
+      {
+        float wr[D];
+#pragma unroll
+        for (int ff = 0; ff < D; ++ff) wr[ff] = W2[(long long)j * D + ff];
+#pragma unroll 1
+        for (int t = 0; t < CH; ++t) {
+          float g = 0.f;
+#pragma unroll
+          for (int ff = 0; ff < D; ++ff) g = fmaf(sE[t * DP + ff], wr[ff], g);
+          d1[t] = g * GPT[(long long)j * CH + t];
+        }
+      }
+#pragma unroll 1
+      for (int t = 0; t < CH; ++t) {
+        float corr = 0.f;
+        for (int u = 0; u <= t; ++u) corr = fmaf(sM[t * (CH + 1) + u], d1[u], corr);
+        xq[t] = gelu_f32(fmaf(-a, corr, xq[t]));
+      }
+      float gk[D];
+#pragma unroll
+      for (int ff = 0; ff < D; ++ff) gk[ff] = 0.f;
+#pragma unroll 1
+      for (int t = 0; t < CH; ++t) {
+        const float dt = d1[t];
+#pragma unroll
+        for (int ff = 0; ff < D; ++ff) gk[ff] = fmaf(sK[t * DP + ff], dt, gk[ff]);
+      }
+#pragma unroll
+      for (int ff = 0; ff < D; ++ff) W1[(long long)ff * Dh + j] = fmaf(-a, gk[ff], W1[(long long)ff * Dh + j]);
     }
     __syncthreads();
     // N2 = tril(X2q X2^T)
     for (int e = tid; e < CH * CH; e += kGenThreads) {
-      const int i = e / CH, j = e % CH;
+      const int i = e / CH, u = e % CH;
       float m = 0.f;
-      if (j <= i)
-        for (int u = 0; u < Dh; ++u) m = fmaf(Z1[(long long)i * Dh + u], X2[(long long)j * Dh + u], m);
-      sN2[i][j] = m;
+      if (u <= i)
+        for (int j = 0; j < Dh; ++j) m = fmaf(XQT[(long long)j * CH + i], X2T[(long long)j * CH + u], m);
+      sN2[i * (CH + 1) + u] = m;
     }
     __syncthreads();
     // O = X2q W2 - a N2 E
-    for (int e = tid; e < CH * D; e += kGenThreads) {
-      const int t = e / D, f = e % D;
-      float z = 0.f, corr = 0.f;
-      for (int j = 0; j < Dh; ++j) z = fmaf(Z1[(long long)t * Dh + j], W2[(long long)j * D + f], z);
-      for (int u = 0; u <= t; ++u) corr = fmaf(sN2[t][u], sE[u][f], corr);
-      store_io(o + head0 + (long long)(c0 + t) * ts + f, fmaf(-a, corr, z));
-    }
-    // W1 -= a K^T D1, W2 -= a X2^T E (the read-out above used the start state)
-    __syncthreads();
-    for (long long e = tid; e < DDh; e += kGenThreads) {
-      const int f = (int)(e / Dh), j = (int)(e % Dh);
-      float g = 0.f;
-      for (int t = 0; t < CH; ++t) g = fmaf(sK[t][f], D1[(long long)t * Dh + j], g);
-      W1[e] = fmaf(-a, g, W1[e]);
-    }
-    for (long long e = tid; e < DDh; e += kGenThreads) {
-      const int j = (int)(e / D), f = (int)(e % D);
-      float g = 0.f;
-      for (int t = 0; t < CH; ++t) g = fmaf(X2[(long long)t * Dh + j], sE[t][f], g);
-      W2[e] = fmaf(-a, g, W2[e]);
+    T* oc = o + head0 + (long long)c0 * ts;
+    hidden_contraction(XQT, [&](int t, int ff, float sum) {
+      float corr = 0.f;
+      for (int u = 0; u <= t; ++u) corr = fmaf(sN2[t * (CH + 1) + u], sE[u * DP + ff], corr);
+      store_io(oc + (long long)t * ts + ff, fmaf(-a, corr, sum));
+    });
+    // W2[j, :] -= a X2[:, j]^T E (every read of the start state W2 is done: the last barrier above)
+    for (int j = tid; j < Dh; j += kGenThreads) {
+      float g[D];
+#pragma unroll
+      for (int ff = 0; ff < D; ++ff) g[ff] = 0.f;
+#pragma unroll 1
+      for (int t = 0; t < CH; ++t) {
+        const float xt = X2T[(long long)j * CH + t];
+#pragma unroll
+        for (int ff = 0; ff < D; ++ff) g[ff] = fmaf(xt, sE[t * DP + ff], g[ff]);
+      }
+#pragma unroll
+      for (int ff = 0; ff < D; ++ff) W2[(long long)j * D + ff] = fmaf(-a, g[ff], W2[(long long)j * D + ff]);
     }
     __syncthreads();
   }
@@ -653,6 +712,37 @@ __global__ __launch_bounds__(kGenThreads) void mlp_fwd_generic(
     for (long long e = tid; e < DDh; e += kGenThreads) w1_out[(long long)bh * DDh + e] = W1[e];
   if (w2_out)
     for (long long e = tid; e < DDh; e += kGenThreads) w2_out[(long long)bh * DDh + e] = W2[e];
+}
+
+template <class T, int D>
+void launch_generic_d(int BH, int H, int N, int Dh, int CH, float a, const void* q, const void* k,
+                      const void* v, const float* w1, const float* w2, long long wbs, void* o,
+                      float* w1_out, float* w2_out, float* ws, hipStream_t st) {
+  const T *Q = (const T*)q, *K = (const T*)k, *V = (const T*)v;
+  switch (CH) {
+    case 16:
+      hipLaunchKernelGGL((mlp_fwd_generic<T, D, 16>), dim3(BH), dim3(kGenThreads), 0, st, Q, K, V, w1, w2, wbs, H,
+                         N, Dh, a, (T*)o, w1_out, w2_out, ws);
+      break;
+    case 32:
+      hipLaunchKernelGGL((mlp_fwd_generic<T, D, 32>), dim3(BH), dim3(kGenThreads), 0, st, Q, K, V, w1, w2, wbs, H,
+                         N, Dh, a, (T*)o, w1_out, w2_out, ws);
+      break;
+    default:
+      hipLaunchKernelGGL((mlp_fwd_generic<T, D, 64>), dim3(BH), dim3(kGenThreads), 0, st, Q, K, V, w1, w2, wbs, H,
+                         N, Dh, a, (T*)o, w1_out, w2_out, ws);
+  }
+}
+
+template <class T>
+void launch_generic(int BH, int H, int N, int D, int Dh, int CH, float a, const void* q, const void* k,
+                    const void* v, const float* w1, const float* w2, long long wbs, void* o, float* w1_out,
+                    float* w2_out, float* ws, hipStream_t st) {
+  switch (D) {
+    case 16: launch_generic_d<T, 16>(BH, H, N, Dh, CH, a, q, k, v, w1, w2, wbs, o, w1_out, w2_out, ws, st); break;
+    case 32: launch_generic_d<T, 32>(BH, H, N, Dh, CH, a, q, k, v, w1, w2, wbs, o, w1_out, w2_out, ws, st); break;
+    default: launch_generic_d<T, 64>(BH, H, N, Dh, CH, a, q, k, v, w1, w2, wbs, o, w1_out, w2_out, ws, st);
+  }
 }
 
 }  // namespace
@@ -681,13 +771,11 @@ hipError_t mlp_launch(bool bf16_io, int B, int H, int N, int D, int Dh, int chun
   if (!mlp_fast_path(bf16_io, D, Dh, chunk)) {
     if (!mlp_supported(D, Dh, chunk)) return hipErrorInvalidValue;
     if (bf16_io)
-      hipLaunchKernelGGL(mlp_fwd_generic<bf16>, dim3(B * H), dim3(kGenThreads), 0, st, (const bf16*)q,
-                         (const bf16*)k, (const bf16*)v, w1, w2, wbs, H, N, D, Dh, chunk, a, (bf16*)o,
-                         w1_out, w2_out, static_cast<float*>(ws));
+      launch_generic<bf16>(B * H, H, N, D, Dh, chunk, a, q, k, v, w1, w2, wbs, o, w1_out, w2_out,
+                           static_cast<float*>(ws), st);
     else
-      hipLaunchKernelGGL(mlp_fwd_generic<float>, dim3(B * H), dim3(kGenThreads), 0, st, (const float*)q,
-                         (const float*)k, (const float*)v, w1, w2, wbs, H, N, D, Dh, chunk, a, (float*)o,
-                         w1_out, w2_out, static_cast<float*>(ws));
+      launch_generic<float>(B * H, H, N, D, Dh, chunk, a, q, k, v, w1, w2, wbs, o, w1_out, w2_out,
+                            static_cast<float*>(ws), st);
     return hipGetLastError();
   }
   int* flags = static_cast<int*>(ws);
