@@ -145,7 +145,8 @@ def _oracle_task(args):
 
 
 def cpu_workers() -> int:
-    """Host cores for the oracle: OMP_NUM_THREADS (the machine's CPU share) or the core count, at most 16."""
+    """Host cores for the oracle: OMP_NUM_THREADS (the host threads this process may use) or the core count, at most
+    16 (a host's share per GPU)."""
     n = int(os.environ.get("OMP_NUM_THREADS") or 0) or (os.cpu_count() or 1)
     return max(1, min(16, n, os.cpu_count() or 1))
 

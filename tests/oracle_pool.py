@@ -15,7 +15,7 @@ import numpy as np
 
 
 def workers() -> int:
-    """Worker count: the host's cores, at most 16 (the CPU share of a one-GPU machine)."""
+    """Worker count: the host's cores, at most 16 (a host's share per GPU)."""
     n = int(os.environ.get("OMP_NUM_THREADS") or 0) or (os.cpu_count() or 1)
     return max(1, min(16, n, os.cpu_count() or 1))
 
