@@ -551,8 +551,9 @@ __global__ __launch_bounds__(kGenThreads) void mlp_fwd_generic(
     const float* __restrict__ w1, const float* __restrict__ w2, long long wbs, int H, int N, int Dh,
     float a, T* __restrict__ o, float* __restrict__ w1_out, float* __restrict__ w2_out,
     float* __restrict__ ws) {
-  constexpr int DP = D + 1, G = kGenThreads / D;  // G hidden-unit groups of the E / O partial sums
-  __shared__ float sK[CH * DP], sV[CH * DP], sQ[CH * DP], sE[CH * DP];
+  // DP: LDS row pitch; 16-byte rows, so that the unrolled broadcast reads of a row vectorise
+  constexpr int DP = D + 4, G = kGenThreads / D;  // G hidden-unit groups of the E / O partial sums
+  __shared__ __align__(16) float sK[CH * DP], sV[CH * DP], sQ[CH * DP], sE[CH * DP];
   __shared__ float sM[CH * (CH + 1)], sN2[CH * (CH + 1)];
   __shared__ float sPart[kGenThreads * (kGenTB + 1)];
   const int bh = blockIdx.x, b = bh / H, h = bh % H, tid = threadIdx.x;
