@@ -81,10 +81,13 @@ struct Stager {
   }
 };
 
-// W* for the read-out is stored in bf16 as the read-out's MFMA A operands (W*^T tiles), so that
-// a lane loads each operand with one access. Operand (head hl, column tile n, k step ks), lane
-// l = r + 16g, element i holds W*[kb * ks + e * g + i][16n + r] with e = 8 (D >= 32, k steps of
-// 32) or e = 4 (D = 16, one k step of 16), kb = 4e.
+// W* for the read-out is stored as the read-out's MFMA A operands (W*^T tiles), so that a lane
+// loads each operand with one access, in two bf16 parts: hi = bf16(W*) and lo = bf16(W* - hi). The
+// read-out multiplies by both (same-shape products into one fp32 accumulator), so W* enters with
+// about 16 significant bits instead of bf16's 8: the read-out is bound by HBM, not by the matrix
+// cores. Operand (head hl, column tile n, k step ks), lane l = r + 16g, element i holds
+// W*[kb * ks + e * g + i][16n + r] with e = 8 (D >= 32, k steps of 32) or e = 4 (D = 16, one k
+// step of 16), kb = 4e; the lo part follows the hi part at an offset of HG d^2 elements.
 template <int D>
 constexpr int kOpElems = D >= 32 ? 8 : 4;
 
@@ -103,8 +106,8 @@ __device__ __forceinline__ int wstar_operand_offset(int hl, int row, int col) {
 // fp32 to w_out and W1 in fp32 to wnext (the next epoch's W0, same layout as W0).
 template <int D>
 __device__ __forceinline__ void wstar_rows(const f32x4* acc, int hl, int m, const float* W0,
-                                           float scale, bf16* wop_grp, float* w_out, float* wnext,
-                                           int r, int g) {
+                                           float scale, bf16* wop_grp, int lo_offset, float* w_out,
+                                           float* wnext, int r, int g) {
   constexpr int NT = D / 16;
   bf16x4 ka[NT];
   for (int c = 0; c < NT; ++c) ka[c] = to_bf16x4(acc[c]);
@@ -118,7 +121,11 @@ __device__ __forceinline__ void wstar_rows(const f32x4* acc, int hl, int m, cons
     for (int j = 0; j < 4; ++j) {  // W*[16m + 4g + j][16n + r]
       const int row = 16 * m + 4 * g + j, col = 16 * n + r;
       const float wv = W0[row * D + col] - scale * (gw[j] - acc[NT + n][j]);
-      if (wop_grp) wop_grp[wstar_operand_offset<D>(hl, row, col)] = (bf16)wv;
+      if (wop_grp) {
+        const bf16 hi = (bf16)wv;
+        wop_grp[wstar_operand_offset<D>(hl, row, col)] = hi;
+        wop_grp[lo_offset + wstar_operand_offset<D>(hl, row, col)] = (bf16)(wv - (float)hi);
+      }
       if (w_out) w_out[row * D + col] = wv;
       if (wnext) wnext[row * D + col] = wv;
     }
@@ -267,7 +274,7 @@ __global__ __launch_bounds__(kThreads) void fb_readout_bf16(
   __shared__ __align__(16) bf16 sO[4][16 * G::P];
   __shared__ __align__(16) float sW0[HG * D * D];
   __shared__ __align__(16) float sW1[HG * D * D];  // the other epoch buffer
-  __shared__ __align__(16) bf16 sWop[HG * D * D];
+  __shared__ __align__(16) bf16 sWop[2 * HG * D * D];  // hi, then lo
   __shared__ f32x4 sSum[(4 - TASKS) > 0 ? (4 - TASKS) : 1][T2][64];
   const int item = xcd_item(blockIdx.x, gridDim.x);
   const int grp = item / S, s = item % S;
@@ -342,7 +349,7 @@ __global__ __launch_bounds__(kThreads) void fb_readout_bf16(
     for (int e = 0; e < epochs; ++e) {
       const bool last = e + 1 == epochs;
       if (tw == 0)
-        wstar_rows<D>(acc, hl, m, wcur + hl * DD, scale, last ? sWop : nullptr,
+        wstar_rows<D>(acc, hl, m, wcur + hl * DD, scale, last ? sWop : nullptr, HG * D * D,
                       (last && w_out && s == 0) ? w_out + ((long long)b * H + h0 + hl) * DD : nullptr,
                       last ? nullptr : wnxt + hl * DD, r, g);
       __syncthreads();
@@ -352,11 +359,14 @@ __global__ __launch_bounds__(kThreads) void fb_readout_bf16(
     }
   }
   using Op = typename std::conditional<(D >= 32), bf16x8, bf16x4>::type;
-  Op wa[HG][NT][KS];  // A operands W*^T
+  Op wa[HG][NT][KS], wl[HG][NT][KS];  // A operands W*^T, hi and lo parts
   for (int hl2 = 0; hl2 < HG; ++hl2)
     for (int n = 0; n < NT; ++n)
-      for (int ks = 0; ks < KS; ++ks)
-        wa[hl2][n][ks] = *reinterpret_cast<const Op*>(sWop + (((hl2 * NT + n) * KS + ks) * 64 + l) * E);
+      for (int ks = 0; ks < KS; ++ks) {
+        const int off = (((hl2 * NT + n) * KS + ks) * 64 + l) * E;
+        wa[hl2][n][ks] = *reinterpret_cast<const Op*>(sWop + off);
+        wl[hl2][n][ks] = *reinterpret_cast<const Op*>(sWop + HG * D * D + off);
+      }
 
   auto step = [&](int i, Regs& R) {
     const int t0 = n0 + 16 * (w + 4 * i);
@@ -371,8 +381,8 @@ __global__ __launch_bounds__(kThreads) void fb_readout_bf16(
         f32x4 acc = zero4();
         for (int ks = 0; ks < KS; ++ks) {
           const Op qb = *reinterpret_cast<const Op*>(myQ + r * G::P + hl * D + 4 * E * ks + E * g);
-          if constexpr (D >= 32) acc = mma32(wa[hl][n][ks], qb, acc);
-          else acc = mma16(wa[hl][n][ks], qb, acc);
+          if constexpr (D >= 32) acc = mma32(wl[hl][n][ks], qb, mma32(wa[hl][n][ks], qb, acc));
+          else acc = mma16(wl[hl][n][ks], qb, mma16(wa[hl][n][ks], qb, acc));
         }
         *reinterpret_cast<bf16x4*>(myO + r * G::P + hl * D + 16 * n + 4 * g) = to_bf16x4(acc);
       }
