@@ -266,10 +266,25 @@ def extra_legs(T, torch, inputs, dev, time_rotated) -> dict:
         causal TTT-Linear layer (2 x 16384 x 12 x 64, b = 16) and of the Vision-TTT bidirectional
         scan (8 x 6400 x 3 x 64, b = 64), bf16;
       * design-space variants: 4 full-batch epochs at the H-ViT^3-T stage-1 shape, the Vision-TTT scan
-        with b = 16, and a 4x wider inner MLP (Dh = 1024) at a reduced shape."""
+        with b = 16, and a 4x wider inner MLP (Dh = 1024) at a reduced shape;
+      * vit3s_fullbatch: the ViT^3-S-shaped full-batch layer (64 images x 196 tokens, 6 heads of 64,
+        bf16), which runs as one launch (one workgroup per (image, head))."""
+    from test_sequence_layers_amd import synth
+
+    out = {}
+    vw = synth.WORKLOADS["vit3s_fullbatch"]
+    dv3 = to_device(synth.make_inputs(vw), torch)
+    cold, warm, nsets = time_rotated(lambda d: make_call(T, vw, d, torch), dv3, vw.io_bytes)
+    sec = cold / 1000.0
+    out["vit3s_fullbatch"] = {
+        "ms": round(cold, 5), "ms_warm": round(warm, 5), "tokens_per_s": vw.tokens / sec, "alg_bytes": vw.io_bytes,
+        "alg_GBs": vw.io_bytes / sec / 1e9, "hbm_frac": vw.io_bytes / sec / 1e9 / PEAK_HBM_GBS,
+        "hbm_frac_warm": vw.io_bytes / (warm / 1000.0) / 1e9 / PEAK_HBM_GBS,
+        "timing": f"cold: inputs rotated over {nsets} copies (> 1 GiB)"}
+    del dv3
     name = "vittt_bidir_1280"
     if name not in inputs:
-        return {}
+        return out
     wl = inputs[name].wl
     Hi = Wi = 80
     C = wl.H * wl.D
@@ -291,7 +306,6 @@ def extra_legs(T, torch, inputs, dev, time_rotated) -> dict:
         return run
 
     conv_bytes = 4 * wl.B * wl.N * C * 2          # read K and V, write both convolved
-    out = {}
     fb = "hvit3t_stage1_fullbatch"
     if fb in inputs:  # the full-batch layer's backward pass at the H-ViT^3-T stage-1 shape
         fw = inputs[fb].wl
@@ -406,8 +420,6 @@ def extra_legs(T, torch, inputs, dev, time_rotated) -> dict:
         "alg_bytes": wl.io_bytes, "alg_GBs": wl.io_bytes / sec / 1e9, "hbm_frac": wl.io_bytes / sec / 1e9 / PEAK_HBM_GBS,
         "timing": f"cold: inputs rotated over {nsets} copies (> 1 GiB); mini-batches of 16 tokens"}
     # a wider inner MLP (Dh = 1024, 4 x the suite's) on the plain fp32 path, at a reduced shape
-    from test_sequence_layers_amd import synth
-
     mw = synth.WORKLOADS["ttt_mlp_causal_8k"].with_(B=1, N=1024, H=12, Dh=1024, seed=4545)
     xm = synth.make_inputs(mw)
     dm = to_device(xm, torch)

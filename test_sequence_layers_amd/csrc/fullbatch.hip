@@ -15,7 +15,9 @@
 //                    through wave-private LDS tiles, one wave per 16-token block, and write
 //                    O = Q W*.
 // HBM traffic is the algorithmic Q, K, V read plus the O write; the split records are two d x d
-// fp32 matrices per split and stay in L2 / Infinity Cache.
+// fp32 matrices per split and stay in L2 / Infinity Cache. When the plan gives each group one
+// split (many groups of few tokens, e.g. 64 images of 196 tokens), fb_fused_bf16 does both in one
+// launch, the sums kept in registers: no records, one launch fewer.
 //
 // fp32 I/O: three plain-FMA launches (the splits' K^T K and K^T V, a fixed-order reduction that
 // also runs the epochs, read-out).
@@ -98,38 +100,58 @@ __device__ __forceinline__ int wstar_operand_offset(int hl, int row, int col) {
          row % E;
 }
 
-// Row block m of W1 = W0 - scale ((K^T K) W0 - K^T V) for head hl of a group (one epoch from W0),
-// from the summed accumulator tiles acc[0 .. NT) = (c, m) of K^T K and acc[NT .. 2NT) = (m, n) of
-// K^T V. By symmetry, tile (c, m) of K^T K in accumulator layout is the A operand of rows 16m..
-// and k block c. (The 16x16x16 products keep their own accumulators: they must not take a
-// 16x16x32 result as their accumulator input.) Writes, where set, the read-out operands, W1 in
-// fp32 to w_out and W1 in fp32 to wnext (the next epoch's W0, same layout as W0).
+// A head's state W in LDS for the product (K^T K) W: its bf16 transpose, rows of pitch D + 8
+// (WbT[col][row]), so that each MFMA B operand of W (lane (r, g): W[16c + 4g + i][16n + r], i < 4)
+// is one 8-byte read. The fp32 W itself stays in the registers of the waves that own its rows.
 template <int D>
-__device__ __forceinline__ void wstar_rows(const f32x4* acc, int hl, int m, const float* W0,
-                                           float scale, bf16* wop_grp, int lo_offset, float* w_out,
-                                           float* wnext, int r, int g) {
+constexpr int kWtPitch = D + 8;
+
+// Row block m of W (tiles (m, n), accumulator layout: lane (r, g) holds W[16m + 4g + j][16n + r]):
+// loaded from HBM (w: the head's d x d matrix) and stored to LDS as part of W's bf16 transpose.
+template <int D>
+__device__ __forceinline__ void load_rows(const float* __restrict__ w, int m, int r, int g, f32x4 (&wr)[D / 16]) {
+  for (int n = 0; n < D / 16; ++n)
+    for (int j = 0; j < 4; ++j) wr[n][j] = w[(16 * m + 4 * g + j) * D + 16 * n + r];
+}
+template <int D>
+__device__ __forceinline__ void put_rows_t(const f32x4 (&wr)[D / 16], int m, int r, int g, bf16* wbt) {
+  for (int n = 0; n < D / 16; ++n)
+    *reinterpret_cast<bf16x4*>(wbt + (16 * n + r) * kWtPitch<D> + 16 * m + 4 * g) = to_bf16x4(wr[n]);
+}
+
+// One epoch for row block m of head hl of a group: W1 = W - scale ((K^T K) W - K^T V), from the
+// summed accumulator tiles acc[0 .. NT) = (c, m) of K^T K and acc[NT .. 2NT) = (m, n) of K^T V,
+// the row block wr of W (replaced by W1's) and W's bf16 transpose wbt (all rows). By symmetry,
+// tile (c, m) of K^T K in accumulator layout is the A operand of rows 16m.. and k block c. (The
+// 16x16x16 products keep their own accumulators: they must not take a 16x16x32 result as their
+// accumulator input.) Writes, where set: the read-out operands (8-byte pieces: a lane's four
+// rows of a column are adjacent there), W1 in fp32 to w_out, W1's bf16 transpose to nbt (the next
+// epoch's wbt).
+template <int D>
+__device__ __forceinline__ void wstar_rows(const f32x4* acc, int hl, int m, f32x4 (&wr)[D / 16],
+                                           const bf16* wbt, float scale, bf16* wop_grp, int lo_offset,
+                                           float* w_out, bf16* nbt, int r, int g) {
   constexpr int NT = D / 16;
   bf16x4 ka[NT];
   for (int c = 0; c < NT; ++c) ka[c] = to_bf16x4(acc[c]);
   for (int n = 0; n < NT; ++n) {
     f32x4 gw = zero4();
-    for (int c = 0; c < NT; ++c) {
-      bf16x4 wb;  // B operand: W0[16c + 4g + i][16n + r]
-      for (int i = 0; i < 4; ++i) wb[i] = (bf16)W0[(16 * c + 4 * g + i) * D + 16 * n + r];
-      gw = mma16(ka[c], wb, gw);
+    for (int c = 0; c < NT; ++c) gw = mma16(ka[c], ld4(wbt + (16 * n + r) * kWtPitch<D> + 16 * c + 4 * g), gw);
+    f32x4 wv;  // W1[16m + 4g + j][16n + r]
+    for (int j = 0; j < 4; ++j) wv[j] = wr[n][j] - scale * (gw[j] - acc[NT + n][j]);
+    wr[n] = wv;
+    if (wop_grp) {
+      const bf16x4 hi = to_bf16x4(wv);
+      f32x4 rest;
+      for (int j = 0; j < 4; ++j) rest[j] = wv[j] - (float)hi[j];
+      const int off = wstar_operand_offset<D>(hl, 16 * m + 4 * g, 16 * n + r);
+      *reinterpret_cast<bf16x4*>(wop_grp + off) = hi;
+      *reinterpret_cast<bf16x4*>(wop_grp + lo_offset + off) = to_bf16x4(rest);
     }
-    for (int j = 0; j < 4; ++j) {  // W*[16m + 4g + j][16n + r]
-      const int row = 16 * m + 4 * g + j, col = 16 * n + r;
-      const float wv = W0[row * D + col] - scale * (gw[j] - acc[NT + n][j]);
-      if (wop_grp) {
-        const bf16 hi = (bf16)wv;
-        wop_grp[wstar_operand_offset<D>(hl, row, col)] = hi;
-        wop_grp[lo_offset + wstar_operand_offset<D>(hl, row, col)] = (bf16)(wv - (float)hi);
-      }
-      if (w_out) w_out[row * D + col] = wv;
-      if (wnext) wnext[row * D + col] = wv;
-    }
+    if (w_out)
+      for (int j = 0; j < 4; ++j) w_out[(16 * m + 4 * g + j) * D + 16 * n + r] = wv[j];
   }
+  if (nbt) put_rows_t<D>(wr, m, r, g, nbt);
 }
 
 // Blocks of one launch go to the 8 XCDs in turn (block i to XCD i mod 8); the work items of a
@@ -140,42 +162,28 @@ __device__ __forceinline__ int xcd_item(int i, int items) {
   return x * q + min(x, rem) + i / 8;
 }
 
-// 1. Gradient sums of one token split of one head group: the split's gradient at W0 is
-// K_s^T (K_s W0 - V_s) = (K_s^T K_s) W0 - K_s^T V_s, so the kernel accumulates K_s^T K_s and
-// K_s^T V_s over the split's tokens, every MFMA operand read from LDS by transpose reads
-// (contraction over tokens); W0 is applied once per group by the reduction. Wave w owns task
-// (head, 16-row block m); waves sharing a task split the 32-token steps. K^T K is symmetric, so
-// the wave accumulates its column block m, tiles (c, m) in accumulator layout, which are the A
-// operands of row block m, k block c, in the product with W0.
+// Gradient sums over tokens [n0, n1) of one head group: the gradient at W0 of those tokens is
+// K_s^T (K_s W0 - V_s) = (K_s^T K_s) W0 - K_s^T V_s, so K_s^T K_s and K_s^T V_s are accumulated,
+// every MFMA operand read from LDS by transpose reads (contraction over tokens); W0 is applied
+// once per group, when W* is formed. Wave w owns task (head hl, 16-row block m); waves sharing a
+// task split the 32-token steps. K^T K is symmetric, so the wave accumulates its column block m,
+// tiles (c, m) in accumulator layout, which are the A operands of row block m, k block c, in the
+// product with W0. The tiles stream through the double-buffered sK, sV ([2][kTile * P] each).
 template <int D, int HG>
-__global__ __launch_bounds__(kThreads, 4) void fb_partial_bf16(
-    const bf16* __restrict__ k, const bf16* __restrict__ v, const float* __restrict__ w0,
-    long long w0_bstride, int H, int N, int S, int tps, float* __restrict__ partial) {
+__device__ __forceinline__ void gram_sums(const bf16* __restrict__ k, const bf16* __restrict__ v,
+                                          long long base, long long ts, int n0, int n1, bf16* sK,
+                                          bf16* sV, f32x4 (&kk)[D / 16], f32x4 (&kv)[D / 16]) {
   using G = Geo<D, HG>;
   constexpr int NT = G::NT;
-  constexpr long long DD = (long long)D * D;
   constexpr int TASKS = HG * NT;  // (head, 16-row block) of G_s
   constexpr int WPT = 4 / TASKS;  // waves per task
-  __shared__ __align__(16) bf16 sK[2][kTile * G::P];
-  __shared__ __align__(16) bf16 sV[2][kTile * G::P];
   static_assert(TASKS * WPT == 4, "tasks divide the waves");
-  static_assert(sizeof(float) * (4 - TASKS) * 2 * NT * 256 <= sizeof(bf16) * 2 * kTile * G::P,
-                "sums of the waves sharing a task fit in sK");
-  float* sG = reinterpret_cast<float*>(&sK[0][0]);
-
-  const int item = xcd_item(blockIdx.x, gridDim.x);
-  const int grp = item / S, s = item % S;
-  const int b = grp / (H / HG), h0 = (grp % (H / HG)) * HG;
-  const int n0 = s * tps, n1 = min(N, n0 + tps);
   const int ntiles = (n1 - n0 + kTile - 1) / kTile;
-  const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
+  const int w = wave_id(), l = lane_id();
   const int task = w % TASKS, tw = w / TASKS;
   const int hl = task / NT, m = task % NT;  // head within the group, row block
-  const long long ts = (long long)H * D;
-  const long long base = (long long)b * N * ts + (long long)h0 * D;
   const Stager<G> stk{k, base, ts, n1}, stv{v, base, ts, n1};
 
-  f32x4 kk[NT], kv[NT];  // tiles (c, m) of K^T K and (m, n) of K^T V
   for (int c = 0; c < NT; ++c) kk[c] = kv[c] = zero4();
   constexpr int SETS = tile_sets(D);
   struct Regs {
@@ -189,13 +197,14 @@ __global__ __launch_bounds__(kThreads, 4) void fb_partial_bf16(
   for (int u = 0; u < SETS; ++u)
     if (u < ntiles) load(sets[u], u);
   auto step = [&](int it, Regs& R) {
-    const int buf = it & 1;
-    Stager<G>::store(sK[buf], R.k);
-    Stager<G>::store(sV[buf], R.v);
+    bf16* bK = sK + (it & 1) * (kTile * G::P);
+    bf16* bV = sV + (it & 1) * (kTile * G::P);
+    Stager<G>::store(bK, R.k);
+    Stager<G>::store(bV, R.v);
     if (it + SETS < ntiles) load(R, it + SETS);
     __syncthreads();
-    const bf16* tK = sK[buf] + hl * D;
-    const bf16* tV = sV[buf] + hl * D;
+    const bf16* tK = bK + hl * D;
+    const bf16* tV = bV + hl * D;
     for (int ks = tw; ks < kTile / 32; ks += WPT) {
       // Operands over 32 tokens, k map {4g + j} u {16 + 4g + j}: lane (r, g) holds column r.
       const bf16* k0 = tK + 32 * ks * G::P;
@@ -217,12 +226,17 @@ __global__ __launch_bounds__(kThreads, 4) void fb_partial_bf16(
     for (int u = 0; u < SETS; ++u)
       if (it + u < ntiles) step(it + u, sets[u]);
   }
-  // The split's partial record holds, per task (head, row block m), the accumulator tiles
-  // (c, m) of K^T K then (m, n) of K^T V, lane by lane (16 bytes a lane, coalesced). Waves
-  // sharing a task add theirs first through sK, in a fixed order.
-  float* part = partial + ((long long)grp * S + s) * (2 * HG * D * D) + (long long)task * (2 * NT * 256);
+}
+
+// Waves sharing a task (when a group has fewer than four tasks) add their sums into those of the
+// task's wave tw = 0, in a fixed order, through sG ((4 - TASKS) * 2 NT fp32 tiles of 64 lanes; it
+// may alias the tile buffers of gram_sums: the first barrier frees them).
+template <int D, int HG>
+__device__ __forceinline__ void task_sum(float* sG, f32x4 (&kk)[D / 16], f32x4 (&kv)[D / 16]) {
+  constexpr int NT = D / 16, TASKS = HG * NT, WPT = 4 / TASKS;
   if constexpr (WPT > 1) {
-    __syncthreads();  // tile buffers free
+    const int w = wave_id(), l = lane_id(), task = w % TASKS, tw = w / TASKS;
+    __syncthreads();
     if (tw > 0)
       for (int c = 0; c < NT; ++c) {
         *reinterpret_cast<f32x4*>(sG + (((w - TASKS) * 2 * NT + c) * 64 + l) * 4) = kk[c];
@@ -238,6 +252,36 @@ __global__ __launch_bounds__(kThreads, 4) void fb_partial_bf16(
         }
       }
   }
+}
+
+// 1. Gradient sums of one token split of one head group (gram_sums); the split's record holds,
+// per task (head, row block m), the accumulator tiles (c, m) of K^T K then (m, n) of K^T V, lane
+// by lane (16 bytes a lane, coalesced).
+template <int D, int HG>
+__global__ __launch_bounds__(kThreads, 4) void fb_partial_bf16(
+    const bf16* __restrict__ k, const bf16* __restrict__ v, const float* __restrict__ w0,
+    long long w0_bstride, int H, int N, int S, int tps, float* __restrict__ partial) {
+  using G = Geo<D, HG>;
+  constexpr int NT = G::NT;
+  constexpr int TASKS = HG * NT;
+  __shared__ __align__(16) bf16 sK[2][kTile * G::P];
+  __shared__ __align__(16) bf16 sV[2][kTile * G::P];
+  static_assert(sizeof(float) * (4 - TASKS) * 2 * NT * 256 <= sizeof(bf16) * 2 * kTile * G::P,
+                "sums of the waves sharing a task fit in sK");
+
+  const int item = xcd_item(blockIdx.x, gridDim.x);
+  const int grp = item / S, s = item % S;
+  const int b = grp / (H / HG), h0 = (grp % (H / HG)) * HG;
+  const int n0 = s * tps, n1 = min(N, n0 + tps);
+  const int w = wave_id(), l = lane_id();
+  const int task = w % TASKS, tw = w / TASKS;
+  const long long ts = (long long)H * D;
+  const long long base = (long long)b * N * ts + (long long)h0 * D;
+
+  f32x4 kk[NT], kv[NT];  // tiles (c, m) of K^T K and (m, n) of K^T V
+  gram_sums<D, HG>(k, v, base, ts, n0, n1, &sK[0][0], &sV[0][0], kk, kv);
+  task_sum<D, HG>(reinterpret_cast<float*>(&sK[0][0]), kk, kv);
+  float* part = partial + ((long long)grp * S + s) * (2 * HG * D * D) + (long long)task * (2 * NT * 256);
   if (tw == 0)
     for (int c = 0; c < NT; ++c) {
       *reinterpret_cast<f32x4*>(part + (c * 64 + l) * 4) = kk[c];
@@ -245,119 +289,83 @@ __global__ __launch_bounds__(kThreads, 4) void fb_partial_bf16(
     }
 }
 
-// 2. O = Q W*, computed as O^T = W*^T Q^T (lane (r, g) gets 4 adjacent outputs of token r).
-// Each workgroup first forms its group's W* = W0 - (eta/N) ((sum_s K_s^T K_s) W0 - sum_s K_s^T V_s)
-// from the split records (wave (task, tw) sums the task's tiles of splits tw, tw + WPT, ...; the
-// waves of a task add theirs in a fixed order, so every workgroup of a group gets the same W*),
-// with its first Q blocks already in flight; the work items of a group share an XCD (xcd_item).
-// W* goes to LDS as the read-out's MFMA operands (wstar_rows).
-// Then each wave streams its own 16-token blocks of the split (blocks w, w + 4, ...), kReadSets
-// of them in flight, through a wave-private LDS tile: full-row 16-byte pieces to and from HBM,
-// operand-shaped pieces to and from the matrix cores. No workgroup barriers in that loop: a wave's
-// LDS operations execute in order, and a wavefront-scope fence keeps the compiler from reordering
-// them.
+// W* of the group from the summed tiles acc of the waves tw = 0 (acc[0 .. NT): tiles (c, m) of
+// K^T K, acc[NT .. 2NT): tiles (m, n) of K^T V) and their row blocks wr of W0 (load_rows). Epoch e
+// takes W_{e+1} = W_e - scale ((K^T K) W_e - K^T V) with W_e's bf16 transpose in wbt[e & 1]
+// (HG heads of d rows of pitch kWtPitch each; the first stored here); the last epoch writes the
+// read-out operands sWop (hi, then lo) and, where w_out_grp is set, W* in fp32 (the group's heads,
+// contiguous). Starts and ends with a barrier.
+template <int D, int HG>
+__device__ __forceinline__ void form_wstar(const f32x4* acc, f32x4 (&wr)[D / 16], bf16* wbt0, bf16* wbt1,
+                                           bf16* sWop, float scale, int epochs, float* w_out_grp) {
+  constexpr int NT = D / 16, TASKS = HG * NT;
+  constexpr long long DD = (long long)D * D;
+  constexpr int WT = D * kWtPitch<D>;
+  const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
+  const int task = w % TASKS, tw = w / TASKS, hl = task / NT, m = task % NT;
+  if (tw == 0) put_rows_t<D>(wr, m, r, g, wbt0 + hl * WT);
+  __syncthreads();
+  for (int e = 0; e < epochs; ++e) {
+    const bool last = e + 1 == epochs;
+    bf16* cur = (e & 1) ? wbt1 : wbt0;
+    bf16* nxt = (e & 1) ? wbt0 : wbt1;
+    if (tw == 0)
+      wstar_rows<D>(acc, hl, m, wr, cur + hl * WT, scale, last ? sWop : nullptr, HG * D * D,
+                    (last && w_out_grp) ? w_out_grp + hl * DD : nullptr, last ? nullptr : nxt + hl * WT, r, g);
+    __syncthreads();
+  }
+}
+
+// A wave's 16-token blocks of Q within [n0, n1) (blocks w, w + 4, ...), loaded as full-row 16-byte
+// pieces into register sets.
 constexpr int kReadSets = 4;
 
 template <int D, int HG>
-__global__ __launch_bounds__(kThreads) void fb_readout_bf16(
-    const bf16* __restrict__ q, const float* __restrict__ partial, const float* __restrict__ w0,
-    long long w0_bstride, int H, int N, int S, int tps, float scale, int epochs,
-    bf16* __restrict__ o, float* __restrict__ w_out) {
+struct QBlocks {
   using G = Geo<D, HG>;
-  constexpr int NT = D / 16, E = kOpElems<D>, KS = D / (4 * E);
-  constexpr long long DD = (long long)D * D;
-  constexpr int TASKS = HG * NT, WPT = 4 / TASKS, T2 = 2 * NT;
-  constexpr int BP = 16 * G::CPR;       // 16-byte pieces of a 16-token block
-  constexpr int PPL = (BP + 63) / 64;   // pieces per lane
-  constexpr int WPER = (HG * D * D + kThreads - 1) / kThreads;
-  __shared__ __align__(16) bf16 sQ[4][16 * G::P];
-  __shared__ __align__(16) bf16 sO[4][16 * G::P];
-  __shared__ __align__(16) float sW0[HG * D * D];
-  __shared__ __align__(16) float sW1[HG * D * D];  // the other epoch buffer
-  __shared__ __align__(16) bf16 sWop[2 * HG * D * D];  // hi, then lo
-  __shared__ f32x4 sSum[(4 - TASKS) > 0 ? (4 - TASKS) : 1][T2][64];
-  const int item = xcd_item(blockIdx.x, gridDim.x);
-  const int grp = item / S, s = item % S;
-  const int b = grp / (H / HG), h0 = (grp % (H / HG)) * HG;
-  const int n0 = s * tps, n1 = min(N, n0 + tps);
-  const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
-  const int task = w % TASKS, tw = w / TASKS, hl = task / NT, m = task % NT;
-  const int blocks = (n1 - n0 + 15) / 16;
-  const int mine = blocks > w ? (blocks - w + 3) / 4 : 0;
-  const long long ts = (long long)H * D;
-  const long long base = (long long)b * N * ts + (long long)h0 * D;
-  bf16* myQ = sQ[w];
-  bf16* myO = sO[w];
-
+  static constexpr int BP = 16 * G::CPR;      // 16-byte pieces of a 16-token block
+  static constexpr int PPL = (BP + 63) / 64;  // pieces per lane
   struct Regs {
     uint4 x[PPL];
-  } sets[kReadSets];
-  auto valid = [&](int c) { return BP % 64 == 0 || c < BP; };
-  auto load = [&](Regs& R, int i) {
+  };
+  const bf16* q;
+  long long base, ts;
+  int n0, n1, w, l, mine;
+  __device__ __forceinline__ QBlocks(const bf16* q_, long long base_, long long ts_, int n0_, int n1_)
+      : q(q_), base(base_), ts(ts_), n0(n0_), n1(n1_), w(wave_id()), l(lane_id()) {
+    const int blocks = (n1 - n0 + 15) / 16;
+    mine = blocks > w ? (blocks - w + 3) / 4 : 0;
+  }
+  __device__ __forceinline__ static bool valid(int c) { return BP % 64 == 0 || c < BP; }
+  __device__ __forceinline__ void load(Regs& R, int i) const {
     const int t0 = n0 + 16 * (w + 4 * i);
     for (int u = 0; u < PPL; ++u) {
       const int c = l + 64 * u, row = c / G::CPR;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (valid(c) && t0 + row < n1) v = ld16(q + base + (t0 + row) * ts + (c % G::CPR) * 8);
-      R.x[u] = v;
-    }
-  };
-#pragma unroll
-  for (int u = 0; u < kReadSets; ++u)
-    if (u < mine) load(sets[u], u);
-
-  // W* of the group, while those loads are in flight.
-  {
-    const float* W0g = w0 + b * w0_bstride + (long long)h0 * DD;  // the group's heads, contiguous
-    float w0v[WPER];
-    for (int i = 0; i < WPER; ++i) {
-      const int e = threadIdx.x + i * kThreads;
-      w0v[i] = (HG * D * D) % kThreads == 0 || e < HG * D * D ? W0g[e] : 0.f;
-    }
-    const float* pt = partial + (long long)grp * S * (2 * HG * DD) + (long long)task * (T2 * 256) + l * 4;
-    f32x4 acc[T2];
-    for (int t = 0; t < T2; ++t) acc[t] = zero4();
-    constexpr int UB = T2 >= 8 ? 2 : 4;  // splits in flight (16 tiles of loads)
-    for (int s0 = tw; s0 < S; s0 += UB * WPT) {
-      f32x4 x[UB][T2];
-      for (int u = 0; u < UB; ++u) {
-        const int sp = s0 + u * WPT;
-        for (int t = 0; t < T2; ++t)
-          x[u][t] = sp < S ? *reinterpret_cast<const f32x4*>(pt + (long long)sp * (2 * HG * DD) + t * 256) : zero4();
-      }
-      for (int u = 0; u < UB; ++u)
-        for (int t = 0; t < T2; ++t) acc[t] += x[u][t];
-    }
-    for (int i = 0; i < WPER; ++i) {
-      const int e = threadIdx.x + i * kThreads;
-      if ((HG * D * D) % kThreads == 0 || e < HG * D * D) sW0[e] = w0v[i];
-    }
-    if constexpr (WPT > 1) {
-      if (tw > 0)
-        for (int t = 0; t < T2; ++t) sSum[w - TASKS][t][l] = acc[t];
-    }
-    __syncthreads();
-    if constexpr (WPT > 1) {
-      if (tw == 0)
-        for (int u = 1; u < WPT; ++u)
-          for (int t = 0; t < T2; ++t) acc[t] += sSum[(u - 1) * TASKS + task][t][l];
-    }
-    // Epoch e: W_{e+1} = W_e - scale ((K^T K) W_e - K^T V), between the two LDS buffers; the last
-    // epoch writes the read-out operands (and w_out, from split 0's workgroup).
-    float* wcur = sW0;
-    float* wnxt = sW1;
-    for (int e = 0; e < epochs; ++e) {
-      const bool last = e + 1 == epochs;
-      if (tw == 0)
-        wstar_rows<D>(acc, hl, m, wcur + hl * DD, scale, last ? sWop : nullptr, HG * D * D,
-                      (last && w_out && s == 0) ? w_out + ((long long)b * H + h0 + hl) * DD : nullptr,
-                      last ? nullptr : wnxt + hl * DD, r, g);
-      __syncthreads();
-      float* t = wcur;
-      wcur = wnxt;
-      wnxt = t;
+      uint4 x = make_uint4(0u, 0u, 0u, 0u);
+      if (valid(c) && t0 + row < n1) x = ld16(q + base + (t0 + row) * ts + (c % G::CPR) * 8);
+      R.x[u] = x;
     }
   }
+  __device__ __forceinline__ void load_first(Regs (&sets)[kReadSets]) const {
+#pragma unroll
+    for (int u = 0; u < kReadSets; ++u)
+      if (u < mine) load(sets[u], u);
+  }
+};
+
+// O = Q W* for a wave's blocks, computed as O^T = W*^T Q^T (lane (r, g) gets 4 adjacent outputs of
+// token r), from the read-out operands sWop (wstar_rows) and the blocks' register sets (the first
+// kReadSets already loaded), kReadSets blocks in flight, through the wave-private LDS tiles myQ,
+// myO: full-row 16-byte pieces to and from HBM, operand-shaped pieces to and from the matrix
+// cores. No workgroup barriers: a wave's LDS operations execute in order, and a wavefront-scope
+// fence keeps the compiler from reordering them.
+template <int D, int HG>
+__device__ __forceinline__ void readout_blocks(const QBlocks<D, HG>& qb, typename QBlocks<D, HG>::Regs (&sets)[kReadSets],
+                                               const bf16* sWop, bf16* myQ, bf16* myO, bf16* __restrict__ o) {
+  using G = Geo<D, HG>;
+  using QB = QBlocks<D, HG>;
+  constexpr int NT = D / 16, E = kOpElems<D>, KS = D / (4 * E);
+  const int l = qb.l, r = l & 15, g = l >> 4;
   using Op = typename std::conditional<(D >= 32), bf16x8, bf16x4>::type;
   Op wa[HG][NT][KS], wl[HG][NT][KS];  // A operands W*^T, hi and lo parts
   for (int hl2 = 0; hl2 < HG; ++hl2)
@@ -368,37 +376,164 @@ __global__ __launch_bounds__(kThreads) void fb_readout_bf16(
         wl[hl2][n][ks] = *reinterpret_cast<const Op*>(sWop + HG * D * D + off);
       }
 
-  auto step = [&](int i, Regs& R) {
-    const int t0 = n0 + 16 * (w + 4 * i);
-    for (int u = 0; u < PPL; ++u) {
+  auto step = [&](int i, typename QB::Regs& R) {
+    const int t0 = qb.n0 + 16 * (qb.w + 4 * i);
+    for (int u = 0; u < QB::PPL; ++u) {
       const int c = l + 64 * u;
-      if (valid(c)) st16(myQ + (c / G::CPR) * G::P + (c % G::CPR) * 8, R.x[u]);
+      if (QB::valid(c)) st16(myQ + (c / G::CPR) * G::P + (c % G::CPR) * 8, R.x[u]);
     }
-    if (i + kReadSets < mine) load(R, i + kReadSets);
+    if (i + kReadSets < qb.mine) qb.load(R, i + kReadSets);
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     for (int hl = 0; hl < HG; ++hl)
       for (int n = 0; n < NT; ++n) {
         f32x4 acc = zero4();
         for (int ks = 0; ks < KS; ++ks) {
-          const Op qb = *reinterpret_cast<const Op*>(myQ + r * G::P + hl * D + 4 * E * ks + E * g);
-          if constexpr (D >= 32) acc = mma32(wl[hl][n][ks], qb, mma32(wa[hl][n][ks], qb, acc));
-          else acc = mma16(wl[hl][n][ks], qb, mma16(wa[hl][n][ks], qb, acc));
+          const Op qv = *reinterpret_cast<const Op*>(myQ + r * G::P + hl * D + 4 * E * ks + E * g);
+          if constexpr (D >= 32) acc = mma32(wl[hl][n][ks], qv, mma32(wa[hl][n][ks], qv, acc));
+          else acc = mma16(wl[hl][n][ks], qv, mma16(wa[hl][n][ks], qv, acc));
         }
         *reinterpret_cast<bf16x4*>(myO + r * G::P + hl * D + 16 * n + 4 * g) = to_bf16x4(acc);
       }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    for (int u = 0; u < PPL; ++u) {
+    for (int u = 0; u < QB::PPL; ++u) {
       const int c = l + 64 * u, row = c / G::CPR;
-      if (valid(c) && t0 + row < n1)
-        st16(o + base + (t0 + row) * ts + (c % G::CPR) * 8, ld16(myO + row * G::P + (c % G::CPR) * 8));
+      if (QB::valid(c) && t0 + row < qb.n1)
+        st16(o + qb.base + (t0 + row) * qb.ts + (c % G::CPR) * 8, ld16(myO + row * G::P + (c % G::CPR) * 8));
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   };
-  for (int i = 0; i < mine; i += kReadSets) {
+  for (int i = 0; i < qb.mine; i += kReadSets) {
 #pragma unroll
     for (int u = 0; u < kReadSets; ++u)
-      if (i + u < mine) step(i + u, sets[u]);
+      if (i + u < qb.mine) step(i + u, sets[u]);
   }
+}
+
+// 2. O = Q W* for one token split. Each workgroup first forms its group's
+// W* = W0 - (eta/N) ((sum_s K_s^T K_s) W0 - sum_s K_s^T V_s) from the split records (wave
+// (task, tw) sums the task's tiles of splits tw, tw + WPT, ...; the waves of a task add theirs in
+// a fixed order, so every workgroup of a group gets the same W*), with its first Q blocks already
+// in flight; the work items of a group share an XCD (xcd_item). Then readout_blocks.
+template <int D, int HG>
+__global__ __launch_bounds__(kThreads) void fb_readout_bf16(
+    const bf16* __restrict__ q, const float* __restrict__ partial, const float* __restrict__ w0,
+    long long w0_bstride, int H, int N, int S, int tps, float scale, int epochs,
+    bf16* __restrict__ o, float* __restrict__ w_out) {
+  using G = Geo<D, HG>;
+  constexpr int NT = D / 16;
+  constexpr long long DD = (long long)D * D;
+  constexpr int TASKS = HG * NT, WPT = 4 / TASKS, T2 = 2 * NT;
+  __shared__ __align__(16) bf16 sQ[4][16 * G::P];
+  __shared__ __align__(16) bf16 sO[4][16 * G::P];
+  __shared__ __align__(16) bf16 sWt[2][HG * D * kWtPitch<D>];  // W_e^T in bf16, by epoch parity
+  __shared__ __align__(16) bf16 sWop[2 * HG * D * D];  // hi, then lo
+  __shared__ f32x4 sSum[(4 - TASKS) > 0 ? (4 - TASKS) : 1][T2][64];
+  const int item = xcd_item(blockIdx.x, gridDim.x);
+  const int grp = item / S, s = item % S;
+  const int b = grp / (H / HG), h0 = (grp % (H / HG)) * HG;
+  const int n0 = s * tps, n1 = min(N, n0 + tps);
+  const int w = wave_id(), l = lane_id();
+  const int task = w % TASKS, tw = w / TASKS, hl = task / NT, m = task % NT;
+  const long long ts = (long long)H * D;
+  const long long base = (long long)b * N * ts + (long long)h0 * D;
+
+  const QBlocks<D, HG> qb(q, base, ts, n0, n1);
+  typename QBlocks<D, HG>::Regs sets[kReadSets];
+  qb.load_first(sets);
+
+  // W* of the group, while those loads are in flight.
+  f32x4 wr[NT];
+  if (tw == 0) load_rows<D>(w0 + b * w0_bstride + (long long)(h0 + hl) * DD, m, l & 15, l >> 4, wr);
+  const float* pt = partial + (long long)grp * S * (2 * HG * DD) + (long long)task * (T2 * 256) + l * 4;
+  f32x4 acc[T2];
+  for (int t = 0; t < T2; ++t) acc[t] = zero4();
+  constexpr int UB = T2 >= 8 ? 2 : 4;  // splits in flight (16 tiles of loads)
+  for (int s0 = tw; s0 < S; s0 += UB * WPT) {
+    f32x4 x[UB][T2];
+    for (int u = 0; u < UB; ++u) {
+      const int sp = s0 + u * WPT;
+      for (int t = 0; t < T2; ++t)
+        x[u][t] = sp < S ? *reinterpret_cast<const f32x4*>(pt + (long long)sp * (2 * HG * DD) + t * 256) : zero4();
+    }
+    for (int u = 0; u < UB; ++u)
+      for (int t = 0; t < T2; ++t) acc[t] += x[u][t];
+  }
+  if constexpr (WPT > 1) {
+    if (tw > 0)
+      for (int t = 0; t < T2; ++t) sSum[w - TASKS][t][l] = acc[t];
+    __syncthreads();
+    if (tw == 0)
+      for (int u = 1; u < WPT; ++u)
+        for (int t = 0; t < T2; ++t) acc[t] += sSum[(u - 1) * TASKS + task][t][l];
+  }
+  form_wstar<D, HG>(acc, wr, sWt[0], sWt[1], &sWop[0], scale, epochs,
+                    (w_out && s == 0) ? w_out + ((long long)b * H + h0) * DD : nullptr);
+  readout_blocks<D, HG>(qb, sets, sWop, sQ[w], sO[w], o);
+}
+
+// 1 + 2 in one launch, for plans with one split per group (many groups of few tokens, e.g. 64
+// images x 196 tokens x 6 heads of 64): one workgroup per group sums K^T K and K^T V over all of
+// the group's tokens (gram_sums, with the group's Q blocks and W0 already in flight), forms W*
+// from the sums in its registers and reads out Q. No split records, one launch instead of two;
+// the same arithmetic as the two launches with one split (a record sum from zero adds nothing).
+// The read-out's LDS buffers reuse those of the sums.
+template <int D, int HG>
+struct FusedLds {
+  using G = Geo<D, HG>;
+  static constexpr int kTileB = kTile * G::P * 2;  // bytes of one staged 64-token tile
+  static constexpr int kBlockB = 16 * G::P * 2;    // bytes of one wave's 16-token tile
+  static constexpr int kWtB = HG * D * kWtPitch<D> * 2;  // bytes of the group's W^T (bf16)
+  static constexpr int kSums = 4 * kTileB;                // sK[2], sV[2]
+  static constexpr int kQ = 0, kO = 4 * kBlockB, kWop = 8 * kBlockB;
+  static constexpr int kReadout = kWop + 2 * HG * D * D * 2;
+  // W^T by epoch parity: beside the other buffers (stored while the sums' tiles may still be read)
+  static constexpr int kWt = (kSums > kReadout ? kSums : kReadout);
+  static constexpr int kBytes = kWt + 2 * kWtB;
+};
+
+template <int D, int HG>
+__global__ __launch_bounds__(kThreads, 2) void fb_fused_bf16(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const float* __restrict__ w0, long long w0_bstride, int H, int N, float scale, int epochs,
+    bf16* __restrict__ o, float* __restrict__ w_out) {
+  using G = Geo<D, HG>;
+  using L = FusedLds<D, HG>;
+  constexpr int NT = D / 16;
+  constexpr long long DD = (long long)D * D;
+  static_assert(sizeof(float) * (4 - HG * NT) * 2 * NT * 256 <= 2 * L::kTileB, "task sums fit in sK");
+  __shared__ __align__(16) unsigned char smem[L::kBytes];
+  bf16* sK = reinterpret_cast<bf16*>(smem);
+  bf16* sV = reinterpret_cast<bf16*>(smem + 2 * L::kTileB);
+  const int grp = blockIdx.x;
+  const int b = grp / (H / HG), h0 = (grp % (H / HG)) * HG;
+  const int w = wave_id(), l = lane_id();
+  const int task = w % (HG * NT), tw = w / (HG * NT), hl = task / NT, m = task % NT;
+  const long long ts = (long long)H * D;
+  const long long base = (long long)b * N * ts + (long long)h0 * D;
+
+  const QBlocks<D, HG> qb(q, base, ts, 0, N);
+  typename QBlocks<D, HG>::Regs sets[kReadSets];
+  qb.load_first(sets);
+  f32x4 wr[NT];
+  if (tw == 0) load_rows<D>(w0 + b * w0_bstride + (long long)(h0 + hl) * DD, m, l & 15, l >> 4, wr);
+
+  f32x4 acc[2 * NT];  // tiles (c, m) of K^T K, then (m, n) of K^T V
+  {
+    f32x4 kk[NT], kv[NT];
+    gram_sums<D, HG>(k, v, base, ts, 0, N, sK, sV, kk, kv);
+    task_sum<D, HG>(reinterpret_cast<float*>(sK), kk, kv);
+    for (int c = 0; c < NT; ++c) {
+      acc[c] = kk[c];
+      acc[NT + c] = kv[c];
+    }
+  }
+  // (form_wstar's first barrier also ends every read of the tile buffers and task sums, which the
+  // read-out's buffers reuse)
+  bf16* sWop = reinterpret_cast<bf16*>(smem + L::kWop);
+  form_wstar<D, HG>(acc, wr, reinterpret_cast<bf16*>(smem + L::kWt), reinterpret_cast<bf16*>(smem + L::kWt + L::kWtB),
+                    sWop, scale, epochs, w_out ? w_out + ((long long)b * H + h0) * DD : nullptr);
+  readout_blocks<D, HG>(qb, sets, sWop, reinterpret_cast<bf16*>(smem + L::kQ + w * L::kBlockB),
+                        reinterpret_cast<bf16*>(smem + L::kO + w * L::kBlockB), o);
 }
 
 // ---------------------------------------------------------------- fp32 I/O, plain FMA
@@ -559,6 +694,11 @@ hipError_t launch_bf16(int B, int H, int N, int epochs, float eta, const void* q
   float* partial = static_cast<float*>(ws);
   const int items = groups * pl.splits;
   const float scale = eta / (float)N;
+  if (pl.splits == 1) {  // no split records: one launch (the workspace is not used)
+    hipLaunchKernelGGL((fb_fused_bf16<D, HG>), dim3(groups), dim3(kThreads), 0, st, (const bf16*)q,
+                       (const bf16*)k, (const bf16*)v, w0, w0s, H, N, scale, epochs, (bf16*)o, w_out);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((fb_partial_bf16<D, HG>), dim3(items), dim3(kThreads), 0, st, (const bf16*)k,
                      (const bf16*)v, w0, w0s, H, N, pl.splits, pl.tokens_per_split, partial);
   hipLaunchKernelGGL((fb_readout_bf16<D, HG>), dim3(items), dim3(kThreads), 0, st, (const bf16*)q,

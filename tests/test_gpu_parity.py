@@ -280,6 +280,39 @@ def test_fullbatch_split_plans(wl):
     assert np.abs(st[0] - ref_w).max() / np.abs(ref_w).max() <= BF16_TOL
 
 
+# One split per group (many groups of few tokens): the sums, W* and the read-out in one launch.
+FB_ONE_SPLIT = [
+    W["vit3s_fullbatch"].with_(B=50, N=256, seed=181),                      # D = 64: 4 full tiles, one split's most
+    W["hvit3t_stage1_fullbatch"].with_(B=256, N=500, seed=182),             # 2 heads of 32 a row, ragged last tile
+    W["hvit3t_stage1_fullbatch"].with_(B=90, N=300, H=3, seed=183),         # one head of 32 a group: 2 waves a task
+    W["hvit3t_stage1_fullbatch"].with_(B=256, N=260, H=4, D=16, seed=184),  # four heads of 16 a row
+    W["hvit3t_stage1_fullbatch"].with_(B=256, N=100, H=1, D=16, seed=185),  # one 16-wide head: 4 waves a task
+    W["hvit3t_stage1_fullbatch"].with_(B=128, N=40, H=2, D=16, seed=186),   # fewer groups, one partial tile
+]
+
+
+def fullbatch_splits(wl) -> int:
+    """Splits per head group of the bf16 full-batch plan, read off the workspace size (each split
+    of a group of hg heads records 2 hg d x d fp32 matrices)."""
+    hg = 64 // wl.D
+    while hg > 1 and wl.H % hg:
+        hg //= 2
+    groups = wl.B * (wl.H // hg)
+    ws = T().ttt_workspace_size(T().TTT_OP_FULLBATCH, T().TTT_BF16, wl.B, wl.H, wl.N, wl.D)
+    return ws // (groups * 2 * hg * wl.D * wl.D * 4)
+
+
+@pytest.mark.parametrize("wl", FB_ONE_SPLIT, ids=lambda w: f"B{w.B}N{w.N}H{w.H}D{w.D}")
+def test_fullbatch_one_split_plans(wl):
+    print(f"one-split full-batch B={wl.B} N={wl.N} H={wl.H} D={wl.D}", flush=True)
+    assert fullbatch_splits(wl) == 1
+    x = synth.make_inputs(wl)
+    out, st = run_gpu(x, want_state=True)
+    ref_o, ref_w = oracle_full(x)
+    assert slice_err(out, ref_o) <= BF16_TOL
+    assert np.abs(st[0] - ref_w).max() / np.abs(ref_w).max() <= BF16_TOL
+
+
 @pytest.mark.parametrize("wl", [W["ttt_mlp_causal_8k"].with_(B=1, N=64, H=2, seed=64),
                                 W["ttt_mlp_causal_8k"].with_(B=2, N=64, H=2, chunk=32, dtype="fp32", seed=69),
                                 W["ttt_mlp_causal_8k"].with_(B=1, N=64, H=1, D=32, Dh=192, dtype="fp32", seed=70)],
@@ -386,6 +419,7 @@ def test_eta_zero_reads_initial_state(op):
 
 
 @pytest.mark.parametrize("wl", [W["hvit3t_stage1_fullbatch"].with_(B=3, N=130, seed=81),
+                                W["hvit3t_stage1_fullbatch"].with_(B=128, N=64, seed=88),  # one split per group
                                 W["vittt_bidir_1280"].with_(B=2, N=128, seed=82),
                                 W["ttt_linear_causal_16k"].with_(B=3, N=64, H=2, seed=83)],
                          ids=lambda w: w.op)
@@ -574,6 +608,7 @@ EPOCH_CASES = [
     (W["fullbatch_tiny_fp32"].with_(B=2, N=300, H=3, D=32, seed=164), 4),    # fp32: 1e-4 bar
     (W["fullbatch_tiny_fp32"].with_(B=1, N=77, H=2, D=64, seed=165), 1),
     (W["hvit3t_stage1_fullbatch"], 3),                                       # full size
+    (W["vit3s_fullbatch"].with_(B=50, N=200, seed=166), 3),                  # one split per group (one launch)
 ]
 
 
