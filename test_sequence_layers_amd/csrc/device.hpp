@@ -105,4 +105,13 @@ __device__ __forceinline__ bf16x4 ld4_col(const bf16* p, int stride) {
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
 
+// A 16-byte store of a streamed output that the kernel does not read back, with the nontemporal
+// hint: it leaves the caches to the inputs and to the small records a later launch reads. Used where
+// a wave writes whole 128-byte rows (the full-batch read-out); for 8-byte pieces, and for the
+// chunked scans' O tiles, the hint measured slower.
+typedef unsigned u32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void st16_out(void* p, uint4 v) {
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4_nt, v), reinterpret_cast<u32x4_nt*>(p));
+}
+
 }  // namespace ttt

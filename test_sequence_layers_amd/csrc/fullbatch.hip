@@ -398,7 +398,7 @@ __device__ __forceinline__ void readout_blocks(const QBlocks<D, HG>& qb, typenam
     for (int u = 0; u < QB::PPL; ++u) {
       const int c = l + 64 * u, row = c / G::CPR;
       if (QB::valid(c) && t0 + row < qb.n1)
-        st16(o + qb.base + (t0 + row) * qb.ts + (c % G::CPR) * 8, ld16(myO + row * G::P + (c % G::CPR) * 8));
+        st16_out(o + qb.base + (t0 + row) * qb.ts + (c % G::CPR) * 8, ld16(myO + row * G::P + (c % G::CPR) * 8));
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   };
