@@ -113,5 +113,9 @@ typedef unsigned u32x4_nt __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void st16_out(void* p, uint4 v) {
   __builtin_nontemporal_store(__builtin_bit_cast(u32x4_nt, v), reinterpret_cast<u32x4_nt*>(p));
 }
+// A 16-byte load with the nontemporal hint, for input read once.
+__device__ __forceinline__ uint4 ld16_stream(const void* p) {
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(p)));
+}
 
 }  // namespace ttt

@@ -59,7 +59,11 @@ struct Geo {
 };
 
 // Register <-> LDS staging of one 64-token tile of a head group (rows past n1 read as zeros).
-template <class G>
+// STREAM: loads with the nontemporal hint (the forward's split-sum launch, which reads K and V once:
+// measured faster with the inputs in HBM and in the caches alike; the one-launch kernel, whose Q
+// loads are in flight beside them, and the backward's split sums were slower with it when the
+// inputs were cached).
+template <class G, bool STREAM = false>
 struct Stager {
   const bf16* src;
   long long base, ts;
@@ -70,7 +74,10 @@ struct Stager {
       uint4 val = make_uint4(0u, 0u, 0u, 0u);
       if (G::PIECES % kThreads == 0 || c < G::PIECES) {
         const int row = c / G::CPR, col = (c % G::CPR) * 8;
-        if (t0 + row < n1) val = ld16(src + base + (long long)(t0 + row) * ts + col);
+        if (t0 + row < n1) {
+          const bf16* p = src + base + (long long)(t0 + row) * ts + col;
+          val = STREAM ? ld16_stream(p) : ld16(p);
+        }
       }
       regs[i] = val;
     }
@@ -169,7 +176,7 @@ __device__ __forceinline__ int xcd_item(int i, int items) {
 // task split the 32-token steps. K^T K is symmetric, so the wave accumulates its column block m,
 // tiles (c, m) in accumulator layout, which are the A operands of row block m, k block c, in the
 // product with W0. The tiles stream through the double-buffered sK, sV ([2][kTile * P] each).
-template <int D, int HG>
+template <int D, int HG, bool STREAM>
 __device__ __forceinline__ void gram_sums(const bf16* __restrict__ k, const bf16* __restrict__ v,
                                           long long base, long long ts, int n0, int n1, bf16* sK,
                                           bf16* sV, f32x4 (&kk)[D / 16], f32x4 (&kv)[D / 16]) {
@@ -182,7 +189,7 @@ __device__ __forceinline__ void gram_sums(const bf16* __restrict__ k, const bf16
   const int w = wave_id(), l = lane_id();
   const int task = w % TASKS, tw = w / TASKS;
   const int hl = task / NT, m = task % NT;  // head within the group, row block
-  const Stager<G> stk{k, base, ts, n1}, stv{v, base, ts, n1};
+  const Stager<G, STREAM> stk{k, base, ts, n1}, stv{v, base, ts, n1};
 
   for (int c = 0; c < NT; ++c) kk[c] = kv[c] = zero4();
   constexpr int SETS = tile_sets(D);
@@ -199,8 +206,8 @@ __device__ __forceinline__ void gram_sums(const bf16* __restrict__ k, const bf16
   auto step = [&](int it, Regs& R) {
     bf16* bK = sK + (it & 1) * (kTile * G::P);
     bf16* bV = sV + (it & 1) * (kTile * G::P);
-    Stager<G>::store(bK, R.k);
-    Stager<G>::store(bV, R.v);
+    Stager<G, STREAM>::store(bK, R.k);
+    Stager<G, STREAM>::store(bV, R.v);
     if (it + SETS < ntiles) load(R, it + SETS);
     __syncthreads();
     const bf16* tK = bK + hl * D;
@@ -257,7 +264,7 @@ __device__ __forceinline__ void task_sum(float* sG, f32x4 (&kk)[D / 16], f32x4 (
 // 1. Gradient sums of one token split of one head group (gram_sums); the split's record holds,
 // per task (head, row block m), the accumulator tiles (c, m) of K^T K then (m, n) of K^T V, lane
 // by lane (16 bytes a lane, coalesced).
-template <int D, int HG>
+template <int D, int HG, bool STREAM>
 __global__ __launch_bounds__(kThreads, 4) void fb_partial_bf16(
     const bf16* __restrict__ k, const bf16* __restrict__ v, const float* __restrict__ w0,
     long long w0_bstride, int H, int N, int S, int tps, float* __restrict__ partial) {
@@ -279,7 +286,7 @@ __global__ __launch_bounds__(kThreads, 4) void fb_partial_bf16(
   const long long base = (long long)b * N * ts + (long long)h0 * D;
 
   f32x4 kk[NT], kv[NT];  // tiles (c, m) of K^T K and (m, n) of K^T V
-  gram_sums<D, HG>(k, v, base, ts, n0, n1, &sK[0][0], &sV[0][0], kk, kv);
+  gram_sums<D, HG, STREAM>(k, v, base, ts, n0, n1, &sK[0][0], &sV[0][0], kk, kv);
   task_sum<D, HG>(reinterpret_cast<float*>(&sK[0][0]), kk, kv);
   float* part = partial + ((long long)grp * S + s) * (2 * HG * D * D) + (long long)task * (2 * NT * 256);
   if (tw == 0)
@@ -520,7 +527,7 @@ __global__ __launch_bounds__(kThreads, 2) void fb_fused_bf16(
   f32x4 acc[2 * NT];  // tiles (c, m) of K^T K, then (m, n) of K^T V
   {
     f32x4 kk[NT], kv[NT];
-    gram_sums<D, HG>(k, v, base, ts, 0, N, sK, sV, kk, kv);
+    gram_sums<D, HG, false>(k, v, base, ts, 0, N, sK, sV, kk, kv);
     task_sum<D, HG>(reinterpret_cast<float*>(sK), kk, kv);
     for (int c = 0; c < NT; ++c) {
       acc[c] = kk[c];
@@ -699,7 +706,7 @@ hipError_t launch_bf16(int B, int H, int N, int epochs, float eta, const void* q
                        (const bf16*)k, (const bf16*)v, w0, w0s, H, N, scale, epochs, (bf16*)o, w_out);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((fb_partial_bf16<D, HG>), dim3(items), dim3(kThreads), 0, st, (const bf16*)k,
+  hipLaunchKernelGGL((fb_partial_bf16<D, HG, true>), dim3(items), dim3(kThreads), 0, st, (const bf16*)k,
                      (const bf16*)v, w0, w0s, H, N, pl.splits, pl.tokens_per_split, partial);
   hipLaunchKernelGGL((fb_readout_bf16<D, HG>), dim3(items), dim3(kThreads), 0, st, (const bf16*)q,
                      partial, w0, w0s, H, N, pl.splits, pl.tokens_per_split, scale, epochs, (bf16*)o,
@@ -949,9 +956,9 @@ hipError_t launch_bwd_bf16(int B, int H, int N, float eta, const void* q, const 
   float* rqd = rkv + rec;
   bf16* ops = reinterpret_cast<bf16*>(rqd + rec);
   const int items = groups * pl.splits;
-  hipLaunchKernelGGL((fb_partial_bf16<D, HG>), dim3(items), dim3(kThreads), 0, st, (const bf16*)k,
+  hipLaunchKernelGGL((fb_partial_bf16<D, HG, false>), dim3(items), dim3(kThreads), 0, st, (const bf16*)k,
                      (const bf16*)v, w0, w0s, H, N, pl.splits, pl.tokens_per_split, rkv);
-  hipLaunchKernelGGL((fb_partial_bf16<D, HG>), dim3(items), dim3(kThreads), 0, st, (const bf16*)q,
+  hipLaunchKernelGGL((fb_partial_bf16<D, HG, false>), dim3(items), dim3(kThreads), 0, st, (const bf16*)q,
                      (const bf16*)d_o, w0, w0s, H, N, pl.splits, pl.tokens_per_split, rqd);
   hipLaunchKernelGGL((fbb_finish<D, HG, true>), dim3(B * H), dim3(kThreads), 0, st, rkv, rqd, w0, w0s,
                      H, pl.splits, eta / (float)N, (void*)ops, d_w0);
