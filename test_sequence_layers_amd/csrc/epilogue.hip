@@ -9,7 +9,8 @@
 // 64 outputs, the contraction (K = 2C) in blocks of 64 through double-buffered LDS, one barrier a
 // block; the next block's pieces are loaded into registers while the current one is multiplied.
 // The matrix-core A operand is Wo (rows = outputs) and B the activations (columns = tokens), so
-// lane (r, g) ends with 4 adjacent outputs of token r: one 8-byte store. At the workloads' widths
+// lane (r, g) ends with 4 adjacent outputs of token r; the output tile is written out through LDS
+// as whole 128-byte rows. At the workloads' widths
 // (C = 64..192) the arithmetic intensity is about 50-100 flop/byte, below the ridge point: bound
 // by reading O, G, X and writing y. fp32: plain FMA, one thread per output element.
 #include "device.hpp"
@@ -92,14 +93,19 @@ __global__ __launch_bounds__(kEpThreads) void epilogue_bf16(
     if (kb + 1 < nkb) store(buf ^ 1);
     __syncthreads();
   }
-  // lane (r, g) of tile t: y[token m0 + 16t + r][outputs n0 + 16w + 4g .. + 3]
-  const int oc = n0 + 16 * w + 4 * g;
+  // lane (r, g) of tile t holds y[token m0 + 16t + r][outputs n0 + 16w + 4g .. + 3]. The 64 x 64 tile
+  // goes through LDS (sA[0], free after the loop's last barrier), so that y is written as whole
+  // rows: 16-byte pieces, 8 lanes to a token's 128 bytes, with the nontemporal hint.
+  const int oc = 16 * w + 4 * g;
   f32x4 bs = zero4();
   if (bias)
-    for (int j = 0; j < 4; ++j) bs[j] = bias[oc + j];
-  for (int t = 0; t < 4; ++t) {
-    const int tok = m0 + 16 * t + r;
-    if (tok < M) *reinterpret_cast<bf16x4*>(y + (long long)tok * Cout + oc) = to_bf16x4(acc[t] + bs);
+    for (int j = 0; j < 4; ++j) bs[j] = bias[n0 + oc + j];
+  bf16* sY = sA[0];
+  for (int t = 0; t < 4; ++t) *reinterpret_cast<bf16x4*>(&sY[(16 * t + r) * kEpP + oc]) = to_bf16x4(acc[t] + bs);
+  __syncthreads();
+  for (int u = 0; u < 2; ++u) {
+    const int p = tid + u * kEpThreads, row = p >> 3, c8 = (p & 7) * 8, tok = m0 + row;
+    if (tok < M) st16_out(y + (long long)tok * Cout + n0 + c8, ld16(&sY[row * kEpP + c8]));
   }
 }
 
