@@ -198,7 +198,10 @@ ttt_status ttt_backward_chunked_bidir(ttt_dtype dt, int B, int H, int N, int D, 
  * tokens of each batch element are an image in raster order (token i * width + j is pixel (i, j)).
  * w_out (nullable): fp32 [4, B, H, D, D]: raster forward end, raster reverse end, column forward
  * end, column reverse end. Workspace: ttt_workspace_size(TTT_OP_BIDIR2D, ..., N, D, 0, chunk) with
- * N = height * width (the inputs and output in column order, and the scans' workspace).
+ * N = height * width: for bf16 I/O the scans' own workspace (the column-order scan reads q, k, v in
+ * place and adds its output into o; null is accepted when the size is 0), for fp32 I/O also
+ * column-order copies of the inputs and output. The column-order sum is rounded once: o = bf16(raster
+ * result + column result), each term as the bidirectional scan rounds it.
  */
 ttt_status ttt_forward_chunked_bidir2d(ttt_dtype dt, int B, int H, int height, int width, int D,
                                        int chunk, float eta, const void* q, const void* k,

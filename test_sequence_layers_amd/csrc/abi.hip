@@ -179,8 +179,10 @@ size_t ttt_workspace_size(ttt_op op, ttt_dtype dt, int B, int H, int N, int D, i
       return round_up(ttt::chunked_workspace_bytes(op == TTT_OP_BIDIR, bf, B, H, N, D, chunk), 256);
     case TTT_OP_BIDIR2D: {
       if (!supported_chunk(chunk) || N % chunk != 0) return 0;
+      const size_t scan = round_up(ttt::chunked_workspace_bytes(true, bf, B, H, N, D, chunk), 256);
+      if (bf) return scan;  // bf16: the column-order scan reads and adds in place
       const size_t act = round_up((size_t)B * N * H * D * elem_size(dt), 256);
-      return 4 * act + round_up(ttt::chunked_workspace_bytes(true, bf, B, H, N, D, chunk), 256);
+      return 4 * act + scan;  // fp32: column-order copies of q, k, v and of the output, then the scans'
     }
     case TTT_OP_MLP:
       if (!ttt::mlp_supported(D, Dh, chunk) || N % chunk != 0) return 0;
@@ -317,13 +319,25 @@ ttt_status ttt_forward_chunked_bidir2d(ttt_dtype dt, int B, int H, int height, i
       return TTT_ERR_INVALID;
   }
   const size_t need = ttt_workspace_size(TTT_OP_BIDIR2D, dt, B, H, N, D, 0, chunk);
-  if (!workspace || workspace_bytes < need) return TTT_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return TTT_ERR_INVALID;
-  const Range rws = range_of(workspace, need);
-  if (overlaps(rws, rq) || overlaps(rws, rk) || overlaps(rws, rv) || overlaps(rws, rw0) ||
-      overlaps(rws, range_of(o, act)) || (w_out && overlaps(rws, range_of(w_out, 4 * dd * 4))))
-    return TTT_ERR_INVALID;
-  // Workspace: q, k, v and the output in column order, then the scans' own workspace.
+  if (need > 0) {  // (a bf16 call whose scans are one segment each needs none)
+    if (!workspace || workspace_bytes < need) return TTT_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return TTT_ERR_INVALID;
+    const Range rws = range_of(workspace, need);
+    if (overlaps(rws, rq) || overlaps(rws, rk) || overlaps(rws, rv) || overlaps(rws, rw0) ||
+        overlaps(rws, range_of(o, act)) || (w_out && overlaps(rws, range_of(w_out, 4 * dd * 4))))
+      return TTT_ERR_INVALID;
+  }
+  const bool bf = dt == TTT_BF16;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (bf) {  // the raster-order scan writes o, the column-order one reads in place and adds into o
+    hipError_t e = ttt::chunked_launch(true, true, B, H, N, D, chunk, eta, q, k, v, w0, w0_batch_stride, o,
+                                       w_out, workspace, s);
+    if (e == hipSuccess)
+      e = ttt::chunked_bidir_cols_launch(B, H, height, width, D, chunk, eta, q, k, v, w0, w0_batch_stride, o,
+                                         w_out ? w_out + 2 * dd : nullptr, workspace, s);
+    return from_hip(e);
+  }
+  // fp32 workspace: q, k, v and the output in column order, then the scans' own workspace.
   char* wsb = static_cast<char*>(workspace);
   const size_t actp = round_up(act, 256);
   void* qt = wsb;
@@ -331,8 +345,6 @@ ttt_status ttt_forward_chunked_bidir2d(ttt_dtype dt, int B, int H, int height, i
   void* vt = wsb + 2 * actp;
   void* ot = wsb + 3 * actp;
   void* scan_ws = wsb + 4 * actp;
-  const bool bf = dt == TTT_BF16;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
   const void* srcs[3] = {q, k, v};
   void* dsts[3] = {qt, kt, vt};
   hipError_t e = ttt::gather_columns_launch(bf, B, height, width, H * D, srcs, dsts, 3, s);

@@ -86,6 +86,43 @@ constexpr int kRevLdsBytes = 80 * 1024;
 template <int D>
 constexpr int max_seg_len() { return kRevLdsBytes / (D * D * 2); }
 
+// ---------------------------------------------------------------- column order of a token grid
+// The 2-D scan (Vision-TTT summary, "De Oplossing": the scanner also reads top to bottom) runs the
+// bidirectional scan a second time over the tokens of a height x width grid in column order:
+// position p' of that sequence is the raster token (p' mod height) * width + p' / height. The
+// column-order kernels read and write the raster tensors in place through this map. ColPos follows
+// one row of a chunk tile from chunk to chunk (p' moves by a fixed step, forward or back) with one
+// conditional wrap and no division.
+struct ColMap {
+  int hg, wg;
+};
+struct ColPos {
+  int i, j;  // grid row and column of the tracked token
+  __device__ __forceinline__ void init(int pp, ColMap m) {
+    pp = pp < 0 ? 0 : pp;
+    j = pp / m.hg;
+    i = pp - j * m.hg;
+  }
+  // p' += step (di = step mod hg, dj = step / hg), or p' -= step
+  __device__ __forceinline__ void fwd(int di, int dj, ColMap m) {
+    i += di;
+    j += dj;
+    if (i >= m.hg) {
+      i -= m.hg;
+      ++j;
+    }
+  }
+  __device__ __forceinline__ void back(int di, int dj, ColMap m) {
+    i -= di;
+    j -= dj;
+    if (i < 0) {
+      i += m.hg;
+      --j;
+    }
+  }
+  __device__ __forceinline__ long long token(ColMap m) const { return (long long)i * m.wg + j; }
+};
+
 // ---------------------------------------------------------------- staging with prefetch
 // The [CH x D] bf16 tiles of NTS tensors of one chunk move HBM -> registers -> LDS (row pitch P).
 // The workgroup's threads form G groups; group j holds the chunks whose step index is j mod G: it
@@ -93,7 +130,9 @@ constexpr int max_seg_len() { return kRevLdsBytes / (D * D * 2); }
 // step, so each load has G steps to arrive with one register set per thread. A thread's 16-byte
 // pieces sit at fixed offsets within a chunk tile, computed once; when a tile spans whole waves,
 // the tensor of a piece is the same across the wave, and choosing its base pointer is scalar work.
-template <int D, int CH, int NTH, int NTS, int G, int P>
+// COLS: the tile rows come from the column map instead (ChunkStager::track, load_cols): each piece
+// keeps its row's grid position for the next chunk its group loads.
+template <int D, int CH, int NTH, int NTS, int G, int P, bool COLS = false>
 struct ChunkStager {
   static_assert(NTH % G == 0 && NTS >= 1 && NTS <= 4, "staging geometry");
   static constexpr int CPR = D / 8;  // 16-byte pieces per row
@@ -105,6 +144,7 @@ struct ChunkStager {
   uint4 v[PER];
   int group;
   int sel[PER], goff[PER], loff[PER];
+  ColPos pos[COLS ? PER : 1];  // COLS: grid position of the piece's row in the group's next chunk
   __device__ __forceinline__ explicit ChunkStager(long long ts) : group(threadIdx.x / GT) {
     const int idx = threadIdx.x % GT;
     for (int i = 0; i < PER; ++i) {
@@ -117,6 +157,25 @@ struct ChunkStager {
   __device__ __forceinline__ bool mine(int step) const { return step % G == group; }
   __device__ __forceinline__ bool valid(int i) const {
     return PIECES % GT == 0 || (int)(threadIdx.x % GT) + i * GT < PIECES;
+  }
+  // COLS: start at chunk c of the column-order sequence (this thread's group's first load).
+  __device__ __forceinline__ void track(int c, ColMap m) {
+    for (int i = 0; i < PER; ++i) pos[i].init(c * CH + ((threadIdx.x % GT) + i * GT) % TILE / CPR, m);
+  }
+  // COLS: load the tracked chunk from the head base pointers t0 .. t3 (raster layout), then move
+  // every piece G chunks on (dir > 0) or back (dir < 0).
+  __device__ __forceinline__ void load_cols(const bf16* t0, const bf16* t1, const bf16* t2, const bf16* t3,
+                                            ColMap m, long long ts, int dir) {
+    const int di = (G * CH) % m.hg, dj = (G * CH) / m.hg;
+    for (int i = 0; i < PER; ++i) {
+      if (valid(i)) {
+        const bf16* src = sel[i] == 0 ? t0 : (sel[i] == 1 ? t1 : (sel[i] == 2 ? t2 : t3));
+        const int col = (((threadIdx.x % GT) + i * GT) % TILE % CPR) * 8;
+        v[i] = ld16(src + pos[i].token(m) * ts + col);
+      }
+      if (dir > 0) pos[i].fwd(di, dj, m);
+      else pos[i].back(di, dj, m);
+    }
   }
   // t0 .. t3: the chunk's first row in each tensor (unused ones may be null).
   __device__ __forceinline__ void load(const bf16* t0, const bf16* t1, const bf16* t2,
@@ -149,6 +208,38 @@ __device__ __forceinline__ void store_chunk(bf16* dst, const bf16* src, long lon
     st16(dst + row * ts + col, ld16_lds8(src + row * P + col));
   }
 }
+
+// The O tile of a column-order chunk (bf16 in LDS, row pitch P) added into the raster output, which
+// already holds the raster-order scan's result: o[token] = bf16(o[token] + tile), summed in fp32 and
+// rounded once. Each thread tracks the rows of its pieces (tid, tid + NTH, ...) from chunk to chunk;
+// the chunks are stored in order.
+template <int D, int CH, int P, int NTH>
+struct ColStore {
+  static constexpr int CPR = D / 8, PIECES = CH * CPR, PER = (PIECES + NTH - 1) / NTH;
+  ColPos pos[PER];
+  __device__ __forceinline__ static bool valid(int k) { return PIECES % NTH == 0 || (int)threadIdx.x + k * NTH < PIECES; }
+  __device__ __forceinline__ void track(int c, ColMap m) {
+    for (int k = 0; k < PER; ++k) pos[k].init(c * CH + ((int)threadIdx.x + k * NTH) / CPR, m);
+  }
+  __device__ __forceinline__ void add(bf16* o_head, const bf16* src, long long ts, ColMap m) {
+    const int di = CH % m.hg, dj = CH / m.hg;
+    for (int k = 0; k < PER; ++k) {
+      if (valid(k)) {
+        const int c = threadIdx.x + k * NTH, row = c / CPR, col = (c % CPR) * 8;
+        bf16* dst = o_head + pos[k].token(m) * ts + col;
+        const bf16x8 a = ld8(dst);
+        const bf16x8 b = __builtin_bit_cast(bf16x8, ld16_lds8(src + row * P + col));
+        f32x4 lo, hi;
+        for (int t = 0; t < 4; ++t) {
+          lo[t] = (float)a[t] + (float)b[t];
+          hi[t] = (float)a[4 + t] + (float)b[4 + t];
+        }
+        st16(dst, __builtin_bit_cast(uint4, cat8(to_bf16x4(lo), to_bf16x4(hi))));
+      }
+      pos[k].fwd(di, dj, m);
+    }
+  }
+};
 
 // ---------------------------------------------------------------- MFMA building blocks
 // B operand from a state held in C layout (tiles m = 2ks, 2ks + 1 cover features 32ks..32ks+31).
@@ -225,10 +316,10 @@ __device__ __forceinline__ void residuals(f32x4* E, const f32x4* W, const bf16* 
 }
 
 // ---------------------------------------------------------------- 1. compose
-template <int D, int CH, bool BIDIR>
+template <int D, int CH, bool BIDIR, bool COLS = false>
 __global__ __launch_bounds__(D / 8 * 64) void chunk_compose_bf16(
     const bf16* __restrict__ k, const bf16* __restrict__ v, int H, int N, float a, int S, int L,
-    float* __restrict__ comp) {
+    float* __restrict__ comp, ColMap cmap) {
   constexpr int P = lds_pitch<D>(), NT = D / 16, NP = CH / 16, NTH = 2 * NT * 64;
   constexpr long long DD = (long long)D * D;
   // Double-buffered chunk tiles: chunk c is staged while other waves may still read chunk c - 1,
@@ -253,18 +344,23 @@ __global__ __launch_bounds__(D / 8 * 64) void chunk_compose_bf16(
     }
 
   constexpr int G = stage_groups<CH>();
-  ChunkStager<D, CH, NTH, 2, G, P> st(ts);
+  ChunkStager<D, CH, NTH, 2, G, P, COLS> st(ts);
   const long long cs = (long long)CH * ts;  // elements between consecutive chunks
   const bf16* kn = k + head0 + lo * cs;     // chunk lo + j (j < G), then chunk c + G
   const bf16* vn = v + head0 + lo * cs;
+  if constexpr (COLS) st.track(lo + st.group, cmap);
+  auto load_next = [&]() {
+    if constexpr (COLS) st.load_cols(k + head0, v + head0, nullptr, nullptr, cmap, ts, 1);
+    else st.load(kn, vn, nullptr);
+  };
   for (int j = 0; j < G; ++j, kn += cs, vn += cs)
-    if (lo + j < hi && st.mine(j)) st.load(kn, vn, nullptr);
+    if (lo + j < hi && st.mine(j)) load_next();
   for (int c = lo; c < hi; ++c, kn += cs, vn += cs) {
     bf16* sK = sKb[(c - lo) & 1];
     bf16* sV = sVb[(c - lo) & 1];
     if (st.mine(c - lo)) {
       st.store(sK, sV, nullptr);
-      if (c + G < hi) st.load(kn, vn, nullptr);
+      if (c + G < hi) load_next();
     }
     __syncthreads();
     f32x4 Y[NP];
@@ -405,11 +501,11 @@ __global__ __launch_bounds__(64) void chunk_prefix(const float* __restrict__ w0,
 }
 
 // ---------------------------------------------------------------- 3. segment scan
-template <int D, int CH, int MODE>
+template <int D, int CH, int MODE, bool COLS = false>
 __global__ __launch_bounds__(D / 16 * 64) void chunk_scan_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ w0, long long w0_bstride, int H, int N, float a, int S, int L,
-    const float* __restrict__ win, bf16* __restrict__ o, float* __restrict__ w_out) {
+    const float* __restrict__ win, bf16* __restrict__ o, float* __restrict__ w_out, ColMap cmap) {
   constexpr int P = lds_pitch<D>();
   constexpr int NT = D / 16;   // waves = column tiles = row tiles
   constexpr int NP = CH / 16;  // 16-token tiles per chunk
@@ -468,11 +564,16 @@ __global__ __launch_bounds__(D / 16 * 64) void chunk_scan_bf16(
     // Reverse scan over the segment's chunks (last to first), keeping each W^r_c in LDS.
     entry(1, W);
     entry_done();
-    ChunkStager<D, CH, NTH, 2, G, P> sr(ts);
+    ChunkStager<D, CH, NTH, 2, G, P, COLS> sr(ts);
     const bf16* kn = kb + (hi - 1) * cs;  // chunk hi - 1 - j (j < G), then chunk c - G
     const bf16* vn = vb + (hi - 1) * cs;
+    if constexpr (COLS) sr.track(hi - 1 - sr.group, cmap);
+    auto load_next = [&]() {
+      if constexpr (COLS) sr.load_cols(kb, vb, nullptr, nullptr, cmap, ts, -1);
+      else sr.load(kn, vn, nullptr);
+    };
     for (int j = 0; j < G; ++j, kn -= cs, vn -= cs)
-      if (hi - 1 - j >= lo && sr.mine(j)) sr.load(kn, vn, nullptr);
+      if (hi - 1 - j >= lo && sr.mine(j)) load_next();
     for (int c = hi - 1; c >= lo; --c, kn -= cs, vn -= cs) {
       const int buf = NBUF == 2 ? (hi - 1 - c) & 1 : 0;
       bf16* sK = sKb[buf];
@@ -480,7 +581,7 @@ __global__ __launch_bounds__(D / 16 * 64) void chunk_scan_bf16(
       if (NBUF == 1) __syncthreads();
       if (sr.mine(hi - 1 - c)) {
         sr.store(sK, sV, nullptr);
-        if (c - G >= lo) sr.load(kn, vn, nullptr);
+        if (c - G >= lo) load_next();
       }
       __syncthreads();
       f32x4 E[NP];
@@ -496,12 +597,19 @@ __global__ __launch_bounds__(D / 16 * 64) void chunk_scan_bf16(
   if (MODE == kBidir) __syncthreads();
   entry(0, W);
   entry_done();
-  ChunkStager<D, CH, NTH, 3, G, P> sf(ts);
+  ChunkStager<D, CH, NTH, 3, G, P, COLS> sf(ts);
   const bf16* kn = kb + lo * cs;  // chunk lo + j (j < G), then chunk c + G
   const bf16* vn = vb + lo * cs;
   const bf16* qn = qb + lo * cs;
+  if constexpr (COLS) sf.track(lo + sf.group, cmap);
+  ColStore<D, CH, P, NTH> ost;  // COLS: the O tiles' rows (chunks lo, lo + 1, ...)
+  if constexpr (COLS) ost.track(lo, cmap);
+  auto load_next = [&]() {
+    if constexpr (COLS) sf.load_cols(kb, vb, qb, nullptr, cmap, ts, 1);
+    else sf.load(kn, vn, qn);
+  };
   for (int j = 0; j < G; ++j, kn += cs, vn += cs, qn += cs)
-    if (lo + j < hi && sf.mine(j)) sf.load(kn, vn, qn);
+    if (lo + j < hi && sf.mine(j)) load_next();
   for (int c = lo; c < hi; ++c, kn += cs, vn += cs, qn += cs) {
     const long long tok0 = head0 + (long long)c * CH * ts;
     const int buf = NBUF == 2 ? (c - lo) & 1 : 0;
@@ -512,10 +620,13 @@ __global__ __launch_bounds__(D / 16 * 64) void chunk_scan_bf16(
     if (NBUF == 1) __syncthreads();
     if (sf.mine(c - lo)) {
       sf.store(sK, sV, sQ);
-      if (c + G < hi) sf.load(kn, vn, qn);
+      if (c + G < hi) load_next();
     }
     __syncthreads();
-    if (NBUF == 2 && c > lo) store_chunk<D, CH, P, NTH>(o + tok0 - CH * ts, sOb[buf ^ 1], ts);
+    if (NBUF == 2 && c > lo) {
+      if constexpr (COLS) ost.add(o + head0, sOb[buf ^ 1], ts, cmap);
+      else store_chunk<D, CH, P, NTH>(o + tok0 - CH * ts, sOb[buf ^ 1], ts);
+    }
 
     f32x4 E[NP];
     residuals<D, NP, P>(E, W, sK, sV, w, r, g, l);
@@ -560,12 +671,14 @@ __global__ __launch_bounds__(D / 16 * 64) void chunk_scan_bf16(
     }
     if (NBUF == 1) {
       __syncthreads();
-      store_chunk<D, CH, P, NTH>(o + tok0, sO, ts);
+      if constexpr (COLS) ost.add(o + head0, sO, ts, cmap);
+      else store_chunk<D, CH, P, NTH>(o + tok0, sO, ts);
     }
   }
   if (NBUF == 2) {  // the last chunk's O tile
     __syncthreads();
-    store_chunk<D, CH, P, NTH>(o + head0 + (long long)(hi - 1) * CH * ts, sOb[(hi - 1 - lo) & 1], ts);
+    if constexpr (COLS) ost.add(o + head0, sOb[(hi - 1 - lo) & 1], ts, cmap);
+    else store_chunk<D, CH, P, NTH>(o + head0 + (long long)(hi - 1) * CH * ts, sOb[(hi - 1 - lo) & 1], ts);
   }
   if (s == S - 1 && w_out) save(w_out + bh * DD, W);
 }
@@ -835,36 +948,46 @@ ChunkPlan chunk_plan(bool bidir, int B, int H, int N, int D, int CH) {
   }
 }
 
+// cols: the bidirectional scan over the column order of a token grid, added into o (null: raster order).
 template <int D, int CH>
 hipError_t launch_bf16(bool bidir, int B, int H, int N, float a, const void* q, const void* k,
                        const void* v, const float* w0, long long w0s, void* o, float* w_out,
-                       void* ws, hipStream_t st) {
+                       void* ws, hipStream_t st, const ColMap* cols) {
   const int BH = B * H;
   const ChunkPlan pl = chunk_plan(bidir, B, H, N, D, CH);
   const long long DD = (long long)D * D;
   float* comp = static_cast<float*>(ws);
   float* win = comp + (long long)BH * pl.S * (bidir ? 2 : 1) * kMapFloats<D>;
+  const ColMap cm = cols ? *cols : ColMap{1, 1};
   if (pl.S > 1) {
     if (bidir) {
-      hipLaunchKernelGGL((chunk_compose_bf16<D, CH, true>), dim3(pl.S, BH), dim3(D / 8 * 64), 0, st,
-                         (const bf16*)k, (const bf16*)v, H, N, a, pl.S, pl.L, comp);
+      if (cols)
+        hipLaunchKernelGGL((chunk_compose_bf16<D, CH, true, true>), dim3(pl.S, BH), dim3(D / 8 * 64), 0, st,
+                           (const bf16*)k, (const bf16*)v, H, N, a, pl.S, pl.L, comp, cm);
+      else
+        hipLaunchKernelGGL((chunk_compose_bf16<D, CH, true>), dim3(pl.S, BH), dim3(D / 8 * 64), 0, st,
+                           (const bf16*)k, (const bf16*)v, H, N, a, pl.S, pl.L, comp, cm);
       hipLaunchKernelGGL((chunk_prefix<D, 2>), dim3(BH, 2, D / 16), dim3(64), 0, st, w0, w0s, 2, H,
                          pl.S, comp, win);
     } else {
       hipLaunchKernelGGL((chunk_compose_bf16<D, CH, false>), dim3(pl.S, BH), dim3(D / 8 * 64), 0,
-                         st, (const bf16*)k, (const bf16*)v, H, N, a, pl.S, pl.L, comp);
+                         st, (const bf16*)k, (const bf16*)v, H, N, a, pl.S, pl.L, comp, cm);
       hipLaunchKernelGGL((chunk_prefix<D, 1>), dim3(BH, 1, D / 16), dim3(64), 0, st, w0, w0s, 1,
                          H, pl.S, comp, win);
     }
   }
-  if (bidir) {
+  if (bidir && cols) {
+    hipLaunchKernelGGL((chunk_scan_bf16<D, CH, kBidir, true>), dim3(pl.S, BH), dim3(D / 16 * 64), 0, st,
+                       (const bf16*)q, (const bf16*)k, (const bf16*)v, w0, w0s, H, N, a, pl.S,
+                       pl.L, win, (bf16*)o, w_out, cm);
+  } else if (bidir) {
     hipLaunchKernelGGL((chunk_scan_bf16<D, CH, kBidir>), dim3(pl.S, BH), dim3(D / 16 * 64), 0, st,
                        (const bf16*)q, (const bf16*)k, (const bf16*)v, w0, w0s, H, N, a, pl.S,
-                       pl.L, win, (bf16*)o, w_out);
+                       pl.L, win, (bf16*)o, w_out, cm);
   } else {
     hipLaunchKernelGGL((chunk_scan_bf16<D, CH, kCausal>), dim3(pl.S, BH), dim3(D / 16 * 64), 0,
                        st, (const bf16*)q, (const bf16*)k, (const bf16*)v, w0, w0s, H, N, a, pl.S,
-                       pl.L, win, (bf16*)o, w_out);
+                       pl.L, win, (bf16*)o, w_out, cm);
   }
   return hipGetLastError();
 }
@@ -906,11 +1029,11 @@ hipError_t launch_f32(bool bidir, int B, int H, int N, int CH, float a, const vo
 template <int D>
 hipError_t launch_bf16_d(bool bidir, int B, int H, int N, int CH, float a, const void* q,
                          const void* k, const void* v, const float* w0, long long w0s, void* o,
-                         float* w_out, void* ws, hipStream_t st) {
+                         float* w_out, void* ws, hipStream_t st, const ColMap* cols = nullptr) {
   switch (CH) {
-    case 16: return launch_bf16<D, 16>(bidir, B, H, N, a, q, k, v, w0, w0s, o, w_out, ws, st);
-    case 32: return launch_bf16<D, 32>(bidir, B, H, N, a, q, k, v, w0, w0s, o, w_out, ws, st);
-    case 64: return launch_bf16<D, 64>(bidir, B, H, N, a, q, k, v, w0, w0s, o, w_out, ws, st);
+    case 16: return launch_bf16<D, 16>(bidir, B, H, N, a, q, k, v, w0, w0s, o, w_out, ws, st, cols);
+    case 32: return launch_bf16<D, 32>(bidir, B, H, N, a, q, k, v, w0, w0s, o, w_out, ws, st, cols);
+    case 64: return launch_bf16<D, 64>(bidir, B, H, N, a, q, k, v, w0, w0s, o, w_out, ws, st, cols);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1621,6 +1744,20 @@ hipError_t chunked_launch(bool bidir, bool bf16_io, int B, int H, int N, int D, 
     case 16: return launch_f32<16>(bidir, B, H, N, chunk, a, q, k, v, w0, w0s, o, w_out, ws, st);
     case 32: return launch_f32<32>(bidir, B, H, N, chunk, a, q, k, v, w0, w0s, o, w_out, ws, st);
     case 64: return launch_f32<64>(bidir, B, H, N, chunk, a, q, k, v, w0, w0s, o, w_out, ws, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t chunked_bidir_cols_launch(int B, int H, int Hg, int Wg, int D, int chunk, float eta,
+                                     const void* q, const void* k, const void* v, const float* w0,
+                                     long long w0s, void* o, float* w_out, void* ws, hipStream_t st) {
+  const float a = eta / (float)chunk;
+  const int N = Hg * Wg;
+  const ColMap cm{Hg, Wg};
+  switch (D) {
+    case 16: return launch_bf16_d<16>(true, B, H, N, chunk, a, q, k, v, w0, w0s, o, w_out, ws, st, &cm);
+    case 32: return launch_bf16_d<32>(true, B, H, N, chunk, a, q, k, v, w0, w0s, o, w_out, ws, st, &cm);
+    case 64: return launch_bf16_d<64>(true, B, H, N, chunk, a, q, k, v, w0, w0s, o, w_out, ws, st, &cm);
     default: return hipErrorInvalidValue;
   }
 }

@@ -31,6 +31,12 @@ size_t chunked_workspace_bytes(bool bidir, bool bf16_io, int B, int H, int N, in
 hipError_t chunked_launch(bool bidir, bool bf16_io, int B, int H, int N, int D, int chunk,
                           float eta, const void* q, const void* k, const void* v, const float* w0,
                           long long w0_bstride, void* o, float* w_out, void* ws, hipStream_t st);
+// bf16 bidirectional scan over the column order of a Hg x Wg token grid, reading q, k, v in place
+// (raster layout) and adding its output into o (which holds the raster-order scan's); the workspace
+// is chunked_workspace_bytes(true, true, B, H, Hg * Wg, D, chunk).
+hipError_t chunked_bidir_cols_launch(int B, int H, int Hg, int Wg, int D, int chunk, float eta,
+                                     const void* q, const void* k, const void* v, const float* w0,
+                                     long long w0_bstride, void* o, float* w_out, void* ws, hipStream_t st);
 size_t chunked_bwd_workspace_bytes(bool bidir, bool bf16_io, int B, int H, int N, int D, int chunk);
 hipError_t chunked_bwd_launch(bool bidir, bool bf16_io, int B, int H, int N, int D, int chunk,
                               float eta, const void* q, const void* k, const void* v,

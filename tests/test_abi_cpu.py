@@ -44,7 +44,8 @@ def test_block_epilogue_validation():
 
 def test_bidir2d_validation_rejects_before_launch():
     lib = T.load_library()
-    call = lambda hg=8, wg=8, chunk=16, ws=5, wsb=1 << 30, o=4, wout=None: lib.ttt_forward_chunked_bidir2d(  # noqa: E731
+    # 80 x 80 tokens in chunks of 64: several segments per scan, so that a workspace is required
+    call = lambda hg=80, wg=80, chunk=64, ws=5, wsb=1 << 30, o=4, wout=None: lib.ttt_forward_chunked_bidir2d(  # noqa: E731
         T.TTT_BF16, 1, 1, hg, wg, 64, chunk, 1.0, _p(0), _p(1), _p(2), _p(3), 0, None if o is None else _p(o),
         None if wout is None else _p(wout), None if ws is None else _p(ws), wsb, None)
     assert call(hg=0) == 1
@@ -54,8 +55,12 @@ def test_bidir2d_validation_rejects_before_launch():
     assert call(ws=None) == 3
     assert call(wsb=64) == 3
     assert call(wout=1) == 1              # end states overlap k
-    assert T.ttt_workspace_size(T.TTT_OP_BIDIR2D, T.TTT_BF16, 8, 3, 6400, 64, 0, 64) > \
-        4 * 8 * 6400 * 3 * 64 * 2
+    # bf16: the scans' workspace only (the column-order scan reads and adds in place); fp32 also holds
+    # column-order copies of q, k, v and of the output
+    for dt, es in ((T.TTT_BF16, 2), (T.TTT_F32, 4)):
+        scan = T.ttt_workspace_size(T.TTT_OP_BIDIR, dt, 8, 3, 6400, 64, 0, 64)
+        two_d = T.ttt_workspace_size(T.TTT_OP_BIDIR2D, dt, 8, 3, 6400, 64, 0, 64)
+        assert two_d == scan if dt == T.TTT_BF16 else two_d >= 4 * 8 * 6400 * 3 * 64 * es + scan
 
 
 def test_backward_validation_rejects_before_launch():

@@ -174,7 +174,9 @@ def _occ_table(src, name):
 def test_chunk_plan_occupancy_tables_match_the_compiled_kernels(tmp_path):
     """The chunked scans size their segment plan from fixed tables of the waves per SIMD that each
     compiled compose / scan kernel sustains (so that the plan does not depend on the device a call
-    runs on). Those tables must equal the compiler's occupancy report for the current sources."""
+    runs on). Those tables must equal the compiler's occupancy report for the current sources. The
+    column-order instances of the bidirectional kernels (the 2-D scan) run on the same plan, so they
+    must sustain at least the table's occupancy."""
     src_path = os.path.join(B.CSRC, "chunked.hip")
     src = open(src_path).read()
     compose, scan = _occ_table(src, "kComposeOcc"), _occ_table(src, "kScanOcc")
@@ -182,7 +184,7 @@ def test_chunk_plan_occupancy_tables_match_the_compiled_kernels(tmp_path):
            "-o", str(tmp_path / "c.o"), "-Rpass-analysis=kernel-resource-usage"]
     p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     assert p.returncode == 0, p.stdout[-2000:]
-    found = {}
+    found, cols = {}, {}
     kernel = None
     for line in p.stdout.splitlines():
         m = re.search(r"Function Name: (\S+)", line)
@@ -191,11 +193,17 @@ def test_chunk_plan_occupancy_tables_match_the_compiled_kernels(tmp_path):
             continue
         m = re.search(r"Occupancy \[waves/SIMD\]: (\d+)", line)
         if m and kernel:
-            k = re.search(r"(chunk_compose_bf16|chunk_scan_bf16)ILi(\d+)ELi(\d+)EL([bi])(\d)E", kernel)
+            k = re.search(r"(chunk_compose_bf16|chunk_scan_bf16)ILi(\d+)ELi(\d+)EL([bi])(\d)E(Lb1E)?", kernel)
             if k:
-                found[(k.group(1), int(k.group(2)), int(k.group(3)), int(k.group(5)))] = int(m.group(1))
+                key = (k.group(1), int(k.group(2)), int(k.group(3)), int(k.group(5)))
+                (cols if k.group(6) else found)[key] = int(m.group(1))
     assert len(found) == 36, sorted(found)
+    assert len(cols) == 18 and all(key[3] == 1 for key in cols), sorted(cols)
     for (kind, d, c, bidir), occ in found.items():
         table = compose if kind == "chunk_compose_bf16" else scan
         assert table[(d, c, bidir)] == occ, f"{kind}<{d}, {c}, {'bidir' if bidir else 'causal'}>: table " \
                                              f"{table[(d, c, bidir)]}, compiler {occ}"
+    for (kind, d, c, bidir), occ in cols.items():
+        table = compose if kind == "chunk_compose_bf16" else scan
+        assert occ >= table[(d, c, bidir)], f"{kind}<{d}, {c}, bidir, column order>: table " \
+                                            f"{table[(d, c, bidir)]}, compiler {occ}"

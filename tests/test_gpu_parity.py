@@ -639,6 +639,9 @@ BIDIR2D_CASES = [
     (W["vittt_bidir_1280"].with_(B=1, N=24 * 40, H=2, D=32, chunk=16, seed=182), 24, 40),
     (W["vittt_bidir_1280"].with_(B=2, N=12 * 16, H=1, D=16, chunk=32, seed=183), 12, 16),  # chunks span columns
     (W["vittt_bidir_1280"].with_(B=1, N=8 * 16, H=2, D=64, chunk=16, dtype="fp32", seed=184), 8, 16),
+    (W["vittt_bidir_1280"].with_(B=1, N=48 * 84, seed=185), 48, 84),       # 63 chunks: ragged last segment
+    (W["vittt_bidir_1280"].with_(B=1, N=1 * 128, H=1, seed=186), 1, 128),  # one row: column order = raster
+    (W["vittt_bidir_1280"].with_(B=2, N=40 * 64, H=2, chunk=16, seed=187), 40, 64),  # b = 16, many segments
 ]
 
 
