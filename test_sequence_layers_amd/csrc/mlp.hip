@@ -517,6 +517,246 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
 }
 
 
+// ---------------------------------------------------------------- wide inner model, matrix cores
+// The layer for bf16 I/O, D = 64, b = 16 and hidden widths of 2 to 4 blocks of 256 units (ViT^3
+// review, design-space study: a wider inner model). One workgroup of 8 waves per (batch, head), as
+// above, but the state (W1 and W2, 2 D Dh fp32 values) no longer fits in registers: it lives in the
+// workspace in fp32, in layouts chosen so that each lane moves its MFMA operands and update tiles as
+// 16-byte pieces: W1^T [Dh][D], W2 [Dh][D] and a second copy W2^T [D][Dh] (the operand layouts of
+// X2 W2 and of E W2^T differ). In each block of 256 hidden units wave w owns units [32w, 32w + 32),
+// and every state element is loaded and stored by the same lane (initial copy, operands, updates,
+// final copy), so the waves share no state. Per chunk, with the start state (W1, W2) and the read-
+// out in the start-state dual form (one state per chunk step):
+//   forward, per block:  Z1 = K W1; X2 = GELU(Z1) and GELU'(Z1) kept in registers; the Z2^T partial
+//                        accumulates W2^T X2^T over the blocks;
+//   cross-wave sum:      -a E = a (V - Z2)  (LDS, fixed wave order);
+//   per block:           -a D1 = ((-a E) W2^T) * GELU'(Z1);
+//                        Z1q^T = W1^T Q^T + (-a D1)^T tril(Q K^T)^T, X2q = GELU(Z1q),
+//                        O^T partial += W2^T X2q^T + (-a E)^T tril(X2q X2^T)^T;
+//   cross-wave sum:      O;
+//   update, per block:   W1 += K^T (-a D1), W2 += X2^T (-a E) (both copies).
+// tril keeps t' <= t. All products take bf16 operands (fp32's exponent range: no range checks) and
+// accumulate in fp32; GELU is the exact erf form in fp32.
+constexpr int kWideBlock = 256;  // hidden units per block (8 waves x 32)
+
+__device__ __forceinline__ f32x4 ld4f(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ void st4f(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
+
+template <int NB>
+__global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_wide(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const float* __restrict__ w1, const float* __restrict__ w2, long long wbs, int H, int N,
+    float a, bf16* __restrict__ o, float* __restrict__ w1_out, float* __restrict__ w2_out,
+    float* __restrict__ ws) {
+  constexpr int Dh = NB * kWideBlock;
+  __shared__ __align__(16) bf16 sKVQ[2][3][kCh * kP];
+  __shared__ __align__(16) bf16 sE[kCh * kP];                 // -a E [token][out]
+  __shared__ __align__(16) f32x4 sRed[kWaves * kSlots * 64];  // lane-private partial tiles
+
+  const int bh = blockIdx.x, b = bh / H, h = bh % H;
+  const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
+  const long long ts = (long long)H * kD;
+  const float* W1g = w1 + b * wbs + (long long)h * kD * Dh;  // [D][Dh]
+  const float* W2g = w2 + b * wbs + (long long)h * Dh * kD;  // [Dh][D]
+  float* W1T = ws + (long long)bh * 3 * kD * Dh;             // [Dh][D]
+  float* W2s = W1T + kD * Dh;                                // [Dh][D]
+  float* W2T = W2s + kD * Dh;                                // [D][Dh]
+
+  // The lane's state tiles (the same elements its operand loads and updates touch):
+  //   W1 [feature 16m + 4g + j][unit u0 + 16n + r]  at W1T[(u0 + 16n + r) D + 16m + 4g + j]
+  //   W2 [unit u0 + 16n + 4g + j][out 16o + r]      at W2T[(16o + r) Dh + u0 + 16n + 4g + j]
+  //   W2 [unit u0 + 16n + r][out 16o + 4g + j]      at W2s[(u0 + 16n + r) D + 16o + 4g + j]
+  for (int nb = 0; nb < NB; ++nb) {
+    const int u0 = nb * kWideBlock + kHw * w;
+    for (int n = 0; n < kNh; ++n) {
+      const int u = u0 + 16 * n + r;
+      for (int m = 0; m < 4; ++m) {
+        f32x4 t1, t2;
+        for (int j = 0; j < 4; ++j) {
+          t1[j] = W1g[(16 * m + 4 * g + j) * Dh + u];
+          t2[j] = W2g[(u0 + 16 * n + 4 * g + j) * kD + 16 * m + r];
+        }
+        st4f(W1T + (long long)u * kD + 16 * m + 4 * g, t1);
+        st4f(W2T + (long long)(16 * m + r) * Dh + u0 + 16 * n + 4 * g, t2);
+        st4f(W2s + (long long)u * kD + 16 * m + 4 * g, ld4f(W2g + (long long)u * kD + 16 * m + 4 * g));
+      }
+    }
+  }
+  const bf16x4 ident = identity_b(r, g);
+
+  const int C = N / kCh;
+  const long long head0 = (long long)b * N * ts + (long long)h * kD;
+  // Staging: threads 0..383 each move one 16-byte piece of K, V or Q (16 rows x 8 pieces each), one
+  // chunk ahead through a register.
+  const int t = threadIdx.x;
+  const int prow = (t & 127) >> 3, pcol = (t & 7) * 8, which = t >> 7;
+  const bf16* psrc = (t < 128 ? k : (t < 256 ? v : q)) + head0 + prow * ts + pcol;
+  if (t < 384) st16_lds8(&sKVQ[0][which][prow * kP + pcol], ld16(psrc));
+  __syncthreads();
+
+  for (int c = 0; c < C; ++c) {
+    const int cb = c & 1;
+    uint4 pf = make_uint4(0u, 0u, 0u, 0u);
+    if (t < 384 && c + 1 < C) pf = ld16(psrc + (long long)(c + 1) * kCh * ts);
+    const bf16* sK = sKVQ[cb][0];
+    const bf16* sV = sKVQ[cb][1];
+    const bf16* sQ = sKVQ[cb][2];
+
+    // ---------------- forward
+    bf16x4 x2b[NB][kNh];  // X2 [token 4g + j][unit 16n + r]
+    bf16x8 x2t[NB];       // X2^T as a B operand (k = units, n = token)
+    f32x4 gpr[NB][kNh];   // GELU'(Z1), same layout as X2
+    f32x4 zacc[4];        // Z2^T partial [out][token] over this wave's units
+    for (int o2 = 0; o2 < 4; ++o2) zacc[o2] = zero4();
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int u0 = nb * kWideBlock + kHw * w;
+      for (int n = 0; n < kNh; ++n) {
+        const float* p = W1T + (long long)(u0 + 16 * n + r) * kD + 4 * g;
+        f32x4 z = zero4();
+        for (int ks = 0; ks < 2; ++ks) {
+          const bf16* pk = &sK[r * kP + 32 * ks + 4 * g];
+          z = mma32(cat8(ld4(pk), ld4(pk + 16)), cat_tiles(ld4f(p + 32 * ks), ld4f(p + 32 * ks + 16)), z);
+        }
+        f32x4 xf, gp;
+        for (int j = 0; j < 4; ++j) {
+          const float x = z[j], cdf = cdf_lib(x);
+          xf[j] = x * cdf;
+          gp[j] = fmaf(x, __builtin_amdgcn_exp2f(fmaf(x * x, kNegHalfLog2e, kLog2InvSqrt2Pi)), cdf);
+        }
+        x2b[nb][n] = to_bf16x4(xf);
+        gpr[nb][n] = gp;
+      }
+      f32x4 xt[kNh];
+      for (int n = 0; n < kNh; ++n) xt[n] = mma16(x2b[nb][n], ident, zero4());  // [unit][token]
+      x2t[nb] = cat_tiles(xt[0], xt[1]);
+      for (int o2 = 0; o2 < 4; ++o2) {
+        const float* p = W2T + (long long)(16 * o2 + r) * Dh + u0 + 4 * g;
+        zacc[o2] = mma32(cat_tiles(ld4f(p), ld4f(p + 16)), x2t[nb], zacc[o2]);
+      }
+    }
+    for (int o2 = 0; o2 < 4; ++o2) sRed[(w * kSlots + o2) * 64 + l] = zacc[o2];
+    __syncthreads();
+    if (w < 4) {  // E^T tile w = Z2^T - V^T, stored as -a E [token][out]
+      f32x4 pt[kWaves];
+      for (int ww = 0; ww < kWaves; ++ww) pt[ww] = sRed[(ww * kSlots + w) * 64 + l];
+      const bf16x4 vv = ld4(&sV[r * kP + 16 * w + 4 * g]);
+      f32x4 s = pt[0];
+      for (int ww = 1; ww < kWaves; ++ww) s = s + pt[ww];
+      f32x4 e;
+      for (int j = 0; j < 4; ++j) e[j] = a * ((float)vv[j] - s[j]);
+      *reinterpret_cast<bf16x4*>(&sE[r * kP + 16 * w + 4 * g]) = to_bf16x4(e);
+    }
+    __syncthreads();
+
+    // ---------------- backward and read-out
+    bf16x8 ea[2];  // -a E rows (k = outputs)
+    for (int ko = 0; ko < 2; ++ko) {
+      const bf16* pe = &sE[r * kP + 32 * ko + 4 * g];
+      ea[ko] = cat8(ld4(pe), ld4(pe + 16));
+    }
+    bf16x4 et[4];  // (-a E)^T tiles: lane (r, g) holds -a E[token 4g + j][out 16o + r]
+    for (int o2 = 0; o2 < 4; ++o2) et[o2] = tile_tr(&sE[16 * o2], kP, l);
+    // M[t'][t] = k_t' . q_t, kept for t' <= t
+    f32x4 mt = zero4();
+    for (int ks = 0; ks < 2; ++ks)
+      mt = mma32(cat8(ld4(&sK[r * kP + 32 * ks + 4 * g]), ld4(&sK[r * kP + 32 * ks + 16 + 4 * g])),
+                 cat8(ld4(&sQ[r * kP + 32 * ks + 4 * g]), ld4(&sQ[r * kP + 32 * ks + 16 + 4 * g])), mt);
+    for (int j = 0; j < 4; ++j) mt[j] = 4 * g + j <= r ? mt[j] : 0.f;
+    const bf16x4 mb = to_bf16x4(mt);
+    bf16x4 d1b[NB][kNh];  // -a D1 [token][unit]
+    f32x4 oacc[4];        // O^T partial [out][token]
+    for (int o2 = 0; o2 < 4; ++o2) oacc[o2] = zero4();
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int u0 = nb * kWideBlock + kHw * w;
+      f32x4 zq[kNh];
+      for (int n = 0; n < kNh; ++n) {
+        // -a dX2 = (-a E) W2^T: B = W2 [k = out][n = unit]
+        const float* p2 = W2s + (long long)(u0 + 16 * n + r) * kD + 4 * g;
+        f32x4 acc = zero4();
+        for (int ko = 0; ko < 2; ++ko)
+          acc = mma32(ea[ko], cat_tiles(ld4f(p2 + 32 * ko), ld4f(p2 + 32 * ko + 16)), acc);
+        f32x4 d1;
+        for (int j = 0; j < 4; ++j) d1[j] = acc[j] * gpr[nb][n][j];
+        d1b[nb][n] = to_bf16x4(d1);
+        // Z1q^T = W1^T Q^T + (-a D1)^T M: A = W1 tiles as W1^T (rows = units), B = Q rows; the
+        // correction as a 16x16x32 product with a zero upper k half (same-shape chain)
+        const float* p1 = W1T + (long long)(u0 + 16 * n + r) * kD + 4 * g;
+        f32x4 z = zero4();
+        for (int ks = 0; ks < 2; ++ks) {
+          const bf16* pq = &sQ[r * kP + 32 * ks + 4 * g];
+          z = mma32(cat_tiles(ld4f(p1 + 32 * ks), ld4f(p1 + 32 * ks + 16)), cat8(ld4(pq), ld4(pq + 16)), z);
+        }
+        zq[n] = mma32(cat8(d1b[nb][n], bf16x4{}), cat8(mb, bf16x4{}), z);  // [unit][token]
+      }
+      bf16x4 xq[kNh];
+      for (int n = 0; n < kNh; ++n) {
+        f32x4 x;
+        for (int j = 0; j < 4; ++j) x[j] = zq[n][j] * cdf_lib(zq[n][j]);
+        xq[n] = to_bf16x4(x);
+      }
+      const bf16x8 x2q = cat8(xq[0], xq[1]);  // B operand (k = units, n = token)
+      f32x4 n2 = mma32(x2t[nb], x2q, zero4());  // [t'][t] = sum over the units of X2[t'] X2q[t]
+      for (int j = 0; j < 4; ++j) n2[j] = 4 * g + j <= r ? n2[j] : 0.f;
+      const bf16x4 n2b = to_bf16x4(n2);
+      for (int o2 = 0; o2 < 4; ++o2) {
+        const float* p = W2T + (long long)(16 * o2 + r) * Dh + u0 + 4 * g;
+        oacc[o2] = mma32(cat_tiles(ld4f(p), ld4f(p + 16)), x2q, oacc[o2]);
+        oacc[o2] = mma32(cat8(et[o2], bf16x4{}), cat8(n2b, bf16x4{}), oacc[o2]);
+      }
+    }
+    for (int o2 = 0; o2 < 4; ++o2) sRed[(w * kSlots + 4 + o2) * 64 + l] = oacc[o2];
+    __syncthreads();
+    if (w >= 4) {  // O^T tile w - 4 = sum of the waves' shares
+      const int o4 = w - 4;
+      f32x4 pt[kWaves];
+      for (int ww = 0; ww < kWaves; ++ww) pt[ww] = sRed[(ww * kSlots + 4 + o4) * 64 + l];
+      f32x4 s = pt[0];
+      for (int ww = 1; ww < kWaves; ++ww) s = s + pt[ww];
+      const long long tok = head0 + (long long)c * kCh * ts;
+      *reinterpret_cast<bf16x4*>(o + tok + r * ts + 16 * o4 + 4 * g) = to_bf16x4(s);
+    }
+
+    // ---------------- update (lane-private state tiles)
+    bf16x4 kt[4];  // K^T tiles: lane (r, g) holds K[token 4g + j][feature 16m + r]
+    for (int m = 0; m < 4; ++m) kt[m] = tile_tr(&sK[16 * m], kP, l);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int u0 = nb * kWideBlock + kHw * w;
+      for (int n = 0; n < kNh; ++n) {
+        float* p1 = W1T + (long long)(u0 + 16 * n + r) * kD + 4 * g;
+        for (int m = 0; m < 4; ++m) st4f(p1 + 16 * m, mma16(kt[m], d1b[nb][n], ld4f(p1 + 16 * m)));
+        for (int o2 = 0; o2 < 4; ++o2) {
+          float* pa = W2T + (long long)(16 * o2 + r) * Dh + u0 + 16 * n + 4 * g;
+          st4f(pa, mma16(x2b[nb][n], et[o2], ld4f(pa)));
+          float* pb = W2s + (long long)(u0 + 16 * n + r) * kD + 16 * o2 + 4 * g;
+          st4f(pb, mma16(et[o2], x2b[nb][n], ld4f(pb)));
+        }
+      }
+    }
+    if (t < 384 && c + 1 < C) st16_lds8(&sKVQ[cb ^ 1][which][prow * kP + pcol], pf);
+    __syncthreads();
+  }
+
+  // End states from the lane's own tiles.
+  for (int nb = 0; nb < NB; ++nb) {
+    const int u0 = nb * kWideBlock + kHw * w;
+    for (int n = 0; n < kNh; ++n) {
+      const int u = u0 + 16 * n + r;
+      for (int m = 0; m < 4; ++m) {
+        if (w1_out) {
+          const f32x4 t1 = ld4f(W1T + (long long)u * kD + 16 * m + 4 * g);
+          for (int j = 0; j < 4; ++j) w1_out[(long long)bh * kD * Dh + (16 * m + 4 * g + j) * Dh + u] = t1[j];
+        }
+        if (w2_out)
+          st4f(w2_out + (long long)bh * Dh * kD + (long long)u * kD + 16 * m + 4 * g,
+               ld4f(W2s + (long long)u * kD + 16 * m + 4 * g));
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- any size, fp32 arithmetic
 // The same layer for every other supported size (D in {16, 32, 64}, Dh a multiple of 64 up to
 // 1024, b in {16, 32, 64}) and for fp32 I/O, in plain fp32 FMA arithmetic (the exact erf GELU of
@@ -751,6 +991,10 @@ void launch_generic(int BH, int H, int N, int D, int Dh, int CH, float a, const 
 bool mlp_fast_path(bool bf16_io, int D, int Dh, int chunk) {
   return bf16_io && D == kD && Dh == kDh && chunk == kCh;
 }
+// The matrix-core kernel with the state in the workspace: 2 to 4 blocks of 256 hidden units.
+bool mlp_wide_path(bool bf16_io, int D, int Dh, int chunk) {
+  return bf16_io && D == kD && chunk == kCh && Dh % kWideBlock == 0 && Dh >= 2 * kWideBlock && Dh <= 4 * kWideBlock;
+}
 
 bool mlp_supported(int D, int Dh, int chunk) {
   if (D != 16 && D != 32 && D != 64) return false;
@@ -761,6 +1005,7 @@ bool mlp_supported(int D, int Dh, int chunk) {
 // Fast path: one flag per (batch, head) chain. Otherwise the state and intermediates per chain.
 size_t mlp_workspace_bytes(bool bf16_io, int B, int H, int, int D, int Dh, int chunk) {
   if (mlp_fast_path(bf16_io, D, Dh, chunk)) return (size_t)B * H * sizeof(int);
+  if (mlp_wide_path(bf16_io, D, Dh, chunk)) return (size_t)B * H * 3 * (size_t)D * Dh * sizeof(float);
   return (size_t)B * H * (2 * (size_t)D * Dh + 4 * (size_t)chunk * Dh) * sizeof(float);
 }
 
@@ -769,6 +1014,17 @@ hipError_t mlp_launch(bool bf16_io, int B, int H, int N, int D, int Dh, int chun
                       const float* w2, long long wbs, void* o, float* w1_out, float* w2_out,
                       void* ws, hipStream_t st) {
   const float a = eta / (float)chunk;
+  if (mlp_wide_path(bf16_io, D, Dh, chunk)) {
+    const int nb = Dh / kWideBlock;
+    auto go = [&](auto kern) {
+      hipLaunchKernelGGL(kern, dim3(B * H), dim3(kWaves * 64), 0, st, (const bf16*)q, (const bf16*)k,
+                         (const bf16*)v, w1, w2, wbs, H, N, a, (bf16*)o, w1_out, w2_out, static_cast<float*>(ws));
+    };
+    if (nb == 2) go(mlp_fwd_wide<2>);
+    else if (nb == 3) go(mlp_fwd_wide<3>);
+    else go(mlp_fwd_wide<4>);
+    return hipGetLastError();
+  }
   if (!mlp_fast_path(bf16_io, D, Dh, chunk)) {
     if (!mlp_supported(D, Dh, chunk)) return hipErrorInvalidValue;
     if (bf16_io)

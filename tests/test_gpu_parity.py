@@ -313,6 +313,50 @@ def test_fullbatch_one_split_plans(wl):
     assert np.abs(st[0] - ref_w).max() / np.abs(ref_w).max() <= BF16_TOL
 
 
+# The wider inner model (hidden widths of 2 to 4 blocks of 256 units, bf16, D = 64, b = 16) runs on
+# the matrix-core kernel whose fp32 state lives in the workspace.
+WIDE_MLP = [
+    W["ttt_mlp_causal_8k"].with_(B=1, N=48, H=2, Dh=512, seed=191),       # 3 chunks
+    W["ttt_mlp_causal_8k"].with_(B=2, N=80, H=1, Dh=768, seed=192),       # 5 chunks
+    W["ttt_mlp_causal_8k"].with_(B=1, N=16, H=1, Dh=1024, seed=193),      # one chunk
+    W["ttt_mlp_causal_8k"].with_(B=2, N=96, H=3, Dh=1024, seed=194),      # 6 chunks, several chains
+]
+
+
+@pytest.mark.parametrize("wl", WIDE_MLP, ids=lambda w: f"B{w.B}N{w.N}H{w.H}Dh{w.Dh}")
+def test_wide_mlp_parity_and_end_states(wl):
+    print(f"wide mlp B={wl.B} N={wl.N} H={wl.H} Dh={wl.Dh}", flush=True)
+    x = synth.make_inputs(wl)
+    got, s1, s2, _ = run_mlp(x, want_state=True)
+    ref_o, r1, r2 = oracle_full(x)
+    assert report(f"wide mlp Dh={wl.Dh}", got, ref_o) <= BF16_TOL
+    assert np.abs(s1 - r1).max() / np.abs(r1).max() <= BF16_TOL
+    assert np.abs(s2 - r2).max() / np.abs(r2).max() <= BF16_TOL
+
+
+def test_wide_mlp_per_batch_states():
+    wl = W["ttt_mlp_causal_8k"].with_(B=2, N=64, H=2, Dh=512, seed=195)
+    x = synth.make_inputs(wl)
+    rs = np.random.default_rng(9)
+    w1 = (rs.standard_normal((wl.B, wl.H, wl.D, wl.Dh)) * 0.02).astype(np.float32)
+    w2 = (rs.standard_normal((wl.B, wl.H, wl.Dh, wl.D)) * 0.02).astype(np.float32)
+    got = run_mlp(x, w1=w1, w2=w2)[0]
+    ref = O.mlp_causal(x.q64, x.k64, x.v64, w1, w2, wl.eta, wl.chunk)[0]
+    assert report("wide mlp per-batch states", got, ref) <= BF16_TOL
+
+
+def test_wide_mlp_bench_shape_every_head():
+    """The wide-MLP bench leg's shape (1 x 1024 tokens x 12 heads, Dh = 1024, its seed), every chain."""
+    from oracle_pool import mlp_causal_sliced
+
+    wl = W["ttt_mlp_causal_8k"].with_(B=1, N=1024, H=12, Dh=1024, seed=4545)
+    print(f"wide mlp bench shape: B={wl.B} N={wl.N} H={wl.H} Dh={wl.Dh}", flush=True)
+    x = synth.make_inputs(wl)
+    got = run_mlp(x)[0]
+    ref = mlp_causal_sliced(x.q64, x.k64, x.v64, x.w1, x.w2, wl.eta, wl.chunk, heads_per_task=1)
+    assert report("wide mlp bench shape", got, ref) <= BF16_TOL
+
+
 @pytest.mark.parametrize("wl", [W["ttt_mlp_causal_8k"].with_(B=1, N=64, H=2, seed=64),
                                 W["ttt_mlp_causal_8k"].with_(B=2, N=64, H=2, chunk=32, dtype="fp32", seed=69),
                                 W["ttt_mlp_causal_8k"].with_(B=1, N=64, H=1, D=32, Dh=192, dtype="fp32", seed=70)],
