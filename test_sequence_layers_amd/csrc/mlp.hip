@@ -536,8 +536,24 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
 //   cross-wave sum:      O;
 //   update, per block:   W1 += K^T (-a D1), W2 += X2^T (-a E) (both copies).
 // tril keeps t' <= t. All products take bf16 operands (fp32's exponent range: no range checks) and
-// accumulate in fp32; GELU is the exact erf form in fp32.
+// accumulate in fp32; GELU is the erf form in fp32 (cdf_as: erf within 1.5e-7).
 constexpr int kWideBlock = 256;  // hidden units per block (8 waves x 32)
+
+// GELU and GELU' in fp32 without the library erf (whose range branches and long polynomials would
+// dominate this kernel's instruction count): erf by Abramowitz and Stegun, Handbook of Mathematical
+// Functions, formula 7.1.26, erf(u) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) e^(-u^2) with
+// t = 1 / (1 + p u), u >= 0 (absolute error at most 1.5e-7), extended as an odd function. With
+// u = |x| / sqrt 2 the factor e^(-u^2) = e^(-x^2 / 2) also gives the normal density of
+// GELU'(x) = Phi(x) + x phi(x). One exp2, one reciprocal, no branch.
+constexpr float kAsP = 0.3275911f, kAsA1 = 0.254829592f, kAsA2 = -0.284496736f, kAsA3 = 1.421413741f,
+                kAsA4 = -1.453152027f, kAsA5 = 1.061405429f;
+constexpr float kInvSqrt2Pi = 0.39894228040143267794f;
+__device__ __forceinline__ float cdf_as(float x, float& e) {  // Phi(x); e = e^(-x^2 / 2)
+  e = __builtin_amdgcn_exp2f(x * x * kNegHalfLog2e);
+  const float t = __builtin_amdgcn_rcpf(fmaf(kAsP, fabsf(x) * kInvSqrt2, 1.f));
+  const float poly = t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, kAsA5, kAsA4), kAsA3), kAsA2), kAsA1);
+  return 0.5f + copysignf(0.5f * fmaf(-poly, e, 1.f), x);
+}
 
 __device__ __forceinline__ f32x4 ld4f(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 __device__ __forceinline__ void st4f(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
@@ -620,9 +636,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_wide(
         }
         f32x4 xf, gp;
         for (int j = 0; j < 4; ++j) {
-          const float x = z[j], cdf = cdf_lib(x);
+          float e;
+          const float x = z[j], cdf = cdf_as(x, e);
           xf[j] = x * cdf;
-          gp[j] = fmaf(x, __builtin_amdgcn_exp2f(fmaf(x * x, kNegHalfLog2e, kLog2InvSqrt2Pi)), cdf);
+          gp[j] = fmaf(x * e, kInvSqrt2Pi, cdf);
         }
         x2b[nb][n] = to_bf16x4(xf);
         gpr[nb][n] = gp;
@@ -693,7 +710,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_wide(
       bf16x4 xq[kNh];
       for (int n = 0; n < kNh; ++n) {
         f32x4 x;
-        for (int j = 0; j < 4; ++j) x[j] = zq[n][j] * cdf_lib(zq[n][j]);
+        for (int j = 0; j < 4; ++j) {
+          float e;
+          x[j] = zq[n][j] * cdf_as(zq[n][j], e);
+        }
         xq[n] = to_bf16x4(x);
       }
       const bf16x8 x2q = cat8(xq[0], xq[1]);  // B operand (k = units, n = token)

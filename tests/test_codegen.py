@@ -207,3 +207,34 @@ def test_chunk_plan_occupancy_tables_match_the_compiled_kernels(tmp_path):
         table = compose if kind == "chunk_compose_bf16" else scan
         assert occ >= table[(d, c, bidir)], f"{kind}<{d}, {c}, bidir, column order>: table " \
                                             f"{table[(d, c, bidir)]}, compiler {occ}"
+
+
+def _mlp_as_constants():
+    src = open(os.path.join(B.CSRC, "mlp.hip")).read()
+    names = ["kAsP", "kAsA1", "kAsA2", "kAsA3", "kAsA4", "kAsA5"]
+    vals = {n: float(m.group(1)) for n in names for m in [re.search(n + r"\s*=\s*([-+0-9.eE]+)f", src)] if m}
+    assert sorted(vals) == sorted(names), "Abramowitz-Stegun constants not found in mlp.hip"
+    return [vals[n] for n in names]
+
+
+def test_mlp_wide_gelu_erf_approximation():
+    """The wide TTT-MLP kernel's GELU and GELU' (cdf_as): erf by Abramowitz and Stegun 7.1.26 with the
+    kernel's constants, in fp32 like the kernel (exp2 and the reciprocal rounded to fp32), against
+    scipy's normal CDF and density: GELU within 3e-7 relative to max(1, |x|), GELU' within 3e-7,
+    over |x| <= 12 (the published bound on erf is 1.5e-7)."""
+    import numpy as np
+    from scipy.special import ndtr
+
+    p, a1, a2, a3, a4, a5 = [np.float32(c) for c in _mlp_as_constants()]
+    f = np.float32
+    x = np.linspace(-12.0, 12.0, 2000001).astype(f)
+    e = np.exp2(x * x * f(-0.72134752044448170368)).astype(f)
+    t = (f(1) / (p * (np.abs(x) * f(0.70710678118654752440)) + f(1))).astype(f)
+    poly = t * (a1 + t * (a2 + t * (a3 + t * (a4 + t * a5))))
+    cdf = (f(0.5) + np.copysign(f(0.5) * (f(1) - poly * e), x)).astype(f)
+    gelu = (x * cdf).astype(np.float64)
+    slope = (x * e * f(0.39894228040143267794) + cdf).astype(np.float64)
+    xd = x.astype(np.float64)
+    phi = np.exp(-xd * xd / 2) / np.sqrt(2 * np.pi)
+    assert np.max(np.abs(gelu - xd * ndtr(xd)) / np.maximum(1.0, np.abs(xd))) < 3e-7
+    assert np.max(np.abs(slope - (ndtr(xd) + xd * phi))) < 3e-7
