@@ -219,8 +219,10 @@ ttt_status ttt_forward_chunked_bidir2d(ttt_dtype dt, int B, int H, int height, i
  * multiple of 4); it applies to both w1_0 and w2_0, which hold D*Dh elements per head.
  * w1_out / w2_out (nullable): fp32 [B, H, D, Dh] / [B, H, Dh, D] end states.
  * Sizes: D in {16, 32, 64}, Dh a multiple of 64 in [64, 1024], chunk in {16, 32, 64}. bf16 I/O with
- * (D, Dh, chunk) = (64, 256, 16) runs on the matrix cores with the state held in registers; every
- * other size, and fp32 I/O, runs in plain fp32 arithmetic with the state in the workspace.
+ * (D, Dh, chunk) = (64, 256, 16) runs on the matrix cores with the state held in registers; bf16
+ * I/O with D = 64, chunk = 16 and Dh = 512, 768 or 1024 runs on the matrix cores with the fp32 state
+ * in the workspace (bf16 operands, fp32 accumulation); every other size, and fp32 I/O, runs in
+ * plain fp32 arithmetic with the state in the workspace.
  * Operand ranges (bf16 I/O, (D, Dh, chunk) = (64, 256, 16)): the products on the W2 side take
  * fp16 operands while the hidden pre-activations stay at least 2^-10 in magnitude (per lane of a
  * wave and chunk, unless all zero) and either within sqrt 2 or with GELU outputs within 32, the W2
