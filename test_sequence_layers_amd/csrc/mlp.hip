@@ -240,16 +240,18 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
 
   const int C = N / kCh;
   const long long head0 = (long long)b * N * ts + (long long)h * kD;
-  // Staging: threads 0..383 each move one 16-byte piece of K, V or Q (16 rows x 8 pieces each).
-  const int t = threadIdx.x;
-  const int prow = (t & 127) >> 3, pcol = (t & 7) * 8, which = t >> 7;
-  const bf16* psrc = (t < 128 ? k : (t < 256 ? v : q)) + head0 + prow * ts + pcol;
-  uint4 pfA = make_uint4(0u, 0u, 0u, 0u), pfB = make_uint4(0u, 0u, 0u, 0u);
-  if (t < 384) {
-    st16_lds8(&sKVQ[0][which][prow * kP + pcol], ld16(psrc));
-    if (C > 1) st16_lds8(&sKVQ[1][which][prow * kP + pcol], ld16(psrc + kCh * ts));
-    if (C > 2) pfB = ld16(psrc + 2 * kCh * ts);
-  }
+  // Staging: every thread moves one 16-byte piece of K, V or Q per chunk (16 rows x 8 pieces each);
+  // threads 384..511 repeat the Q pieces of threads 256..383 (same source, same LDS address, same
+  // value). Chunk indices past the end are clamped to the last chunk. So every wave issues the same
+  // loads on every step, and the compiler's wait before a staged piece's LDS write counts only the
+  // memory operations issued after its load: no wait drains the loads in flight or the O stores.
+  const int t = threadIdx.x, u = t < 384 ? t : t - 128;
+  const int prow = (u & 127) >> 3, pcol = (u & 7) * 8, which = u >> 7;
+  const bf16* psrc = (u < 128 ? k : (u < 256 ? v : q)) + head0 + prow * ts + pcol;
+  bf16* const pdst = &sKVQ[0][which][prow * kP + pcol];
+  auto chunk_src = [&](int cc) { return psrc + (long long)min(cc, C - 1) * kCh * ts; };
+  st16_lds8(pdst, ld16(psrc));
+  uint4 pfA = ld16(chunk_src(1)), pfB = ld16(chunk_src(2));  // chunks 1 and 2
   __syncthreads();
 
   bf16x4 d1p[kNh];  // -a D1 of the previous chunk, [token][hidden] tiles
@@ -257,12 +259,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
   for (int n = 0; n < kNh; ++n) d1p[n] = bf16x4{};
   x2tp = x8{};
 
-  // One chunk step: forward of chunk c, read-out of chunk c - 1. pf_cur holds chunk c + 2 (loaded
-  // one step earlier); chunk c + 3 is loaded into pf_next.
-  auto step = [&](const int c, uint4& pf_next, const uint4& pf_cur, auto rd_tag, auto fwd_tag) {
+  // One chunk step: forward of chunk c, read-out of chunk c - 1. pf holds chunk c + 1 (loaded two
+  // steps earlier); at the end of phase 1 it goes to its ring slot and is reloaded with chunk c + 3.
+  auto step = [&](const int c, uint4& pf, auto rd_tag, auto fwd_tag) {
     constexpr bool rd = decltype(rd_tag)::value;    // read-out of chunk c - 1
     constexpr bool fwd = decltype(fwd_tag)::value;  // forward of chunk c
-    if (t < 384 && c + 3 < C) pf_next = ld16(psrc + (long long)(c + 3) * kCh * ts);
     const bf16* sK = sKVQ[c % kRing][0];
     const bf16* sV = sKVQ[c % kRing][1];
     const bf16* sKp = sKVQ[(c + kRing - 1) % kRing][0];  // chunk c - 1
@@ -409,6 +410,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
         bad |= wave_out_of_range(wm, 0x1p-10f, 0x1p15f);
       }
     }
+    // Chunk c + 1 into its slot, which no wave reads in this step (slots c and c - 1 are in use;
+    // past the end the slot receives a repeat of the last chunk, which no step reads).
+    st16_lds8(pdst + ((c + 1) % kRing) * (3 * kCh * kP), pf);
+    pf = ld16(chunk_src(c + 3));
     __syncthreads();
 
     // ---------------- phase 2: cross-wave sums (fixed wave order)
@@ -467,23 +472,22 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
         }
       }
     }
-    if (t < 384 && c + 2 < C) st16_lds8(&sKVQ[(c + 2) % kRing][which][prow * kP + pcol], pf_cur);
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
-  // Step 0 has no read-out, step C no forward; the steps between have both (two per trip: the
-  // register sets swap roles).
-  if (C > 0) step(0, pfA, pfB, F_{}, T_{});
+  // Step 0 has no read-out, step C no forward; the steps between have both (two per trip: even
+  // steps stage from pfA, odd ones from pfB).
+  step(0, pfA, F_{}, T_{});
   int c = 1;
   for (; c + 1 < C; c += 2) {
-    step(c, pfB, pfA, T_{}, T_{});
-    step(c + 1, pfA, pfB, T_{}, T_{});
+    step(c, pfB, T_{}, T_{});
+    step(c + 1, pfA, T_{}, T_{});
   }
   if (c < C) {
-    step(c, pfB, pfA, T_{}, T_{});
-    step(c + 1, pfA, pfB, T_{}, F_{});
+    step(c, pfB, T_{}, T_{});
+    step(c + 1, pfA, T_{}, F_{});
   } else {
-    step(c, pfB, pfA, T_{}, F_{});
+    step(c, pfB, T_{}, F_{});
   }
 
   const long long bhl = bh;
