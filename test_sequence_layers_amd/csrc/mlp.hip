@@ -195,27 +195,32 @@ __device__ __forceinline__ void st16_lds8(bf16* p, uint4 v) {
   reinterpret_cast<uint2*>(p)[1] = make_uint2(v.z, v.w);
 }
 
-// F16: first launch (fp16 operands on the W2 side, range checks; writes flags[bh] = 1 when a check
-// failed, else 0). !F16: recomputation with bf16 operands of the chains whose flag is set.
+// The workgroup's shared memory, used by both passes of a chain.
+struct MlpLds {
+  bf16 kvq[kRing][3][kCh * kP];     // K, V, Q staging ring
+  unsigned short e[2][kCh * kP];    // -a E [token][out], fp16 or bf16 bits
+  f32x4 red[kWaves * kSlots * 64];  // lane-private partial tiles
+  int bad;
+};
+
+// One (b, h) chain. F16: fp16 operands on the W2 side with range checks; returns true (the same in
+// every thread) when a check failed. !F16: bf16 operands, no checks; returns false.
 template <bool F16>
-__global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
+__device__ __forceinline__ bool mlp_chain(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ w1, const float* __restrict__ w2, long long wbs, int H, int N,
     float a, bf16* __restrict__ o, float* __restrict__ w1_out, float* __restrict__ w2_out,
-    int* __restrict__ flags) {
+    MlpLds& lds) {
   using S = W2Side<F16>;
   using x4 = typename S::x4;
   using x8 = typename S::x8;
   using GpT = typename std::conditional<F16, f16x4, f32x4>::type;  // GELU'(Z1) tiles
-  __shared__ __align__(16) bf16 sKVQ[kRing][3][kCh * kP];
-  __shared__ __align__(16) typename S::elem sE[2][kCh * kP];  // -a E [token][out]
-  __shared__ __align__(16) f32x4 sRed[kWaves * kSlots * 64];  // lane-private partial tiles
-  __shared__ int sBad;
+  auto& sKVQ = lds.kvq;
+  auto sE = reinterpret_cast<typename S::elem(*)[kCh * kP]>(lds.e);
+  f32x4* const sRed = lds.red;
+  int& sBad = lds.bad;
 
   const int bh = blockIdx.x, b = bh / H, h = bh % H;
-  if constexpr (!F16) {
-    if (flags[bh] == 0) return;  // this chain's fp16 result stands
-  }
   const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
   const long long ts = (long long)H * kD;
   const float* W1g = w1 + b * wbs + (long long)h * kD * kDh;
@@ -516,7 +521,34 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
     bad |= wave_out_of_range(wm, 0x1p-10f, 0x1p15f) || __any(!(sm <= 3.0e38f));
     if (bad && l == 0) sBad = 1;  // (every writer stores the same value)
     __syncthreads();
-    if (threadIdx.x == 0) flags[bh] = sBad;
+    return sBad != 0;
+  }
+  return false;
+}
+
+// The bf16 pass as a call of its own: compiled apart from the kernel, it leaves the fp16 pass's code
+// as it is when that pass is the whole kernel.
+__device__ __noinline__ void mlp_chain_bf16(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const float* __restrict__ w1, const float* __restrict__ w2, long long wbs, int H, int N,
+    float a, bf16* __restrict__ o, float* __restrict__ w1_out, float* __restrict__ w2_out,
+    MlpLds& lds) {
+  mlp_chain<false>(q, k, v, w1, w2, wbs, H, N, a, o, w1_out, w2_out, lds);
+}
+
+// One workgroup per (b, h) chain: the fp16 pass, and only when one of its range checks failed, the
+// bf16 pass over the same chain (its outputs replace the first pass's). flags[bh] records which.
+__global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const float* __restrict__ w1, const float* __restrict__ w2, long long wbs, int H, int N,
+    float a, bf16* __restrict__ o, float* __restrict__ w1_out, float* __restrict__ w2_out,
+    int* __restrict__ flags) {
+  __shared__ __align__(16) MlpLds lds;
+  const bool bad = mlp_chain<true>(q, k, v, w1, w2, wbs, H, N, a, o, w1_out, w2_out, lds);
+  if (threadIdx.x == 0) flags[blockIdx.x] = bad ? 1 : 0;
+  if (bad) {
+    __syncthreads();  // every wave is done with the first pass's shared memory
+    mlp_chain_bf16(q, k, v, w1, w2, wbs, H, N, a, o, w1_out, w2_out, lds);
   }
 }
 
@@ -1059,13 +1091,9 @@ hipError_t mlp_launch(bool bf16_io, int B, int H, int N, int D, int Dh, int chun
                             static_cast<float*>(ws), st);
     return hipGetLastError();
   }
-  int* flags = static_cast<int*>(ws);
-  hipLaunchKernelGGL(mlp_fwd_bf16<true>, dim3(B * H), dim3(kWaves * 64), 0, st, (const bf16*)q,
+  hipLaunchKernelGGL(mlp_fwd_bf16, dim3(B * H), dim3(kWaves * 64), 0, st, (const bf16*)q,
                      (const bf16*)k, (const bf16*)v, w1, w2, wbs, H, N, a, (bf16*)o, w1_out, w2_out,
-                     flags);
-  hipLaunchKernelGGL(mlp_fwd_bf16<false>, dim3(B * H), dim3(kWaves * 64), 0, st, (const bf16*)q,
-                     (const bf16*)k, (const bf16*)v, w1, w2, wbs, H, N, a, (bf16*)o, w1_out, w2_out,
-                     flags);
+                     static_cast<int*>(ws));
   return hipGetLastError();
 }
 
