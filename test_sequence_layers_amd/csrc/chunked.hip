@@ -316,11 +316,15 @@ __device__ __forceinline__ void residuals(f32x4* E, const f32x4* W, const bf16* 
 }
 
 // ---------------------------------------------------------------- 1. compose
+// Wave w owns column tile w of both halves of the state [P | R]: the P tile (from I, no V) and the
+// R tile (from 0, with V). The two tiles share their operands of K (the rows for the residuals, the
+// transpose reads for the update), so each wave reads the chunk's K tile from LDS once for both,
+// and the workgroup has D / 16 waves.
 template <int D, int CH, bool BIDIR, bool COLS = false>
-__global__ __launch_bounds__(D / 8 * 64) void chunk_compose_bf16(
+__global__ __launch_bounds__(D / 16 * 64) void chunk_compose_bf16(
     const bf16* __restrict__ k, const bf16* __restrict__ v, int H, int N, float a, int S, int L,
     float* __restrict__ comp, ColMap cmap) {
-  constexpr int P = lds_pitch<D>(), NT = D / 16, NP = CH / 16, NTH = 2 * NT * 64;
+  constexpr int P = lds_pitch<D>(), NT = D / 16, NP = CH / 16, NTH = NT * 64;
   constexpr long long DD = (long long)D * D;
   // Double-buffered chunk tiles: chunk c is staged while other waves may still read chunk c - 1,
   // so one barrier per chunk suffices.
@@ -328,18 +332,17 @@ __global__ __launch_bounds__(D / 8 * 64) void chunk_compose_bf16(
   __shared__ __align__(16) bf16 sVb[2][CH * P];
 
   const int s = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H;
-  const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
-  const bool pwave = w < NT;        // P columns (init I, no V); else R columns (init 0, V)
-  const int col = pwave ? w : w - NT;
+  const int col = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
   const int C = N / CH;
   const int lo = s * L, hi = min(C, lo + L);
   const long long ts = (long long)H * D;
   const long long head0 = (long long)b * N * ts + (long long)h * D;
 
-  f32x4 X[NT], RR[NT];
+  f32x4 XP[NT], XR[NT], RR[NT];
   for (int m = 0; m < NT; ++m)
     for (int j = 0; j < 4; ++j) {
-      X[m][j] = (pwave && 16 * m + 4 * g + j == 16 * col + r) ? 1.f : 0.f;
+      XP[m][j] = 16 * m + 4 * g + j == 16 * col + r ? 1.f : 0.f;
+      XR[m][j] = 0.f;
       RR[m][j] = 0.f;
     }
 
@@ -363,24 +366,59 @@ __global__ __launch_bounds__(D / 8 * 64) void chunk_compose_bf16(
       if (c + G < hi) load_next();
     }
     __syncthreads();
-    f32x4 Y[NP];
-    residuals<D, NP, P>(Y, X, sK, sV, pwave ? -1 : col, r, g, l);
-    if constexpr (BIDIR) {
-      if (pwave) {  // R_rev[16col + i][16n + .] += a (K_c P_{c-1})^T V_c
-        if constexpr (NP == 1) {
-          const bf16x4 ya = to_bf16x4_scaled(Y[0], a);
-          for (int n = 0; n < NT; ++n) RR[n] = mma16(ya, tile_tr(&sV[16 * n], P, l), RR[n]);
-        } else {  // 32 tokens per product, k map {4g + j} u {16 + 4g + j}
-          for (int p = 0; p < NP; p += 2) {
-            const bf16x8 ya = cat8(to_bf16x4_scaled(Y[p], a), to_bf16x4_scaled(Y[p + 1], a));
-            for (int n = 0; n < NT; ++n)
-              RR[n] = mma32(ya, cat8(tile_tr(&sV[16 * p * P + 16 * n], P, l),
-                                     tile_tr(&sV[16 * (p + 1) * P + 16 * n], P, l)), RR[n]);
-          }
+    // Residuals of both tiles: YP_p = K_p P, YR_p = K_p R - V_p[:, 16 col ..].
+    f32x4 YP[NP], YR[NP];
+    for (int p = 0; p < NP; ++p) {
+      const bf16x4 vt = tile_tr(&sV[16 * p * P + 16 * col], P, l);  // V tile, accumulator layout
+      f32x4 yp = zero4(), yr;
+      for (int j = 0; j < 4; ++j) yr[j] = -(float)vt[j];
+      if constexpr (D >= 32) {
+        for (int ks = 0; ks < D / 32; ++ks) {
+          const bf16* pk = sK + (16 * p + r) * P + 32 * ks + 4 * g;
+          const bf16x8 ka = cat8(ld4(pk), ld4(pk + 16));
+          yp = mma32(ka, b_state(XP, ks), yp);
+          yr = mma32(ka, b_state(XR, ks), yr);
+        }
+      } else {
+        const bf16x4 ka = ld4(sK + (16 * p + r) * P + 4 * g);
+        yp = mma16(ka, to_bf16x4(XP[0]), yp);
+        yr = mma16(ka, to_bf16x4(XR[0]), yr);
+      }
+      YP[p] = yp;
+      YR[p] = yr;
+    }
+    if constexpr (BIDIR) {  // R_rev[16col + i][16n + .] += a (K_c P_{c-1})^T V_c
+      if constexpr (NP == 1) {
+        const bf16x4 ya = to_bf16x4_scaled(YP[0], a);
+        for (int n = 0; n < NT; ++n) RR[n] = mma16(ya, tile_tr(&sV[16 * n], P, l), RR[n]);
+      } else {  // 32 tokens per product, k map {4g + j} u {16 + 4g + j}
+        for (int p = 0; p < NP; p += 2) {
+          const bf16x8 ya = cat8(to_bf16x4_scaled(YP[p], a), to_bf16x4_scaled(YP[p + 1], a));
+          for (int n = 0; n < NT; ++n)
+            RR[n] = mma32(ya, cat8(tile_tr(&sV[16 * p * P + 16 * n], P, l),
+                                   tile_tr(&sV[16 * (p + 1) * P + 16 * n], P, l)), RR[n]);
         }
       }
     }
-    update_state<D, NP, P>(X, Y, sK, a, l);
+    // [P | R] += K^T (-a [YP | YR]): the transpose reads of K serve both tiles.
+    if constexpr (NP == 1) {
+      const bf16x4 ep = to_bf16x4_scaled(YP[0], -a), er = to_bf16x4_scaled(YR[0], -a);
+      for (int m = 0; m < NT; ++m) {
+        const bf16x4 kt = tile_tr(&sK[16 * m], P, l);
+        XP[m] = mma16(kt, ep, XP[m]);
+        XR[m] = mma16(kt, er, XR[m]);
+      }
+    } else {
+      for (int p = 0; p < NP; p += 2) {
+        const bf16x8 ep = cat8(to_bf16x4_scaled(YP[p], -a), to_bf16x4_scaled(YP[p + 1], -a));
+        const bf16x8 er = cat8(to_bf16x4_scaled(YR[p], -a), to_bf16x4_scaled(YR[p + 1], -a));
+        for (int m = 0; m < NT; ++m) {
+          const bf16x8 kt = cat8(tile_tr(&sK[16 * p * P + 16 * m], P, l), tile_tr(&sK[16 * (p + 1) * P + 16 * m], P, l));
+          XP[m] = mma32(kt, ep, XP[m]);
+          XR[m] = mma32(kt, er, XR[m]);
+        }
+      }
+    }
   }
 
   // comp[(bh * S + s)] holds the forward map record and, for the bidirectional scan, the
@@ -393,18 +431,13 @@ __global__ __launch_bounds__(D / 8 * 64) void chunk_compose_bf16(
   for (int m = 0; m < NT; ++m)
     for (int j = 0; j < 4; ++j) {
       const int row = 16 * m + 4 * g + j, cc = 16 * col + r;
-      if (pwave) {
-        const bf16 nd = (bf16)(X[m][j] - (row == cc ? 1.f : 0.f));  // -Dev = P - I
-        ndev_f[dev_offset<D>(row, cc)] = nd;
-        if constexpr (BIDIR) ndev_r[dev_offset<D>(cc, row)] = nd;  // Dev_r = Dev_f^T
-      }
+      const bf16 nd = (bf16)(XP[m][j] - (row == cc ? 1.f : 0.f));  // -Dev = P - I
+      ndev_f[dev_offset<D>(row, cc)] = nd;
+      if constexpr (BIDIR) ndev_r[dev_offset<D>(cc, row)] = nd;  // Dev_r = Dev_f^T
     }
-  if (!pwave)
-    for (int m = 0; m < NT; ++m) *reinterpret_cast<f32x4*>(r_f + state_tile<D>(col, m, l)) = X[m];
-  if constexpr (BIDIR) {
-    if (pwave)  // RR[n] is R_rev's tile (column tile n, row tile col)
-      for (int n = 0; n < NT; ++n) *reinterpret_cast<f32x4*>(r_r + state_tile<D>(n, col, l)) = RR[n];
-  }
+  for (int m = 0; m < NT; ++m) *reinterpret_cast<f32x4*>(r_f + state_tile<D>(col, m, l)) = XR[m];
+  if constexpr (BIDIR)  // RR[n] is R_rev's tile (column tile n, row tile col)
+    for (int n = 0; n < NT; ++n) *reinterpret_cast<f32x4*>(r_r + state_tile<D>(n, col, l)) = RR[n];
 }
 
 // ---------------------------------------------------------------- 2. prefix over segments
@@ -897,12 +930,18 @@ struct ChunkPlan {
 //    tests/test_codegen.py checks these tables against the compiler's resource report of the
 //    current sources.
 // A kernel of w waves per workgroup then keeps floor(4 * occupancy / w) workgroups on a CU (at most
-// kMaxGroupsPerCU), and the plan takes the smaller figure of compose and scan.
+// kMaxGroupsPerCU), and the plan takes the smaller figure of compose and scan, and at most
+// kPlanWavesPerCU waves of them per CU. Compose and scan are walks of dependent chunk steps whose
+// CU throughput (chunk steps per us) stays about flat above three 4-wave workgroups per CU, while
+// every extra segment adds a step to the prefix fold: for the causal layer of 2 x 16384 x 12 heads
+// (d = 64, b = 16) S = 41 segments (4 workgroups per CU) measured 82.4 us cold and S = 32 (3 per CU)
+// 76.4 us, and a sweep of S from 16 to 41 put 28-32 best.
 constexpr int kPlanCUs = 256;
 constexpr int kMaxGroupsPerCU = 16;
-constexpr int kComposeOcc[3][3][2] = {{{8, 8}, {8, 8}, {7, 6}},   // D = 16: CH = 16, 32, 64
-                                      {{8, 8}, {8, 8}, {7, 5}},   // D = 32
-                                      {{8, 6}, {7, 5}, {6, 4}}};  // D = 64
+constexpr int kPlanWavesPerCU = 12;
+constexpr int kComposeOcc[3][3][2] = {{{8, 8}, {7, 6}, {4, 4}},   // D = 16: CH = 16, 32, 64
+                                      {{7, 5}, {5, 4}, {4, 3}},   // D = 32
+                                      {{4, 4}, {4, 3}, {3, 2}}};  // D = 64
 constexpr int kScanOcc[3][3][2] = {{{7, 1}, {4, 1}, {2, 1}},
                                    {{7, 1}, {4, 1}, {2, 1}},
                                    {{5, 1}, {4, 1}, {2, 1}}};
@@ -911,9 +950,10 @@ constexpr int log2_16(int x) { return x == 16 ? 0 : (x == 32 ? 1 : 2); }
 
 template <int D, int CH>
 int groups_per_cu(bool bidir) {
-  const int comp = 4 * kComposeOcc[log2_16(D)][log2_16(CH)][bidir] / (D / 8);
+  const int comp = 4 * kComposeOcc[log2_16(D)][log2_16(CH)][bidir] / (D / 16);
   const int scan = 4 * kScanOcc[log2_16(D)][log2_16(CH)][bidir] / (D / 16);
-  const int n = comp < scan ? comp : scan;
+  int n = comp < scan ? comp : scan;
+  if (n > kPlanWavesPerCU / (D / 16)) n = kPlanWavesPerCU / (D / 16);
   return n < 1 ? 1 : (n > kMaxGroupsPerCU ? kMaxGroupsPerCU : n);
 }
 
@@ -962,15 +1002,15 @@ hipError_t launch_bf16(bool bidir, int B, int H, int N, float a, const void* q, 
   if (pl.S > 1) {
     if (bidir) {
       if (cols)
-        hipLaunchKernelGGL((chunk_compose_bf16<D, CH, true, true>), dim3(pl.S, BH), dim3(D / 8 * 64), 0, st,
+        hipLaunchKernelGGL((chunk_compose_bf16<D, CH, true, true>), dim3(pl.S, BH), dim3(D / 16 * 64), 0, st,
                            (const bf16*)k, (const bf16*)v, H, N, a, pl.S, pl.L, comp, cm);
       else
-        hipLaunchKernelGGL((chunk_compose_bf16<D, CH, true>), dim3(pl.S, BH), dim3(D / 8 * 64), 0, st,
+        hipLaunchKernelGGL((chunk_compose_bf16<D, CH, true>), dim3(pl.S, BH), dim3(D / 16 * 64), 0, st,
                            (const bf16*)k, (const bf16*)v, H, N, a, pl.S, pl.L, comp, cm);
       hipLaunchKernelGGL((chunk_prefix<D, 2>), dim3(BH, 2, D / 16), dim3(64), 0, st, w0, w0s, 2, H,
                          pl.S, comp, win);
     } else {
-      hipLaunchKernelGGL((chunk_compose_bf16<D, CH, false>), dim3(pl.S, BH), dim3(D / 8 * 64), 0,
+      hipLaunchKernelGGL((chunk_compose_bf16<D, CH, false>), dim3(pl.S, BH), dim3(D / 16 * 64), 0,
                          st, (const bf16*)k, (const bf16*)v, H, N, a, pl.S, pl.L, comp, cm);
       hipLaunchKernelGGL((chunk_prefix<D, 1>), dim3(BH, 1, D / 16), dim3(64), 0, st, w0, w0s, 1,
                          H, pl.S, comp, win);

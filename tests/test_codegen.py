@@ -176,7 +176,8 @@ def test_chunk_plan_occupancy_tables_match_the_compiled_kernels(tmp_path):
     compiled compose / scan kernel sustains (so that the plan does not depend on the device a call
     runs on). Those tables must equal the compiler's occupancy report for the current sources. The
     column-order instances of the bidirectional kernels (the 2-D scan) run on the same plan, so they
-    must sustain at least the table's occupancy."""
+    must keep at least the plan's workgroups per CU resident (both kernels have D / 16 waves per
+    workgroup; the plan takes the smaller figure of compose and scan, at most 12 waves per CU)."""
     src_path = os.path.join(B.CSRC, "chunked.hip")
     src = open(src_path).read()
     compose, scan = _occ_table(src, "kComposeOcc"), _occ_table(src, "kScanOcc")
@@ -203,10 +204,18 @@ def test_chunk_plan_occupancy_tables_match_the_compiled_kernels(tmp_path):
         table = compose if kind == "chunk_compose_bf16" else scan
         assert table[(d, c, bidir)] == occ, f"{kind}<{d}, {c}, {'bidir' if bidir else 'causal'}>: table " \
                                              f"{table[(d, c, bidir)]}, compiler {occ}"
+    waves_per_cu = int(re.search(r"kPlanWavesPerCU = (\d+);", src).group(1))
+    max_groups = int(re.search(r"kMaxGroupsPerCU = (\d+);", src).group(1))
+
+    def plan_groups(d, c, bidir):
+        w = d // 16
+        n = min(4 * compose[(d, c, bidir)] // w, 4 * scan[(d, c, bidir)] // w, waves_per_cu // w)
+        return max(1, min(max_groups, n))
+
     for (kind, d, c, bidir), occ in cols.items():
-        table = compose if kind == "chunk_compose_bf16" else scan
-        assert occ >= table[(d, c, bidir)], f"{kind}<{d}, {c}, bidir, column order>: table " \
-                                            f"{table[(d, c, bidir)]}, compiler {occ}"
+        need = plan_groups(d, c, bidir)
+        assert 4 * occ // (d // 16) >= need, f"{kind}<{d}, {c}, bidir, column order>: {occ} waves per SIMD " \
+                                             f"keep fewer than the plan's {need} workgroups per CU"
 
 
 def _mlp_as_constants():
