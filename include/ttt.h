@@ -219,7 +219,10 @@ ttt_status ttt_forward_chunked_bidir2d(ttt_dtype dt, int B, int H, int height, i
  * multiple of 4); it applies to both w1_0 and w2_0, which hold D*Dh elements per head.
  * w1_out / w2_out (nullable): fp32 [B, H, D, Dh] / [B, H, Dh, D] end states.
  * Sizes: D in {16, 32, 64}, Dh a multiple of 64 in [64, 1024], chunk in {16, 32, 64}. bf16 I/O with
- * (D, Dh, chunk) = (64, 256, 16) runs on the matrix cores with the state held in registers; bf16
+ * (D, Dh, chunk) = (64, 256, 16) runs on the matrix cores with the state held in registers, the
+ * forward chain of each (b, h) on one CU and the read-outs beside it on other CUs from per-chunk
+ * intermediates and state checkpoints kept in the workspace (about (N / 16) * 18 KiB plus
+ * (N / 1024 + 4) * 128 KiB per (b, h)); bf16
  * I/O with D = 64, chunk = 16 and Dh = 512, 768 or 1024 runs on the matrix cores with the fp32 state
  * in the workspace (bf16 operands, fp32 accumulation); every other size, and fp32 I/O, runs in
  * plain fp32 arithmetic with the state in the workspace.
@@ -227,9 +230,11 @@ ttt_status ttt_forward_chunked_bidir2d(ttt_dtype dt, int B, int H, int height, i
  * fp16 operands while the hidden pre-activations stay at least 2^-10 in magnitude (per lane of a
  * wave and chunk, unless all zero) and either within sqrt 2 or with GELU outputs within 32, the W2
  * state's largest magnitude (checked every 32 chunks and at the end) is in [2^-10, 2^15], and the
- * state stays finite. A (batch, head) chain that leaves these ranges is recomputed by a second
- * kernel with bf16 operands (fp32's exponent range); the workspace then holds, as its first B*H
- * ints, 1 for each recomputed chain and 0 for the others.
+ * state stays finite; the read-outs check their own pre-activations and GELU outputs the same way.
+ * A (batch, head) chain that leaves these ranges is recomputed in full by a last kernel with bf16
+ * operands (fp32's exponent range); the workspace then holds, as its first B*H ints, a nonzero
+ * value for each recomputed chain (bit 0: the forward chain, bit 1: a read-out) and 0 for the
+ * others.
  * Precision: TTT_F32 keeps everything in fp32 (no reduced-precision operands).
  */
 ttt_status ttt_mlp_forward(ttt_dtype dt, int B, int H, int N, int D, int Dh, int chunk, float eta,

@@ -21,12 +21,24 @@
 // operands of K and E (contractions over tokens) come from LDS by gfx950 transpose reads, and
 // X2^T (for the contraction over hidden units) is a product with an identity tile. The
 // cross-wave sums over hidden units (Z2 and the read-out) go through LDS in a fixed wave order,
-// so results are deterministic. The steps between the first and the last have both a read-out
-// and a forward, known at compile time, so that their products and GELUs share basic blocks and
-// interleave. E is kept as -a E (a = eta / b), so that -a D1 and the weight updates' operands come
-// out of the products with the right sign (no separate negations). Two workgroup barriers per
-// chunk; K, V, Q are staged through a four-deep LDS ring: each chunk's global loads are issued
-// three chunks ahead into one of two alternating register sets and stored to LDS two chunks ahead.
+// so results are deterministic. E is kept as -a E (a = eta / b), so that -a D1 and the weight
+// updates' operands come out of the products with the right sign (no separate negations). Two
+// workgroup barriers per chunk; K, V (and Q) are staged through a four-deep LDS ring: each chunk's
+// global loads are issued three chunks ahead into one of two alternating register sets and stored
+// to LDS two chunks ahead.
+//
+// Schedule. The forward chain (the state updates) is sequential per (b, h), and only 48 chains
+// exist at the reference shape, so it holds 48 of the 256 CUs. The read-outs do not feed the chain:
+// the chain workgroup stores, per chunk, the -a D1 and X2 tiles of each wave and the -a E tile,
+// and at each segment start a checkpoint of its state; read-out workgroups on other CUs replay a
+// segment's state updates from its checkpoint with those tiles (the chain's own products, so the
+// same states bit for bit) and read each chunk out with its end state (the end-state form above).
+// Both roles share one launch (chain workgroups first, so that they are dispatched before any
+// read-out workgroup waits on them; see mlp_fwd_fused). Without the read-outs in its steps the
+// chain runs 785 us instead of 945 at 4 x 8192 x 12 heads. The steps between the first and the last
+// of the generic single-workgroup form (used by the bf16 recomputation) have both a read-out and a
+// forward, known at compile time, so that their products and GELUs share basic blocks and
+// interleave.
 //
 // Operand precision. The products on the W1 side (inputs K, Q and D1) take bf16 operands. Those
 // on the W2 side (X2, X2q, W2, E and X2q X2^T) take fp16 operands in the first launch: three more
@@ -43,9 +55,10 @@
 // fp16's normal range (at most 2^-25 a value) stays negligible beside them when a = eta / b is
 // small, and inputs or weights small enough to make those terms small too fail the other checks.
 // A (batch,
-// head) chain that fails any check is flagged in the workspace, and a second launch recomputes
-// exactly the flagged chains with bf16 operands on the W2 side (bf16 has fp32's exponent range)
-// and the fp32 GELU; every other chain returns at once. All products accumulate in fp32.
+// head) chain that fails any check (in its forward chain or in a read-out) is flagged in the
+// workspace, and a last launch recomputes exactly the flagged chains in the single-workgroup form
+// with bf16 operands on the W2 side (bf16 has fp32's exponent range) and the fp32 GELU; every other
+// chain returns at once. All products accumulate in fp32.
 //
 // No 16x16x16 product accumulates onto the result of a 16x16x32 product: on gfx950 such a
 // mixed-shape accumulator chain was measured to read a stale accumulator (wrong results that
@@ -203,14 +216,61 @@ struct MlpLds {
   int bad;
 };
 
+// Intermediates of the split schedule (SPLIT), per (b, h) chain in the workspace: for every chunk and
+// thread the -a D1 and X2 tiles the thread's wave holds (bf16x4 x 2, then fp16x4 x 2: 32 bytes), for
+// every chunk the -a E tile (four 16 x 16 tiles, lane l of wave w < 4 holds tile w's accumulator
+// fragment: 8 bytes), and at the start of every read-out segment a checkpoint of the state (each
+// thread's W1 and W2 tiles: 16 fp32x4).
+// Segments: kSegLong chunks each, except that the last (up to kSegLong) chunks are cut into
+// segments of kSegTail, so that little read-out work is left when the chain ends; every segment end
+// is a publication of the chain (a wait for its stores and an L2 write-back), which is why the
+// other segments are long.
+constexpr int kSegLong = 64;
+constexpr int kSegTail = 16;
+constexpr int kReadoutWorkers = 64;  // read-out workgroups of the fused launch
+struct SegPlan {
+  int C, R, nlong;  // chunks; start of the tail region; segments before it
+  __host__ __device__ explicit SegPlan(int C_) : C(C_), R((C_ - 1) / kSegLong * kSegLong), nlong((C_ - 1) / kSegLong) {}
+  __host__ __device__ int count() const { return nlong + (C - R + kSegTail - 1) / kSegTail; }
+  __host__ __device__ int lo(int s) const { return s < nlong ? s * kSegLong : R + (s - nlong) * kSegTail; }
+  __host__ __device__ int hi(int s) const { return min(C, s < nlong ? (s + 1) * kSegLong : R + (s - nlong + 1) * kSegTail); }
+  // the segment that starts at chunk c, or -1
+  __host__ __device__ int starting_at(int c) const {
+    if (c < R) return c % kSegLong == 0 ? c / kSegLong : -1;
+    return (c - R) % kSegTail == 0 ? nlong + (c - R) / kSegTail : -1;
+  }
+  __host__ __device__ bool is_end(int done) const {
+    return done <= R ? done % kSegLong == 0 : ((done - R) % kSegTail == 0 || done == C);
+  }
+};
+// The intermediates are stored with the nontemporal hint: the chain never reads them back, and
+// fewer dirty lines are left in the L2 for each publication's write-back (measured 898 -> 881 us).
+__device__ __forceinline__ void st8_out(void* p, uint2 v) {
+  typedef unsigned u32x2_nt __attribute__((ext_vector_type(2)));
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x2_nt, v), reinterpret_cast<u32x2_nt*>(p));
+}
+struct MlpSplitWs {
+  uint4* inter;   // [bh][chunk][thread][2]
+  uint2* etile;   // [bh][chunk][4 waves][64 lanes]
+  f32x4* ckpt;    // [bh][segment][thread][16]
+  int* progress;  // [bh]: chunks whose intermediates are published (release, agent scope)
+};
+__host__ __device__ inline long long mlp_inter_uint4(int C) { return (long long)C * kWaves * 64 * 2; }
+__host__ __device__ inline long long mlp_etile_uint2(int C) { return (long long)C * 4 * 64; }
+__host__ __device__ inline long long mlp_ckpt_f32x4(int C) { return (long long)SegPlan(C).count() * kWaves * 64 * 16; }
+
 // One (b, h) chain. F16: fp16 operands on the W2 side with range checks; returns true (the same in
 // every thread) when a check failed. !F16: bf16 operands, no checks; returns false.
-template <bool F16>
+// SPLIT (with F16): the forward chain only, no read-out and no Q staging; each step stores its
+// intermediates and at each segment start the state into sw, from which the read-out workgroups compute the
+// read-outs of all chunks in parallel.
+template <bool F16, bool SPLIT = false>
 __device__ __forceinline__ bool mlp_chain(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ w1, const float* __restrict__ w2, long long wbs, int H, int N,
     float a, bf16* __restrict__ o, float* __restrict__ w1_out, float* __restrict__ w2_out,
-    MlpLds& lds) {
+    MlpLds& lds, MlpSplitWs sw = MlpSplitWs{}) {
+  static_assert(!SPLIT || F16, "the split schedule runs the fp16 pass");
   using S = W2Side<F16>;
   using x4 = typename S::x4;
   using x8 = typename S::x8;
@@ -250,7 +310,7 @@ __device__ __forceinline__ bool mlp_chain(
   // value). Chunk indices past the end are clamped to the last chunk. So every wave issues the same
   // loads on every step, and the compiler's wait before a staged piece's LDS write counts only the
   // memory operations issued after its load: no wait drains the loads in flight or the O stores.
-  const int t = threadIdx.x, u = t < 384 ? t : t - 128;
+  const int t = threadIdx.x, u = SPLIT ? (t & 255) : (t < 384 ? t : t - 128);
   const int prow = (u & 127) >> 3, pcol = (u & 7) * 8, which = u >> 7;
   const bf16* psrc = (u < 128 ? k : (u < 256 ? v : q)) + head0 + prow * ts + pcol;
   bf16* const pdst = &sKVQ[0][which][prow * kP + pcol];
@@ -259,6 +319,10 @@ __device__ __forceinline__ bool mlp_chain(
   uint4 pfA = ld16(chunk_src(1)), pfB = ld16(chunk_src(2));  // chunks 1 and 2
   __syncthreads();
 
+  const long long bhs = blockIdx.x;
+  uint4* const inter = sw.inter + bhs * mlp_inter_uint4(C) + 2 * t;
+  uint2* const etile = sw.etile + bhs * mlp_etile_uint2(C) + 64 * (w & 3) + l;
+  f32x4* const ckpt = sw.ckpt + bhs * mlp_ckpt_f32x4(C) + 16 * t;
   bf16x4 d1p[kNh];  // -a D1 of the previous chunk, [token][hidden] tiles
   x8 x2tp;          // X2^T of the previous chunk, [hidden][token] tiles (both, c-layout k map)
   for (int n = 0; n < kNh; ++n) d1p[n] = bf16x4{};
@@ -279,6 +343,16 @@ __device__ __forceinline__ bool mlp_chain(
     // ---------------- phase 1: products with the current weights. The read-out of chunk c - 1
     // and the forward of chunk c are independent; their products, GELUs and remaining products
     // are grouped so that one basic block holds both chains.
+    if constexpr (SPLIT) {
+      const int sg = SegPlan(C).starting_at(c);
+      if (sg >= 0) {  // the chunk's start state
+        f32x4* dst = ckpt + (long long)sg * kWaves * 64 * 16;
+        for (int m = 0; m < 4; ++m)
+          for (int n = 0; n < kNh; ++n) dst[m * kNh + n] = W1t[m][n];
+        for (int n = 0; n < kNh; ++n)
+          for (int o2 = 0; o2 < 4; ++o2) dst[8 + n * 4 + o2] = W2t[n][o2];
+      }
+    }
     bf16x8 w1b[2][kNh];  // W1 tiles (k = features, c-layout k map)
     for (int ks = 0; ks < 2; ++ks)
       for (int n = 0; n < kNh; ++n) w1b[ks][n] = cat_tiles(W1t[2 * ks][n], W1t[2 * ks + 1][n]);
@@ -389,6 +463,10 @@ __device__ __forceinline__ bool mlp_chain(
       f32x4 xt[kNh];
       for (int n = 0; n < kNh; ++n) xt[n] = S::mma16(x2b[n], ident, zero4());  // X2^T [hidden][token]
       x2tp = S::cat(S::cvt(xt[0]), S::cvt(xt[1]));
+      if constexpr (SPLIT) {
+        const uint2 x0 = __builtin_bit_cast(uint2, x2b[0]), x1 = __builtin_bit_cast(uint2, x2b[1]);
+        st16_out(&inter[(long long)c * kWaves * 64 * 2 + 1], make_uint4(x0.x, x0.y, x1.x, x1.y));
+      }
     }
     x8 w2a[4];  // W2^T tiles (k = this wave's hidden units), for both products below
     for (int o2 = 0; o2 < 4; ++o2) w2a[o2] = S::cat(S::cvt(W2t[0][o2]), S::cvt(W2t[1][o2]));
@@ -422,18 +500,23 @@ __device__ __forceinline__ bool mlp_chain(
     __syncthreads();
 
     // ---------------- phase 2: cross-wave sums (fixed wave order)
-    if (fwd && w < 4) {  // E^T tile w = Z2^T - V^T, stored as -a E [token][out]
+    if (fwd && (SPLIT || w < 4)) {  // E^T tile w = Z2^T - V^T, stored as -a E [token][out]
+      // (SPLIT: waves 4-7 have no read-out sums; they repeat waves 0-3, same values and stores,
+      // so that every wave issues the same memory operations)
+      const int we = w & 3;
       // All nine LDS reads are issued before the adds (the compiler otherwise keeps only two or
       // three of them in flight, and this phase is their latency).
       f32x4 pt[kWaves];
-      for (int ww = 0; ww < kWaves; ++ww) pt[ww] = sRed[(ww * kSlots + w) * 64 + l];
-      const bf16x4 vv = ld4(&sV[r * kP + 16 * w + 4 * g]);
+      for (int ww = 0; ww < kWaves; ++ww) pt[ww] = sRed[(ww * kSlots + we) * 64 + l];
+      const bf16x4 vv = ld4(&sV[r * kP + 16 * we + 4 * g]);
       __builtin_amdgcn_sched_group_barrier(0x100, 9, 0);
       f32x4 s = pt[0];
       for (int ww = 1; ww < kWaves; ++ww) s = s + pt[ww];
       f32x4 e;
       for (int j = 0; j < 4; ++j) e[j] = a * ((float)vv[j] - s[j]);
-      *reinterpret_cast<x4*>(&sEc[r * kP + 16 * w + 4 * g]) = S::cvt(e);
+      const x4 eh = S::cvt(e);
+      *reinterpret_cast<x4*>(&sEc[r * kP + 16 * we + 4 * g]) = eh;
+      if constexpr (SPLIT) st8_out(&etile[(long long)c * 4 * 64], __builtin_bit_cast(uint2, eh));
     }
     if (rd && w >= 4) {  // O^T tile of chunk c - 1 = sum of the waves' shares
       const int o4 = w - 4;
@@ -463,6 +546,10 @@ __device__ __forceinline__ bool mlp_chain(
         for (int j = 0; j < 4; ++j) d1[j] = acc[j] * (float)gph[n][j];
         d1p[n] = to_bf16x4(d1);
       }
+      if constexpr (SPLIT) {
+        const uint2 d0 = __builtin_bit_cast(uint2, d1p[0]), d1 = __builtin_bit_cast(uint2, d1p[1]);
+        st16_out(&inter[(long long)c * kWaves * 64 * 2], make_uint4(d0.x, d0.y, d1.x, d1.y));
+      }
       // W1 += K^T (-a D1): A = K^T (row feature, k token; LDS transpose read), B = -a D1.
       for (int m = 0; m < 4; ++m) {
         const bf16x4 kt = tile_tr(&sK[16 * m], kP, l);
@@ -481,18 +568,43 @@ __device__ __forceinline__ bool mlp_chain(
   using T_ = std::true_type;
   using F_ = std::false_type;
   // Step 0 has no read-out, step C no forward; the steps between have both (two per trip: even
-  // steps stage from pfA, odd ones from pfB).
-  step(0, pfA, F_{}, T_{});
-  int c = 1;
-  for (; c + 1 < C; c += 2) {
-    step(c, pfB, T_{}, T_{});
-    step(c + 1, pfA, T_{}, T_{});
-  }
-  if (c < C) {
-    step(c, pfB, T_{}, T_{});
-    step(c + 1, pfA, T_{}, F_{});
+  // steps stage from pfA, odd ones from pfB). SPLIT: forward steps only.
+  if constexpr (SPLIT) {
+    // At each segment end (SegPlan) the count of finished chunks is published for the
+    // read-out workgroups: every wave waits for its own stores, and after the barrier one release at
+    // agent scope (which writes the CU's L2 back) covers the whole workgroup's stores.
+    const SegPlan plan(C);
+    auto publish = [&](int done) {
+      if (plan.is_end(done)) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (t == 0) __hip_atomic_store(sw.progress + bhs, done, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    };
+    int c = 0;
+    for (; c + 1 < C; c += 2) {
+      step(c, pfA, F_{}, T_{});
+      publish(c + 1);
+      step(c + 1, pfB, F_{}, T_{});
+      publish(c + 2);
+    }
+    if (c < C) {
+      step(c, pfA, F_{}, T_{});
+      publish(c + 1);
+    }
   } else {
-    step(c, pfB, T_{}, F_{});
+    step(0, pfA, F_{}, T_{});
+    int c = 1;
+    for (; c + 1 < C; c += 2) {
+      step(c, pfB, T_{}, T_{});
+      step(c + 1, pfA, T_{}, T_{});
+    }
+    if (c < C) {
+      step(c, pfB, T_{}, T_{});
+      step(c + 1, pfA, T_{}, F_{});
+    } else {
+      step(c, pfB, T_{}, F_{});
+    }
   }
 
   const long long bhl = bh;
@@ -536,20 +648,248 @@ __device__ __noinline__ void mlp_chain_bf16(
   mlp_chain<false>(q, k, v, w1, w2, wbs, H, N, a, o, w1_out, w2_out, lds);
 }
 
-// One workgroup per (b, h) chain: the fp16 pass, and only when one of its range checks failed, the
-// bf16 pass over the same chain (its outputs replace the first pass's). flags[bh] records which.
-__global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_bf16(
+// The fast path in three launches (split schedule):
+//  1. mlp_clear zeroes the chains' flags and published-chunk counts.
+//  2. mlp_fwd_fused: workgroups 0 .. BH-1 run the forward chains (one per (b, h); the fp16 pass
+//     without read-outs), storing their intermediates and checkpoints and publishing their progress
+//     at each segment end (SegPlan); the next n_workers workgroups take the read-out segments in order
+//     (segment-major: task = segment * BH + bh, worker j takes tasks j, j + n_workers, ...), each
+//     waiting until its chain has published the segment. The chain workgroups have the lowest ids,
+//     so they are dispatched before any read-out workgroup, never wait, and every wait ends; a wait
+//     is also bounded (then the chain is flagged and recomputed). With 48 chains on 48 CUs the
+//     read-outs run beside the chains on other CUs.
+//  3. mlp_fixup_bf16 recomputes in full (bf16 W2-side operands, read-outs and end states) every
+//     chain that a range check flagged, in the forward chain (bit 0), in a read-out (bit 1) or by a
+//     wait that timed out (bit 2).
+__global__ void mlp_clear(int* __restrict__ flags, int* __restrict__ progress, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) {
+    flags[i] = 0;
+    progress[i] = 0;
+  }
+}
+
+struct MlpReadoutLds {
+  bf16 kq[2][2][kCh * kP];         // [parity][K, Q][token][feature]
+  f16 e[2][kCh * kP];              // [parity] -a E [token][out]
+  f32x4 red[2][kWaves * 4 * 64];   // [parity] O^T partial tiles, lane-private
+};
+struct MlpChunkRegs {
+  uint4 kq;      // this thread's 16-byte piece of the K or Q tile
+  uint4 d1, x2;  // -a D1 and X2 tiles of the thread's wave
+  uint2 e;       // -a E fragment of tile w & 3
+};
+
+// Reads out segment seg of chain bh; returns true (in every thread of a wave that saw it) when a
+// value left the range its fp16 operands allow.
+__device__ __forceinline__ bool readout_segment(
+    int seg, int bh, const bf16* __restrict__ q, const bf16* __restrict__ k, int H, int N, float a,
+    bf16* __restrict__ o, const MlpSplitWs& sw, MlpReadoutLds& lds) {
+  using S = W2Side<true>;
+  const int b = bh / H, h = bh % H;
+  const int t = threadIdx.x, w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
+  const int C = N / kCh;
+  const SegPlan plan(C);
+  const int c0 = plan.lo(seg), c1 = plan.hi(seg);
+  const long long ts = (long long)H * kD;
+  const long long head0 = (long long)b * N * ts + (long long)h * kD;
+
+  f32x4 W1t[4][kNh], W2t[kNh][4];  // layouts as in mlp_chain
+  {
+    const f32x4* ck = sw.ckpt + (long long)bh * mlp_ckpt_f32x4(C) + (long long)seg * kWaves * 64 * 16 + 16 * t;
+    for (int m = 0; m < 4; ++m)
+      for (int n = 0; n < kNh; ++n) W1t[m][n] = ck[m * kNh + n];
+    for (int n = 0; n < kNh; ++n)
+      for (int o2 = 0; o2 < 4; ++o2) W2t[n][o2] = ck[8 + n * 4 + o2];
+  }
+  const uint4* inter = sw.inter + (long long)bh * mlp_inter_uint4(C) + 2 * t;
+  const uint2* etile = sw.etile + (long long)bh * mlp_etile_uint2(C) + 64 * (w & 3) + l;
+  // Threads 0..255 move one 16-byte piece of K or Q per chunk; 256..511 repeat them (same source and
+  // LDS address), so that every wave issues the same loads.
+  const int u = t & 255, prow = (u & 127) >> 3, pcol = (u & 7) * 8, which = u >> 7;
+  const bf16* psrc = (which == 0 ? k : q) + head0 + prow * ts + pcol;
+  const int poff = which * kCh * kP + prow * kP + pcol;  // within lds.kq[parity]
+  auto load = [&](int cc, MlpChunkRegs& d) {  // chunk indices past the segment repeat its last chunk
+    cc = min(cc, c1 - 1);
+    d.kq = ld16(psrc + (long long)cc * kCh * ts);
+    const uint4* pi = inter + (long long)cc * kWaves * 64 * 2;
+    d.d1 = pi[0];
+    d.x2 = pi[1];
+    d.e = etile[(long long)cc * 4 * 64];
+  };
+  auto to_lds = [&](int parity, const MlpChunkRegs& d) {
+    st16_lds8(&lds.kq[parity][0][0] + poff, d.kq);
+    *reinterpret_cast<uint2*>(&lds.e[parity][r * kP + 16 * (w & 3) + 4 * g]) = d.e;
+  };
+  f16x4 ident;  // identity tile as the B operand: lane holds I[4g + i][r]
+  for (int i = 0; i < 4; ++i) ident[i] = (f16)(4 * g + i == r ? 1.f : 0.f);
+
+  MlpChunkRegs set0, set1;  // data of the even and of the odd chunks
+  load(c0, set0);
+  load(c0 + 1, set1);
+  to_lds(0, set0);  // c0 is even (segment lengths are)
+  __syncthreads();
+  bool bad = false;
+
+  auto step = [&](const int c, MlpChunkRegs& cur, MlpChunkRegs& nxt) {
+    const int p = c & 1;
+    const bf16* sK = lds.kq[p][0];
+    const bf16* sQ = lds.kq[p][1];
+    const f16* sE = lds.e[p];
+    f32x4* const sRed = lds.red[p];
+    bf16x4 d1p[kNh];
+    f16x4 x2b[kNh];
+    {
+      const uint2 d0 = make_uint2(cur.d1.x, cur.d1.y), d1 = make_uint2(cur.d1.z, cur.d1.w);
+      d1p[0] = __builtin_bit_cast(bf16x4, d0);
+      d1p[1] = __builtin_bit_cast(bf16x4, d1);
+      const uint2 x0 = make_uint2(cur.x2.x, cur.x2.y), x1 = make_uint2(cur.x2.z, cur.x2.w);
+      x2b[0] = __builtin_bit_cast(f16x4, x0);
+      x2b[1] = __builtin_bit_cast(f16x4, x1);
+    }
+    // The chunk's state update (the forward chain's phase 3 products): W1 += K^T (-a D1),
+    // W2 += X2^T (-a E).
+    for (int m = 0; m < 4; ++m) {
+      const bf16x4 kt = tile_tr(&sK[16 * m], kP, l);
+      for (int n = 0; n < kNh; ++n) W1t[m][n] = mma16(kt, d1p[n], W1t[m][n]);
+    }
+    for (int o2 = 0; o2 < 4; ++o2) {
+      const f16x4 e = S::tr(&sE[16 * o2], kP, l);
+      for (int n = 0; n < kNh; ++n) W2t[n][o2] = S::mma16(x2b[n], e, W2t[n][o2]);
+    }
+    // Read-out with the end state.
+    bf16x8 w1b[2][kNh];
+    for (int ks = 0; ks < 2; ++ks)
+      for (int n = 0; n < kNh; ++n) w1b[ks][n] = cat_tiles(W1t[2 * ks][n], W1t[2 * ks + 1][n]);
+    f32x4 mt = zero4();  // M[t'][t] = k_t' . q_t, kept for t' > t
+    for (int ks = 0; ks < 2; ++ks)
+      mt = mma32(cat8(ld4(&sK[r * kP + 32 * ks + 4 * g]), ld4(&sK[r * kP + 32 * ks + 16 + 4 * g])),
+                 cat8(ld4(&sQ[r * kP + 32 * ks + 4 * g]), ld4(&sQ[r * kP + 32 * ks + 16 + 4 * g])), mt);
+    for (int j = 0; j < 4; ++j) mt[j] = 4 * g + j <= r ? 0.f : -mt[j];
+    const bf16x4 mb = to_bf16x4(mt);  // -M (the stored D1 is -a D1)
+    f32x4 Z1q[kNh];  // Z1q^T [hidden][token] = W1^T Q^T + (-a D1)^T (-M)
+    for (int n = 0; n < kNh; ++n) {
+      f32x4 z = zero4();
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16* pq = &sQ[r * kP + 32 * ks + 4 * g];
+        z = mma32(w1b[ks][n], cat8(ld4(pq), ld4(pq + 16)), z);
+      }
+      Z1q[n] = mma32(cat8(d1p[n], bf16x4{}), cat8(mb, bf16x4{}), z);
+    }
+    f16x4 x2qh[kNh];
+    float zm = 0.f;
+    for (int n = 0; n < kNh; ++n) zm = fmaxf(zm, absmax4(Z1q[n]));
+    const bool poly = __float_as_uint(zm) - kZLoBits <= kZHiBits - kZLoBits;
+    if (!__any(!poly)) {
+      for (int n = 0; n < kNh; ++n) {
+        const f16x4 zq = to_f16x4(Z1q[n]), tq = zq * zq;
+        x2qh[n] = zq * cdf_fast_h(zq, tq);
+      }
+    } else {
+      float xm = 0.f;
+      for (int n = 0; n < kNh; ++n) {
+        f32x4 xq;
+        for (int j = 0; j < 4; ++j) xq[j] = Z1q[n][j] * cdf_lib(Z1q[n][j]);
+        x2qh[n] = to_f16x4(xq);
+        xm = fmaxf(xm, absmax4(xq));
+      }
+      bad |= __any(!(xm <= 32.f)) || __any(zm > 0.f && zm < 0x1p-10f);
+    }
+    const f16x8 x2q = cat8h(x2qh[0], x2qh[1]);
+    f32x4 xt[kNh];
+    for (int n = 0; n < kNh; ++n) xt[n] = S::mma16(x2b[n], ident, zero4());  // X2^T [hidden][token]
+    const f16x8 x2tp = cat8h(to_f16x4(xt[0]), to_f16x4(xt[1]));
+    f32x4 n2 = S::mma32(x2tp, x2q, zero4());  // [t'][t] = sum_h X2[t'][h] X2q[t][h]
+    for (int j = 0; j < 4; ++j) n2[j] = 4 * g + j <= r ? 0.f : -n2[j];
+    const f16x4 n2b = to_f16x4(n2);
+    for (int o2 = 0; o2 < 4; ++o2) {
+      const f16x8 w2a = cat8h(to_f16x4(W2t[0][o2]), to_f16x4(W2t[1][o2]));
+      const f32x4 ow = S::mma32(w2a, x2q, zero4());
+      sRed[(w * 4 + o2) * 64 + l] = S::mma32(cat8h(S::tr(&sE[16 * o2], kP, l), f16x4{}), cat8h(n2b, f16x4{}), ow);
+    }
+    // Chunk c + 1 into the other parity's buffers (last read in step c - 1), chunk c + 2 into cur.
+    to_lds(p ^ 1, nxt);
+    load(c + 2, cur);
+    __syncthreads();
+    if (w >= 4) {  // O^T tile w - 4 of chunk c = the sum of the waves' shares (fixed order)
+      const int o4 = w - 4;
+      f32x4 pt[kWaves];
+      for (int ww = 0; ww < kWaves; ++ww) pt[ww] = sRed[(ww * 4 + o4) * 64 + l];
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+      f32x4 sum = pt[0];
+      for (int ww = 1; ww < kWaves; ++ww) sum = sum + pt[ww];
+      const long long tok = head0 + (long long)c * kCh * ts;
+      *reinterpret_cast<bf16x4*>(o + tok + r * ts + 16 * o4 + 4 * g) = to_bf16x4(sum);
+    }
+  };
+  int c = c0;
+  for (; c + 1 < c1; c += 2) {
+    step(c, set0, set1);
+    step(c + 1, set1, set0);
+  }
+  if (c < c1) step(c, set0, set1);
+  return bad;
+}
+
+union MlpFusedLds {
+  MlpLds chain;
+  MlpReadoutLds readout;
+};
+
+__global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_fused(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ w1, const float* __restrict__ w2, long long wbs, int H, int N,
     float a, bf16* __restrict__ o, float* __restrict__ w1_out, float* __restrict__ w2_out,
-    int* __restrict__ flags) {
-  __shared__ __align__(16) MlpLds lds;
-  const bool bad = mlp_chain<true>(q, k, v, w1, w2, wbs, H, N, a, o, w1_out, w2_out, lds);
-  if (threadIdx.x == 0) flags[blockIdx.x] = bad ? 1 : 0;
-  if (bad) {
-    __syncthreads();  // every wave is done with the first pass's shared memory
-    mlp_chain_bf16(q, k, v, w1, w2, wbs, H, N, a, o, w1_out, w2_out, lds);
+    int* __restrict__ flags, MlpSplitWs sw, int BH) {
+  __shared__ __align__(16) MlpFusedLds lds;
+  __shared__ int s_wait;
+  if ((int)blockIdx.x < BH) {
+    const bool bad = mlp_chain<true, true>(q, k, v, w1, w2, wbs, H, N, a, o, w1_out, w2_out, lds.chain, sw);
+    if (bad && threadIdx.x == 0) atomicOr(flags + blockIdx.x, 1);
+    return;
   }
+  const int C = N / kCh;
+  const SegPlan plan(C);
+  const int tasks = plan.count() * BH;
+  const int workers = gridDim.x - BH;
+  // Bound on one wait (s_sleep polls of about a microsecond): far beyond the chain's own time.
+  const int max_polls = 64 * C + (1 << 20);
+  for (int task = blockIdx.x - BH; task < tasks; task += workers) {
+    const int seg = task / BH, bh = task % BH;
+    const int need = plan.hi(seg);
+    if (threadIdx.x == 0) {
+      int polls = 0;
+      // Relaxed polls (an acquire per poll would invalidate the L2 each time); one acquire fence
+      // after the wait orders the loads of the published data.
+      while (__hip_atomic_load(sw.progress + bh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need &&
+             polls < max_polls) {
+        __builtin_amdgcn_s_sleep(16);
+        ++polls;
+      }
+      s_wait = polls < max_polls ? 0 : 1;
+    }
+    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (s_wait) {
+      if (threadIdx.x == 0) atomicOr(flags + bh, 4);
+    } else {
+      const bool bad = readout_segment(seg, bh, q, k, H, N, a, o, sw, lds.readout);
+      if (bad && lane_id() == 0) atomicOr(flags + bh, 2);
+    }
+    __syncthreads();  // the workgroup's shared memory is free for the next task
+  }
+}
+
+// Launch 3: the flagged chains, recomputed in full with bf16 W2-side operands (read-outs and end
+// states); every other workgroup returns at once.
+__global__ __launch_bounds__(kWaves * 64, 1) void mlp_fixup_bf16(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const float* __restrict__ w1, const float* __restrict__ w2, long long wbs, int H, int N,
+    float a, bf16* __restrict__ o, float* __restrict__ w1_out, float* __restrict__ w2_out,
+    const int* __restrict__ flags) {
+  __shared__ __align__(16) MlpLds lds;
+  if (flags[blockIdx.x] == 0) return;
+  mlp_chain_bf16(q, k, v, w1, w2, wbs, H, N, a, o, w1_out, w2_out, lds);
 }
 
 
@@ -1058,9 +1398,26 @@ bool mlp_supported(int D, int Dh, int chunk) {
   return Dh >= 64 && Dh <= 1024 && Dh % 64 == 0;
 }
 
-// Fast path: one flag per (batch, head) chain. Otherwise the state and intermediates per chain.
-size_t mlp_workspace_bytes(bool bf16_io, int B, int H, int, int D, int Dh, int chunk) {
-  if (mlp_fast_path(bf16_io, D, Dh, chunk)) return (size_t)B * H * sizeof(int);
+// Fast path: one flag per (batch, head) chain, then the split schedule's intermediates and
+// checkpoints (MlpSplitWs), each part 256-byte aligned. Otherwise the state and intermediates per
+// chain.
+struct MlpSplitLayout {
+  size_t flags, progress, inter, etile, ckpt, total;
+};
+MlpSplitLayout mlp_split_layout(int BH, int N) {
+  const int C = N / kCh;
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  MlpSplitLayout L;
+  L.flags = 0;
+  L.progress = up((size_t)BH * sizeof(int));
+  L.inter = L.progress + up((size_t)BH * sizeof(int));
+  L.etile = L.inter + up((size_t)BH * mlp_inter_uint4(C) * sizeof(uint4));
+  L.ckpt = L.etile + up((size_t)BH * mlp_etile_uint2(C) * sizeof(uint2));
+  L.total = L.ckpt + up((size_t)BH * mlp_ckpt_f32x4(C) * sizeof(f32x4));
+  return L;
+}
+size_t mlp_workspace_bytes(bool bf16_io, int B, int H, int N, int D, int Dh, int chunk) {
+  if (mlp_fast_path(bf16_io, D, Dh, chunk)) return mlp_split_layout(B * H, N).total;
   if (mlp_wide_path(bf16_io, D, Dh, chunk)) return (size_t)B * H * 3 * (size_t)D * Dh * sizeof(float);
   return (size_t)B * H * (2 * (size_t)D * Dh + 4 * (size_t)chunk * Dh) * sizeof(float);
 }
@@ -1091,9 +1448,21 @@ hipError_t mlp_launch(bool bf16_io, int B, int H, int N, int D, int Dh, int chun
                             static_cast<float*>(ws), st);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(mlp_fwd_bf16, dim3(B * H), dim3(kWaves * 64), 0, st, (const bf16*)q,
+  const MlpSplitLayout L = mlp_split_layout(B * H, N);
+  char* base = static_cast<char*>(ws);
+  int* flags = reinterpret_cast<int*>(base + L.flags);
+  int* progress = reinterpret_cast<int*>(base + L.progress);
+  const MlpSplitWs sw{reinterpret_cast<uint4*>(base + L.inter), reinterpret_cast<uint2*>(base + L.etile),
+                      reinterpret_cast<f32x4*>(base + L.ckpt), progress};
+  const int BH = B * H, tasks = SegPlan(N / kCh).count() * BH;
+  const int workers = tasks < kReadoutWorkers ? tasks : kReadoutWorkers;
+  hipLaunchKernelGGL(mlp_clear, dim3((BH + 255) / 256), dim3(256), 0, st, flags, progress, BH);
+  hipLaunchKernelGGL(mlp_fwd_fused, dim3(BH + workers), dim3(kWaves * 64), 0, st, (const bf16*)q,
                      (const bf16*)k, (const bf16*)v, w1, w2, wbs, H, N, a, (bf16*)o, w1_out, w2_out,
-                     static_cast<int*>(ws));
+                     flags, sw, BH);
+  hipLaunchKernelGGL(mlp_fixup_bf16, dim3(B * H), dim3(kWaves * 64), 0, st, (const bf16*)q,
+                     (const bf16*)k, (const bf16*)v, w1, w2, wbs, H, N, a, (bf16*)o, w1_out, w2_out,
+                     (const int*)flags);
   return hipGetLastError();
 }
 
