@@ -216,8 +216,9 @@ struct MlpLds {
   int bad;
 };
 
-// Intermediates of the split schedule (SPLIT), per (b, h) chain in the workspace: for every chunk and
-// thread the -a D1 and X2 tiles the thread's wave holds (bf16x4 x 2, then fp16x4 x 2: 32 bytes), for
+// Intermediates of the split schedule (SPLIT), per (b, h) chain in the workspace: for every chunk the
+// -a D1 tiles of every thread's wave (bf16x4 x 2 per thread), then the X2 tiles (fp16x4 x 2), so
+// that each store instruction writes whole lines, for
 // every chunk the -a E tile (four 16 x 16 tiles, lane l of wave w < 4 holds tile w's accumulator
 // fragment: 8 bytes), and at the start of every read-out segment a checkpoint of the state (each
 // thread's W1 and W2 tiles: 16 fp32x4).
@@ -250,7 +251,7 @@ __device__ __forceinline__ void st8_out(void* p, uint2 v) {
   __builtin_nontemporal_store(__builtin_bit_cast(u32x2_nt, v), reinterpret_cast<u32x2_nt*>(p));
 }
 struct MlpSplitWs {
-  uint4* inter;   // [bh][chunk][thread][2]
+  uint4* inter;   // [bh][chunk][D1, X2][thread]
   uint2* etile;   // [bh][chunk][4 waves][64 lanes]
   f32x4* ckpt;    // [bh][segment][thread][16]
   int* progress;  // [bh]: chunks whose intermediates are published (release, agent scope)
@@ -320,7 +321,7 @@ __device__ __forceinline__ bool mlp_chain(
   __syncthreads();
 
   const long long bhs = blockIdx.x;
-  uint4* const inter = sw.inter + bhs * mlp_inter_uint4(C) + 2 * t;
+  uint4* const inter = sw.inter + bhs * mlp_inter_uint4(C) + t;
   uint2* const etile = sw.etile + bhs * mlp_etile_uint2(C) + 64 * (w & 3) + l;
   f32x4* const ckpt = sw.ckpt + bhs * mlp_ckpt_f32x4(C) + 16 * t;
   bf16x4 d1p[kNh];  // -a D1 of the previous chunk, [token][hidden] tiles
@@ -465,7 +466,7 @@ __device__ __forceinline__ bool mlp_chain(
       x2tp = S::cat(S::cvt(xt[0]), S::cvt(xt[1]));
       if constexpr (SPLIT) {
         const uint2 x0 = __builtin_bit_cast(uint2, x2b[0]), x1 = __builtin_bit_cast(uint2, x2b[1]);
-        st16_out(&inter[(long long)c * kWaves * 64 * 2 + 1], make_uint4(x0.x, x0.y, x1.x, x1.y));
+        st16_out(&inter[((long long)c * 2 + 1) * kWaves * 64], make_uint4(x0.x, x0.y, x1.x, x1.y));
       }
     }
     x8 w2a[4];  // W2^T tiles (k = this wave's hidden units), for both products below
@@ -548,7 +549,7 @@ __device__ __forceinline__ bool mlp_chain(
       }
       if constexpr (SPLIT) {
         const uint2 d0 = __builtin_bit_cast(uint2, d1p[0]), d1 = __builtin_bit_cast(uint2, d1p[1]);
-        st16_out(&inter[(long long)c * kWaves * 64 * 2], make_uint4(d0.x, d0.y, d1.x, d1.y));
+        st16_out(&inter[(long long)c * 2 * kWaves * 64], make_uint4(d0.x, d0.y, d1.x, d1.y));
       }
       // W1 += K^T (-a D1): A = K^T (row feature, k token; LDS transpose read), B = -a D1.
       for (int m = 0; m < 4; ++m) {
@@ -702,7 +703,7 @@ __device__ __forceinline__ bool readout_segment(
     for (int n = 0; n < kNh; ++n)
       for (int o2 = 0; o2 < 4; ++o2) W2t[n][o2] = ck[8 + n * 4 + o2];
   }
-  const uint4* inter = sw.inter + (long long)bh * mlp_inter_uint4(C) + 2 * t;
+  const uint4* inter = sw.inter + (long long)bh * mlp_inter_uint4(C) + t;
   const uint2* etile = sw.etile + (long long)bh * mlp_etile_uint2(C) + 64 * (w & 3) + l;
   // Threads 0..255 move one 16-byte piece of K or Q per chunk; 256..511 repeat them (same source and
   // LDS address), so that every wave issues the same loads.
@@ -712,9 +713,9 @@ __device__ __forceinline__ bool readout_segment(
   auto load = [&](int cc, MlpChunkRegs& d) {  // chunk indices past the segment repeat its last chunk
     cc = min(cc, c1 - 1);
     d.kq = ld16(psrc + (long long)cc * kCh * ts);
-    const uint4* pi = inter + (long long)cc * kWaves * 64 * 2;
+    const uint4* pi = inter + (long long)cc * 2 * kWaves * 64;
     d.d1 = pi[0];
-    d.x2 = pi[1];
+    d.x2 = pi[kWaves * 64];
     d.e = etile[(long long)cc * 4 * 64];
   };
   auto to_lds = [&](int parity, const MlpChunkRegs& d) {
