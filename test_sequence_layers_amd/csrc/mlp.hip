@@ -228,7 +228,7 @@ struct MlpLds {
 // other segments are long.
 constexpr int kSegLong = 64;
 constexpr int kSegTail = 16;
-constexpr int kReadoutWorkers = 64;  // read-out workgroups of the fused launch
+constexpr int kReadoutWorkers = 96;  // read-out workgroups of the fused launch (48, 64, 96, 128, 192 measured: 96 best)
 struct SegPlan {
   int C, R, nlong;  // chunks; start of the tail region; segments before it
   __host__ __device__ explicit SegPlan(int C_) : C(C_), R((C_ - 1) / kSegLong * kSegLong), nlong((C_ - 1) / kSegLong) {}
