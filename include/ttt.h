@@ -221,7 +221,7 @@ ttt_status ttt_forward_chunked_bidir2d(ttt_dtype dt, int B, int H, int height, i
  * Sizes: D in {16, 32, 64}, Dh a multiple of 64 in [64, 1024], chunk in {16, 32, 64}. bf16 I/O with
  * (D, Dh, chunk) = (64, 256, 16) runs on the matrix cores with the state held in registers, the
  * forward chain of each (b, h) on one CU and the read-outs beside it on other CUs from per-chunk
- * intermediates and state checkpoints kept in the workspace (about (N / 16) * 18 KiB plus
+ * intermediates and state checkpoints kept in the workspace (about (N / 16) * 20 KiB plus
  * (N / 1024 + 4) * 128 KiB per (b, h)); bf16
  * I/O with D = 64, chunk = 16 and Dh = 512, 768 or 1024 runs on the matrix cores with the fp32 state
  * in the workspace (bf16 operands, fp32 accumulation); every other size, and fp32 I/O, runs in
