@@ -870,6 +870,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_fused(
         __builtin_amdgcn_s_sleep(16);
         ++polls;
       }
+      // The polling thread's acquire pairs with the chain's release; the barrier orders the other
+      // waves after it, and each wave's own acquire fence drops its stale cache lines.
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       s_wait = polls < max_polls ? 0 : 1;
     }
     __syncthreads();
