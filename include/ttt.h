@@ -222,7 +222,10 @@ ttt_status ttt_forward_chunked_bidir2d(ttt_dtype dt, int B, int H, int height, i
  * (D, Dh, chunk) = (64, 256, 16) runs on the matrix cores with the state held in registers, the
  * forward chain of each (b, h) on one CU and the read-outs beside it on other CUs from per-chunk
  * intermediates and state checkpoints kept in the workspace (about (N / 16) * 20 KiB plus
- * (N / 1024 + 4) * 128 KiB per (b, h)); bf16
+ * (N / 1024 + 4) * 128 KiB per (b, h): the size ttt_workspace_size returns). On that path a
+ * workspace of at least B*H ints but less than that size runs the single-workgroup schedule
+ * instead (forward and read-outs in one workgroup per (b, h), about 13 % slower at 4 x 8192 x 12),
+ * for sequences whose intermediates the caller cannot hold; bf16
  * I/O with D = 64, chunk = 16 and Dh = 512, 768 or 1024 runs on the matrix cores with the fp32 state
  * in the workspace (bf16 operands, fp32 accumulation); every other size, and fp32 I/O, runs in
  * plain fp32 arithmetic with the state in the workspace.

@@ -391,7 +391,11 @@ ttt_status ttt_mlp_forward(ttt_dtype dt, int B, int H, int N, int D, int Dh, int
       return TTT_ERR_INVALID;
   }
   if (w1_out && w2_out && overlaps(outs[0], outs[1])) return TTT_ERR_INVALID;
-  const size_t need = ttt_workspace_size(TTT_OP_MLP, dt, B, H, N, D, Dh, chunk);
+  // ttt_workspace_size's figure runs the fastest schedule; on the matrix-core path a workspace of at
+  // least one int per chain, but less than that, runs the single-workgroup schedule.
+  const size_t full = ttt_workspace_size(TTT_OP_MLP, dt, B, H, N, D, Dh, chunk);
+  const size_t least = ttt::mlp_min_workspace_bytes(dt == TTT_BF16, B, H, N, D, Dh, chunk);
+  const size_t need = workspace_bytes >= full ? full : least;
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return TTT_ERR_WORKSPACE;
     if (!aligned16(workspace)) return TTT_ERR_INVALID;
@@ -401,7 +405,7 @@ ttt_status ttt_mlp_forward(ttt_dtype dt, int B, int H, int N, int D, int Dh, int
       return TTT_ERR_INVALID;
   }
   return from_hip(ttt::mlp_launch(dt == TTT_BF16, B, H, N, D, Dh, chunk, eta, q, k, v, w1_0, w2_0,
-                                  w_batch_stride, o, w1_out, w2_out, workspace,
+                                  w_batch_stride, o, w1_out, w2_out, workspace, need,
                                   static_cast<hipStream_t>(stream)));
 }
 

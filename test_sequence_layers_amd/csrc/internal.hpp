@@ -46,10 +46,11 @@ hipError_t chunked_bwd_launch(bool bidir, bool bf16_io, int B, int H, int N, int
 // ---- TTT-MLP --------------------------------------------------------------------------------
 bool mlp_supported(int D, int Dh, int chunk);
 size_t mlp_workspace_bytes(bool bf16_io, int B, int H, int N, int D, int Dh, int chunk);
+size_t mlp_min_workspace_bytes(bool bf16_io, int B, int H, int N, int D, int Dh, int chunk);
 hipError_t mlp_launch(bool bf16_io, int B, int H, int N, int D, int Dh, int chunk, float eta,
                       const void* q, const void* k, const void* v, const float* w1,
                       const float* w2, long long w_bstride, void* o, float* w1_out,
-                      float* w2_out, void* ws, hipStream_t st);
+                      float* w2_out, void* ws, size_t ws_bytes, hipStream_t st);
 
 // ---- token-grid permutations (column order) ---------------------------------------------------
 hipError_t gather_columns_launch(bool bf16_io, int B, int Hg, int Wg, int C,

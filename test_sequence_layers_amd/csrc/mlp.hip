@@ -665,6 +665,24 @@ __device__ __noinline__ void mlp_chain_bf16(
 //  3. mlp_fixup_bf16 recomputes in full (bf16 W2-side operands, read-outs and end states) every
 //     chain that a range check flagged, in the forward chain (bit 0), in a read-out (bit 1) or by a
 //     wait that timed out (bit 2).
+// The single-workgroup schedule, for callers whose workspace holds only the flags (one int per
+// chain): the fp16 pass with the read-outs in the chain's own steps, and only when a range check
+// failed the bf16 pass over the same chain (its outputs replace the first pass's); flags[bh]
+// records which.
+__global__ __launch_bounds__(kWaves * 64, 1) void mlp_fwd_single(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const float* __restrict__ w1, const float* __restrict__ w2, long long wbs, int H, int N,
+    float a, bf16* __restrict__ o, float* __restrict__ w1_out, float* __restrict__ w2_out,
+    int* __restrict__ flags) {
+  __shared__ __align__(16) MlpLds lds;
+  const bool bad = mlp_chain<true>(q, k, v, w1, w2, wbs, H, N, a, o, w1_out, w2_out, lds);
+  if (threadIdx.x == 0) flags[blockIdx.x] = bad ? 1 : 0;
+  if (bad) {
+    __syncthreads();  // every wave is done with the first pass's shared memory
+    mlp_chain_bf16(q, k, v, w1, w2, wbs, H, N, a, o, w1_out, w2_out, lds);
+  }
+}
+
 __global__ void mlp_clear(int* __restrict__ flags, int* __restrict__ progress, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) {
@@ -1425,6 +1443,11 @@ MlpSplitLayout mlp_split_layout(int BH, int N) {
 }
 size_t mlp_workspace_bytes(bool bf16_io, int B, int H, int N, int D, int Dh, int chunk) {
   if (mlp_fast_path(bf16_io, D, Dh, chunk)) return mlp_split_layout(B * H, N).total;
+  return mlp_min_workspace_bytes(bf16_io, B, H, N, D, Dh, chunk);
+}
+// The least workspace a call accepts: on the fast path the single-workgroup schedule's flags.
+size_t mlp_min_workspace_bytes(bool bf16_io, int B, int H, int N, int D, int Dh, int chunk) {
+  if (mlp_fast_path(bf16_io, D, Dh, chunk)) return (size_t)B * H * sizeof(int);
   if (mlp_wide_path(bf16_io, D, Dh, chunk)) return (size_t)B * H * 3 * (size_t)D * Dh * sizeof(float);
   return (size_t)B * H * (2 * (size_t)D * Dh + 4 * (size_t)chunk * Dh) * sizeof(float);
 }
@@ -1432,7 +1455,7 @@ size_t mlp_workspace_bytes(bool bf16_io, int B, int H, int N, int D, int Dh, int
 hipError_t mlp_launch(bool bf16_io, int B, int H, int N, int D, int Dh, int chunk, float eta,
                       const void* q, const void* k, const void* v, const float* w1,
                       const float* w2, long long wbs, void* o, float* w1_out, float* w2_out,
-                      void* ws, hipStream_t st) {
+                      void* ws, size_t ws_bytes, hipStream_t st) {
   const float a = eta / (float)chunk;
   if (mlp_wide_path(bf16_io, D, Dh, chunk)) {
     const int nb = Dh / kWideBlock;
@@ -1456,6 +1479,11 @@ hipError_t mlp_launch(bool bf16_io, int B, int H, int N, int D, int Dh, int chun
     return hipGetLastError();
   }
   const MlpSplitLayout L = mlp_split_layout(B * H, N);
+  if (ws_bytes < L.total) {  // the single-workgroup schedule
+    hipLaunchKernelGGL(mlp_fwd_single, dim3(B * H), dim3(kWaves * 64), 0, st, (const bf16*)q, (const bf16*)k,
+                       (const bf16*)v, w1, w2, wbs, H, N, a, (bf16*)o, w1_out, w2_out, static_cast<int*>(ws));
+    return hipGetLastError();
+  }
   char* base = static_cast<char*>(ws);
   int* flags = reinterpret_cast<int*>(base + L.flags);
   int* progress = reinterpret_cast<int*>(base + L.progress);

@@ -204,9 +204,10 @@ def mlp_flags(x, ws):
     return ws[: 4 * x.wl.B * x.wl.H].view(torch.int32).cpu().numpy().reshape(x.wl.B, x.wl.H)
 
 
-def run_mlp(x, w1=None, w2=None, want_state=False):
+def run_mlp(x, w1=None, w2=None, want_state=False, flags_only_workspace=False):
     """The TTT-MLP layer of x through the binding with a workspace of our own; returns
-    (out, w1_end, w2_end, flags)."""
+    (out, w1_end, w2_end, flags). flags_only_workspace: a workspace of one int per chain, which runs
+    the single-workgroup schedule on the matrix-core path."""
     lib = T()
     wl = x.wl
     q, k, v = dev(x.q, wl.dtype), dev(x.k, wl.dtype), dev(x.v, wl.dtype)
@@ -214,6 +215,8 @@ def run_mlp(x, w1=None, w2=None, want_state=False):
     W2 = torch.from_numpy(np.ascontiguousarray(x.w2 if w2 is None else w2)).cuda()
     need = lib.ttt_workspace_size(lib.TTT_OP_MLP, lib.TTT_BF16 if wl.dtype == "bf16" else lib.TTT_F32, wl.B, wl.H,
                                   wl.N, wl.D, wl.Dh, wl.chunk)
+    if flags_only_workspace:
+        need = 4 * wl.B * wl.H
     ws = torch.full((max(need, 4 * wl.B * wl.H),), 0x55, dtype=torch.uint8, device="cuda")
     s1 = torch.full((wl.B, wl.H, wl.D, wl.Dh), float("nan"), device="cuda") if want_state else None
     s2 = torch.full((wl.B, wl.H, wl.Dh, wl.D), float("nan"), device="cuda") if want_state else None
@@ -239,6 +242,39 @@ def test_full_size_mlp_every_head(name):
     print(f"{name}: worst slice (b, h) = {tuple(int(i) for i in worst)}", flush=True)
     assert report(name, got, ref) <= BF16_TOL
     assert not flags.any(), f"chains recomputed in bf16: {np.argwhere(flags)}"
+
+
+@pytest.mark.parametrize("wl", [W["ttt_mlp_causal_8k"].with_(B=1, N=2048, H=4, seed=160),
+                                W["ttt_mlp_causal_8k"].with_(B=2, N=1040, H=2, seed=161)],
+                         ids=lambda w: f"B{w.B}N{w.N}H{w.H}")
+def test_mlp_single_workgroup_schedule(wl):
+    """A workspace of one int per chain (less than ttt_workspace_size, which sizes the split schedule's
+    intermediates) runs the single-workgroup schedule: outputs and end states against the oracle, and
+    against the split schedule (same algebra, both within the bf16 bar of the oracle)."""
+    print(f"mlp single-workgroup schedule B={wl.B} N={wl.N} H={wl.H}", flush=True)
+    x = synth.make_inputs(wl)
+    got, s1, s2, flags = run_mlp(x, want_state=True, flags_only_workspace=True)
+    split, t1, t2, _ = run_mlp(x, want_state=True)
+    ref, r1, r2 = O.mlp_causal(x.q64, x.k64, x.v64, x.w1, x.w2, wl.eta, wl.chunk)
+    assert report("mlp single", got, ref) <= BF16_TOL
+    assert report("mlp split", split, ref) <= BF16_TOL
+    for st, rf in ((s1, r1), (s2, r2), (t1, r1), (t2, r2)):
+        assert np.abs(st - rf).max() / np.abs(rf).max() <= BF16_TOL
+    assert not flags.any()
+
+
+def test_mlp_single_workgroup_schedule_recomputes_out_of_range_chains():
+    """The single-workgroup schedule's own bf16 recomputation, with first-layer weights that drive one
+    chain's activations beyond fp16's range (as test_mlp_recomputes_only_the_flagged_chains does for
+    the split schedule)."""
+    wl = W["ttt_mlp_causal_8k"].with_(B=2, N=64, H=3, seed=162, eta=1e-3)
+    x = synth.make_inputs(wl)
+    w1 = x.w1.copy()
+    w1[1] *= 2000.0  # head 1's pre-activations in the hundreds
+    out, _, _, flags = run_mlp(x, w1=w1, flags_only_workspace=True)
+    ref = O.mlp_causal(x.q64, x.k64, x.v64, w1, x.w2, wl.eta, wl.chunk)[0]
+    assert flags[:, 1].all() and not flags[:, 0].any() and not flags[:, 2].any(), flags
+    assert report("mlp single, flagged chain", out, ref) <= BF16_TOL
 
 
 # ------------------------------------------------------------------ states, edge cases, invariants
