@@ -29,7 +29,9 @@ FLAGS = [
 # Measured: causal TTT-Linear 91 -> 86 us; the TTT-MLP kernel (no AGPR moves either way) is left
 # as it was. The chunk-step kernels (chunked scans, TTT-MLP) are chains of dependent short
 # operations; the scheduler's ILP-maximising strategy orders them slightly better (bidirectional
-# 46.1 -> 45.1 us, TTT-MLP 958 -> 947-954 us; the full-batch kernels are unchanged by it).
+# 46.1 -> 45.1 us, TTT-MLP 958 -> 947-954 us; the full-batch kernels are unchanged by it). For the
+# split TTT-MLP schedule: 0.815-0.819 ms, against 0.826 (default), 0.828 (max-memory-clause), 0.840
+# (iterative-ilp) and 0.858 ms (iterative-minreg).
 SCHED_ILP = ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]
 SOURCE_FLAGS = {
     "fullbatch.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
